@@ -1,0 +1,211 @@
+/*
+ * hcsa.h -- C ABI of libhcsa, the hybrid compressed attention (CSA + HCA) of DeepSeek-V4
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Method (web pages on the DeepSeek-V4 release):
+ *   Lighthouse, "deep deepseek v4 release", section 八 item 3: CSA pools the KV of every
+ *   m = 4 tokens into one entry, a Lightning Indexer keeps the top-k compressed entries
+ *   (1024 Pro / 512 Flash) for sparse attention, and a sliding-window branch of
+ *   n_win = 128 raw tokens restores local detail; HCA pools every m' = 128 tokens into
+ *   one entry and attends densely over all of them.
+ *   Same page, item 7: the indexer keeps its own compressed keys.
+ *   9fzt.com digest, item 4: FP4 on the indexer's QK path; FP32 index scores compressed
+ *   to BF16 for the top-k selector.
+ *   tulong.co Q&A, 技术架构创新 item 1: every 4 tokens -> one block, every 128 -> one entry.
+ *
+ * Readings where the pages are silent (the library implements exactly these):
+ *   - pooling: y[j] = sum_i alpha_i x[j*r + i], alpha = softmax(omega), omega [r] shared
+ *     by every block, sequence and channel; the T mod r tail is not pooled.
+ *   - indexer score: s_j = sum_g w_g * max(0, q_g . k_j), fp32 accumulate, optionally
+ *     rounded to bf16 (nearest-even); -0 is stored as +0.
+ *   - top-k: the min(k, n) largest scores, ties to the lowest index, output ascending,
+ *     padded with -1.
+ *   - CSA attention: one softmax over [selected entries] ++ [raw window tokens
+ *     max(0, p-n_win+1) .. p]; HCA attention: one softmax over all visible entries.
+ *   - visibility: entry j of a stream with ratio r is visible to the token at position p
+ *     iff (j+1)*r <= p+1.  Query i of every sequence sits at position pos0 + i (all
+ *     sequences of a call share one length).
+ *   - one KV head shared by all query heads (MQA); logits are scale * q.k.
+ *   - MXFP4: OCP MX e2m1 elements with one e8m0 scale per 32 elements, scale exponent
+ *     floor(log2 amax) - 2 (clamped to [-127, 127]; amax = 0 gives -127), elements
+ *     rounded to nearest-even on the e2m1 grid and saturated at +-6.  Two elements per
+ *     byte, element 2i in the low nibble.  Scale byte = exponent + 127.
+ *
+ * Conventions for every call:
+ *   - All data pointers are device pointers owned by the caller; the library never
+ *     allocates device memory.  Calls that need scratch take (workspace, ws_bytes) and a
+ *     matching *_workspace_size() query; workspace must be 256-byte aligned.
+ *   - Tensors are row-major with contiguous rows; "bstride" is the distance between
+ *     sequences, in elements for F32/BF16 tensors and in bytes for MXFP4 tensors.
+ *   - Data pointers must be 16-byte aligned and bstrides must keep that alignment.
+ *   - Every call validates its arguments on the host before any launch and returns
+ *     HCSA_OK (0) or a negative code; hcsa_last_error() gives a message (thread-local).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = default stream) and
+ *     never synchronizes.  Outputs are defined once the stream reaches the call.
+ *   - Calls that share a workspace on different streams race.
+ */
+#ifndef HCSA_H
+#define HCSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *hcsa_stream; /* hipStream_t */
+
+enum hcsa_dtype { HCSA_F32 = 0, HCSA_BF16 = 1, HCSA_MXFP4 = 2 };
+
+enum hcsa_status {
+  HCSA_OK = 0,
+  HCSA_EINVAL = -1,     /* bad size, pointer or combination of arguments */
+  HCSA_EDTYPE = -2,     /* unsupported dtype for this call */
+  HCSA_EALIGN = -3,     /* pointer or stride not 16-byte aligned */
+  HCSA_EWORKSPACE = -4, /* workspace missing, misaligned or too small */
+  HCSA_EHIP = -5        /* a HIP launch failed; message has hipGetErrorString */
+};
+
+/* Library version (major*10000 + minor*100 + patch). */
+int hcsa_version(void);
+
+/* Message of the last non-zero status returned on this thread ("" if none). */
+const char *hcsa_last_error(void);
+
+/*
+ * Block pooling (CSA m = 4, HCA m' = 128, indexer keys m = 4)
+ * [Lighthouse section 八 item 3; tulong.co 技术架构创新 item 1].
+ *
+ * x      [B][T][D] F32 or BF16; sequence b starts at x + b*x_bstride (elements).
+ * omega  [ratio] F32 pooling logits; alpha = softmax(omega) is computed on the device.
+ * y      F32/BF16: [B][T/ratio][D], sequence stride y_bstride elements.
+ *        MXFP4: packed codes [B][T/ratio][D/2] bytes, sequence stride y_bstride bytes,
+ *        and y_scales [B][T/ratio][D/32] e8m0 bytes, stride ys_bstride bytes.
+ * Writes floor(T/ratio) rows per sequence; accumulates in fp32 and rounds once.
+ * Limits: 1 <= ratio <= 1024, D % 8 == 0, D <= 2048 (MXFP4: D % 32 == 0); T >= 0, B >= 1.
+ */
+int hcsa_compress_kv(const void *x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                     const float *omega, int ratio, void *y, int y_dtype, int64_t y_bstride,
+                     uint8_t *y_scales, int64_t ys_bstride, hcsa_stream stream);
+
+/*
+ * Several pooling jobs of one batch in a single launch (for instance the CSA K, V and
+ * indexer-key blocks and the HCA K and V blocks that one decode token completes).  Each job
+ * has the meaning and limits of hcsa_compress_kv (x has its own T; jobs share B).  The
+ * call validates every job first and launches nothing if any is invalid.  Outputs of
+ * different jobs must not overlap.
+ */
+#define HCSA_MAX_POOL_JOBS 8
+typedef struct hcsa_pool_job {
+  const void *x;
+  int x_dtype;
+  int64_t x_bstride;
+  int T, D;
+  const float *omega;
+  int ratio;
+  void *y;
+  int y_dtype;
+  int64_t y_bstride;
+  uint8_t *y_scales;
+  int64_t ys_bstride;
+} hcsa_pool_job;
+int hcsa_compress_kv_batched(const hcsa_pool_job *jobs, int n_jobs, int B, hcsa_stream stream);
+
+/*
+ * MXFP4 quantization of rows [rows][D] (F32 or BF16) into packed codes [rows][D/2] and
+ * e8m0 scales [rows][D/32] [9fzt.com digest item 4: FP4 on the indexer QK path].
+ * D % 32 == 0.
+ */
+int hcsa_mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int D, uint8_t *packed,
+                        uint8_t *scales, hcsa_stream stream);
+
+/*
+ * Top-k selector over score rows [Lighthouse section 八 item 3: the indexer keeps the
+ * top-k compressed blocks; 9fzt.com digest item 4: BF16 scores for the selector].
+ *
+ * scores  [B*Nq][row_stride] F32 or BF16; row r = b*Nq + i belongs to the token at
+ *         position pos0 + i, which sees n = min(N, (pos0+i+1)/ratio) entries; only
+ *         scores[r][0..n) are read.
+ * idx     [B*Nq][k] int32 output: the min(k, n) entries with the largest scores (ties to
+ *         the lowest index) in ascending order, then -1.  Bit-exact and deterministic.
+ * Limits: 1 <= k <= 4096, 1 <= N, row_stride >= N, ratio >= 1, pos0 >= 0.
+ */
+size_t hcsa_topk_workspace_size(int score_dtype, int B, int Nq, int N, int k);
+int hcsa_topk(const void *scores, int score_dtype, int64_t row_stride, int B, int Nq, int N,
+              int ratio, int64_t pos0, int k, int32_t *idx, void *workspace,
+              size_t ws_bytes, hcsa_stream stream);
+
+/*
+ * Lightning indexer + top-k [Lighthouse section 八 items 3 and 7; 9fzt.com digest item 4].
+ *
+ * q_idx   [B][Nq][H_I][d_I] F32 or BF16 indexer queries.
+ * w_idx   [B][Nq][H_I] F32 head weights.
+ * k_idx   compressed indexer keys of every sequence: F32/BF16 [B][N][d_I] (bstride in
+ *         elements) or MXFP4 packed [B][N][d_I/2] (bstride in bytes) with k_scales
+ *         [B][N][d_I/32] (ks_bstride bytes).  With MXFP4 keys the queries are quantized
+ *         to MXFP4 (per head vector) inside the call and the dot products are exact.
+ * Scores s_j = sum_g w_g max(0, q_g . k_j) for the visible j (see hcsa_topk), rounded to
+ * score_dtype, then top-k as in hcsa_topk.
+ * scores_out  optional [B*Nq][N] score_dtype copy of the scores (NULL to skip).
+ * Limits: H_I in {1, 2, 4, 8, 16}; d_I in {32, 64, 128} (F32 keys: {32, 64}; MXFP4: {32, 64, 128});
+ *         q dtype F32 with F32 keys, BF16 with BF16 keys, F32 or BF16 with MXFP4 keys.
+ */
+size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score_dtype);
+int hcsa_csa_index_topk(const void *q_idx, int q_dtype, const float *w_idx, const void *k_idx,
+                        int k_dtype, int64_t k_bstride, const uint8_t *k_scales,
+                        int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
+                        int64_t pos0, int k, int score_dtype, int32_t *topk_idx,
+                        void *scores_out, void *workspace, size_t ws_bytes,
+                        hcsa_stream stream);
+
+/*
+ * Lightning-indexer scores only (the first half of hcsa_csa_index_topk; same arguments
+ * and limits): scores [B*Nq][N] in score_dtype, entries at or past the visible count of a
+ * row are left untouched.  No workspace.
+ */
+int hcsa_csa_index_scores(const void *q_idx, int q_dtype, const float *w_idx,
+                          const void *k_idx, int k_dtype, int64_t k_bstride,
+                          const uint8_t *k_scales, int64_t ks_bstride, int B, int Nq, int H_I,
+                          int d_I, int N, int ratio, int64_t pos0, int score_dtype,
+                          void *scores, hcsa_stream stream);
+
+/*
+ * CSA sparse attention [Lighthouse section 八 item 3]: for each query token (position
+ * p = pos0 + i) and head, one softmax over the selected compressed entries (topk_idx,
+ * entries outside [0, n_c(p)) are skipped) followed by the raw window tokens
+ * max(0, p-n_win+1) .. p.
+ *
+ * q       [B][Nq][H][d]; kc, vc [B][N][d] (c_bstride elements); topk_idx [B][Nq][k].
+ * k_raw, v_raw [B][T_raw][d] (raw_bstride elements); row t holds position raw_pos0 + t.
+ *         Every window position of every query must lie in [raw_pos0, raw_pos0 + T_raw).
+ * out     [B][Nq][H][d] F32, lse [B][Nq][H] F32 (natural log; -inf and o = 0 when no key).
+ * kv_dtype F32 or BF16 (q has the same dtype).  ratio is the CSA pooling ratio.
+ * Limits: 1 <= H <= 64, d % 8 == 0, 8 <= d <= 256, H*d <= 4096, 0 <= k <= 4096,
+ *         0 <= n_win <= 4096.
+ */
+size_t hcsa_csa_sparse_attn_workspace_size(int B, int Nq, int H, int d, int k, int n_win);
+int hcsa_csa_sparse_attn(const void *q, const void *kc, const void *vc, int64_t c_bstride,
+                         int N, const int32_t *topk_idx, int k, const void *k_raw,
+                         const void *v_raw, int64_t raw_bstride, int64_t T_raw,
+                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0, int kv_dtype,
+                         int B, int Nq, int H, int d, float scale, float *out, float *lse,
+                         void *workspace, size_t ws_bytes, hcsa_stream stream);
+
+/*
+ * HCA dense attention [Lighthouse section 八 item 3; tulong.co 技术架构创新 item 1]:
+ * for each query token (position pos0 + i) and head, one softmax over every visible
+ * entry j < min(N, (p+1)/ratio) of kh/vh [B][N][d] (h_bstride elements).
+ * Same q/out/lse layout and limits as hcsa_csa_sparse_attn.
+ */
+size_t hcsa_hca_dense_attn_workspace_size(int B, int Nq, int H, int d, int N);
+int hcsa_hca_dense_attn(const void *q, const void *kh, const void *vh, int64_t h_bstride,
+                        int N, int ratio, int64_t pos0, int kv_dtype, int B, int Nq, int H,
+                        int d, float scale, float *out, float *lse, void *workspace,
+                        size_t ws_bytes, hcsa_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCSA_H */

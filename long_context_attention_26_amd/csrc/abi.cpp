@@ -1,0 +1,358 @@
+// C ABI of libhcsa: argument validation on the host, then asynchronous launches on the
+// caller's stream.  No call allocates device memory or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return HCSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HCSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+int elem_size(int dt) { return dt == HCSA_F32 ? 4 : 2; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return HCSA_OK;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(HCSA_EWORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                ws == nullptr ? " (null)" : "");
+  if (!aligned256(ws)) return fail(HCSA_EWORKSPACE, "workspace must be 256-byte aligned");
+  return HCSA_OK;
+}
+
+// Common checks of the attention calls (q/out/lse shape and dtype).
+int check_attn_common(const void* q, int kv_dtype, int B, int Nq, int H, int d, float scale,
+                      const float* out, const float* lse, int ratio, int64_t pos0) {
+  if (kv_dtype != HCSA_F32 && kv_dtype != HCSA_BF16)
+    return fail(HCSA_EDTYPE, "kv_dtype must be F32 or BF16");
+  if (B < 1 || Nq < 1) return fail(HCSA_EINVAL, "B and Nq must be >= 1");
+  if (static_cast<int64_t>(B) * Nq > 65535) return fail(HCSA_EINVAL, "B*Nq must be <= 65535");
+  if (H < 1 || H > 64) return fail(HCSA_EINVAL, "H must be in [1, 64]");
+  if (d < 8 || d > 256 || d % 8 != 0) return fail(HCSA_EINVAL, "d must be a multiple of 8 in [8, 256]");
+  if (H * d > 4096) return fail(HCSA_EINVAL, "H*d must be <= 4096");
+  if (!(scale == scale)) return fail(HCSA_EINVAL, "scale is NaN");
+  if (ratio < 1) return fail(HCSA_EINVAL, "ratio must be >= 1");
+  if (pos0 < 0) return fail(HCSA_EINVAL, "pos0 must be >= 0");
+  if (!q || !out || !lse) return fail(HCSA_EINVAL, "q, out and lse must be non-null");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(lse))
+    return fail(HCSA_EALIGN, "q, out and lse must be 16-byte aligned");
+  return HCSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hcsa_version(void) { return 100; }
+
+const char* hcsa_last_error(void) { return g_err.c_str(); }
+
+static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                          const float* omega, int ratio, void* y, int y_dtype,
+                          int64_t y_bstride, uint8_t* y_scales, int64_t ys_bstride);
+
+int hcsa_compress_kv(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                     const float* omega, int ratio, void* y, int y_dtype, int64_t y_bstride,
+                     uint8_t* y_scales, int64_t ys_bstride, hcsa_stream stream) {
+  const int rc = check_compress(x, x_dtype, x_bstride, B, T, D, omega, ratio, y, y_dtype,
+                                y_bstride, y_scales, ys_bstride);
+  if (rc) return rc;
+  if (T / ratio == 0) return ok();
+  return hip_status(hcsa::launch_compress(x, x_dtype, x_bstride, B, T, D, omega, ratio, y,
+                                          y_dtype, y_bstride, y_scales, ys_bstride,
+                                          static_cast<hipStream_t>(stream)),
+                    "hcsa_compress_kv");
+}
+
+int hcsa_compress_kv_batched(const hcsa_pool_job* jobs, int n_jobs, int B, hcsa_stream stream) {
+  if (n_jobs < 0 || n_jobs > HCSA_MAX_POOL_JOBS)
+    return fail(HCSA_EINVAL, "n_jobs must be in [0, %d]", HCSA_MAX_POOL_JOBS);
+  if (n_jobs > 0 && !jobs) return fail(HCSA_EINVAL, "jobs must be non-null");
+  for (int i = 0; i < n_jobs; ++i) {
+    const hcsa_pool_job& q = jobs[i];
+    const int rc = check_compress(q.x, q.x_dtype, q.x_bstride, B, q.T, q.D, q.omega, q.ratio,
+                                  q.y, q.y_dtype, q.y_bstride, q.y_scales, q.ys_bstride);
+    if (rc) return fail(rc, "job %d: %s", i, g_err.c_str());
+  }
+  return hip_status(hcsa::launch_compress_batched(jobs, n_jobs, B, static_cast<hipStream_t>(stream)),
+                    "hcsa_compress_kv_batched");
+}
+
+static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                          const float* omega, int ratio, void* y, int y_dtype,
+                          int64_t y_bstride, uint8_t* y_scales, int64_t ys_bstride) {
+  if (x_dtype != HCSA_F32 && x_dtype != HCSA_BF16)
+    return fail(HCSA_EDTYPE, "x_dtype must be F32 or BF16");
+  if (y_dtype != HCSA_F32 && y_dtype != HCSA_BF16 && y_dtype != HCSA_MXFP4)
+    return fail(HCSA_EDTYPE, "y_dtype must be F32, BF16 or MXFP4");
+  if (B < 1 || B > 65535) return fail(HCSA_EINVAL, "B must be in [1, 65535]");
+  if (T < 0) return fail(HCSA_EINVAL, "T must be >= 0");
+  if (D < 8 || D > 2048 || D % 8 != 0) return fail(HCSA_EINVAL, "D must be a multiple of 8 in [8, 2048]");
+  if (y_dtype == HCSA_MXFP4 && D % 32 != 0) return fail(HCSA_EINVAL, "MXFP4 output needs D % 32 == 0");
+  if (ratio < 1 || ratio > 1024) return fail(HCSA_EINVAL, "ratio must be in [1, 1024]");
+  if (!x || !y || !omega) return fail(HCSA_EINVAL, "x, omega and y must be non-null");
+  if (y_dtype == HCSA_MXFP4 && !y_scales) return fail(HCSA_EINVAL, "MXFP4 output needs y_scales");
+  const int n_out = T / ratio;
+  if (B > 1) {
+    if (x_bstride < static_cast<int64_t>(T) * D) return fail(HCSA_EINVAL, "x_bstride < T*D");
+    const int64_t yrow = y_dtype == HCSA_MXFP4 ? D / 2 : D;
+    if (y_bstride < static_cast<int64_t>(n_out) * yrow) return fail(HCSA_EINVAL, "y_bstride too small");
+    if (y_dtype == HCSA_MXFP4 && ys_bstride < static_cast<int64_t>(n_out) * (D / 32))
+      return fail(HCSA_EINVAL, "ys_bstride too small");
+  }
+  if (!aligned16(x) || !aligned16(y)) return fail(HCSA_EALIGN, "x and y must be 16-byte aligned");
+  if ((x_bstride * elem_size(x_dtype)) % 16 != 0)
+    return fail(HCSA_EALIGN, "x_bstride must keep 16-byte alignment");
+  const int64_t yb = y_dtype == HCSA_MXFP4 ? y_bstride : y_bstride * elem_size(y_dtype);
+  if (yb % 16 != 0) return fail(HCSA_EALIGN, "y_bstride must keep 16-byte alignment");
+  return HCSA_OK;
+}
+
+int hcsa_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int D, uint8_t* packed,
+                        uint8_t* scales, hcsa_stream stream) {
+  if (x_dtype != HCSA_F32 && x_dtype != HCSA_BF16)
+    return fail(HCSA_EDTYPE, "x_dtype must be F32 or BF16");
+  if (rows < 0 || rows > 0x7fffffffLL) return fail(HCSA_EINVAL, "rows must be in [0, 2^31)");
+  if (D < 32 || D > 2048 || D % 32 != 0) return fail(HCSA_EINVAL, "D must be a multiple of 32 in [32, 2048]");
+  if (!x || !packed || !scales) return fail(HCSA_EINVAL, "null pointer");
+  if (!aligned16(x) || !aligned16(packed)) return fail(HCSA_EALIGN, "x and packed must be 16-byte aligned");
+  if (rows == 0) return ok();
+  return hip_status(hcsa::launch_mxfp4_quantize(x, x_dtype, rows, D, packed, scales,
+                                                static_cast<hipStream_t>(stream)),
+                    "hcsa_mxfp4_quantize");
+}
+
+size_t hcsa_topk_workspace_size(int score_dtype, int B, int Nq, int N, int k) {
+  if (B < 1 || Nq < 1 || N < 1 || k < 1) return 0;
+  return hcsa::plan_topk(score_dtype, B * Nq, N, k).total_bytes;
+}
+
+static int check_topk_args(int score_dtype, int B, int Nq, int N, int ratio, int64_t pos0,
+                           int k) {
+  if (score_dtype != HCSA_F32 && score_dtype != HCSA_BF16)
+    return fail(HCSA_EDTYPE, "score_dtype must be F32 or BF16");
+  if (B < 1 || Nq < 1) return fail(HCSA_EINVAL, "B and Nq must be >= 1");
+  if (static_cast<int64_t>(B) * Nq > 65535) return fail(HCSA_EINVAL, "B*Nq must be <= 65535");
+  if (N < 1) return fail(HCSA_EINVAL, "N must be >= 1");
+  if (k < 1 || k > 4096) return fail(HCSA_EINVAL, "k must be in [1, 4096]");
+  if (ratio < 1) return fail(HCSA_EINVAL, "ratio must be >= 1");
+  if (pos0 < 0) return fail(HCSA_EINVAL, "pos0 must be >= 0");
+  return HCSA_OK;
+}
+
+int hcsa_topk(const void* scores, int score_dtype, int64_t row_stride, int B, int Nq, int N,
+              int ratio, int64_t pos0, int k, int32_t* idx, void* workspace,
+              size_t ws_bytes, hcsa_stream stream) {
+  int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
+  if (rc) return rc;
+  if (row_stride < N) return fail(HCSA_EINVAL, "row_stride < N");
+  if (!scores || !idx) return fail(HCSA_EINVAL, "scores and idx must be non-null");
+  if (!aligned16(scores) || !aligned16(idx)) return fail(HCSA_EALIGN, "scores and idx must be 16-byte aligned");
+  const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
+  rc = check_ws(workspace, ws_bytes, plan.total_bytes);
+  if (rc) return rc;
+  return hip_status(hcsa::launch_topk(plan, scores, score_dtype, row_stride, Nq, ratio, pos0,
+                                      idx, workspace, static_cast<hipStream_t>(stream)),
+                    "hcsa_topk");
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score_dtype) {
+  if (B < 1 || Nq < 1 || N < 1 || k < 1) return 0;
+  const size_t scores = align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
+  return scores + hcsa::plan_topk(score_dtype, B * Nq, N, k).total_bytes;
+}
+
+static int check_index_args(const void* q_idx, int q_dtype, const float* w_idx,
+                            const void* k_idx, int k_dtype, int64_t k_bstride,
+                            const uint8_t* k_scales, int64_t ks_bstride, int B, int Nq,
+                            int H_I, int d_I, int N) {
+  if (k_dtype != HCSA_F32 && k_dtype != HCSA_BF16 && k_dtype != HCSA_MXFP4)
+    return fail(HCSA_EDTYPE, "k_dtype must be F32, BF16 or MXFP4");
+  if (q_dtype != HCSA_F32 && q_dtype != HCSA_BF16) return fail(HCSA_EDTYPE, "q_dtype must be F32 or BF16");
+  if (k_dtype != HCSA_MXFP4 && q_dtype != k_dtype)
+    return fail(HCSA_EDTYPE, "q_dtype must equal k_dtype for F32/BF16 keys");
+  if (!is_pow2(H_I) || H_I > 16) return fail(HCSA_EINVAL, "H_I must be 1, 2, 4, 8 or 16");
+  if (k_dtype == HCSA_F32 && d_I != 32 && d_I != 64) return fail(HCSA_EINVAL, "F32 keys need d_I in {32, 64}");
+  if (k_dtype != HCSA_F32 && d_I != 32 && d_I != 64 && d_I != 128)
+    return fail(HCSA_EINVAL, "d_I must be 32, 64 or 128");
+  if (!q_idx || !w_idx || !k_idx) return fail(HCSA_EINVAL, "null pointer");
+  if (k_dtype == HCSA_MXFP4 && !k_scales) return fail(HCSA_EINVAL, "MXFP4 keys need k_scales");
+  if (!aligned16(q_idx) || !aligned16(k_idx))
+    return fail(HCSA_EALIGN, "q_idx and k_idx must be 16-byte aligned");
+  const int64_t kb = k_dtype == HCSA_MXFP4 ? k_bstride : k_bstride * elem_size(k_dtype);
+  if (kb % 16 != 0) return fail(HCSA_EALIGN, "k_bstride must keep 16-byte alignment");
+  if (B > 1) {
+    const int64_t row = k_dtype == HCSA_MXFP4 ? d_I / 2 : d_I;
+    if (k_bstride < static_cast<int64_t>(N) * row) return fail(HCSA_EINVAL, "k_bstride too small");
+    if (k_dtype == HCSA_MXFP4 && ks_bstride < static_cast<int64_t>(N) * (d_I / 32))
+      return fail(HCSA_EINVAL, "ks_bstride too small");
+  }
+  return HCSA_OK;
+}
+
+int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
+                          const void* k_idx, int k_dtype, int64_t k_bstride,
+                          const uint8_t* k_scales, int64_t ks_bstride, int B, int Nq, int H_I,
+                          int d_I, int N, int ratio, int64_t pos0, int score_dtype,
+                          void* scores, hcsa_stream stream) {
+  int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, 1);
+  if (rc) return rc;
+  rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
+                        B, Nq, H_I, d_I, N);
+  if (rc) return rc;
+  if (!scores) return fail(HCSA_EINVAL, "scores must be non-null");
+  if (!aligned16(scores)) return fail(HCSA_EALIGN, "scores must be 16-byte aligned");
+  return hip_status(hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
+                                              k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
+                                              pos0, score_dtype, scores,
+                                              static_cast<hipStream_t>(stream)),
+                    "hcsa_csa_index_scores");
+}
+
+int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, const void* k_idx,
+                        int k_dtype, int64_t k_bstride, const uint8_t* k_scales,
+                        int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
+                        int64_t pos0, int k, int score_dtype, int32_t* topk_idx,
+                        void* scores_out, void* workspace, size_t ws_bytes,
+                        hcsa_stream stream) {
+  int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
+  if (rc) return rc;
+  rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
+                        B, Nq, H_I, d_I, N);
+  if (rc) return rc;
+  if (!topk_idx) return fail(HCSA_EINVAL, "topk_idx must be non-null");
+  if (!aligned16(topk_idx) || (scores_out && !aligned16(scores_out)))
+    return fail(HCSA_EALIGN, "topk_idx and scores_out must be 16-byte aligned");
+  const size_t sbytes = align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
+  const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
+  rc = check_ws(workspace, ws_bytes, sbytes + plan.total_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scores = scores_out ? scores_out : workspace;
+  hipError_t e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
+                                           k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
+                                           pos0, score_dtype, scores, s);
+  if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (scores)");
+  e = hcsa::launch_topk(plan, scores, score_dtype, N, Nq, ratio, pos0, topk_idx,
+                        static_cast<char*>(workspace) + sbytes, s);
+  return hip_status(e, "hcsa_csa_index_topk (select)");
+}
+
+static int attn_max_len_csa(int k, int n_win) { return k + n_win; }
+
+size_t hcsa_csa_sparse_attn_workspace_size(int B, int Nq, int H, int d, int k, int n_win) {
+  if (B < 1 || Nq < 1 || H < 1 || d < 1 || k < 0 || n_win < 0) return 0;
+  // the plan depends on the dtype only through the fast-path choice; take the larger
+  const size_t a = hcsa::plan_attention(true, HCSA_BF16, B, Nq, H, d, attn_max_len_csa(k, n_win)).total_bytes;
+  const size_t b = hcsa::plan_attention(true, HCSA_F32, B, Nq, H, d, attn_max_len_csa(k, n_win)).total_bytes;
+  return a > b ? a : b;
+}
+
+int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t c_bstride,
+                         int N, const int32_t* topk_idx, int k, const void* k_raw,
+                         const void* v_raw, int64_t raw_bstride, int64_t T_raw,
+                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0, int kv_dtype,
+                         int B, int Nq, int H, int d, float scale, float* out, float* lse,
+                         void* workspace, size_t ws_bytes, hcsa_stream stream) {
+  int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
+  if (rc) return rc;
+  if (k < 0 || k > 4096) return fail(HCSA_EINVAL, "k must be in [0, 4096]");
+  if (n_win < 0 || n_win > 4096) return fail(HCSA_EINVAL, "n_win must be in [0, 4096]");
+  if (k > 0) {
+    if (N < 1) return fail(HCSA_EINVAL, "N must be >= 1 when k > 0");
+    if (!kc || !vc || !topk_idx) return fail(HCSA_EINVAL, "kc, vc and topk_idx must be non-null");
+    if (!aligned16(kc) || !aligned16(vc)) return fail(HCSA_EALIGN, "kc and vc must be 16-byte aligned");
+    if ((c_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "c_bstride alignment");
+    if (B > 1 && c_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "c_bstride < N*d");
+  }
+  if (n_win > 0) {
+    if (!k_raw || !v_raw) return fail(HCSA_EINVAL, "k_raw and v_raw must be non-null");
+    if (!aligned16(k_raw) || !aligned16(v_raw)) return fail(HCSA_EALIGN, "k_raw and v_raw alignment");
+    if ((raw_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "raw_bstride alignment");
+    if (T_raw < 1) return fail(HCSA_EINVAL, "T_raw must be >= 1");
+    if (B > 1 && raw_bstride < T_raw * d) return fail(HCSA_EINVAL, "raw_bstride < T_raw*d");
+    const int64_t first = pos0 - n_win + 1 > 0 ? pos0 - n_win + 1 : 0;
+    const int64_t last = pos0 + Nq - 1;
+    if (first < raw_pos0 || last >= raw_pos0 + T_raw)
+      return fail(HCSA_EINVAL, "window positions [%lld, %lld] not inside the raw rows [%lld, %lld)",
+                  static_cast<long long>(first), static_cast<long long>(last),
+                  static_cast<long long>(raw_pos0), static_cast<long long>(raw_pos0 + T_raw));
+  }
+  const hcsa::AttnPlan plan =
+      hcsa::plan_attention(true, kv_dtype, B, Nq, H, d, attn_max_len_csa(k, n_win));
+  rc = check_ws(workspace, ws_bytes, plan.total_bytes);
+  if (rc) return rc;
+  hcsa::AttnArgs a{};
+  a.q = q; a.kc = kc; a.vc = vc; a.c_bstride = c_bstride; a.N = N > 0 ? N : 0; a.ratio = ratio;
+  a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
+  a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0;
+  a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
+  a.out = out; a.lse = lse;
+  return hip_status(hcsa::launch_attention(true, a, plan, workspace, static_cast<hipStream_t>(stream)),
+                    "hcsa_csa_sparse_attn");
+}
+
+size_t hcsa_hca_dense_attn_workspace_size(int B, int Nq, int H, int d, int N) {
+  if (B < 1 || Nq < 1 || H < 1 || d < 1 || N < 0) return 0;
+  const size_t a = hcsa::plan_attention(false, HCSA_BF16, B, Nq, H, d, N).total_bytes;
+  const size_t b = hcsa::plan_attention(false, HCSA_F32, B, Nq, H, d, N).total_bytes;
+  return a > b ? a : b;
+}
+
+int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h_bstride,
+                        int N, int ratio, int64_t pos0, int kv_dtype, int B, int Nq, int H,
+                        int d, float scale, float* out, float* lse, void* workspace,
+                        size_t ws_bytes, hcsa_stream stream) {
+  int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
+  if (rc) return rc;
+  if (N < 0) return fail(HCSA_EINVAL, "N must be >= 0");
+  if (N > 0) {
+    if (!kh || !vh) return fail(HCSA_EINVAL, "kh and vh must be non-null");
+    if (!aligned16(kh) || !aligned16(vh)) return fail(HCSA_EALIGN, "kh and vh must be 16-byte aligned");
+    if ((h_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "h_bstride alignment");
+    if (B > 1 && h_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "h_bstride < N*d");
+  }
+  const hcsa::AttnPlan plan = hcsa::plan_attention(false, kv_dtype, B, Nq, H, d, N);
+  rc = check_ws(workspace, ws_bytes, plan.total_bytes);
+  if (rc) return rc;
+  hcsa::AttnArgs a{};
+  a.q = q; a.kc = kh; a.vc = vh; a.c_bstride = h_bstride; a.N = N; a.ratio = ratio;
+  a.idx = nullptr; a.k = 0; a.k_raw = nullptr; a.v_raw = nullptr; a.raw_bstride = 0;
+  a.T_raw = 0; a.raw_pos0 = 0; a.n_win = 0; a.pos0 = pos0;
+  a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
+  a.out = out; a.lse = lse;
+  return hip_status(hcsa::launch_attention(false, a, plan, workspace, static_cast<hipStream_t>(stream)),
+                    "hcsa_hca_dense_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,486 @@
+// CSA sparse attention and HCA dense attention, split over the key list, with an
+// online-softmax log-sum-exp merge of the splits.
+//
+// CSA attends over the top-k compressed entries plus a sliding window of n_win = 128 raw
+// tokens; HCA attends densely over every compressed entry (Lighthouse, "deep deepseek v4
+// release", section 八 item 3).  One softmax runs over the concatenated key list (the
+// reading taken for how the window branch joins the sparse branch).  All query heads
+// share one KV head (MQA).
+//
+// Key list of a query token at position p:
+//   CSA: positions 0..k-1 are the selected entries (entries outside [0, n_c(p)) are
+//        skipped), positions k.. are the raw tokens max(0, p-n_win+1) .. p.
+//   HCA: positions 0..n_h(p)-1 are the entries themselves.
+// A block owns one contiguous range (split) of one query's key list and writes either
+// the final output (one split) or a normalized partial plus its log-sum-exp.
+//
+// Kernels:
+//   attn_mfma_kernel     bf16, 16 heads, head dim 128 (the MI355X fast path).  Each wave
+//                        takes 32 keys per step; S^T = K Q^T and O^T += V^T P^T run on
+//                        v_mfma_f32_16x16x32_bf16 with every lane owning one head, so the
+//                        softmax statistics never cross lanes except across the 4 k-groups.
+//                        K rows feed the A operand straight from 16-byte global loads; each
+//                        lane reads a 16-byte slice of 8 V rows and byte-permutes them into
+//                        the A operand of 8 channel tiles (channel 8*i + tile), so no LDS
+//                        transpose is needed.  The 4 waves of a block merge in LDS.
+//   attn_generic_kernel  any head count / head dim, fp32 or bf16, plain VALU (small and
+//                        fp32 shapes).
+//   lse_merge_kernel     o = sum_s e^{lse_s - L} o_s, L = log sum_s e^{lse_s}.
+#include "common.h"
+#include "internal.h"
+
+#include <algorithm>
+
+namespace hcsa {
+
+namespace {
+
+struct AttnDev {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  int64_t c_bstride;
+  int N, ratio;
+  const int32_t* idx;
+  int k;
+  const void* k_raw;
+  const void* v_raw;
+  int64_t raw_bstride, T_raw, raw_pos0;
+  int n_win;
+  int64_t pos0;
+  int Nq, H, d;
+  float scale;
+  int chunk, splits, rows;
+  float* out;      // final [rows][H][d] (splits == 1) or partial [splits][rows][H][d]
+  float* lse;      // final [rows][H] or partial [splits][rows][H]
+};
+
+// Key-list geometry of one query row.
+struct RowKeys {
+  int b;
+  int nv;          // visible compressed entries
+  int L;           // key list length
+  int64_t wstart;  // first window position (CSA)
+};
+
+template <bool CSA>
+__device__ __forceinline__ RowKeys row_keys(const AttnDev& A, int row) {
+  RowKeys r;
+  r.b = row / A.Nq;
+  const int64_t p = A.pos0 + (row % A.Nq);
+  const int64_t v = (p + 1) / A.ratio;
+  r.nv = static_cast<int>(v < A.N ? v : A.N);
+  if constexpr (CSA) {
+    r.wstart = p - A.n_win + 1 > 0 ? p - A.n_win + 1 : 0;
+    const int winlen = A.n_win > 0 ? static_cast<int>(p - r.wstart + 1) : 0;
+    r.L = A.k + winlen;
+  } else {
+    r.wstart = 0;
+    r.L = r.nv;
+  }
+  return r;
+}
+
+// Source of key-list position `pos`: >= 0 compressed row, -1 none, <= -2 raw row -(code+2).
+template <bool CSA>
+__device__ __forceinline__ int key_code(const AttnDev& A, const RowKeys& r, int row, int pos) {
+  if (pos >= r.L) return -1;
+  if constexpr (CSA) {
+    if (pos < A.k) {
+      const int e = A.idx[static_cast<int64_t>(row) * A.k + pos];
+      return (e >= 0 && e < r.nv) ? e : -1;
+    }
+    const int64_t t = r.wstart + (pos - A.k) - A.raw_pos0;
+    return -static_cast<int>(t) - 2;
+  } else {
+    return pos;
+  }
+}
+
+template <typename TE>
+__device__ __forceinline__ const TE* key_row(const AttnDev& A, int b, int code, bool value) {
+  if (code >= 0) {
+    const TE* base = static_cast<const TE*>(value ? A.vc : A.kc);
+    return base + b * A.c_bstride + static_cast<int64_t>(code) * A.d;
+  }
+  const TE* base = static_cast<const TE*>(value ? A.v_raw : A.k_raw);
+  return base + b * A.raw_bstride + static_cast<int64_t>(-code - 2) * A.d;
+}
+
+// ------------------------------------------------------------------ generic VALU path
+
+constexpr int kGenChunk = 64;
+
+template <bool BF16>
+__device__ __forceinline__ float ld(const void* p, int64_t i) {
+  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  else return static_cast<const float*>(p)[i];
+}
+
+// grid: (splits, rows); block 256; dynamic LDS: H*d + H*kGenChunk floats + kGenChunk ints.
+template <bool CSA, bool BF16>
+__global__ __launch_bounds__(256) void attn_generic_kernel(AttnDev A) {
+  extern __shared__ float smem[];
+  float* qf = smem;                              // [H][d]
+  float* pr = qf + A.H * A.d;                    // [H][kGenChunk] logits, then weights
+  int* code = reinterpret_cast<int*>(pr + A.H * kGenChunk);
+  __shared__ float s_m[64], s_sum[64];
+  typedef typename std::conditional<BF16, uint16_t, float>::type TE;
+
+  const int row = blockIdx.y;
+  const int split = blockIdx.x;
+  const RowKeys r = row_keys<CSA>(A, row);
+  const int k0 = split * A.chunk;
+  const int cnt = max(0, min(A.chunk, r.L - k0));
+  const int H = A.H, d = A.d;
+
+  for (int i = threadIdx.x; i < H * d; i += 256)
+    qf[i] = ld<BF16>(A.q, static_cast<int64_t>(row) * H * d + i);
+  for (int i = threadIdx.x; i < cnt; i += 256) code[i] = key_code<CSA>(A, r, row, k0 + i);
+  __syncthreads();
+
+  for (int t = threadIdx.x; t < H * cnt; t += 256) {
+    const int h = t / cnt, i = t - h * cnt;
+    float lg = -INFINITY;
+    if (code[i] != -1) {
+      const TE* kr = key_row<TE>(A, r.b, code[i], false);
+      float acc = 0.0f;
+      for (int c = 0; c < d; ++c) acc = fmaf(qf[h * d + c], ld<BF16>(kr, c), acc);
+      lg = acc * A.scale;
+    }
+    pr[h * kGenChunk + i] = lg;
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int h = wave; h < H; h += 4) {
+    const float lg = lane < cnt ? pr[h * kGenChunk + lane] : -INFINITY;
+    const float m = wave_max(lg);
+    const float e = (m == -INFINITY || lg == -INFINITY) ? 0.0f : expf(lg - m);
+    const float s = wave_sum(e);
+    if (lane < cnt) pr[h * kGenChunk + lane] = e;
+    if (lane == 0) {
+      s_m[h] = m;
+      s_sum[h] = s;
+    }
+  }
+  __syncthreads();
+
+  float* o = A.out + (static_cast<int64_t>(split) * A.rows + row) * H * d;
+  float* ls = A.lse + static_cast<int64_t>(split) * A.rows * H + static_cast<int64_t>(row) * H;
+  for (int t = threadIdx.x; t < H * d; t += 256) {
+    const int h = t / d, c = t - h * d;
+    const float s = s_sum[h];
+    float acc = 0.0f;
+    if (s > 0.0f) {
+      for (int i = 0; i < cnt; ++i) {
+        const float pw = pr[h * kGenChunk + i];
+        if (pw != 0.0f) acc = fmaf(pw, ld<BF16>(key_row<TE>(A, r.b, code[i], true), c), acc);
+      }
+      acc = acc / s;
+    }
+    o[t] = acc;
+    if (c == 0) ls[h] = s > 0.0f ? s_m[h] + logf(s) : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------ MFMA path (H=16, d=128)
+
+constexpr int kMfmaMaxChunk = 4096;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// grid: (splits, rows); block 256 (4 waves).
+template <bool CSA>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
+  __shared__ int s_code[kMfmaMaxChunk];
+  __shared__ float s_o[4][16][129];
+  __shared__ float s_ml[4][2][16];
+
+  const int row = blockIdx.y;
+  const int split = blockIdx.x;
+  const RowKeys r = row_keys<CSA>(A, row);
+  const int k0 = split * A.chunk;
+  const int cnt = max(0, min(A.chunk, r.L - k0));
+  for (int i = threadIdx.x; i < cnt; i += 256) s_code[i] = key_code<CSA>(A, r, row, k0 + i);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;   // head owned by this lane
+  const int g = lane >> 4;     // k-group
+
+  // B operand of S^T = K Q^T: Q[head col][32s + 8g .. +8] for s = 0..3.
+  u32x4 qB[4];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(A.q) + (static_cast<int64_t>(row) * 16 + col) * 128;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qB[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+  }
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0, 0, 0, 0};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  const float sl2 = A.scale * 1.4426950408889634f;  // logits in base 2
+
+  for (int base = wave * 32; base < cnt; base += 128) {
+    // ---- K rows for the A operand: keys base + col and base + 16 + col
+    u32x4 ka[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int pos = base + 16 * t + col;
+      const int c = pos < cnt ? s_code[pos] : -1;
+      if (c != -1) {
+        const uint16_t* kr = key_row<uint16_t>(A, r.b, c, false);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[t][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[t][s] = u32x4{0, 0, 0, 0};
+      }
+    }
+    // ---- V slices: keys base + 4g + j (j<4) and base + 16 + 4g + (j-4), channels 8col..8col+7
+    u32x4 vv[8];
+    bool ok[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int pos = base + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+      const int c = pos < cnt ? s_code[pos] : -1;
+      ok[j] = c != -1;
+      if (ok[j])
+        vv[j] = *reinterpret_cast<const u32x4*>(key_row<uint16_t>(A, r.b, c, true) + 8 * col);
+      else
+        vv[j] = u32x4{0, 0, 0, 0};
+    }
+    // ---- S^T tiles: lane holds logits of keys (tile t, 4g + i) for head col
+    f32x4 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) st[t] = mfma16x16x32(ka[t][s], qB[s], st[t]);
+    }
+    float lg[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lg[j] = ok[j] ? st[j >> 2][j & 3] * sl2 : -INFINITY;
+    float mt = lg[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, lg[j]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float m_new = fmaxf(m_run, mt);
+    if (m_new == -INFINITY) continue;      // nothing visible yet for this head
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float pj[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pj[j] = exp2f(lg[j] - m_new);
+      psum += pj[j];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    u32x4 pB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pB[m] = pack_bf16x2(pj[2 * m], pj[2 * m + 1]);
+    // ---- O^T tiles: channel 8*i + t for tile t, row i
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 va;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        va[m] = __builtin_amdgcn_perm(vv[2 * m + 1][t >> 1], vv[2 * m][t >> 1], sel);
+      acc[t] = mfma16x16x32(va, pB, acc[t]);
+    }
+  }
+
+  // per-head totals across the 4 k-groups
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  // lane holds O^T[channel 32g + 8i + t][head col] = acc[t][i]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s_o[wave][col][32 * g + 8 * i + t] = acc[t][i];
+  if (g == 0) {
+    s_ml[wave][0][col] = m_run;
+    s_ml[wave][1][col] = l_run;
+  }
+  __syncthreads();
+
+  float* o = A.out + (static_cast<int64_t>(split) * A.rows + row) * 2048;
+  float* ls = A.lse + static_cast<int64_t>(split) * A.rows * 16 + static_cast<int64_t>(row) * 16;
+  for (int t = threadIdx.x; t < 2048; t += 256) {
+    const int h = t >> 7, c = t & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = s_ml[w][0][h];
+        if (mw != -INFINITY) {
+          const float f = exp2f(mw - M);
+          num = fmaf(f, s_o[w][h][c], num);
+          den = fmaf(f, s_ml[w][1][h], den);
+        }
+      }
+    }
+    o[t] = den > 0.0f ? num / den : 0.0f;
+    if (c == 0) ls[h] = den > 0.0f ? (M + log2f(den)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------ merge
+
+// grid: (H, rows); block = d threads (<= 256).  The split weights of the (row, head) are
+// formed once in LDS, then each thread sums one channel over the splits with independent
+// coalesced loads.
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_l,
+                                                        int splits, int rows, int H, int d,
+                                                        float* __restrict__ out,
+                                                        float* __restrict__ lse) {
+  __shared__ float s_w[1024];
+  __shared__ float s_red[2];
+  const int h = blockIdx.x, row = blockIdx.y;
+  const int64_t lstride = static_cast<int64_t>(rows) * H;
+  const float* pl = part_l + static_cast<int64_t>(row) * H + h;
+  if (threadIdx.x < kWave) {
+    float M = -INFINITY;
+    for (int s = threadIdx.x; s < splits; s += kWave) M = fmaxf(M, pl[s * lstride]);
+    M = wave_max(M);
+    float den = 0.0f;
+    for (int s = threadIdx.x; s < splits; s += kWave) {
+      const float l = pl[s * lstride];
+      const float w = (M == -INFINITY || l == -INFINITY) ? 0.0f : expf(l - M);
+      if (s < 1024) s_w[s] = w;
+      den += w;
+    }
+    den = wave_sum(den);
+    if (threadIdx.x == 0) {
+      s_red[0] = M;
+      s_red[1] = den;
+    }
+  }
+  __syncthreads();
+  const float M = s_red[0], den = s_red[1];
+  const int c = threadIdx.x;
+  if (c < d) {
+    const int64_t ostride = static_cast<int64_t>(rows) * H * d;
+    const float* po = part_o + (static_cast<int64_t>(row) * H + h) * d + c;
+    float num = 0.0f;
+    for (int s = 0; s < splits; ++s) {
+      float w;
+      if (s < 1024) {
+        w = s_w[s];
+      } else {
+        const float l = pl[s * lstride];
+        w = (M == -INFINITY || l == -INFINITY) ? 0.0f : expf(l - M);
+      }
+      if (w != 0.0f) num = fmaf(w, po[s * ostride], num);
+    }
+    out[(static_cast<int64_t>(row) * H + h) * d + c] = den > 0.0f ? num / den : 0.0f;
+    if (c == 0) lse[static_cast<int64_t>(row) * H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
+  }
+}
+
+}  // namespace
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len) {
+  (void)csa;
+  AttnPlan p{};
+  p.rows = B * Nq;
+  p.max_len = max_len;
+  p.mfma = kv_dtype == 1 && H == 16 && d == 128;
+  if (p.mfma) {
+    // about two blocks per CU over the whole call, 128-key granules, at most kMfmaMaxChunk
+    const int64_t total = static_cast<int64_t>(p.rows) * std::max(max_len, 1);
+    int64_t c = (total + 511) / 512;
+    c = (c + 127) / 128 * 128;
+    c = std::max<int64_t>(c, 128);
+    c = std::min<int64_t>(c, kMfmaMaxChunk);
+    p.chunk = static_cast<int>(c);
+  } else {
+    p.chunk = kGenChunk;
+  }
+  p.splits = std::max(1, (max_len + p.chunk - 1) / p.chunk);
+  if (p.splits > 1) {
+    const size_t o = align256(static_cast<size_t>(p.splits) * p.rows * H * d * 4);
+    const size_t l = align256(static_cast<size_t>(p.splits) * p.rows * H * 4);
+    p.part_bytes = o + l;
+  }
+  p.total_bytes = p.part_bytes;
+  return p;
+}
+
+hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
+                            hipStream_t s) {
+  AttnDev A;
+  A.q = a.q;
+  A.kc = a.kc;
+  A.vc = a.vc;
+  A.c_bstride = a.c_bstride;
+  A.N = a.N;
+  A.ratio = a.ratio;
+  A.idx = a.idx;
+  A.k = a.k;
+  A.k_raw = a.k_raw;
+  A.v_raw = a.v_raw;
+  A.raw_bstride = a.raw_bstride;
+  A.T_raw = a.T_raw;
+  A.raw_pos0 = a.raw_pos0;
+  A.n_win = a.n_win;
+  A.pos0 = a.pos0;
+  A.Nq = a.Nq;
+  A.H = a.H;
+  A.d = a.d;
+  A.scale = a.scale;
+  A.chunk = plan.chunk;
+  A.splits = plan.splits;
+  A.rows = plan.rows;
+  float* part_o = nullptr;
+  float* part_l = nullptr;
+  if (plan.splits > 1) {
+    part_o = static_cast<float*>(ws);
+    part_l = reinterpret_cast<float*>(
+        static_cast<char*>(ws) +
+        align256(static_cast<size_t>(plan.splits) * plan.rows * a.H * a.d * 4));
+    A.out = part_o;
+    A.lse = part_l;
+  } else {
+    A.out = a.out;
+    A.lse = a.lse;
+  }
+  dim3 grid(plan.splits, plan.rows);
+  if (plan.mfma) {
+    if (csa) attn_mfma_kernel<true><<<grid, 256, 0, s>>>(A);
+    else attn_mfma_kernel<false><<<grid, 256, 0, s>>>(A);
+  } else {
+    const size_t lds = (static_cast<size_t>(a.H) * a.d + static_cast<size_t>(a.H) * kGenChunk +
+                        kGenChunk) * 4;
+    const bool bf = a.kv_dtype == 1;
+    if (csa && bf) attn_generic_kernel<true, true><<<grid, 256, lds, s>>>(A);
+    else if (csa) attn_generic_kernel<true, false><<<grid, 256, lds, s>>>(A);
+    else if (bf) attn_generic_kernel<false, true><<<grid, 256, lds, s>>>(A);
+    else attn_generic_kernel<false, false><<<grid, 256, lds, s>>>(A);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  lse_merge_kernel<<<dim3(a.H, plan.rows), a.d, 0, s>>>(part_o, part_l, plan.splits,
+                                                          plan.rows, a.H, a.d, a.out, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace hcsa

@@ -1,0 +1,110 @@
+// Device helpers shared by the libhcsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hcsa {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (b >> 16) | 0x40u;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- order-preserving keys
+// Larger score <=> larger unsigned key; -0 and +0 map to the same key.
+
+__device__ __forceinline__ uint32_t f32_key(uint32_t b) {
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t bf16_key(uint32_t h) {
+  if (h == 0x8000u) h = 0u;
+  return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ unsigned lane_id() { return __lane_id(); }
+
+// Number of set bits of a 64-bit wave ballot below this lane.
+__device__ __forceinline__ int ballot_rank(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+// ---------------------------------------------------------------- MXFP4 (OCP MX e2m1/e8m0)
+
+// floor(log2 |a|) for a finite non-zero float (subnormals included).
+__device__ __forceinline__ int ilog2_floor(float a) {
+  return __builtin_amdgcn_frexp_expf(a) - 1;
+}
+
+// Shared scale exponent of a block whose largest magnitude is amax.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e = ilog2_floor(amax) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// e2m1 code (sign in bit 3) of v / 2^e, nearest-even on {0,.5,1,1.5,2,3,4,6}, saturating.
+// Each comparison is a decision boundary of the grid; ">=" where the tie goes up (to an
+// even code), ">" where it stays down.
+__device__ __forceinline__ uint32_t e2m1_code(float v, int e) {
+  float t = __builtin_fabsf(__builtin_ldexpf(v, -e));
+  uint32_t m = (t > 0.25f) + (t >= 0.75f) + (t > 1.25f) + (t >= 1.75f) + (t > 2.5f) +
+               (t >= 3.5f) + (t > 5.0f);
+  return m | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Value of an e2m1 code times 2 (an integer in [-12, 12]).
+__device__ __forceinline__ int e2m1_twice(uint32_t c) {
+  int m = c & 7u;
+  int v = m < 4 ? m : (m == 4 ? 4 : (m == 5 ? 6 : (m == 6 ? 8 : 12)));
+  return (c & 8u) ? -v : v;
+}
+
+__device__ __forceinline__ float exp2_int(int e) { return __builtin_ldexpf(1.0f, e); }
+
+}  // namespace hcsa

@@ -1,0 +1,242 @@
+// Block pooling of K / V / indexer-key streams and the MXFP4 quantizer.
+//
+// CSA pools every m = 4 tokens into one entry and HCA every m' = 128 tokens
+// (Lighthouse, "deep deepseek v4 release", section 八 item 3; tulong.co Q&A, 技术架构创新
+// item 1).  The pooling weights are a softmax over per-position logits omega, shared by
+// every block and channel; the pages do not fix the weighting, this is the reading taken.
+//
+// HBM-streaming kernel: one thread owns 8 consecutive channels of one output entry and
+// walks the r input rows of its block with 16-byte loads (a wave covers whole rows, so
+// every load instruction is contiguous), accumulating in fp32 and rounding once.
+#include "common.h"
+#include "internal.h"
+#include "../../include/hcsa.h"
+
+namespace hcsa {
+
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_MXFP4 = 2 };
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+  if constexpr (IN_BF16) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[2 * c] = bf16_lo(w[c]);
+      v[2 * c + 1] = bf16_hi(w[c]);
+    }
+  } else {
+    f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+    f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = a[c];
+      v[4 + c] = b[c];
+    }
+  }
+}
+
+// Writes 8 values of one row: F32, BF16, or MXFP4 (4 code bytes; the lane holding the
+// first 8 channels of each 32-channel block also writes the block's scale byte).
+template <int OUT>
+__device__ __forceinline__ void store8(const float (&acc)[8], void* y, int64_t y_row_elems,
+                                       uint8_t* ys, int64_t ys_row, int c8) {
+  if constexpr (OUT == OUT_F32) {
+    f32x4* d = reinterpret_cast<f32x4*>(static_cast<float*>(y) + y_row_elems + c8 * 8);
+    d[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    d[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else if constexpr (OUT == OUT_BF16) {
+    u32x4 w;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = pack_bf16x2(acc[2 * c], acc[2 * c + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + y_row_elems + c8 * 8) = w;
+  } else {
+    // y_row_elems is the byte offset of the packed row here.
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) amax = fmaxf(amax, __builtin_fabsf(acc[c]));
+    // the 4 lanes of a 32-channel block are consecutive and quad-aligned
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const int e = mx_scale_exp(amax);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) packed |= e2m1_code(acc[c], e) << (4 * c);
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(y) + y_row_elems + c8 * 4) = packed;
+    if ((c8 & 3) == 0) ys[ys_row + (c8 >> 2)] = static_cast<uint8_t>(e + 127);
+  }
+}
+
+// Softmax of the pooling logits into LDS (weight 1 when omega is null and r == 1).
+__device__ __forceinline__ void pool_weights(const float* __restrict__ omega, int r,
+                                             float* alpha) {
+  if (threadIdx.x < kWave) {
+    if (omega == nullptr) {
+      if (threadIdx.x == 0) alpha[0] = 1.0f;
+    } else {
+      float m = -INFINITY;
+      for (int i = threadIdx.x; i < r; i += kWave) m = fmaxf(m, omega[i]);
+      m = wave_max(m);
+      float s = 0.0f;
+      for (int i = threadIdx.x; i < r; i += kWave) {
+        const float e = expf(omega[i] - m);
+        alpha[i] = e;
+        s += e;
+      }
+      s = wave_sum(s);
+      for (int i = threadIdx.x; i < r; i += kWave) alpha[i] = alpha[i] / s;
+    }
+  }
+  __syncthreads();
+}
+
+// One block of the pooling: this thread's 8 channels of entry `j` (block-local row `local`).
+template <bool IN_BF16, int OUT>
+__device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_bs, int D,
+                                          const float* alpha, int r, void* __restrict__ y,
+                                          int64_t y_bs, uint8_t* __restrict__ ys, int64_t ys_bs,
+                                          int n_out, int64_t jblock, int b) {
+  const int tpr = D >> 3;                       // threads per output row
+  const int rows_per_block = blockDim.x / tpr;
+  const int local = threadIdx.x / tpr;
+  const int c8 = threadIdx.x - local * tpr;
+  if (local >= rows_per_block) return;
+  const int64_t j = jblock * rows_per_block + local;
+  if (j >= n_out) return;
+  constexpr int ES = IN_BF16 ? 2 : 4;
+  const char* src = static_cast<const char*>(x) + (b * x_bs + j * r * D + c8 * 8) * ES;
+  const int64_t row_bytes = static_cast<int64_t>(D) * ES;
+
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 4
+  for (int i = 0; i < r; ++i) {
+    float v[8];
+    load8<IN_BF16>(src + i * row_bytes, v);
+    const float a = alpha[i];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = fmaf(a, v[c], acc[c]);
+  }
+
+  if constexpr (OUT == OUT_MXFP4) {
+    store8<OUT>(acc, y, b * y_bs + j * (D >> 1), ys, b * ys_bs + j * (D >> 5), c8);
+  } else {
+    store8<OUT>(acc, y, b * y_bs + j * D, nullptr, 0, c8);
+  }
+}
+
+// grid: (ceil(n_out / rows_per_block), B); block 256.
+template <bool IN_BF16, int OUT>
+__global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ x,
+                                                       int64_t x_bs, int D,
+                                                       const float* __restrict__ omega, int r,
+                                                       void* __restrict__ y, int64_t y_bs,
+                                                       uint8_t* __restrict__ ys, int64_t ys_bs,
+                                                       int n_out) {
+  __shared__ float alpha[1024];
+  pool_weights(omega, r, alpha);
+  pool_rows<IN_BF16, OUT>(x, x_bs, D, alpha, r, y, y_bs, ys, ys_bs, n_out, blockIdx.x,
+                          blockIdx.y);
+}
+
+// Several pooling jobs in one launch (the blocks completed by a decode token in every
+// stream): grid.x is the concatenation of the jobs' block ranges.
+struct PoolJobs {
+  hcsa_pool_job job[HCSA_MAX_POOL_JOBS];
+  int first_block[HCSA_MAX_POOL_JOBS + 1];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
+  __shared__ float alpha[1024];
+  int t = 0;
+  while (t + 1 < J.n && static_cast<int>(blockIdx.x) >= J.first_block[t + 1]) ++t;
+  const hcsa_pool_job& q = J.job[t];
+  pool_weights(q.omega, q.ratio, alpha);
+  const int64_t jb = blockIdx.x - J.first_block[t];
+  const int n_out = q.T / q.ratio;
+  const bool ib = q.x_dtype == 1;
+  if (ib && q.y_dtype == 1)
+    pool_rows<true, OUT_BF16>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+  else if (ib && q.y_dtype == 2)
+    pool_rows<true, OUT_MXFP4>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+  else if (ib)
+    pool_rows<true, OUT_F32>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+  else if (q.y_dtype == 1)
+    pool_rows<false, OUT_BF16>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+  else if (q.y_dtype == 2)
+    pool_rows<false, OUT_MXFP4>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+  else
+    pool_rows<false, OUT_F32>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+}
+
+hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B, hipStream_t s) {
+  PoolJobs J{};
+  J.n = 0;
+  int blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const int n_out = jobs[i].T / jobs[i].ratio;
+    if (n_out == 0) continue;
+    const int rpb = 256 / (jobs[i].D / 8);
+    J.job[J.n] = jobs[i];
+    J.first_block[J.n] = blocks;
+    blocks += (n_out + rpb - 1) / rpb;
+    ++J.n;
+  }
+  J.first_block[J.n] = blocks;
+  if (blocks == 0) return hipSuccess;
+  compress_batched_kernel<<<dim3(blocks, B), 256, 0, s>>>(J);
+  return hipGetLastError();
+}
+
+template <bool IN_BF16>
+static hipError_t launch_compress_t(const void* x, int64_t x_bs, int B, int T, int D,
+                                    const float* omega, int r, void* y, int y_dtype,
+                                    int64_t y_bs, uint8_t* ys, int64_t ys_bs, hipStream_t s) {
+  const int n_out = T / r;
+  if (n_out == 0) return hipSuccess;
+  const int tpr = D / 8;
+  const int rpb = 256 / tpr;
+  dim3 grid((n_out + rpb - 1) / rpb, B);
+  if (y_dtype == 0)
+    compress_kernel<IN_BF16, OUT_F32><<<grid, 256, 0, s>>>(x, x_bs, D, omega, r, y, y_bs, ys,
+                                                           ys_bs, n_out);
+  else if (y_dtype == 1)
+    compress_kernel<IN_BF16, OUT_BF16><<<grid, 256, 0, s>>>(x, x_bs, D, omega, r, y, y_bs, ys,
+                                                            ys_bs, n_out);
+  else
+    compress_kernel<IN_BF16, OUT_MXFP4><<<grid, 256, 0, s>>>(x, x_bs, D, omega, r, y, y_bs, ys,
+                                                             ys_bs, n_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                           const float* omega, int ratio, void* y, int y_dtype,
+                           int64_t y_bstride, uint8_t* ys, int64_t ys_bstride,
+                           hipStream_t s) {
+  if (x_dtype == 1)
+    return launch_compress_t<true>(x, x_bstride, B, T, D, omega, ratio, y, y_dtype, y_bstride,
+                                   ys, ys_bstride, s);
+  return launch_compress_t<false>(x, x_bstride, B, T, D, omega, ratio, y, y_dtype, y_bstride,
+                                  ys, ys_bstride, s);
+}
+
+// MXFP4 quantization of [rows][D]: the pooling kernel with a single-row block and
+// weight 1 (exact), so both share one quantizer.
+hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int D,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int tpr = D / 8;
+  const int rpb = 256 / tpr;
+  const int64_t nb = (rows + rpb - 1) / rpb;
+  if (nb > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(nb), 1);
+  if (x_dtype == 1)
+    compress_kernel<true, OUT_MXFP4><<<grid, 256, 0, s>>>(x, 0, D, nullptr, 1, packed, 0,
+                                                          scales, 0, static_cast<int>(rows));
+  else
+    compress_kernel<false, OUT_MXFP4><<<grid, 256, 0, s>>>(x, 0, D, nullptr, 1, packed, 0,
+                                                           scales, 0, static_cast<int>(rows));
+  return hipGetLastError();
+}
+
+}  // namespace hcsa

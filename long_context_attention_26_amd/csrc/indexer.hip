@@ -1,0 +1,391 @@
+// Lightning-indexer scores of the compressed indexer keys.
+//
+// The indexer scores compressed entries with its own compressed keys (Lighthouse, "deep
+// deepseek v4 release", section 八 items 3 and 7) on a low-precision QK path whose scores
+// are fp32, optionally stored as bf16 (9fzt.com digest, item 4).  The score form
+// s_j = sum_g w_g * max(0, q_g . k_j) is the reading taken (the pages print no formula).
+//
+// Decode kernel (one or few query tokens per sequence): HBM-bound key scan.  A group of
+// LPE lanes reads one key row with 16-byte loads (a wave covers 64/LPE contiguous rows per
+// instruction), each lane forms H_I partial dot products with packed bf16 dot2 (or fp32
+// fma), the group reduces them with cross-lane adds, and the group's first lane applies
+// ReLU, the head weights (fixed order g = 0..H_I-1) and writes the score.
+#include "common.h"
+#include "internal.h"
+
+namespace hcsa {
+
+namespace {
+
+struct IdxDev {
+  const void* q;     // [rows][H_I][d_I]
+  const float* w;    // [rows][H_I]
+  const void* k;     // [B][N][d_I] (bstride elements)
+  int64_t k_bstride;
+  int Nq, N, ratio, d_I;
+  int64_t pos0;
+  void* scores;      // [rows][N]
+  int chunk;
+};
+
+// Keys per block: enough blocks to cover every CU several times even for one sequence,
+// and at least 256 keys so a block issues a few loads per lane.
+static int index_chunk(int rows, int N) {
+  int64_t c = static_cast<int64_t>(N) * rows / 2048;
+  c = (c + 255) / 256 * 256;
+  return static_cast<int>(c < 256 ? 256 : (c > 4096 ? 4096 : c));
+}
+
+__device__ __forceinline__ float dot16b_bf16(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // copy the element out first: a bit_cast of a vector subscript is miscompiled
+    // (every iteration read element 0)
+    const uint32_t x = a[c], y = b[c];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                          __builtin_bit_cast(bf16x2, y), acc, false);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float dot16b_f32(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc = fmaf(__uint_as_float(a[c]), __uint_as_float(b[c]), acc);
+  return acc;
+}
+
+// grid: (ceil(N / kChunk), rows); block 256.
+template <int HI, int LPE, bool KBF16, bool SBF16>
+__global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
+  constexpr int ES = KBF16 ? 2 : 4;
+  constexpr int GROUPS = 256 / LPE;
+  constexpr int U = 4;
+  const int row = blockIdx.y;
+  const int b = row / A.Nq;
+  const int64_t p = A.pos0 + (row % A.Nq);
+  const int64_t nv64 = (p + 1) / A.ratio;
+  const int nv = static_cast<int>(nv64 < A.N ? nv64 : A.N);
+  const int start = blockIdx.x * A.chunk;
+  const int end = min(start + A.chunk, nv);
+  if (start >= end) return;
+
+  const int sub = threadIdx.x % LPE;
+  const int grp = threadIdx.x / LPE;
+  const int row_bytes = A.d_I * ES;
+
+  u32x4 qv[HI];
+  float w[HI];
+  const char* qrow = static_cast<const char*>(A.q) + static_cast<int64_t>(row) * HI * row_bytes;
+#pragma unroll
+  for (int g = 0; g < HI; ++g) {
+    qv[g] = *reinterpret_cast<const u32x4*>(qrow + g * row_bytes + sub * 16);
+    w[g] = A.w[static_cast<int64_t>(row) * HI + g];
+  }
+  const char* kbase = static_cast<const char*>(A.k) + b * A.k_bstride * ES + sub * 16;
+  float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
+  uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
+
+  for (int j0 = start + grp; j0 < end; j0 += GROUPS * U) {
+    u32x4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * GROUPS;
+      if (j < end)
+        kv[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * row_bytes));
+      else
+        kv[u] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float part[HI];
+#pragma unroll
+      for (int g = 0; g < HI; ++g)
+        part[g] = KBF16 ? dot16b_bf16(qv[g], kv[u], 0.0f) : dot16b_f32(qv[g], kv[u], 0.0f);
+#pragma unroll
+      for (int o = 1; o < LPE; o <<= 1)
+#pragma unroll
+        for (int g = 0; g < HI; ++g) part[g] += __shfl_xor(part[g], o, kWave);
+      const int j = j0 + u * GROUPS;
+      if (sub == 0 && j < end) {
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < HI; ++g) s = fmaf(w[g], fmaxf(part[g], 0.0f), s);
+        s += 0.0f;  // -0 -> +0
+        if constexpr (SBF16)
+          s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+        else
+          s32[j] = s;
+      }
+    }
+  }
+}
+
+template <int HI, int LPE, bool KBF16>
+hipError_t launch_hi(const IdxDev& A, int rows, int score_dtype, hipStream_t s) {
+  const int nchunks = (A.N + A.chunk - 1) / A.chunk;
+  dim3 grid(nchunks, rows);
+  if (score_dtype == 1)
+    index_scores_kernel<HI, LPE, KBF16, true><<<grid, 256, 0, s>>>(A);
+  else
+    index_scores_kernel<HI, LPE, KBF16, false><<<grid, 256, 0, s>>>(A);
+  return hipGetLastError();
+}
+
+template <int LPE, bool KBF16>
+hipError_t launch_lpe(const IdxDev& A, int rows, int H_I, int score_dtype, hipStream_t s) {
+  switch (H_I) {
+    case 1: return launch_hi<1, LPE, KBF16>(A, rows, score_dtype, s);
+    case 2: return launch_hi<2, LPE, KBF16>(A, rows, score_dtype, s);
+    case 4: return launch_hi<4, LPE, KBF16>(A, rows, score_dtype, s);
+    case 8: return launch_hi<8, LPE, KBF16>(A, rows, score_dtype, s);
+    case 16: return launch_hi<16, LPE, KBF16>(A, rows, score_dtype, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------ MXFP4 keys
+// Indexer keys stored as MXFP4 (e2m1 codes, one e8m0 scale per 32 channels); the query
+// vectors are quantized the same way at block start.  One lane owns one 32-channel block
+// of one key (16 code bytes + 1 scale byte), so a wave reads 64 contiguous blocks per
+// instruction.  Codes become exact small integers (twice the e2m1 value, in [-12, 12])
+// through a byte-permute table, and sdot4 accumulates exact integer block sums; each
+// block sum times 2^(e_q + e_k - 2) is exact in fp32.
+
+// 4 codes (one per byte, sign in bit 3) -> 4 int8 holding twice the e2m1 value.
+__device__ __forceinline__ uint32_t e2m1x4_to_i8x4(uint32_t c) {
+  const uint32_t m = c & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, m);  // 0,1,2,3,4,6,8,12
+  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, m);  // negated
+  const uint32_t mask = ((c >> 3) & 0x01010101u) * 0xFFu;
+  return (neg & mask) | (pos & ~mask);
+}
+
+struct IdxMxDev {
+  const void* q;       // [rows][H_I][d_I] bf16 or f32
+  const float* w;      // [rows][H_I]
+  const uint8_t* k;    // [B][N][d_I/2] packed codes (bstride bytes)
+  const uint8_t* ks;   // [B][N][d_I/32] scale bytes (bstride bytes)
+  int64_t k_bstride, ks_bstride;
+  int Nq, N, ratio, d_I;
+  int64_t pos0;
+  void* scores;
+  int chunk;
+};
+
+// grid: (ceil(N / kChunk), rows); block 256.  LPE = d_I / 32 lanes per key.
+template <int HI, int LPE, bool QBF16, bool SBF16>
+__global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
+  constexpr int GROUPS = 256 / LPE;
+  constexpr int U = 4;
+  const int row = blockIdx.y;
+  const int b = row / A.Nq;
+  const int64_t p = A.pos0 + (row % A.Nq);
+  const int64_t nv64 = (p + 1) / A.ratio;
+  const int nv = static_cast<int>(nv64 < A.N ? nv64 : A.N);
+  const int start = blockIdx.x * A.chunk;
+  const int end = min(start + A.chunk, nv);
+  if (start >= end) return;
+  const int sub = threadIdx.x % LPE;
+  const int grp = threadIdx.x / LPE;
+
+  // Quantize every 32-channel block of every query head once per block (LDS), then each
+  // lane keeps the blocks it needs: words 0..3 hold elements 8c, 8c+2, 8c+4, 8c+6 and
+  // words 4..7 elements 8c+1, 8c+3, 8c+5, 8c+7 (c = word index mod 4), as int8 = 2*value.
+  __shared__ uint32_t s_q[16][4][8];
+  __shared__ int s_qe[16][4];
+  if (threadIdx.x < HI * LPE) {
+    const int g = threadIdx.x / LPE, blk = threadIdx.x % LPE;
+    const int64_t off = (static_cast<int64_t>(row) * HI + g) * A.d_I + blk * 32;
+    float amax = 0.0f;
+    for (int e = 0; e < 32; ++e) {
+      const float v = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[off + e])
+                            : static_cast<const float*>(A.q)[off + e];
+      amax = fmaxf(amax, __builtin_fabsf(v));
+    }
+    const int se = mx_scale_exp(amax);
+    s_qe[g][blk] = se;
+    for (int c = 0; c < 4; ++c) {
+      uint32_t lo = 0, hi = 0;
+      for (int t = 0; t < 4; ++t) {
+        const int64_t i0 = off + 8 * c + 2 * t;
+        const float v0 = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[i0])
+                               : static_cast<const float*>(A.q)[i0];
+        const float v1 = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[i0 + 1])
+                               : static_cast<const float*>(A.q)[i0 + 1];
+        lo |= (static_cast<uint32_t>(e2m1_twice(e2m1_code(v0, se))) & 0xFFu) << (8 * t);
+        hi |= (static_cast<uint32_t>(e2m1_twice(e2m1_code(v1, se))) & 0xFFu) << (8 * t);
+      }
+      s_q[g][blk][c] = lo;
+      s_q[g][blk][4 + c] = hi;
+    }
+  }
+  __syncthreads();
+  uint32_t qlo[HI][4], qhi[HI][4];
+  int qe[HI];
+  float w[HI];
+#pragma unroll
+  for (int g = 0; g < HI; ++g) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qlo[g][c] = s_q[g][sub][c];
+      qhi[g][c] = s_q[g][sub][4 + c];
+    }
+    qe[g] = s_qe[g][sub];
+    w[g] = A.w[static_cast<int64_t>(row) * HI + g];
+  }
+
+  const uint8_t* kbase = A.k + b * A.k_bstride + sub * 16;
+  const uint8_t* sbase = A.ks + b * A.ks_bstride + sub;
+  const int rowb = A.d_I / 2;
+  const int rows_s = A.d_I / 32;
+  float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
+  uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
+
+  for (int j0 = start + grp; j0 < end; j0 += GROUPS * U) {
+    u32x4 kv[U];
+    int ke[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * GROUPS;
+      if (j < end) {
+        kv[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * rowb));
+        ke[u] = static_cast<int>(sbase[static_cast<int64_t>(j) * rows_s]) - 127;
+      } else {
+        kv[u] = u32x4{0, 0, 0, 0};
+        ke[u] = 0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t klo[4], khi[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        klo[c] = e2m1x4_to_i8x4(kv[u][c] & 0x0F0F0F0Fu);
+        khi[c] = e2m1x4_to_i8x4((kv[u][c] >> 4) & 0x0F0F0F0Fu);
+      }
+      float part[HI];
+#pragma unroll
+      for (int g = 0; g < HI; ++g) {
+        int acc = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc = __builtin_amdgcn_sdot4(static_cast<int>(qlo[g][c]), static_cast<int>(klo[c]), acc, false);
+          acc = __builtin_amdgcn_sdot4(static_cast<int>(qhi[g][c]), static_cast<int>(khi[c]), acc, false);
+        }
+        part[g] = __builtin_ldexpf(static_cast<float>(acc), qe[g] + ke[u] - 2);
+      }
+#pragma unroll
+      for (int o = 1; o < LPE; o <<= 1)
+#pragma unroll
+        for (int g = 0; g < HI; ++g) part[g] += __shfl_xor(part[g], o, kWave);
+      const int j = j0 + u * GROUPS;
+      if (sub == 0 && j < end) {
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < HI; ++g) s = fmaf(w[g], fmaxf(part[g], 0.0f), s);
+        s += 0.0f;
+        if constexpr (SBF16)
+          s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+        else
+          s32[j] = s;
+      }
+    }
+  }
+}
+
+template <int HI, int LPE, bool QBF16>
+hipError_t launch_mx_hi(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
+  const int nchunks = (A.N + A.chunk - 1) / A.chunk;
+  dim3 grid(nchunks, rows);
+  if (score_dtype == 1)
+    index_scores_mx_kernel<HI, LPE, QBF16, true><<<grid, 256, 0, s>>>(A);
+  else
+    index_scores_mx_kernel<HI, LPE, QBF16, false><<<grid, 256, 0, s>>>(A);
+  return hipGetLastError();
+}
+
+template <int LPE, bool QBF16>
+hipError_t launch_mx_lpe(const IdxMxDev& A, int rows, int H_I, int score_dtype, hipStream_t s) {
+  switch (H_I) {
+    case 1: return launch_mx_hi<1, LPE, QBF16>(A, rows, score_dtype, s);
+    case 2: return launch_mx_hi<2, LPE, QBF16>(A, rows, score_dtype, s);
+    case 4: return launch_mx_hi<4, LPE, QBF16>(A, rows, score_dtype, s);
+    case 8: return launch_mx_hi<8, LPE, QBF16>(A, rows, score_dtype, s);
+    case 16: return launch_mx_hi<16, LPE, QBF16>(A, rows, score_dtype, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool QBF16>
+hipError_t launch_mx_q(const IdxMxDev& A, int rows, int H_I, int score_dtype, hipStream_t s) {
+  switch (A.d_I / 32) {
+    case 1: return launch_mx_lpe<1, QBF16>(A, rows, H_I, score_dtype, s);
+    case 2: return launch_mx_lpe<2, QBF16>(A, rows, H_I, score_dtype, s);
+    case 4: return launch_mx_lpe<4, QBF16>(A, rows, H_I, score_dtype, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
+                                     const uint8_t* kx, int64_t k_bstride, const uint8_t* ks,
+                                     int64_t ks_bstride, int B, int Nq, int H_I, int d_I,
+                                     int N, int ratio, int64_t pos0, int score_dtype,
+                                     void* scores, hipStream_t s) {
+  IdxMxDev A;
+  A.q = q;
+  A.w = w;
+  A.k = kx;
+  A.ks = ks;
+  A.k_bstride = k_bstride;
+  A.ks_bstride = ks_bstride;
+  A.Nq = Nq;
+  A.N = N;
+  A.ratio = ratio;
+  A.d_I = d_I;
+  A.pos0 = pos0;
+  A.scores = scores;
+  A.chunk = index_chunk(B * Nq, N);
+  if (q_dtype == 1) return launch_mx_q<true>(A, B * Nq, H_I, score_dtype, s);
+  return launch_mx_q<false>(A, B * Nq, H_I, score_dtype, s);
+}
+
+
+hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const void* kx,
+                               int k_dtype, int64_t k_bstride, const uint8_t* ks,
+                               int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
+                               int ratio, int64_t pos0, int score_dtype, void* scores,
+                               hipStream_t s) {
+  if (k_dtype == 2)
+    return launch_mxfp4_index_scores(q, q_dtype, w, static_cast<const uint8_t*>(kx), k_bstride,
+                                     ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0,
+                                     score_dtype, scores, s);
+  IdxDev A;
+  A.q = q;
+  A.w = w;
+  A.k = kx;
+  A.k_bstride = k_bstride;
+  A.Nq = Nq;
+  A.N = N;
+  A.ratio = ratio;
+  A.d_I = d_I;
+  A.pos0 = pos0;
+  A.scores = scores;
+  A.chunk = index_chunk(B * Nq, N);
+  const int rows = B * Nq;
+  const int lpe = d_I * (k_dtype == 1 ? 2 : 4) / 16;
+  if (k_dtype == 1) {
+    if (lpe == 4) return launch_lpe<4, true>(A, rows, H_I, score_dtype, s);
+    if (lpe == 8) return launch_lpe<8, true>(A, rows, H_I, score_dtype, s);
+    if (lpe == 16) return launch_lpe<16, true>(A, rows, H_I, score_dtype, s);
+  } else {
+    if (lpe == 8) return launch_lpe<8, false>(A, rows, H_I, score_dtype, s);
+    if (lpe == 16) return launch_lpe<16, false>(A, rows, H_I, score_dtype, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hcsa

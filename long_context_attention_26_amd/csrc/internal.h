@@ -1,0 +1,69 @@
+// Host-side launchers shared between the ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hcsa.h"
+
+namespace hcsa {
+
+// ---- compress.hip
+hipError_t launch_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                           const float* omega, int ratio, void* y, int y_dtype,
+                           int64_t y_bstride, uint8_t* ys, int64_t ys_bstride,
+                           hipStream_t s);
+hipError_t launch_compress_batched(const struct hcsa_pool_job* jobs, int n, int B,
+                                   hipStream_t s);
+hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int D,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t s);
+
+// ---- topk.hip
+struct TopkPlan {
+  int rows, N, k, key_bits, chunk, nchunks;
+  size_t hist_bytes, count_bytes, total_bytes;
+};
+TopkPlan plan_topk(int score_dtype, int rows, int N, int k);
+hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
+                       int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
+                       void* ws, hipStream_t s);
+
+// ---- indexer.hip
+hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const void* kx,
+                               int k_dtype, int64_t k_bstride, const uint8_t* ks,
+                               int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
+                               int ratio, int64_t pos0, int score_dtype, void* scores,
+                               hipStream_t s);
+
+// ---- attention.hip
+struct AttnArgs {
+  const void* q;
+  const void* kc;      // compressed K (CSA) or HCA K
+  const void* vc;
+  int64_t c_bstride;
+  int N;
+  int ratio;
+  const int32_t* idx;  // CSA only (nullptr for HCA)
+  int k;
+  const void* k_raw;
+  const void* v_raw;
+  int64_t raw_bstride;
+  int64_t T_raw, raw_pos0;
+  int n_win;
+  int64_t pos0;
+  int kv_dtype, B, Nq, H, d;
+  float scale;
+  float* out;
+  float* lse;
+};
+struct AttnPlan {
+  int rows, max_len, chunk, splits;
+  bool mfma;
+  size_t part_bytes, total_bytes;
+};
+AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len);
+hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
+                            hipStream_t s);
+
+}  // namespace hcsa

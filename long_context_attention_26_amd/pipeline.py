@@ -1,0 +1,123 @@
+"""One decode step / prefill chunk of a CSA layer and an HCA layer, as a sequence of
+libhcsa calls on one stream (argument marshalling only; every step runs in HIP kernels).
+
+Layout in HBM (all caller-owned torch tensors, row-major):
+  raw K, V        [B, T, d]     kv dtype (the uncompressed tokens; the window reads the tail)
+  raw indexer K   [B, T, d_I]   bf16 / f32
+  CSA K, V        [B, T/4, d]   kv dtype           (pool ratio 4)
+  indexer keys    [B, T/4, d_I] bf16 / f32, or MXFP4 codes [B, T/4, d_I/2] + scales
+                  [B, T/4, d_I/32]
+  HCA K, V        [B, T/128, d] kv dtype           (pool ratio 128)
+Workspaces are allocated once per shape and reused by every step.
+"""
+import torch
+
+from . import hcsa
+
+R_CSA, R_HCA = 4, 128
+
+
+class HybridAttentionState:
+    """Caches of one CSA layer and one HCA layer for B sequences of capacity T tokens."""
+
+    def clone_caches(self):
+        """A state with private copies of the pooled caches that shares the raw tokens."""
+        c = object.__new__(HybridAttentionState)
+        c.__dict__.update(self.__dict__)
+        for name in ("Kc", "Vc", "Kh", "Vh", "Ic", "Ics"):
+            t = getattr(self, name)
+            setattr(c, name, None if t is None else t.clone())
+        return c
+
+    def __init__(self, B, T, d, d_I, kv_dtype, idx_store, device, omegas):
+        self.B, self.T, self.d, self.d_I = B, T, d, d_I
+        self.kv_dtype = kv_dtype                      # torch.bfloat16 / torch.float32
+        self.idx_store = idx_store                    # "f32" | "bf16" | "mxfp4"
+        self.device = device
+        self.omegas = omegas                          # dict of fp32 tensors on device
+        Nc, Nh = T // R_CSA, T // R_HCA
+        self.Nc, self.Nh = Nc, Nh
+        e = lambda *s, dt=kv_dtype: torch.empty(*s, dtype=dt, device=device)
+        self.Kc, self.Vc = e(B, Nc, d), e(B, Nc, d)
+        self.Kh, self.Vh = e(B, Nh, d), e(B, Nh, d)
+        if idx_store == "mxfp4":
+            self.Ic = e(B, Nc, d_I // 2, dt=torch.uint8)
+            self.Ics = e(B, Nc, d_I // 32, dt=torch.uint8)
+        else:
+            self.Ic = e(B, Nc, d_I, dt=torch.float32 if idx_store == "f32" else torch.bfloat16)
+            self.Ics = None
+        self.K_raw = self.V_raw = self.I_raw = None
+
+    def attach_raw(self, K_raw, V_raw, I_raw):
+        self.K_raw, self.V_raw, self.I_raw = K_raw, V_raw, I_raw
+
+    def compress_range(self, t0, t1, stream=None):
+        """Pool the CSA and HCA blocks whose last token lies in [t0, t1), all streams in
+        one launch; each block is written at its own entry index."""
+        jobs = []
+        for ratio, pairs in ((R_CSA, ((self.K_raw, "csa_k", self.Kc), (self.V_raw, "csa_v", self.Vc),
+                                      (self.I_raw, "idx_k", self.Ic))),
+                             (R_HCA, ((self.K_raw, "hca_k", self.Kh), (self.V_raw, "hca_v", self.Vh)))):
+            # block j covers tokens [j*ratio, (j+1)*ratio) and completes at its last token
+            j0 = -(-(t0 + 1) // ratio) - 1
+            j1 = t1 // ratio
+            if j1 <= j0:
+                continue
+            for x, name, y in pairs:
+                ys = self.Ics[:, j0:j1] if (y is self.Ic and self.Ics is not None) else None
+                jobs.append(hcsa.pool_job(x[:, j0 * ratio: j1 * ratio], self.omegas[name], ratio,
+                                          y[:, j0:j1], ys))
+        if jobs:
+            hcsa.compress_kv_batched(jobs, self.B, stream=stream)
+
+
+class DecodeStep:
+    """Query token(s) at positions pos0 .. pos0+Nq-1 of every sequence through one CSA and
+    one HCA layer.  Owns its outputs and workspaces."""
+
+    def __init__(self, state, Nq, H, H_I, topk, n_win, score_dtype, scale):
+        st = state
+        self.st, self.Nq, self.H, self.H_I = st, Nq, H, H_I
+        self.topk, self.n_win, self.scale = topk, n_win, scale
+        self.score_code = hcsa.BF16 if score_dtype == "bf16" else hcsa.F32
+        B, d, dev = st.B, st.d, st.device
+        self.idx = torch.empty(B, Nq, topk, dtype=torch.int32, device=dev)
+        self.out_csa = torch.empty(B, Nq, H, d, dtype=torch.float32, device=dev)
+        self.lse_csa = torch.empty(B, Nq, H, dtype=torch.float32, device=dev)
+        self.out_hca = torch.empty(B, Nq, H, d, dtype=torch.float32, device=dev)
+        self.lse_hca = torch.empty(B, Nq, H, dtype=torch.float32, device=dev)
+        self.scores = torch.empty(B * Nq, st.Nc, device=dev,
+                                  dtype=torch.bfloat16 if score_dtype == "bf16" else torch.float32)
+        self.ws_topk = hcsa.alloc_workspace(
+            hcsa.topk_workspace_size(self.score_code, B, Nq, st.Nc, topk), dev)
+        self.ws_csa = hcsa.alloc_workspace(
+            hcsa.csa_attn_workspace_size(B, Nq, H, d, topk, n_win), dev)
+        self.ws_hca = hcsa.alloc_workspace(hcsa.hca_attn_workspace_size(B, Nq, H, d, st.Nh), dev)
+
+    def run(self, q, q_idx, w_idx, pos0, append=True, scores_out=None, stream=None,
+            marks=None):
+        """Full hot path for the query tokens at pos0..pos0+Nq-1: pool the blocks those
+        tokens complete (append), indexer scores, top-k, CSA sparse attention, HCA attention.
+        `marks`, if given, is called with a stage name before each stage and with "end"
+        after the last (used to record timing events on the stream)."""
+        st = self.st
+        mark = marks or (lambda name: None)
+        if append:
+            mark("compress")
+            st.compress_range(pos0, pos0 + self.Nq, stream=stream)
+        scores = self.scores if scores_out is None else scores_out
+        mark("index_scores")
+        hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, scores, k_scales=st.Ics,
+                              stream=stream)
+        mark("topk")
+        hcsa.topk(scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
+                  workspace=self.ws_topk, stream=stream)
+        mark("csa_attn")
+        hcsa.csa_sparse_attn(q, st.Kc, st.Vc, st.Nc, self.idx, st.K_raw, st.V_raw, 0, self.n_win,
+                             R_CSA, pos0, self.scale, self.out_csa, self.lse_csa,
+                             workspace=self.ws_csa, stream=stream)
+        mark("hca_attn")
+        hcsa.hca_dense_attn(q, st.Kh, st.Vh, st.Nh, R_HCA, pos0, self.scale, self.out_hca,
+                            self.lse_hca, workspace=self.ws_hca, stream=stream)
+        mark("end")
+        return self.idx, (self.out_csa, self.lse_csa), (self.out_hca, self.lse_hca)

@@ -1,0 +1,71 @@
+"""Helpers shared by the GPU parity tests: conversions, tolerances, reporting."""
+import numpy as np
+import torch
+
+import oracle as O
+
+
+def f64(t):
+    """Exact float64 copy of a tensor (bf16 and fp32 widen exactly)."""
+    return t.detach().to("cpu", torch.float32).double().numpy()
+
+
+def dev(a, dtype, device):
+    """float64 array holding values of `dtype` -> device tensor (exact)."""
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
+
+
+def bf16_ulp(x):
+    """Distance to the next bf16 above |x| (for |x| in the normal range)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.maximum(x, 2.0 ** -126))
+    return np.ldexp(1.0, e - 8)
+
+
+def assert_bf16_within_one_ulp(gpu, ref, what, acc_err=0.0):
+    """gpu and ref hold bf16 values; allow adjacent values (double rounding through fp32
+    on the GPU vs one rounding from the exact value in the oracle), plus `acc_err`, the
+    bound of the GPU's fp32 accumulation error before its final rounding."""
+    diff = np.abs(gpu - ref)
+    tol = np.maximum(bf16_ulp(ref), bf16_ulp(gpu)) + acc_err
+    bad = diff > tol * (1 + 1e-12)
+    assert not bad.any(), f"{what}: {bad.sum()} values beyond 1 bf16 ulp, worst {diff.max()}"
+    return int((diff > 0).sum())
+
+
+def assert_attention_close(out, lse, ref_o, ref_l, fp32, what):
+    """fp32 inputs: max-abs 1e-4 on the output; bf16 inputs: per (row, head) relative
+    max-norm error 2e-2 (|do|_inf / max(|o_ref|_inf, 1e-6)); lse within 1e-3 (abs)."""
+    out = np.asarray(out)
+    ref_o = np.asarray(ref_o)
+    assert out.shape == ref_o.shape, (out.shape, ref_o.shape)
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: empty-key rows differ"
+    assert (out[empty] == 0).all(), f"{what}: empty rows must be zero"
+    if fp32:
+        err = np.abs(out - ref_o).max() if out.size else 0.0
+        assert err <= 1e-4, f"{what}: max-abs error {err}"
+    else:
+        num = np.abs(out - ref_o).max(axis=-1)
+        den = np.maximum(np.abs(ref_o).max(axis=-1), 1e-6)
+        rel = (num / den)[~empty] if (~empty).any() else np.zeros(1)
+        assert rel.max() <= 2e-2, f"{what}: worst row relative error {rel.max()}"
+    le = np.abs(lse[~empty] - ref_l[~empty])
+    assert (le <= 1e-3).all(), f"{what}: lse error {le.max()}"
+
+
+def topk_set_ok(gpu_idx, ref_idx, ref_scores, k, what, rel=1e-5):
+    """End-to-end index check when scores differ by rounding: the two selections may
+    differ only among entries whose exact scores lie within `rel` of the k-th score."""
+    g = set(int(j) for j in gpu_idx if j >= 0)
+    r = set(int(j) for j in ref_idx if j >= 0)
+    assert list(gpu_idx) == sorted(gpu_idx[gpu_idx >= 0]) + [-1] * int((gpu_idx < 0).sum()), \
+        f"{what}: not ascending / padded"
+    assert len(g) == len(r), f"{what}: sizes differ"
+    if g == r:
+        return 0
+    kth = np.sort(ref_scores)[::-1][min(k, len(ref_scores)) - 1]
+    for j in g ^ r:
+        assert abs(ref_scores[j] - kth) <= rel * max(abs(kth), 1e-30) + 1e-30, \
+            f"{what}: entry {j} differs away from the threshold ({ref_scores[j]} vs {kth})"
+    return len(g ^ r) // 2

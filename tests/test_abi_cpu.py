@@ -1,0 +1,115 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and rejects
+bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hcsa.h")
+
+
+@pytest.fixture(scope="module")
+def H():
+    from long_context_attention_26_amd import hcsa
+    return hcsa
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(hcsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(H):
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(H.lib, n), n
+    assert set(names) == set(H.EXPORTED)
+    assert H.lib.hcsa_version() >= 100
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced on a failed check
+MIS = FAKE + 8          # misaligned
+
+
+def test_compress_validation(H):
+    L = H.lib
+    args = dict(x=FAKE, x_dtype=H.BF16, x_bstride=0, B=1, T=16, D=64, omega=FAKE, ratio=4,
+                y=FAKE, y_dtype=H.BF16, y_bstride=0, ys=None, ys_bstride=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.hcsa_compress_kv(a["x"], a["x_dtype"], a["x_bstride"], a["B"], a["T"], a["D"],
+                                  a["omega"], a["ratio"], a["y"], a["y_dtype"], a["y_bstride"],
+                                  a["ys"], a["ys_bstride"], a["s"])
+    assert call(ratio=0) == H.EINVAL
+    assert call(ratio=2000) == H.EINVAL
+    assert call(D=12) == H.EINVAL
+    assert call(x_dtype=7) == H.EDTYPE
+    assert call(y_dtype=H.MXFP4, D=40) == H.EINVAL
+    assert call(y_dtype=H.MXFP4) == H.EINVAL           # no scales pointer
+    assert call(x=None) == H.EINVAL
+    assert call(x=MIS) == H.EALIGN
+    assert call(B=2, x_bstride=10) == H.EINVAL
+    assert b"x_bstride" in L.hcsa_last_error()
+    assert call(T=3) == H.OK                           # nothing to pool: no launch
+
+
+def test_topk_validation(H):
+    L = H.lib
+    ws = H.lib.hcsa_topk_workspace_size(H.BF16, 1, 1, 100, 10)
+    assert ws > 0
+    def call(k=10, N=100, stride=100, ws_ptr=FAKE, ws_bytes=ws, dt=H.BF16, ratio=1, pos0=99):
+        return L.hcsa_topk(FAKE, dt, stride, 1, 1, N, ratio, pos0, k, FAKE, ws_ptr, ws_bytes, None)
+    assert call(k=0) == H.EINVAL
+    assert call(k=5000) == H.EINVAL
+    assert call(stride=50) == H.EINVAL
+    assert call(ws_ptr=None) == H.EWORKSPACE
+    assert call(ws_bytes=ws - 1) == H.EWORKSPACE
+    assert call(ws_ptr=FAKE + 16) == H.EWORKSPACE     # not 256-byte aligned
+    assert call(dt=H.MXFP4) == H.EDTYPE
+    assert call(ratio=0) == H.EINVAL
+    assert call(pos0=-1) == H.EINVAL
+
+
+def test_index_topk_validation(H):
+    L = H.lib
+    ws = L.hcsa_csa_index_topk_workspace_size(1, 1, 1024, 64, H.F32)
+    def call(q_dt=H.F32, k_dt=H.F32, H_I=1, d_I=32, ks=None):
+        return L.hcsa_csa_index_topk(FAKE, q_dt, FAKE, FAKE, k_dt, 0, ks, 0, 1, 1, H_I, d_I,
+                                     1024, 4, 4095, 64, H.F32, FAKE, None, FAKE, ws, None)
+    assert call(H_I=3) == H.EINVAL
+    assert call(d_I=48) == H.EINVAL
+    assert call(q_dt=H.BF16) == H.EDTYPE
+    assert call(k_dt=H.MXFP4, q_dt=H.BF16) == H.EINVAL   # no scales
+    assert call(k_dt=H.F32, d_I=128) == H.EINVAL
+
+
+def test_attention_validation(H):
+    L = H.lib
+    ws = L.hcsa_csa_sparse_attn_workspace_size(1, 1, 16, 128, 64, 128)
+    def csa(H_=16, d=128, raw_pos0=0, T_raw=4096, pos0=4095, n_win=128, kdt=H.BF16, k=64):
+        return L.hcsa_csa_sparse_attn(FAKE, FAKE, FAKE, 0, 1024, FAKE, k, FAKE, FAKE, 0, T_raw,
+                                      raw_pos0, n_win, 4, pos0, kdt, 1, 1, H_, d, 0.1, FAKE,
+                                      FAKE, FAKE, ws, None)
+    assert csa(H_=65) == H.EINVAL
+    assert csa(d=12) == H.EINVAL
+    assert csa(kdt=H.MXFP4) == H.EDTYPE
+    assert csa(raw_pos0=4000) == H.EINVAL                # window starts before the raw rows
+    assert csa(T_raw=100, raw_pos0=3900, pos0=4095) == H.EINVAL  # window ends after them
+    assert csa(k=5000) == H.EINVAL
+    hws = L.hcsa_hca_dense_attn_workspace_size(1, 1, 16, 128, 32)
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, MIS, 0, 32, 128, 4095, H.BF16, 1, 1, 16, 128,
+                                 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 0, 4095, H.BF16, 1, 1, 16, 128,
+                                 0.1, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
+
+
+def test_workspace_sizes_are_monotone(H):
+    L = H.lib
+    a = L.hcsa_topk_workspace_size(H.F32, 1, 1, 1000, 10)
+    b = L.hcsa_topk_workspace_size(H.F32, 4, 1, 1000, 10)
+    assert b >= a > 0
+    assert L.hcsa_hca_dense_attn_workspace_size(1, 1, 16, 128, 8192) > 0

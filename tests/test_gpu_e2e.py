@@ -1,0 +1,108 @@
+"""End-to-end parity of the full hot path (pool-on-append -> indexer -> top-k -> CSA sparse
+attention, and HCA dense attention) with the CPU oracle, on the five workloads: config 1
+in full, reduced-length versions of the others, and the full-size configs on sampled
+sequences / query rows."""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_helpers import assert_attention_close, f64, topk_set_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_sequence(cfg, raw, om, q, qi, wi, rows):
+    """Oracle results of the query rows `rows` of one sequence from its raw tokens."""
+    K, V, I = (f64(t) for t in raw)
+    omd = {k: f64(v) for k, v in om.items()}
+    kv = cfg.kv
+    Kc = O.round_to(O.compress(K, omd["csa_k"], 4), kv)
+    Vc = O.round_to(O.compress(V, omd["csa_v"], 4), kv)
+    Kh = O.round_to(O.compress(K, omd["hca_k"], 128), kv)
+    Vh = O.round_to(O.compress(V, omd["hca_v"], 128), kv)
+    Ic_exact = O.compress(I, omd["idx_k"], 4)
+    if cfg.idx == "mxfp4":
+        Ic = O.mxfp4_roundtrip(O.round_fp32(Ic_exact))
+    else:
+        Ic = O.round_to(Ic_exact, cfg.idx)
+    res = {}
+    for i in rows:
+        p = cfg.pos0 + i
+        qi_seen = O.mxfp4_roundtrip(qi[i]) if cfg.idx == "mxfp4" else qi[i]
+        r = O.decode_query(q[i], qi_seen, wi[i], Kc, Vc, Ic, K, V, 0, Kh, Vh, p, cfg.topk,
+                           cfg.n_win, cfg.scale, cfg.score)
+        # reference selection for the recall report: fp32 scores of the unquantized keys
+        nv = O.visible_entries(p, Kc.shape[0], 4)
+        ref_unq = O.index_scores(qi[i], wi[i], O.round_fp32(Ic_exact), nv, "f32")
+        r["idx_fp32_ref"] = O.select_topk(ref_unq, nv, cfg.topk)
+        r["exact_scores"] = O.index_scores(qi_seen, wi[i], Ic, nv, "f32")
+        res[i] = r
+    return res
+
+
+def _check(cfg, seqs, rows, label):
+    """Runs the whole batch of cfg on the GPU (the benchmark's launch configuration) and
+    checks sequences `seqs`, query rows `rows` against the oracle."""
+    gpu = torch.device("cuda:0")
+    t0 = time.time()
+    st, step, (q, qi, wi), om = W.build_case(cfg, gpu)
+    idx, (oc, lc), (oh, lh) = step.run(q, qi, wi, cfg.pos0)
+    torch.cuda.synchronize()
+    print(f"{label}: GPU setup+step {time.time() - t0:.1f}s", flush=True)
+    gi, goc, glc, goh, glh = (t.cpu().numpy() for t in (idx, oc, lc, oh, lh))
+    recalls, swaps = [], 0
+    for b in seqs:
+        si = b
+        raw = (st.K_raw[si], st.V_raw[si], st.I_raw[si])
+        res = _oracle_sequence(cfg, raw, om, f64(q[si]), f64(qi[si]), f64(wi[si]), rows)
+        for i in rows:
+            r = res[i]
+            swaps += topk_set_ok(gi[si, i], r["idx"], r["exact_scores"], cfg.topk,
+                                 f"{label} seq {b} row {i}",
+                                 rel=2e-2 if cfg.score == "bf16" else 1e-5)
+            # CSA given the oracle's own selection; HCA as is
+            assert_attention_close(goc[si, i], glc[si, i], *r["csa"], cfg.kv == "f32",
+                                   f"{label} csa seq {b} row {i}")
+            assert_attention_close(goh[si, i], glh[si, i], *r["hca"], cfg.kv == "f32",
+                                   f"{label} hca seq {b} row {i}")
+            sel = set(int(j) for j in gi[si, i] if j >= 0)
+            ref = set(int(j) for j in r["idx_fp32_ref"] if j >= 0)
+            recalls.append(len(sel & ref) / max(1, len(ref)))
+    print(f"{label}: boundary swaps {swaps}, recall vs exact fp32 top-k: "
+          f"mean {np.mean(recalls):.4f} min {np.min(recalls):.4f} "
+          f"({time.time() - t0:.1f}s)", flush=True)
+    return recalls
+
+
+def test_config1_full():
+    """Config 1 (fp32, 4096 tokens): every output, max-abs 1e-4."""
+    _check(W.CONFIGS[1], [0], [0], "config 1")
+
+
+@pytest.mark.parametrize("cid,T,B", [(2, 16384, 3), (3, 32768, 1), (5, 16384, 3)])
+def test_decode_reduced(cid, T, B):
+    cfg = W.small(W.CONFIGS[cid], T=T, B=B, pos0=T - 1)
+    _check(cfg, list(range(B)), [0], f"config {cid} at T={T}")
+
+
+def test_prefill_reduced():
+    cfg = W.small(W.CONFIGS[4], T=8192 + 512, Nq=512, pos0=8192)
+    _check(cfg, [0], [0, 1, 2, 3, 127, 128, 300, 511], "config 4 at 8192+512")
+
+
+@pytest.mark.parametrize("cid,seqs", [(2, [0, 7]), (3, [0]), (5, [0, 31])])
+def test_decode_full_size(cid, seqs):
+    """Full-size decode configs (whole batch on the GPU); the oracle checks the listed
+    sequences."""
+    cfg = W.CONFIGS[cid]
+    _check(cfg, seqs, [0], f"config {cid} full size")
+
+
+def test_prefill_full_size_sampled_rows():
+    cfg = W.CONFIGS[4]
+    _check(cfg, [0], [0, 1, 2, 3, 127, 128, 2048, 4095], "config 4 full size")

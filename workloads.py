@@ -125,3 +125,27 @@ def pool_logits(cfg, device="cpu"):
         r = cfg.r_hca if name.startswith("hca") else cfg.r_csa
         out[name] = normal((r,), cfg.cid, stream, 0, device, "f32", std=r ** -0.5)
     return out
+
+
+def build_case(cfg, device, seqs=None):
+    """Raw tokens, pooled caches (every block completed before pos0) and query inputs of
+    `cfg` on `device`; returns (state, step, (q, q_idx, w_idx), omegas).  The step's own
+    run() pools the blocks completed by the query tokens themselves.  `seqs` restricts
+    the batch to a list of sequence ids (each keeps its own seed)."""
+    from long_context_attention_26_amd.pipeline import DecodeStep, HybridAttentionState
+
+    seqs = list(range(cfg.B)) if seqs is None else list(seqs)
+    B = len(seqs)
+    om = pool_logits(cfg, device)
+    st = HybridAttentionState(B, cfg.T, cfg.d, cfg.d_I, torch_dtype(cfg.kv), cfg.idx, device, om)
+    K = torch.empty(B, cfg.T, cfg.d, dtype=torch_dtype(cfg.kv), device=device)
+    V = torch.empty_like(K)
+    I = torch.empty(B, cfg.T, cfg.d_I, dtype=torch_dtype(cfg.idx_raw), device=device)
+    for i, b in enumerate(seqs):
+        K[i], V[i], I[i] = raw_sequence(cfg, b, device)
+    st.attach_raw(K, V, I)
+    st.compress_range(0, cfg.pos0)
+    q, qi, wi = queries(cfg, device)
+    q, qi, wi = q[seqs].contiguous(), qi[seqs].contiguous(), wi[seqs].contiguous()
+    step = DecodeStep(st, cfg.Nq, cfg.H, cfg.H_I, cfg.topk, cfg.n_win, cfg.score, cfg.scale)
+    return st, step, (q, qi, wi), om
