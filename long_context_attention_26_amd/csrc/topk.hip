@@ -1,20 +1,23 @@
-// Top-k selector: exact, deterministic radix select over order-preserving score keys.
+// Top-k selector: exact and deterministic, on order-preserving integer keys of the scores.
 //
 // The indexer keeps the top-k compressed entries of each query (Lighthouse, "deep
-// deepseek v4 release", section 八 item 3; k = 1024 Pro / 512 Flash) and BF16 scores make
-// the selector cheaper (9fzt.com digest, item 4).  Ties go to the lowest index and the
-// output is ascending, which is the reading taken where the pages are silent.
+// deepseek v4 release", section 八 item 3; k = 1024 Pro / 512 Flash); BF16 scores make the
+// selector cheaper (9fzt.com digest, item 4).  Ties go to the lowest index and the output
+// is ascending, the reading taken where the pages are silent.
 //
-// Design (many CUs per row, one row per grid.y):
-//   pass 0..L-1  every (row, chunk) block histograms the next 8-bit digit of the keys
-//                that match the digits fixed so far (LDS histogram, then one global atomic
-//                per non-empty bin).  A 16-bit bf16 key takes 2 passes, an fp32 key 4.
-//   count        every block re-derives the exact threshold key T and the number `need`
-//                of T-valued keys to keep, and counts its keys > T and == T.
-//   compact      every block sums the counts of the chunks before it and writes its
-//                selected indices with a ballot prefix scan, in index order, so the output
-//                is ascending and ties resolve to the lowest indices without any ordering
-//                from atomics.
+// Three steps after a 12-bit histogram of every row's keys (built by the indexer kernel
+// itself, or by topk_hist_kernel for caller-given scores):
+//   extract  many blocks per row: the histogram gives the 12-bit bin b0 holding the k-th
+//            largest key; every key in bins >= b0 is appended to the row's candidate list
+//            (wave-aggregated atomics; the list order does not matter).  Typically about
+//            k + |bin b0| candidates.
+//   resolve  one block per row: with the candidates in LDS, the remaining key bits give
+//            the exact threshold key T and how many T-valued entries to keep; ties keep the
+//            lowest indices; the k selected indices are written in ascending order (each
+//            index's rank among the selected is counted).  A row whose candidates exceed the
+//            list capacity (massive ties) is resolved exactly from its full score row
+//            instead, with an ordered compaction.
+// Every step is integer-only, so the result does not depend on scheduling.
 #include "common.h"
 #include "internal.h"
 
@@ -24,16 +27,19 @@ namespace hcsa {
 
 namespace {
 
+constexpr int kBins = 4096;        // 12-bit first digit
+constexpr int kCap = 8192;         // candidates kept per row
+constexpr int kExtractChunk = 8192;
+
 struct TopkDev {
   const void* scores;
   int64_t row_stride;
   int Nq, N, ratio, k;
   int64_t pos0;
-  int chunk;
-  uint32_t* hist;    // [rows][levels][256]
-  uint32_t* counts;  // [rows][nchunks][2]
-  int nchunks;
-  int32_t* idx;      // [rows][k]
+  uint32_t* hist;       // [rows][kBins]
+  uint32_t* cnt;        // [rows]
+  uint64_t* cand;       // [rows][kCap]
+  int32_t* idx;         // [rows][k]
 };
 
 template <int KB>
@@ -50,72 +56,136 @@ __device__ __forceinline__ int visible(const TopkDev& P, int row) {
   return static_cast<int>(v < P.N ? v : P.N);
 }
 
-// Wave 0 walks the histograms of levels [0, L) from the top bin down and leaves in LDS
-// the fixed digit prefix and how many keys with that prefix must still be taken.
-__device__ void walk_levels(const uint32_t* hrow, int L, int k, uint32_t* s_prefix,
-                            int* s_krem) {
+// Wave 0 finds the 12-bit bin b0 holding the k-th largest key: count(bins > b0) < k <=
+// count(bins >= b0).  Lane l owns bins 4095-64l .. 4032-64l.  Results go to LDS.
+__device__ void find_b0(const uint32_t* hrow, int k, int* s_b0, int* s_above) {
   if (threadIdx.x >= kWave) return;
   const int lane = threadIdx.x;
-  uint32_t prefix = 0;
-  int krem = k;
-  for (int l = 0; l < L; ++l) {
-    const uint32_t* h = hrow + l * 256;
-    uint32_t c[4];
-    uint32_t sum = 0;
+  const int top = kBins - 1 - 64 * lane;
+  uint32_t sum = 0;
+  const u32x4* h4 = reinterpret_cast<const u32x4*>(hrow + top - 63);
+  u32x4 v[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = h[255 - 4 * lane - q];   // lane 0 owns the top bins
-      sum += c[q];
-    }
-    uint32_t incl = sum;
+  for (int i = 0; i < 16; ++i) v[i] = h4[i];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t t = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += t;
-    }
-    uint32_t above = incl - sum;
-    int found_digit = -1;
-    int found_krem = 0;
+  for (int i = 0; i < 16; ++i) sum += v[i][0] + v[i][1] + v[i][2] + v[i][3];
+  uint32_t incl = sum;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (found_digit < 0 && above < static_cast<uint32_t>(krem) &&
-          above + c[q] >= static_cast<uint32_t>(krem)) {
-        found_digit = 255 - 4 * lane - q;
-        found_krem = krem - static_cast<int>(above);
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  uint32_t above = incl - sum;
+  int found = -1, found_above = 0;
+  if (above < static_cast<uint32_t>(k) && incl >= static_cast<uint32_t>(k)) {
+    for (int b = 63; b >= 0; --b) {       // bins top .. top-63, descending
+      const uint32_t c = v[b >> 2][b & 3];
+      if (above + c >= static_cast<uint32_t>(k)) {
+        found = top - 63 + b;
+        found_above = static_cast<int>(above);
+        break;
       }
-      above += c[q];
+      above += c;
     }
-    const uint64_t who = __ballot(found_digit >= 0);
-    const int src = __builtin_ctzll(who);
-    found_digit = __shfl(found_digit, src, kWave);
-    found_krem = __shfl(found_krem, src, kWave);
-    prefix = (prefix << 8) | static_cast<uint32_t>(found_digit);
-    krem = found_krem;
   }
+  const uint64_t who = __ballot(found >= 0);
+  const int src = who ? __builtin_ctzll(who) : 0;
+  found = __shfl(found, src, kWave);
+  found_above = __shfl(found_above, src, kWave);
   if (lane == 0) {
-    *s_prefix = prefix;
-    *s_krem = krem;
+    *s_b0 = found;
+    *s_above = found_above;
   }
 }
 
-// Every block owns kChunk = 256 * kPer consecutive scores of one row; thread t holds the
-// kPer consecutive scores start + kPer*t .. +kPer-1 in registers (independent loads, one
-// round trip), so the ordered compaction needs only two block-wide scans.
-constexpr int kPer = 8;
-constexpr int kChunk = 256 * kPer;
+// ---------------------------------------------------------------- histogram of given scores
 
+// grid: (ceil(N / 2048), rows); block 256.
 template <int KB>
-__device__ __forceinline__ void load_keys(const TopkDev& P, int row, int j0, int end,
-                                          uint32_t (&key)[kPer], bool (&valid)[kPer]) {
+__global__ __launch_bounds__(256) void topk_hist_kernel(TopkDev P) {
+  __shared__ uint32_t h[kBins];
+  const int row = blockIdx.y;
+  const int nv = visible(P, row);
+  if (P.k >= nv) return;
+  const int start = blockIdx.x * 2048;
+  const int end = min(start + 2048, nv);
+  if (start >= end) return;
+  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
+  __syncthreads();
+  uint32_t key[8];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    valid[u] = j0 + u < end;
-    key[u] = valid[u] ? key_at<KB>(P, row, j0 + u) : 0u;
+  for (int u = 0; u < 8; ++u) {
+    const int j = start + threadIdx.x + 256 * u;
+    key[u] = j < end ? key_at<KB>(P, row, j) : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (start + static_cast<int>(threadIdx.x) + 256 * u < end) atomicAdd(&h[key[u] >> (KB - 12)], 1u);
+  __syncthreads();
+  uint32_t* hrow = P.hist + static_cast<int64_t>(row) * kBins;
+  for (int i = threadIdx.x; i < kBins; i += 256)
+    if (h[i]) atomicAdd(&hrow[i], h[i]);
+}
+
+// ---------------------------------------------------------------- extract candidates
+
+// grid: (ceil(N / kExtractChunk), rows); block 256.
+template <int KB>
+__global__ __launch_bounds__(256) void topk_extract_kernel(TopkDev P) {
+  __shared__ int s_b0, s_above;
+  const int row = blockIdx.y;
+  const int nv = visible(P, row);
+  if (P.k >= nv) return;
+  const int start = blockIdx.x * kExtractChunk;
+  const int end = min(start + kExtractChunk, nv);
+  if (start >= end) return;
+  find_b0(P.hist + static_cast<int64_t>(row) * kBins, P.k, &s_b0, &s_above);
+  __syncthreads();
+  const uint32_t b0 = static_cast<uint32_t>(s_b0);
+  uint64_t* cand = P.cand + static_cast<int64_t>(row) * kCap;
+  const int lane = threadIdx.x & 63;
+  for (int base = start; base < end; base += 256 * 8) {
+    uint32_t key[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = base + threadIdx.x + 256 * u;
+      key[u] = j < end ? key_at<KB>(P, row, j) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = base + threadIdx.x + 256 * u;
+      const bool c = j < end && (key[u] >> (KB - 12)) >= b0;
+      const uint64_t m = __ballot(c);
+      if (m == 0) continue;
+      uint32_t slot0 = 0;
+      if (lane == 0) slot0 = atomicAdd(&P.cnt[row], static_cast<uint32_t>(__popcll(m)));
+      slot0 = __shfl(slot0, 0, kWave);
+      const uint32_t slot = slot0 + ballot_rank(m);
+      if (c && slot < static_cast<uint32_t>(kCap)) {
+        const uint32_t inv = KB == 16 ? (0xFFFFu - key[u]) : ~key[u];
+        cand[slot] = (static_cast<uint64_t>(inv) << 32) | static_cast<uint32_t>(j);
+      }
+    }
   }
 }
 
-// Exclusive prefix sum of one int per thread over the 256 threads (thread order).
-__device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
+// ---------------------------------------------------------------- resolve one row
+
+constexpr int kResolveThreads = 1024;
+
+__device__ __forceinline__ int block_sum_1024(int v, int* s_red) {
+  v = wave_sum_i(v);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kResolveThreads / 64; ++i) t += s_red[i];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix of one int per thread over 1024 threads (thread order).
+__device__ __forceinline__ int block_scan_1024(int v, int* s_w, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -126,141 +196,145 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
   if (lane == kWave - 1) s_w[w] = incl;
   __syncthreads();
   int before = 0;
-  for (int i = 0; i < w; ++i) before += s_w[i];
-  total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < kResolveThreads / 64; ++i) {
+    before += i < w ? s_w[i] : 0;
+    total += s_w[i];
+  }
   __syncthreads();
   return before + incl - v;
 }
 
-template <int KB>
-__global__ __launch_bounds__(256) void topk_hist_kernel(TopkDev P, int level) {
-  constexpr int LEVELS = KB / 8;
-  const int row = blockIdx.y;
-  const int nv = visible(P, row);
-  if (P.k >= nv) return;
-  const int start = blockIdx.x * kChunk;
-  const int end = min(start + kChunk, nv);
-  if (start >= end) return;
-  __shared__ uint32_t h[256];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
-  h[threadIdx.x] = 0;
-  uint32_t key[kPer];
-  bool valid[kPer];
-  load_keys<KB>(P, row, start + kPer * threadIdx.x, end, key, valid);
-  uint32_t* hrow = P.hist + static_cast<int64_t>(row) * LEVELS * 256;
-  walk_levels(hrow, level, P.k, &s_prefix, &s_krem);
-  __syncthreads();
-  const uint32_t prefix = s_prefix;
-  const int shift = KB - 8 * (level + 1);
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    if (valid[u] && (level == 0 || (key[u] >> (shift + 8)) == prefix))
-      atomicAdd(&h[(key[u] >> shift) & 255u], 1u);
-  __syncthreads();
-  const uint32_t v = h[threadIdx.x];
-  if (v) atomicAdd(&hrow[level * 256 + threadIdx.x], v);
-}
-
-__device__ __forceinline__ int block_sum(int v, int* s_red) {
-  v = wave_sum_i(v);
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const int t = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-  __syncthreads();
-  return t;
-}
-
-template <int KB>
-__global__ __launch_bounds__(256) void topk_count_kernel(TopkDev P) {
-  constexpr int LEVELS = KB / 8;
-  const int row = blockIdx.y;
-  const int nv = visible(P, row);
-  if (P.k >= nv) return;
-  const int start = blockIdx.x * kChunk;
-  const int end = min(start + kChunk, nv);
-  if (start >= end) return;
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
-  __shared__ int s_red[4];
-  uint32_t key[kPer];
-  bool valid[kPer];
-  load_keys<KB>(P, row, start + kPer * threadIdx.x, end, key, valid);
-  walk_levels(P.hist + static_cast<int64_t>(row) * LEVELS * 256, LEVELS, P.k, &s_prefix,
-              &s_krem);
-  __syncthreads();
-  const uint32_t T = s_prefix;
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    gt += valid[u] && key[u] > T;
-    eq += valid[u] && key[u] == T;
-  }
-  gt = block_sum(gt, s_red);
-  eq = block_sum(eq, s_red);
-  if (threadIdx.x == 0) {
-    uint32_t* c = P.counts + (static_cast<int64_t>(row) * P.nchunks + blockIdx.x) * 2;
-    c[0] = gt;
-    c[1] = eq;
+// Radix over the bits below the 12-bit digit: finds the exact threshold key T and the number
+// `need` of T-valued keys to keep, given that `krem` keys must still be taken from bin b0.
+// `get(i)` returns the key of element i of a list of n elements (keys outside bin b0 do not
+// count).
+template <int KB, typename Get>
+__device__ void resolve_threshold(Get get, int n, uint32_t b0, int krem, uint32_t* s_h,
+                                  uint32_t* s_T, int* s_need) {
+  constexpr int LOW = KB - 12;                    // 4 (bf16) or 20 (fp32)
+  constexpr int DIG = LOW > 10 ? 10 : LOW;        // digit width
+  uint32_t prefix = b0;
+  int have = LOW;
+  while (have > 0) {
+    const int dw = have < DIG ? have : DIG;
+    const int nb = 1 << dw;
+    for (int i = threadIdx.x; i < nb; i += kResolveThreads) s_h[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kResolveThreads) {
+      const uint32_t key = get(i);
+      if ((key >> have) == prefix) atomicAdd(&s_h[(key >> (have - dw)) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int cum = 0;
+      for (int d = nb - 1; d >= 0; --d) {
+        const int c = static_cast<int>(s_h[d]);
+        if (cum + c >= krem) {
+          *s_T = (prefix << dw) | static_cast<uint32_t>(d);
+          *s_need = krem - cum;
+          break;
+        }
+        cum += c;
+      }
+    }
+    __syncthreads();
+    prefix = *s_T;
+    krem = *s_need;
+    have -= dw;
+    __syncthreads();
   }
 }
 
+// grid: rows; block 1024.
 template <int KB>
-__global__ __launch_bounds__(256) void topk_compact_kernel(TopkDev P) {
-  constexpr int LEVELS = KB / 8;
-  const int row = blockIdx.y;
+__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P) {
+  __shared__ uint64_t s_c[kCap];
+  __shared__ int32_t s_sel[4096];
+  __shared__ uint32_t s_h[1024];
+  __shared__ int s_red[kResolveThreads / 64];
+  __shared__ int s_b0, s_above, s_need, s_nsel;
+  __shared__ uint32_t s_T;
+  const int row = blockIdx.x;
   const int nv = visible(P, row);
-  const int start = blockIdx.x * kChunk;
-  const int end = min(start + kChunk, nv);
   int32_t* out = P.idx + static_cast<int64_t>(row) * P.k;
   if (P.k >= nv) {
-    for (int j = start + threadIdx.x; j < end; j += 256) out[j] = j;
-    if (blockIdx.x == 0)
-      for (int j = nv + threadIdx.x; j < P.k; j += 256) out[j] = -1;
+    for (int j = threadIdx.x; j < P.k; j += kResolveThreads) out[j] = j < nv ? j : -1;
     return;
   }
-  if (start >= end) return;
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
-  __shared__ int s_red[4];
-  const int j0 = start + kPer * threadIdx.x;
-  uint32_t key[kPer];
-  bool valid[kPer];
-  load_keys<KB>(P, row, j0, end, key, valid);
-  walk_levels(P.hist + static_cast<int64_t>(row) * LEVELS * 256, LEVELS, P.k, &s_prefix,
-              &s_krem);
-  const uint32_t* crow = P.counts + static_cast<int64_t>(row) * P.nchunks * 2;
-  int bg = 0, be = 0;
-  for (int c = threadIdx.x; c < static_cast<int>(blockIdx.x); c += 256) {
-    bg += crow[2 * c];
-    be += crow[2 * c + 1];
-  }
+  find_b0(P.hist + static_cast<int64_t>(row) * kBins, P.k, &s_b0, &s_above);
   __syncthreads();
-  const uint32_t T = s_prefix;
-  const int need = s_krem;
-  bg = block_sum(bg, s_red);
-  be = block_sum(be, s_red);
-  // rank of this thread's first T-valued key among the row's T-valued keys
-  int my_eq = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) my_eq += valid[u] && key[u] == T;
-  int tot;
-  int eq_rank = be + block_excl_scan(my_eq, s_red, tot);
-  bool sel[kPer];
-  int my_sel = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const bool gt = valid[u] && key[u] > T;
-    const bool eq = valid[u] && key[u] == T;
-    sel[u] = gt || (eq && eq_rank < need);
-    eq_rank += eq;
-    my_sel += sel[u];
+  const uint32_t b0 = static_cast<uint32_t>(s_b0);
+  const int krem = P.k - s_above;
+  const int C = static_cast<int>(P.cnt[row]);
+
+  if (C <= kCap) {
+    // ---- candidates in LDS
+    const uint64_t* cand = P.cand + static_cast<int64_t>(row) * kCap;
+    for (int i = threadIdx.x; i < C; i += kResolveThreads) s_c[i] = cand[i];
+    if (threadIdx.x == 0) s_nsel = 0;
+    __syncthreads();
+    auto key_of = [&](int i) -> uint32_t {
+      const uint32_t inv = static_cast<uint32_t>(s_c[i] >> 32);
+      return KB == 16 ? (0xFFFFu - inv) : ~inv;
+    };
+    resolve_threshold<KB>(key_of, C, b0, krem, s_h, &s_T, &s_need);
+    const uint32_t T = s_T;
+    const int need = s_need;
+    // count T-valued candidates; if more than needed, keep the lowest indices
+    int e = 0;
+    for (int i = threadIdx.x; i < C; i += kResolveThreads) e += key_of(i) == T;
+    const int E = block_sum_1024(e, s_red);
+    for (int i = threadIdx.x; i < C; i += kResolveThreads) {
+      const uint32_t key = key_of(i);
+      bool sel = key > T;
+      if (key == T) {
+        if (E == need) {
+          sel = true;
+        } else {
+          const uint32_t j = static_cast<uint32_t>(s_c[i]);
+          int rank = 0;
+          for (int m = 0; m < C; ++m)
+            rank += key_of(m) == T && static_cast<uint32_t>(s_c[m]) < j;
+          sel = rank < need;
+        }
+      }
+      if (sel) {
+        const int slot = atomicAdd(&s_nsel, 1);
+        if (slot < 4096) s_sel[slot] = static_cast<int32_t>(static_cast<uint32_t>(s_c[i]));
+      }
+    }
+    __syncthreads();
+    const int ns = min(s_nsel, P.k);
+    // ascending output: each index's rank among the selected
+    for (int i = threadIdx.x; i < ns; i += kResolveThreads) {
+      const int32_t j = s_sel[i];
+      int rank = 0;
+      for (int m = 0; m < ns; ++m) rank += s_sel[m] < j;
+      out[rank] = j;
+    }
+    return;
   }
-  int slot = bg + min(be, need) + block_excl_scan(my_sel, s_red, tot);
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if (sel[u] && slot < P.k) out[slot] = j0 + u;
-    slot += sel[u];
+
+  // ---- too many candidates: exact resolution from the full score row
+  auto key_row = [&](int j) -> uint32_t { return key_at<KB>(P, row, j); };
+  resolve_threshold<KB>(key_row, nv, b0, krem, s_h, &s_T, &s_need);
+  const uint32_t T = s_T;
+  const int need = s_need;
+  int sel_before = 0, eq_before = 0;
+  for (int base = 0; base < nv; base += kResolveThreads) {
+    const int j = base + threadIdx.x;
+    const uint32_t key = j < nv ? key_row(j) : 0u;
+    const bool gt = j < nv && key > T;
+    const bool eq = j < nv && key == T;
+    int tot;
+    const int er = eq_before + block_scan_1024(eq, s_red, tot);
+    eq_before += tot;
+    const bool sel = gt || (eq && er < need);
+    const int slot = sel_before + block_scan_1024(sel, s_red, tot);
+    sel_before += tot;
+    if (sel && slot < P.k) out[slot] = j;
   }
 }
 
@@ -278,17 +352,24 @@ TopkPlan plan_topk(int score_dtype, int rows, int N, int k) {
   p.N = N;
   p.k = k;
   p.key_bits = score_dtype == 1 ? 16 : 32;
-  p.chunk = 2048;   // = kChunk
+  p.chunk = kExtractChunk;
   p.nchunks = N > 0 ? (N + p.chunk - 1) / p.chunk : 1;
-  p.hist_bytes = align256(static_cast<size_t>(rows) * (p.key_bits / 8) * 256 * 4);
-  p.count_bytes = align256(static_cast<size_t>(rows) * p.nchunks * 2 * 4);
+  p.hist_bytes = align256(static_cast<size_t>(rows) * (kBins + 1) * 4);   // hist + counter
+  p.count_bytes = align256(static_cast<size_t>(rows) * kCap * 8);         // candidates
   p.total_bytes = p.hist_bytes + p.count_bytes;
   return p;
 }
 
-hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
-                       int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
-                       void* ws, hipStream_t s) {
+hipError_t launch_topk_clear(const TopkPlan& plan, void* ws, hipStream_t s) {
+  const int64_t words = static_cast<int64_t>(plan.rows) * (kBins + 1);
+  const int blocks = static_cast<int>(std::min<int64_t>((words + 255) / 256, 4096));
+  fill_u32_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(ws), words, 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t row_stride,
+                              int Nq, int ratio, int64_t pos0, int32_t* idx, void* ws,
+                              bool need_hist, hipStream_t s) {
   TopkDev P;
   P.scores = scores;
   P.row_stride = row_stride;
@@ -297,25 +378,31 @@ hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype
   P.ratio = ratio;
   P.k = plan.k;
   P.pos0 = pos0;
-  P.chunk = plan.chunk;
   P.hist = static_cast<uint32_t*>(ws);
-  P.counts = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + plan.hist_bytes);
-  P.nchunks = plan.nchunks;
+  P.cnt = P.hist + static_cast<int64_t>(plan.rows) * kBins;
+  P.cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + plan.hist_bytes);
   P.idx = idx;
-  const int64_t hist_words = static_cast<int64_t>(plan.hist_bytes / 4);
-  const int fill_blocks = static_cast<int>(std::min<int64_t>((hist_words + 255) / 256, 4096));
-  fill_u32_kernel<<<fill_blocks, 256, 0, s>>>(P.hist, hist_words, 0u);
-  dim3 grid(plan.nchunks, plan.rows);
   if (plan.key_bits == 16) {
-    for (int l = 0; l < 2; ++l) topk_hist_kernel<16><<<grid, 256, 0, s>>>(P, l);
-    topk_count_kernel<16><<<grid, 256, 0, s>>>(P);
-    topk_compact_kernel<16><<<grid, 256, 0, s>>>(P);
+    if (need_hist)
+      topk_hist_kernel<16><<<dim3((plan.N + 2047) / 2048, plan.rows), 256, 0, s>>>(P);
+    topk_extract_kernel<16><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
+    topk_resolve_kernel<16><<<plan.rows, kResolveThreads, 0, s>>>(P);
   } else {
-    for (int l = 0; l < 4; ++l) topk_hist_kernel<32><<<grid, 256, 0, s>>>(P, l);
-    topk_count_kernel<32><<<grid, 256, 0, s>>>(P);
-    topk_compact_kernel<32><<<grid, 256, 0, s>>>(P);
+    if (need_hist)
+      topk_hist_kernel<32><<<dim3((plan.N + 2047) / 2048, plan.rows), 256, 0, s>>>(P);
+    topk_extract_kernel<32><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
+    topk_resolve_kernel<32><<<plan.rows, kResolveThreads, 0, s>>>(P);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
+                       int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
+                       void* ws, hipStream_t s) {
+  (void)score_dtype;
+  hipError_t e = launch_topk_clear(plan, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_topk_select(plan, scores, row_stride, Nq, ratio, pos0, idx, ws, true, s);
 }
 
 }  // namespace hcsa

@@ -94,6 +94,21 @@ class DecodeStep:
             hcsa.csa_attn_workspace_size(B, Nq, H, d, topk, n_win), dev)
         self.ws_hca = hcsa.alloc_workspace(hcsa.hca_attn_workspace_size(B, Nq, H, d, st.Nh), dev)
 
+    def run_index_scores(self, q_idx, w_idx, pos0, stream=None):
+        st = self.st
+        hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, self.scores,
+                              k_scales=st.Ics, stream=stream)
+
+    def run_select_attend(self, q, pos0, stream=None):
+        st = self.st
+        hcsa.topk(self.scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
+                  workspace=self.ws_topk, stream=stream)
+        hcsa.csa_sparse_attn(q, st.Kc, st.Vc, st.Nc, self.idx, st.K_raw, st.V_raw, 0, self.n_win,
+                             R_CSA, pos0, self.scale, self.out_csa, self.lse_csa,
+                             workspace=self.ws_csa, stream=stream)
+        hcsa.hca_dense_attn(q, st.Kh, st.Vh, st.Nh, R_HCA, pos0, self.scale, self.out_hca,
+                            self.lse_hca, workspace=self.ws_hca, stream=stream)
+
     def run(self, q, q_idx, w_idx, pos0, append=True, scores_out=None, stream=None,
             marks=None):
         """Full hot path for the query tokens at pos0..pos0+Nq-1: pool the blocks those

@@ -334,3 +334,21 @@ def test_compress_batched_equals_single_calls(H, gpu):
         assert torch.equal(a, b)
     with pytest.raises(H.HcsaError):
         H.compress_kv_batched([H.pool_job(K, om4, 3, outs_b[0])] * 9, B)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_topk_massive_ties_take_lowest_indices(H, gpu, sdt):
+    """More tied candidates than the selector's candidate list holds: the exact full-row
+    resolution still returns the lowest indices."""
+    N, k = 50000, 777
+    s = np.zeros((2, N))
+    s[1, ::3] = 1.0                                     # row 1: 16667 tied maxima
+    st = dev(s, W.torch_dtype(sdt), gpu)
+    idx = torch.empty(2, k, dtype=torch.int32, device=gpu)
+    H.topk(st, 2, 1, N, 1, N - 1, k, idx)
+    _sync()
+    got = idx.cpu().numpy()
+    assert np.array_equal(got[0], np.arange(k))
+    assert np.array_equal(got[1], np.arange(0, 3 * k, 3))
+    for r in range(2):
+        assert np.array_equal(got[r], O.select_topk(s[r], N, k))
