@@ -143,7 +143,7 @@ def main():
         g_pool, g_idx, g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.stream(cap_stream):
             g_pool.capture_begin()
-            stp.st.compress_range(cfg.pos0, cfg.pos0 + cfg.Nq)
+            stp.run_pool(cfg.pos0)
             g_pool.capture_end()
             g_idx.capture_begin()
             stp.run_index_scores(qi, wi, cfg.pos0)

@@ -171,6 +171,29 @@ int hcsa_csa_index_scores(const void *q_idx, int q_dtype, const float *w_idx,
                           void *scores, hcsa_stream stream);
 
 /*
+ * Split-phase form of hcsa_csa_index_topk, for callers that schedule (or time) the
+ * indexer kernel on its own.  With one workspace of hcsa_topk_workspace_size(score_dtype,
+ * B, Nq, N, k) bytes, in stream order:
+ *   hcsa_topk_clear             zero the selector's histogram and candidate counters;
+ *   hcsa_csa_index_scores_hist  scores (as hcsa_csa_index_scores) plus, in the same kernel,
+ *                               the selector's histogram of every row's scores;
+ *   hcsa_topk_from_hist         the selection of hcsa_topk, reusing that histogram.
+ * The result equals hcsa_csa_index_topk's.  Arguments have the meanings and limits given
+ * above; `scores` is [B*Nq][N].
+ */
+int hcsa_topk_clear(int score_dtype, int B, int Nq, int N, int k, void *workspace,
+                    size_t ws_bytes, hcsa_stream stream);
+int hcsa_csa_index_scores_hist(const void *q_idx, int q_dtype, const float *w_idx,
+                               const void *k_idx, int k_dtype, int64_t k_bstride,
+                               const uint8_t *k_scales, int64_t ks_bstride, int B, int Nq,
+                               int H_I, int d_I, int N, int ratio, int64_t pos0, int k,
+                               int score_dtype, void *scores, void *workspace, size_t ws_bytes,
+                               hcsa_stream stream);
+int hcsa_topk_from_hist(const void *scores, int score_dtype, int64_t row_stride, int B, int Nq,
+                        int N, int ratio, int64_t pos0, int k, int32_t *idx, void *workspace,
+                        size_t ws_bytes, hcsa_stream stream);
+
+/*
  * CSA sparse attention [Lighthouse section 八 item 3]: for each query token (position
  * p = pos0 + i) and head, one softmax over the selected compressed entries (topk_idx,
  * entries outside [0, n_c(p)) are skipped) followed by the raw window tokens

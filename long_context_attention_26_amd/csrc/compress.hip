@@ -124,7 +124,59 @@ __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_
   }
 }
 
-// grid: (ceil(n_out / rows_per_block), B); block 256.
+// Long blocks (ratio >= kWideRatio): one block per output entry.  Thread (g, c8) sums
+// rows g, g + G, g + 2G, ... of its 8 channels (G = 256 / (D/8) row groups), so all of a
+// thread's loads are independent; the G partial sums are added in group order in LDS.
+constexpr int kWideRatio = 32;
+
+template <bool IN_BF16, int OUT>
+__device__ __forceinline__ void pool_rows_wide(const void* __restrict__ x, int64_t x_bs, int D,
+                                               const float* alpha, int r, void* __restrict__ y,
+                                               int64_t y_bs, uint8_t* __restrict__ ys,
+                                               int64_t ys_bs, int64_t j, int b, float* s_part) {
+  const int tpr = D >> 3;
+  const int G = blockDim.x / tpr;
+  const int g = threadIdx.x / tpr;
+  const int c8 = threadIdx.x - g * tpr;
+  constexpr int ES = IN_BF16 ? 2 : 4;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (g < G) {
+    const char* src = static_cast<const char*>(x) + (b * x_bs + j * r * D + c8 * 8) * ES;
+    const int64_t row_bytes = static_cast<int64_t>(D) * ES;
+#pragma unroll 8
+    for (int i = g; i < r; i += G) {
+      float v[8];
+      load8<IN_BF16>(src + i * row_bytes, v);
+      const float a = alpha[i];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(a, v[c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s_part[g * D + c8 * 8 + c] = acc[c];
+  }
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = s_part[c8 * 8 + c];
+    for (int gg = 1; gg < G; ++gg)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] += s_part[gg * D + c8 * 8 + c];
+    if constexpr (OUT == OUT_MXFP4) {
+      store8<OUT>(acc, y, b * y_bs + j * (D >> 1), ys, b * ys_bs + j * (D >> 5), c8);
+    } else {
+      store8<OUT>(acc, y, b * y_bs + j * D, nullptr, 0, c8);
+    }
+  }
+}
+
+// Blocks a pooling job needs: one per entry for long blocks, else rows_per_block entries.
+__host__ __device__ inline int64_t pool_blocks(int n_out, int D, int r) {
+  if (r >= kWideRatio) return n_out;
+  const int rpb = 256 / (D / 8);
+  return (static_cast<int64_t>(n_out) + rpb - 1) / rpb;
+}
+
+// grid: (pool_blocks(...), B); block 256.
 template <bool IN_BF16, int OUT>
 __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ x,
                                                        int64_t x_bs, int D,
@@ -133,9 +185,14 @@ __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ 
                                                        uint8_t* __restrict__ ys, int64_t ys_bs,
                                                        int n_out) {
   __shared__ float alpha[1024];
+  __shared__ float s_part[2048];
   pool_weights(omega, r, alpha);
-  pool_rows<IN_BF16, OUT>(x, x_bs, D, alpha, r, y, y_bs, ys, ys_bs, n_out, blockIdx.x,
-                          blockIdx.y);
+  if (r >= kWideRatio)
+    pool_rows_wide<IN_BF16, OUT>(x, x_bs, D, alpha, r, y, y_bs, ys, ys_bs, blockIdx.x,
+                                 blockIdx.y, s_part);
+  else
+    pool_rows<IN_BF16, OUT>(x, x_bs, D, alpha, r, y, y_bs, ys, ys_bs, n_out, blockIdx.x,
+                            blockIdx.y);
 }
 
 // Several pooling jobs in one launch (the blocks completed by a decode token in every
@@ -146,8 +203,20 @@ struct PoolJobs {
   int n;
 };
 
+template <bool IN_BF16, int OUT>
+__device__ __forceinline__ void pool_job_blocks(const hcsa_pool_job& q, const float* alpha,
+                                                int64_t jb, int n_out, float* s_part) {
+  if (q.ratio >= kWideRatio)
+    pool_rows_wide<IN_BF16, OUT>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride,
+                                 q.y_scales, q.ys_bstride, jb, blockIdx.y, s_part);
+  else
+    pool_rows<IN_BF16, OUT>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride,
+                            q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+}
+
 __global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
   __shared__ float alpha[1024];
+  __shared__ float s_part[2048];
   int t = 0;
   while (t + 1 < J.n && static_cast<int>(blockIdx.x) >= J.first_block[t + 1]) ++t;
   const hcsa_pool_job& q = J.job[t];
@@ -155,18 +224,12 @@ __global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
   const int64_t jb = blockIdx.x - J.first_block[t];
   const int n_out = q.T / q.ratio;
   const bool ib = q.x_dtype == 1;
-  if (ib && q.y_dtype == 1)
-    pool_rows<true, OUT_BF16>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
-  else if (ib && q.y_dtype == 2)
-    pool_rows<true, OUT_MXFP4>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
-  else if (ib)
-    pool_rows<true, OUT_F32>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
-  else if (q.y_dtype == 1)
-    pool_rows<false, OUT_BF16>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
-  else if (q.y_dtype == 2)
-    pool_rows<false, OUT_MXFP4>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
-  else
-    pool_rows<false, OUT_F32>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+  if (ib && q.y_dtype == 1) pool_job_blocks<true, OUT_BF16>(q, alpha, jb, n_out, s_part);
+  else if (ib && q.y_dtype == 2) pool_job_blocks<true, OUT_MXFP4>(q, alpha, jb, n_out, s_part);
+  else if (ib) pool_job_blocks<true, OUT_F32>(q, alpha, jb, n_out, s_part);
+  else if (q.y_dtype == 1) pool_job_blocks<false, OUT_BF16>(q, alpha, jb, n_out, s_part);
+  else if (q.y_dtype == 2) pool_job_blocks<false, OUT_MXFP4>(q, alpha, jb, n_out, s_part);
+  else pool_job_blocks<false, OUT_F32>(q, alpha, jb, n_out, s_part);
 }
 
 hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B, hipStream_t s) {
@@ -176,10 +239,9 @@ hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B, hipS
   for (int i = 0; i < n; ++i) {
     const int n_out = jobs[i].T / jobs[i].ratio;
     if (n_out == 0) continue;
-    const int rpb = 256 / (jobs[i].D / 8);
     J.job[J.n] = jobs[i];
     J.first_block[J.n] = blocks;
-    blocks += (n_out + rpb - 1) / rpb;
+    blocks += static_cast<int>(pool_blocks(n_out, jobs[i].D, jobs[i].ratio));
     ++J.n;
   }
   J.first_block[J.n] = blocks;
@@ -194,9 +256,7 @@ static hipError_t launch_compress_t(const void* x, int64_t x_bs, int B, int T, i
                                     int64_t y_bs, uint8_t* ys, int64_t ys_bs, hipStream_t s) {
   const int n_out = T / r;
   if (n_out == 0) return hipSuccess;
-  const int tpr = D / 8;
-  const int rpb = 256 / tpr;
-  dim3 grid((n_out + rpb - 1) / rpb, B);
+  dim3 grid(static_cast<unsigned>(pool_blocks(n_out, D, r)), B);
   if (y_dtype == 0)
     compress_kernel<IN_BF16, OUT_F32><<<grid, 256, 0, s>>>(x, x_bs, D, omega, r, y, y_bs, ys,
                                                            ys_bs, n_out);

@@ -26,6 +26,7 @@ struct IdxDev {
   int64_t pos0;
   void* scores;      // [rows][N]
   int chunk;
+  uint32_t* hist;    // optional [rows][4096] selector histogram (12-bit key digit)
 };
 
 // Keys per block: enough blocks to cover every CU several times even for one sequence,
@@ -54,7 +55,35 @@ __device__ __forceinline__ float dot16b_f32(const u32x4& a, const u32x4& b, floa
   return acc;
 }
 
-// grid: (ceil(N / kChunk), rows); block 256.
+// Selector histogram fused into the score kernels: a 4096-bin LDS histogram of the 12-bit
+// top digit of each stored score's order-preserving key, flushed with one global atomic per
+// non-empty bin.
+constexpr int kHistBins = 4096;
+
+__device__ __forceinline__ void hist_clear(uint32_t* h, bool on) {
+  if (on)
+    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+  __syncthreads();
+}
+
+template <bool SBF16>
+__device__ __forceinline__ void hist_add(uint32_t* h, float s) {
+  if constexpr (SBF16)
+    atomicAdd(&h[bf16_key(f32_to_bf16_bits(s)) >> 4], 1u);
+  else
+    atomicAdd(&h[f32_key(__float_as_uint(s)) >> 20], 1u);
+}
+
+__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* g, int row) {
+  __syncthreads();
+  uint32_t* grow = g + static_cast<int64_t>(row) * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) {
+    const uint32_t v = h[i];
+    if (v) atomicAdd(&grow[i], v);
+  }
+}
+
+// grid: (ceil(N / chunk), rows); block 256.
 template <int HI, int LPE, bool KBF16, bool SBF16>
 __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
   constexpr int ES = KBF16 ? 2 : 4;
@@ -72,6 +101,9 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
   const int sub = threadIdx.x % LPE;
   const int grp = threadIdx.x / LPE;
   const int row_bytes = A.d_I * ES;
+  __shared__ uint32_t s_hist[kHistBins];
+  const bool hist = A.hist != nullptr;
+  hist_clear(s_hist, hist);
 
   u32x4 qv[HI];
   float w[HI];
@@ -116,9 +148,11 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
           s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
         else
           s32[j] = s;
+        if (hist) hist_add<SBF16>(s_hist, s);
       }
     }
   }
+  if (hist) hist_flush(s_hist, A.hist, row);
 }
 
 template <int HI, int LPE, bool KBF16>
@@ -171,6 +205,7 @@ struct IdxMxDev {
   int64_t pos0;
   void* scores;
   int chunk;
+  uint32_t* hist;
 };
 
 // grid: (ceil(N / kChunk), rows); block 256.  LPE = d_I / 32 lanes per key.
@@ -194,6 +229,10 @@ __global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
   // words 4..7 elements 8c+1, 8c+3, 8c+5, 8c+7 (c = word index mod 4), as int8 = 2*value.
   __shared__ uint32_t s_q[16][4][8];
   __shared__ int s_qe[16][4];
+  __shared__ uint32_t s_hist[kHistBins];
+  const bool hist = A.hist != nullptr;
+  if (hist)
+    for (int i = threadIdx.x; i < kHistBins; i += 256) s_hist[i] = 0;
   if (threadIdx.x < HI * LPE) {
     const int g = threadIdx.x / LPE, blk = threadIdx.x % LPE;
     const int64_t off = (static_cast<int64_t>(row) * HI + g) * A.d_I + blk * 32;
@@ -290,9 +329,11 @@ __global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
           s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
         else
           s32[j] = s;
+        if (hist) hist_add<SBF16>(s_hist, s);
       }
     }
   }
+  if (hist) hist_flush(s_hist, A.hist, row);
 }
 
 template <int HI, int LPE, bool QBF16>
@@ -334,7 +375,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
                                      const uint8_t* kx, int64_t k_bstride, const uint8_t* ks,
                                      int64_t ks_bstride, int B, int Nq, int H_I, int d_I,
                                      int N, int ratio, int64_t pos0, int score_dtype,
-                                     void* scores, hipStream_t s) {
+                                     void* scores, uint32_t* hist, hipStream_t s) {
   IdxMxDev A;
   A.q = q;
   A.w = w;
@@ -349,6 +390,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.pos0 = pos0;
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
+  A.hist = hist;
   if (q_dtype == 1) return launch_mx_q<true>(A, B * Nq, H_I, score_dtype, s);
   return launch_mx_q<false>(A, B * Nq, H_I, score_dtype, s);
 }
@@ -358,11 +400,11 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, int score_dtype, void* scores,
-                               hipStream_t s) {
+                               uint32_t* hist, hipStream_t s) {
   if (k_dtype == 2)
     return launch_mxfp4_index_scores(q, q_dtype, w, static_cast<const uint8_t*>(kx), k_bstride,
                                      ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0,
-                                     score_dtype, scores, s);
+                                     score_dtype, scores, hist, s);
   IdxDev A;
   A.q = q;
   A.w = w;
@@ -375,6 +417,7 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.pos0 = pos0;
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
+  A.hist = hist;
   const int rows = B * Nq;
   const int lpe = d_I * (k_dtype == 1 ? 2 : 4) / 16;
   if (k_dtype == 1) {

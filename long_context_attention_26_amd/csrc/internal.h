@@ -28,13 +28,19 @@ TopkPlan plan_topk(int score_dtype, int rows, int N, int k);
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
                        int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
                        void* ws, hipStream_t s);
+// split phases: clear the histogram/counters; select from scores whose histogram was
+// already accumulated into ws (need_hist = false) or is built here (need_hist = true)
+hipError_t launch_topk_clear(const TopkPlan& plan, void* ws, hipStream_t s);
+hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t row_stride,
+                              int Nq, int ratio, int64_t pos0, int32_t* idx, void* ws,
+                              bool need_hist, hipStream_t s);
 
 // ---- indexer.hip
 hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const void* kx,
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, int score_dtype, void* scores,
-                               hipStream_t s);
+                               uint32_t* hist, hipStream_t s);
 
 // ---- attention.hip
 struct AttnArgs {

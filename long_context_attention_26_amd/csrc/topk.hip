@@ -9,12 +9,13 @@
 // itself, or by topk_hist_kernel for caller-given scores):
 //   extract  many blocks per row: the histogram gives the 12-bit bin b0 holding the k-th
 //            largest key; every key in bins >= b0 is appended to the row's candidate list
-//            (wave-aggregated atomics; the list order does not matter).  Typically about
-//            k + |bin b0| candidates.
+//            (one atomic per block reserves its slots; the list order does not matter).
+//            Typically about k + |bin b0| candidates.
 //   resolve  one block per row: with the candidates in LDS, the remaining key bits give
 //            the exact threshold key T and how many T-valued entries to keep; ties keep the
-//            lowest indices; the k selected indices are written in ascending order (each
-//            index's rank among the selected is counted).  A row whose candidates exceed the
+//            lowest indices (each tie's rank among the ties is counted); the k selected
+//            indices are written in ascending order by a counting sort on their top 10 bits
+//            and a rank count inside each bucket.  A row whose candidates exceed the
 //            list capacity (massive ties) is resolved exactly from its full score row
 //            instead, with an ordered compaction.
 // Every step is integer-only, so the result does not depend on scheduling.
@@ -100,26 +101,26 @@ __device__ void find_b0(const uint32_t* hrow, int k, int* s_b0, int* s_above) {
 
 // ---------------------------------------------------------------- histogram of given scores
 
-// grid: (ceil(N / 2048), rows); block 256.
+// grid: (ceil(N / kExtractChunk), rows); block 256; 32 keys per thread.
 template <int KB>
 __global__ __launch_bounds__(256) void topk_hist_kernel(TopkDev P) {
   __shared__ uint32_t h[kBins];
   const int row = blockIdx.y;
   const int nv = visible(P, row);
   if (P.k >= nv) return;
-  const int start = blockIdx.x * 2048;
-  const int end = min(start + 2048, nv);
+  const int start = blockIdx.x * kExtractChunk;
+  const int end = min(start + kExtractChunk, nv);
   if (start >= end) return;
   for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
-  __syncthreads();
-  uint32_t key[8];
+  uint32_t key[32];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 32; ++u) {
     const int j = start + threadIdx.x + 256 * u;
     key[u] = j < end ? key_at<KB>(P, row, j) : 0u;
   }
+  __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int u = 0; u < 32; ++u)
     if (start + static_cast<int>(threadIdx.x) + 256 * u < end) atomicAdd(&h[key[u] >> (KB - 12)], 1u);
   __syncthreads();
   uint32_t* hrow = P.hist + static_cast<int64_t>(row) * kBins;
@@ -129,42 +130,66 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkDev P) {
 
 // ---------------------------------------------------------------- extract candidates
 
-// grid: (ceil(N / kExtractChunk), rows); block 256.
+// Exclusive prefix of one int per thread over 256 threads (thread order).
+__device__ __forceinline__ int block_scan_256(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += s_w[i];
+  total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// grid: (ceil(N / kExtractChunk), rows); block 256; 32 keys per thread, one global atomic
+// per block reserves the block's slots in the row's candidate list.
 template <int KB>
 __global__ __launch_bounds__(256) void topk_extract_kernel(TopkDev P) {
-  __shared__ int s_b0, s_above;
+  __shared__ int s_b0, s_above, s_w[4];
+  __shared__ uint32_t s_base;
   const int row = blockIdx.y;
   const int nv = visible(P, row);
   if (P.k >= nv) return;
   const int start = blockIdx.x * kExtractChunk;
   const int end = min(start + kExtractChunk, nv);
   if (start >= end) return;
+  uint32_t key[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    const int j = start + threadIdx.x + 256 * u;
+    key[u] = j < end ? key_at<KB>(P, row, j) : 0u;
+  }
   find_b0(P.hist + static_cast<int64_t>(row) * kBins, P.k, &s_b0, &s_above);
   __syncthreads();
   const uint32_t b0 = static_cast<uint32_t>(s_b0);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    const int j = start + threadIdx.x + 256 * u;
+    if (j < end && (key[u] >> (KB - 12)) >= b0) mask |= 1u << u;
+  }
+  int total;
+  const int before = block_scan_256(__popc(mask), s_w, total);
+  if (threadIdx.x == 0) s_base = atomicAdd(&P.cnt[row], static_cast<uint32_t>(total));
+  __syncthreads();
+  uint32_t slot = s_base + before;
   uint64_t* cand = P.cand + static_cast<int64_t>(row) * kCap;
-  const int lane = threadIdx.x & 63;
-  for (int base = start; base < end; base += 256 * 8) {
-    uint32_t key[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = base + threadIdx.x + 256 * u;
-      key[u] = j < end ? key_at<KB>(P, row, j) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = base + threadIdx.x + 256 * u;
-      const bool c = j < end && (key[u] >> (KB - 12)) >= b0;
-      const uint64_t m = __ballot(c);
-      if (m == 0) continue;
-      uint32_t slot0 = 0;
-      if (lane == 0) slot0 = atomicAdd(&P.cnt[row], static_cast<uint32_t>(__popcll(m)));
-      slot0 = __shfl(slot0, 0, kWave);
-      const uint32_t slot = slot0 + ballot_rank(m);
-      if (c && slot < static_cast<uint32_t>(kCap)) {
+  for (int u = 0; u < 32; ++u) {
+    if (mask & (1u << u)) {
+      if (slot < static_cast<uint32_t>(kCap)) {
         const uint32_t inv = KB == 16 ? (0xFFFFu - key[u]) : ~key[u];
-        cand[slot] = (static_cast<uint64_t>(inv) << 32) | static_cast<uint32_t>(j);
+        cand[slot] = (static_cast<uint64_t>(inv) << 32) |
+                     static_cast<uint32_t>(start + threadIdx.x + 256 * u);
       }
+      ++slot;
     }
   }
 }
@@ -247,14 +272,48 @@ __device__ void resolve_threshold(Get get, int n, uint32_t b0, int krem, uint32_
   }
 }
 
+// Pads an LDS list of n indices with never-smaller sentinels up to a multiple of 4.
+__device__ __forceinline__ void pad4(uint32_t* a, int n) {
+  if (threadIdx.x < 4 && n + static_cast<int>(threadIdx.x) < ((n + 3) & ~3))
+    a[n + threadIdx.x] = 0xFFFFFFFFu;
+}
+
+// Number of entries of the LDS list a[0..n) (padded to a multiple of 4) below j; 16-byte
+// broadcast reads and independent partial counts keep the loop issue-bound.
+__device__ __forceinline__ int count_below(const uint32_t* a, int n, uint32_t j) {
+  const u32x4* v = reinterpret_cast<const u32x4*>(a);
+  const int n4 = (n + 3) >> 2;
+  int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  int m = 0;
+  for (; m + 1 < n4; m += 2) {
+    const u32x4 x = v[m], y = v[m + 1];
+    c0 += (x[0] < j) + (y[0] < j);
+    c1 += (x[1] < j) + (y[1] < j);
+    c2 += (x[2] < j) + (y[2] < j);
+    c3 += (x[3] < j) + (y[3] < j);
+  }
+  if (m < n4) {
+    const u32x4 x = v[m];
+    c0 += x[0] < j;
+    c1 += x[1] < j;
+    c2 += x[2] < j;
+    c3 += x[3] < j;
+  }
+  return c0 + c1 + c2 + c3;
+}
+
 // grid: rows; block 1024.
 template <int KB>
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P) {
-  __shared__ uint64_t s_c[kCap];
-  __shared__ int32_t s_sel[4096];
+  __shared__ __align__(16) uint32_t s_key[kCap];
+  __shared__ __align__(16) uint32_t s_j[kCap];
+  __shared__ __align__(16) uint32_t s_tie[kCap + 4];
+  __shared__ __align__(16) uint32_t s_sel[4096 + 4];
   __shared__ uint32_t s_h[1024];
+  __shared__ uint32_t s_bcnt[1024];
+  __shared__ uint32_t s_bstart[1024];
   __shared__ int s_red[kResolveThreads / 64];
-  __shared__ int s_b0, s_above, s_need, s_nsel;
+  __shared__ int s_b0, s_above, s_need, s_nsel, s_ntie;
   __shared__ uint32_t s_T;
   const int row = blockIdx.x;
   const int nv = visible(P, row);
@@ -270,49 +329,67 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P
   const int C = static_cast<int>(P.cnt[row]);
 
   if (C <= kCap) {
-    // ---- candidates in LDS
+    // ---- candidates in LDS: keys and indices
     const uint64_t* cand = P.cand + static_cast<int64_t>(row) * kCap;
-    for (int i = threadIdx.x; i < C; i += kResolveThreads) s_c[i] = cand[i];
-    if (threadIdx.x == 0) s_nsel = 0;
+    for (int i = threadIdx.x; i < C; i += kResolveThreads) {
+      const uint64_t c = cand[i];
+      const uint32_t inv = static_cast<uint32_t>(c >> 32);
+      s_key[i] = KB == 16 ? (0xFFFFu - inv) : ~inv;
+      s_j[i] = static_cast<uint32_t>(c);
+    }
+    if (threadIdx.x == 0) {
+      s_nsel = 0;
+      s_ntie = 0;
+    }
     __syncthreads();
-    auto key_of = [&](int i) -> uint32_t {
-      const uint32_t inv = static_cast<uint32_t>(s_c[i] >> 32);
-      return KB == 16 ? (0xFFFFu - inv) : ~inv;
-    };
+    auto key_of = [&](int i) -> uint32_t { return s_key[i]; };
     resolve_threshold<KB>(key_of, C, b0, krem, s_h, &s_T, &s_need);
     const uint32_t T = s_T;
     const int need = s_need;
-    // count T-valued candidates; if more than needed, keep the lowest indices
-    int e = 0;
-    for (int i = threadIdx.x; i < C; i += kResolveThreads) e += key_of(i) == T;
-    const int E = block_sum_1024(e, s_red);
+    // keys above T are selected; T-valued ones go to the tie list
     for (int i = threadIdx.x; i < C; i += kResolveThreads) {
-      const uint32_t key = key_of(i);
-      bool sel = key > T;
-      if (key == T) {
-        if (E == need) {
-          sel = true;
-        } else {
-          const uint32_t j = static_cast<uint32_t>(s_c[i]);
-          int rank = 0;
-          for (int m = 0; m < C; ++m)
-            rank += key_of(m) == T && static_cast<uint32_t>(s_c[m]) < j;
-          sel = rank < need;
-        }
-      }
-      if (sel) {
-        const int slot = atomicAdd(&s_nsel, 1);
-        if (slot < 4096) s_sel[slot] = static_cast<int32_t>(static_cast<uint32_t>(s_c[i]));
-      }
+      const uint32_t key = s_key[i];
+      if (key > T) s_sel[atomicAdd(&s_nsel, 1) & 4095] = s_j[i];
+      else if (key == T) s_tie[atomicAdd(&s_ntie, 1)] = s_j[i];
+    }
+    __syncthreads();
+    const int E = s_ntie;
+    pad4(s_tie, E);
+    __syncthreads();
+    // the `need` lowest indices among the ties
+    for (int i = threadIdx.x; i < E; i += kResolveThreads) {
+      const uint32_t j = s_tie[i];
+      if (E == need || count_below(s_tie, E, j) < need) s_sel[atomicAdd(&s_nsel, 1) & 4095] = j;
     }
     __syncthreads();
     const int ns = min(s_nsel, P.k);
-    // ascending output: each index's rank among the selected
+    // ascending output: counting sort on the top (up to) 10 bits of the index, then each
+    // index's rank inside its bucket
+    const int bits = 32 - __clz(max(nv - 1, 1));
+    const int shift = bits > 10 ? bits - 10 : 0;
+    s_bcnt[threadIdx.x] = 0;
+    s_h[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < ns; i += kResolveThreads) atomicAdd(&s_bcnt[s_sel[i] >> shift], 1u);
+    __syncthreads();
+    int tot;
+    const uint32_t cnt_b = s_bcnt[threadIdx.x];
+    s_bstart[threadIdx.x] = block_scan_1024(static_cast<int>(cnt_b), s_red, tot);
+    __syncthreads();
     for (int i = threadIdx.x; i < ns; i += kResolveThreads) {
-      const int32_t j = s_sel[i];
+      const uint32_t j = s_sel[i];
+      const uint32_t b = j >> shift;
+      s_tie[s_bstart[b] + atomicAdd(&s_h[b], 1u)] = j;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < ns; i += kResolveThreads) {
+      const uint32_t j = s_tie[i];
+      const uint32_t b = j >> shift;
+      const int st = static_cast<int>(s_bstart[b]);
+      const int n = static_cast<int>(s_bcnt[b]);
       int rank = 0;
-      for (int m = 0; m < ns; ++m) rank += s_sel[m] < j;
-      out[rank] = j;
+      for (int m = st; m < st + n; ++m) rank += s_tie[m] < j;
+      out[st + rank] = static_cast<int32_t>(j);
     }
     return;
   }
@@ -384,12 +461,12 @@ hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t 
   P.idx = idx;
   if (plan.key_bits == 16) {
     if (need_hist)
-      topk_hist_kernel<16><<<dim3((plan.N + 2047) / 2048, plan.rows), 256, 0, s>>>(P);
+      topk_hist_kernel<16><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
     topk_extract_kernel<16><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
     topk_resolve_kernel<16><<<plan.rows, kResolveThreads, 0, s>>>(P);
   } else {
     if (need_hist)
-      topk_hist_kernel<32><<<dim3((plan.N + 2047) / 2048, plan.rows), 256, 0, s>>>(P);
+      topk_hist_kernel<32><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
     topk_extract_kernel<32><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
     topk_resolve_kernel<32><<<plan.rows, kResolveThreads, 0, s>>>(P);
   }

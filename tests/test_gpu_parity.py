@@ -195,7 +195,15 @@ def test_index_scores_and_topk(H, gpu, case):
     scores = torch.zeros(B * Nq, N, device=gpu, dtype=W.torch_dtype(case["sdt"]))
     idx = torch.empty(B, Nq, k, dtype=torch.int32, device=gpu)
     H.csa_index_topk(qt, wt, kt, N, ratio, pos0, k, sdt, idx, k_scales=kst, scores_out=scores)
+    # the split-phase calls give the same selection
+    ws = H.alloc_workspace(H.topk_workspace_size(sdt, B, Nq, N, k), gpu)
+    scores2 = torch.zeros_like(scores)
+    idx2 = torch.empty_like(idx)
+    H.topk_clear(sdt, B, Nq, N, k, ws)
+    H.csa_index_scores_hist(qt, wt, kt, N, ratio, pos0, k, scores2, ws, k_scales=kst)
+    H.topk_from_hist(scores2, B, Nq, N, ratio, pos0, k, idx2, ws)
     _sync()
+    assert torch.equal(scores, scores2) and torch.equal(idx, idx2)
     gs = f64(scores)
     gi = idx.cpu().numpy().reshape(B * Nq, k)
     for b in range(B):
