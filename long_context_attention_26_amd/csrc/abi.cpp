@@ -234,7 +234,7 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
   if (!aligned16(scores)) return fail(HCSA_EALIGN, "scores must be 16-byte aligned");
   return hip_status(hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
                                               k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                              pos0, score_dtype, scores, nullptr,
+                                              pos0, score_dtype, scores, nullptr, 0,
                                               static_cast<hipStream_t>(stream)),
                     "hcsa_csa_index_scores");
 }
@@ -269,7 +269,7 @@ int hcsa_csa_index_scores_hist(const void* q_idx, int q_dtype, const float* w_id
   return hip_status(hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
                                               k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
                                               pos0, score_dtype, scores,
-                                              static_cast<uint32_t*>(workspace),
+                                              static_cast<uint32_t*>(workspace), k,
                                               static_cast<hipStream_t>(stream)),
                     "hcsa_csa_index_scores_hist");
 }
@@ -315,7 +315,7 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (clear)");
   e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales,
                                 ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, score_dtype,
-                                scores, static_cast<uint32_t*>(tws), s);
+                                scores, static_cast<uint32_t*>(tws), k, s);
   if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (scores)");
   e = hcsa::launch_topk_select(plan, scores, N, Nq, ratio, pos0, topk_idx, tws, false, s);
   return hip_status(e, "hcsa_csa_index_topk (select)");

@@ -379,15 +379,27 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
     const int64_t ostride = static_cast<int64_t>(rows) * H * d;
     const float* po = part_o + (static_cast<int64_t>(row) * H + h) * d + c;
     float num = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      float w;
-      if (s < 1024) {
-        w = s_w[s];
-      } else {
-        const float l = pl[s * lstride];
-        w = (M == -INFINITY || l == -INFINITY) ? 0.0f : expf(l - M);
+    int s = 0;
+    if (splits <= 1024) {
+      // eight independent loads in flight; a zero weight multiplies a finite partial (empty
+      // splits store zeros), so no branch is needed
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (; s + 8 <= splits; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = po[(s + u) * ostride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(s_w[s + u], v[u], acc[u]);
       }
-      if (w != 0.0f) num = fmaf(w, po[s * ostride], num);
+      for (; s < splits; ++s) acc[0] = fmaf(s_w[s], po[s * ostride], acc[0]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) num += acc[u];
+    } else {
+      for (; s < splits; ++s) {
+        const float l = pl[s * lstride];
+        const float w = (M == -INFINITY || l == -INFINITY) ? 0.0f : expf(l - M);
+        if (w != 0.0f) num = fmaf(w, po[s * ostride], num);
+      }
     }
     out[(static_cast<int64_t>(row) * H + h) * d + c] = den > 0.0f ? num / den : 0.0f;
     if (c == 0) lse[static_cast<int64_t>(row) * H + h] = den > 0.0f ? M + logf(den) : -INFINITY;

@@ -12,6 +12,7 @@
 // ReLU, the head weights (fixed order g = 0..H_I-1) and writes the score.
 #include "common.h"
 #include "internal.h"
+#include "select_common.h"
 
 namespace hcsa {
 
@@ -26,7 +27,8 @@ struct IdxDev {
   int64_t pos0;
   void* scores;      // [rows][N]
   int chunk;
-  uint32_t* hist;    // optional [rows][4096] selector histogram (12-bit key digit)
+  uint32_t* hist;    // optional selector workspace (see select_common.h)
+  int topk;
 };
 
 // Keys per block: enough blocks to cover every CU several times even for one sequence,
@@ -74,13 +76,17 @@ __device__ __forceinline__ void hist_add(uint32_t* h, float s) {
     atomicAdd(&h[f32_key(__float_as_uint(s)) >> 20], 1u);
 }
 
-__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* g, int row) {
+// Flushes the block histogram into the row's and, in the row's last block, finds b0.
+__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* ws, int row, int nv,
+                                           int chunk, int k) {
   __syncthreads();
-  uint32_t* grow = g + static_cast<int64_t>(row) * kHistBins;
+  const SelState S = sel_state(ws, gridDim.y, 0);
+  uint32_t* grow = S.hist + static_cast<int64_t>(row) * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += 256) {
     const uint32_t v = h[i];
     if (v) atomicAdd(&grow[i], v);
   }
+  sel_finish_row(S, row, (nv + chunk - 1) / chunk, k);
 }
 
 // grid: (ceil(N / chunk), rows); block 256.
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
   const int grp = threadIdx.x / LPE;
   const int row_bytes = A.d_I * ES;
   __shared__ uint32_t s_hist[kHistBins];
-  const bool hist = A.hist != nullptr;
+  const bool hist = A.hist != nullptr && A.topk < nv;
   hist_clear(s_hist, hist);
 
   u32x4 qv[HI];
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
       }
     }
   }
-  if (hist) hist_flush(s_hist, A.hist, row);
+  if (hist) hist_flush(s_hist, A.hist, row, nv, A.chunk, A.topk);
 }
 
 template <int HI, int LPE, bool KBF16>
@@ -206,6 +212,7 @@ struct IdxMxDev {
   void* scores;
   int chunk;
   uint32_t* hist;
+  int topk;
 };
 
 // grid: (ceil(N / kChunk), rows); block 256.  LPE = d_I / 32 lanes per key.
@@ -230,7 +237,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
   __shared__ uint32_t s_q[16][4][8];
   __shared__ int s_qe[16][4];
   __shared__ uint32_t s_hist[kHistBins];
-  const bool hist = A.hist != nullptr;
+  const bool hist = A.hist != nullptr && A.topk < nv;
   if (hist)
     for (int i = threadIdx.x; i < kHistBins; i += 256) s_hist[i] = 0;
   if (threadIdx.x < HI * LPE) {
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
       }
     }
   }
-  if (hist) hist_flush(s_hist, A.hist, row);
+  if (hist) hist_flush(s_hist, A.hist, row, nv, A.chunk, A.topk);
 }
 
 template <int HI, int LPE, bool QBF16>
@@ -375,7 +382,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
                                      const uint8_t* kx, int64_t k_bstride, const uint8_t* ks,
                                      int64_t ks_bstride, int B, int Nq, int H_I, int d_I,
                                      int N, int ratio, int64_t pos0, int score_dtype,
-                                     void* scores, uint32_t* hist, hipStream_t s) {
+                                     void* scores, uint32_t* hist, int k, hipStream_t s) {
   IdxMxDev A;
   A.q = q;
   A.w = w;
@@ -391,6 +398,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
   A.hist = hist;
+  A.topk = k;
   if (q_dtype == 1) return launch_mx_q<true>(A, B * Nq, H_I, score_dtype, s);
   return launch_mx_q<false>(A, B * Nq, H_I, score_dtype, s);
 }
@@ -400,11 +408,11 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, int score_dtype, void* scores,
-                               uint32_t* hist, hipStream_t s) {
+                               uint32_t* hist, int k, hipStream_t s) {
   if (k_dtype == 2)
     return launch_mxfp4_index_scores(q, q_dtype, w, static_cast<const uint8_t*>(kx), k_bstride,
                                      ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0,
-                                     score_dtype, scores, hist, s);
+                                     score_dtype, scores, hist, k, s);
   IdxDev A;
   A.q = q;
   A.w = w;
@@ -418,6 +426,7 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
   A.hist = hist;
+  A.topk = k;
   const int rows = B * Nq;
   const int lpe = d_I * (k_dtype == 1 ? 2 : 4) / 16;
   if (k_dtype == 1) {

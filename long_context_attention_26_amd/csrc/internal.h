@@ -40,7 +40,7 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, int score_dtype, void* scores,
-                               uint32_t* hist, hipStream_t s);
+                               uint32_t* hist, int k, hipStream_t s);
 
 // ---- attention.hip
 struct AttnArgs {

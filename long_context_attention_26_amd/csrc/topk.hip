@@ -5,10 +5,10 @@
 // selector cheaper (9fzt.com digest, item 4).  Ties go to the lowest index and the output
 // is ascending, the reading taken where the pages are silent.
 //
-// Three steps after a 12-bit histogram of every row's keys (built by the indexer kernel
-// itself, or by topk_hist_kernel for caller-given scores):
-//   extract  many blocks per row: the histogram gives the 12-bit bin b0 holding the k-th
-//            largest key; every key in bins >= b0 is appended to the row's candidate list
+// Two steps after a 12-bit histogram of every row's keys, built by the indexer kernel
+// itself or by topk_hist_kernel for caller-given scores; the last block of each row to
+// finish its histogram finds the bin b0 holding the row's k-th largest key:
+//   extract  many blocks per row: every key in bins >= b0 is appended to the row's candidate list
 //            (one atomic per block reserves its slots; the list order does not matter).
 //            Typically about k + |bin b0| candidates.
 //   resolve  one block per row: with the candidates in LDS, the remaining key bits give
@@ -21,6 +21,7 @@
 // Every step is integer-only, so the result does not depend on scheduling.
 #include "common.h"
 #include "internal.h"
+#include "select_common.h"
 
 #include <algorithm>
 
@@ -28,8 +29,8 @@ namespace hcsa {
 
 namespace {
 
-constexpr int kBins = 4096;        // 12-bit first digit
-constexpr int kCap = 8192;         // candidates kept per row
+constexpr int kBins = kSelBins;    // 12-bit first digit
+constexpr int kCap = kSelCap;      // candidates kept per row
 constexpr int kExtractChunk = 8192;
 
 struct TopkDev {
@@ -37,9 +38,7 @@ struct TopkDev {
   int64_t row_stride;
   int Nq, N, ratio, k;
   int64_t pos0;
-  uint32_t* hist;       // [rows][kBins]
-  uint32_t* cnt;        // [rows]
-  uint64_t* cand;       // [rows][kCap]
+  SelState S;
   int32_t* idx;         // [rows][k]
 };
 
@@ -55,48 +54,6 @@ __device__ __forceinline__ int visible(const TopkDev& P, int row) {
   const int64_t p = P.pos0 + (row % P.Nq);
   const int64_t v = (p + 1) / P.ratio;
   return static_cast<int>(v < P.N ? v : P.N);
-}
-
-// Wave 0 finds the 12-bit bin b0 holding the k-th largest key: count(bins > b0) < k <=
-// count(bins >= b0).  Lane l owns bins 4095-64l .. 4032-64l.  Results go to LDS.
-__device__ void find_b0(const uint32_t* hrow, int k, int* s_b0, int* s_above) {
-  if (threadIdx.x >= kWave) return;
-  const int lane = threadIdx.x;
-  const int top = kBins - 1 - 64 * lane;
-  uint32_t sum = 0;
-  const u32x4* h4 = reinterpret_cast<const u32x4*>(hrow + top - 63);
-  u32x4 v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = h4[i];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) sum += v[i][0] + v[i][1] + v[i][2] + v[i][3];
-  uint32_t incl = sum;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
-  uint32_t above = incl - sum;
-  int found = -1, found_above = 0;
-  if (above < static_cast<uint32_t>(k) && incl >= static_cast<uint32_t>(k)) {
-    for (int b = 63; b >= 0; --b) {       // bins top .. top-63, descending
-      const uint32_t c = v[b >> 2][b & 3];
-      if (above + c >= static_cast<uint32_t>(k)) {
-        found = top - 63 + b;
-        found_above = static_cast<int>(above);
-        break;
-      }
-      above += c;
-    }
-  }
-  const uint64_t who = __ballot(found >= 0);
-  const int src = who ? __builtin_ctzll(who) : 0;
-  found = __shfl(found, src, kWave);
-  found_above = __shfl(found_above, src, kWave);
-  if (lane == 0) {
-    *s_b0 = found;
-    *s_above = found_above;
-  }
 }
 
 // ---------------------------------------------------------------- histogram of given scores
@@ -123,9 +80,10 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkDev P) {
   for (int u = 0; u < 32; ++u)
     if (start + static_cast<int>(threadIdx.x) + 256 * u < end) atomicAdd(&h[key[u] >> (KB - 12)], 1u);
   __syncthreads();
-  uint32_t* hrow = P.hist + static_cast<int64_t>(row) * kBins;
+  uint32_t* hrow = P.S.hist + static_cast<int64_t>(row) * kBins;
   for (int i = threadIdx.x; i < kBins; i += 256)
     if (h[i]) atomicAdd(&hrow[i], h[i]);
+  sel_finish_row(P.S, row, (nv + kExtractChunk - 1) / kExtractChunk, P.k);
 }
 
 // ---------------------------------------------------------------- extract candidates
@@ -152,7 +110,7 @@ __device__ __forceinline__ int block_scan_256(int v, int* s_w, int& total) {
 // per block reserves the block's slots in the row's candidate list.
 template <int KB>
 __global__ __launch_bounds__(256) void topk_extract_kernel(TopkDev P) {
-  __shared__ int s_b0, s_above, s_w[4];
+  __shared__ int s_w[4];
   __shared__ uint32_t s_base;
   const int row = blockIdx.y;
   const int nv = visible(P, row);
@@ -166,9 +124,7 @@ __global__ __launch_bounds__(256) void topk_extract_kernel(TopkDev P) {
     const int j = start + threadIdx.x + 256 * u;
     key[u] = j < end ? key_at<KB>(P, row, j) : 0u;
   }
-  find_b0(P.hist + static_cast<int64_t>(row) * kBins, P.k, &s_b0, &s_above);
-  __syncthreads();
-  const uint32_t b0 = static_cast<uint32_t>(s_b0);
+  const uint32_t b0 = static_cast<uint32_t>(P.S.b0info[2 * row]);
   uint32_t mask = 0;
 #pragma unroll
   for (int u = 0; u < 32; ++u) {
@@ -177,10 +133,10 @@ __global__ __launch_bounds__(256) void topk_extract_kernel(TopkDev P) {
   }
   int total;
   const int before = block_scan_256(__popc(mask), s_w, total);
-  if (threadIdx.x == 0) s_base = atomicAdd(&P.cnt[row], static_cast<uint32_t>(total));
+  if (threadIdx.x == 0) s_base = atomicAdd(&P.S.cnt[row], static_cast<uint32_t>(total));
   __syncthreads();
   uint32_t slot = s_base + before;
-  uint64_t* cand = P.cand + static_cast<int64_t>(row) * kCap;
+  uint64_t* cand = P.S.cand + static_cast<int64_t>(row) * kCap;
 #pragma unroll
   for (int u = 0; u < 32; ++u) {
     if (mask & (1u << u)) {
@@ -313,7 +269,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P
   __shared__ uint32_t s_bcnt[1024];
   __shared__ uint32_t s_bstart[1024];
   __shared__ int s_red[kResolveThreads / 64];
-  __shared__ int s_b0, s_above, s_need, s_nsel, s_ntie;
+  __shared__ int s_need, s_nsel, s_ntie;
   __shared__ uint32_t s_T;
   const int row = blockIdx.x;
   const int nv = visible(P, row);
@@ -322,15 +278,13 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P
     for (int j = threadIdx.x; j < P.k; j += kResolveThreads) out[j] = j < nv ? j : -1;
     return;
   }
-  find_b0(P.hist + static_cast<int64_t>(row) * kBins, P.k, &s_b0, &s_above);
-  __syncthreads();
-  const uint32_t b0 = static_cast<uint32_t>(s_b0);
-  const int krem = P.k - s_above;
-  const int C = static_cast<int>(P.cnt[row]);
+  const uint32_t b0 = static_cast<uint32_t>(P.S.b0info[2 * row]);
+  const int krem = P.k - P.S.b0info[2 * row + 1];
+  const int C = static_cast<int>(P.S.cnt[row]);
 
   if (C <= kCap) {
     // ---- candidates in LDS: keys and indices
-    const uint64_t* cand = P.cand + static_cast<int64_t>(row) * kCap;
+    const uint64_t* cand = P.S.cand + static_cast<int64_t>(row) * kCap;
     for (int i = threadIdx.x; i < C; i += kResolveThreads) {
       const uint64_t c = cand[i];
       const uint32_t inv = static_cast<uint32_t>(c >> 32);
@@ -431,14 +385,14 @@ TopkPlan plan_topk(int score_dtype, int rows, int N, int k) {
   p.key_bits = score_dtype == 1 ? 16 : 32;
   p.chunk = kExtractChunk;
   p.nchunks = N > 0 ? (N + p.chunk - 1) / p.chunk : 1;
-  p.hist_bytes = align256(static_cast<size_t>(rows) * (kBins + 1) * 4);   // hist + counter
+  p.hist_bytes = align256(sel_words(rows) * 4);                           // selector state
   p.count_bytes = align256(static_cast<size_t>(rows) * kCap * 8);         // candidates
   p.total_bytes = p.hist_bytes + p.count_bytes;
   return p;
 }
 
 hipError_t launch_topk_clear(const TopkPlan& plan, void* ws, hipStream_t s) {
-  const int64_t words = static_cast<int64_t>(plan.rows) * (kBins + 1);
+  const int64_t words = static_cast<int64_t>(sel_words(plan.rows));
   const int blocks = static_cast<int>(std::min<int64_t>((words + 255) / 256, 4096));
   fill_u32_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(ws), words, 0u);
   return hipGetLastError();
@@ -455,9 +409,7 @@ hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t 
   P.ratio = ratio;
   P.k = plan.k;
   P.pos0 = pos0;
-  P.hist = static_cast<uint32_t*>(ws);
-  P.cnt = P.hist + static_cast<int64_t>(plan.rows) * kBins;
-  P.cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + plan.hist_bytes);
+  P.S = sel_state(ws, plan.rows, plan.hist_bytes);
   P.idx = idx;
   if (plan.key_bits == 16) {
     if (need_hist)
