@@ -31,13 +31,6 @@ struct IdxDev {
   int topk;
 };
 
-// Keys per block: enough blocks to cover every CU several times even for one sequence,
-// and at least 256 keys so a block issues a few loads per lane.
-static int index_chunk(int rows, int N) {
-  int64_t c = static_cast<int64_t>(N) * rows / 2048;
-  c = (c + 255) / 256 * 256;
-  return static_cast<int>(c < 256 ? 256 : (c > 4096 ? 4096 : c));
-}
 
 __device__ __forceinline__ float dot16b_bf16(const u32x4& a, const u32x4& b, float acc) {
 #pragma unroll
@@ -76,17 +69,15 @@ __device__ __forceinline__ void hist_add(uint32_t* h, float s) {
     atomicAdd(&h[f32_key(__float_as_uint(s)) >> 20], 1u);
 }
 
-// Flushes the block histogram into the row's and, in the row's last block, finds b0.
-__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* ws, int row, int nv,
-                                           int chunk, int k) {
+// Flushes the block histogram into replica (block % copies) of the row's histogram.
+__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* ws, int row, int N) {
   __syncthreads();
-  const SelState S = sel_state(ws, gridDim.y, 0);
-  uint32_t* grow = S.hist + static_cast<int64_t>(row) * kHistBins;
+  const SelState S = sel_state(ws, gridDim.y, sel_copies(gridDim.y, N), 0);
+  uint32_t* grow = sel_hist_row(S, blockIdx.x % S.copies, row);
   for (int i = threadIdx.x; i < kHistBins; i += 256) {
     const uint32_t v = h[i];
     if (v) atomicAdd(&grow[i], v);
   }
-  sel_finish_row(S, row, (nv + chunk - 1) / chunk, k);
 }
 
 // grid: (ceil(N / chunk), rows); block 256.
@@ -158,7 +149,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
       }
     }
   }
-  if (hist) hist_flush(s_hist, A.hist, row, nv, A.chunk, A.topk);
+  if (hist) hist_flush(s_hist, A.hist, row, A.N);
 }
 
 template <int HI, int LPE, bool KBF16>
@@ -340,7 +331,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
       }
     }
   }
-  if (hist) hist_flush(s_hist, A.hist, row, nv, A.chunk, A.topk);
+  if (hist) hist_flush(s_hist, A.hist, row, A.N);
 }
 
 template <int HI, int LPE, bool QBF16>

@@ -21,7 +21,7 @@ hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int D
 
 // ---- topk.hip
 struct TopkPlan {
-  int rows, N, k, key_bits, chunk, nchunks;
+  int rows, N, k, key_bits, chunk, nchunks, copies;
   size_t hist_bytes, count_bytes, total_bytes;
 };
 TopkPlan plan_topk(int score_dtype, int rows, int N, int k);

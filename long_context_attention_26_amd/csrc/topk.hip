@@ -5,12 +5,13 @@
 // selector cheaper (9fzt.com digest, item 4).  Ties go to the lowest index and the output
 // is ascending, the reading taken where the pages are silent.
 //
-// Two steps after a 12-bit histogram of every row's keys, built by the indexer kernel
-// itself or by topk_hist_kernel for caller-given scores; the last block of each row to
-// finish its histogram finds the bin b0 holding the row's k-th largest key:
-//   extract  many blocks per row: every key in bins >= b0 is appended to the row's candidate list
-//            (one atomic per block reserves its slots; the list order does not matter).
-//            Typically about k + |bin b0| candidates.
+// After a 12-bit histogram of every row's keys (built by the indexer kernel itself, or by
+// topk_hist_kernel for caller-given scores; block i of a row adds into replica i % copies):
+//   b0       one block per row sums the replicas and finds the bin b0 holding the row's
+//            k-th largest key.
+//   extract  many blocks per row: every key in bins >= b0 is appended to a replica's
+//            candidate list (one atomic per block reserves its slots; list order does not
+//            matter).  Typically about k + |bin b0| candidates.
 //   resolve  one block per row: with the candidates in LDS, the remaining key bits give
 //            the exact threshold key T and how many T-valued entries to keep; ties keep the
 //            lowest indices (each tie's rank among the ties is counted); the k selected
@@ -30,7 +31,7 @@ namespace hcsa {
 namespace {
 
 constexpr int kBins = kSelBins;    // 12-bit first digit
-constexpr int kCap = kSelCap;      // candidates kept per row
+constexpr int kCap = kSelCap;      // candidates kept per row (over all replicas)
 constexpr int kExtractChunk = 8192;
 
 struct TopkDev {
@@ -54,6 +55,24 @@ __device__ __forceinline__ int visible(const TopkDev& P, int row) {
   const int64_t p = P.pos0 + (row % P.Nq);
   const int64_t v = (p + 1) / P.ratio;
   return static_cast<int>(v < P.N ? v : P.N);
+}
+
+// Exclusive prefix of one int per thread over 256 threads (thread order).
+__device__ __forceinline__ int block_scan_256(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += s_w[i];
+  total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+  __syncthreads();
+  return before + incl - v;
 }
 
 // ---------------------------------------------------------------- histogram of given scores
@@ -80,34 +99,55 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkDev P) {
   for (int u = 0; u < 32; ++u)
     if (start + static_cast<int>(threadIdx.x) + 256 * u < end) atomicAdd(&h[key[u] >> (KB - 12)], 1u);
   __syncthreads();
-  uint32_t* hrow = P.S.hist + static_cast<int64_t>(row) * kBins;
+  uint32_t* hrow = sel_hist_row(P.S, blockIdx.x % P.S.copies, row);
   for (int i = threadIdx.x; i < kBins; i += 256)
     if (h[i]) atomicAdd(&hrow[i], h[i]);
-  sel_finish_row(P.S, row, (nv + kExtractChunk - 1) / kExtractChunk, P.k);
+}
+
+// ---------------------------------------------------------------- threshold bin per row
+
+// grid: rows; block 256.  Sums the replicas and finds the 12-bit bin b0 holding the k-th
+// largest key: count(bins > b0) < k <= count(bins >= b0).  Thread t owns the 16 bins
+// 4095-16t .. 4080-16t (thread 0 the top ones).
+__global__ __launch_bounds__(256) void topk_b0_kernel(TopkDev P) {
+  __shared__ int s_w[4];
+  const int row = blockIdx.x;
+  const int nv = visible(P, row);
+  if (P.k >= nv) return;
+  const int lo = kBins - 16 * (threadIdx.x + 1);
+  uint32_t v[16];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) v[b] = 0;
+  for (int c = 0; c < P.S.copies; ++c) {
+    const u32x4* h4 = reinterpret_cast<const u32x4*>(sel_hist_row(P.S, c, row) + lo);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 x = h4[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] += x[e];
+    }
+  }
+  int sum = 0;
+#pragma unroll
+  for (int b = 0; b < 16; ++b) sum += static_cast<int>(v[b]);
+  int total;
+  int above = block_scan_256(sum, s_w, total);
+  if (above < P.k && above + sum >= P.k) {
+    for (int b = 15; b >= 0; --b) {
+      if (above + static_cast<int>(v[b]) >= P.k) {
+        P.S.b0info[2 * row] = lo + b;
+        P.S.b0info[2 * row + 1] = above;
+        break;
+      }
+      above += static_cast<int>(v[b]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- extract candidates
 
-// Exclusive prefix of one int per thread over 256 threads (thread order).
-__device__ __forceinline__ int block_scan_256(int v, int* s_w, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
-  if (lane == kWave - 1) s_w[w] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += s_w[i];
-  total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
-  __syncthreads();
-  return before + incl - v;
-}
-
-// grid: (ceil(N / kExtractChunk), rows); block 256; 32 keys per thread, one global atomic
-// per block reserves the block's slots in the row's candidate list.
+// grid: (ceil(N / kExtractChunk), rows); block 256; 32 keys per thread.  One atomic per
+// block (on its replica's counter) reserves the block's slots in the replica's list.
 template <int KB>
 __global__ __launch_bounds__(256) void topk_extract_kernel(TopkDev P) {
   __shared__ int s_w[4];
@@ -133,14 +173,16 @@ __global__ __launch_bounds__(256) void topk_extract_kernel(TopkDev P) {
   }
   int total;
   const int before = block_scan_256(__popc(mask), s_w, total);
-  if (threadIdx.x == 0) s_base = atomicAdd(&P.S.cnt[row], static_cast<uint32_t>(total));
+  const int copy = blockIdx.x % P.S.copies;
+  if (threadIdx.x == 0)
+    s_base = total ? atomicAdd(&P.S.cnt[copy * P.S.rows + row], static_cast<uint32_t>(total)) : 0u;
   __syncthreads();
   uint32_t slot = s_base + before;
-  uint64_t* cand = P.S.cand + static_cast<int64_t>(row) * kCap;
+  uint64_t* cand = P.S.cand + (static_cast<int64_t>(row) * P.S.copies + copy) * P.S.capc;
 #pragma unroll
   for (int u = 0; u < 32; ++u) {
     if (mask & (1u << u)) {
-      if (slot < static_cast<uint32_t>(kCap)) {
+      if (slot < static_cast<uint32_t>(P.S.capc)) {
         const uint32_t inv = KB == 16 ? (0xFFFFu - key[u]) : ~key[u];
         cand[slot] = (static_cast<uint64_t>(inv) << 32) |
                      static_cast<uint32_t>(start + threadIdx.x + 256 * u);
@@ -280,16 +322,27 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P
   }
   const uint32_t b0 = static_cast<uint32_t>(P.S.b0info[2 * row]);
   const int krem = P.k - P.S.b0info[2 * row + 1];
-  const int C = static_cast<int>(P.S.cnt[row]);
+  int C = 0;
+  bool overflow = false;
+  for (int c = 0; c < P.S.copies; ++c) {
+    const int n = static_cast<int>(P.S.cnt[c * P.S.rows + row]);
+    overflow |= n > P.S.capc;
+    C += n;
+  }
 
-  if (C <= kCap) {
-    // ---- candidates in LDS: keys and indices
-    const uint64_t* cand = P.S.cand + static_cast<int64_t>(row) * kCap;
-    for (int i = threadIdx.x; i < C; i += kResolveThreads) {
-      const uint64_t c = cand[i];
-      const uint32_t inv = static_cast<uint32_t>(c >> 32);
-      s_key[i] = KB == 16 ? (0xFFFFu - inv) : ~inv;
-      s_j[i] = static_cast<uint32_t>(c);
+  if (!overflow) {
+    // ---- candidates of every replica into LDS: keys and indices
+    int off = 0;
+    for (int c = 0; c < P.S.copies; ++c) {
+      const int n = static_cast<int>(P.S.cnt[c * P.S.rows + row]);
+      const uint64_t* cand = P.S.cand + (static_cast<int64_t>(row) * P.S.copies + c) * P.S.capc;
+      for (int i = threadIdx.x; i < n; i += kResolveThreads) {
+        const uint64_t x = cand[i];
+        const uint32_t inv = static_cast<uint32_t>(x >> 32);
+        s_key[off + i] = KB == 16 ? (0xFFFFu - inv) : ~inv;
+        s_j[off + i] = static_cast<uint32_t>(x);
+      }
+      off += n;
     }
     if (threadIdx.x == 0) {
       s_nsel = 0;
@@ -385,14 +438,19 @@ TopkPlan plan_topk(int score_dtype, int rows, int N, int k) {
   p.key_bits = score_dtype == 1 ? 16 : 32;
   p.chunk = kExtractChunk;
   p.nchunks = N > 0 ? (N + p.chunk - 1) / p.chunk : 1;
-  p.hist_bytes = align256(sel_words(rows) * 4);                           // selector state
+  p.copies = sel_copies(rows, N);
+  p.hist_bytes = align256(sel_words(rows, p.copies) * 4);                 // selector words
   p.count_bytes = align256(static_cast<size_t>(rows) * kCap * 8);         // candidates
   p.total_bytes = p.hist_bytes + p.count_bytes;
   return p;
 }
 
+SelState topk_sel_state(const TopkPlan& plan, void* ws) {
+  return sel_state(ws, plan.rows, plan.copies, plan.hist_bytes);
+}
+
 hipError_t launch_topk_clear(const TopkPlan& plan, void* ws, hipStream_t s) {
-  const int64_t words = static_cast<int64_t>(sel_words(plan.rows));
+  const int64_t words = static_cast<int64_t>(sel_words(plan.rows, plan.copies));
   const int blocks = static_cast<int>(std::min<int64_t>((words + 255) / 256, 4096));
   fill_u32_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(ws), words, 0u);
   return hipGetLastError();
@@ -409,17 +467,18 @@ hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t 
   P.ratio = ratio;
   P.k = plan.k;
   P.pos0 = pos0;
-  P.S = sel_state(ws, plan.rows, plan.hist_bytes);
+  P.S = topk_sel_state(plan, ws);
   P.idx = idx;
+  const dim3 grid(plan.nchunks, plan.rows);
   if (plan.key_bits == 16) {
-    if (need_hist)
-      topk_hist_kernel<16><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
-    topk_extract_kernel<16><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
+    if (need_hist) topk_hist_kernel<16><<<grid, 256, 0, s>>>(P);
+    topk_b0_kernel<<<plan.rows, 256, 0, s>>>(P);
+    topk_extract_kernel<16><<<grid, 256, 0, s>>>(P);
     topk_resolve_kernel<16><<<plan.rows, kResolveThreads, 0, s>>>(P);
   } else {
-    if (need_hist)
-      topk_hist_kernel<32><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
-    topk_extract_kernel<32><<<dim3(plan.nchunks, plan.rows), 256, 0, s>>>(P);
+    if (need_hist) topk_hist_kernel<32><<<grid, 256, 0, s>>>(P);
+    topk_b0_kernel<<<plan.rows, 256, 0, s>>>(P);
+    topk_extract_kernel<32><<<grid, 256, 0, s>>>(P);
     topk_resolve_kernel<32><<<plan.rows, kResolveThreads, 0, s>>>(P);
   }
   return hipGetLastError();
