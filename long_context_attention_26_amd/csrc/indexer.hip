@@ -334,6 +334,152 @@ __global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
   if (hist) hist_flush(s_hist, A.hist, row, A.N);
 }
 
+// MXFP4 keys on the matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1 operands and
+// e8m0 scales per 32 channels computes D[head][key] for 32 keys at once (A = the quantized
+// query heads as rows, B = the keys as columns), so the e2m1 codes are never unpacked.
+// Operand lane layout (measured): lane l holds row/column l % 32 and the 32 channels
+// 32*(l/32) .. +31 of one 64-channel step, channel e in bits 4e..4e+3 (the stored packing:
+// element 2i in the low nibble of byte i); the scale operand's low byte is that block's
+// e8m0 scale; D register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// grid: (ceil(N / chunk), rows); block 256 (4 waves, 32 keys per MFMA).
+template <int HI, bool QBF16, bool SBF16>
+__global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
+  constexpr int U = 4;
+  const int row = blockIdx.y;
+  const int b = row / A.Nq;
+  const int64_t p = A.pos0 + (row % A.Nq);
+  const int64_t nv64 = (p + 1) / A.ratio;
+  const int nv = static_cast<int>(nv64 < A.N ? nv64 : A.N);
+  const int start = blockIdx.x * A.chunk;
+  const int end = min(start + A.chunk, nv);
+  if (start >= end) return;
+  __shared__ uint32_t s_hist[kHistBins];
+  const bool hist = A.hist != nullptr && A.topk < nv;
+  hist_clear(s_hist, hist);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int ksteps = A.d_I > 64 ? A.d_I / 64 : 1;       // 64-channel MFMA steps
+  const int nblk = A.d_I / 32;                          // 32-channel scale blocks per row
+
+  // A operand: this lane's head (col) and block (2*step + half), quantized here.
+  i32x8 qa[2];
+  int qs[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    qa[st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    qs[st] = 127;
+    const int blk = 2 * st + half;
+    if (st < ksteps && col < HI && blk < nblk) {
+      const int64_t off = (static_cast<int64_t>(row) * HI + col) * A.d_I + blk * 32;
+      float v[32];
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        v[e] = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[off + e])
+                     : static_cast<const float*>(A.q)[off + e];
+        amax = fmaxf(amax, __builtin_fabsf(v[e]));
+      }
+      const int se = mx_scale_exp(amax);
+      qs[st] = se + 127;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= e2m1_code(v[8 * d + e], se) << (4 * e);
+        qa[st][d] = static_cast<int>(w);
+      }
+    }
+  }
+  float w[HI];
+#pragma unroll
+  for (int g = 0; g < HI; ++g) w[g] = A.w[static_cast<int64_t>(row) * HI + g];
+
+  const int rowb = A.d_I / 2;
+  const uint8_t* kbase = A.k + b * A.k_bstride;
+  const uint8_t* sbase = A.ks + b * A.ks_bstride;
+  float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
+  uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
+
+  for (int j0 = start + wave * 32; j0 < end; j0 += 4 * 32 * U) {
+    i32x8 kb[U][2];
+    int ksc[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * 128 + col;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        kb[u][st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        ksc[u][st] = 127;
+        const int blk = 2 * st + half;
+        if (st < ksteps && blk < nblk && j < end) {
+          const u32x4 c = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * rowb + blk * 16));
+          kb[u][st][0] = static_cast<int>(c[0]);
+          kb[u][st][1] = static_cast<int>(c[1]);
+          kb[u][st][2] = static_cast<int>(c[2]);
+          kb[u][st][3] = static_cast<int>(c[3]);
+          ksc[u][st] = sbase[static_cast<int64_t>(j) * nblk + blk];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u * 128 >= end) break;                 // wave-uniform
+      f32x16 d = {};
+      d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0], kb[u][0], d, 4, 4, 0, qs[0],
+                                                          0, ksc[u][0]);
+      if (ksteps > 1)
+        d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1], kb[u][1], d, 4, 4, 0,
+                                                            qs[1], 0, ksc[u][1]);
+      // rows (heads) held by this lane: 8*(r/4) + 4*half + r%4
+      float part = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int g = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (g < HI) part = fmaf(w[g], fmaxf(d[r], 0.0f), part);
+      }
+      if constexpr (HI > 4) part += __shfl_xor(part, 32, kWave);
+      const int j = j0 + u * 128 + col;
+      if (half == 0 && j < end) {
+        const float s = part + 0.0f;
+        if constexpr (SBF16)
+          s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+        else
+          s32[j] = s;
+        if (hist) hist_add<SBF16>(s_hist, s);
+      }
+    }
+  }
+  if (hist) hist_flush(s_hist, A.hist, row, A.N);
+}
+
+template <int HI, bool QBF16>
+hipError_t launch_mx_mfma_hi(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
+  const int nchunks = (A.N + A.chunk - 1) / A.chunk;
+  dim3 grid(nchunks, rows);
+  if (score_dtype == 1)
+    index_scores_mx_mfma_kernel<HI, QBF16, true><<<grid, 256, 0, s>>>(A);
+  else
+    index_scores_mx_mfma_kernel<HI, QBF16, false><<<grid, 256, 0, s>>>(A);
+  return hipGetLastError();
+}
+
+template <bool QBF16>
+hipError_t launch_mx_mfma(const IdxMxDev& A, int rows, int H_I, int score_dtype, hipStream_t s) {
+  switch (H_I) {
+    case 1: return launch_mx_mfma_hi<1, QBF16>(A, rows, score_dtype, s);
+    case 2: return launch_mx_mfma_hi<2, QBF16>(A, rows, score_dtype, s);
+    case 4: return launch_mx_mfma_hi<4, QBF16>(A, rows, score_dtype, s);
+    case 8: return launch_mx_mfma_hi<8, QBF16>(A, rows, score_dtype, s);
+    case 16: return launch_mx_mfma_hi<16, QBF16>(A, rows, score_dtype, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int HI, int LPE, bool QBF16>
 hipError_t launch_mx_hi(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
@@ -390,8 +536,8 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.chunk = index_chunk(B * Nq, N);
   A.hist = hist;
   A.topk = k;
-  if (q_dtype == 1) return launch_mx_q<true>(A, B * Nq, H_I, score_dtype, s);
-  return launch_mx_q<false>(A, B * Nq, H_I, score_dtype, s);
+  if (q_dtype == 1) return launch_mx_mfma<true>(A, B * Nq, H_I, score_dtype, s);
+  return launch_mx_mfma<false>(A, B * Nq, H_I, score_dtype, s);
 }
 
 
