@@ -228,11 +228,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
   float l_run = 0.0f;
   const float sl2 = A.scale * 1.4426950408889634f;  // logits in base 2
 
-  // One step = 32 keys.  K rows (keys base + col, base + 16 + col) feed the A operand of
-  // S^T = K Q^T; each lane also reads channels 8col..8col+7 of the V rows of its 8 keys
-  // (base + 4g + j for j < 4, base + 16 + 4g + j - 4 otherwise).  The next step's rows are
-  // loaded before the current step's MFMAs (software pipeline).
-  auto load_step = [&](int base, u32x4 (&ka)[2][4], u32x4 (&vv)[8], bool (&ok)[8]) {
+  for (int base = wave * 32; base < cnt; base += 128) {
+    // ---- K rows for the A operand: keys base + col and base + 16 + col
+    u32x4 ka[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int pos = base + 16 * t + col;
@@ -246,6 +244,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
         for (int s = 0; s < 4; ++s) ka[t][s] = u32x4{0, 0, 0, 0};
       }
     }
+    // ---- V slices: keys base + 4g + j (j<4) and base + 16 + 4g + (j-4), channels 8col..8col+7
+    u32x4 vv[8];
+    bool ok[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int pos = base + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
@@ -256,13 +257,6 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
       else
         vv[j] = u32x4{0, 0, 0, 0};
     }
-  };
-  u32x4 ka[2][4], vv[8], kan[2][4], vvn[8];
-  bool ok[8], okn[8];
-  int base = wave * 32;
-  if (base < cnt) load_step(base, ka, vv, ok);
-  for (; base < cnt; base += 128) {
-    if (base + 128 < cnt) load_step(base + 128, kan, vvn, okn);
     // ---- S^T tiles: lane holds logits of keys (tile t, 4g + i) for head col
     f32x4 st[2];
 #pragma unroll
@@ -280,41 +274,31 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
     mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
     const float m_new = fmaxf(m_run, mt);
-    if (m_new != -INFINITY) {                 // uniform: validity is per key, shared by heads
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      float pj[8];
-      float psum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pj[j] = exp2f(lg[j] - m_new);
-        psum += pj[j];
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-      u32x4 pB;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) pB[m] = pack_bf16x2(pj[2 * m], pj[2 * m + 1]);
-      // ---- O^T tiles: channel 8*i + t for tile t, row i
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 va;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          va[m] = __builtin_amdgcn_perm(vv[2 * m + 1][t >> 1], vv[2 * m][t >> 1], sel);
-        acc[t] = mfma16x16x32(va, pB, acc[t]);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ka[t][s] = kan[t][s];
+    if (m_new == -INFINITY) continue;      // nothing visible yet for this head
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float pj[8];
+    float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      vv[j] = vvn[j];
-      ok[j] = okn[j];
+      pj[j] = exp2f(lg[j] - m_new);
+      psum += pj[j];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    u32x4 pB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pB[m] = pack_bf16x2(pj[2 * m], pj[2 * m + 1]);
+    // ---- O^T tiles: channel 8*i + t for tile t, row i
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 va;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        va[m] = __builtin_amdgcn_perm(vv[2 * m + 1][t >> 1], vv[2 * m][t >> 1], sel);
+      acc[t] = mfma16x16x32(va, pB, acc[t]);
     }
   }
 

@@ -114,8 +114,8 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
   float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
   uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
 
-  // software pipeline: the next group of rows is loaded while the current one is reduced
-  auto load_rows = [&](int j0, u32x4 (&kv)[U]) {
+  for (int j0 = start + grp; j0 < end; j0 += GROUPS * U) {
+    u32x4 kv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * GROUPS;
@@ -125,13 +125,6 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
       else
         kv[u] = u32x4{0, 0, 0, 0};
     }
-  };
-  u32x4 kv[U], kvn[U];
-  int j0 = start + grp;
-  // the loop bound is uniform per group of LPE lanes (the cross-lane reduction stays inside it)
-  if (j0 < end) load_rows(j0, kv);
-  for (; j0 < end; j0 += GROUPS * U) {
-    if (j0 + GROUPS * U < end) load_rows(j0 + GROUPS * U, kvn);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float part[HI];
@@ -155,8 +148,6 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
         if (hist) hist_add<SBF16>(s_hist, s);
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) kv[u] = kvn[u];
   }
   if (hist) hist_flush(s_hist, A.hist, row, A.N);
 }
@@ -413,8 +404,9 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
   uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
 
-  // software pipeline: the next tile's loads are issued before the current tile's MFMAs
-  auto load_tile = [&](int j0, i32x8 (&kb)[U][2], int (&ksc)[U][2]) {
+  for (int j0 = start + wave * 32; j0 < end; j0 += 4 * 32 * U) {
+    i32x8 kb[U][2];
+    int ksc[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * 128 + col;
@@ -434,14 +426,6 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
         }
       }
     }
-  };
-  constexpr int STRIDE = 4 * 32 * U;
-  i32x8 kb[U][2], kbn[U][2];
-  int ksc[U][2], kscn[U][2];
-  int j0 = start + wave * 32;
-  if (j0 < end) load_tile(j0, kb, ksc);
-  for (; j0 < end; j0 += STRIDE) {
-    if (j0 + STRIDE < end) load_tile(j0 + STRIDE, kbn, kscn);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u * 128 >= end) break;                 // wave-uniform
@@ -469,13 +453,6 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
         if (hist) hist_add<SBF16>(s_hist, s);
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        kb[u][st] = kbn[u][st];
-        ksc[u][st] = kscn[u][st];
-      }
   }
   if (hist) hist_flush(s_hist, A.hist, row, A.N);
 }
