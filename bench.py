@@ -103,7 +103,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, help="workload id (1..5); default 3")
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload id (1..5); default 5: decode, batch 32, 1M-token context")
     ap.add_argument("--rotate", type=int, default=0, help="cache copies (0 = enough to defeat the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

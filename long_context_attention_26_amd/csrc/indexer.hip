@@ -347,7 +347,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 // grid: (ceil(N / chunk), rows); block 256 (4 waves, 32 keys per MFMA).
 template <int HI, bool QBF16, bool SBF16>
 __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
-  constexpr int U = 8;
+  constexpr int U = 4;
   const int row = blockIdx.y;
   const int b = row / A.Nq;
   const int64_t p = A.pos0 + (row % A.Nq);
