@@ -74,6 +74,14 @@ int hcsa_version(void);
 const char *hcsa_last_error(void);
 
 /*
+ * Kernel timing for benchmarks and profiling: the next indexer-score kernel launched by
+ * this thread (hcsa_csa_index_scores, _hist or _topk) records start_event and stop_event
+ * (hipEvent_t, timing enabled) as part of its own dispatch, so their elapsed time is the
+ * kernel's execution alone.  NULL, NULL cancels.  Not for use under graph capture.
+ */
+int hcsa_time_next_indexer(void *start_event, void *stop_event);
+
+/*
  * Block pooling (CSA m = 4, HCA m' = 128, indexer keys m = 4)
  * [Lighthouse section 八 item 3; tulong.co 技术架构创新 item 1].
  *

@@ -73,6 +73,13 @@ extern "C" {
 
 int hcsa_version(void) { return 100; }
 
+int hcsa_time_next_indexer(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(HCSA_EINVAL, "give both events or neither");
+  hcsa::time_next_indexer(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+  return ok();
+}
+
 const char* hcsa_last_error(void) { return g_err.c_str(); }
 
 static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,

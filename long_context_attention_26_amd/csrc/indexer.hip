@@ -11,12 +11,34 @@
 // fma), the group reduces them with cross-lane adds, and the group's first lane applies
 // ReLU, the head weights (fixed order g = 0..H_I-1) and writes the score.
 #include "common.h"
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 #include "select_common.h"
 
 namespace hcsa {
 
+// Optional timing of the next indexer kernel launched on this thread: the dispatch itself
+// records the start and stop events (hipExtLaunchKernel), so the measured interval is the
+// kernel's own execution.
+static thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void time_next_indexer(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
+}
+
 namespace {
+
+template <typename K, typename... Args>
+void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  if (t_ev_start != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t_ev_start, t_ev_stop, 0, args...);
+    t_ev_start = t_ev_stop = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+}
 
 struct IdxDev {
   const void* q;     // [rows][H_I][d_I]
@@ -157,9 +179,9 @@ hipError_t launch_hi(const IdxDev& A, int rows, int score_dtype, hipStream_t s) 
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
   dim3 grid(nchunks, rows);
   if (score_dtype == 1)
-    index_scores_kernel<HI, LPE, KBF16, true><<<grid, 256, 0, s>>>(A);
+    launch_timed(index_scores_kernel<HI, LPE, KBF16, true>, grid, dim3(256), s, A);
   else
-    index_scores_kernel<HI, LPE, KBF16, false><<<grid, 256, 0, s>>>(A);
+    launch_timed(index_scores_kernel<HI, LPE, KBF16, false>, grid, dim3(256), s, A);
   return hipGetLastError();
 }
 
@@ -462,9 +484,9 @@ hipError_t launch_mx_mfma_hi(const IdxMxDev& A, int rows, int score_dtype, hipSt
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
   dim3 grid(nchunks, rows);
   if (score_dtype == 1)
-    index_scores_mx_mfma_kernel<HI, QBF16, true><<<grid, 256, 0, s>>>(A);
+    launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true>, grid, dim3(256), s, A);
   else
-    index_scores_mx_mfma_kernel<HI, QBF16, false><<<grid, 256, 0, s>>>(A);
+    launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false>, grid, dim3(256), s, A);
   return hipGetLastError();
 }
 

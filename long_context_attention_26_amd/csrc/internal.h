@@ -42,6 +42,8 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int ratio, int64_t pos0, int score_dtype, void* scores,
                                uint32_t* hist, int k, hipStream_t s);
 
+void time_next_indexer(hipEvent_t start, hipEvent_t stop);
+
 // ---- attention.hip
 struct AttnArgs {
   const void* q;

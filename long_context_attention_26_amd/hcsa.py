@@ -23,6 +23,7 @@ _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_
 _SIGS = {
     "hcsa_version": (_i, []),
     "hcsa_last_error": (ctypes.c_char_p, []),
+    "hcsa_time_next_indexer": (_i, [_p, _p]),
     "hcsa_compress_kv": (_i, [_p, _i, _i64, _i, _i, _i, _p, _i, _p, _i, _i64, _p, _i64, _p]),
     "hcsa_compress_kv_batched": (_i, [_p, _i, _i, _p]),
     "hcsa_mxfp4_quantize": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
@@ -89,6 +90,15 @@ def _ptr(t):
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def time_next_indexer(start_event, stop_event):
+    """The next indexer kernel launched by this thread records these torch.cuda.Events
+    (timing enabled) as part of its dispatch."""
+    for e in (start_event, stop_event):
+        if e.cuda_event == 0:
+            e.record()          # creates the underlying event
+    _check(lib.hcsa_time_next_indexer(start_event.cuda_event, stop_event.cuda_event))
 
 
 def alloc_workspace(nbytes, device):
