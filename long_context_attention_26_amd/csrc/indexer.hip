@@ -51,6 +51,7 @@ struct IdxDev {
   int chunk;
   uint32_t* hist;    // optional selector workspace (see select_common.h)
   int topk;
+  int rows_total;    // B*Nq*H_I (prefill GEMM)
 };
 
 
@@ -172,6 +173,92 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
     }
   }
   if (hist) hist_flush(s_hist, A.hist, row, A.N);
+}
+
+// ------------------------------------------------------------------ prefill GEMM
+// Many query tokens per sequence (chunked prefill): the indexer is a GEMM
+// [Nq*H_I x d_I] x [d_I x N] on v_mfma_f32_32x32x16_bf16.  A wave owns 32 rows (32/H_I query
+// tokens x H_I heads, operand A kept in registers) and walks its block's key range 32 keys
+// at a time (operand B loaded straight from global; the block's 4 waves read the same keys,
+// so most loads hit the L1/L2).  Output lane layout: register r of lane l holds row
+// 8*(r/4) + 4*(l/32) + r%4 and key l%32, so the H_I <= 4 heads of a query token sit in
+// consecutive registers of one lane and the ReLU / weight / head-sum epilogue is lane-local.
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16g;
+
+template <int HI, bool SBF16>
+__global__ __launch_bounds__(256) void index_scores_gemm_kernel(IdxDev A) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.y) * 4 + wave) * 32;   // first row of the wave
+  const int q_first = static_cast<int>(row0 / HI);             // first query row (b*Nq + i)
+  const int rows_total = A.rows_total;                          // B*Nq*H_I
+  if (row0 >= rows_total) return;
+  const int b = q_first / A.Nq;                                 // whole wave in one sequence
+  const int kstart = blockIdx.x * A.chunk;
+  const int kend = min(kstart + A.chunk, A.N);
+  // visible keys of the wave's last query token bound the keys worth computing
+  const int q_last = q_first + 32 / HI - 1;
+  const int64_t p_last = A.pos0 + (q_last % A.Nq);
+  const int64_t nv_last64 = (p_last + 1) / A.ratio;
+  const int nv_last = static_cast<int>(nv_last64 < A.N ? nv_last64 : A.N);
+  const int kstop = min(kend, nv_last);
+  if (kstart >= kstop) return;
+
+  // operand A: row col of the wave (query q_first + col/HI, head col%HI), 16 channels per step
+  const int ksteps = A.d_I / 16;
+  const uint16_t* qrow = static_cast<const uint16_t*>(A.q) + (row0 + col) * A.d_I + 8 * half;
+  u32x4 qa[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qa[s] = s < ksteps ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+  // weights and visible counts of the query tokens whose scores this lane writes
+  constexpr int QPL = 16 / HI;          // query tokens per lane (one per group of HI registers)
+  float w[QPL][HI];
+  int nvq[QPL];
+  int64_t qrow_idx[QPL];
+#pragma unroll
+  for (int t = 0; t < QPL; ++t) {
+    const int r0 = t * HI;                                      // first register of the group
+    const int row_in_wave = 8 * (r0 >> 2) + 4 * half + (r0 & 3);
+    const int qi = q_first + row_in_wave / HI;
+    qrow_idx[t] = qi;
+#pragma unroll
+    for (int g = 0; g < HI; ++g) w[t][g] = A.w[static_cast<int64_t>(qi) * HI + g];
+    const int64_t p = A.pos0 + (qi % A.Nq);
+    const int64_t v = (p + 1) / A.ratio;
+    nvq[t] = static_cast<int>(v < A.N ? v : A.N);
+  }
+  const uint16_t* kbase = static_cast<const uint16_t*>(A.k) + b * A.k_bstride + 8 * half;
+  for (int j0 = kstart; j0 < kstop; j0 += 32) {
+    const int j = j0 + col;
+    u32x4 kb[8];
+    const bool jv = j < kstop;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      kb[s] = (s < ksteps && jv)
+                  ? *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * A.d_I + 16 * s)
+                  : u32x4{0, 0, 0, 0};
+    f32x16g d = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < ksteps)
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[s]),
+                                                    __builtin_bit_cast(bf16x8, kb[s]), d, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < QPL; ++t) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int g = 0; g < HI; ++g) sc = fmaf(w[t][g], fmaxf(d[t * HI + g], 0.0f), sc);
+      sc += 0.0f;
+      if (jv && j < nvq[t]) {
+        if constexpr (SBF16)
+          static_cast<uint16_t*>(A.scores)[qrow_idx[t] * A.N + j] =
+              static_cast<uint16_t>(f32_to_bf16_bits(sc));
+        else
+          static_cast<float*>(A.scores)[qrow_idx[t] * A.N + j] = sc;
+      }
+    }
+  }
 }
 
 template <int HI, int LPE, bool KBF16>
@@ -587,6 +674,27 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.hist = hist;
   A.topk = k;
   const int rows = B * Nq;
+  // many query tokens per sequence: the GEMM form on the matrix cores
+  if (k_dtype == 1 && (H_I == 1 || H_I == 2 || H_I == 4) && Nq * H_I >= 128 &&
+      (Nq * H_I) % 32 == 0 && d_I % 16 == 0 && d_I <= 128) {
+    A.rows_total = rows * H_I;
+    A.chunk = 4096;
+    dim3 grid((N + A.chunk - 1) / A.chunk, (A.rows_total + 127) / 128);
+    hipError_t e;
+    if (H_I == 1) {
+      if (score_dtype == 1) launch_timed(index_scores_gemm_kernel<1, true>, grid, dim3(256), s, A);
+      else launch_timed(index_scores_gemm_kernel<1, false>, grid, dim3(256), s, A);
+    } else if (H_I == 2) {
+      if (score_dtype == 1) launch_timed(index_scores_gemm_kernel<2, true>, grid, dim3(256), s, A);
+      else launch_timed(index_scores_gemm_kernel<2, false>, grid, dim3(256), s, A);
+    } else {
+      if (score_dtype == 1) launch_timed(index_scores_gemm_kernel<4, true>, grid, dim3(256), s, A);
+      else launch_timed(index_scores_gemm_kernel<4, false>, grid, dim3(256), s, A);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess || hist == nullptr) return e;
+    return launch_sel_hist(scores, score_dtype, N, B, Nq, N, ratio, pos0, k, hist, s);
+  }
   const int lpe = d_I * (k_dtype == 1 ? 2 : 4) / 16;
   if (k_dtype == 1) {
     if (lpe == 4) return launch_lpe<4, true>(A, rows, H_I, score_dtype, s);

@@ -43,6 +43,10 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                uint32_t* hist, int k, hipStream_t s);
 
 void time_next_indexer(hipEvent_t start, hipEvent_t stop);
+// selector histogram of caller-given scores into a top-k workspace (topk.hip)
+hipError_t launch_sel_hist(const void* scores, int score_dtype, int64_t row_stride, int B,
+                           int Nq, int N, int ratio, int64_t pos0, int k, void* ws,
+                           hipStream_t s);
 
 // ---- attention.hip
 struct AttnArgs {

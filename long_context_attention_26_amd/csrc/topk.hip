@@ -484,6 +484,26 @@ hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t 
   return hipGetLastError();
 }
 
+hipError_t launch_sel_hist(const void* scores, int score_dtype, int64_t row_stride, int B,
+                           int Nq, int N, int ratio, int64_t pos0, int k, void* ws,
+                           hipStream_t s) {
+  const TopkPlan plan = plan_topk(score_dtype, B * Nq, N, k);
+  TopkDev P;
+  P.scores = scores;
+  P.row_stride = row_stride;
+  P.Nq = Nq;
+  P.N = N;
+  P.ratio = ratio;
+  P.k = k;
+  P.pos0 = pos0;
+  P.S = topk_sel_state(plan, ws);
+  P.idx = nullptr;
+  const dim3 grid(plan.nchunks, plan.rows);
+  if (plan.key_bits == 16) topk_hist_kernel<16><<<grid, 256, 0, s>>>(P);
+  else topk_hist_kernel<32><<<grid, 256, 0, s>>>(P);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
                        int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
                        void* ws, hipStream_t s) {
