@@ -22,25 +22,59 @@ sys.path.insert(0, ROOT)
 
 METRIC = "1M-ctx compressed-attn decode queries/s + achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 MALL_BYTES = 256 << 20
 
 
+def _visible(cfg, ratio):
+    """Entries of one compressed stream seen by each query token of a step."""
+    N = cfg.T // ratio
+    return [min(N, (cfg.pos0 + i + 1) // ratio) for i in range(cfg.Nq)]
+
+
 def step_bytes(cfg):
-    """Algorithmic HBM bytes of one step (per sequence: indexer-key scan, gathered top-k +
-    window K/V rows, HCA entries, pooling reads of the completed blocks, q and outputs)."""
+    """Algorithmic HBM bytes of one step.  Decode (one query token per sequence): per
+    sequence the indexer-key scan, the gathered top-k + window K/V rows, the HCA entries,
+    the pooling reads of the completed blocks, q and outputs.  Prefill (a chunk of query
+    tokens per sequence): every cache row is needed once per chunk, so the same items count
+    the caches once (the CSA rows gathered at most once each), the chunk's raw tokens for
+    the window and pooling, and q and outputs per token."""
     kv = 4 if cfg.kv == "f32" else 2
     if cfg.idx == "mxfp4":
         key = cfg.d_I // 2 + cfg.d_I // 32
     else:
         key = cfg.d_I * (4 if cfg.idx == "f32" else 2)
-    per = {
-        "index_scan": cfg.N_c * key,
-        "gather": (cfg.topk + cfg.n_win) * 2 * cfg.d * kv,
-        "hca": cfg.N_h * 2 * cfg.d * kv,
-        "pool": (2 * 4 * cfg.d + 4 * cfg.d_I) * kv + 2 * 128 * cfg.d * kv,
-        "q_out": cfg.H * cfg.d * (kv + 2 * 4),
-    }
-    return {k: v * cfg.B * cfg.Nq for k, v in per.items()}
+    if cfg.Nq == 1:
+        per = {
+            "index_scan": cfg.N_c * key,
+            "gather": (cfg.topk + cfg.n_win) * 2 * cfg.d * kv,
+            "hca": cfg.N_h * 2 * cfg.d * kv,
+            "pool": (2 * 4 * cfg.d + 4 * cfg.d_I) * kv + 2 * 128 * cfg.d * kv,
+            "q_out": cfg.H * cfg.d * (kv + 2 * 4),
+        }
+    else:
+        per = {
+            "index_scan": cfg.N_c * key,
+            "gather": min(cfg.N_c, cfg.Nq * cfg.topk) * 2 * cfg.d * kv
+                      + (cfg.Nq + cfg.n_win) * 2 * cfg.d * kv,
+            "hca": cfg.N_h * 2 * cfg.d * kv,
+            "pool": cfg.Nq * (2 * cfg.d + cfg.d_I + 2 * cfg.d) * kv,
+            "q_out": cfg.Nq * cfg.H * cfg.d * (kv + 2 * 4),
+        }
+    return {k: v * cfg.B for k, v in per.items()}
+
+
+def step_flops(cfg):
+    """Algorithmic floating-point operations of one step (multiply-add = 2): indexer dot
+    products over the visible compressed entries of every query token and indexer head,
+    CSA attention over the selected entries plus the window, HCA attention over every
+    visible entry (QK^T and PV, 4 per key per channel per head)."""
+    nv_c, nv_h = _visible(cfg, cfg.r_csa), _visible(cfg, cfg.r_hca)
+    idx = sum(nv_c) * cfg.H_I * cfg.d_I * 2
+    csa = sum(min(cfg.topk, n) + min(cfg.n_win, cfg.pos0 + i + 1)
+              for i, n in enumerate(nv_c)) * cfg.H * cfg.d * 4
+    hca = sum(nv_h) * cfg.H * cfg.d * 4
+    return {"index": idx * cfg.B, "csa": csa * cfg.B, "hca": hca * cfg.B}
 
 
 def index_scan_bytes(cfg):
@@ -227,11 +261,29 @@ def main():
     br = {s: sum(e[j].elapsed_time(e[j + 1]) for e in ev) * 1e3 / len(ev)
           for j, s in enumerate(stages)}
     idx_us = sum(a.elapsed_time(b) for a, b in kev) * 1e3 / len(kev)
-    achieved = index_scan_bytes(cfg) / (idx_us * 1e-6) / 1e9
+    flops = step_flops(cfg)
+    if cfg.Nq == 1:
+        # decode: the indexer streams every compressed key once per query
+        achieved = index_scan_bytes(cfg) / (idx_us * 1e-6) / 1e9
+        roof = {"kernel": "index_scores (lightning-indexer key scan)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg),
+                "bytes_per_launch": index_scan_bytes(cfg)}
+    else:
+        # prefill: one launch scores every query token of the chunk against every visible
+        # key, a bf16 matrix-core contraction
+        achieved = flops["index"] / (idx_us * 1e-6) / 1e12
+        roof = {"kernel": "index_scores (lightning-indexer MFMA GEMM)", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "flops_per_launch": flops["index"]}
+    roof.update({"avg_launch_us": round(idx_us, 3),
+                 "timing": "dispatch-recorded start/stop events on the launch stream"})
+    unit = "decode queries/s" if cfg.Nq == 1 else "prefill query tokens/s"
     out = {
         "metric": METRIC,
         "value": round(qps, 2),
-        "unit": "decode queries/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -248,15 +300,11 @@ def main():
         "step_hbm_gbps": round(total_bytes / (el / args.steps) / 1e9, 1),
         "step_hbm_frac": round(total_bytes / (el / args.steps) / 1e9 / HBM_PEAK_GBPS, 4),
         "step_bytes": total_bytes,
+        "step_tflops": round(sum(flops.values()) / (el / args.steps) / 1e12, 2),
         "breakdown_us": {k: round(v, 2) for k, v in br.items()},
         "breakdown_note": f"sampled every {SAMPLE}th step ({len(ev)} samples): pooling graph | "
                           "indexer launch | selection + attention graph",
-        "roofline": {"kernel": "index_scores (lightning-indexer key scan)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg),
-                     "bytes_per_launch": index_scan_bytes(cfg),
-                     "avg_launch_us": round(idx_us, 3),
-                     "timing": "dispatch-recorded start/stop events on the launch stream"},
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, st, om, q, qi, wi, args.cpu_seconds)

@@ -643,6 +643,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.pos0 = pos0;
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
+  if (hist != nullptr && topk_uses_rows_path(plan_topk(score_dtype, B * Nq, N, k))) hist = nullptr;
   A.hist = hist;
   A.topk = k;
   if (q_dtype == 1) return launch_mx_mfma<true>(A, B * Nq, H_I, score_dtype, s);
@@ -671,6 +672,8 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.pos0 = pos0;
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
+  // rows resolved one block per row need no shared histogram
+  if (hist != nullptr && topk_uses_rows_path(plan_topk(score_dtype, B * Nq, N, k))) hist = nullptr;
   A.hist = hist;
   A.topk = k;
   const int rows = B * Nq;

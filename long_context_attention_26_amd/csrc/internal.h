@@ -25,6 +25,7 @@ struct TopkPlan {
   size_t hist_bytes, count_bytes, total_bytes;
 };
 TopkPlan plan_topk(int score_dtype, int rows, int N, int k);
+bool topk_uses_rows_path(const TopkPlan& plan);   // one block per row, no shared state
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
                        int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
                        void* ws, hipStream_t s);

@@ -422,6 +422,182 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P
   }
 }
 
+// ---------------------------------------------------------------- many rows: one block per row
+
+// Prefill: many rows of at most 72K BF16 (64K F32) scores.  One 1024-thread block per row
+// keeps the row's keys in registers: wave w owns a contiguous span of 64*NCH 16-byte chunks
+// and lane l holds chunk 64*i + l of it (coalesced loads), so key order is (wave, i, lane,
+// element).  The threshold key T (the k-th largest) is found bit by bit from the top: a
+// candidate bit stays set when at least k keys are >= the candidate, each step one block
+// count.  Keys past the visible count are zeroed, and no candidate is 0, so they never
+// count.  The selection (keys above T, then the lowest-index keys equal to T) is written in
+// index order from ballots.  No shared-memory atomics: prefill scores crowd a few values
+// (many are exactly 0), which would serialize a histogram.
+constexpr int kRowsThreads = 1024;
+constexpr int kRowsMaxBf16 = 73728, kRowsMaxF32 = 65536;   // 9 (16) chunks per thread
+
+__host__ __device__ inline bool rows_path(int rows, int N, int key_bits) {
+  return rows >= 64 && N <= (key_bits == 16 ? kRowsMaxBf16 : kRowsMaxF32);
+}
+
+template <int KB, int NCH>
+__global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int vec) {
+  constexpr int EPC = KB == 16 ? 8 : 4;          // keys per 16-byte chunk
+  constexpr int kWaves = kRowsThreads / 64;
+  __shared__ int s_cnt[2][kWaves];
+  __shared__ int s_gt[kWaves], s_eq[kWaves];
+  const int row = blockIdx.x;
+  const int nv = visible(P, row);
+  int32_t* out = P.idx + static_cast<int64_t>(row) * P.k;
+  if (P.k >= nv) {
+    for (int j = threadIdx.x; j < P.k; j += kRowsThreads) out[j] = j < nv ? j : -1;
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+
+  // ---- keys of this lane's chunks
+  const int cbase = w * 64 * NCH + lane;
+  const char* rowp = static_cast<const char*>(P.scores) +
+                     static_cast<int64_t>(row) * P.row_stride * (KB / 8);
+  u32x4 kv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int j0 = (cbase + 64 * i) * EPC;
+    if (vec && j0 < nv && j0 + EPC <= P.N)
+      kv[i] = *reinterpret_cast<const u32x4*>(rowp + static_cast<int64_t>(j0) * (KB / 8));
+    else
+      kv[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {                // unaligned rows, or the allocation's tail
+    const int j0 = (cbase + 64 * i) * EPC;
+    if (j0 < nv && !(vec && j0 + EPC <= P.N)) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if (j0 + e < nv) {
+          if constexpr (KB == 16) {
+            const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[j0 + e];
+            kv[i][e >> 1] |= h << (16 * (e & 1));
+          } else {
+            kv[i][e] = reinterpret_cast<const uint32_t*>(rowp)[j0 + e];
+          }
+        }
+      }
+    }
+  }
+  auto nvalid = [&](int i) -> int {
+    const int r = nv - (cbase + 64 * i) * EPC;
+    return r < 0 ? 0 : (r > EPC ? EPC : r);
+  };
+  // order-preserving keys; 0 past the visible count
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int nvl = nvalid(i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t x = kv[i][c];
+      if constexpr (KB == 16) {
+        const uint32_t lo = 2 * c < nvl ? bf16_key(x & 0xffffu) : 0u;
+        const uint32_t hi = 2 * c + 1 < nvl ? bf16_key(x >> 16) : 0u;
+        kv[i][c] = lo | (hi << 16);
+      } else {
+        kv[i][c] = c < nvl ? f32_key(x) : 0u;
+      }
+    }
+  }
+  auto key = [&](int i, int e) -> uint32_t {
+    if constexpr (KB == 16)
+      return (kv[i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+    else
+      return kv[i][e];
+  };
+
+  // ---- T: the largest value with at least k keys >= T
+  uint32_t T = 0;
+#pragma unroll 1
+  for (int b = KB - 1; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) c += key(i, e) >= cand;
+    c = wave_sum_i(c);
+    if (lane == 0) s_cnt[b & 1][w] = c;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) tot += s_cnt[b & 1][u];
+    if (tot >= P.k) T = cand;
+  }
+
+  // ---- selection in index order: keys above T, and the first `need` keys equal to T
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int nvl = nvalid(i);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const uint32_t kk = key(i, e);
+      gt += kk > T;
+      eq += e < nvl && kk == T;
+    }
+  }
+  gt = wave_sum_i(gt);
+  eq = wave_sum_i(eq);
+  if (lane == 0) {
+    s_gt[w] = gt;
+    s_eq[w] = eq;
+  }
+  __syncthreads();
+  int slot = 0, eq_rank = 0, gt_all = 0;
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) {
+    slot += u < w ? s_gt[u] : 0;
+    eq_rank += u < w ? s_eq[u] : 0;
+    gt_all += s_gt[u];
+  }
+  const int need = P.k - gt_all;                 // 1 <= need <= keys equal to T
+  slot += min(need, eq_rank);
+  const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int nvl = nvalid(i);
+    const int jc = (cbase + 64 * i) * EPC;
+    // T-valued keys of the lanes before this one (and of this wave's chunk in total)
+    int eq_before = 0, eq_all = 0;
+    bool is_eq[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      is_eq[e] = e < nvl && key(i, e) == T;
+      const uint64_t m = __ballot(is_eq[e]);
+      eq_before += __popcll(m & below);
+      eq_all += __popcll(m);
+    }
+    int r = eq_rank + eq_before;
+    bool sel[EPC];
+    int sel_before = 0, sel_all = 0;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      sel[e] = key(i, e) > T || (is_eq[e] && r < need);
+      r += is_eq[e];
+      const uint64_t m = __ballot(sel[e]);
+      sel_before += __popcll(m & below);
+      sel_all += __popcll(m);
+    }
+    int o = slot + sel_before;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      if (sel[e]) {
+        if (o < P.k) out[o] = jc + e;
+        ++o;
+      }
+    }
+    slot += sel_all;
+    eq_rank += eq_all;
+  }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
   for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += 256LL * gridDim.x) p[i] = v;
 }
@@ -439,8 +615,12 @@ TopkPlan plan_topk(int score_dtype, int rows, int N, int k) {
   p.chunk = kExtractChunk;
   p.nchunks = N > 0 ? (N + p.chunk - 1) / p.chunk : 1;
   p.copies = sel_copies(rows, N);
-  p.hist_bytes = align256(sel_words(rows, p.copies) * 4);                 // selector words
-  p.count_bytes = align256(static_cast<size_t>(rows) * kCap * 8);         // candidates
+  if (rows_path(rows, N, p.key_bits)) {
+    p.hist_bytes = p.count_bytes = 0;     // one block per row, all state in LDS
+  } else {
+    p.hist_bytes = align256(sel_words(rows, p.copies) * 4);               // selector words
+    p.count_bytes = align256(static_cast<size_t>(rows) * kCap * 8);       // candidates
+  }
   p.total_bytes = p.hist_bytes + p.count_bytes;
   return p;
 }
@@ -449,7 +629,41 @@ SelState topk_sel_state(const TopkPlan& plan, void* ws) {
   return sel_state(ws, plan.rows, plan.copies, plan.hist_bytes);
 }
 
+template <int KB>
+static hipError_t launch_rows_kb(const TopkPlan& plan, const TopkDev& P, int vec, hipStream_t s) {
+  constexpr int EPC = KB == 16 ? 8 : 4;
+  const int per = (plan.N + kRowsThreads * EPC - 1) / (kRowsThreads * EPC);   // chunks / thread
+#define HCSA_ROWS(n) \
+  if (per <= n) { topk_rows_kernel<KB, n><<<plan.rows, kRowsThreads, 0, s>>>(P, vec); return hipGetLastError(); }
+  // BF16 keys are unpacked for comparison, so their register budget ends at 9 chunks
+  HCSA_ROWS(2) HCSA_ROWS(4) HCSA_ROWS(6) HCSA_ROWS(9)
+  if constexpr (KB == 32) { HCSA_ROWS(12) HCSA_ROWS(16) }
+#undef HCSA_ROWS
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_topk_rows(const TopkPlan& plan, const void* scores,
+                                   int64_t row_stride, int Nq, int ratio, int64_t pos0,
+                                   int32_t* idx, hipStream_t s) {
+  TopkDev P{};
+  P.scores = scores;
+  P.row_stride = row_stride;
+  P.Nq = Nq;
+  P.N = plan.N;
+  P.ratio = ratio;
+  P.k = plan.k;
+  P.pos0 = pos0;
+  P.idx = idx;
+  const int esz = plan.key_bits / 8;
+  const int vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride * esz) % 16 == 0;
+  return plan.key_bits == 16 ? launch_rows_kb<16>(plan, P, vec, s)
+                             : launch_rows_kb<32>(plan, P, vec, s);
+}
+
+bool topk_uses_rows_path(const TopkPlan& plan) { return rows_path(plan.rows, plan.N, plan.key_bits); }
+
 hipError_t launch_topk_clear(const TopkPlan& plan, void* ws, hipStream_t s) {
+  if (rows_path(plan.rows, plan.N, plan.key_bits)) return hipSuccess;   // no shared state
   const int64_t words = static_cast<int64_t>(sel_words(plan.rows, plan.copies));
   const int blocks = static_cast<int>(std::min<int64_t>((words + 255) / 256, 4096));
   fill_u32_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(ws), words, 0u);
@@ -459,6 +673,8 @@ hipError_t launch_topk_clear(const TopkPlan& plan, void* ws, hipStream_t s) {
 hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t row_stride,
                               int Nq, int ratio, int64_t pos0, int32_t* idx, void* ws,
                               bool need_hist, hipStream_t s) {
+  if (rows_path(plan.rows, plan.N, plan.key_bits))
+    return launch_topk_rows(plan, scores, row_stride, Nq, ratio, pos0, idx, s);
   TopkDev P;
   P.scores = scores;
   P.row_stride = row_stride;
@@ -488,6 +704,7 @@ hipError_t launch_sel_hist(const void* scores, int score_dtype, int64_t row_stri
                            int Nq, int N, int ratio, int64_t pos0, int k, void* ws,
                            hipStream_t s) {
   const TopkPlan plan = plan_topk(score_dtype, B * Nq, N, k);
+  if (rows_path(plan.rows, plan.N, plan.key_bits)) return hipSuccess;   // not needed
   TopkDev P;
   P.scores = scores;
   P.row_stride = row_stride;
@@ -508,6 +725,8 @@ hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype
                        int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
                        void* ws, hipStream_t s) {
   (void)score_dtype;
+  if (rows_path(plan.rows, plan.N, plan.key_bits))
+    return launch_topk_rows(plan, scores, row_stride, Nq, ratio, pos0, idx, s);
   hipError_t e = launch_topk_clear(plan, ws, s);
   if (e != hipSuccess) return e;
   return launch_topk_select(plan, scores, row_stride, Nq, ratio, pos0, idx, ws, true, s);

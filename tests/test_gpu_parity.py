@@ -149,6 +149,42 @@ def test_topk_bit_exact(H, gpu, sdt, N, k, kind):
         assert np.array_equal(got[r], want), (r, nv)
 
 
+@pytest.mark.parametrize("sdt,N,B,Nq,k,kind,pad", [
+    ("bf16", 60000, 2, 48, 512, "normal", 0),     # 96 rows, ragged visible counts
+    ("bf16", 73728, 1, 64, 1024, "ties", 0),      # the longest rows held on chip
+    ("f32", 65536, 1, 64, 300, "normal", 0),
+    ("f32", 34817, 1, 70, 300, "normal", 3),      # ragged last chunk, unaligned stride
+    ("bf16", 9001, 1, 64, 700, "ties", 1),
+    ("f32", 5000, 3, 40, 4096, "ties", 0),        # k near the visible count
+    ("bf16", 3000, 1, 64, 4096, "normal", 0),     # k above it: every visible entry, then -1
+    ("bf16", 2000, 1, 100, 1, "normal", 0),
+])
+def test_topk_many_rows_bit_exact(H, gpu, sdt, N, B, Nq, k, kind, pad):
+    """Many short rows (prefill): one block per row holds the row's keys on chip."""
+    print(f"topk rows {sdt} N={N} B={B} Nq={Nq} k={k} {kind}", flush=True)
+    ratio = 4
+    pos0 = 4 * N - 2 * Nq                 # visible counts from N - Nq/2 up to N, capped
+    s = O.round_to(_scores((B * Nq, N), kind), sdt)
+    if kind == "normal":
+        s[..., ::89] = -np.inf
+    st = dev(s, W.torch_dtype(sdt), gpu)
+    assert H.topk_workspace_size(H.dtype_code(st), B, Nq, N, k) == 0
+    over = 73729 if sdt == "bf16" else 65537          # one past the on-chip row limit
+    assert H.topk_workspace_size(H.dtype_code(st), B, Nq, over, k) > 0
+    if pad:                               # unaligned row stride: element loads
+        wide = torch.zeros(B * Nq, N + pad, dtype=st.dtype, device=gpu)
+        wide[:, :N] = st
+        st = wide[:, :N]
+    idx = torch.full((B * Nq, k), -7, dtype=torch.int32, device=gpu)
+    H.topk(st, B, Nq, N, ratio, pos0, k, idx)
+    _sync()
+    got = idx.cpu().numpy()
+    for r in range(B * Nq):
+        nv = O.visible_entries(pos0 + r % Nq, N, ratio)
+        want = O.select_topk(s[r], nv, k)
+        assert np.array_equal(got[r], want), (r, nv)
+
+
 def test_topk_deterministic(H, gpu):
     s = dev(O.round_bf16(rng.integers(0, 3, size=(1, 262144)).astype(float)), torch.bfloat16, gpu)
     outs = []
