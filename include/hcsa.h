@@ -139,8 +139,8 @@ int hcsa_mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int D, uint8_t
  *         the lowest index) in ascending order, then -1.  Bit-exact and deterministic.
  * Limits: 1 <= k <= 4096, 1 <= N, row_stride >= N, ratio >= 1, pos0 >= 0.
  * Workspace: caller-owned device memory of hcsa_topk_workspace_size bytes, 256-byte
- * aligned.  The size is 0 (workspace may be NULL) when at least 64 rows of at most 73728
- * BF16 or 65536 F32 scores are resolved one block per row entirely in on-chip memory.
+ * aligned.  The size is 0 (workspace may be NULL) when at least 64 rows of at most 131072
+ * scores are resolved one block per row with on-chip state only.
  */
 size_t hcsa_topk_workspace_size(int score_dtype, int B, int Nq, int N, int k);
 int hcsa_topk(const void *scores, int score_dtype, int64_t row_stride, int B, int Nq, int N,

@@ -424,28 +424,79 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkDev P
 
 // ---------------------------------------------------------------- many rows: one block per row
 
-// Prefill: many rows of at most 72K BF16 (64K F32) scores.  One 1024-thread block per row
-// keeps the row's keys in registers: wave w owns a contiguous span of 64*NCH 16-byte chunks
-// and lane l holds chunk 64*i + l of it (coalesced loads), so key order is (wave, i, lane,
-// element).  The threshold key T (the k-th largest) is found bit by bit from the top: a
-// candidate bit stays set when at least k keys are >= the candidate, each step one block
-// count.  Keys past the visible count are zeroed, and no candidate is 0, so they never
-// count.  The selection (keys above T, then the lowest-index keys equal to T) is written in
-// index order from ballots.  No shared-memory atomics: prefill scores crowd a few values
-// (many are exactly 0), which would serialize a histogram.
-constexpr int kRowsThreads = 1024;
-constexpr int kRowsMaxBf16 = 73728, kRowsMaxF32 = 65536;   // 9 (16) chunks per thread
+// Prefill: many rows of at most 128K scores (BF16 or F32).  One 512-thread block per row
+// streams the row from HBM once; four such blocks share a CU, so one block's loads overlap
+// the others' arithmetic.  Wave w owns a contiguous run of 16-byte chunks and walks it 64
+// chunks at a time, so index order is (wave, step, lane, element).  A wave64 vector
+// instruction occupies its SIMD for four cycles, so each key gets only a few instructions:
+//   1. the top 16 bits L of the m-th largest of up to 2048 sampled keys (the first key of
+//      each lane's first four chunks; m twice the expected rank of the k-th largest key,
+//      plus a margin) bound the candidates;
+//   2. the streaming pass writes every key >= L (key and index) to its wave's LDS list, in
+//      index order (a few percent of the row);
+//   3. the exact threshold T and the selection are resolved among those candidates.
+// When a wave's list overflows or the candidates fall short of k (many tied keys, a skewed
+// row, an unlucky sample), T is found bit by bit over the whole row, re-read from the
+// caches, and the selection is written from ballots.  Either way the result is the keys
+// above T, then the lowest-index keys equal to T, in index order.
+constexpr int kRowsThreads = 512;
+constexpr int kRowsWaves = kRowsThreads / 64;
+constexpr int kRowsMaxKeys = 131072;
+constexpr int kRowsWaveCap = 512;   // candidates per wave list (four blocks share a CU)
 
 __host__ __device__ inline bool rows_path(int rows, int N, int key_bits) {
-  return rows >= 64 && N <= (key_bits == 16 ? kRowsMaxBf16 : kRowsMaxF32);
+  (void)key_bits;
+  return rows >= 64 && N <= kRowsMaxKeys;
 }
 
-template <int KB, int NCH>
+// Wave sum of a small non-negative int (< 2^BITS) from the ballots of its bits: scalar
+// popcounts, no cross-lane data movement (a lane shuffle goes through the LDS crossbar).
+template <int BITS>
+__device__ __forceinline__ int wave_sum_bits(int v) {
+  int t = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) t += __popcll(__ballot((v >> b) & 1)) << b;
+  return t;
+}
+
+// Exclusive prefix over the lanes (and wave total) of a small non-negative int.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_bits(int v, uint64_t below, int& total) {
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const uint64_t m = __ballot((v >> b) & 1);
+    pre += __popcll(m & below) << b;
+    total += __popcll(m) << b;
+  }
+  return pre;
+}
+
+// Block-wide sum of a small non-negative int per thread; s[buf] is written, so consecutive
+// calls without a barrier in between must alternate buf.
+template <int BITS>
+__device__ __forceinline__ int block_total_bits(int v, int (*s)[kRowsWaves], int buf) {
+  const int t = wave_sum_bits<BITS>(v);
+  if ((threadIdx.x & 63) == 0) s[buf][threadIdx.x >> 6] = t;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int u = 0; u < kRowsWaves; ++u) r += s[buf][u];
+  return r;
+}
+
+// grid: rows; block 512.
+template <int KB>
 __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int vec) {
-  constexpr int EPC = KB == 16 ? 8 : 4;          // keys per 16-byte chunk
-  constexpr int kWaves = kRowsThreads / 64;
-  __shared__ int s_cnt[2][kWaves];
-  __shared__ int s_gt[kWaves], s_eq[kWaves];
+  using KT = typename std::conditional<KB == 16, uint16_t, uint32_t>::type;
+  constexpr int EPC = 16 / sizeof(KT);           // keys per 16-byte chunk
+  constexpr int STEPS = kRowsWaveCap / 64;       // list entries per lane at most
+  __shared__ uint32_t s_ck[kRowsWaves][kRowsWaveCap];
+  __shared__ int32_t s_cj[kRowsWaves][kRowsWaveCap];
+  __shared__ int s_cnt[2][kRowsWaves];
+  __shared__ int s_wave[kRowsWaves], s_gt[kRowsWaves], s_eq[kRowsWaves], s_hb[kRowsWaves];
+  __shared__ int s_rdx[2][kRowsWaves][3];
   const int row = blockIdx.x;
   const int nv = visible(P, row);
   int32_t* out = P.idx + static_cast<int64_t>(row) * P.k;
@@ -454,147 +505,311 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
     return;
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  const int nch = (nv + EPC - 1) / EPC;          // chunks holding visible keys
+  const int CW = (nch + kRowsThreads - 1) / kRowsThreads * 64;   // chunks per wave
+  const int cw0 = w * CW, cw1 = min(cw0 + CW, nch);
+  const KT* rowp = reinterpret_cast<const KT*>(static_cast<const char*>(P.scores) +
+                                               static_cast<int64_t>(row) * P.row_stride * sizeof(KT));
+  const int nfull = vec ? min(nch, P.N / EPC) : 0;   // chunks read as one 16-byte load
 
-  // ---- keys of this lane's chunks
-  const int cbase = w * 64 * NCH + lane;
-  const char* rowp = static_cast<const char*>(P.scores) +
-                     static_cast<int64_t>(row) * P.row_stride * (KB / 8);
-  u32x4 kv[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int j0 = (cbase + 64 * i) * EPC;
-    if (vec && j0 < nv && j0 + EPC <= P.N)
-      kv[i] = *reinterpret_cast<const u32x4*>(rowp + static_cast<int64_t>(j0) * (KB / 8));
+  // raw bits of chunk ch < nch (elements past the visible count are never used)
+  auto load_raw = [&](int ch) -> u32x4 {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (ch < nfull) {
+      x = *reinterpret_cast<const u32x4*>(rowp + static_cast<int64_t>(ch) * EPC);
+    } else {
+      for (int e = 0; e < EPC && ch * EPC + e < nv; ++e) {
+        const uint32_t v = rowp[ch * EPC + e];
+        if constexpr (KB == 16)
+          x[e >> 1] |= v << (16 * (e & 1));
+        else
+          x[e] = v;
+      }
+    }
+    return x;
+  };
+  auto to_key = [&](uint32_t raw) -> uint32_t {
+    if constexpr (KB == 16)
+      return bf16_key(raw);
     else
-      kv[i] = u32x4{0u, 0u, 0u, 0u};
-  }
+      return f32_key(raw);
+  };
+  auto raw_of = [&](const u32x4& x, int e) -> uint32_t {
+    if constexpr (KB == 16) {
+      const int c = e >> 1;
+      const uint32_t v = c == 0 ? x[0] : c == 1 ? x[1] : c == 2 ? x[2] : x[3];
+      return (v >> (16 * (e & 1))) & 0xffffu;
+    } else {
+      return e == 0 ? x[0] : e == 1 ? x[1] : e == 2 ? x[2] : x[3];
+    }
+  };
+  // bit e set when element e of a raw chunk (first index j0) is a visible key >= L.  For a
+  // floor above +0 the keys >= L are exactly the non-negative raw values in
+  // [raw(L), largest positive pattern], an unsigned range test on the raw bits.
+  constexpr uint32_t kSign = KB == 16 ? 0x8000u : 0x80000000u;
+  auto ge_mask = [&](const u32x4& x, int j0, uint32_t L) -> uint32_t {
+    uint32_t m = 0;
+    if (L > kSign) {
+      const uint32_t lo_raw = L - kSign, span = kSign - 1 - lo_raw;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {                // unaligned rows, or the allocation's tail
-    const int j0 = (cbase + 64 * i) * EPC;
-    if (j0 < nv && !(vec && j0 + EPC <= P.N)) {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        if (j0 + e < nv) {
-          if constexpr (KB == 16) {
-            const uint32_t h = reinterpret_cast<const uint16_t*>(rowp)[j0 + e];
-            kv[i][e >> 1] |= h << (16 * (e & 1));
-          } else {
-            kv[i][e] = reinterpret_cast<const uint32_t*>(rowp)[j0 + e];
-          }
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (KB == 16) {
+          m |= static_cast<uint32_t>((x[c] & 0xffffu) - lo_raw <= span) << (2 * c);
+          m |= static_cast<uint32_t>((x[c] >> 16) - lo_raw <= span) << (2 * c + 1);
+        } else {
+          m |= static_cast<uint32_t>(x[c] - lo_raw <= span) << c;
         }
       }
-    }
-  }
-  auto nvalid = [&](int i) -> int {
-    const int r = nv - (cbase + 64 * i) * EPC;
-    return r < 0 ? 0 : (r > EPC ? EPC : r);
-  };
-  // order-preserving keys; 0 past the visible count
+    } else {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int nvl = nvalid(i);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t x = kv[i][c];
-      if constexpr (KB == 16) {
-        const uint32_t lo = 2 * c < nvl ? bf16_key(x & 0xffffu) : 0u;
-        const uint32_t hi = 2 * c + 1 < nvl ? bf16_key(x >> 16) : 0u;
-        kv[i][c] = lo | (hi << 16);
-      } else {
-        kv[i][c] = c < nvl ? f32_key(x) : 0u;
-      }
+      for (int e = 0; e < EPC; ++e) m |= static_cast<uint32_t>(to_key(raw_of(x, e)) >= L) << e;
     }
-  }
-  auto key = [&](int i, int e) -> uint32_t {
-    if constexpr (KB == 16)
-      return (kv[i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-    else
-      return kv[i][e];
+    const int r = nv - j0;
+    return r >= EPC ? m : m & ((1u << r) - 1u);
   };
 
-  // ---- T: the largest value with at least k keys >= T
+  // first stream loads, in flight while the floor is chosen
+  u32x4 cur[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ch = cw0 + 64 * u + lane;
+    cur[u] = ch < cw1 ? load_raw(ch) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- 1. candidate floor L from up to 2048 sampled keys: the first element of each of
+  // the lane's four prefetched chunks (all keys are candidates when few)
+  uint32_t L = 0;
+  if (nv > kRowsWaves * kRowsWaveCap / 2) {
+    bool sv[4];
+    uint32_t st[4];
+    int nmine = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sv[u] = cw0 + 64 * u + lane < cw1;          // first elements are visible keys
+      st[u] = sv[u] ? to_key(raw_of(cur[u], 0)) >> (KB - 16) : 0u;
+      nmine += sv[u];
+    }
+    const int ns = block_total_bits<3>(nmine, s_cnt, 0);
+    const int m = min(ns, static_cast<int>((2LL * P.k * ns + nv - 1) / nv) + 16);
+    // radix-4 select of the m-th largest 16-bit prefix (a 128th of a binade: a coarser
+    // floor would admit up to a whole bin of extra candidates): three thresholds a round
+    uint32_t pre = 0;
+#pragma unroll 1
+    for (int sh = 14; sh >= 0; sh -= 2) {
+      int cnt[3];
+#pragma unroll
+      for (int d = 1; d <= 3; ++d) {
+        const uint32_t th = pre | (static_cast<uint32_t>(d) << sh);
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) n += sv[u] && st[u] >= th;
+        cnt[d - 1] = wave_sum_bits<3>(n);
+      }
+      const int buf = (sh >> 1) & 1;
+      if (lane == 0) {
+        s_rdx[buf][w][0] = cnt[0];
+        s_rdx[buf][w][1] = cnt[1];
+        s_rdx[buf][w][2] = cnt[2];
+      }
+      __syncthreads();
+      int tot[3] = {0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < kRowsWaves; ++u) {
+        tot[0] += s_rdx[buf][u][0];
+        tot[1] += s_rdx[buf][u][1];
+        tot[2] += s_rdx[buf][u][2];
+      }
+      const uint32_t d = tot[2] >= m ? 3u : tot[1] >= m ? 2u : tot[0] >= m ? 1u : 0u;
+      pre |= d << sh;
+    }
+    L = ns > 0 ? pre << (KB - 16) : 0u;
+  }
+
+  // ---- 2. stream the wave's chunks 256 at a time (the next 256 loading meanwhile),
+  // appending keys >= L to the wave's list
+  int wslot = 0;
+  for (int base = cw0; base < cw1; base += 256) {
+    u32x4 nxt[4];
+    const bool more = base + 256 < cw1;          // wave-uniform
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ch = base + 256 + 64 * u + lane;
+        nxt[u] = ch < cw1 ? load_raw(ch) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ch = base + 64 * u + lane;
+      uint32_t msk = ch < cw1 ? ge_mask(cur[u], ch * EPC, L) : 0u;
+      int tot;
+      int o = wslot + wave_prefix_bits<4>(__popc(msk), below, tot);
+      while (msk) {
+        const int e = __ffs(msk) - 1;
+        msk &= msk - 1;
+        if (o < kRowsWaveCap) {
+          s_ck[w][o] = to_key(raw_of(cur[u], e));
+          s_cj[w][o] = ch * EPC + e;
+        }
+        ++o;
+      }
+      wslot += tot;
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    }
+  }
+  if (lane == 0) s_wave[w] = wslot;
+  __syncthreads();
+  int C = 0, before = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int u = 0; u < kRowsWaves; ++u) {
+    before += u < w ? s_wave[u] : 0;
+    C += s_wave[u];
+    overflow |= s_wave[u] > kRowsWaveCap;
+  }
+
+  if (!overflow && C >= P.k) {
+    // ---- 3. exact threshold among the candidates (lane l of wave w holds entries
+    // l, l+64, ... of the wave's list); the bits above the highest one in which some
+    // candidate differs from L are shared by every candidate and by T
+    uint32_t ck[STEPS];
+    uint32_t dor = 0;
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      const bool in = 64 * u + lane < wslot;
+      ck[u] = in ? s_ck[w][64 * u + lane] : 0u;
+      dor |= in ? (ck[u] ^ L) : 0u;
+    }
+    int hb = 0;
+    for (int b = KB - 1; b >= 0; --b) {
+      if (__ballot((dor >> b) & 1u)) {
+        hb = b + 1;
+        break;
+      }
+    }
+    if (lane == 0) s_hb[w] = hb;
+    __syncthreads();
+    int nb = 0;
+#pragma unroll
+    for (int u = 0; u < kRowsWaves; ++u) nb = s_hb[u] > nb ? s_hb[u] : nb;
+    uint32_t T = nb >= 32 ? 0u : (L >> nb) << nb;
+#pragma unroll 1
+    for (int b = nb - 1; b >= 0; --b) {
+      const uint32_t cand = T | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int u = 0; u < STEPS; ++u) n += (64 * u + lane < wslot) && ck[u] >= cand;
+      if (block_total_bits<4>(n, s_cnt, b & 1) >= P.k) T = cand;
+    }
+    // per-wave counts of entries above T and equal to T
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      const bool in = 64 * u + lane < wslot;
+      gt += in && ck[u] > T;
+      eq += in && ck[u] == T;
+    }
+    gt = wave_sum_bits<4>(gt);
+    eq = wave_sum_bits<4>(eq);
+    if (lane == 0) {
+      s_gt[w] = gt;
+      s_eq[w] = eq;
+    }
+    __syncthreads();
+    int gt_before = 0, eq_rank = 0, gt_all = 0;
+#pragma unroll
+    for (int u = 0; u < kRowsWaves; ++u) {
+      gt_before += u < w ? s_gt[u] : 0;
+      eq_rank += u < w ? s_eq[u] : 0;
+      gt_all += s_gt[u];
+    }
+    const int need = P.k - gt_all;               // 1 <= need <= candidates equal to T
+    int o = gt_before + min(need, eq_rank);
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      if (64 * u < wslot) {                        // wave-uniform
+        const bool in = 64 * u + lane < wslot;
+        const bool is_eq = in && ck[u] == T;
+        const uint64_t meq = __ballot(is_eq);
+        const int r = eq_rank + __popcll(meq & below);
+        const bool sel = in && (ck[u] > T || (is_eq && r < need));
+        const uint64_t msel = __ballot(sel);
+        if (sel) {
+          const int oo = o + __popcll(msel & below);
+          if (oo < P.k) out[oo] = s_cj[w][64 * u + lane];
+        }
+        o += __popcll(msel);
+        eq_rank += __popcll(meq);
+      }
+    }
+    return;
+  }
+
+  // ---- fallback: T bit by bit over the whole row, re-read from the caches (keys past the
+  // visible count are 0 and every tested value is >= 1, so they never count), selection
+  // from ballots
   uint32_t T = 0;
 #pragma unroll 1
   for (int b = KB - 1; b >= 0; --b) {
     const uint32_t cand = T | (1u << b);
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) c += key(i, e) >= cand;
-    c = wave_sum_i(c);
-    if (lane == 0) s_cnt[b & 1][w] = c;
-    __syncthreads();
-    int tot = 0;
-#pragma unroll
-    for (int u = 0; u < kWaves; ++u) tot += s_cnt[b & 1][u];
-    if (tot >= P.k) T = cand;
+    int n = 0;
+    for (int ch = cw0 + lane; ch < cw1; ch += 64) n += __popc(ge_mask(load_raw(ch), ch * EPC, cand));
+    if (block_total_bits<9>(n, s_cnt, b & 1) >= P.k) T = cand;   // n <= 32 chunks * 8
   }
-
-  // ---- selection in index order: keys above T, and the first `need` keys equal to T
+  // bits of a chunk: keys above T (gtm) and keys equal to T (eqm)
+  auto gt_eq = [&](int ch, uint32_t& gtm, uint32_t& eqm) {
+    const u32x4 x = load_raw(ch);
+    const uint32_t ge = ge_mask(x, ch * EPC, T);
+    gtm = T == 0xffffffffu ? 0u : ge_mask(x, ch * EPC, T + 1);
+    eqm = ge & ~gtm;
+  };
   int gt = 0, eq = 0;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int nvl = nvalid(i);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      const uint32_t kk = key(i, e);
-      gt += kk > T;
-      eq += e < nvl && kk == T;
-    }
+  for (int ch = cw0 + lane; ch < cw1; ch += 64) {
+    uint32_t gtm, eqm;
+    gt_eq(ch, gtm, eqm);
+    gt += __popc(gtm);
+    eq += __popc(eqm);
   }
-  gt = wave_sum_i(gt);
-  eq = wave_sum_i(eq);
+  gt = wave_sum_bits<9>(gt);
+  eq = wave_sum_bits<9>(eq);
   if (lane == 0) {
     s_gt[w] = gt;
     s_eq[w] = eq;
   }
   __syncthreads();
-  int slot = 0, eq_rank = 0, gt_all = 0;
+  int gslot = 0, eq_rank = 0, gt_all = 0;
 #pragma unroll
-  for (int u = 0; u < kWaves; ++u) {
-    slot += u < w ? s_gt[u] : 0;
+  for (int u = 0; u < kRowsWaves; ++u) {
+    gslot += u < w ? s_gt[u] : 0;
     eq_rank += u < w ? s_eq[u] : 0;
     gt_all += s_gt[u];
   }
   const int need = P.k - gt_all;                 // 1 <= need <= keys equal to T
-  slot += min(need, eq_rank);
-  const uint64_t below = (1ull << lane) - 1;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int nvl = nvalid(i);
-    const int jc = (cbase + 64 * i) * EPC;
-    // T-valued keys of the lanes before this one (and of this wave's chunk in total)
-    int eq_before = 0, eq_all = 0;
-    bool is_eq[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      is_eq[e] = e < nvl && key(i, e) == T;
-      const uint64_t m = __ballot(is_eq[e]);
-      eq_before += __popcll(m & below);
-      eq_all += __popcll(m);
+  gslot += min(need, eq_rank);
+  for (int base = cw0; base < cw1; base += 64) {
+    const int ch = base + lane;
+    uint32_t gtm = 0, eqm = 0;
+    if (ch < cw1) gt_eq(ch, gtm, eqm);
+    int eq_tot;
+    int r = eq_rank + wave_prefix_bits<4>(__popc(eqm), below, eq_tot);
+    uint32_t sel = gtm;
+    for (uint32_t m = eqm; m; m &= m - 1) {      // ties in index order while some are needed
+      if (r < need) sel |= m & (~m + 1);
+      ++r;
     }
-    int r = eq_rank + eq_before;
-    bool sel[EPC];
-    int sel_before = 0, sel_all = 0;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      sel[e] = key(i, e) > T || (is_eq[e] && r < need);
-      r += is_eq[e];
-      const uint64_t m = __ballot(sel[e]);
-      sel_before += __popcll(m & below);
-      sel_all += __popcll(m);
+    int tot;
+    int o = gslot + wave_prefix_bits<4>(__popc(sel), below, tot);
+    while (sel) {
+      if (o < P.k) out[o] = ch * EPC + __ffs(sel) - 1;
+      ++o;
+      sel &= sel - 1;
     }
-    int o = slot + sel_before;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      if (sel[e]) {
-        if (o < P.k) out[o] = jc + e;
-        ++o;
-      }
-    }
-    slot += sel_all;
-    eq_rank += eq_all;
+    gslot += tot;
+    eq_rank += eq_tot;
   }
 }
 
@@ -631,15 +846,8 @@ SelState topk_sel_state(const TopkPlan& plan, void* ws) {
 
 template <int KB>
 static hipError_t launch_rows_kb(const TopkPlan& plan, const TopkDev& P, int vec, hipStream_t s) {
-  constexpr int EPC = KB == 16 ? 8 : 4;
-  const int per = (plan.N + kRowsThreads * EPC - 1) / (kRowsThreads * EPC);   // chunks / thread
-#define HCSA_ROWS(n) \
-  if (per <= n) { topk_rows_kernel<KB, n><<<plan.rows, kRowsThreads, 0, s>>>(P, vec); return hipGetLastError(); }
-  // BF16 keys are unpacked for comparison, so their register budget ends at 9 chunks
-  HCSA_ROWS(2) HCSA_ROWS(4) HCSA_ROWS(6) HCSA_ROWS(9)
-  if constexpr (KB == 32) { HCSA_ROWS(12) HCSA_ROWS(16) }
-#undef HCSA_ROWS
-  return hipErrorInvalidValue;
+  topk_rows_kernel<KB><<<plan.rows, kRowsThreads, 0, s>>>(P, vec);
+  return hipGetLastError();
 }
 
 static hipError_t launch_topk_rows(const TopkPlan& plan, const void* scores,

@@ -151,10 +151,13 @@ def test_topk_bit_exact(H, gpu, sdt, N, k, kind):
 
 @pytest.mark.parametrize("sdt,N,B,Nq,k,kind,pad", [
     ("bf16", 60000, 2, 48, 512, "normal", 0),     # 96 rows, ragged visible counts
-    ("bf16", 73728, 1, 64, 1024, "ties", 0),      # the longest rows held on chip
-    ("f32", 65536, 1, 64, 300, "normal", 0),
-    ("f32", 34817, 1, 70, 300, "normal", 3),      # ragged last chunk, unaligned stride
+    ("bf16", 131072, 1, 64, 1024, "ties", 0),     # the longest rows of this path
+    ("f32", 131072, 1, 64, 300, "normal", 0),
+    ("bf16", 66560, 1, 64, 512, "normal", 0),     # a prefill chunk's row length
+    ("f32", 32767, 1, 70, 300, "normal", 3),      # ragged last chunk, unaligned stride
     ("bf16", 9001, 1, 64, 700, "ties", 1),
+    ("bf16", 9001, 1, 64, 100, "normal", 1),
+    ("bf16", 20000, 1, 64, 777, "zeros", 0),      # every key tied
     ("f32", 5000, 3, 40, 4096, "ties", 0),        # k near the visible count
     ("bf16", 3000, 1, 64, 4096, "normal", 0),     # k above it: every visible entry, then -1
     ("bf16", 2000, 1, 100, 1, "normal", 0),
@@ -169,7 +172,7 @@ def test_topk_many_rows_bit_exact(H, gpu, sdt, N, B, Nq, k, kind, pad):
         s[..., ::89] = -np.inf
     st = dev(s, W.torch_dtype(sdt), gpu)
     assert H.topk_workspace_size(H.dtype_code(st), B, Nq, N, k) == 0
-    over = 73729 if sdt == "bf16" else 65537          # one past the on-chip row limit
+    over = 131073                                     # one past this path's row limit
     assert H.topk_workspace_size(H.dtype_code(st), B, Nq, over, k) > 0
     if pad:                               # unaligned row stride: element loads
         wide = torch.zeros(B * Nq, N + pad, dtype=st.dtype, device=gpu)
