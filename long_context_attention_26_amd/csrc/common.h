@@ -46,6 +46,12 @@ __device__ __forceinline__ uint32_t bf16_key(uint32_t h) {
   return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
 }
 
+// max(x, 0) in one instruction (median of x, 0, +inf); fmaxf costs a canonicalizing max
+// first.  The sign of a zero result is not defined; callers add it to a +0-started sum.
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_amdgcn_fmed3f(x, 0.0f, __builtin_inff());
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
       if (sub == 0 && j < end) {
         float s = 0.0f;
 #pragma unroll
-        for (int g = 0; g < HI; ++g) s = fmaf(w[g], fmaxf(part[g], 0.0f), s);
+        for (int g = 0; g < HI; ++g) s = fmaf(w[g], relu(part[g]), s);
         s += 0.0f;  // -0 -> +0
         if constexpr (SBF16)
           s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
@@ -177,87 +177,193 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
 
 // ------------------------------------------------------------------ prefill GEMM
 // Many query tokens per sequence (chunked prefill): the indexer is a GEMM
-// [Nq*H_I x d_I] x [d_I x N] on v_mfma_f32_32x32x16_bf16.  A wave owns 32 rows (32/H_I query
-// tokens x H_I heads, operand A kept in registers) and walks its block's key range 32 keys
-// at a time (operand B loaded straight from global; the block's 4 waves read the same keys,
-// so most loads hit the L1/L2).  Output lane layout: register r of lane l holds row
-// 8*(r/4) + 4*(l/32) + r%4 and key l%32, so the H_I <= 4 heads of a query token sit in
-// consecutive registers of one lane and the ReLU / weight / head-sum epilogue is lane-local.
+// [Nq*H_I x d_I] x [d_I x N] on v_mfma_f32_32x32x16_bf16.  A block of W waves owns 32*W
+// consecutive rows (row = query token * H_I + head, all in one sequence); each wave keeps
+// its 32-row tile of operand A in registers.  The block walks its key range 128 keys at a
+// time: the 128 x d_I key tile is loaded once per block into LDS (double buffered, the next
+// tile's global loads in flight during the current tile's MFMAs) and every wave reads its
+// operand B from there.  Within a tile the four 32-key sub-tiles ping-pong between two
+// accumulator sets, so one sub-tile's epilogue overlaps the next one's MFMAs.  Output lane
+// layout: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 of the tile and key l%32,
+// so the H_I <= 4 heads of a query token sit in consecutive registers of one lane and the
+// ReLU / weight / head-sum epilogue is lane-local.  A wave stages a sub-tile's scores in LDS
+// as [token][32 keys] and writes each token's 32 scores with 16-byte stores; sub-tiles that
+// straddle the causal edge of the block's tokens are written score by score, masked.
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16g;
 
-template <int HI, bool SBF16>
-__global__ __launch_bounds__(256) void index_scores_gemm_kernel(IdxDev A) {
+// fp32 -> bf16 bits, round to nearest even (the gfx950 conversion instruction): a pair
+// (a in the low half) and one value
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
+}
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return static_cast<uint16_t>(bf16_pair(x, x) & 0xffffu);
+}
+
+constexpr int kGemmKeys = 32;           // keys per MFMA tile
+constexpr int kGemmTile = 128;          // keys per LDS tile (four MFMA tiles)
+
+template <int HI, bool SBF16, int KSTEPS, int NT>
+__global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
+  constexpr int DI = KSTEPS * 16;                 // channels
+  constexpr int STRIDE = DI + 8;                  // LDS row pitch (elements): no bank conflicts
+  constexpr int CHUNKS = kGemmTile * DI / 8;      // 16-byte pieces of one key tile
+  constexpr int QPL = 16 / HI;                    // query tokens per lane
+  constexpr int TOK = 32 / HI;                    // query tokens of a wave
+  constexpr int ES = SBF16 ? 2 : 4;               // score bytes
+  __shared__ __align__(16) uint16_t s_k[2][kGemmTile * STRIDE];
+  __shared__ __align__(16) uint32_t s_o[NT / 64][TOK * kGemmKeys * ES / 4];   // per wave
+  // 16-byte score stores need 16-byte aligned rows
+  const bool vec_out = (A.N * ES) % 16 == 0 && reinterpret_cast<uintptr_t>(A.scores) % 16 == 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.y) * 4 + wave) * 32;   // first row of the wave
-  const int q_first = static_cast<int>(row0 / HI);             // first query row (b*Nq + i)
-  const int rows_total = A.rows_total;                          // B*Nq*H_I
-  if (row0 >= rows_total) return;
-  const int b = q_first / A.Nq;                                 // whole wave in one sequence
+  constexpr int64_t rows_block = NT / 64 * 32;
+  const int64_t row0_block = blockIdx.y * rows_block;
+  const int64_t row0 = row0_block + static_cast<int64_t>(wave) * 32;   // wave's first row
+  const int64_t tok0 = row0 / HI;                 // the wave's first query token
+  const int b = static_cast<int>(row0_block / HI) / A.Nq;   // the block's sequence
   const int kstart = blockIdx.x * A.chunk;
   const int kend = min(kstart + A.chunk, A.N);
-  // visible keys of the wave's last query token bound the keys worth computing
-  const int q_last = q_first + 32 / HI - 1;
-  const int64_t p_last = A.pos0 + (q_last % A.Nq);
-  const int64_t nv_last64 = (p_last + 1) / A.ratio;
-  const int nv_last = static_cast<int>(nv_last64 < A.N ? nv_last64 : A.N);
-  const int kstop = min(kend, nv_last);
-  if (kstart >= kstop) return;
+  auto visible_tok = [&](int64_t tok) -> int {
+    const int64_t p = A.pos0 + tok % A.Nq;
+    const int64_t v = (p + 1) / A.ratio;
+    return static_cast<int>(v < A.N ? v : A.N);
+  };
+  // tokens ascend with rows: the block's first token sees the fewest keys, its last the most
+  const int nv_lo = visible_tok(row0_block / HI);
+  const int kstop = min(kend, visible_tok((row0_block + rows_block - 1) / HI));
+  if (kstart >= kstop) return;                    // whole block: no barrier reached
 
-  // operand A: row col of the wave (query q_first + col/HI, head col%HI), 16 channels per step
-  const int ksteps = A.d_I / 16;
-  const uint16_t* qrow = static_cast<const uint16_t*>(A.q) + (row0 + col) * A.d_I + 8 * half;
-  u32x4 qa[8];
+  u32x4 qa[KSTEPS];                               // operand A: row col, 16 channels per step
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(A.q) + (row0 + col) * DI + 8 * half;
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    qa[s] = s < ksteps ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
-  // weights and visible counts of the query tokens whose scores this lane writes
-  constexpr int QPL = 16 / HI;          // query tokens per lane (one per group of HI registers)
+    for (int s = 0; s < KSTEPS; ++s) qa[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
+  }
+  // this lane's score groups t: rows 8*(t*HI/4) + 4*half + t*HI%4 .. +HI-1 of the tile
   float w[QPL][HI];
-  int nvq[QPL];
-  int64_t qrow_idx[QPL];
+  int qloc[QPL];                    // token within the wave
+  int nvt[QPL];                     // its visible count (sub-tiles at the causal edge)
 #pragma unroll
   for (int t = 0; t < QPL; ++t) {
-    const int r0 = t * HI;                                      // first register of the group
-    const int row_in_wave = 8 * (r0 >> 2) + 4 * half + (r0 & 3);
-    const int qi = q_first + row_in_wave / HI;
-    qrow_idx[t] = qi;
+    const int r0 = t * HI;
+    qloc[t] = (8 * (r0 >> 2) + 4 * half + (r0 & 3)) / HI;
 #pragma unroll
-    for (int g = 0; g < HI; ++g) w[t][g] = A.w[static_cast<int64_t>(qi) * HI + g];
-    const int64_t p = A.pos0 + (qi % A.Nq);
-    const int64_t v = (p + 1) / A.ratio;
-    nvq[t] = static_cast<int>(v < A.N ? v : A.N);
+    for (int g = 0; g < HI; ++g) w[t][g] = A.w[(tok0 + qloc[t]) * HI + g];
+    nvt[t] = visible_tok(tok0 + qloc[t]);
   }
-  const uint16_t* kbase = static_cast<const uint16_t*>(A.k) + b * A.k_bstride + 8 * half;
-  for (int j0 = kstart; j0 < kstop; j0 += 32) {
-    const int j = j0 + col;
-    u32x4 kb[8];
-    const bool jv = j < kstop;
+  const uint16_t* kseq = static_cast<const uint16_t*>(A.k) + static_cast<int64_t>(b) * A.k_bstride;
+  constexpr int PPT = (CHUNKS + NT - 1) / NT;     // key-tile pieces per thread
+  u32x4 pf[PPT];
+  auto fetch = [&](int j0) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      kb[s] = (s < ksteps && jv)
-                  ? *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * A.d_I + 16 * s)
-                  : u32x4{0, 0, 0, 0};
-    f32x16g d = {};
+    for (int u = 0; u < PPT; ++u) {
+      const int c = threadIdx.x + u * NT;
+      const int key = c / (DI / 8), part = c % (DI / 8);
+      pf[u] = (c < CHUNKS && j0 + key < A.N)
+                  ? *reinterpret_cast<const u32x4*>(kseq + static_cast<int64_t>(j0 + key) * DI + 8 * part)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&](int buf) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s < ksteps)
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[s]),
-                                                    __builtin_bit_cast(bf16x8, kb[s]), d, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < QPL; ++t) {
-      float sc = 0.0f;
-#pragma unroll
-      for (int g = 0; g < HI; ++g) sc = fmaf(w[t][g], fmaxf(d[t * HI + g], 0.0f), sc);
-      sc += 0.0f;
-      if (jv && j < nvq[t]) {
-        if constexpr (SBF16)
-          static_cast<uint16_t*>(A.scores)[qrow_idx[t] * A.N + j] =
-              static_cast<uint16_t>(f32_to_bf16_bits(sc));
-        else
-          static_cast<float*>(A.scores)[qrow_idx[t] * A.N + j] = sc;
+    for (int u = 0; u < PPT; ++u) {
+      const int c = threadIdx.x + u * NT;
+      if (c < CHUNKS) {
+        const int key = c / (DI / 8), part = c % (DI / 8);
+        *reinterpret_cast<u32x4*>(&s_k[buf][key * STRIDE + 8 * part]) = pf[u];
       }
     }
+  };
+  auto mma = [&](f32x16g& d, int buf, int sub) {
+    u32x4 kb[KSTEPS];                             // operand B: key col, channels 16s + 8*half
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      kb[s] = *reinterpret_cast<const u32x4*>(
+          &s_k[buf][(sub * kGemmKeys + col) * STRIDE + 16 * s + 8 * half]);
+    d = f32x16g{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[s]),
+                                                  __builtin_bit_cast(bf16x8, kb[s]), d, 0, 0, 0);
+  };
+  // scores sum_g w_g max(d_g, 0) of the sub-tile starting at key js (a +0-started chain
+  // never ends at -0)
+  auto emit = [&](const f32x16g& d, int js) {
+    const int j = js + col;
+    float sc[QPL];
+#pragma unroll
+    for (int t = 0; t < QPL; ++t) {
+      float v = 0.0f;
+#pragma unroll
+      for (int g = 0; g < HI; ++g) v = fmaf(w[t][g], relu(d[t * HI + g]), v);
+      sc[t] = v;
+    }
+    if (vec_out && js + kGemmKeys <= nv_lo) {
+      // every token of the block sees the whole sub-tile
+#pragma unroll
+      for (int t = 0; t < QPL; t += 2) {
+        if constexpr (SBF16) {
+          uint16_t* o16 = reinterpret_cast<uint16_t*>(&s_o[wave][0]);
+          const uint32_t pk = bf16_pair(sc[t], sc[t + 1]);
+          o16[qloc[t] * kGemmKeys + col] = static_cast<uint16_t>(pk & 0xffffu);
+          o16[qloc[t + 1] * kGemmKeys + col] = static_cast<uint16_t>(pk >> 16);
+        } else {
+          float* o32 = reinterpret_cast<float*>(&s_o[wave][0]);
+          o32[qloc[t] * kGemmKeys + col] = sc[t];
+          o32[qloc[t + 1] * kGemmKeys + col] = sc[t + 1];
+        }
+      }
+      constexpr int EPP = 16 / ES;                 // scores per 16-byte piece
+      constexpr int PPQ = kGemmKeys / EPP;         // pieces per token
+      constexpr int NPIECE = TOK * PPQ;
+#pragma unroll
+      for (int p0 = 0; p0 < NPIECE; p0 += 64) {
+        const int p = p0 + lane;
+        if (NPIECE % 64 == 0 || p < NPIECE) {
+          const int ql = p / PPQ, kp = p % PPQ;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(
+              reinterpret_cast<const char*>(&s_o[wave][0]) + (ql * kGemmKeys + kp * EPP) * ES);
+          *reinterpret_cast<u32x4*>(static_cast<char*>(A.scores) +
+                                    ((tok0 + ql) * A.N + js + kp * EPP) * ES) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < QPL; ++t) {
+        if (j < nvt[t] && j < kstop) {
+          const int64_t o = (tok0 + qloc[t]) * A.N + j;
+          if constexpr (SBF16)
+            static_cast<uint16_t*>(A.scores)[o] = bf16_bits(sc[t]);
+          else
+            static_cast<float*>(A.scores)[o] = sc[t];
+        }
+      }
+    }
+  };
+
+  fetch(kstart);
+  stash(0);
+  __syncthreads();
+  int buf = 0;
+  for (int j0 = kstart; j0 < kstop; j0 += kGemmTile) {
+    const bool more = j0 + kGemmTile < kstop;
+    if (more) fetch(j0 + kGemmTile);              // in flight during this tile
+    const int nsub = min(kGemmTile, kstop - j0 + kGemmKeys - 1) / kGemmKeys;   // block-uniform
+    f32x16g da, db;
+    mma(da, buf, 0);
+#pragma unroll
+    for (int u = 0; u < kGemmTile / kGemmKeys; u += 2) {
+      if (u + 1 < nsub) mma(db, buf, u + 1);
+      if (u < nsub) emit(da, j0 + u * kGemmKeys);
+      if (u + 2 < nsub) mma(da, buf, u + 2);
+      if (u + 1 < nsub) emit(db, j0 + (u + 1) * kGemmKeys);
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
 }
 
@@ -430,7 +536,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
       if (sub == 0 && j < end) {
         float s = 0.0f;
 #pragma unroll
-        for (int g = 0; g < HI; ++g) s = fmaf(w[g], fmaxf(part[g], 0.0f), s);
+        for (int g = 0; g < HI; ++g) s = fmaf(w[g], relu(part[g]), s);
         s += 0.0f;
         if constexpr (SBF16)
           s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
@@ -549,7 +655,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int g = 8 * (r >> 2) + 4 * half + (r & 3);
-        if (g < HI) part = fmaf(w[g], fmaxf(d[r], 0.0f), part);
+        if (g < HI) part = fmaf(w[g], relu(d[r]), part);
       }
       if constexpr (HI > 4) part += __shfl_xor(part, 32, kWave);
       const int j = j0 + u * 128 + col;
@@ -677,24 +783,29 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.hist = hist;
   A.topk = k;
   const int rows = B * Nq;
-  // many query tokens per sequence: the GEMM form on the matrix cores
-  if (k_dtype == 1 && (H_I == 1 || H_I == 2 || H_I == 4) && Nq * H_I >= 128 &&
-      (Nq * H_I) % 32 == 0 && d_I % 16 == 0 && d_I <= 128) {
+  // many query tokens per sequence: the GEMM form on the matrix cores, for sequences whose
+  // rows split into whole blocks of 256 rows (8 waves) or 128 rows (4 waves)
+  const int seq_rows = Nq * H_I;
+  if (k_dtype == 1 && (H_I == 1 || H_I == 2 || H_I == 4) && seq_rows % 128 == 0 &&
+      (d_I == 32 || d_I == 64 || d_I == 128)) {
     A.rows_total = rows * H_I;
-    A.chunk = 4096;
-    dim3 grid((N + A.chunk - 1) / A.chunk, (A.rows_total + 127) / 128);
-    hipError_t e;
-    if (H_I == 1) {
-      if (score_dtype == 1) launch_timed(index_scores_gemm_kernel<1, true>, grid, dim3(256), s, A);
-      else launch_timed(index_scores_gemm_kernel<1, false>, grid, dim3(256), s, A);
-    } else if (H_I == 2) {
-      if (score_dtype == 1) launch_timed(index_scores_gemm_kernel<2, true>, grid, dim3(256), s, A);
-      else launch_timed(index_scores_gemm_kernel<2, false>, grid, dim3(256), s, A);
-    } else {
-      if (score_dtype == 1) launch_timed(index_scores_gemm_kernel<4, true>, grid, dim3(256), s, A);
-      else launch_timed(index_scores_gemm_kernel<4, false>, grid, dim3(256), s, A);
-    }
-    e = hipGetLastError();
+    const int nt = seq_rows % 256 == 0 ? 512 : 256;
+    A.chunk = 2048;
+    dim3 grid((N + A.chunk - 1) / A.chunk, A.rows_total / (nt / 2));
+    dim3 block(nt);
+    const bool sb = score_dtype == 1;
+#define HCSA_GEMM(HI_, KS_, NT_)                                                        \
+  if (H_I == HI_ && d_I == 16 * KS_ && nt == NT_) {                                    \
+    if (sb) launch_timed(index_scores_gemm_kernel<HI_, true, KS_, NT_>, grid, block, s, A); \
+    else launch_timed(index_scores_gemm_kernel<HI_, false, KS_, NT_>, grid, block, s, A);   \
+  }
+#define HCSA_GEMM_HI(HI_) \
+  HCSA_GEMM(HI_, 2, 256) HCSA_GEMM(HI_, 2, 512) HCSA_GEMM(HI_, 4, 256) \
+  HCSA_GEMM(HI_, 4, 512) HCSA_GEMM(HI_, 8, 256) HCSA_GEMM(HI_, 8, 512)
+    HCSA_GEMM_HI(1) HCSA_GEMM_HI(2) HCSA_GEMM_HI(4)
+#undef HCSA_GEMM_HI
+#undef HCSA_GEMM
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess || hist == nullptr) return e;
     return launch_sel_hist(scores, score_dtype, N, B, Nq, N, ratio, pos0, k, hist, s);
   }

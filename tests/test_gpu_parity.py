@@ -212,8 +212,11 @@ def test_topk_deterministic(H, gpu):
     dict(kdt="mxfp4", H_I=16, d_I=64, N=1500, Nq=1, B=1, k=200, sdt="bf16"),
     # many query tokens per sequence: the prefill GEMM kernel
     dict(kdt="bf16", H_I=4, d_I=64, N=3000, Nq=64, B=2, k=256, sdt="bf16"),
-    dict(kdt="bf16", H_I=2, d_I=128, N=2000, Nq=96, B=1, k=100, sdt="f32"),
-    dict(kdt="bf16", H_I=1, d_I=64, N=5000, Nq=160, B=1, k=512, sdt="bf16"),
+    dict(kdt="bf16", H_I=2, d_I=128, N=2000, Nq=64, B=1, k=100, sdt="f32"),
+    dict(kdt="bf16", H_I=1, d_I=64, N=5000, Nq=384, B=1, k=512, sdt="bf16"),
+    dict(kdt="bf16", H_I=4, d_I=32, N=4100, Nq=256, B=2, k=300, sdt="bf16"),
+    dict(kdt="bf16", H_I=4, d_I=64, N=8000, Nq=512, B=2, k=512, sdt="bf16"),
+    dict(kdt="bf16", H_I=2, d_I=64, N=2500, Nq=96, B=1, k=64, sdt="f32"),   # wave kernel
 ])
 def test_index_scores_and_topk(H, gpu, case):
     print(f"indexer {case}", flush=True)
