@@ -23,6 +23,8 @@
 //                        lane reads a 16-byte slice of 8 V rows and byte-permutes them into
 //                        the A operand of 8 channel tiles (channel 8*i + tile), so no LDS
 //                        transpose is needed.  The 4 waves of a block merge in LDS.
+//   hca_tiled_kernel     HCA with many query tokens per sequence (chunked prefill): 16
+//                        tokens share each streamed tile of entries (see its comment).
 //   attn_generic_kernel  any head count / head dim, fp32 or bf16, plain VALU (small and
 //                        fp32 shapes).
 //   lse_merge_kernel     o = sum_s e^{lse_s - L} o_s, L = log sum_s e^{lse_s}.
@@ -340,6 +342,181 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
   }
 }
 
+// ------------------------------------------------------------------ HCA, many query tokens
+
+// Chunked prefill (many query tokens per sequence): consecutive tokens see almost the same
+// HCA entries, so a block takes 16 tokens x 16 heads (8 waves, each 2 tokens x 16 heads =
+// 32 query rows) and streams the entries once for all of them in 64-entry tiles through
+// LDS (K rows and V transposed, double buffered, the next tile's loads in flight).  Per
+// 32-entry half tile a wave computes S^T = K Q^T on v_mfma_f32_32x32x16_bf16: lane
+// (column) = query row, register r = entry 8*(r/4) + 4*(lane/32) + r%4, so the online
+// softmax is lane-local (two lanes share a row) and the probabilities, packed to bf16, are
+// already the B operand of O^T += V^T P^T: step s takes registers 8s..8s+7, which hold
+// entries 16s + 8*(e/4) + 4*(lane/32) + e%4 -- the A operand (V^T) reads the same
+// entries, two runs of four, from the transposed tile.  Both halves' S^T products are
+// issued before the softmax so the matrix cores stay busy, there is one running-max update
+// per tile, and the accumulator rescale is skipped when no row's maximum moved.
+constexpr int kTokTile = 16;              // query tokens per block
+constexpr int kHKeys = 64;                // entries per tile (two MFMA tiles)
+constexpr int kKPitch = 128 + 8;          // K tile row pitch (elements): no bank conflicts
+constexpr int kVPitch = kHKeys + 8;       // V^T tile row pitch (elements)
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16a;
+
+__device__ __forceinline__ f32x16a mfma32x32x16(const u32x4& a, const u32x4& b, f32x16a c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// grid: (ceil(Nq / 16), B); block 512.
+__global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
+  __shared__ __align__(16) uint16_t s_k[2][kHKeys * kKPitch];
+  __shared__ __align__(16) uint16_t s_vt[2][128 * kVPitch];
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kTokTile;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  const int tok = t0 + 2 * wave + (col >> 4);     // this lane's query row: token, head
+  const int head = col & 15;
+  const bool tok_ok = tok < A.Nq;
+  auto visible = [&](int t) -> int {
+    const int64_t p = A.pos0 + t;
+    const int64_t v = (p + 1) / A.ratio;
+    return static_cast<int>(v < A.N ? v : A.N);
+  };
+  const int nv = tok_ok ? visible(tok) : 0;
+  const int nv_max = visible(min(t0 + kTokTile, A.Nq) - 1);   // tokens ascend
+  const int ntiles = (nv_max + kHKeys - 1) / kHKeys;
+  const int64_t row = static_cast<int64_t>(b) * A.Nq + tok;
+
+  u32x4 qb[8];                                    // B of S^T: Q[row][16s + 8hh .. +7]
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(A.q) + (row * 16 + head) * 128 + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qb[s] = tok_ok ? *reinterpret_cast<const u32x4*>(qr + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const uint16_t* kseq = static_cast<const uint16_t*>(A.kc) + b * A.c_bstride;
+  const uint16_t* vseq = static_cast<const uint16_t*>(A.vc) + b * A.c_bstride;
+  // tile loads: thread i moves K channels 8*(i%16) .. +7 of entries i/16 and i/16 + 32, and
+  // V channels 8*(i%16) .. +7 of entries 2*(i/16) and 2*(i/16)+1 (packed in pairs for the
+  // transposed tile)
+  const int lkey = threadIdx.x >> 4, lpart = threadIdx.x & 15;
+  u32x4 kf[2], vf[2];
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ek = tile * kHKeys + lkey + 32 * u;
+      kf[u] = ek < A.N ? *reinterpret_cast<const u32x4*>(kseq + static_cast<int64_t>(ek) * 128 + 8 * lpart)
+                       : u32x4{0u, 0u, 0u, 0u};
+      const int ev = tile * kHKeys + 2 * lkey + u;
+      vf[u] = ev < A.N ? *reinterpret_cast<const u32x4*>(vseq + static_cast<int64_t>(ev) * 128 + 8 * lpart)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<u32x4*>(&s_k[buf][(lkey + 32 * u) * kKPitch + 8 * lpart]) = kf[u];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {                 // channel 8*lpart + 2c (+1): entries 2*lkey, +1
+      const uint32_t lo = (vf[0][c] & 0xffffu) | (vf[1][c] << 16);
+      const uint32_t hi = (vf[0][c] >> 16) | (vf[1][c] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * lpart + 2 * c) * kVPitch + 2 * lkey]) = lo;
+      *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * lpart + 2 * c + 1) * kVPitch + 2 * lkey]) = hi;
+    }
+  };
+
+  f32x16a acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16a{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float sl2 = A.scale * 1.4426950408889634f;   // logits in base 2
+
+  if (ntiles > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const bool more = tile + 1 < ntiles;
+    if (more) fetch(tile + 1);
+    // S^T of both halves: A = K rows (entry 32h + col), k-slots 16s + 8hh
+    f32x16a st[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      st[h2] = f32x16a{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        st[h2] = mfma32x32x16(
+            *reinterpret_cast<const u32x4*>(&s_k[buf][(32 * h2 + col) * kKPitch + 16 * s + 8 * hh]),
+            qb[s], st[h2]);
+    }
+    const int kb = tile * kHKeys;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = kb + 32 * h2 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        st[h2][r] = e < nv ? st[h2][r] * sl2 : -INFINITY;
+        mx = fmaxf(mx, st[h2][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    if (__ballot(m_new > m_run)) {                // some row's maximum moved: rescale
+      const float alpha = m_new > m_run ? exp2f(m_run - m_new) : 1.0f;   // exp2(-inf) = 0
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mref = m_run == -INFINITY ? 0.0f : m_run;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      u32x4 pb[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float p0 = exp2f(st[h2][8 * s + 2 * m] - mref);
+          const float p1 = exp2f(st[h2][8 * s + 2 * m + 1] - mref);
+          l_run += p0 + p1;
+          pb[s][m] = pack_bf16x2(p0, p1);
+        }
+      // O^T tiles: A = V^T rows (channel 32ct + col), entries 32h + 16s + 4hh + 0..3 and +8
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint16_t* vr = &s_vt[buf][(32 * ct + col) * kVPitch + 32 * h2 + 16 * s + 4 * hh];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+          acc[ct] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[s], acc[ct]);
+        }
+      }
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!tok_ok) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  float* o = A.out + (row * 16 + head) * 128;
+  // acc[ct] register r: channel 32ct + 8*(r/4) + 4*hh + r%4
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(o + 32 * ct + 8 * q + 4 * hh) =
+          f32x4{acc[ct][4 * q] * inv, acc[ct][4 * q + 1] * inv, acc[ct][4 * q + 2] * inv,
+                acc[ct][4 * q + 3] * inv};
+  if (hh == 0)
+    A.lse[row * 16 + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+}
+
 // ------------------------------------------------------------------ merge
 
 // grid: (H, rows); block = d threads (<= 256).  The split weights of the (row, head) are
@@ -411,11 +588,17 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len) {
-  (void)csa;
   AttnPlan p{};
   p.rows = B * Nq;
   p.max_len = max_len;
   p.mfma = kv_dtype == 1 && H == 16 && d == 128;
+  p.tiled = !csa && p.mfma && Nq >= kTokTile;
+  if (p.tiled) {                                  // one pass per 16-token tile, no splits
+    p.chunk = std::max(max_len, 1);
+    p.splits = 1;
+    p.part_bytes = p.total_bytes = 0;
+    return p;
+  }
   if (p.mfma) {
     // about two blocks per CU over the whole call, 128-key granules, at most kMfmaMaxChunk
     const int64_t total = static_cast<int64_t>(p.rows) * std::max(max_len, 1);
@@ -474,6 +657,10 @@ hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, v
   } else {
     A.out = a.out;
     A.lse = a.lse;
+  }
+  if (plan.tiled) {
+    hca_tiled_kernel<<<dim3((a.Nq + kTokTile - 1) / kTokTile, a.B), 512, 0, s>>>(A);
+    return hipGetLastError();
   }
   dim3 grid(plan.splits, plan.rows);
   if (plan.mfma) {

@@ -72,7 +72,7 @@ struct AttnArgs {
 };
 struct AttnPlan {
   int rows, max_len, chunk, splits;
-  bool mfma;
+  bool mfma, tiled;
   size_t part_bytes, total_bytes;
 };
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len);

@@ -330,6 +330,9 @@ def test_csa_sparse_attention(H, gpu, case):
     dict(dt="bf16", H=16, d=128, N=1024, Nq=1, B=2, pos0=131071),     # config 2 shape
     dict(dt="bf16", H=16, d=128, N=5000, Nq=1, B=1, pos0=640000 - 1), # many splits
     dict(dt="bf16", H=16, d=128, N=40, Nq=300, B=1, pos0=4900),       # causal prefill rows
+    dict(dt="bf16", H=16, d=128, N=2100, Nq=64, B=2, pos0=128 * 2000 - 30),  # 16-token tiles
+    dict(dt="bf16", H=16, d=128, N=8, Nq=40, B=1, pos0=100),          # tiles partly empty
+    dict(dt="bf16", H=16, d=128, N=300, Nq=33, B=3, pos0=128 * 290),  # ragged last tile
     dict(dt="bf16", H=8, d=64, N=50, Nq=3, B=2, pos0=6399),           # generic path
     dict(dt="bf16", H=16, d=128, N=8, Nq=2, B=1, pos0=100),           # nothing visible
 ])
