@@ -75,7 +75,7 @@ const char *hcsa_last_error(void);
 
 /*
  * Kernel timing for benchmarks and profiling: the next indexer-score kernel launched by
- * this thread (hcsa_csa_index_scores, _hist or _topk) records start_event and stop_event
+ * this thread (hcsa_csa_index_scores or hcsa_csa_index_topk) records start_event and stop_event
  * (hipEvent_t, timing enabled) as part of its own dispatch, so their elapsed time is the
  * kernel's execution alone.  NULL, NULL cancels.  Not for use under graph capture.
  */
@@ -137,10 +137,13 @@ int hcsa_mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int D, uint8_t
  *         scores[r][0..n) are read.
  * idx     [B*Nq][k] int32 output: the min(k, n) entries with the largest scores (ties to
  *         the lowest index) in ascending order, then -1.  Bit-exact and deterministic.
- * Limits: 1 <= k <= 4096, 1 <= N, row_stride >= N, ratio >= 1, pos0 >= 0.
+ * Limits: 1 <= k <= 4096, 1 <= N <= 2^25, row_stride >= N, ratio >= 1, pos0 >= 0.
  * Workspace: caller-owned device memory of hcsa_topk_workspace_size bytes, 256-byte
- * aligned.  The size is 0 (workspace may be NULL) when at least 64 rows of at most 131072
- * scores are resolved one block per row with on-chip state only.
+ * aligned, fully rewritten by each call (no state is kept between calls).  The size is 0
+ * (workspace may be NULL) when at least 64 rows of at most 131072 scores are resolved one
+ * block per row with on-chip state only; otherwise it holds per-row candidate lists of
+ * about 8 KB per 8192 entries.  Scoring and selection as two calls (hcsa_csa_index_scores,
+ * then hcsa_topk on its scores) give the result of hcsa_csa_index_topk.
  */
 size_t hcsa_topk_workspace_size(int score_dtype, int B, int Nq, int N, int k);
 int hcsa_topk(const void *scores, int score_dtype, int64_t row_stride, int B, int Nq, int N,
@@ -180,29 +183,6 @@ int hcsa_csa_index_scores(const void *q_idx, int q_dtype, const float *w_idx,
                           const uint8_t *k_scales, int64_t ks_bstride, int B, int Nq, int H_I,
                           int d_I, int N, int ratio, int64_t pos0, int score_dtype,
                           void *scores, hcsa_stream stream);
-
-/*
- * Split-phase form of hcsa_csa_index_topk, for callers that schedule (or time) the
- * indexer kernel on its own.  With one workspace of hcsa_topk_workspace_size(score_dtype,
- * B, Nq, N, k) bytes, in stream order:
- *   hcsa_topk_clear             zero the selector's histogram and candidate counters;
- *   hcsa_csa_index_scores_hist  scores (as hcsa_csa_index_scores) plus, in the same kernel,
- *                               the selector's histogram of every row's scores;
- *   hcsa_topk_from_hist         the selection of hcsa_topk, reusing that histogram.
- * The result equals hcsa_csa_index_topk's.  Arguments have the meanings and limits given
- * above; `scores` is [B*Nq][N].
- */
-int hcsa_topk_clear(int score_dtype, int B, int Nq, int N, int k, void *workspace,
-                    size_t ws_bytes, hcsa_stream stream);
-int hcsa_csa_index_scores_hist(const void *q_idx, int q_dtype, const float *w_idx,
-                               const void *k_idx, int k_dtype, int64_t k_bstride,
-                               const uint8_t *k_scales, int64_t ks_bstride, int B, int Nq,
-                               int H_I, int d_I, int N, int ratio, int64_t pos0, int k,
-                               int score_dtype, void *scores, void *workspace, size_t ws_bytes,
-                               hcsa_stream stream);
-int hcsa_topk_from_hist(const void *scores, int score_dtype, int64_t row_stride, int B, int Nq,
-                        int N, int ratio, int64_t pos0, int k, int32_t *idx, void *workspace,
-                        size_t ws_bytes, hcsa_stream stream);
 
 /*
  * CSA sparse attention [Lighthouse section 八 item 3]: for each query token (position

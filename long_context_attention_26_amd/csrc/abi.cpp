@@ -169,6 +169,8 @@ static int check_topk_args(int score_dtype, int B, int Nq, int N, int ratio, int
   if (B < 1 || Nq < 1) return fail(HCSA_EINVAL, "B and Nq must be >= 1");
   if (static_cast<int64_t>(B) * Nq > 65535) return fail(HCSA_EINVAL, "B*Nq must be <= 65535");
   if (N < 1) return fail(HCSA_EINVAL, "N must be >= 1");
+  if (!hcsa::topk_plan_ok(hcsa::plan_topk(score_dtype, B * Nq, N, 1)))
+    return fail(HCSA_EINVAL, "N too large for the selector (at most 2^25 entries per row)");
   if (k < 1 || k > 4096) return fail(HCSA_EINVAL, "k must be in [1, 4096]");
   if (ratio < 1) return fail(HCSA_EINVAL, "ratio must be >= 1");
   if (pos0 < 0) return fail(HCSA_EINVAL, "pos0 must be >= 0");
@@ -241,60 +243,9 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
   if (!aligned16(scores)) return fail(HCSA_EALIGN, "scores must be 16-byte aligned");
   return hip_status(hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
                                               k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                              pos0, score_dtype, scores, nullptr, 0,
+                                              pos0, score_dtype, scores,
                                               static_cast<hipStream_t>(stream)),
                     "hcsa_csa_index_scores");
-}
-
-int hcsa_topk_clear(int score_dtype, int B, int Nq, int N, int k, void* workspace,
-                    size_t ws_bytes, hcsa_stream stream) {
-  int rc = check_topk_args(score_dtype, B, Nq, N, 1, 0, k);
-  if (rc) return rc;
-  const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
-  rc = check_ws(workspace, ws_bytes, plan.total_bytes);
-  if (rc) return rc;
-  return hip_status(hcsa::launch_topk_clear(plan, workspace, static_cast<hipStream_t>(stream)),
-                    "hcsa_topk_clear");
-}
-
-int hcsa_csa_index_scores_hist(const void* q_idx, int q_dtype, const float* w_idx,
-                               const void* k_idx, int k_dtype, int64_t k_bstride,
-                               const uint8_t* k_scales, int64_t ks_bstride, int B, int Nq,
-                               int H_I, int d_I, int N, int ratio, int64_t pos0, int k,
-                               int score_dtype, void* scores, void* workspace, size_t ws_bytes,
-                               hcsa_stream stream) {
-  int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
-  if (rc) return rc;
-  rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
-                        B, Nq, H_I, d_I, N);
-  if (rc) return rc;
-  if (!scores) return fail(HCSA_EINVAL, "scores must be non-null");
-  if (!aligned16(scores)) return fail(HCSA_EALIGN, "scores must be 16-byte aligned");
-  const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
-  rc = check_ws(workspace, ws_bytes, plan.total_bytes);
-  if (rc) return rc;
-  return hip_status(hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
-                                              k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                              pos0, score_dtype, scores,
-                                              static_cast<uint32_t*>(workspace), k,
-                                              static_cast<hipStream_t>(stream)),
-                    "hcsa_csa_index_scores_hist");
-}
-
-int hcsa_topk_from_hist(const void* scores, int score_dtype, int64_t row_stride, int B, int Nq,
-                        int N, int ratio, int64_t pos0, int k, int32_t* idx, void* workspace,
-                        size_t ws_bytes, hcsa_stream stream) {
-  int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
-  if (rc) return rc;
-  if (row_stride < N) return fail(HCSA_EINVAL, "row_stride < N");
-  if (!scores || !idx) return fail(HCSA_EINVAL, "scores and idx must be non-null");
-  if (!aligned16(scores) || !aligned16(idx)) return fail(HCSA_EALIGN, "scores and idx must be 16-byte aligned");
-  const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
-  rc = check_ws(workspace, ws_bytes, plan.total_bytes);
-  if (rc) return rc;
-  return hip_status(hcsa::launch_topk_select(plan, scores, row_stride, Nq, ratio, pos0, idx,
-                                             workspace, false, static_cast<hipStream_t>(stream)),
-                    "hcsa_topk_from_hist");
 }
 
 int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, const void* k_idx,
@@ -318,13 +269,11 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* scores = scores_out ? scores_out : workspace;
   void* tws = static_cast<char*>(workspace) + sbytes;
-  hipError_t e = hcsa::launch_topk_clear(plan, tws, s);
-  if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (clear)");
-  e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales,
-                                ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, score_dtype,
-                                scores, static_cast<uint32_t*>(tws), k, s);
+  hipError_t e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
+                                           k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
+                                           pos0, score_dtype, scores, s);
   if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (scores)");
-  e = hcsa::launch_topk_select(plan, scores, N, Nq, ratio, pos0, topk_idx, tws, false, s);
+  e = hcsa::launch_topk(plan, scores, score_dtype, N, Nq, ratio, pos0, topk_idx, tws, s);
   return hip_status(e, "hcsa_csa_index_topk (select)");
 }
 

@@ -14,7 +14,6 @@
 #include <hip/hip_ext.h>
 
 #include "internal.h"
-#include "select_common.h"
 
 namespace hcsa {
 
@@ -49,10 +48,16 @@ struct IdxDev {
   int64_t pos0;
   void* scores;      // [rows][N]
   int chunk;
-  uint32_t* hist;    // optional selector workspace (see select_common.h)
-  int topk;
   int rows_total;    // B*Nq*H_I (prefill GEMM)
 };
+
+// Keys per block of the decode kernels: enough blocks to cover every CU several times even
+// for one sequence, and at least 256 keys so a block issues a few loads per lane.
+inline int index_chunk(int rows, int N) {
+  int64_t c = static_cast<int64_t>(N) * rows / 2048;
+  c = (c + 255) / 256 * 256;
+  return static_cast<int>(c < 256 ? 256 : (c > 4096 ? 4096 : c));
+}
 
 
 __device__ __forceinline__ float dot16b_bf16(const u32x4& a, const u32x4& b, float acc) {
@@ -73,36 +78,6 @@ __device__ __forceinline__ float dot16b_f32(const u32x4& a, const u32x4& b, floa
   return acc;
 }
 
-// Selector histogram fused into the score kernels: a 4096-bin LDS histogram of the 12-bit
-// top digit of each stored score's order-preserving key, flushed with one global atomic per
-// non-empty bin.
-constexpr int kHistBins = 4096;
-
-__device__ __forceinline__ void hist_clear(uint32_t* h, bool on) {
-  if (on)
-    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
-  __syncthreads();
-}
-
-template <bool SBF16>
-__device__ __forceinline__ void hist_add(uint32_t* h, float s) {
-  if constexpr (SBF16)
-    atomicAdd(&h[bf16_key(f32_to_bf16_bits(s)) >> 4], 1u);
-  else
-    atomicAdd(&h[f32_key(__float_as_uint(s)) >> 20], 1u);
-}
-
-// Flushes the block histogram into replica (block % copies) of the row's histogram.
-__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* ws, int row, int N) {
-  __syncthreads();
-  const SelState S = sel_state(ws, gridDim.y, sel_copies(gridDim.y, N), 0);
-  uint32_t* grow = sel_hist_row(S, blockIdx.x % S.copies, row);
-  for (int i = threadIdx.x; i < kHistBins; i += 256) {
-    const uint32_t v = h[i];
-    if (v) atomicAdd(&grow[i], v);
-  }
-}
-
 // grid: (ceil(N / chunk), rows); block 256.
 template <int HI, int LPE, bool KBF16, bool SBF16>
 __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
@@ -121,9 +96,6 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
   const int sub = threadIdx.x % LPE;
   const int grp = threadIdx.x / LPE;
   const int row_bytes = A.d_I * ES;
-  __shared__ uint32_t s_hist[kHistBins];
-  const bool hist = A.hist != nullptr && A.topk < nv;
-  hist_clear(s_hist, hist);
 
   u32x4 qv[HI];
   float w[HI];
@@ -168,11 +140,9 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
           s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
         else
           s32[j] = s;
-        if (hist) hist_add<SBF16>(s_hist, s);
       }
     }
   }
-  if (hist) hist_flush(s_hist, A.hist, row, A.N);
 }
 
 // ------------------------------------------------------------------ prefill GEMM
@@ -392,20 +362,7 @@ hipError_t launch_lpe(const IdxDev& A, int rows, int H_I, int score_dtype, hipSt
 
 // ------------------------------------------------------------------ MXFP4 keys
 // Indexer keys stored as MXFP4 (e2m1 codes, one e8m0 scale per 32 channels); the query
-// vectors are quantized the same way at block start.  One lane owns one 32-channel block
-// of one key (16 code bytes + 1 scale byte), so a wave reads 64 contiguous blocks per
-// instruction.  Codes become exact small integers (twice the e2m1 value, in [-12, 12])
-// through a byte-permute table, and sdot4 accumulates exact integer block sums; each
-// block sum times 2^(e_q + e_k - 2) is exact in fp32.
-
-// 4 codes (one per byte, sign in bit 3) -> 4 int8 holding twice the e2m1 value.
-__device__ __forceinline__ uint32_t e2m1x4_to_i8x4(uint32_t c) {
-  const uint32_t m = c & 0x07070707u;
-  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, m);  // 0,1,2,3,4,6,8,12
-  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, m);  // negated
-  const uint32_t mask = ((c >> 3) & 0x01010101u) * 0xFFu;
-  return (neg & mask) | (pos & ~mask);
-}
+// vectors are quantized the same way at block start.
 
 struct IdxMxDev {
   const void* q;       // [rows][H_I][d_I] bf16 or f32
@@ -417,137 +374,7 @@ struct IdxMxDev {
   int64_t pos0;
   void* scores;
   int chunk;
-  uint32_t* hist;
-  int topk;
 };
-
-// grid: (ceil(N / kChunk), rows); block 256.  LPE = d_I / 32 lanes per key.
-template <int HI, int LPE, bool QBF16, bool SBF16>
-__global__ __launch_bounds__(256) void index_scores_mx_kernel(IdxMxDev A) {
-  constexpr int GROUPS = 256 / LPE;
-  constexpr int U = 4;
-  const int row = blockIdx.y;
-  const int b = row / A.Nq;
-  const int64_t p = A.pos0 + (row % A.Nq);
-  const int64_t nv64 = (p + 1) / A.ratio;
-  const int nv = static_cast<int>(nv64 < A.N ? nv64 : A.N);
-  const int start = blockIdx.x * A.chunk;
-  const int end = min(start + A.chunk, nv);
-  if (start >= end) return;
-  const int sub = threadIdx.x % LPE;
-  const int grp = threadIdx.x / LPE;
-
-  // Quantize every 32-channel block of every query head once per block (LDS), then each
-  // lane keeps the blocks it needs: words 0..3 hold elements 8c, 8c+2, 8c+4, 8c+6 and
-  // words 4..7 elements 8c+1, 8c+3, 8c+5, 8c+7 (c = word index mod 4), as int8 = 2*value.
-  __shared__ uint32_t s_q[16][4][8];
-  __shared__ int s_qe[16][4];
-  __shared__ uint32_t s_hist[kHistBins];
-  const bool hist = A.hist != nullptr && A.topk < nv;
-  if (hist)
-    for (int i = threadIdx.x; i < kHistBins; i += 256) s_hist[i] = 0;
-  if (threadIdx.x < HI * LPE) {
-    const int g = threadIdx.x / LPE, blk = threadIdx.x % LPE;
-    const int64_t off = (static_cast<int64_t>(row) * HI + g) * A.d_I + blk * 32;
-    float amax = 0.0f;
-    for (int e = 0; e < 32; ++e) {
-      const float v = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[off + e])
-                            : static_cast<const float*>(A.q)[off + e];
-      amax = fmaxf(amax, __builtin_fabsf(v));
-    }
-    const int se = mx_scale_exp(amax);
-    s_qe[g][blk] = se;
-    for (int c = 0; c < 4; ++c) {
-      uint32_t lo = 0, hi = 0;
-      for (int t = 0; t < 4; ++t) {
-        const int64_t i0 = off + 8 * c + 2 * t;
-        const float v0 = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[i0])
-                               : static_cast<const float*>(A.q)[i0];
-        const float v1 = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[i0 + 1])
-                               : static_cast<const float*>(A.q)[i0 + 1];
-        lo |= (static_cast<uint32_t>(e2m1_twice(e2m1_code(v0, se))) & 0xFFu) << (8 * t);
-        hi |= (static_cast<uint32_t>(e2m1_twice(e2m1_code(v1, se))) & 0xFFu) << (8 * t);
-      }
-      s_q[g][blk][c] = lo;
-      s_q[g][blk][4 + c] = hi;
-    }
-  }
-  __syncthreads();
-  uint32_t qlo[HI][4], qhi[HI][4];
-  int qe[HI];
-  float w[HI];
-#pragma unroll
-  for (int g = 0; g < HI; ++g) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      qlo[g][c] = s_q[g][sub][c];
-      qhi[g][c] = s_q[g][sub][4 + c];
-    }
-    qe[g] = s_qe[g][sub];
-    w[g] = A.w[static_cast<int64_t>(row) * HI + g];
-  }
-
-  const uint8_t* kbase = A.k + b * A.k_bstride + sub * 16;
-  const uint8_t* sbase = A.ks + b * A.ks_bstride + sub;
-  const int rowb = A.d_I / 2;
-  const int rows_s = A.d_I / 32;
-  float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
-  uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
-
-  for (int j0 = start + grp; j0 < end; j0 += GROUPS * U) {
-    u32x4 kv[U];
-    int ke[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * GROUPS;
-      if (j < end) {
-        kv[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * rowb));
-        ke[u] = static_cast<int>(sbase[static_cast<int64_t>(j) * rows_s]) - 127;
-      } else {
-        kv[u] = u32x4{0, 0, 0, 0};
-        ke[u] = 0;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t klo[4], khi[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        klo[c] = e2m1x4_to_i8x4(kv[u][c] & 0x0F0F0F0Fu);
-        khi[c] = e2m1x4_to_i8x4((kv[u][c] >> 4) & 0x0F0F0F0Fu);
-      }
-      float part[HI];
-#pragma unroll
-      for (int g = 0; g < HI; ++g) {
-        int acc = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc = __builtin_amdgcn_sdot4(static_cast<int>(qlo[g][c]), static_cast<int>(klo[c]), acc, false);
-          acc = __builtin_amdgcn_sdot4(static_cast<int>(qhi[g][c]), static_cast<int>(khi[c]), acc, false);
-        }
-        part[g] = __builtin_ldexpf(static_cast<float>(acc), qe[g] + ke[u] - 2);
-      }
-#pragma unroll
-      for (int o = 1; o < LPE; o <<= 1)
-#pragma unroll
-        for (int g = 0; g < HI; ++g) part[g] += __shfl_xor(part[g], o, kWave);
-      const int j = j0 + u * GROUPS;
-      if (sub == 0 && j < end) {
-        float s = 0.0f;
-#pragma unroll
-        for (int g = 0; g < HI; ++g) s = fmaf(w[g], relu(part[g]), s);
-        s += 0.0f;
-        if constexpr (SBF16)
-          s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
-        else
-          s32[j] = s;
-        if (hist) hist_add<SBF16>(s_hist, s);
-      }
-    }
-  }
-  if (hist) hist_flush(s_hist, A.hist, row, A.N);
-}
 
 // MXFP4 keys on the matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1 operands and
 // e8m0 scales per 32 channels computes D[head][key] for 32 keys at once (A = the quantized
@@ -571,9 +398,6 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   const int start = blockIdx.x * A.chunk;
   const int end = min(start + A.chunk, nv);
   if (start >= end) return;
-  __shared__ uint32_t s_hist[kHistBins];
-  const bool hist = A.hist != nullptr && A.topk < nv;
-  hist_clear(s_hist, hist);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -665,11 +489,9 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
           s16[j] = static_cast<uint16_t>(f32_to_bf16_bits(s));
         else
           s32[j] = s;
-        if (hist) hist_add<SBF16>(s_hist, s);
       }
     }
   }
-  if (hist) hist_flush(s_hist, A.hist, row, A.N);
 }
 
 template <int HI, bool QBF16>
@@ -695,46 +517,13 @@ hipError_t launch_mx_mfma(const IdxMxDev& A, int rows, int H_I, int score_dtype,
   return hipErrorInvalidValue;
 }
 
-template <int HI, int LPE, bool QBF16>
-hipError_t launch_mx_hi(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
-  const int nchunks = (A.N + A.chunk - 1) / A.chunk;
-  dim3 grid(nchunks, rows);
-  if (score_dtype == 1)
-    index_scores_mx_kernel<HI, LPE, QBF16, true><<<grid, 256, 0, s>>>(A);
-  else
-    index_scores_mx_kernel<HI, LPE, QBF16, false><<<grid, 256, 0, s>>>(A);
-  return hipGetLastError();
-}
-
-template <int LPE, bool QBF16>
-hipError_t launch_mx_lpe(const IdxMxDev& A, int rows, int H_I, int score_dtype, hipStream_t s) {
-  switch (H_I) {
-    case 1: return launch_mx_hi<1, LPE, QBF16>(A, rows, score_dtype, s);
-    case 2: return launch_mx_hi<2, LPE, QBF16>(A, rows, score_dtype, s);
-    case 4: return launch_mx_hi<4, LPE, QBF16>(A, rows, score_dtype, s);
-    case 8: return launch_mx_hi<8, LPE, QBF16>(A, rows, score_dtype, s);
-    case 16: return launch_mx_hi<16, LPE, QBF16>(A, rows, score_dtype, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <bool QBF16>
-hipError_t launch_mx_q(const IdxMxDev& A, int rows, int H_I, int score_dtype, hipStream_t s) {
-  switch (A.d_I / 32) {
-    case 1: return launch_mx_lpe<1, QBF16>(A, rows, H_I, score_dtype, s);
-    case 2: return launch_mx_lpe<2, QBF16>(A, rows, H_I, score_dtype, s);
-    case 4: return launch_mx_lpe<4, QBF16>(A, rows, H_I, score_dtype, s);
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
                                      const uint8_t* kx, int64_t k_bstride, const uint8_t* ks,
                                      int64_t ks_bstride, int B, int Nq, int H_I, int d_I,
                                      int N, int ratio, int64_t pos0, int score_dtype,
-                                     void* scores, uint32_t* hist, int k, hipStream_t s) {
+                                     void* scores, hipStream_t s) {
   IdxMxDev A;
   A.q = q;
   A.w = w;
@@ -749,9 +538,6 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.pos0 = pos0;
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
-  if (hist != nullptr && topk_uses_rows_path(plan_topk(score_dtype, B * Nq, N, k))) hist = nullptr;
-  A.hist = hist;
-  A.topk = k;
   if (q_dtype == 1) return launch_mx_mfma<true>(A, B * Nq, H_I, score_dtype, s);
   return launch_mx_mfma<false>(A, B * Nq, H_I, score_dtype, s);
 }
@@ -761,11 +547,11 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, int score_dtype, void* scores,
-                               uint32_t* hist, int k, hipStream_t s) {
+                               hipStream_t s) {
   if (k_dtype == 2)
     return launch_mxfp4_index_scores(q, q_dtype, w, static_cast<const uint8_t*>(kx), k_bstride,
                                      ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0,
-                                     score_dtype, scores, hist, k, s);
+                                     score_dtype, scores, s);
   IdxDev A;
   A.q = q;
   A.w = w;
@@ -778,10 +564,6 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.pos0 = pos0;
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
-  // rows resolved one block per row need no shared histogram
-  if (hist != nullptr && topk_uses_rows_path(plan_topk(score_dtype, B * Nq, N, k))) hist = nullptr;
-  A.hist = hist;
-  A.topk = k;
   const int rows = B * Nq;
   // many query tokens per sequence: the GEMM form on the matrix cores, for sequences whose
   // rows split into whole blocks of 256 rows (8 waves) or 128 rows (4 waves)
@@ -805,9 +587,7 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
     HCSA_GEMM_HI(1) HCSA_GEMM_HI(2) HCSA_GEMM_HI(4)
 #undef HCSA_GEMM_HI
 #undef HCSA_GEMM
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || hist == nullptr) return e;
-    return launch_sel_hist(scores, score_dtype, N, B, Nq, N, ratio, pos0, k, hist, s);
+    return hipGetLastError();
   }
   const int lpe = d_I * (k_dtype == 1 ? 2 : 4) / 16;
   if (k_dtype == 1) {

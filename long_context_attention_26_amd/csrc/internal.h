@@ -21,33 +21,24 @@ hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int D
 
 // ---- topk.hip
 struct TopkPlan {
-  int rows, N, k, key_bits, chunk, nchunks, copies;
-  size_t hist_bytes, count_bytes, total_bytes;
+  int rows, N, k, key_bits, nseg;
+  bool rows_path;                               // one block per row, no workspace
+  size_t floor_off, cnt_off, cand_off, total_bytes;
 };
 TopkPlan plan_topk(int score_dtype, int rows, int N, int k);
-bool topk_uses_rows_path(const TopkPlan& plan);   // one block per row, no shared state
+bool topk_plan_ok(const TopkPlan& plan);        // the row length is within the selector's range
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
                        int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
                        void* ws, hipStream_t s);
-// split phases: clear the histogram/counters; select from scores whose histogram was
-// already accumulated into ws (need_hist = false) or is built here (need_hist = true)
-hipError_t launch_topk_clear(const TopkPlan& plan, void* ws, hipStream_t s);
-hipError_t launch_topk_select(const TopkPlan& plan, const void* scores, int64_t row_stride,
-                              int Nq, int ratio, int64_t pos0, int32_t* idx, void* ws,
-                              bool need_hist, hipStream_t s);
 
 // ---- indexer.hip
 hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const void* kx,
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, int score_dtype, void* scores,
-                               uint32_t* hist, int k, hipStream_t s);
+                               hipStream_t s);
 
 void time_next_indexer(hipEvent_t start, hipEvent_t stop);
-// selector histogram of caller-given scores into a top-k workspace (topk.hip)
-hipError_t launch_sel_hist(const void* scores, int score_dtype, int64_t row_stride, int B,
-                           int Nq, int N, int ratio, int64_t pos0, int k, void* ws,
-                           hipStream_t s);
 
 // ---- attention.hip
 struct AttnArgs {

@@ -34,10 +34,6 @@ _SIGS = {
                                  _i64, _i, _i, _p, _p, _p, _sz, _p]),
     "hcsa_csa_index_scores": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
                                    _i64, _i, _p, _p]),
-    "hcsa_topk_clear": (_i, [_i, _i, _i, _i, _i, _p, _sz, _p]),
-    "hcsa_csa_index_scores_hist": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i,
-                                        _i, _i64, _i, _i, _p, _p, _sz, _p]),
-    "hcsa_topk_from_hist": (_i, [_p, _i, _i64, _i, _i, _i, _i, _i64, _i, _p, _p, _sz, _p]),
     "hcsa_csa_sparse_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "hcsa_csa_sparse_attn": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64, _i,
                                   _i, _i64, _i, _i, _i, _i, _i, _f, _p, _p, _p, _sz, _p]),
@@ -201,35 +197,6 @@ def csa_index_scores(q_idx, w_idx, k_idx, N, ratio, pos0, scores, k_scales=None,
                                      d_I, N, ratio, pos0, dtype_code(scores), _ptr(scores),
                                      _stream(stream)))
     return scores
-
-
-def topk_clear(score_dtype, B, Nq, N, k, workspace, stream=None):
-    _check(lib.hcsa_topk_clear(score_dtype, B, Nq, N, k, _ptr(workspace), workspace.numel(),
-                               _stream(stream)))
-
-
-def csa_index_scores_hist(q_idx, w_idx, k_idx, N, ratio, pos0, k, scores, workspace,
-                          k_scales=None, stream=None):
-    """Scores plus the selector histogram accumulated into `workspace` (a top-k workspace
-    cleared by topk_clear)."""
-    B, Nq, H_I, d_I = q_idx.shape
-    if k_idx.dtype == torch.uint8:
-        k_dt, ksb = MXFP4, k_scales.stride(0)
-    else:
-        k_dt, ksb = dtype_code(k_idx), 0
-    _check(lib.hcsa_csa_index_scores_hist(_ptr(q_idx), dtype_code(q_idx), _ptr(w_idx),
-                                          _ptr(k_idx), k_dt, k_idx.stride(0), _ptr(k_scales),
-                                          ksb, B, Nq, H_I, d_I, N, ratio, pos0, k,
-                                          dtype_code(scores), _ptr(scores), _ptr(workspace),
-                                          workspace.numel(), _stream(stream)))
-    return scores
-
-
-def topk_from_hist(scores, B, Nq, N, ratio, pos0, k, idx, workspace, stream=None):
-    _check(lib.hcsa_topk_from_hist(_ptr(scores), dtype_code(scores), scores.stride(0), B, Nq, N,
-                                   ratio, pos0, k, _ptr(idx), _ptr(workspace), workspace.numel(),
-                                   _stream(stream)))
-    return idx
 
 
 def csa_attn_workspace_size(B, Nq, H, d, k, n_win):

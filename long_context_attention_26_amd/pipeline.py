@@ -95,22 +95,19 @@ class DecodeStep:
         self.ws_hca = hcsa.alloc_workspace(hcsa.hca_attn_workspace_size(B, Nq, H, d, st.Nh), dev)
 
     def run_pool(self, pos0, stream=None):
-        """Pool the blocks completed by the query tokens and clear the selector state."""
-        st = self.st
-        st.compress_range(pos0, pos0 + self.Nq, stream=stream)
-        hcsa.topk_clear(self.score_code, st.B, self.Nq, st.Nc, self.topk, self.ws_topk,
-                        stream=stream)
+        """Pool the blocks completed by the query tokens."""
+        self.st.compress_range(pos0, pos0 + self.Nq, stream=stream)
 
     def run_index_scores(self, q_idx, w_idx, pos0, stream=None):
-        """Indexer scores with the selector histogram fused in (one kernel)."""
+        """Indexer scores of every visible compressed entry (one kernel)."""
         st = self.st
-        hcsa.csa_index_scores_hist(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, self.topk,
-                                   self.scores, self.ws_topk, k_scales=st.Ics, stream=stream)
+        hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, self.scores,
+                              k_scales=st.Ics, stream=stream)
 
     def run_select_attend(self, q, pos0, stream=None):
         st = self.st
-        hcsa.topk_from_hist(self.scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
-                            self.ws_topk, stream=stream)
+        hcsa.topk(self.scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
+                  workspace=self.ws_topk, stream=stream)
         hcsa.csa_sparse_attn(q, st.Kc, st.Vc, st.Nc, self.idx, st.K_raw, st.V_raw, 0, self.n_win,
                              R_CSA, pos0, self.scale, self.out_csa, self.lse_csa,
                              workspace=self.ws_csa, stream=stream)
@@ -128,15 +125,13 @@ class DecodeStep:
         mark("compress")
         if append:
             st.compress_range(pos0, pos0 + self.Nq, stream=stream)
-        hcsa.topk_clear(self.score_code, st.B, self.Nq, st.Nc, self.topk, self.ws_topk,
-                        stream=stream)
         scores = self.scores if scores_out is None else scores_out
         mark("index_scores")
-        hcsa.csa_index_scores_hist(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, self.topk, scores,
-                                   self.ws_topk, k_scales=st.Ics, stream=stream)
+        hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, scores,
+                              k_scales=st.Ics, stream=stream)
         mark("topk")
-        hcsa.topk_from_hist(scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
-                            self.ws_topk, stream=stream)
+        hcsa.topk(scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
+                  workspace=self.ws_topk, stream=stream)
         mark("csa_attn")
         hcsa.csa_sparse_attn(q, st.Kc, st.Vc, st.Nc, self.idx, st.K_raw, st.V_raw, 0, self.n_win,
                              R_CSA, pos0, self.scale, self.out_csa, self.lse_csa,

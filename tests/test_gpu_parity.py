@@ -188,6 +188,30 @@ def test_topk_many_rows_bit_exact(H, gpu, sdt, N, B, Nq, k, kind, pad):
         assert np.array_equal(got[r], want), (r, nv)
 
 
+@pytest.mark.parametrize("sdt,N,rows,k,kind", [
+    ("bf16", 262144, 4, 1024, "normal"),       # decode rows: segment lists
+    ("bf16", 262144, 2, 1024, "skewed"),       # the top keys crowd one segment: exact fallback
+    ("f32", 100000, 3, 500, "normal"),
+    ("bf16", 8193, 2, 10, "normal"),           # second segment holds one key
+    ("f32", 30000, 5, 4096, "ties"),
+])
+def test_topk_long_rows_bit_exact(H, gpu, sdt, N, rows, k, kind):
+    """Few long rows (decode): per-segment candidate lists, then one resolve block per row."""
+    print(f"topk segments {sdt} N={N} rows={rows} k={k} {kind}", flush=True)
+    ratio, pos0 = 4, 4 * N - 1                  # every row sees all N entries
+    base = rng.standard_normal((rows, N)) * 3 if kind != "ties" else _scores((rows, N), "ties")
+    if kind == "skewed":
+        base[:, 100000:108000] += 40.0
+    s = O.round_to(base, sdt)
+    st = dev(s, W.torch_dtype(sdt), gpu)
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device=gpu)
+    H.topk(st, rows, 1, N, ratio, pos0, k, idx)
+    _sync()
+    got = idx.cpu().numpy()
+    for r in range(rows):
+        assert np.array_equal(got[r], O.select_topk(s[r], N, k)), r
+
+
 def test_topk_deterministic(H, gpu):
     s = dev(O.round_bf16(rng.integers(0, 3, size=(1, 262144)).astype(float)), torch.bfloat16, gpu)
     outs = []
@@ -243,13 +267,12 @@ def test_index_scores_and_topk(H, gpu, case):
     scores = torch.zeros(B * Nq, N, device=gpu, dtype=W.torch_dtype(case["sdt"]))
     idx = torch.empty(B, Nq, k, dtype=torch.int32, device=gpu)
     H.csa_index_topk(qt, wt, kt, N, ratio, pos0, k, sdt, idx, k_scales=kst, scores_out=scores)
-    # the split-phase calls give the same selection
+    # scoring and selection as two calls give the same result
     ws = H.alloc_workspace(H.topk_workspace_size(sdt, B, Nq, N, k), gpu)
     scores2 = torch.zeros_like(scores)
     idx2 = torch.empty_like(idx)
-    H.topk_clear(sdt, B, Nq, N, k, ws)
-    H.csa_index_scores_hist(qt, wt, kt, N, ratio, pos0, k, scores2, ws, k_scales=kst)
-    H.topk_from_hist(scores2, B, Nq, N, ratio, pos0, k, idx2, ws)
+    H.csa_index_scores(qt, wt, kt, N, ratio, pos0, scores2, k_scales=kst)
+    H.topk(scores2, B, Nq, N, ratio, pos0, k, idx2.view(B * Nq, k), ws)
     _sync()
     assert torch.equal(scores, scores2) and torch.equal(idx, idx2)
     gs = f64(scores)
