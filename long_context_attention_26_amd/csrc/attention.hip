@@ -195,6 +195,105 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f3
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// One 32-key step of the MFMA attention (16 heads, d = 128), for lane (head col, k-group g):
+// S^T tiles t = 0, 1 from the K rows ka[t] (keys 16t + col of the step), online softmax of
+// the logits of keys 16*(j/4) + 4g + j%4 (valid where ok[j]), O^T += V^T P^T with the V rows
+// vv[j] of the same keys.
+__device__ __forceinline__ void attend_step(const u32x4 (&ka)[2][4], const u32x4 (&vv)[8],
+                                            const bool (&ok)[8], const u32x4 (&qB)[4],
+                                            f32x4 (&acc)[8], float& m_run, float& l_run,
+                                            float sl2) {
+  // ---- S^T tiles: lane holds logits of keys (tile t, 4g + i) for head col
+  f32x4 st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) st[t] = mfma16x16x32(ka[t][s], qB[s], st[t]);
+  }
+  float lg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lg[j] = ok[j] ? st[j >> 2][j & 3] * sl2 : -INFINITY;
+  float mt = lg[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mt = fmaxf(mt, lg[j]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+  const float m_new = fmaxf(m_run, mt);
+  if (m_new == -INFINITY) return;        // nothing visible yet for this head
+  const float alpha = exp2f(m_run - m_new);
+  m_run = m_new;
+  float pj[8];
+  float psum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pj[j] = exp2f(lg[j] - m_new);
+    psum += pj[j];
+  }
+  l_run = l_run * alpha + psum;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+  u32x4 pB;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) pB[m] = pack_bf16x2(pj[2 * m], pj[2 * m + 1]);
+  // ---- O^T tiles: channel 8*i + t for tile t, row i
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 va;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      va[m] = __builtin_amdgcn_perm(vv[2 * m + 1][t >> 1], vv[2 * m][t >> 1], sel);
+    acc[t] = mfma16x16x32(va, pB, acc[t]);
+  }
+}
+
+// The 4 waves' partial results of one (split, row) block merged in LDS and written as the
+// split's normalized output and log-sum-exp (or the final ones with a single split).
+__device__ __forceinline__ void combine_waves(const AttnDev& A, const f32x4 (&acc)[8],
+                                              float m_run, float l_run, float (*s_o)[16][129],
+                                              float (*s_ml)[2][16], int split, int row) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, g = lane >> 4;
+  // per-head totals across the 4 k-groups
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  // lane holds O^T[channel 32g + 8i + t][head col] = acc[t][i]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s_o[wave][col][32 * g + 8 * i + t] = acc[t][i];
+  if (g == 0) {
+    s_ml[wave][0][col] = m_run;
+    s_ml[wave][1][col] = l_run;
+  }
+  __syncthreads();
+
+  float* o = A.out + (static_cast<int64_t>(split) * A.rows + row) * 2048;
+  float* ls = A.lse + static_cast<int64_t>(split) * A.rows * 16 + static_cast<int64_t>(row) * 16;
+  for (int t = threadIdx.x; t < 2048; t += 256) {
+    const int h = t >> 7, c = t & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = s_ml[w][0][h];
+        if (mw != -INFINITY) {
+          const float f = exp2f(mw - M);
+          num = fmaf(f, s_o[w][h][c], num);
+          den = fmaf(f, s_ml[w][1][h], den);
+        }
+      }
+    }
+    o[t] = den > 0.0f ? num / den : 0.0f;
+    if (c == 0) ls[h] = den > 0.0f ? (M + log2f(den)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
 // grid: (splits, rows); block 256 (4 waves).
 template <bool CSA>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
@@ -259,87 +358,74 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
       else
         vv[j] = u32x4{0, 0, 0, 0};
     }
-    // ---- S^T tiles: lane holds logits of keys (tile t, 4g + i) for head col
-    f32x4 st[2];
+    attend_step(ka, vv, ok, qB, acc, m_run, l_run, sl2);
+  }
+
+  combine_waves(A, acc, m_run, l_run, s_o, s_ml, split, row);
+}
+
+// ------------------------------------------------------------------ HCA, one token per sequence
+
+// Decode HCA: the visible entries 0..nv-1 are contiguous, so no key list is built; each of
+// a block's 4 waves streams its own contiguous run of the block's chunk, 32 entries a step,
+// the next step's K and V rows loaded while the current step is computed.
+// grid: (splits, rows); block 256.
+__global__ __launch_bounds__(256, 2) void hca_decode_kernel(AttnDev A) {
+  __shared__ float s_o[4][16][129];
+  __shared__ float s_ml[4][2][16];
+  const int row = blockIdx.y, split = blockIdx.x;
+  const RowKeys r = row_keys<false>(A, row);       // r.L = visible entries
+  const int k0 = split * A.chunk;
+  const int cnt = max(0, min(A.chunk, r.L - k0));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, g = lane >> 4;
+  const int per = (cnt + 127) / 128 * 32;          // a quarter of the chunk, whole steps
+  const int w0 = k0 + wave * per;
+  const int w1 = min(w0 + per, k0 + cnt);
+
+  u32x4 qB[4];                                     // B of S^T: Q[head col][32s + 8g .. +8]
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(A.q) + (static_cast<int64_t>(row) * 16 + col) * 128;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qB[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0, 0, 0, 0};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float sl2 = A.scale * 1.4426950408889634f;   // logits in base 2
+
+  const uint16_t* kb = static_cast<const uint16_t*>(A.kc) + r.b * A.c_bstride;
+  const uint16_t* vb = static_cast<const uint16_t*>(A.vc) + r.b * A.c_bstride;
+  // K rows of keys base + 16t + col; V slices (channels 8col..) of keys base + 16*(j/4) + 4g + j%4
+  auto load = [&](int base, u32x4 (&ka)[2][4], u32x4 (&vv)[8], bool (&ok)[8]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      st[t] = f32x4{0, 0, 0, 0};
+      const int e = base + 16 * t + col;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) st[t] = mfma16x16x32(ka[t][s], qB[s], st[t]);
+      for (int s = 0; s < 4; ++s)
+        ka[t][s] = e < w1 ? *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(e) * 128 + 32 * s + 8 * g)
+                          : u32x4{0, 0, 0, 0};
     }
-    float lg[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lg[j] = ok[j] ? st[j >> 2][j & 3] * sl2 : -INFINITY;
-    float mt = lg[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, lg[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m_run, mt);
-    if (m_new == -INFINITY) continue;      // nothing visible yet for this head
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float pj[8];
-    float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pj[j] = exp2f(lg[j] - m_new);
-      psum += pj[j];
+      const int e = base + 16 * (j >> 2) + 4 * g + (j & 3);
+      ok[j] = e < w1;
+      vv[j] = ok[j] ? *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(e) * 128 + 8 * col)
+                    : u32x4{0, 0, 0, 0};
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-    u32x4 pB;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) pB[m] = pack_bf16x2(pj[2 * m], pj[2 * m + 1]);
-    // ---- O^T tiles: channel 8*i + t for tile t, row i
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 va;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        va[m] = __builtin_amdgcn_perm(vv[2 * m + 1][t >> 1], vv[2 * m][t >> 1], sel);
-      acc[t] = mfma16x16x32(va, pB, acc[t]);
-    }
+  };
+  u32x4 kaA[2][4], vvA[8], kaB[2][4], vvB[8];
+  bool okA[8], okB[8];
+  if (w0 < w1) load(w0, kaA, vvA, okA);
+  for (int base = w0; base < w1; base += 64) {
+    if (base + 32 < w1) load(base + 32, kaB, vvB, okB);
+    attend_step(kaA, vvA, okA, qB, acc, m_run, l_run, sl2);
+    if (base + 32 >= w1) break;
+    if (base + 64 < w1) load(base + 64, kaA, vvA, okA);
+    attend_step(kaB, vvB, okB, qB, acc, m_run, l_run, sl2);
   }
-
-  // per-head totals across the 4 k-groups
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
-  // lane holds O^T[channel 32g + 8i + t][head col] = acc[t][i]
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) s_o[wave][col][32 * g + 8 * i + t] = acc[t][i];
-  if (g == 0) {
-    s_ml[wave][0][col] = m_run;
-    s_ml[wave][1][col] = l_run;
-  }
-  __syncthreads();
-
-  float* o = A.out + (static_cast<int64_t>(split) * A.rows + row) * 2048;
-  float* ls = A.lse + static_cast<int64_t>(split) * A.rows * 16 + static_cast<int64_t>(row) * 16;
-  for (int t = threadIdx.x; t < 2048; t += 256) {
-    const int h = t >> 7, c = t & 127;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = s_ml[w][0][h];
-        if (mw != -INFINITY) {
-          const float f = exp2f(mw - M);
-          num = fmaf(f, s_o[w][h][c], num);
-          den = fmaf(f, s_ml[w][1][h], den);
-        }
-      }
-    }
-    o[t] = den > 0.0f ? num / den : 0.0f;
-    if (c == 0) ls[h] = den > 0.0f ? (M + log2f(den)) * 0.6931471805599453f : -INFINITY;
-  }
+  combine_waves(A, acc, m_run, l_run, s_o, s_ml, split, row);
 }
 
 // ------------------------------------------------------------------ HCA, many query tokens
@@ -519,9 +605,12 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
 
 // ------------------------------------------------------------------ merge
 
-// grid: (H, rows); block = d threads (<= 256).  The split weights of the (row, head) are
-// formed once in LDS, then each thread sums one channel over the splits with independent
-// coalesced loads.
+constexpr int kMergeRegSplits = 16;
+
+// grid: (H, rows); block = d threads (<= 256).  Up to kMergeRegSplits splits every thread
+// issues all of its loads -- the splits' log-sum-exps and its channel's partial outputs --
+// before using any, so the merge costs one memory latency; beyond that the split weights
+// are formed once in LDS and each thread sums its channel over the splits.
 __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_l,
                                                         int splits, int rows, int H, int d,
@@ -531,7 +620,35 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   __shared__ float s_red[2];
   const int h = blockIdx.x, row = blockIdx.y;
   const int64_t lstride = static_cast<int64_t>(rows) * H;
+  const int64_t ostride = static_cast<int64_t>(rows) * H * d;
   const float* pl = part_l + static_cast<int64_t>(row) * H + h;
+  const int c = threadIdx.x;
+  const float* po = part_o + (static_cast<int64_t>(row) * H + h) * d + min(c, d - 1);
+  float* orow = out + (static_cast<int64_t>(row) * H + h) * d;
+  if (splits <= kMergeRegSplits) {
+    float l[kMergeRegSplits], v[kMergeRegSplits];
+#pragma unroll
+    for (int u = 0; u < kMergeRegSplits; ++u) {
+      l[u] = u < splits ? pl[u * lstride] : -INFINITY;
+      v[u] = u < splits ? po[u * ostride] : 0.0f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMergeRegSplits; ++u) M = fmaxf(M, l[u]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int u = 0; u < kMergeRegSplits; ++u) {
+        // an empty split has lse -inf and a zero partial: weight 0
+        const float w = l[u] == -INFINITY ? 0.0f : expf(l[u] - M);
+        den += w;
+        num = fmaf(w, v[u], num);
+      }
+    }
+    if (c < d) orow[c] = den > 0.0f ? num / den : 0.0f;
+    if (c == 0) lse[static_cast<int64_t>(row) * H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
+    return;
+  }
   if (threadIdx.x < kWave) {
     float M = -INFINITY;
     for (int s = threadIdx.x; s < splits; s += kWave) M = fmaxf(M, pl[s * lstride]);
@@ -551,10 +668,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   }
   __syncthreads();
   const float M = s_red[0], den = s_red[1];
-  const int c = threadIdx.x;
   if (c < d) {
-    const int64_t ostride = static_cast<int64_t>(rows) * H * d;
-    const float* po = part_o + (static_cast<int64_t>(row) * H + h) * d + c;
     float num = 0.0f;
     int s = 0;
     if (splits <= 1024) {
@@ -578,7 +692,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
         if (w != 0.0f) num = fmaf(w, po[s * ostride], num);
       }
     }
-    out[(static_cast<int64_t>(row) * H + h) * d + c] = den > 0.0f ? num / den : 0.0f;
+    orow[c] = den > 0.0f ? num / den : 0.0f;
     if (c == 0) lse[static_cast<int64_t>(row) * H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
   }
 }
@@ -599,7 +713,14 @@ AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int
     p.part_bytes = p.total_bytes = 0;
     return p;
   }
-  if (p.mfma) {
+  p.hca_decode = !csa && p.mfma;
+  if (p.hca_decode) {
+    // about one block per CU over the whole call, 128-entry granules
+    const int64_t total = static_cast<int64_t>(p.rows) * std::max(max_len, 1);
+    int64_t c = (total + 255) / 256;
+    c = (c + 127) / 128 * 128;
+    p.chunk = static_cast<int>(std::min<int64_t>(std::max<int64_t>(c, 128), kMfmaMaxChunk));
+  } else if (p.mfma) {
     // about two blocks per CU over the whole call, 128-key granules, at most kMfmaMaxChunk
     const int64_t total = static_cast<int64_t>(p.rows) * std::max(max_len, 1);
     int64_t c = (total + 511) / 512;
@@ -663,7 +784,9 @@ hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, v
     return hipGetLastError();
   }
   dim3 grid(plan.splits, plan.rows);
-  if (plan.mfma) {
+  if (plan.hca_decode) {
+    hca_decode_kernel<<<grid, 256, 0, s>>>(A);
+  } else if (plan.mfma) {
     if (csa) attn_mfma_kernel<true><<<grid, 256, 0, s>>>(A);
     else attn_mfma_kernel<false><<<grid, 256, 0, s>>>(A);
   } else {

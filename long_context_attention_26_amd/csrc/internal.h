@@ -63,7 +63,7 @@ struct AttnArgs {
 };
 struct AttnPlan {
   int rows, max_len, chunk, splits;
-  bool mfma, tiled;
+  bool mfma, tiled, hca_decode;
   size_t part_bytes, total_bytes;
 };
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len);
