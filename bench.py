@@ -154,6 +154,20 @@ def cpu_baseline(cfg, st, om, q, qi, wi, seconds):
                       f"float64 numpy oracle, {el:.1f} s; caches pooled untimed"}
 
 
+def copy_calibration():
+    """Three launches of a plain copy of exactly 2 GiB (read 2 GiB, write 2 GiB): what the
+    FETCH_SIZE / WRITE_SIZE counters read for it converts their units into bytes."""
+    import torch
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,7 +178,13 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="cache copies (0 = enough to defeat the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 2 GiB device-to-device copy 3 times (the known-size "
+                         "kernel that scales the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -386,6 +386,8 @@ struct IdxMxDev {
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
+constexpr int kMxMaxUnits = 16 * 4;   // H_I <= 16 heads x d_I / 32 <= 4 blocks
+
 // grid: (ceil(N / chunk), rows); block 256 (4 waves, 32 keys per MFMA).
 template <int HI, bool QBF16, bool SBF16>
 __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
@@ -404,7 +406,35 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   const int ksteps = A.d_I > 64 ? A.d_I / 64 : 1;       // 64-channel MFMA steps
   const int nblk = A.d_I / 32;                          // 32-channel scale blocks per row
 
-  // A operand: this lane's head (col) and block (2*step + half), quantized here.
+  // The query heads quantized once per block: eight threads per 32-channel block (head g,
+  // block blk), four channels each; the block's absolute maximum is reduced across the
+  // eight, and each thread writes its four codes (16 bits) of the block's packed row.
+  __shared__ uint32_t s_qa[kMxMaxUnits][4];
+  __shared__ int s_qs[kMxMaxUnits];
+  const int units = HI * nblk;
+  for (int t = threadIdx.x; t < units * 8; t += 256) {   // whole groups of 8 stay together
+    const int u = t >> 3, sub = t & 7;
+    const int g = u / nblk, blk = u - g * nblk;
+    const int64_t off = (static_cast<int64_t>(row) * HI + g) * A.d_I + blk * 32 + 4 * sub;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[off + e])
+                   : static_cast<const float*>(A.q)[off + e];
+    float amax = fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                       fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+    const int se = mx_scale_exp(amax);
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c |= e2m1_code(v[e], se) << (4 * e);
+    reinterpret_cast<uint16_t*>(s_qa[u])[sub] = static_cast<uint16_t>(c);
+    if (sub == 0) s_qs[u] = se + 127;
+  }
+  __syncthreads();
+  // A operand: this lane's head (col) and block (2*step + half)
   i32x8 qa[2];
   int qs[2];
 #pragma unroll
@@ -413,24 +443,10 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
     qs[st] = 127;
     const int blk = 2 * st + half;
     if (st < ksteps && col < HI && blk < nblk) {
-      const int64_t off = (static_cast<int64_t>(row) * HI + col) * A.d_I + blk * 32;
-      float v[32];
-      float amax = 0.0f;
+      const int u = col * nblk + blk;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        v[e] = QBF16 ? bf16_to_f32(static_cast<const uint16_t*>(A.q)[off + e])
-                     : static_cast<const float*>(A.q)[off + e];
-        amax = fmaxf(amax, __builtin_fabsf(v[e]));
-      }
-      const int se = mx_scale_exp(amax);
-      qs[st] = se + 127;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w |= e2m1_code(v[8 * d + e], se) << (4 * e);
-        qa[st][d] = static_cast<int>(w);
-      }
+      for (int d = 0; d < 4; ++d) qa[st][d] = static_cast<int>(s_qa[u][d]);
+      qs[st] = s_qs[u];
     }
   }
   float w[HI];
@@ -537,7 +553,8 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.d_I = d_I;
   A.pos0 = pos0;
   A.scores = scores;
-  A.chunk = index_chunk(B * Nq, N);
+  // at most 2048 keys per block: more, shorter blocks shorten the grid's last round
+  A.chunk = std::min(index_chunk(B * Nq, N), 2048);
   if (q_dtype == 1) return launch_mx_mfma<true>(A, B * Nq, H_I, score_dtype, s);
   return launch_mx_mfma<false>(A, B * Nq, H_I, score_dtype, s);
 }
