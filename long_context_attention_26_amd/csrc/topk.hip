@@ -594,10 +594,14 @@ __global__ __launch_bounds__(kFloorThreads) void seg_floor_kernel(TopkDev P, Seg
       top[u * EPC + e] = e < r ? V_t::to_key(V_t::raw_of(x, e)) >> (KB - 16) : 0u;
   }
   // all but at most one sampled chunk are full; a missing key reads as 0 and never counts
-  // (every tested threshold is >= 1)
+  // (every tested threshold is >= 1).  Each wave selects the ceil(m/W)-th largest of its
+  // own 1024 samples (radix 4 from the top, ballot counts, no barriers) and the floor is the
+  // smallest of the W results: at least m samples are >= it, so it is at or below the
+  // block's m-th largest sample.  Only the candidate count depends on the floor.
   const int m = min(kFloorSamples - EPC,
-                    static_cast<int>((2LL * P.k * kFloorSamples + nv - 1) / nv) + 16);
-  uint32_t pre = 0;                              // radix-4 select of the m-th largest
+                    static_cast<int>((2LL * P.k * kFloorSamples + nv - 1) / nv) + 8);
+  const int mw = (m + W - 1) / W;
+  uint32_t pre = 0;
 #pragma unroll 1
   for (int sh = 14; sh >= 0; sh -= 2) {
     int cnt[3];
@@ -607,25 +611,15 @@ __global__ __launch_bounds__(kFloorThreads) void seg_floor_kernel(TopkDev P, Seg
       int n = 0;
 #pragma unroll
       for (int u = 0; u < PT; ++u) n += top[u] >= th;
-      cnt[d - 1] = wave_sum_bits<6>(n);
+      cnt[d - 1] = wave_sum_bits<5>(n);
     }
-    const int buf = (sh >> 1) & 1;
-    if (lane == 0) {
-      s_rdx[buf][w][0] = cnt[0];
-      s_rdx[buf][w][1] = cnt[1];
-      s_rdx[buf][w][2] = cnt[2];
-    }
-    __syncthreads();
-    int tot[3] = {0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < W; ++u) {
-      tot[0] += s_rdx[buf][u][0];
-      tot[1] += s_rdx[buf][u][1];
-      tot[2] += s_rdx[buf][u][2];
-    }
-    const uint32_t d = tot[2] >= m ? 3u : tot[1] >= m ? 2u : tot[0] >= m ? 1u : 0u;
+    const uint32_t d = cnt[2] >= mw ? 3u : cnt[1] >= mw ? 2u : cnt[0] >= mw ? 1u : 0u;
     pre |= d << sh;
   }
+  if (lane == 0) s_rdx[0][w][0] = static_cast<int>(pre);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < W; ++u) pre = min(pre, static_cast<uint32_t>(s_rdx[0][u][0]));
   if (threadIdx.x == 0) S.floor[row] = pre << (KB - 16);
 }
 

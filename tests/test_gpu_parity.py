@@ -299,6 +299,60 @@ def test_index_scores_and_topk(H, gpu, case):
                         rel=2e-2 if case["sdt"] == "bf16" else 1e-5)
 
 
+@pytest.mark.parametrize("case", [
+    # 16 sequences x 262144 entries
+    dict(B=16, Nq=1, N=262144, H_I=4, d_I=64, k=1024, sdt="bf16", kind="normal"),
+    # ragged visible counts (several query tokens per sequence), fp32 scores, 2 MFMA steps
+    dict(B=3, Nq=5, N=150001, H_I=8, d_I=128, k=700, sdt="f32", kind="normal"),
+    # a run of identical keys far above the rest: lists overflow, exact full-row fallback
+    dict(B=8, Nq=1, N=200000, H_I=4, d_I=64, k=1024, sdt="bf16", kind="crowd"),
+    # every key identical: all scores tie, the lowest indices win
+    dict(B=4, Nq=1, N=70000, H_I=2, d_I=32, k=512, sdt="bf16", kind="equal"),
+])
+def test_mx_index_topk_long_rows(H, gpu, case):
+    """MXFP4 keys, long rows at the decode workload's scale (segment candidate lists, the
+    exact fallback on overflow, all-equal rows): the one-call form equals the two-call form
+    bit for bit, and the selection on the GPU's own score array equals the oracle's."""
+    print(f"mx index+topk {case}", flush=True)
+    B, Nq, N, H_I, d_I, k = case["B"], case["Nq"], case["N"], case["H_I"], case["d_I"], case["k"]
+    ratio, pos0 = 4, 4 * N - Nq
+    g = torch.Generator().manual_seed(7)
+    codes = torch.randint(0, 256, (B, N, d_I // 2), generator=g, dtype=torch.uint8)
+    scl = torch.randint(121, 128, (B, N, d_I // 32), generator=g, dtype=torch.uint8)
+    if case["kind"] == "crowd":
+        codes[:, 50000:60000] = 0x77                  # every element +6: the largest scores
+        scl[:, 50000:60000] = 127
+    if case["kind"] == "equal":
+        codes[:] = 0x22
+        scl[:] = 127
+    q = torch.randn(B, Nq, H_I, d_I, generator=g).to(torch.bfloat16)
+    if case["kind"] in ("crowd", "equal"):
+        q = q.abs()                                   # positive dots with the all-positive keys
+    w = torch.rand(B, Nq, H_I, generator=g) + 0.1
+    kt, kst, qt, wt = codes.to(gpu), scl.to(gpu), q.to(gpu), w.to(gpu)
+    sdt = H.BF16 if case["sdt"] == "bf16" else H.F32
+    sdtype = W.torch_dtype(case["sdt"])
+    scores = torch.zeros(B * Nq, N, device=gpu, dtype=sdtype)
+    idx = torch.full((B, Nq, k), -7, dtype=torch.int32, device=gpu)
+    H.csa_index_topk(qt, wt, kt, N, ratio, pos0, k, sdt, idx, k_scales=kst, scores_out=scores)
+    ws = H.alloc_workspace(H.topk_workspace_size(sdt, B, Nq, N, k), gpu)
+    scores2 = torch.zeros_like(scores)
+    idx2 = torch.empty_like(idx)
+    H.csa_index_scores(qt, wt, kt, N, ratio, pos0, scores2, k_scales=kst)
+    H.topk(scores2, B, Nq, N, ratio, pos0, k, idx2.view(B * Nq, k), ws)
+    _sync()
+    assert torch.equal(scores, scores2)
+    assert torch.equal(idx, idx2)
+    gs = f64(scores)
+    gi = idx.cpu().numpy().reshape(B * Nq, k)
+    for r in sorted({0, B * Nq - 1, (B * Nq) // 2}):
+        nv = O.visible_entries(pos0 + r % Nq, N, ratio)
+        assert np.array_equal(gi[r], O.select_topk(gs[r], nv, k)), r
+    if case["kind"] == "equal":
+        assert (gs[:, :1] == gs[:, : N - Nq]).all()
+        assert np.array_equal(gi[0], np.arange(k))
+
+
 # ----------------------------------------------------------------------- attention
 
 def _attn_inputs(B, Nq, Hh, d, N, T_raw, dt):
