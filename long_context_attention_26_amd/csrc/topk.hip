@@ -172,6 +172,47 @@ __device__ __forceinline__ void take_all(int nv, int k, int32_t* out, int nthrea
   for (int j = threadIdx.x; j < k; j += nthreads) out[j] = j < nv ? j : -1;
 }
 
+// One wave: the bin b (of 256) holding the m-th largest of the values counted in hist, and
+// the number of values in the bins above it: out = {b, above}; b = -1 when the bins hold
+// fewer than m values.  Lane l holds bins 255-4l .. 252-4l, so a prefix over the lanes runs
+// from the largest bin down.
+__device__ __forceinline__ void hist_pick(const int* hist, int m, int* out) {
+  const int lane = threadIdx.x & 63;
+  int c[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = hist[255 - 4 * lane - j];
+    sum += c[j];
+  }
+  int inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += y;
+  }
+  const int exc = inc - sum;
+  const bool here = exc < m && inc >= m;          // exactly one lane when the total >= m
+  if (here) {
+    int acc = exc, j = 3;
+    bool found = false;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (!found && acc + c[jj] >= m) {
+        j = jj;
+        found = true;
+      } else if (!found) {
+        acc += c[jj];
+      }
+    }
+    out[0] = 255 - 4 * lane - j;
+    out[1] = acc;
+  }
+  if (lane == 63 && inc < m) {
+    out[0] = -1;
+    out[1] = 0;
+  }
+}
+
 // Exact selection over a whole row by NT threads (the fallback of both paths): T bit by bit
 // from the top (a bit stays set while at least k keys are >= the candidate value; keys past
 // the visible count are masked), then every key above T and the first need = k - #(> T)
@@ -345,7 +386,8 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
   __shared__ int32_t s_cj[kRowsWaves][kRowsWaveCap];
   __shared__ int s_cnt[2][kRowsWaves];
   __shared__ int s_wave[kRowsWaves], s_gt[kRowsWaves], s_eq[kRowsWaves], s_hb[kRowsWaves];
-  __shared__ int s_rdx[2][kRowsWaves][3];
+  __shared__ int s_hist[2][256];
+  __shared__ int s_sel[4];
   const int row = blockIdx.x;
   const V_t V(P, row, vec);
   const int nv = V.nv;
@@ -368,52 +410,38 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
     cur[u] = ch < cw1 ? V.load_raw(ch) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---- 1. candidate floor L (all keys are candidates when few)
+  // ---- 1. candidate floor L (all keys are candidates when few): the m-th largest 16-bit
+  // sample prefix (a 128th of a binade: a coarser floor would admit up to a whole bin of
+  // extra candidates), by two LDS histograms of 8 bits (the high byte, then the low byte
+  // within the chosen high byte): a few atomics per thread and four barriers in all.
   uint32_t L = 0;
   if (nv > kRowsWaves * kRowsWaveCap / 2) {
-    bool sv[4];
-    uint32_t st[4];
+    s_hist[threadIdx.x >> 8][threadIdx.x & 255] = 0;
+    uint32_t st[4];                              // 0 = no sample (never counts)
     int nmine = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      sv[u] = cw0 + 64 * u + lane < cw1;          // first elements are visible keys
-      st[u] = sv[u] ? V_t::to_key(V_t::raw_of(cur[u], 0)) >> (KB - 16) : 0u;
-      nmine += sv[u];
+      const bool sv = cw0 + 64 * u + lane < cw1;  // first elements are visible keys
+      st[u] = sv ? V_t::to_key(V_t::raw_of(cur[u], 0)) >> (KB - 16) : 0u;
+      nmine += sv;
     }
-    const int ns = block_total_bits<kRowsWaves, 3>(nmine, s_cnt, 0);
-    const int m = min(ns, static_cast<int>((2LL * P.k * ns + nv - 1) / nv) + 16);
-    // radix-4 select of the m-th largest 16-bit prefix (a 128th of a binade: a coarser
-    // floor would admit up to a whole bin of extra candidates): three thresholds a round
-    uint32_t pre = 0;
-#pragma unroll 1
-    for (int sh = 14; sh >= 0; sh -= 2) {
-      int cnt[3];
+    const int ns = block_total_bits<kRowsWaves, 3>(nmine, s_cnt, 0);   // also orders the zeroing
+    const int m = max(1, min(ns, static_cast<int>((2LL * P.k * ns + nv - 1) / nv) + 16));
 #pragma unroll
-      for (int d = 1; d <= 3; ++d) {
-        const uint32_t th = pre | (static_cast<uint32_t>(d) << sh);
-        int n = 0;
+    for (int u = 0; u < 4; ++u)
+      if (st[u] != 0u) atomicAdd(&s_hist[0][st[u] >> 8], 1);
+    __syncthreads();
+    if (w == 0) hist_pick(s_hist[0], m, s_sel);  // s_sel = {high byte, samples above it}
+    __syncthreads();
+    const uint32_t hi = static_cast<uint32_t>(s_sel[0]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) n += sv[u] && st[u] >= th;
-        cnt[d - 1] = wave_sum_bits<3>(n);
-      }
-      const int buf = (sh >> 1) & 1;
-      if (lane == 0) {
-        s_rdx[buf][w][0] = cnt[0];
-        s_rdx[buf][w][1] = cnt[1];
-        s_rdx[buf][w][2] = cnt[2];
-      }
-      __syncthreads();
-      int tot[3] = {0, 0, 0};
-#pragma unroll
-      for (int u = 0; u < kRowsWaves; ++u) {
-        tot[0] += s_rdx[buf][u][0];
-        tot[1] += s_rdx[buf][u][1];
-        tot[2] += s_rdx[buf][u][2];
-      }
-      const uint32_t d = tot[2] >= m ? 3u : tot[1] >= m ? 2u : tot[0] >= m ? 1u : 0u;
-      pre |= d << sh;
-    }
-    L = ns > 0 ? pre << (KB - 16) : 0u;
+    for (int u = 0; u < 4; ++u)
+      if (st[u] != 0u && (st[u] >> 8) == hi) atomicAdd(&s_hist[1][st[u] & 255u], 1);
+    __syncthreads();
+    if (w == 0) hist_pick(s_hist[1], m - s_sel[1], s_sel + 2);
+    __syncthreads();
+    // fewer than m nonzero samples: no floor
+    L = s_sel[0] < 0 || s_sel[2] < 0 ? 0u : ((hi << 8) | static_cast<uint32_t>(s_sel[2])) << (KB - 16);
   }
 
   // ---- 2. stream the wave's chunks 256 at a time (the next 256 loading meanwhile),
@@ -484,18 +512,34 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
     }
   }
   if (lane == 0) s_hb[w] = hb;
+  s_hist[threadIdx.x >> 8][threadIdx.x & 255] = 0;
   __syncthreads();
   int nb = 0;
 #pragma unroll
   for (int u = 0; u < kRowsWaves; ++u) nb = s_hb[u] > nb ? s_hb[u] : nb;
-  uint32_t T = nb >= 32 ? 0u : (L >> nb) << nb;
+  // T = the k-th largest candidate, 8 bits a pass below the bits every candidate shares
+  // with L: an LDS histogram of the pass's digit over the candidates that match T so far
+  const int D = (nb + 7) / 8;
+  uint32_t T = 8 * D >= 32 ? 0u : (L >> (8 * D)) << (8 * D);
+  int rem = P.k;                                 // rank of T among the candidates still open
 #pragma unroll 1
-  for (int b = nb - 1; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    int n = 0;
+  for (int p = 0; p < D; ++p) {
+    const int sh = 8 * (D - 1 - p);
+    int* hist = s_hist[p & 1];
+    const uint32_t hi = sh + 8 >= 32 ? 0u : T >> (sh + 8);
 #pragma unroll
-    for (int u = 0; u < STEPS; ++u) n += (64 * u + lane < wslot) && ck[u] >= cand;
-    if (block_total_bits<kRowsWaves, 4>(n, s_cnt, b & 1) >= P.k) T = cand;
+    for (int u = 0; u < STEPS; ++u) {
+      const bool in = 64 * u + lane < wslot;
+      if (in && (sh + 8 >= 32 || (ck[u] >> (sh + 8)) == hi)) atomicAdd(&hist[(ck[u] >> sh) & 255u], 1);
+    }
+    if (p >= 1) s_hist[(p + 1) & 1][threadIdx.x & 255] = 0;   // the previous pass's bins
+    __syncthreads();
+    if (w == 0) hist_pick(hist, rem, s_sel);
+    __syncthreads();
+    // every thread reads s_sel before it reaches the next pass's first barrier, and the
+    // next pick comes after that barrier
+    T |= static_cast<uint32_t>(s_sel[0]) << sh;
+    rem -= s_sel[1];
   }
   // per-wave counts of entries above T and equal to T
   int gt = 0, eq = 0;
