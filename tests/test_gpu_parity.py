@@ -353,6 +353,58 @@ def test_mx_index_topk_long_rows(H, gpu, case):
         assert np.array_equal(gi[0], np.arange(k))
 
 
+@pytest.mark.parametrize("case", [
+    # the chunked-prefill shape: 4096 query tokens x 4 heads against 66560 entries
+    dict(B=1, Nq=4096, N=66560, H_I=4, d_I=64, k=512, sdt="bf16", kind="normal"),
+    # two sequences, fp32 scores, d_I 128, ragged causal edges inside the key chunks
+    dict(B=2, Nq=256, N=9000, H_I=2, d_I=128, k=300, sdt="f32", kind="normal"),
+    # one query head (32 tokens per wave); k at or above the visible count of the first rows
+    # (all taken), and for the others every visible key is a candidate (short rows)
+    dict(B=1, Nq=128, N=1500, H_I=1, d_I=32, k=1480, sdt="bf16", kind="normal"),
+    # a run of identical keys far above the rest: candidate lists overflow, exact path
+    dict(B=1, Nq=512, N=40000, H_I=4, d_I=64, k=512, sdt="bf16", kind="crowd"),
+])
+def test_gemm_index_topk_prefill_scale(H, gpu, case):
+    """Prefill shapes at the chunked-prefill scale (the GEMM scan, the one-block-per-row
+    selector with its list overflow and take-all cases): the one-call form equals scoring and
+    selecting in two calls bit for bit, and the selection on the GPU's own score array equals
+    the oracle's."""
+    print(f"gemm index+topk {case}", flush=True)
+    B, Nq, N, H_I, d_I, k = case["B"], case["Nq"], case["N"], case["H_I"], case["d_I"], case["k"]
+    ratio = 4
+    pos0 = 4 * N - Nq - 37 if case["kind"] != "crowd" else 4 * N - Nq   # ragged: early rows see fewer
+    g = torch.Generator().manual_seed(11)
+    keys = torch.randn(B, N, d_I, generator=g)
+    if case["kind"] == "crowd":
+        keys[:, 20000:24000] = 3.0
+    q = torch.randn(B, Nq, H_I, d_I, generator=g)
+    if case["kind"] == "crowd":
+        q = q.abs()
+    w = torch.rand(B, Nq, H_I, generator=g) + 0.1
+    kt = keys.to(torch.bfloat16).to(gpu)
+    qt = q.to(torch.bfloat16).to(gpu)
+    wt = w.to(gpu)
+    sdt = H.BF16 if case["sdt"] == "bf16" else H.F32
+    sdtype = W.torch_dtype(case["sdt"])
+    scores = torch.zeros(B * Nq, N, device=gpu, dtype=sdtype)
+    idx = torch.full((B, Nq, k), -7, dtype=torch.int32, device=gpu)
+    H.csa_index_topk(qt, wt, kt, N, ratio, pos0, k, sdt, idx, scores_out=scores)
+    ws = H.alloc_workspace(H.topk_workspace_size(sdt, B, Nq, N, k), gpu)
+    scores2 = torch.zeros_like(scores)
+    idx2 = torch.empty_like(idx)
+    H.csa_index_scores(qt, wt, kt, N, ratio, pos0, scores2)
+    H.topk(scores2, B, Nq, N, ratio, pos0, k, idx2.view(B * Nq, k), ws)
+    _sync()
+    assert torch.equal(scores, scores2)
+    assert torch.equal(idx, idx2)
+    gi = idx.cpu().numpy().reshape(B * Nq, k)
+    rows = sorted({0, 1, 63, Nq - 1, B * Nq - 1, (B * Nq) // 2})
+    gs = f64(scores[rows])
+    for r, srow in zip(rows, gs):
+        nv = O.visible_entries(pos0 + r % Nq, N, ratio)
+        assert np.array_equal(gi[r], O.select_topk(srow, nv, k)), r
+
+
 # ----------------------------------------------------------------------- attention
 
 def _attn_inputs(B, Nq, Hh, d, N, T_raw, dt):
