@@ -23,8 +23,9 @@
  *   - CSA attention: one softmax over [selected entries] ++ [raw window tokens
  *     max(0, p-n_win+1) .. p]; HCA attention: one softmax over all visible entries.
  *   - visibility: entry j of a stream with ratio r is visible to the token at position p
- *     iff (j+1)*r <= p+1.  Query i of every sequence sits at position pos0 + i (all
- *     sequences of a call share one length).
+ *     iff (j+1)*r <= p+1.  Query i of sequence b sits at position pos0 + i, or at
+ *     seq_pos[b] + i when the call is given seq_pos (ragged batches: each sequence at its
+ *     own length).
  *   - one KV head shared by all query heads (MQA); logits are scale * q.k.
  *   - MXFP4: OCP MX e2m1 elements with one e8m0 scale per 32 elements, scale exponent
  *     floor(log2 amax) - 2 (clamped to [-127, 127]; amax = 0 gives -127), elements
@@ -43,6 +44,9 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = default stream) and
  *     never synchronizes.  Outputs are defined once the stream reaches the call.
  *   - Calls that share a workspace on different streams race.
+ *   - seq_pos (the calls that take pos0): NULL, or a device array of B int64 positions,
+ *     8-byte aligned, each >= 0, giving the position of query 0 of each sequence; pos0 is
+ *     then unused.  Its values sit in device memory and are not validated on the host.
  */
 #ifndef HCSA_H
 #define HCSA_H
@@ -133,8 +137,8 @@ int hcsa_mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int D, uint8_t
  * top-k compressed blocks; 9fzt.com digest item 4: BF16 scores for the selector].
  *
  * scores  [B*Nq][row_stride] F32 or BF16; row r = b*Nq + i belongs to the token at
- *         position pos0 + i, which sees n = min(N, (pos0+i+1)/ratio) entries; only
- *         scores[r][0..n) are read.
+ *         position p = pos0 + i (or seq_pos[b] + i), which sees n = min(N, (p+1)/ratio)
+ *         entries; only scores[r][0..n) are read.
  * idx     [B*Nq][k] int32 output: the min(k, n) entries with the largest scores (ties to
  *         the lowest index) in ascending order, then -1.  Bit-exact and deterministic.
  * Limits: 1 <= k <= 4096, 1 <= N <= 2^25, row_stride >= N, ratio >= 1, pos0 >= 0.
@@ -147,8 +151,8 @@ int hcsa_mxfp4_quantize(const void *x, int x_dtype, int64_t rows, int D, uint8_t
  */
 size_t hcsa_topk_workspace_size(int score_dtype, int B, int Nq, int N, int k);
 int hcsa_topk(const void *scores, int score_dtype, int64_t row_stride, int B, int Nq, int N,
-              int ratio, int64_t pos0, int k, int32_t *idx, void *workspace,
-              size_t ws_bytes, hcsa_stream stream);
+              int ratio, int64_t pos0, const int64_t *seq_pos, int k, int32_t *idx,
+              void *workspace, size_t ws_bytes, hcsa_stream stream);
 
 /*
  * Lightning indexer + top-k [Lighthouse section 八 items 3 and 7; 9fzt.com digest item 4].
@@ -169,8 +173,8 @@ size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score
 int hcsa_csa_index_topk(const void *q_idx, int q_dtype, const float *w_idx, const void *k_idx,
                         int k_dtype, int64_t k_bstride, const uint8_t *k_scales,
                         int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
-                        int64_t pos0, int k, int score_dtype, int32_t *topk_idx,
-                        void *scores_out, void *workspace, size_t ws_bytes,
+                        int64_t pos0, const int64_t *seq_pos, int k, int score_dtype,
+                        int32_t *topk_idx, void *scores_out, void *workspace, size_t ws_bytes,
                         hcsa_stream stream);
 
 /*
@@ -181,18 +185,19 @@ int hcsa_csa_index_topk(const void *q_idx, int q_dtype, const float *w_idx, cons
 int hcsa_csa_index_scores(const void *q_idx, int q_dtype, const float *w_idx,
                           const void *k_idx, int k_dtype, int64_t k_bstride,
                           const uint8_t *k_scales, int64_t ks_bstride, int B, int Nq, int H_I,
-                          int d_I, int N, int ratio, int64_t pos0, int score_dtype,
-                          void *scores, hcsa_stream stream);
+                          int d_I, int N, int ratio, int64_t pos0, const int64_t *seq_pos,
+                          int score_dtype, void *scores, hcsa_stream stream);
 
 /*
  * CSA sparse attention [Lighthouse section 八 item 3]: for each query token (position
- * p = pos0 + i) and head, one softmax over the selected compressed entries (topk_idx,
- * entries outside [0, n_c(p)) are skipped) followed by the raw window tokens
- * max(0, p-n_win+1) .. p.
+ * p = pos0 + i, or seq_pos[b] + i) and head, one softmax over the selected compressed
+ * entries (topk_idx, entries outside [0, n_c(p)) are skipped) followed by the raw window
+ * tokens max(0, p-n_win+1) .. p.
  *
  * q       [B][Nq][H][d]; kc, vc [B][N][d] (c_bstride elements); topk_idx [B][Nq][k].
  * k_raw, v_raw [B][T_raw][d] (raw_bstride elements); row t holds position raw_pos0 + t.
- *         Every window position of every query must lie in [raw_pos0, raw_pos0 + T_raw).
+ *         Every window position of every query must lie in [raw_pos0, raw_pos0 + T_raw)
+ *         (checked on the host when seq_pos is NULL; the caller's guarantee otherwise).
  * out     [B][Nq][H][d] F32, lse [B][Nq][H] F32 (natural log; -inf and o = 0 when no key).
  * kv_dtype F32 or BF16 (q has the same dtype).  ratio is the CSA pooling ratio.
  * Limits: 1 <= H <= 64, d % 8 == 0, 8 <= d <= 256, H*d <= 4096, 0 <= k <= 4096,
@@ -202,21 +207,23 @@ size_t hcsa_csa_sparse_attn_workspace_size(int B, int Nq, int H, int d, int k, i
 int hcsa_csa_sparse_attn(const void *q, const void *kc, const void *vc, int64_t c_bstride,
                          int N, const int32_t *topk_idx, int k, const void *k_raw,
                          const void *v_raw, int64_t raw_bstride, int64_t T_raw,
-                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0, int kv_dtype,
-                         int B, int Nq, int H, int d, float scale, float *out, float *lse,
-                         void *workspace, size_t ws_bytes, hcsa_stream stream);
+                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
+                         const int64_t *seq_pos, int kv_dtype, int B, int Nq, int H, int d,
+                         float scale, float *out, float *lse, void *workspace, size_t ws_bytes,
+                         hcsa_stream stream);
 
 /*
  * HCA dense attention [Lighthouse section 八 item 3; tulong.co 技术架构创新 item 1]:
- * for each query token (position pos0 + i) and head, one softmax over every visible
- * entry j < min(N, (p+1)/ratio) of kh/vh [B][N][d] (h_bstride elements).
+ * for each query token (position p = pos0 + i, or seq_pos[b] + i) and head, one softmax
+ * over every visible entry j < min(N, (p+1)/ratio) of kh/vh [B][N][d] (h_bstride
+ * elements).
  * Same q/out/lse layout and limits as hcsa_csa_sparse_attn.
  */
 size_t hcsa_hca_dense_attn_workspace_size(int B, int Nq, int H, int d, int N);
 int hcsa_hca_dense_attn(const void *q, const void *kh, const void *vh, int64_t h_bstride,
-                        int N, int ratio, int64_t pos0, int kv_dtype, int B, int Nq, int H,
-                        int d, float scale, float *out, float *lse, void *workspace,
-                        size_t ws_bytes, hcsa_stream stream);
+                        int N, int ratio, int64_t pos0, const int64_t *seq_pos, int kv_dtype,
+                        int B, int Nq, int H, int d, float scale, float *out, float *lse,
+                        void *workspace, size_t ws_bytes, hcsa_stream stream);
 
 #ifdef __cplusplus
 }

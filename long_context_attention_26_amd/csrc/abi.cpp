@@ -162,6 +162,14 @@ size_t hcsa_topk_workspace_size(int score_dtype, int B, int Nq, int N, int k) {
   return hcsa::plan_topk(score_dtype, B * Nq, N, k).total_bytes;
 }
 
+// Per-sequence positions (ragged batches): a device array of B int64 values, each >= 0
+// (not checked: device memory), or null.
+static int check_seq_pos(const int64_t* seq_pos) {
+  if (seq_pos && reinterpret_cast<uintptr_t>(seq_pos) % 8 != 0)
+    return fail(HCSA_EALIGN, "seq_pos must be 8-byte aligned");
+  return HCSA_OK;
+}
+
 static int check_topk_args(int score_dtype, int B, int Nq, int N, int ratio, int64_t pos0,
                            int k) {
   if (score_dtype != HCSA_F32 && score_dtype != HCSA_BF16)
@@ -178,9 +186,11 @@ static int check_topk_args(int score_dtype, int B, int Nq, int N, int ratio, int
 }
 
 int hcsa_topk(const void* scores, int score_dtype, int64_t row_stride, int B, int Nq, int N,
-              int ratio, int64_t pos0, int k, int32_t* idx, void* workspace,
-              size_t ws_bytes, hcsa_stream stream) {
+              int ratio, int64_t pos0, const int64_t* seq_pos, int k, int32_t* idx,
+              void* workspace, size_t ws_bytes, hcsa_stream stream) {
   int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
+  if (rc) return rc;
+  rc = check_seq_pos(seq_pos);
   if (rc) return rc;
   if (row_stride < N) return fail(HCSA_EINVAL, "row_stride < N");
   if (!scores || !idx) return fail(HCSA_EINVAL, "scores and idx must be non-null");
@@ -189,7 +199,7 @@ int hcsa_topk(const void* scores, int score_dtype, int64_t row_stride, int B, in
   rc = check_ws(workspace, ws_bytes, plan.total_bytes);
   if (rc) return rc;
   return hip_status(hcsa::launch_topk(plan, scores, score_dtype, row_stride, Nq, ratio, pos0,
-                                      idx, workspace, static_cast<hipStream_t>(stream)),
+                                      seq_pos, idx, workspace, static_cast<hipStream_t>(stream)),
                     "hcsa_topk");
 }
 
@@ -232,9 +242,11 @@ static int check_index_args(const void* q_idx, int q_dtype, const float* w_idx,
 int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
                           const void* k_idx, int k_dtype, int64_t k_bstride,
                           const uint8_t* k_scales, int64_t ks_bstride, int B, int Nq, int H_I,
-                          int d_I, int N, int ratio, int64_t pos0, int score_dtype,
-                          void* scores, hcsa_stream stream) {
+                          int d_I, int N, int ratio, int64_t pos0, const int64_t* seq_pos,
+                          int score_dtype, void* scores, hcsa_stream stream) {
   int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, 1);
+  if (rc) return rc;
+  rc = check_seq_pos(seq_pos);
   if (rc) return rc;
   rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
                         B, Nq, H_I, d_I, N);
@@ -243,7 +255,7 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
   if (!aligned16(scores)) return fail(HCSA_EALIGN, "scores must be 16-byte aligned");
   return hip_status(hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
                                               k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                              pos0, score_dtype, scores,
+                                              pos0, seq_pos, score_dtype, scores,
                                               static_cast<hipStream_t>(stream)),
                     "hcsa_csa_index_scores");
 }
@@ -251,10 +263,12 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
 int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, const void* k_idx,
                         int k_dtype, int64_t k_bstride, const uint8_t* k_scales,
                         int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
-                        int64_t pos0, int k, int score_dtype, int32_t* topk_idx,
-                        void* scores_out, void* workspace, size_t ws_bytes,
+                        int64_t pos0, const int64_t* seq_pos, int k, int score_dtype,
+                        int32_t* topk_idx, void* scores_out, void* workspace, size_t ws_bytes,
                         hcsa_stream stream) {
   int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
+  if (rc) return rc;
+  rc = check_seq_pos(seq_pos);
   if (rc) return rc;
   rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
                         B, Nq, H_I, d_I, N);
@@ -271,9 +285,9 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   void* tws = static_cast<char*>(workspace) + sbytes;
   hipError_t e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
                                            k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                           pos0, score_dtype, scores, s);
+                                           pos0, seq_pos, score_dtype, scores, s);
   if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (scores)");
-  e = hcsa::launch_topk(plan, scores, score_dtype, N, Nq, ratio, pos0, topk_idx, tws, s);
+  e = hcsa::launch_topk(plan, scores, score_dtype, N, Nq, ratio, pos0, seq_pos, topk_idx, tws, s);
   return hip_status(e, "hcsa_csa_index_topk (select)");
 }
 
@@ -290,10 +304,13 @@ size_t hcsa_csa_sparse_attn_workspace_size(int B, int Nq, int H, int d, int k, i
 int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t c_bstride,
                          int N, const int32_t* topk_idx, int k, const void* k_raw,
                          const void* v_raw, int64_t raw_bstride, int64_t T_raw,
-                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0, int kv_dtype,
-                         int B, int Nq, int H, int d, float scale, float* out, float* lse,
-                         void* workspace, size_t ws_bytes, hcsa_stream stream) {
+                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
+                         const int64_t* seq_pos, int kv_dtype, int B, int Nq, int H, int d,
+                         float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                         hcsa_stream stream) {
   int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
+  if (rc) return rc;
+  rc = check_seq_pos(seq_pos);
   if (rc) return rc;
   if (k < 0 || k > 4096) return fail(HCSA_EINVAL, "k must be in [0, 4096]");
   if (n_win < 0 || n_win > 4096) return fail(HCSA_EINVAL, "n_win must be in [0, 4096]");
@@ -310,9 +327,10 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
     if ((raw_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "raw_bstride alignment");
     if (T_raw < 1) return fail(HCSA_EINVAL, "T_raw must be >= 1");
     if (B > 1 && raw_bstride < T_raw * d) return fail(HCSA_EINVAL, "raw_bstride < T_raw*d");
+    // (with per-sequence positions, which sit in device memory, the caller guarantees it)
     const int64_t first = pos0 - n_win + 1 > 0 ? pos0 - n_win + 1 : 0;
     const int64_t last = pos0 + Nq - 1;
-    if (first < raw_pos0 || last >= raw_pos0 + T_raw)
+    if (!seq_pos && (first < raw_pos0 || last >= raw_pos0 + T_raw))
       return fail(HCSA_EINVAL, "window positions [%lld, %lld] not inside the raw rows [%lld, %lld)",
                   static_cast<long long>(first), static_cast<long long>(last),
                   static_cast<long long>(raw_pos0), static_cast<long long>(raw_pos0 + T_raw));
@@ -324,7 +342,7 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
   hcsa::AttnArgs a{};
   a.q = q; a.kc = kc; a.vc = vc; a.c_bstride = c_bstride; a.N = N > 0 ? N : 0; a.ratio = ratio;
   a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
-  a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0;
+  a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
   a.out = out; a.lse = lse;
   return hip_status(hcsa::launch_attention(true, a, plan, workspace, static_cast<hipStream_t>(stream)),
@@ -339,10 +357,12 @@ size_t hcsa_hca_dense_attn_workspace_size(int B, int Nq, int H, int d, int N) {
 }
 
 int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h_bstride,
-                        int N, int ratio, int64_t pos0, int kv_dtype, int B, int Nq, int H,
-                        int d, float scale, float* out, float* lse, void* workspace,
-                        size_t ws_bytes, hcsa_stream stream) {
+                        int N, int ratio, int64_t pos0, const int64_t* seq_pos, int kv_dtype,
+                        int B, int Nq, int H, int d, float scale, float* out, float* lse,
+                        void* workspace, size_t ws_bytes, hcsa_stream stream) {
   int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
+  if (rc) return rc;
+  rc = check_seq_pos(seq_pos);
   if (rc) return rc;
   if (N < 0) return fail(HCSA_EINVAL, "N must be >= 0");
   if (N > 0) {
@@ -357,7 +377,7 @@ int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h
   hcsa::AttnArgs a{};
   a.q = q; a.kc = kh; a.vc = vh; a.c_bstride = h_bstride; a.N = N; a.ratio = ratio;
   a.idx = nullptr; a.k = 0; a.k_raw = nullptr; a.v_raw = nullptr; a.raw_bstride = 0;
-  a.T_raw = 0; a.raw_pos0 = 0; a.n_win = 0; a.pos0 = pos0;
+  a.T_raw = 0; a.raw_pos0 = 0; a.n_win = 0; a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
   a.out = out; a.lse = lse;
   return hip_status(hcsa::launch_attention(false, a, plan, workspace, static_cast<hipStream_t>(stream)),

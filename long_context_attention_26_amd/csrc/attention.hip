@@ -50,6 +50,7 @@ struct AttnDev {
   int64_t raw_bstride, T_raw, raw_pos0;
   int n_win;
   int64_t pos0;
+  const int64_t* seq_pos;   // [B] or null
   int Nq, H, d;
   float scale;
   int chunk, splits, rows;
@@ -69,7 +70,7 @@ template <bool CSA>
 __device__ __forceinline__ RowKeys row_keys(const AttnDev& A, int row) {
   RowKeys r;
   r.b = row / A.Nq;
-  const int64_t p = A.pos0 + (row % A.Nq);
+  const int64_t p = query_pos(A.seq_pos, A.pos0, r.b, row % A.Nq);
   const int64_t v = (p + 1) / A.ratio;
   r.nv = static_cast<int>(v < A.N ? v : A.N);
   if constexpr (CSA) {
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
   const int head = col & 15;
   const bool tok_ok = tok < A.Nq;
   auto visible = [&](int t) -> int {
-    const int64_t p = A.pos0 + t;
+    const int64_t p = query_pos(A.seq_pos, A.pos0, b, t);
     const int64_t v = (p + 1) / A.ratio;
     return static_cast<int>(v < A.N ? v : A.N);
   };
@@ -759,6 +760,7 @@ hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, v
   A.raw_pos0 = a.raw_pos0;
   A.n_win = a.n_win;
   A.pos0 = a.pos0;
+  A.seq_pos = a.seq_pos;
   A.Nq = a.Nq;
   A.H = a.H;
   A.d = a.d;

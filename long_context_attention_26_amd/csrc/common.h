@@ -48,6 +48,12 @@ __device__ __forceinline__ uint32_t bf16_key(uint32_t h) {
 
 // max(x, 0) in one instruction (median of x, 0, +inf); fmaxf costs a canonicalizing max
 // first.  The sign of a zero result is not defined; callers add it to a +0-started sum.
+// Position of query token i of sequence b: seq_pos[b] + i when a per-sequence array is
+// given (ragged batches), else pos0 + i.
+__device__ __forceinline__ int64_t query_pos(const int64_t* seq_pos, int64_t pos0, int b, int i) {
+  return (seq_pos ? seq_pos[b] : pos0) + i;
+}
+
 __device__ __forceinline__ float relu(float x) {
   return __builtin_amdgcn_fmed3f(x, 0.0f, __builtin_inff());
 }

@@ -46,6 +46,7 @@ struct IdxDev {
   int64_t k_bstride;
   int Nq, N, ratio, d_I;
   int64_t pos0;
+  const int64_t* seq_pos;   // [B] or null
   void* scores;      // [rows][N]
   int chunk;
   int rows_total;    // B*Nq*H_I (prefill GEMM)
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
   constexpr int U = 4;
   const int row = blockIdx.y;
   const int b = row / A.Nq;
-  const int64_t p = A.pos0 + (row % A.Nq);
+  const int64_t p = query_pos(A.seq_pos, A.pos0, b, row % A.Nq);
   const int64_t nv64 = (p + 1) / A.ratio;
   const int nv = static_cast<int>(nv64 < A.N ? nv64 : A.N);
   const int start = blockIdx.x * A.chunk;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
   const int kstart = blockIdx.x * A.chunk;
   const int kend = min(kstart + A.chunk, A.N);
   auto visible_tok = [&](int64_t tok) -> int {
-    const int64_t p = A.pos0 + tok % A.Nq;
+    const int64_t p = query_pos(A.seq_pos, A.pos0, b, static_cast<int>(tok % A.Nq));
     const int64_t v = (p + 1) / A.ratio;
     return static_cast<int>(v < A.N ? v : A.N);
   };
@@ -372,6 +373,7 @@ struct IdxMxDev {
   int64_t k_bstride, ks_bstride;
   int Nq, N, ratio, d_I;
   int64_t pos0;
+  const int64_t* seq_pos;   // [B] or null
   void* scores;
   int chunk;
 };
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   constexpr int U = 4;
   const int row = blockIdx.y;
   const int b = row / A.Nq;
-  const int64_t p = A.pos0 + (row % A.Nq);
+  const int64_t p = query_pos(A.seq_pos, A.pos0, b, row % A.Nq);
   const int64_t nv64 = (p + 1) / A.ratio;
   const int nv = static_cast<int>(nv64 < A.N ? nv64 : A.N);
   const int start = blockIdx.x * A.chunk;
@@ -538,8 +540,8 @@ hipError_t launch_mx_mfma(const IdxMxDev& A, int rows, int H_I, int score_dtype,
 hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
                                      const uint8_t* kx, int64_t k_bstride, const uint8_t* ks,
                                      int64_t ks_bstride, int B, int Nq, int H_I, int d_I,
-                                     int N, int ratio, int64_t pos0, int score_dtype,
-                                     void* scores, hipStream_t s) {
+                                     int N, int ratio, int64_t pos0, const int64_t* seq_pos,
+                                     int score_dtype, void* scores, hipStream_t s) {
   IdxMxDev A;
   A.q = q;
   A.w = w;
@@ -552,6 +554,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.ratio = ratio;
   A.d_I = d_I;
   A.pos0 = pos0;
+  A.seq_pos = seq_pos;
   A.scores = scores;
   // at most 2048 keys per block: more, shorter blocks shorten the grid's last round
   A.chunk = std::min(index_chunk(B * Nq, N), 2048);
@@ -563,11 +566,11 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
 hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const void* kx,
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
-                               int ratio, int64_t pos0, int score_dtype, void* scores,
-                               hipStream_t s) {
+                               int ratio, int64_t pos0, const int64_t* seq_pos,
+                               int score_dtype, void* scores, hipStream_t s) {
   if (k_dtype == 2)
     return launch_mxfp4_index_scores(q, q_dtype, w, static_cast<const uint8_t*>(kx), k_bstride,
-                                     ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0,
+                                     ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos,
                                      score_dtype, scores, s);
   IdxDev A;
   A.q = q;
@@ -579,6 +582,7 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.ratio = ratio;
   A.d_I = d_I;
   A.pos0 = pos0;
+  A.seq_pos = seq_pos;
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
   const int rows = B * Nq;

@@ -28,15 +28,15 @@ struct TopkPlan {
 TopkPlan plan_topk(int score_dtype, int rows, int N, int k);
 bool topk_plan_ok(const TopkPlan& plan);        // the row length is within the selector's range
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
-                       int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
-                       void* ws, hipStream_t s);
+                       int64_t row_stride, int Nq, int ratio, int64_t pos0,
+                       const int64_t* seq_pos, int32_t* idx, void* ws, hipStream_t s);
 
 // ---- indexer.hip
 hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const void* kx,
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
-                               int ratio, int64_t pos0, int score_dtype, void* scores,
-                               hipStream_t s);
+                               int ratio, int64_t pos0, const int64_t* seq_pos,
+                               int score_dtype, void* scores, hipStream_t s);
 
 void time_next_indexer(hipEvent_t start, hipEvent_t stop);
 
@@ -56,6 +56,7 @@ struct AttnArgs {
   int64_t T_raw, raw_pos0;
   int n_win;
   int64_t pos0;
+  const int64_t* seq_pos;  // [B] or null: query i of sequence b at seq_pos[b] + i
   int kv_dtype, B, Nq, H, d;
   float scale;
   float* out;

@@ -41,11 +41,12 @@ struct TopkDev {
   int64_t row_stride;   // elements
   int Nq, N, ratio, k;
   int64_t pos0;
+  const int64_t* seq_pos;   // [B] or null
   int32_t* idx;         // [rows][k]
 };
 
 __device__ __forceinline__ int visible(const TopkDev& P, int row) {
-  const int64_t p = P.pos0 + (row % P.Nq);
+  const int64_t p = query_pos(P.seq_pos, P.pos0, row / P.Nq, row % P.Nq);
   const int64_t v = (p + 1) / P.ratio;
   return static_cast<int>(v < P.N ? v : P.N);
 }
@@ -822,8 +823,8 @@ TopkPlan plan_topk(int score_dtype, int rows, int N, int k) {
 bool topk_plan_ok(const TopkPlan& plan) { return plan.rows_path || plan.nseg <= kResMaxSeg; }
 
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
-                       int64_t row_stride, int Nq, int ratio, int64_t pos0, int32_t* idx,
-                       void* ws, hipStream_t s) {
+                       int64_t row_stride, int Nq, int ratio, int64_t pos0,
+                       const int64_t* seq_pos, int32_t* idx, void* ws, hipStream_t s) {
   (void)score_dtype;
   TopkDev P{};
   P.scores = scores;
@@ -833,6 +834,7 @@ hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype
   P.ratio = ratio;
   P.k = plan.k;
   P.pos0 = pos0;
+  P.seq_pos = seq_pos;
   P.idx = idx;
   const int esz = plan.key_bits / 8;
   const int vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride * esz) % 16 == 0;

@@ -28,18 +28,18 @@ _SIGS = {
     "hcsa_compress_kv_batched": (_i, [_p, _i, _i, _p]),
     "hcsa_mxfp4_quantize": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
     "hcsa_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
-    "hcsa_topk": (_i, [_p, _i, _i64, _i, _i, _i, _i, _i64, _i, _p, _p, _sz, _p]),
+    "hcsa_topk": (_i, [_p, _i, _i64, _i, _i, _i, _i, _i64, _p, _i, _p, _p, _sz, _p]),
     "hcsa_csa_index_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_csa_index_topk": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
-                                 _i64, _i, _i, _p, _p, _p, _sz, _p]),
+                                 _i64, _p, _i, _i, _p, _p, _p, _sz, _p]),
     "hcsa_csa_index_scores": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
-                                   _i64, _i, _p, _p]),
+                                   _i64, _p, _i, _p, _p]),
     "hcsa_csa_sparse_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "hcsa_csa_sparse_attn": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64, _i,
-                                  _i, _i64, _i, _i, _i, _i, _i, _f, _p, _p, _p, _sz, _p]),
+                                  _i, _i64, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p, _sz, _p]),
     "hcsa_hca_dense_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
-    "hcsa_hca_dense_attn": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _i, _i, _i, _i, _i, _f, _p,
-                                 _p, _p, _sz, _p]),
+    "hcsa_hca_dense_attn": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _p, _i, _i, _i, _i, _i, _f,
+                                 _p, _p, _p, _sz, _p]),
 }
 MAX_POOL_JOBS = 8
 
@@ -86,6 +86,15 @@ def _ptr(t):
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _pos_ptr(seq_pos, B):
+    """Device pointer of an int64 [B] per-sequence position tensor, or None."""
+    if seq_pos is None:
+        return None
+    if seq_pos.dtype != torch.int64 or seq_pos.numel() != B or not seq_pos.is_contiguous():
+        raise ValueError("seq_pos must be a contiguous int64 tensor of B positions")
+    return seq_pos.data_ptr()
 
 
 def time_next_indexer(start_event, stop_event):
@@ -151,13 +160,15 @@ def topk_workspace_size(score_dtype, B, Nq, N, k):
     return lib.hcsa_topk_workspace_size(score_dtype, B, Nq, N, k)
 
 
-def topk(scores, B, Nq, N, ratio, pos0, k, idx, workspace=None, stream=None):
-    """Select per row of scores [B*Nq, row_stride] (F32/BF16) into idx int32 [B*Nq, k]."""
+def topk(scores, B, Nq, N, ratio, pos0, k, idx, workspace=None, stream=None, seq_pos=None):
+    """Select per row of scores [B*Nq, row_stride] (F32/BF16) into idx int32 [B*Nq, k].
+    seq_pos: optional int64 [B] device tensor of per-sequence positions (ragged batches)."""
     sdt = dtype_code(scores)
     if workspace is None:
         workspace = alloc_workspace(topk_workspace_size(sdt, B, Nq, N, k), scores.device)
-    _check(lib.hcsa_topk(_ptr(scores), sdt, scores.stride(0), B, Nq, N, ratio, pos0, k,
-                         _ptr(idx), _ptr(workspace), workspace.numel(), _stream(stream)))
+    _check(lib.hcsa_topk(_ptr(scores), sdt, scores.stride(0), B, Nq, N, ratio, pos0,
+                         _pos_ptr(seq_pos, B), k, _ptr(idx), _ptr(workspace), workspace.numel(),
+                         _stream(stream)))
     return idx
 
 
@@ -166,7 +177,7 @@ def index_topk_workspace_size(B, Nq, N, k, score_dtype):
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx,
-                   k_scales=None, scores_out=None, workspace=None, stream=None):
+                   k_scales=None, scores_out=None, workspace=None, stream=None, seq_pos=None):
     """q_idx [B, Nq, H_I, d_I], w_idx [B, Nq, H_I] f32, k_idx [B, >=N, d_I] (F32/BF16) or
     packed MXFP4 uint8 [B, >=N, d_I/2] with k_scales [B, >=N, d_I/32]."""
     B, Nq, H_I, d_I = q_idx.shape
@@ -179,13 +190,15 @@ def csa_index_topk(q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx
                                     q_idx.device)
     _check(lib.hcsa_csa_index_topk(_ptr(q_idx), dtype_code(q_idx), _ptr(w_idx), _ptr(k_idx),
                                    k_dt, k_idx.stride(0), _ptr(k_scales), ksb, B, Nq, H_I,
-                                   d_I, N, ratio, pos0, k, score_dtype, _ptr(topk_idx),
+                                   d_I, N, ratio, pos0, _pos_ptr(seq_pos, B), k, score_dtype,
+                                   _ptr(topk_idx),
                                    _ptr(scores_out), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
     return topk_idx
 
 
-def csa_index_scores(q_idx, w_idx, k_idx, N, ratio, pos0, scores, k_scales=None, stream=None):
+def csa_index_scores(q_idx, w_idx, k_idx, N, ratio, pos0, scores, k_scales=None, stream=None,
+                     seq_pos=None):
     """Indexer scores only, into scores [B*Nq, N] (F32 or BF16)."""
     B, Nq, H_I, d_I = q_idx.shape
     if k_idx.dtype == torch.uint8:
@@ -194,8 +207,8 @@ def csa_index_scores(q_idx, w_idx, k_idx, N, ratio, pos0, scores, k_scales=None,
         k_dt, ksb = dtype_code(k_idx), 0
     _check(lib.hcsa_csa_index_scores(_ptr(q_idx), dtype_code(q_idx), _ptr(w_idx), _ptr(k_idx),
                                      k_dt, k_idx.stride(0), _ptr(k_scales), ksb, B, Nq, H_I,
-                                     d_I, N, ratio, pos0, dtype_code(scores), _ptr(scores),
-                                     _stream(stream)))
+                                     d_I, N, ratio, pos0, _pos_ptr(seq_pos, B),
+                                     dtype_code(scores), _ptr(scores), _stream(stream)))
     return scores
 
 
@@ -204,7 +217,7 @@ def csa_attn_workspace_size(B, Nq, H, d, k, n_win):
 
 
 def csa_sparse_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio, pos0, scale,
-                    out, lse, workspace=None, stream=None):
+                    out, lse, workspace=None, stream=None, seq_pos=None):
     """q [B, Nq, H, d]; kc, vc [B, >=N, d]; topk_idx [B, Nq, k]; k_raw, v_raw [B, T_raw, d]."""
     B, Nq, H, d = q.shape
     k = topk_idx.shape[-1]
@@ -213,7 +226,8 @@ def csa_sparse_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio
     _check(lib.hcsa_csa_sparse_attn(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N,
                                     _ptr(topk_idx), k, _ptr(k_raw), _ptr(v_raw),
                                     k_raw.stride(0), k_raw.shape[1], raw_pos0, n_win, ratio,
-                                    pos0, dtype_code(q), B, Nq, H, d, scale, _ptr(out),
+                                    pos0, _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d,
+                                    scale, _ptr(out),
                                     _ptr(lse), _ptr(workspace), workspace.numel(),
                                     _stream(stream)))
     return out, lse
@@ -223,12 +237,14 @@ def hca_attn_workspace_size(B, Nq, H, d, N):
     return lib.hcsa_hca_dense_attn_workspace_size(B, Nq, H, d, N)
 
 
-def hca_dense_attn(q, kh, vh, N, ratio, pos0, scale, out, lse, workspace=None, stream=None):
+def hca_dense_attn(q, kh, vh, N, ratio, pos0, scale, out, lse, workspace=None, stream=None,
+                   seq_pos=None):
     """q [B, Nq, H, d]; kh, vh [B, >=N, d]."""
     B, Nq, H, d = q.shape
     if workspace is None:
         workspace = alloc_workspace(hca_attn_workspace_size(B, Nq, H, d, N), q.device)
     _check(lib.hcsa_hca_dense_attn(_ptr(q), _ptr(kh), _ptr(vh), kh.stride(0), N, ratio, pos0,
-                                   dtype_code(q), B, Nq, H, d, scale, _ptr(out), _ptr(lse),
+                                   _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d, scale,
+                                   _ptr(out), _ptr(lse),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse

@@ -61,8 +61,10 @@ def test_topk_validation(H):
     L = H.lib
     ws = H.lib.hcsa_topk_workspace_size(H.BF16, 1, 1, 100, 10)
     assert ws > 0
-    def call(k=10, N=100, stride=100, ws_ptr=FAKE, ws_bytes=ws, dt=H.BF16, ratio=1, pos0=99):
-        return L.hcsa_topk(FAKE, dt, stride, 1, 1, N, ratio, pos0, k, FAKE, ws_ptr, ws_bytes, None)
+    def call(k=10, N=100, stride=100, ws_ptr=FAKE, ws_bytes=ws, dt=H.BF16, ratio=1, pos0=99,
+             seq_pos=None):
+        return L.hcsa_topk(FAKE, dt, stride, 1, 1, N, ratio, pos0, seq_pos, k, FAKE, ws_ptr,
+                           ws_bytes, None)
     assert call(k=0) == H.EINVAL
     assert call(k=5000) == H.EINVAL
     assert call(stride=50) == H.EINVAL
@@ -72,6 +74,7 @@ def test_topk_validation(H):
     assert call(dt=H.MXFP4) == H.EDTYPE
     assert call(ratio=0) == H.EINVAL
     assert call(pos0=-1) == H.EINVAL
+    assert call(seq_pos=FAKE + 4) == H.EALIGN          # per-sequence positions: 8-byte aligned
 
 
 def test_index_topk_validation(H):
@@ -79,7 +82,7 @@ def test_index_topk_validation(H):
     ws = L.hcsa_csa_index_topk_workspace_size(1, 1, 1024, 64, H.F32)
     def call(q_dt=H.F32, k_dt=H.F32, H_I=1, d_I=32, ks=None):
         return L.hcsa_csa_index_topk(FAKE, q_dt, FAKE, FAKE, k_dt, 0, ks, 0, 1, 1, H_I, d_I,
-                                     1024, 4, 4095, 64, H.F32, FAKE, None, FAKE, ws, None)
+                                     1024, 4, 4095, None, 64, H.F32, FAKE, None, FAKE, ws, None)
     assert call(H_I=3) == H.EINVAL
     assert call(d_I=48) == H.EINVAL
     assert call(q_dt=H.BF16) == H.EDTYPE
@@ -90,21 +93,23 @@ def test_index_topk_validation(H):
 def test_attention_validation(H):
     L = H.lib
     ws = L.hcsa_csa_sparse_attn_workspace_size(1, 1, 16, 128, 64, 128)
-    def csa(H_=16, d=128, raw_pos0=0, T_raw=4096, pos0=4095, n_win=128, kdt=H.BF16, k=64):
+    def csa(H_=16, d=128, raw_pos0=0, T_raw=4096, pos0=4095, n_win=128, kdt=H.BF16, k=64,
+            seq_pos=None):
         return L.hcsa_csa_sparse_attn(FAKE, FAKE, FAKE, 0, 1024, FAKE, k, FAKE, FAKE, 0, T_raw,
-                                      raw_pos0, n_win, 4, pos0, kdt, 1, 1, H_, d, 0.1, FAKE,
-                                      FAKE, FAKE, ws, None)
+                                      raw_pos0, n_win, 4, pos0, seq_pos, kdt, 1, 1, H_, d, 0.1,
+                                      FAKE, FAKE, FAKE, ws, None)
     assert csa(H_=65) == H.EINVAL
     assert csa(d=12) == H.EINVAL
     assert csa(kdt=H.MXFP4) == H.EDTYPE
     assert csa(raw_pos0=4000) == H.EINVAL                # window starts before the raw rows
     assert csa(T_raw=100, raw_pos0=3900, pos0=4095) == H.EINVAL  # window ends after them
     assert csa(k=5000) == H.EINVAL
+    assert csa(seq_pos=FAKE + 12) == H.EALIGN
     hws = L.hcsa_hca_dense_attn_workspace_size(1, 1, 16, 128, 32)
-    assert L.hcsa_hca_dense_attn(FAKE, FAKE, MIS, 0, 32, 128, 4095, H.BF16, 1, 1, 16, 128,
-                                 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
-    assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 0, 4095, H.BF16, 1, 1, 16, 128,
-                                 0.1, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, MIS, 0, 32, 128, 4095, None, H.BF16, 1, 1, 16,
+                                 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 0, 4095, None, H.BF16, 1, 1, 16,
+                                 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
 
 
 def test_workspace_sizes_are_monotone(H):
