@@ -47,6 +47,8 @@
  *   - seq_pos (the calls that take pos0): NULL, or a device array of B int64 positions,
  *     8-byte aligned, each >= 0, giving the position of query 0 of each sequence; pos0 is
  *     then unused.  Its values sit in device memory and are not validated on the host.
+ *   - pages (the calls that read or write caches): NULL for contiguous caches, or a paged
+ *     layout (hcsa_pages below).
  */
 #ifndef HCSA_H
 #define HCSA_H
@@ -59,6 +61,21 @@ extern "C" {
 #endif
 
 typedef void *hcsa_stream; /* hipStream_t */
+
+/*
+ * Paged caches [the heterogeneous KV cache in 128-token blocks, lcm(m, m') = lcm(4, 128):
+ * Lighthouse section 八 item 7].  Positions [128*blk, 128*blk + 128) of sequence b live in
+ * page block_table[b*table_stride + blk] of every cache tensor.  A tensor pooled at ratio r
+ * (r divides 128) holds 128/r rows per page: its pointer is then a page pool
+ * [pages][128/r][row] (raw tokens: 128 rows per page, CSA entries and indexer keys 32, HCA
+ * entries 1) and its bstride argument is ignored.  The table is device memory (int32,
+ * 4-byte aligned), must cover every block holding a position a call touches, and is not
+ * validated on the host.
+ */
+typedef struct hcsa_pages {
+  const int32_t *block_table;
+  int64_t table_stride;
+} hcsa_pages;
 
 enum hcsa_dtype { HCSA_F32 = 0, HCSA_BF16 = 1, HCSA_MXFP4 = 2 };
 
@@ -106,7 +123,9 @@ int hcsa_compress_kv(const void *x, int x_dtype, int64_t x_bstride, int B, int T
  * indexer-key blocks and the HCA K and V blocks that one decode token completes).  Each job
  * has the meaning and limits of hcsa_compress_kv (x has its own T; jobs share B).  The
  * call validates every job first and launches nothing if any is invalid.  Outputs of
- * different jobs must not overlap.
+ * different jobs must not overlap.  With pages, x and y (and y_scales) are page pools,
+ * ratio divides 128, and a job pools the tokens [pos0, pos0 + T) of every sequence into
+ * its entries pos0/ratio .. (pos0 + T)/ratio - 1 (pos0 a multiple of ratio).
  */
 #define HCSA_MAX_POOL_JOBS 8
 typedef struct hcsa_pool_job {
@@ -121,8 +140,10 @@ typedef struct hcsa_pool_job {
   int64_t y_bstride;
   uint8_t *y_scales;
   int64_t ys_bstride;
+  int64_t pos0;        /* paged form only: position of x's first token (a multiple of ratio) */
 } hcsa_pool_job;
-int hcsa_compress_kv_batched(const hcsa_pool_job *jobs, int n_jobs, int B, hcsa_stream stream);
+int hcsa_compress_kv_batched(const hcsa_pool_job *jobs, int n_jobs, int B,
+                             const hcsa_pages *pages, hcsa_stream stream);
 
 /*
  * MXFP4 quantization of rows [rows][D] (F32 or BF16) into packed codes [rows][D/2] and
@@ -173,9 +194,9 @@ size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score
 int hcsa_csa_index_topk(const void *q_idx, int q_dtype, const float *w_idx, const void *k_idx,
                         int k_dtype, int64_t k_bstride, const uint8_t *k_scales,
                         int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
-                        int64_t pos0, const int64_t *seq_pos, int k, int score_dtype,
-                        int32_t *topk_idx, void *scores_out, void *workspace, size_t ws_bytes,
-                        hcsa_stream stream);
+                        int64_t pos0, const int64_t *seq_pos, const hcsa_pages *pages, int k,
+                        int score_dtype, int32_t *topk_idx, void *scores_out, void *workspace,
+                        size_t ws_bytes, hcsa_stream stream);
 
 /*
  * Lightning-indexer scores only (the first half of hcsa_csa_index_topk; same arguments
@@ -186,7 +207,8 @@ int hcsa_csa_index_scores(const void *q_idx, int q_dtype, const float *w_idx,
                           const void *k_idx, int k_dtype, int64_t k_bstride,
                           const uint8_t *k_scales, int64_t ks_bstride, int B, int Nq, int H_I,
                           int d_I, int N, int ratio, int64_t pos0, const int64_t *seq_pos,
-                          int score_dtype, void *scores, hcsa_stream stream);
+                          const hcsa_pages *pages, int score_dtype, void *scores,
+                          hcsa_stream stream);
 
 /*
  * CSA sparse attention [Lighthouse section 八 item 3]: for each query token (position
@@ -197,7 +219,8 @@ int hcsa_csa_index_scores(const void *q_idx, int q_dtype, const float *w_idx,
  * q       [B][Nq][H][d]; kc, vc [B][N][d] (c_bstride elements); topk_idx [B][Nq][k].
  * k_raw, v_raw [B][T_raw][d] (raw_bstride elements); row t holds position raw_pos0 + t.
  *         Every window position of every query must lie in [raw_pos0, raw_pos0 + T_raw)
- *         (checked on the host when seq_pos is NULL; the caller's guarantee otherwise).
+ *         (checked on the host when seq_pos and pages are NULL; the caller's guarantee
+ *         otherwise).  With pages, k_raw/v_raw are raw-token page pools and raw_pos0 is 0.
  * out     [B][Nq][H][d] F32, lse [B][Nq][H] F32 (natural log; -inf and o = 0 when no key).
  * kv_dtype F32 or BF16 (q has the same dtype).  ratio is the CSA pooling ratio.
  * Limits: 1 <= H <= 64, d % 8 == 0, 8 <= d <= 256, H*d <= 4096, 0 <= k <= 4096,
@@ -208,9 +231,9 @@ int hcsa_csa_sparse_attn(const void *q, const void *kc, const void *vc, int64_t 
                          int N, const int32_t *topk_idx, int k, const void *k_raw,
                          const void *v_raw, int64_t raw_bstride, int64_t T_raw,
                          int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
-                         const int64_t *seq_pos, int kv_dtype, int B, int Nq, int H, int d,
-                         float scale, float *out, float *lse, void *workspace, size_t ws_bytes,
-                         hcsa_stream stream);
+                         const int64_t *seq_pos, const hcsa_pages *pages, int kv_dtype, int B,
+                         int Nq, int H, int d, float scale, float *out, float *lse,
+                         void *workspace, size_t ws_bytes, hcsa_stream stream);
 
 /*
  * HCA dense attention [Lighthouse section 八 item 3; tulong.co 技术架构创新 item 1]:
@@ -221,9 +244,10 @@ int hcsa_csa_sparse_attn(const void *q, const void *kc, const void *vc, int64_t 
  */
 size_t hcsa_hca_dense_attn_workspace_size(int B, int Nq, int H, int d, int N);
 int hcsa_hca_dense_attn(const void *q, const void *kh, const void *vh, int64_t h_bstride,
-                        int N, int ratio, int64_t pos0, const int64_t *seq_pos, int kv_dtype,
-                        int B, int Nq, int H, int d, float scale, float *out, float *lse,
-                        void *workspace, size_t ws_bytes, hcsa_stream stream);
+                        int N, int ratio, int64_t pos0, const int64_t *seq_pos,
+                        const hcsa_pages *pages, int kv_dtype, int B, int Nq, int H, int d,
+                        float scale, float *out, float *lse, void *workspace, size_t ws_bytes,
+                        hcsa_stream stream);
 
 #ifdef __cplusplus
 }

@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "internal.h"
@@ -67,6 +68,21 @@ int check_attn_common(const void* q, int kv_dtype, int B, int Nq, int H, int d, 
   return HCSA_OK;
 }
 
+// Paged caches: a block table (device int32, 4-byte aligned) and its row stride, or null;
+// every pooling ratio of the call must divide the 128-token page.
+int check_pages(const hcsa_pages* pages, std::initializer_list<int> ratios) {
+  if (!pages) return HCSA_OK;
+  if (!pages->block_table) return fail(HCSA_EINVAL, "pages->block_table must be non-null");
+  if (reinterpret_cast<uintptr_t>(pages->block_table) % 4 != 0)
+    return fail(HCSA_EALIGN, "pages->block_table must be 4-byte aligned");
+  if (pages->table_stride < 1) return fail(HCSA_EINVAL, "pages->table_stride must be >= 1");
+  for (int r : ratios)
+    if (r < 1 || 128 % r != 0) return fail(HCSA_EINVAL, "paged caches need ratios dividing 128 (got %d)", r);
+  return HCSA_OK;
+}
+const int32_t* page_table(const hcsa_pages* pages) { return pages ? pages->block_table : nullptr; }
+int64_t page_stride(const hcsa_pages* pages) { return pages ? pages->table_stride : 0; }
+
 }  // namespace
 
 extern "C" {
@@ -99,17 +115,28 @@ int hcsa_compress_kv(const void* x, int x_dtype, int64_t x_bstride, int B, int T
                     "hcsa_compress_kv");
 }
 
-int hcsa_compress_kv_batched(const hcsa_pool_job* jobs, int n_jobs, int B, hcsa_stream stream) {
+int hcsa_compress_kv_batched(const hcsa_pool_job* jobs, int n_jobs, int B,
+                             const hcsa_pages* pages, hcsa_stream stream) {
   if (n_jobs < 0 || n_jobs > HCSA_MAX_POOL_JOBS)
     return fail(HCSA_EINVAL, "n_jobs must be in [0, %d]", HCSA_MAX_POOL_JOBS);
   if (n_jobs > 0 && !jobs) return fail(HCSA_EINVAL, "jobs must be non-null");
+  int rc = check_pages(pages, {});
+  if (rc) return rc;
   for (int i = 0; i < n_jobs; ++i) {
     const hcsa_pool_job& q = jobs[i];
-    const int rc = check_compress(q.x, q.x_dtype, q.x_bstride, B, q.T, q.D, q.omega, q.ratio,
-                                  q.y, q.y_dtype, q.y_bstride, q.y_scales, q.ys_bstride);
+    // paged: the strides are unused (checked as for one sequence)
+    rc = check_compress(q.x, q.x_dtype, q.x_bstride, pages ? 1 : B, q.T, q.D, q.omega, q.ratio,
+                        q.y, q.y_dtype, q.y_bstride, q.y_scales, q.ys_bstride);
+    if (!rc && pages) {
+      rc = check_pages(pages, {q.ratio});
+      if (!rc && (q.pos0 < 0 || q.pos0 % q.ratio != 0))
+        rc = fail(HCSA_EINVAL, "pos0 must be a non-negative multiple of ratio");
+    }
     if (rc) return fail(rc, "job %d: %s", i, g_err.c_str());
   }
-  return hip_status(hcsa::launch_compress_batched(jobs, n_jobs, B, static_cast<hipStream_t>(stream)),
+  return hip_status(hcsa::launch_compress_batched(jobs, n_jobs, B, page_table(pages),
+                                                  page_stride(pages),
+                                                  static_cast<hipStream_t>(stream)),
                     "hcsa_compress_kv_batched");
 }
 
@@ -214,7 +241,7 @@ size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score
 static int check_index_args(const void* q_idx, int q_dtype, const float* w_idx,
                             const void* k_idx, int k_dtype, int64_t k_bstride,
                             const uint8_t* k_scales, int64_t ks_bstride, int B, int Nq,
-                            int H_I, int d_I, int N) {
+                            int H_I, int d_I, int N, bool paged = false) {
   if (k_dtype != HCSA_F32 && k_dtype != HCSA_BF16 && k_dtype != HCSA_MXFP4)
     return fail(HCSA_EDTYPE, "k_dtype must be F32, BF16 or MXFP4");
   if (q_dtype != HCSA_F32 && q_dtype != HCSA_BF16) return fail(HCSA_EDTYPE, "q_dtype must be F32 or BF16");
@@ -228,6 +255,7 @@ static int check_index_args(const void* q_idx, int q_dtype, const float* w_idx,
   if (k_dtype == HCSA_MXFP4 && !k_scales) return fail(HCSA_EINVAL, "MXFP4 keys need k_scales");
   if (!aligned16(q_idx) || !aligned16(k_idx))
     return fail(HCSA_EALIGN, "q_idx and k_idx must be 16-byte aligned");
+  if (paged) return HCSA_OK;                     // page pools: the strides are unused
   const int64_t kb = k_dtype == HCSA_MXFP4 ? k_bstride : k_bstride * elem_size(k_dtype);
   if (kb % 16 != 0) return fail(HCSA_EALIGN, "k_bstride must keep 16-byte alignment");
   if (B > 1) {
@@ -243,19 +271,23 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
                           const void* k_idx, int k_dtype, int64_t k_bstride,
                           const uint8_t* k_scales, int64_t ks_bstride, int B, int Nq, int H_I,
                           int d_I, int N, int ratio, int64_t pos0, const int64_t* seq_pos,
-                          int score_dtype, void* scores, hcsa_stream stream) {
+                          const hcsa_pages* pages, int score_dtype, void* scores,
+                          hcsa_stream stream) {
   int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, 1);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
   if (rc) return rc;
+  rc = check_pages(pages, {ratio});
+  if (rc) return rc;
   rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
-                        B, Nq, H_I, d_I, N);
+                        B, Nq, H_I, d_I, N, pages != nullptr);
   if (rc) return rc;
   if (!scores) return fail(HCSA_EINVAL, "scores must be non-null");
   if (!aligned16(scores)) return fail(HCSA_EALIGN, "scores must be 16-byte aligned");
   return hip_status(hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
                                               k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                              pos0, seq_pos, score_dtype, scores,
+                                              pos0, seq_pos, page_table(pages),
+                                              page_stride(pages), score_dtype, scores,
                                               static_cast<hipStream_t>(stream)),
                     "hcsa_csa_index_scores");
 }
@@ -263,15 +295,17 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
 int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, const void* k_idx,
                         int k_dtype, int64_t k_bstride, const uint8_t* k_scales,
                         int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
-                        int64_t pos0, const int64_t* seq_pos, int k, int score_dtype,
-                        int32_t* topk_idx, void* scores_out, void* workspace, size_t ws_bytes,
-                        hcsa_stream stream) {
+                        int64_t pos0, const int64_t* seq_pos, const hcsa_pages* pages, int k,
+                        int score_dtype, int32_t* topk_idx, void* scores_out, void* workspace,
+                        size_t ws_bytes, hcsa_stream stream) {
   int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
   if (rc) return rc;
+  rc = check_pages(pages, {ratio});
+  if (rc) return rc;
   rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
-                        B, Nq, H_I, d_I, N);
+                        B, Nq, H_I, d_I, N, pages != nullptr);
   if (rc) return rc;
   if (!topk_idx) return fail(HCSA_EINVAL, "topk_idx must be non-null");
   if (!aligned16(topk_idx) || (scores_out && !aligned16(scores_out)))
@@ -285,7 +319,8 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   void* tws = static_cast<char*>(workspace) + sbytes;
   hipError_t e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
                                            k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                           pos0, seq_pos, score_dtype, scores, s);
+                                           pos0, seq_pos, page_table(pages), page_stride(pages),
+                                           score_dtype, scores, s);
   if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (scores)");
   e = hcsa::launch_topk(plan, scores, score_dtype, N, Nq, ratio, pos0, seq_pos, topk_idx, tws, s);
   return hip_status(e, "hcsa_csa_index_topk (select)");
@@ -305,13 +340,17 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
                          int N, const int32_t* topk_idx, int k, const void* k_raw,
                          const void* v_raw, int64_t raw_bstride, int64_t T_raw,
                          int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
-                         const int64_t* seq_pos, int kv_dtype, int B, int Nq, int H, int d,
-                         float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
-                         hcsa_stream stream) {
+                         const int64_t* seq_pos, const hcsa_pages* pages, int kv_dtype, int B,
+                         int Nq, int H, int d, float scale, float* out, float* lse,
+                         void* workspace, size_t ws_bytes, hcsa_stream stream) {
   int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
   if (rc) return rc;
+  rc = check_pages(pages, {ratio});
+  if (rc) return rc;
+  if (pages && raw_pos0 != 0) return fail(HCSA_EINVAL, "paged raw tokens need raw_pos0 == 0");
+  const bool paged = pages != nullptr;
   if (k < 0 || k > 4096) return fail(HCSA_EINVAL, "k must be in [0, 4096]");
   if (n_win < 0 || n_win > 4096) return fail(HCSA_EINVAL, "n_win must be in [0, 4096]");
   if (k > 0) {
@@ -319,18 +358,19 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
     if (!kc || !vc || !topk_idx) return fail(HCSA_EINVAL, "kc, vc and topk_idx must be non-null");
     if (!aligned16(kc) || !aligned16(vc)) return fail(HCSA_EALIGN, "kc and vc must be 16-byte aligned");
     if ((c_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "c_bstride alignment");
-    if (B > 1 && c_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "c_bstride < N*d");
+    if (!paged && B > 1 && c_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "c_bstride < N*d");
   }
   if (n_win > 0) {
     if (!k_raw || !v_raw) return fail(HCSA_EINVAL, "k_raw and v_raw must be non-null");
     if (!aligned16(k_raw) || !aligned16(v_raw)) return fail(HCSA_EALIGN, "k_raw and v_raw alignment");
     if ((raw_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "raw_bstride alignment");
     if (T_raw < 1) return fail(HCSA_EINVAL, "T_raw must be >= 1");
-    if (B > 1 && raw_bstride < T_raw * d) return fail(HCSA_EINVAL, "raw_bstride < T_raw*d");
-    // (with per-sequence positions, which sit in device memory, the caller guarantees it)
+    if (!paged && B > 1 && raw_bstride < T_raw * d) return fail(HCSA_EINVAL, "raw_bstride < T_raw*d");
+    // (with per-sequence positions, which sit in device memory, or paged raw tokens, the
+    // caller guarantees it)
     const int64_t first = pos0 - n_win + 1 > 0 ? pos0 - n_win + 1 : 0;
     const int64_t last = pos0 + Nq - 1;
-    if (!seq_pos && (first < raw_pos0 || last >= raw_pos0 + T_raw))
+    if (!seq_pos && !paged && (first < raw_pos0 || last >= raw_pos0 + T_raw))
       return fail(HCSA_EINVAL, "window positions [%lld, %lld] not inside the raw rows [%lld, %lld)",
                   static_cast<long long>(first), static_cast<long long>(last),
                   static_cast<long long>(raw_pos0), static_cast<long long>(raw_pos0 + T_raw));
@@ -343,6 +383,7 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
   a.q = q; a.kc = kc; a.vc = vc; a.c_bstride = c_bstride; a.N = N > 0 ? N : 0; a.ratio = ratio;
   a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
   a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0; a.seq_pos = seq_pos;
+  a.block_table = page_table(pages); a.table_stride = page_stride(pages);
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
   a.out = out; a.lse = lse;
   return hip_status(hcsa::launch_attention(true, a, plan, workspace, static_cast<hipStream_t>(stream)),
@@ -357,19 +398,22 @@ size_t hcsa_hca_dense_attn_workspace_size(int B, int Nq, int H, int d, int N) {
 }
 
 int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h_bstride,
-                        int N, int ratio, int64_t pos0, const int64_t* seq_pos, int kv_dtype,
-                        int B, int Nq, int H, int d, float scale, float* out, float* lse,
-                        void* workspace, size_t ws_bytes, hcsa_stream stream) {
+                        int N, int ratio, int64_t pos0, const int64_t* seq_pos,
+                        const hcsa_pages* pages, int kv_dtype, int B, int Nq, int H, int d,
+                        float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                        hcsa_stream stream) {
   int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
+  if (rc) return rc;
+  rc = check_pages(pages, {ratio});
   if (rc) return rc;
   if (N < 0) return fail(HCSA_EINVAL, "N must be >= 0");
   if (N > 0) {
     if (!kh || !vh) return fail(HCSA_EINVAL, "kh and vh must be non-null");
     if (!aligned16(kh) || !aligned16(vh)) return fail(HCSA_EALIGN, "kh and vh must be 16-byte aligned");
     if ((h_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "h_bstride alignment");
-    if (B > 1 && h_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "h_bstride < N*d");
+    if (!pages && B > 1 && h_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "h_bstride < N*d");
   }
   const hcsa::AttnPlan plan = hcsa::plan_attention(false, kv_dtype, B, Nq, H, d, N);
   rc = check_ws(workspace, ws_bytes, plan.total_bytes);
@@ -378,6 +422,7 @@ int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h
   a.q = q; a.kc = kh; a.vc = vh; a.c_bstride = h_bstride; a.N = N; a.ratio = ratio;
   a.idx = nullptr; a.k = 0; a.k_raw = nullptr; a.v_raw = nullptr; a.raw_bstride = 0;
   a.T_raw = 0; a.raw_pos0 = 0; a.n_win = 0; a.pos0 = pos0; a.seq_pos = seq_pos;
+  a.block_table = page_table(pages); a.table_stride = page_stride(pages);
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
   a.out = out; a.lse = lse;
   return hip_status(hcsa::launch_attention(false, a, plan, workspace, static_cast<hipStream_t>(stream)),

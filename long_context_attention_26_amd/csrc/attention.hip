@@ -51,6 +51,8 @@ struct AttnDev {
   int n_win;
   int64_t pos0;
   const int64_t* seq_pos;   // [B] or null
+  PageMap pm;               // paged caches (table null: contiguous)
+  int c_log2;               // log2 of the compressed cache's rows per page
   int Nq, H, d;
   float scale;
   int chunk, splits, rows;
@@ -104,9 +106,12 @@ template <typename TE>
 __device__ __forceinline__ const TE* key_row(const AttnDev& A, int b, int code, bool value) {
   if (code >= 0) {
     const TE* base = static_cast<const TE*>(value ? A.vc : A.kc);
+    if (A.pm.table) return base + row_off<true>(A.pm, 0, b, code, A.c_log2, A.d);
     return base + b * A.c_bstride + static_cast<int64_t>(code) * A.d;
   }
   const TE* base = static_cast<const TE*>(value ? A.v_raw : A.k_raw);
+  // raw rows: one per token, 128 per page, at position raw_pos0 + row
+  if (A.pm.table) return base + row_off<true>(A.pm, 0, b, A.raw_pos0 + (-code - 2), 7, A.d);
   return base + b * A.raw_bstride + static_cast<int64_t>(-code - 2) * A.d;
 }
 
@@ -371,6 +376,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
 // a block's 4 waves streams its own contiguous run of the block's chunk, 32 entries a step,
 // the next step's K and V rows loaded while the current step is computed.
 // grid: (splits, rows); block 256.
+template <bool PAGED>
 __global__ __launch_bounds__(256, 2) void hca_decode_kernel(AttnDev A) {
   __shared__ float s_o[4][16][129];
   __shared__ float s_ml[4][2][16];
@@ -396,23 +402,25 @@ __global__ __launch_bounds__(256, 2) void hca_decode_kernel(AttnDev A) {
   float m_run = -INFINITY, l_run = 0.0f;
   const float sl2 = A.scale * 1.4426950408889634f;   // logits in base 2
 
-  const uint16_t* kb = static_cast<const uint16_t*>(A.kc) + r.b * A.c_bstride;
-  const uint16_t* vb = static_cast<const uint16_t*>(A.vc) + r.b * A.c_bstride;
+  const uint16_t* kb = static_cast<const uint16_t*>(A.kc);
+  const uint16_t* vb = static_cast<const uint16_t*>(A.vc);
+  auto erow = [&](int e) { return row_off<PAGED>(A.pm, A.c_bstride, r.b, e, A.c_log2, 128); };
   // K rows of keys base + 16t + col; V slices (channels 8col..) of keys base + 16*(j/4) + 4g + j%4
   auto load = [&](int base, u32x4 (&ka)[2][4], u32x4 (&vv)[8], bool (&ok)[8]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int e = base + 16 * t + col;
+      const int64_t o = e < w1 ? erow(e) : 0;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        ka[t][s] = e < w1 ? *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(e) * 128 + 32 * s + 8 * g)
+        ka[t][s] = e < w1 ? *reinterpret_cast<const u32x4*>(kb + o + 32 * s + 8 * g)
                           : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int e = base + 16 * (j >> 2) + 4 * g + (j & 3);
       ok[j] = e < w1;
-      vv[j] = ok[j] ? *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(e) * 128 + 8 * col)
+      vv[j] = ok[j] ? *reinterpret_cast<const u32x4*>(vb + erow(e) + 8 * col)
                     : u32x4{0, 0, 0, 0};
     }
   };
@@ -483,8 +491,12 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
     for (int s = 0; s < 8; ++s)
       qb[s] = tok_ok ? *reinterpret_cast<const u32x4*>(qr + 16 * s) : u32x4{0u, 0u, 0u, 0u};
   }
-  const uint16_t* kseq = static_cast<const uint16_t*>(A.kc) + b * A.c_bstride;
-  const uint16_t* vseq = static_cast<const uint16_t*>(A.vc) + b * A.c_bstride;
+  const uint16_t* kpool = static_cast<const uint16_t*>(A.kc);
+  const uint16_t* vpool = static_cast<const uint16_t*>(A.vc);
+  auto erow = [&](int e) -> int64_t {
+    return A.pm.table ? row_off<true>(A.pm, 0, b, e, A.c_log2, 128)
+                      : b * A.c_bstride + static_cast<int64_t>(e) * 128;
+  };
   // tile loads: thread i moves K channels 8*(i%16) .. +7 of entries i/16 and i/16 + 32, and
   // V channels 8*(i%16) .. +7 of entries 2*(i/16) and 2*(i/16)+1 (packed in pairs for the
   // transposed tile)
@@ -494,10 +506,10 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int ek = tile * kHKeys + lkey + 32 * u;
-      kf[u] = ek < A.N ? *reinterpret_cast<const u32x4*>(kseq + static_cast<int64_t>(ek) * 128 + 8 * lpart)
+      kf[u] = ek < A.N ? *reinterpret_cast<const u32x4*>(kpool + erow(ek) + 8 * lpart)
                        : u32x4{0u, 0u, 0u, 0u};
       const int ev = tile * kHKeys + 2 * lkey + u;
-      vf[u] = ev < A.N ? *reinterpret_cast<const u32x4*>(vseq + static_cast<int64_t>(ev) * 128 + 8 * lpart)
+      vf[u] = ev < A.N ? *reinterpret_cast<const u32x4*>(vpool + erow(ev) + 8 * lpart)
                        : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -761,6 +773,10 @@ hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, v
   A.n_win = a.n_win;
   A.pos0 = a.pos0;
   A.seq_pos = a.seq_pos;
+  A.pm.table = a.block_table;
+  A.pm.stride = a.table_stride;
+  A.c_log2 = 0;
+  for (int per = kPageTokens / a.ratio; per > 1; per >>= 1) ++A.c_log2;
   A.Nq = a.Nq;
   A.H = a.H;
   A.d = a.d;
@@ -787,7 +803,8 @@ hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, v
   }
   dim3 grid(plan.splits, plan.rows);
   if (plan.hca_decode) {
-    hca_decode_kernel<<<grid, 256, 0, s>>>(A);
+    if (a.block_table) hca_decode_kernel<true><<<grid, 256, 0, s>>>(A);
+    else hca_decode_kernel<false><<<grid, 256, 0, s>>>(A);
   } else if (plan.mfma) {
     if (csa) attn_mfma_kernel<true><<<grid, 256, 0, s>>>(A);
     else attn_mfma_kernel<false><<<grid, 256, 0, s>>>(A);

@@ -48,6 +48,30 @@ __device__ __forceinline__ uint32_t bf16_key(uint32_t h) {
 
 // max(x, 0) in one instruction (median of x, 0, +inf); fmaxf costs a canonicalizing max
 // first.  The sign of a zero result is not defined; callers add it to a +0-started sum.
+// Paged caches: positions [128 * blk, 128 * blk + 128) of sequence b live in page
+// table[b * stride + blk] of every cache tensor; a tensor pooled at ratio r (r divides 128)
+// holds 128 / r rows per page, so its pointer is a pool [pages][128 / r][row].  A null
+// table means contiguous tensors [B][...] with a per-sequence stride.
+constexpr int kPageTokens = 128;
+
+struct PageMap {
+  const int32_t* table;
+  int64_t stride;
+};
+
+// Offset (in row units of `row` elements or bytes) of row j of sequence b in a tensor with
+// 2^per_log2 rows per page, or b * bstride + j * row when contiguous.
+template <bool PAGED>
+__device__ __forceinline__ int64_t row_off(const PageMap& pm, int64_t bstride, int b, int64_t j,
+                                           int per_log2, int row) {
+  if constexpr (PAGED) {
+    const int64_t pg = pm.table[b * pm.stride + (j >> per_log2)];
+    return ((pg << per_log2) + (j & ((1 << per_log2) - 1))) * row;
+  } else {
+    return b * bstride + j * row;
+  }
+}
+
 // Position of query token i of sequence b: seq_pos[b] + i when a per-sequence array is
 // given (ragged batches), else pos0 + i.
 __device__ __forceinline__ int64_t query_pos(const int64_t* seq_pos, int64_t pos0, int b, int i) {

@@ -90,12 +90,23 @@ __device__ __forceinline__ void pool_weights(const float* __restrict__ omega, in
   __syncthreads();
 }
 
+// Source row (in D-element rows) of entry j's first token and the entry's output row, for
+// paged tensors: the entry's r tokens lie in one 128-token page (r divides 128 and the
+// job starts on an entry boundary), so one lookup serves all of them.
+__device__ __forceinline__ void paged_rows(const PageMap& pm, int b, int64_t pos0, int r,
+                                           int64_t j, int64_t& xrow, int64_t& yrow) {
+  xrow = row_off<true>(pm, 0, b, pos0 + j * r, 7, 1);
+  yrow = row_off<true>(pm, 0, b, pos0 / r + j, __builtin_ctz(kPageTokens / r), 1);
+}
+
 // One block of the pooling: this thread's 8 channels of entry `j` (block-local row `local`).
-template <bool IN_BF16, int OUT>
+template <bool IN_BF16, int OUT, bool PAGED = false>
 __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_bs, int D,
                                           const float* alpha, int r, void* __restrict__ y,
                                           int64_t y_bs, uint8_t* __restrict__ ys, int64_t ys_bs,
-                                          int n_out, int64_t jblock, int b) {
+                                          int n_out, int64_t jblock, int b,
+                                          const PageMap& pm = PageMap{nullptr, 0},
+                                          int64_t pos0 = 0) {
   const int tpr = D >> 3;                       // threads per output row
   const int rows_per_block = blockDim.x / tpr;
   const int local = threadIdx.x / tpr;
@@ -104,7 +115,10 @@ __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_
   const int64_t j = jblock * rows_per_block + local;
   if (j >= n_out) return;
   constexpr int ES = IN_BF16 ? 2 : 4;
-  const char* src = static_cast<const char*>(x) + (b * x_bs + j * r * D + c8 * 8) * ES;
+  int64_t xrow = 0, yrow = 0;
+  if constexpr (PAGED) paged_rows(pm, b, pos0, r, j, xrow, yrow);
+  const char* src = static_cast<const char*>(x) +
+                    ((PAGED ? xrow * D : b * x_bs + j * r * D) + c8 * 8) * ES;
   const int64_t row_bytes = static_cast<int64_t>(D) * ES;
 
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -118,9 +132,10 @@ __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_
   }
 
   if constexpr (OUT == OUT_MXFP4) {
-    store8<OUT>(acc, y, b * y_bs + j * (D >> 1), ys, b * ys_bs + j * (D >> 5), c8);
+    if constexpr (PAGED) store8<OUT>(acc, y, yrow * (D >> 1), ys, yrow * (D >> 5), c8);
+    else store8<OUT>(acc, y, b * y_bs + j * (D >> 1), ys, b * ys_bs + j * (D >> 5), c8);
   } else {
-    store8<OUT>(acc, y, b * y_bs + j * D, nullptr, 0, c8);
+    store8<OUT>(acc, y, PAGED ? yrow * D : b * y_bs + j * D, nullptr, 0, c8);
   }
 }
 
@@ -129,19 +144,24 @@ __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_
 // thread's loads are independent; the G partial sums are added in group order in LDS.
 constexpr int kWideRatio = 32;
 
-template <bool IN_BF16, int OUT>
+template <bool IN_BF16, int OUT, bool PAGED = false>
 __device__ __forceinline__ void pool_rows_wide(const void* __restrict__ x, int64_t x_bs, int D,
                                                const float* alpha, int r, void* __restrict__ y,
                                                int64_t y_bs, uint8_t* __restrict__ ys,
-                                               int64_t ys_bs, int64_t j, int b, float* s_part) {
+                                               int64_t ys_bs, int64_t j, int b, float* s_part,
+                                               const PageMap& pm = PageMap{nullptr, 0},
+                                               int64_t pos0 = 0) {
   const int tpr = D >> 3;
   const int G = blockDim.x / tpr;
   const int g = threadIdx.x / tpr;
   const int c8 = threadIdx.x - g * tpr;
   constexpr int ES = IN_BF16 ? 2 : 4;
+  int64_t xrow = 0, yrow = 0;
+  if constexpr (PAGED) paged_rows(pm, b, pos0, r, j, xrow, yrow);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (g < G) {
-    const char* src = static_cast<const char*>(x) + (b * x_bs + j * r * D + c8 * 8) * ES;
+    const char* src = static_cast<const char*>(x) +
+                      ((PAGED ? xrow * D : b * x_bs + j * r * D) + c8 * 8) * ES;
     const int64_t row_bytes = static_cast<int64_t>(D) * ES;
 #pragma unroll 8
     for (int i = g; i < r; i += G) {
@@ -162,9 +182,10 @@ __device__ __forceinline__ void pool_rows_wide(const void* __restrict__ x, int64
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] += s_part[gg * D + c8 * 8 + c];
     if constexpr (OUT == OUT_MXFP4) {
-      store8<OUT>(acc, y, b * y_bs + j * (D >> 1), ys, b * ys_bs + j * (D >> 5), c8);
+      if constexpr (PAGED) store8<OUT>(acc, y, yrow * (D >> 1), ys, yrow * (D >> 5), c8);
+      else store8<OUT>(acc, y, b * y_bs + j * (D >> 1), ys, b * ys_bs + j * (D >> 5), c8);
     } else {
-      store8<OUT>(acc, y, b * y_bs + j * D, nullptr, 0, c8);
+      store8<OUT>(acc, y, PAGED ? yrow * D : b * y_bs + j * D, nullptr, 0, c8);
     }
   }
 }
@@ -201,19 +222,23 @@ struct PoolJobs {
   hcsa_pool_job job[HCSA_MAX_POOL_JOBS];
   int first_block[HCSA_MAX_POOL_JOBS + 1];
   int n;
+  PageMap pm;        // paged caches (table null: contiguous)
 };
 
-template <bool IN_BF16, int OUT>
-__device__ __forceinline__ void pool_job_blocks(const hcsa_pool_job& q, const float* alpha,
-                                                int64_t jb, int n_out, float* s_part) {
+template <bool IN_BF16, int OUT, bool PAGED>
+__device__ __forceinline__ void pool_job_blocks(const hcsa_pool_job& q, const PageMap& pm,
+                                                const float* alpha, int64_t jb, int n_out,
+                                                float* s_part) {
   if (q.ratio >= kWideRatio)
-    pool_rows_wide<IN_BF16, OUT>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride,
-                                 q.y_scales, q.ys_bstride, jb, blockIdx.y, s_part);
+    pool_rows_wide<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y,
+                                        q.y_bstride, q.y_scales, q.ys_bstride, jb, blockIdx.y,
+                                        s_part, pm, q.pos0);
   else
-    pool_rows<IN_BF16, OUT>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride,
-                            q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y);
+    pool_rows<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride,
+                                   q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y, pm, q.pos0);
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
   __shared__ float alpha[1024];
   __shared__ float s_part[2048];
@@ -224,17 +249,22 @@ __global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
   const int64_t jb = blockIdx.x - J.first_block[t];
   const int n_out = q.T / q.ratio;
   const bool ib = q.x_dtype == 1;
-  if (ib && q.y_dtype == 1) pool_job_blocks<true, OUT_BF16>(q, alpha, jb, n_out, s_part);
-  else if (ib && q.y_dtype == 2) pool_job_blocks<true, OUT_MXFP4>(q, alpha, jb, n_out, s_part);
-  else if (ib) pool_job_blocks<true, OUT_F32>(q, alpha, jb, n_out, s_part);
-  else if (q.y_dtype == 1) pool_job_blocks<false, OUT_BF16>(q, alpha, jb, n_out, s_part);
-  else if (q.y_dtype == 2) pool_job_blocks<false, OUT_MXFP4>(q, alpha, jb, n_out, s_part);
-  else pool_job_blocks<false, OUT_F32>(q, alpha, jb, n_out, s_part);
+  const PageMap& pm = J.pm;
+  if (ib && q.y_dtype == 1) pool_job_blocks<true, OUT_BF16, PAGED>(q, pm, alpha, jb, n_out, s_part);
+  else if (ib && q.y_dtype == 2) pool_job_blocks<true, OUT_MXFP4, PAGED>(q, pm, alpha, jb, n_out, s_part);
+  else if (ib) pool_job_blocks<true, OUT_F32, PAGED>(q, pm, alpha, jb, n_out, s_part);
+  else if (q.y_dtype == 1) pool_job_blocks<false, OUT_BF16, PAGED>(q, pm, alpha, jb, n_out, s_part);
+  else if (q.y_dtype == 2) pool_job_blocks<false, OUT_MXFP4, PAGED>(q, pm, alpha, jb, n_out, s_part);
+  else pool_job_blocks<false, OUT_F32, PAGED>(q, pm, alpha, jb, n_out, s_part);
 }
 
-hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B, hipStream_t s) {
+hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B,
+                                   const int32_t* block_table, int64_t table_stride,
+                                   hipStream_t s) {
   PoolJobs J{};
   J.n = 0;
+  J.pm.table = block_table;
+  J.pm.stride = table_stride;
   int blocks = 0;
   for (int i = 0; i < n; ++i) {
     const int n_out = jobs[i].T / jobs[i].ratio;
@@ -246,7 +276,8 @@ hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B, hipS
   }
   J.first_block[J.n] = blocks;
   if (blocks == 0) return hipSuccess;
-  compress_batched_kernel<<<dim3(blocks, B), 256, 0, s>>>(J);
+  if (block_table) compress_batched_kernel<true><<<dim3(blocks, B), 256, 0, s>>>(J);
+  else compress_batched_kernel<false><<<dim3(blocks, B), 256, 0, s>>>(J);
   return hipGetLastError();
 }
 

@@ -47,6 +47,8 @@ struct IdxDev {
   int Nq, N, ratio, d_I;
   int64_t pos0;
   const int64_t* seq_pos;   // [B] or null
+  PageMap pm;        // paged keys (table null: contiguous)
+  int c_log2;        // log2 of the keys' rows per page
   void* scores;      // [rows][N]
   int chunk;
   int rows_total;    // B*Nq*H_I (prefill GEMM)
@@ -54,6 +56,13 @@ struct IdxDev {
 
 // Keys per block of the decode kernels: enough blocks to cover every CU several times even
 // for one sequence, and at least 256 keys so a block issues a few loads per lane.
+// log2 of the rows a page holds of a tensor pooled at `ratio` (a divisor of 128).
+inline int page_rows_log2(int ratio) {
+  int l = 0;
+  for (int per = kPageTokens / ratio; per > 1; per >>= 1) ++l;
+  return l;
+}
+
 inline int index_chunk(int rows, int N) {
   int64_t c = static_cast<int64_t>(N) * rows / 2048;
   c = (c + 255) / 256 * 256;
@@ -80,7 +89,7 @@ __device__ __forceinline__ float dot16b_f32(const u32x4& a, const u32x4& b, floa
 }
 
 // grid: (ceil(N / chunk), rows); block 256.
-template <int HI, int LPE, bool KBF16, bool SBF16>
+template <int HI, int LPE, bool KBF16, bool SBF16, bool PAGED>
 __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
   constexpr int ES = KBF16 ? 2 : 4;
   constexpr int GROUPS = 256 / LPE;
@@ -106,7 +115,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
     qv[g] = *reinterpret_cast<const u32x4*>(qrow + g * row_bytes + sub * 16);
     w[g] = A.w[static_cast<int64_t>(row) * HI + g];
   }
-  const char* kbase = static_cast<const char*>(A.k) + b * A.k_bstride * ES + sub * 16;
+  const char* kbase = static_cast<const char*>(A.k) + sub * 16;
   float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
   uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
 
@@ -116,8 +125,8 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * GROUPS;
       if (j < end)
-        kv[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * row_bytes));
+        kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            kbase + row_off<PAGED>(A.pm, A.k_bstride * ES, b, j, A.c_log2, row_bytes)));
       else
         kv[u] = u32x4{0, 0, 0, 0};
     }
@@ -225,7 +234,11 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
     for (int g = 0; g < HI; ++g) w[t][g] = A.w[(tok0 + qloc[t]) * HI + g];
     nvt[t] = visible_tok(tok0 + qloc[t]);
   }
-  const uint16_t* kseq = static_cast<const uint16_t*>(A.k) + static_cast<int64_t>(b) * A.k_bstride;
+  const uint16_t* kpool = static_cast<const uint16_t*>(A.k);
+  auto krow = [&](int j) -> int64_t {
+    return A.pm.table ? row_off<true>(A.pm, 0, b, j, A.c_log2, DI)
+                      : static_cast<int64_t>(b) * A.k_bstride + static_cast<int64_t>(j) * DI;
+  };
   constexpr int PPT = (CHUNKS + NT - 1) / NT;     // key-tile pieces per thread
   u32x4 pf[PPT];
   auto fetch = [&](int j0) {
@@ -234,7 +247,7 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
       const int c = threadIdx.x + u * NT;
       const int key = c / (DI / 8), part = c % (DI / 8);
       pf[u] = (c < CHUNKS && j0 + key < A.N)
-                  ? *reinterpret_cast<const u32x4*>(kseq + static_cast<int64_t>(j0 + key) * DI + 8 * part)
+                  ? *reinterpret_cast<const u32x4*>(kpool + krow(j0 + key) + 8 * part)
                   : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -343,9 +356,11 @@ hipError_t launch_hi(const IdxDev& A, int rows, int score_dtype, hipStream_t s) 
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
   dim3 grid(nchunks, rows);
   if (score_dtype == 1)
-    launch_timed(index_scores_kernel<HI, LPE, KBF16, true>, grid, dim3(256), s, A);
+    if (A.pm.table) launch_timed(index_scores_kernel<HI, LPE, KBF16, true, true>, grid, dim3(256), s, A);
+    else launch_timed(index_scores_kernel<HI, LPE, KBF16, true, false>, grid, dim3(256), s, A);
   else
-    launch_timed(index_scores_kernel<HI, LPE, KBF16, false>, grid, dim3(256), s, A);
+    if (A.pm.table) launch_timed(index_scores_kernel<HI, LPE, KBF16, false, true>, grid, dim3(256), s, A);
+    else launch_timed(index_scores_kernel<HI, LPE, KBF16, false, false>, grid, dim3(256), s, A);
   return hipGetLastError();
 }
 
@@ -374,6 +389,8 @@ struct IdxMxDev {
   int Nq, N, ratio, d_I;
   int64_t pos0;
   const int64_t* seq_pos;   // [B] or null
+  PageMap pm;          // paged keys (table null: contiguous)
+  int c_log2;
   void* scores;
   int chunk;
 };
@@ -391,7 +408,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 constexpr int kMxMaxUnits = 16 * 4;   // H_I <= 16 heads x d_I / 32 <= 4 blocks
 
 // grid: (ceil(N / chunk), rows); block 256 (4 waves, 32 keys per MFMA).
-template <int HI, bool QBF16, bool SBF16>
+template <int HI, bool QBF16, bool SBF16, bool PAGED>
 __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   constexpr int U = 4;
   const int row = blockIdx.y;
@@ -456,8 +473,8 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   for (int g = 0; g < HI; ++g) w[g] = A.w[static_cast<int64_t>(row) * HI + g];
 
   const int rowb = A.d_I / 2;
-  const uint8_t* kbase = A.k + b * A.k_bstride;
-  const uint8_t* sbase = A.ks + b * A.ks_bstride;
+  const uint8_t* kbase = PAGED ? A.k : A.k + b * A.k_bstride;
+  const uint8_t* sbase = PAGED ? A.ks : A.ks + b * A.ks_bstride;
   float* s32 = static_cast<float*>(A.scores) + static_cast<int64_t>(row) * A.N;
   uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
 
@@ -467,6 +484,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * 128 + col;
+      const int64_t rj = PAGED && j < end ? row_off<true>(A.pm, 0, b, j, A.c_log2, 1) : j;   // pool row
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         kb[u][st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -474,12 +492,12 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
         const int blk = 2 * st + half;
         if (st < ksteps && blk < nblk && j < end) {
           const u32x4 c = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * rowb + blk * 16));
+              reinterpret_cast<const u32x4*>(kbase + rj * rowb + blk * 16));
           kb[u][st][0] = static_cast<int>(c[0]);
           kb[u][st][1] = static_cast<int>(c[1]);
           kb[u][st][2] = static_cast<int>(c[2]);
           kb[u][st][3] = static_cast<int>(c[3]);
-          ksc[u][st] = sbase[static_cast<int64_t>(j) * nblk + blk];
+          ksc[u][st] = sbase[rj * nblk + blk];
         }
       }
     }
@@ -517,9 +535,11 @@ hipError_t launch_mx_mfma_hi(const IdxMxDev& A, int rows, int score_dtype, hipSt
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
   dim3 grid(nchunks, rows);
   if (score_dtype == 1)
-    launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true>, grid, dim3(256), s, A);
+    if (A.pm.table) launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true, true>, grid, dim3(256), s, A);
+    else launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true, false>, grid, dim3(256), s, A);
   else
-    launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false>, grid, dim3(256), s, A);
+    if (A.pm.table) launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false, true>, grid, dim3(256), s, A);
+    else launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false, false>, grid, dim3(256), s, A);
   return hipGetLastError();
 }
 
@@ -541,6 +561,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
                                      const uint8_t* kx, int64_t k_bstride, const uint8_t* ks,
                                      int64_t ks_bstride, int B, int Nq, int H_I, int d_I,
                                      int N, int ratio, int64_t pos0, const int64_t* seq_pos,
+                                     const int32_t* block_table, int64_t table_stride,
                                      int score_dtype, void* scores, hipStream_t s) {
   IdxMxDev A;
   A.q = q;
@@ -555,6 +576,9 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.d_I = d_I;
   A.pos0 = pos0;
   A.seq_pos = seq_pos;
+  A.pm.table = block_table;
+  A.pm.stride = table_stride;
+  A.c_log2 = page_rows_log2(ratio);
   A.scores = scores;
   // at most 2048 keys per block: more, shorter blocks shorten the grid's last round
   A.chunk = std::min(index_chunk(B * Nq, N), 2048);
@@ -567,11 +591,12 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, const int64_t* seq_pos,
+                               const int32_t* block_table, int64_t table_stride,
                                int score_dtype, void* scores, hipStream_t s) {
   if (k_dtype == 2)
     return launch_mxfp4_index_scores(q, q_dtype, w, static_cast<const uint8_t*>(kx), k_bstride,
                                      ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos,
-                                     score_dtype, scores, s);
+                                     block_table, table_stride, score_dtype, scores, s);
   IdxDev A;
   A.q = q;
   A.w = w;
@@ -583,6 +608,9 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
   A.d_I = d_I;
   A.pos0 = pos0;
   A.seq_pos = seq_pos;
+  A.pm.table = block_table;
+  A.pm.stride = table_stride;
+  A.c_log2 = page_rows_log2(ratio);
   A.scores = scores;
   A.chunk = index_chunk(B * Nq, N);
   const int rows = B * Nq;

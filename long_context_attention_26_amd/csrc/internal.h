@@ -15,6 +15,7 @@ hipError_t launch_compress(const void* x, int x_dtype, int64_t x_bstride, int B,
                            int64_t y_bstride, uint8_t* ys, int64_t ys_bstride,
                            hipStream_t s);
 hipError_t launch_compress_batched(const struct hcsa_pool_job* jobs, int n, int B,
+                                   const int32_t* block_table, int64_t table_stride,
                                    hipStream_t s);
 hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int D,
                                  uint8_t* packed, uint8_t* scales, hipStream_t s);
@@ -36,6 +37,7 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int k_dtype, int64_t k_bstride, const uint8_t* ks,
                                int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                int ratio, int64_t pos0, const int64_t* seq_pos,
+                               const int32_t* block_table, int64_t table_stride,
                                int score_dtype, void* scores, hipStream_t s);
 
 void time_next_indexer(hipEvent_t start, hipEvent_t stop);
@@ -57,6 +59,8 @@ struct AttnArgs {
   int n_win;
   int64_t pos0;
   const int64_t* seq_pos;  // [B] or null: query i of sequence b at seq_pos[b] + i
+  const int32_t* block_table;   // paged caches [B][table_stride], or null (contiguous)
+  int64_t table_stride;
   int kv_dtype, B, Nq, H, d;
   float scale;
   float* out;

@@ -25,21 +25,22 @@ _SIGS = {
     "hcsa_last_error": (ctypes.c_char_p, []),
     "hcsa_time_next_indexer": (_i, [_p, _p]),
     "hcsa_compress_kv": (_i, [_p, _i, _i64, _i, _i, _i, _p, _i, _p, _i, _i64, _p, _i64, _p]),
-    "hcsa_compress_kv_batched": (_i, [_p, _i, _i, _p]),
+    "hcsa_compress_kv_batched": (_i, [_p, _i, _i, _p, _p]),
     "hcsa_mxfp4_quantize": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
     "hcsa_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_topk": (_i, [_p, _i, _i64, _i, _i, _i, _i, _i64, _p, _i, _p, _p, _sz, _p]),
     "hcsa_csa_index_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_csa_index_topk": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
-                                 _i64, _p, _i, _i, _p, _p, _p, _sz, _p]),
+                                 _i64, _p, _p, _i, _i, _p, _p, _p, _sz, _p]),
     "hcsa_csa_index_scores": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
-                                   _i64, _p, _i, _p, _p]),
+                                   _i64, _p, _p, _i, _p, _p]),
     "hcsa_csa_sparse_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "hcsa_csa_sparse_attn": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64, _i,
-                                  _i, _i64, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p, _sz, _p]),
+                                  _i, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p, _sz,
+                                  _p]),
     "hcsa_hca_dense_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
-    "hcsa_hca_dense_attn": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _p, _i, _i, _i, _i, _i, _f,
-                                 _p, _p, _p, _sz, _p]),
+    "hcsa_hca_dense_attn": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _p, _p, _i, _i, _i, _i, _i,
+                                 _f, _p, _p, _p, _sz, _p]),
 }
 MAX_POOL_JOBS = 8
 
@@ -48,7 +49,22 @@ class PoolJob(ctypes.Structure):
     """Mirror of struct hcsa_pool_job."""
     _fields_ = [("x", _p), ("x_dtype", _i), ("x_bstride", _i64), ("T", _i), ("D", _i),
                 ("omega", _p), ("ratio", _i), ("y", _p), ("y_dtype", _i), ("y_bstride", _i64),
-                ("y_scales", _p), ("ys_bstride", _i64)]
+                ("y_scales", _p), ("ys_bstride", _i64), ("pos0", _i64)]
+
+
+class Pages(ctypes.Structure):
+    """Mirror of struct hcsa_pages."""
+    _fields_ = [("block_table", _p), ("table_stride", _i64)]
+
+
+def _pages(table):
+    """hcsa_pages for a block table (int32 [B, max_blocks] device tensor), or None."""
+    if table is None:
+        return None
+    if table.dtype != torch.int32 or table.dim() != 2 or table.stride(1) != 1:
+        raise ValueError("the block table must be an int32 [B, max_blocks] tensor with unit "
+                         "column stride")
+    return ctypes.byref(Pages(table.data_ptr(), table.stride(0)))
 
 
 for _name, (_res, _args) in _SIGS.items():
@@ -129,22 +145,28 @@ def compress_kv(x, omega, ratio, y, y_scales=None, stream=None):
     return y
 
 
-def pool_job(x, omega, ratio, y, y_scales=None):
-    """Describe one pooling job (same tensor conventions as compress_kv)."""
-    B, T, D = x.shape
-    assert x.stride(2) == 1 and x.stride(1) == D
+def pool_job(x, omega, ratio, y, y_scales=None, T=None, pos0=0):
+    """Describe one pooling job (same tensor conventions as compress_kv).  For paged caches
+    x and y are page pools ([pages, 128, D] and [pages, 128/ratio, ...]) and the job pools
+    tokens [pos0, pos0 + T) of every sequence."""
+    D = x.shape[-1]
+    assert x.stride(-1) == 1 and x.stride(-2) == D
+    if T is None:
+        T = x.shape[1]
     if y.dtype == torch.uint8:
         y_dt, ysb = MXFP4, y_scales.stride(0)
     else:
         y_dt, ysb = dtype_code(y), 0
     return PoolJob(_ptr(x), dtype_code(x), x.stride(0), T, D, _ptr(omega), ratio, _ptr(y), y_dt,
-                   y.stride(0), _ptr(y_scales), ysb)
+                   y.stride(0), _ptr(y_scales), ysb, pos0)
 
 
-def compress_kv_batched(jobs, B, stream=None):
-    """Run up to MAX_POOL_JOBS pooling jobs (from pool_job) of one batch in one launch."""
+def compress_kv_batched(jobs, B, stream=None, block_table=None):
+    """Run up to MAX_POOL_JOBS pooling jobs (from pool_job) of one batch in one launch;
+    block_table (int32 [B, max_blocks]) selects the paged form."""
     arr = (PoolJob * max(1, len(jobs)))(*jobs)
-    _check(lib.hcsa_compress_kv_batched(ctypes.cast(arr, _p), len(jobs), B, _stream(stream)))
+    _check(lib.hcsa_compress_kv_batched(ctypes.cast(arr, _p), len(jobs), B, _pages(block_table),
+                                        _stream(stream)))
 
 
 def mxfp4_quantize(x, packed, scales, stream=None):
@@ -177,7 +199,8 @@ def index_topk_workspace_size(B, Nq, N, k, score_dtype):
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx,
-                   k_scales=None, scores_out=None, workspace=None, stream=None, seq_pos=None):
+                   k_scales=None, scores_out=None, workspace=None, stream=None, seq_pos=None,
+                   block_table=None):
     """q_idx [B, Nq, H_I, d_I], w_idx [B, Nq, H_I] f32, k_idx [B, >=N, d_I] (F32/BF16) or
     packed MXFP4 uint8 [B, >=N, d_I/2] with k_scales [B, >=N, d_I/32]."""
     B, Nq, H_I, d_I = q_idx.shape
@@ -190,15 +213,15 @@ def csa_index_topk(q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx
                                     q_idx.device)
     _check(lib.hcsa_csa_index_topk(_ptr(q_idx), dtype_code(q_idx), _ptr(w_idx), _ptr(k_idx),
                                    k_dt, k_idx.stride(0), _ptr(k_scales), ksb, B, Nq, H_I,
-                                   d_I, N, ratio, pos0, _pos_ptr(seq_pos, B), k, score_dtype,
-                                   _ptr(topk_idx),
+                                   d_I, N, ratio, pos0, _pos_ptr(seq_pos, B),
+                                   _pages(block_table), k, score_dtype, _ptr(topk_idx),
                                    _ptr(scores_out), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
     return topk_idx
 
 
 def csa_index_scores(q_idx, w_idx, k_idx, N, ratio, pos0, scores, k_scales=None, stream=None,
-                     seq_pos=None):
+                     seq_pos=None, block_table=None):
     """Indexer scores only, into scores [B*Nq, N] (F32 or BF16)."""
     B, Nq, H_I, d_I = q_idx.shape
     if k_idx.dtype == torch.uint8:
@@ -208,7 +231,8 @@ def csa_index_scores(q_idx, w_idx, k_idx, N, ratio, pos0, scores, k_scales=None,
     _check(lib.hcsa_csa_index_scores(_ptr(q_idx), dtype_code(q_idx), _ptr(w_idx), _ptr(k_idx),
                                      k_dt, k_idx.stride(0), _ptr(k_scales), ksb, B, Nq, H_I,
                                      d_I, N, ratio, pos0, _pos_ptr(seq_pos, B),
-                                     dtype_code(scores), _ptr(scores), _stream(stream)))
+                                     _pages(block_table), dtype_code(scores), _ptr(scores),
+                                     _stream(stream)))
     return scores
 
 
@@ -217,7 +241,7 @@ def csa_attn_workspace_size(B, Nq, H, d, k, n_win):
 
 
 def csa_sparse_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio, pos0, scale,
-                    out, lse, workspace=None, stream=None, seq_pos=None):
+                    out, lse, workspace=None, stream=None, seq_pos=None, block_table=None):
     """q [B, Nq, H, d]; kc, vc [B, >=N, d]; topk_idx [B, Nq, k]; k_raw, v_raw [B, T_raw, d]."""
     B, Nq, H, d = q.shape
     k = topk_idx.shape[-1]
@@ -226,8 +250,8 @@ def csa_sparse_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio
     _check(lib.hcsa_csa_sparse_attn(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N,
                                     _ptr(topk_idx), k, _ptr(k_raw), _ptr(v_raw),
                                     k_raw.stride(0), k_raw.shape[1], raw_pos0, n_win, ratio,
-                                    pos0, _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d,
-                                    scale, _ptr(out),
+                                    pos0, _pos_ptr(seq_pos, B), _pages(block_table),
+                                    dtype_code(q), B, Nq, H, d, scale, _ptr(out),
                                     _ptr(lse), _ptr(workspace), workspace.numel(),
                                     _stream(stream)))
     return out, lse
@@ -238,13 +262,13 @@ def hca_attn_workspace_size(B, Nq, H, d, N):
 
 
 def hca_dense_attn(q, kh, vh, N, ratio, pos0, scale, out, lse, workspace=None, stream=None,
-                   seq_pos=None):
+                   seq_pos=None, block_table=None):
     """q [B, Nq, H, d]; kh, vh [B, >=N, d]."""
     B, Nq, H, d = q.shape
     if workspace is None:
         workspace = alloc_workspace(hca_attn_workspace_size(B, Nq, H, d, N), q.device)
     _check(lib.hcsa_hca_dense_attn(_ptr(q), _ptr(kh), _ptr(vh), kh.stride(0), N, ratio, pos0,
-                                   _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d, scale,
-                                   _ptr(out), _ptr(lse),
+                                   _pos_ptr(seq_pos, B), _pages(block_table), dtype_code(q), B,
+                                   Nq, H, d, scale, _ptr(out), _ptr(lse),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse

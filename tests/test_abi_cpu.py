@@ -82,7 +82,8 @@ def test_index_topk_validation(H):
     ws = L.hcsa_csa_index_topk_workspace_size(1, 1, 1024, 64, H.F32)
     def call(q_dt=H.F32, k_dt=H.F32, H_I=1, d_I=32, ks=None):
         return L.hcsa_csa_index_topk(FAKE, q_dt, FAKE, FAKE, k_dt, 0, ks, 0, 1, 1, H_I, d_I,
-                                     1024, 4, 4095, None, 64, H.F32, FAKE, None, FAKE, ws, None)
+                                     1024, 4, 4095, None, None, 64, H.F32, FAKE, None, FAKE, ws,
+                                     None)
     assert call(H_I=3) == H.EINVAL
     assert call(d_I=48) == H.EINVAL
     assert call(q_dt=H.BF16) == H.EDTYPE
@@ -96,8 +97,8 @@ def test_attention_validation(H):
     def csa(H_=16, d=128, raw_pos0=0, T_raw=4096, pos0=4095, n_win=128, kdt=H.BF16, k=64,
             seq_pos=None):
         return L.hcsa_csa_sparse_attn(FAKE, FAKE, FAKE, 0, 1024, FAKE, k, FAKE, FAKE, 0, T_raw,
-                                      raw_pos0, n_win, 4, pos0, seq_pos, kdt, 1, 1, H_, d, 0.1,
-                                      FAKE, FAKE, FAKE, ws, None)
+                                      raw_pos0, n_win, 4, pos0, seq_pos, None, kdt, 1, 1, H_, d,
+                                      0.1, FAKE, FAKE, FAKE, ws, None)
     assert csa(H_=65) == H.EINVAL
     assert csa(d=12) == H.EINVAL
     assert csa(kdt=H.MXFP4) == H.EDTYPE
@@ -106,10 +107,17 @@ def test_attention_validation(H):
     assert csa(k=5000) == H.EINVAL
     assert csa(seq_pos=FAKE + 12) == H.EALIGN
     hws = L.hcsa_hca_dense_attn_workspace_size(1, 1, 16, 128, 32)
-    assert L.hcsa_hca_dense_attn(FAKE, FAKE, MIS, 0, 32, 128, 4095, None, H.BF16, 1, 1, 16,
-                                 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
-    assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 0, 4095, None, H.BF16, 1, 1, 16,
-                                 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, MIS, 0, 32, 128, 4095, None, None, H.BF16, 1, 1,
+                                 16, 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 0, 4095, None, None, H.BF16, 1, 1,
+                                 16, 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
+    # paged caches: the ratio must divide the 128-token page, the table be 4-byte aligned
+    pg = ctypes.byref(H.Pages(FAKE, 64))
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 96, 4095, None, pg, H.BF16, 1, 1,
+                                 16, 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
+    bad = ctypes.byref(H.Pages(FAKE + 2, 64))
+    assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 128, 4095, None, bad, H.BF16, 1, 1,
+                                 16, 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
 
 
 def test_workspace_sizes_are_monotone(H):
