@@ -93,8 +93,8 @@ def measured_traffic(cfg):
         rec = json.load(f)
     src = open(os.path.join(ROOT, "long_context_attention_26_amd", "csrc", "indexer.hip")).read()
     try:
-        a = src.index("template <int HI, bool QBF16, bool SBF16>\n__global__ __launch_bounds__(256) "
-                      "void index_scores_mx_mfma_kernel")
+        a = src.index("template <int HI, bool QBF16, bool SBF16, bool PAGED>\n__global__ "
+                      "__launch_bounds__(256) void index_scores_mx_mfma_kernel")
         b = src.index("template <int HI, bool QBF16>\nhipError_t launch_mx_mfma_hi(")
     except ValueError:
         return None
