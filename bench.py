@@ -81,21 +81,21 @@ def index_scan_bytes(cfg):
     return step_bytes(cfg)["index_scan"]
 
 
-def measured_traffic(cfg):
+def measured_traffic(cfg, mx_fp8=False):
     """HBM bytes per indexer launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary (scaled by a copy kernel of known size), if it covers this workload and the
     kernel's source text is unchanged since it was taken; else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "index_scores_mx_mfma_decode_b32_1m_counters.json")
-    if cfg.cid != 5 or not os.path.exists(path):
+    if cfg.cid != 5 or mx_fp8 or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     src = open(os.path.join(ROOT, "long_context_attention_26_amd", "csrc", "indexer.hip")).read()
     try:
-        a = src.index("template <int HI, bool QBF16, bool SBF16, bool PAGED>\n__global__ "
-                      "__launch_bounds__(256) void index_scores_mx_mfma_kernel")
-        b = src.index("template <int HI, bool QBF16>\nhipError_t launch_mx_mfma_hi(")
+        a = src.index("template <int HI, bool QBF16, bool SBF16, bool PAGED, bool F8>\n"
+                      "__global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel")
+        b = src.index("template <int HI, bool QBF16, bool F8>\nhipError_t launch_mx_mfma_hi(")
     except ValueError:
         return None
     if hashlib.sha256(src[a:b].encode()).hexdigest() != rec.get("kernel_text_sha256"):
@@ -178,6 +178,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="cache copies (0 = enough to defeat the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mx-fp8", action="store_true",
+                    help="MXFP4 indexer keys (workload 5): scan them on FP8 operands (codes "
+                         "widened to e4m3) instead of FP4 ones")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 2 GiB device-to-device copy 3 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -206,6 +209,11 @@ def main():
     from long_context_attention_26_amd.pipeline import DecodeStep
     steps = [step0] + [DecodeStep(st.clone_caches(), cfg.Nq, cfg.H, cfg.H_I, cfg.topk, cfg.n_win,
                                   cfg.score, cfg.scale) for _ in range(R - 1)]
+    if args.mx_fp8:
+        if cfg.idx != "mxfp4":
+            sys.exit("bench.py: --mx-fp8 needs a workload with MXFP4 indexer keys (5)")
+        for stp in steps:
+            stp.mx_fp8 = True
     torch.cuda.synchronize()
 
     # Each copy's step is captured as one HIP graph (one launch per step), and once more as
@@ -287,7 +295,7 @@ def main():
         achieved = index_scan_bytes(cfg) / (idx_us * 1e-6) / 1e9
         roof = {"kernel": "index_scores (lightning-indexer key scan)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg, args.mx_fp8),
                 "bytes_per_launch": index_scan_bytes(cfg)}
     else:
         # prefill: one launch scores every query token of the chunk against every visible
@@ -314,7 +322,9 @@ def main():
         "dtype": "bf16" if cfg.kv == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) tokens, random pooling logits and indexer weights)",
         "config": {"workload": cfg.workload, "batch": cfg.B, "context": cfg.T, "heads": cfg.H,
-                   "head_dim": cfg.d, "indexer": f"{cfg.H_I}x{cfg.d_I} {cfg.idx}",
+                   "head_dim": cfg.d,
+                   "indexer": f"{cfg.H_I}x{cfg.d_I} {cfg.idx}"
+                              + (" on fp8 operands" if args.mx_fp8 else ""),
                    "scores": cfg.score, "topk": cfg.topk, "n_win": cfg.n_win,
                    "cache_copies_rotated": R},
         "step_hbm_gbps": round(total_bytes / (el / args.steps) / 1e9, 1),

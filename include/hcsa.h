@@ -77,7 +77,15 @@ typedef struct hcsa_pages {
   int64_t table_stride;
 } hcsa_pages;
 
-enum hcsa_dtype { HCSA_F32 = 0, HCSA_BF16 = 1, HCSA_MXFP4 = 2 };
+/*
+ * Element types.  HCSA_MXFP4_FP8 is accepted only as the key type of the indexer calls: the
+ * keys are stored exactly as HCSA_MXFP4 (same codes, same scales), and the scan widens the
+ * e2m1 codes to e4m3 and runs the FP8 matrix-core instruction with the same block scales
+ * [9fzt.com digest item 4: FP4 dequantized to FP8 without loss, reusing an FP8 path;
+ * tulong.co 技术架构创新 item 2: FP4+FP8 mixed precision].  Every e2m1 value is exact in
+ * e4m3, so the scores equal those of HCSA_MXFP4 keys.
+ */
+enum hcsa_dtype { HCSA_F32 = 0, HCSA_BF16 = 1, HCSA_MXFP4 = 2, HCSA_MXFP4_FP8 = 3 };
 
 enum hcsa_status {
   HCSA_OK = 0,
@@ -184,10 +192,12 @@ int hcsa_topk(const void *scores, int score_dtype, int64_t row_stride, int B, in
  *         elements) or MXFP4 packed [B][N][d_I/2] (bstride in bytes) with k_scales
  *         [B][N][d_I/32] (ks_bstride bytes).  With MXFP4 keys the queries are quantized
  *         to MXFP4 (per head vector) inside the call and the dot products are exact.
+ *         k_dtype MXFP4 runs the scan on e2m1 operands, MXFP4_FP8 on the same codes
+ *         widened to e4m3 (same scores).
  * Scores s_j = sum_g w_g max(0, q_g . k_j) for the visible j (see hcsa_topk), rounded to
  * score_dtype, then top-k as in hcsa_topk.
  * scores_out  optional [B*Nq][N] score_dtype copy of the scores (NULL to skip).
- * Limits: H_I in {1, 2, 4, 8, 16}; d_I in {32, 64, 128} (F32 keys: {32, 64}; MXFP4: {32, 64, 128});
+ * Limits: H_I in {1, 2, 4, 8, 16}; d_I in {32, 64, 128} (F32 keys: {32, 64});
  *         q dtype F32 with F32 keys, BF16 with BF16 keys, F32 or BF16 with MXFP4 keys.
  */
 size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score_dtype);

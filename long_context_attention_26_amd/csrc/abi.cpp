@@ -242,26 +242,28 @@ static int check_index_args(const void* q_idx, int q_dtype, const float* w_idx,
                             const void* k_idx, int k_dtype, int64_t k_bstride,
                             const uint8_t* k_scales, int64_t ks_bstride, int B, int Nq,
                             int H_I, int d_I, int N, bool paged = false) {
-  if (k_dtype != HCSA_F32 && k_dtype != HCSA_BF16 && k_dtype != HCSA_MXFP4)
-    return fail(HCSA_EDTYPE, "k_dtype must be F32, BF16 or MXFP4");
+  if (k_dtype != HCSA_F32 && k_dtype != HCSA_BF16 && k_dtype != HCSA_MXFP4 &&
+      k_dtype != HCSA_MXFP4_FP8)
+    return fail(HCSA_EDTYPE, "k_dtype must be F32, BF16, MXFP4 or MXFP4_FP8");
   if (q_dtype != HCSA_F32 && q_dtype != HCSA_BF16) return fail(HCSA_EDTYPE, "q_dtype must be F32 or BF16");
-  if (k_dtype != HCSA_MXFP4 && q_dtype != k_dtype)
+  const bool mx = k_dtype == HCSA_MXFP4 || k_dtype == HCSA_MXFP4_FP8;
+  if (!mx && q_dtype != k_dtype)
     return fail(HCSA_EDTYPE, "q_dtype must equal k_dtype for F32/BF16 keys");
   if (!is_pow2(H_I) || H_I > 16) return fail(HCSA_EINVAL, "H_I must be 1, 2, 4, 8 or 16");
   if (k_dtype == HCSA_F32 && d_I != 32 && d_I != 64) return fail(HCSA_EINVAL, "F32 keys need d_I in {32, 64}");
   if (k_dtype != HCSA_F32 && d_I != 32 && d_I != 64 && d_I != 128)
     return fail(HCSA_EINVAL, "d_I must be 32, 64 or 128");
   if (!q_idx || !w_idx || !k_idx) return fail(HCSA_EINVAL, "null pointer");
-  if (k_dtype == HCSA_MXFP4 && !k_scales) return fail(HCSA_EINVAL, "MXFP4 keys need k_scales");
+  if (mx && !k_scales) return fail(HCSA_EINVAL, "MXFP4 keys need k_scales");
   if (!aligned16(q_idx) || !aligned16(k_idx))
     return fail(HCSA_EALIGN, "q_idx and k_idx must be 16-byte aligned");
   if (paged) return HCSA_OK;                     // page pools: the strides are unused
-  const int64_t kb = k_dtype == HCSA_MXFP4 ? k_bstride : k_bstride * elem_size(k_dtype);
+  const int64_t kb = mx ? k_bstride : k_bstride * elem_size(k_dtype);
   if (kb % 16 != 0) return fail(HCSA_EALIGN, "k_bstride must keep 16-byte alignment");
   if (B > 1) {
-    const int64_t row = k_dtype == HCSA_MXFP4 ? d_I / 2 : d_I;
+    const int64_t row = mx ? d_I / 2 : d_I;
     if (k_bstride < static_cast<int64_t>(N) * row) return fail(HCSA_EINVAL, "k_bstride too small");
-    if (k_dtype == HCSA_MXFP4 && ks_bstride < static_cast<int64_t>(N) * (d_I / 32))
+    if (mx && ks_bstride < static_cast<int64_t>(N) * (d_I / 32))
       return fail(HCSA_EINVAL, "ks_bstride too small");
   }
   return HCSA_OK;

@@ -402,13 +402,36 @@ struct IdxMxDev {
 // 32*(l/32) .. +31 of one 64-channel step, channel e in bits 4e..4e+3 (the stored packing:
 // element 2i in the low nibble of byte i); the scale operand's low byte is that block's
 // e8m0 scale; D register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+//
+// The FP8 form of the same scan (F8 = true) widens the e2m1 codes to e4m3 bytes and runs
+// the instruction with e4m3 operands and the same e8m0 scales: every e2m1 value is exact in
+// e4m3, so the products and the scores are the same, at twice the operand registers and
+// twice the matrix-core cycles [9fzt.com digest item 4: FP4 dequantized to FP8 without
+// loss; tulong.co 技术架构创新 item 2: FP4+FP8 mixed precision, equal FP4 and FP8 peaks on
+// current hardware].  Its operand layout differs (measured): registers 0..3 of lane l
+// hold 16 channels of the step's first 32-channel block, registers 4..7 16 channels of
+// the second, lane halves l/32 = 0 and 1 taking channels 0..15 and 16..31 of each block;
+// the scale operand of lane half h still scales block h.  Within a block the channel
+// order is free as long as queries and keys share it, so the even and odd channels of
+// every packed word are kept in separate registers, with no interleaving.
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+// Eight e2m1 codes (a packed word, channel 2i in the low nibble of byte i) to e4m3: the
+// magnitude (low three bits) indexes a byte table of 0, 0.5, 1, 1.5 | 2, 3, 4, 6 in e4m3
+// (a byte permute), and the sign moves from bit 3 to bit 7.  `ev` receives the even
+// channels (bytes in channel order), `od` the odd ones.
+__device__ __forceinline__ void e2m1x8_to_e4m3(uint32_t w, uint32_t& ev, uint32_t& od) {
+  constexpr uint32_t kMagLo = 0x3C383000u, kMagHi = 0x4C484440u;
+  ev = __builtin_amdgcn_perm(kMagHi, kMagLo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  od = __builtin_amdgcn_perm(kMagHi, kMagLo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+}
 
 constexpr int kMxMaxUnits = 16 * 4;   // H_I <= 16 heads x d_I / 32 <= 4 blocks
 
 // grid: (ceil(N / chunk), rows); block 256 (4 waves, 32 keys per MFMA).
-template <int HI, bool QBF16, bool SBF16, bool PAGED>
+template <int HI, bool QBF16, bool SBF16, bool PAGED, bool F8>
 __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   constexpr int U = 4;
   const int row = blockIdx.y;
@@ -463,9 +486,27 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
     const int blk = 2 * st + half;
     if (st < ksteps && col < HI && blk < nblk) {
       const int u = col * nblk + blk;
+      if constexpr (!F8) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) qa[st][d] = static_cast<int>(s_qa[u][d]);
+        for (int d = 0; d < 4; ++d) qa[st][d] = static_cast<int>(s_qa[u][d]);
+      }
       qs[st] = s_qs[u];
+    }
+    if constexpr (F8) {
+      // registers 4q..4q+3: channels 16*half .. +15 of block 2*st + q
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int bq = 2 * st + q;
+        if (st < ksteps && col < HI && bq < nblk) {
+#pragma unroll
+          for (int wd = 0; wd < 2; ++wd) {
+            uint32_t ev, od;
+            e2m1x8_to_e4m3(s_qa[col * nblk + bq][2 * half + wd], ev, od);
+            qa[st][4 * q + 2 * wd] = static_cast<int>(ev);
+            qa[st][4 * q + 2 * wd + 1] = static_cast<int>(od);
+          }
+        }
+      }
     }
   }
   float w[HI];
@@ -479,7 +520,9 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   uint16_t* s16 = static_cast<uint16_t*>(A.scores) + static_cast<int64_t>(row) * A.N;
 
   for (int j0 = start + wave * 32; j0 < end; j0 += 4 * 32 * U) {
-    i32x8 kb[U][2];
+    // packed codes as loaded: fp4 operands take them as they are (4 words per step); the
+    // FP8 form holds 8 bytes of each of the step's two blocks and widens them at the MFMA
+    u32x4 kraw[U][2];
     int ksc[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -487,28 +530,54 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
       const int64_t rj = PAGED && j < end ? row_off<true>(A.pm, 0, b, j, A.c_log2, 1) : j;   // pool row
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        kb[u][st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        kraw[u][st] = u32x4{0, 0, 0, 0};
         ksc[u][st] = 127;
         const int blk = 2 * st + half;
-        if (st < ksteps && blk < nblk && j < end) {
-          const u32x4 c = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(kbase + rj * rowb + blk * 16));
-          kb[u][st][0] = static_cast<int>(c[0]);
-          kb[u][st][1] = static_cast<int>(c[1]);
-          kb[u][st][2] = static_cast<int>(c[2]);
-          kb[u][st][3] = static_cast<int>(c[3]);
-          ksc[u][st] = sbase[rj * nblk + blk];
+        if (st < ksteps && blk < nblk && j < end) ksc[u][st] = sbase[rj * nblk + blk];
+        if constexpr (!F8) {
+          if (st < ksteps && blk < nblk && j < end)
+            kraw[u][st] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(kbase + rj * rowb + blk * 16));
+        } else {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int bq = 2 * st + q;
+            if (st < ksteps && bq < nblk && j < end) {
+              const u32x2 c = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x2*>(kbase + rj * rowb + bq * 16 + 8 * half));
+              kraw[u][st][2 * q] = c[0];
+              kraw[u][st][2 * q + 1] = c[1];
+            }
+          }
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u * 128 >= end) break;                 // wave-uniform
+      i32x8 kb[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        kb[st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (!F8) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) kb[st][d] = static_cast<int>(kraw[u][st][d]);
+        } else {
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            uint32_t ev, od;
+            e2m1x8_to_e4m3(kraw[u][st][wd], ev, od);
+            kb[st][2 * wd] = static_cast<int>(ev);
+            kb[st][2 * wd + 1] = static_cast<int>(od);
+          }
+        }
+      }
+      constexpr int kFmt = F8 ? 0 : 4;               // operand format: e4m3 or e2m1
       f32x16 d = {};
-      d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0], kb[u][0], d, 4, 4, 0, qs[0],
-                                                          0, ksc[u][0]);
+      d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0], kb[0], d, kFmt, kFmt, 0,
+                                                          qs[0], 0, ksc[u][0]);
       if (ksteps > 1)
-        d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1], kb[u][1], d, 4, 4, 0,
+        d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1], kb[1], d, kFmt, kFmt, 0,
                                                             qs[1], 0, ksc[u][1]);
       // rows (heads) held by this lane: 8*(r/4) + 4*half + r%4
       float part = 0.0f;
@@ -530,27 +599,27 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   }
 }
 
-template <int HI, bool QBF16>
+template <int HI, bool QBF16, bool F8>
 hipError_t launch_mx_mfma_hi(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
   dim3 grid(nchunks, rows);
   if (score_dtype == 1)
-    if (A.pm.table) launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true, true>, grid, dim3(256), s, A);
-    else launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true, false>, grid, dim3(256), s, A);
+    if (A.pm.table) launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true, true, F8>, grid, dim3(256), s, A);
+    else launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, true, false, F8>, grid, dim3(256), s, A);
   else
-    if (A.pm.table) launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false, true>, grid, dim3(256), s, A);
-    else launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false, false>, grid, dim3(256), s, A);
+    if (A.pm.table) launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false, true, F8>, grid, dim3(256), s, A);
+    else launch_timed(index_scores_mx_mfma_kernel<HI, QBF16, false, false, F8>, grid, dim3(256), s, A);
   return hipGetLastError();
 }
 
-template <bool QBF16>
+template <bool QBF16, bool F8>
 hipError_t launch_mx_mfma(const IdxMxDev& A, int rows, int H_I, int score_dtype, hipStream_t s) {
   switch (H_I) {
-    case 1: return launch_mx_mfma_hi<1, QBF16>(A, rows, score_dtype, s);
-    case 2: return launch_mx_mfma_hi<2, QBF16>(A, rows, score_dtype, s);
-    case 4: return launch_mx_mfma_hi<4, QBF16>(A, rows, score_dtype, s);
-    case 8: return launch_mx_mfma_hi<8, QBF16>(A, rows, score_dtype, s);
-    case 16: return launch_mx_mfma_hi<16, QBF16>(A, rows, score_dtype, s);
+    case 1: return launch_mx_mfma_hi<1, QBF16, F8>(A, rows, score_dtype, s);
+    case 2: return launch_mx_mfma_hi<2, QBF16, F8>(A, rows, score_dtype, s);
+    case 4: return launch_mx_mfma_hi<4, QBF16, F8>(A, rows, score_dtype, s);
+    case 8: return launch_mx_mfma_hi<8, QBF16, F8>(A, rows, score_dtype, s);
+    case 16: return launch_mx_mfma_hi<16, QBF16, F8>(A, rows, score_dtype, s);
   }
   return hipErrorInvalidValue;
 }
@@ -562,7 +631,7 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
                                      int64_t ks_bstride, int B, int Nq, int H_I, int d_I,
                                      int N, int ratio, int64_t pos0, const int64_t* seq_pos,
                                      const int32_t* block_table, int64_t table_stride,
-                                     int score_dtype, void* scores, hipStream_t s) {
+                                     int score_dtype, void* scores, bool fp8, hipStream_t s) {
   IdxMxDev A;
   A.q = q;
   A.w = w;
@@ -582,8 +651,12 @@ hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,
   A.scores = scores;
   // at most 2048 keys per block: more, shorter blocks shorten the grid's last round
   A.chunk = std::min(index_chunk(B * Nq, N), 2048);
-  if (q_dtype == 1) return launch_mx_mfma<true>(A, B * Nq, H_I, score_dtype, s);
-  return launch_mx_mfma<false>(A, B * Nq, H_I, score_dtype, s);
+  if (fp8) {
+    if (q_dtype == 1) return launch_mx_mfma<true, true>(A, B * Nq, H_I, score_dtype, s);
+    return launch_mx_mfma<false, true>(A, B * Nq, H_I, score_dtype, s);
+  }
+  if (q_dtype == 1) return launch_mx_mfma<true, false>(A, B * Nq, H_I, score_dtype, s);
+  return launch_mx_mfma<false, false>(A, B * Nq, H_I, score_dtype, s);
 }
 
 
@@ -593,10 +666,11 @@ hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const
                                int ratio, int64_t pos0, const int64_t* seq_pos,
                                const int32_t* block_table, int64_t table_stride,
                                int score_dtype, void* scores, hipStream_t s) {
-  if (k_dtype == 2)
+  if (k_dtype == 2 || k_dtype == 3)   // MXFP4 keys: e2m1 operands, or widened to e4m3
     return launch_mxfp4_index_scores(q, q_dtype, w, static_cast<const uint8_t*>(kx), k_bstride,
                                      ks, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos,
-                                     block_table, table_stride, score_dtype, scores, s);
+                                     block_table, table_stride, score_dtype, scores,
+                                     k_dtype == 3, s);
   IdxDev A;
   A.q = q;
   A.w = w;

@@ -15,7 +15,7 @@ if not os.path.exists(_LIB_PATH):
                       "`python long_context_attention_26_amd/build.py`")
 lib = ctypes.CDLL(_LIB_PATH)
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, MXFP4_FP8 = 0, 1, 2, 3
 OK, EINVAL, EDTYPE, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -200,12 +200,13 @@ def index_topk_workspace_size(B, Nq, N, k, score_dtype):
 
 def csa_index_topk(q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx,
                    k_scales=None, scores_out=None, workspace=None, stream=None, seq_pos=None,
-                   block_table=None):
+                   block_table=None, mx_fp8=False):
     """q_idx [B, Nq, H_I, d_I], w_idx [B, Nq, H_I] f32, k_idx [B, >=N, d_I] (F32/BF16) or
-    packed MXFP4 uint8 [B, >=N, d_I/2] with k_scales [B, >=N, d_I/32]."""
+    packed MXFP4 uint8 [B, >=N, d_I/2] with k_scales [B, >=N, d_I/32].  mx_fp8: scan MXFP4
+    keys on FP8 operands (the codes widened to e4m3) instead of FP4 ones."""
     B, Nq, H_I, d_I = q_idx.shape
     if k_idx.dtype == torch.uint8:
-        k_dt, ksb = MXFP4, k_scales.stride(0)
+        k_dt, ksb = (MXFP4_FP8 if mx_fp8 else MXFP4), k_scales.stride(0)
     else:
         k_dt, ksb = dtype_code(k_idx), 0
     if workspace is None:
@@ -221,11 +222,11 @@ def csa_index_topk(q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx
 
 
 def csa_index_scores(q_idx, w_idx, k_idx, N, ratio, pos0, scores, k_scales=None, stream=None,
-                     seq_pos=None, block_table=None):
+                     seq_pos=None, block_table=None, mx_fp8=False):
     """Indexer scores only, into scores [B*Nq, N] (F32 or BF16)."""
     B, Nq, H_I, d_I = q_idx.shape
     if k_idx.dtype == torch.uint8:
-        k_dt, ksb = MXFP4, k_scales.stride(0)
+        k_dt, ksb = (MXFP4_FP8 if mx_fp8 else MXFP4), k_scales.stride(0)
     else:
         k_dt, ksb = dtype_code(k_idx), 0
     _check(lib.hcsa_csa_index_scores(_ptr(q_idx), dtype_code(q_idx), _ptr(w_idx), _ptr(k_idx),

@@ -79,6 +79,7 @@ class DecodeStep:
         st = state
         self.st, self.Nq, self.H, self.H_I = st, Nq, H, H_I
         self.topk, self.n_win, self.scale = topk, n_win, scale
+        self.mx_fp8 = False          # MXFP4 indexer keys: scan on FP8 operands instead of FP4
         self.score_code = hcsa.BF16 if score_dtype == "bf16" else hcsa.F32
         B, d, dev = st.B, st.d, st.device
         self.idx = torch.empty(B, Nq, topk, dtype=torch.int32, device=dev)
@@ -102,7 +103,7 @@ class DecodeStep:
         """Indexer scores of every visible compressed entry (one kernel)."""
         st = self.st
         hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, self.scores,
-                              k_scales=st.Ics, stream=stream)
+                              k_scales=st.Ics, stream=stream, mx_fp8=self.mx_fp8)
 
     def run_select_attend(self, q, pos0, stream=None):
         st = self.st
@@ -128,7 +129,7 @@ class DecodeStep:
         scores = self.scores if scores_out is None else scores_out
         mark("index_scores")
         hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, scores,
-                              k_scales=st.Ics, stream=stream)
+                              k_scales=st.Ics, stream=stream, mx_fp8=self.mx_fp8)
         mark("topk")
         hcsa.topk(scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
                   workspace=self.ws_topk, stream=stream)

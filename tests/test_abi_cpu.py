@@ -50,6 +50,7 @@ def test_compress_validation(H):
     assert call(x_dtype=7) == H.EDTYPE
     assert call(y_dtype=H.MXFP4, D=40) == H.EINVAL
     assert call(y_dtype=H.MXFP4) == H.EINVAL           # no scales pointer
+    assert call(y_dtype=H.MXFP4_FP8) == H.EDTYPE       # an indexer key type only
     assert call(x=None) == H.EINVAL
     assert call(x=MIS) == H.EALIGN
     assert call(B=2, x_bstride=10) == H.EINVAL
@@ -88,6 +89,8 @@ def test_index_topk_validation(H):
     assert call(d_I=48) == H.EINVAL
     assert call(q_dt=H.BF16) == H.EDTYPE
     assert call(k_dt=H.MXFP4, q_dt=H.BF16) == H.EINVAL   # no scales
+    assert call(k_dt=H.MXFP4_FP8, q_dt=H.BF16) == H.EINVAL   # MXFP4 storage: no scales
+    assert call(k_dt=4, q_dt=H.BF16) == H.EDTYPE
     assert call(k_dt=H.F32, d_I=128) == H.EINVAL
 
 
@@ -102,6 +105,7 @@ def test_attention_validation(H):
     assert csa(H_=65) == H.EINVAL
     assert csa(d=12) == H.EINVAL
     assert csa(kdt=H.MXFP4) == H.EDTYPE
+    assert csa(kdt=H.MXFP4_FP8) == H.EDTYPE
     assert csa(raw_pos0=4000) == H.EINVAL                # window starts before the raw rows
     assert csa(T_raw=100, raw_pos0=3900, pos0=4095) == H.EINVAL  # window ends after them
     assert csa(k=5000) == H.EINVAL
