@@ -63,18 +63,29 @@ extern "C" {
 typedef void *hcsa_stream; /* hipStream_t */
 
 /*
- * Paged caches [the heterogeneous KV cache in 128-token blocks, lcm(m, m') = lcm(4, 128):
- * Lighthouse section 八 item 7].  Positions [128*blk, 128*blk + 128) of sequence b live in
- * page block_table[b*table_stride + blk] of every cache tensor.  A tensor pooled at ratio r
- * (r divides 128) holds 128/r rows per page: its pointer is then a page pool
- * [pages][128/r][row] (raw tokens: 128 rows per page, CSA entries and indexer keys 32, HCA
- * entries 1) and its bstride argument is ignored.  The table is device memory (int32,
- * 4-byte aligned), must cover every block holding a position a call touches, and is not
- * validated on the host.
+ * Cache layout [the heterogeneous KV cache: paged compressed caches in 128-token blocks,
+ * lcm(m, m') = lcm(4, 128), and a fixed-size state cache for the sliding window and the
+ * tokens not yet pooled: Lighthouse section 八 item 7].
+ *
+ * block_table (NULL: caches contiguous, bstride arguments apply): positions
+ * [128*blk, 128*blk + 128) of sequence b live in page block_table[b*table_stride + blk] of
+ * every cache tensor.  A tensor pooled at ratio r (r divides 128) holds 128/r rows per page:
+ * its pointer is then a page pool [pages][128/r][row] (raw tokens: 128 rows per page, CSA
+ * entries and indexer keys 32, HCA entries 1) and its bstride argument is ignored.  The table
+ * is device memory (int32, 4-byte aligned), must cover every block holding a position a call
+ * touches, and is not validated on the host.
+ *
+ * raw_ring (0: raw tokens laid out like the caches): a power of two in [128, 2^30].  Raw
+ * tokens (x of the pooling jobs, k_raw/v_raw of CSA attention) are then a ring of raw_ring
+ * rows per sequence, [B][raw_ring][row] with the call's raw bstride: position t sits in row
+ * t mod raw_ring.  The caller keeps the last raw_ring tokens of every sequence there; a call
+ * may touch only those (a decode step needs the window and the tokens since the last
+ * completed 128-token block).
  */
 typedef struct hcsa_pages {
   const int32_t *block_table;
   int64_t table_stride;
+  int64_t raw_ring;
 } hcsa_pages;
 
 /*
@@ -131,9 +142,12 @@ int hcsa_compress_kv(const void *x, int x_dtype, int64_t x_bstride, int B, int T
  * indexer-key blocks and the HCA K and V blocks that one decode token completes).  Each job
  * has the meaning and limits of hcsa_compress_kv (x has its own T; jobs share B).  The
  * call validates every job first and launches nothing if any is invalid.  Outputs of
- * different jobs must not overlap.  With pages, x and y (and y_scales) are page pools,
- * ratio divides 128, and a job pools the tokens [pos0, pos0 + T) of every sequence into
- * its entries pos0/ratio .. (pos0 + T)/ratio - 1 (pos0 a multiple of ratio).
+ * different jobs must not overlap.  With a block table, x and y (and y_scales) are page
+ * pools, ratio divides 128, and a job pools the tokens [pos0, pos0 + T) of every sequence
+ * into its entries pos0/ratio .. (pos0 + T)/ratio - 1 (pos0 a multiple of ratio).  With a
+ * raw-token ring, x is the ring (x_bstride apart, raw_ring rows per sequence), ratio divides
+ * 128, T <= raw_ring and the job pools the tokens [pos0, pos0 + T) from it, into y's rows
+ * from the first (contiguous y) or into the pages of those entries (paged y).
  */
 #define HCSA_MAX_POOL_JOBS 8
 typedef struct hcsa_pool_job {
@@ -148,7 +162,7 @@ typedef struct hcsa_pool_job {
   int64_t y_bstride;
   uint8_t *y_scales;
   int64_t ys_bstride;
-  int64_t pos0;        /* paged form only: position of x's first token (a multiple of ratio) */
+  int64_t pos0;        /* paged or ring form: position of the first token (a multiple of ratio) */
 } hcsa_pool_job;
 int hcsa_compress_kv_batched(const hcsa_pool_job *jobs, int n_jobs, int B,
                              const hcsa_pages *pages, hcsa_stream stream);
@@ -230,7 +244,9 @@ int hcsa_csa_index_scores(const void *q_idx, int q_dtype, const float *w_idx,
  * k_raw, v_raw [B][T_raw][d] (raw_bstride elements); row t holds position raw_pos0 + t.
  *         Every window position of every query must lie in [raw_pos0, raw_pos0 + T_raw)
  *         (checked on the host when seq_pos and pages are NULL; the caller's guarantee
- *         otherwise).  With pages, k_raw/v_raw are raw-token page pools and raw_pos0 is 0.
+ *         otherwise).  With a block table, k_raw/v_raw are raw-token page pools and
+ *         raw_pos0 is 0.  With a raw-token ring, they are the ring (T_raw == raw_ring,
+ *         raw_pos0 == 0, n_win + Nq - 1 <= raw_ring) holding every window position.
  * out     [B][Nq][H][d] F32, lse [B][Nq][H] F32 (natural log; -inf and o = 0 when no key).
  * kv_dtype F32 or BF16 (q has the same dtype).  ratio is the CSA pooling ratio.
  * Limits: 1 <= H <= 64, d % 8 == 0, 8 <= d <= 256, H*d <= 4096, 0 <= k <= 4096,

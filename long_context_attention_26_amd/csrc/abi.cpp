@@ -68,11 +68,16 @@ int check_attn_common(const void* q, int kv_dtype, int B, int Nq, int H, int d, 
   return HCSA_OK;
 }
 
-// Paged caches: a block table (device int32, 4-byte aligned) and its row stride, or null;
-// every pooling ratio of the call must divide the 128-token page.
+// Cache layout: a block table (device int32, 4-byte aligned) and its row stride, or none
+// (contiguous caches); every pooling ratio of a paged call must divide the 128-token page.
+// raw_ring: 0, or a power of two in [128, 2^30] (raw tokens in a ring of that many rows).
 int check_pages(const hcsa_pages* pages, std::initializer_list<int> ratios) {
   if (!pages) return HCSA_OK;
-  if (!pages->block_table) return fail(HCSA_EINVAL, "pages->block_table must be non-null");
+  if (pages->raw_ring != 0 &&
+      (pages->raw_ring < 128 || pages->raw_ring > (1LL << 30) ||
+       !is_pow2(static_cast<int>(pages->raw_ring))))
+    return fail(HCSA_EINVAL, "pages->raw_ring must be 0 or a power of two in [128, 2^30]");
+  if (!pages->block_table) return HCSA_OK;
   if (reinterpret_cast<uintptr_t>(pages->block_table) % 4 != 0)
     return fail(HCSA_EALIGN, "pages->block_table must be 4-byte aligned");
   if (pages->table_stride < 1) return fail(HCSA_EINVAL, "pages->table_stride must be >= 1");
@@ -82,6 +87,8 @@ int check_pages(const hcsa_pages* pages, std::initializer_list<int> ratios) {
 }
 const int32_t* page_table(const hcsa_pages* pages) { return pages ? pages->block_table : nullptr; }
 int64_t page_stride(const hcsa_pages* pages) { return pages ? pages->table_stride : 0; }
+bool is_paged(const hcsa_pages* pages) { return pages && pages->block_table; }
+int64_t raw_ring(const hcsa_pages* pages) { return pages ? pages->raw_ring : 0; }
 
 }  // namespace
 
@@ -98,14 +105,15 @@ int hcsa_time_next_indexer(void* start_event, void* stop_event) {
 
 const char* hcsa_last_error(void) { return g_err.c_str(); }
 
-static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
-                          const float* omega, int ratio, void* y, int y_dtype,
-                          int64_t y_bstride, uint8_t* y_scales, int64_t ys_bstride);
+static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int T, int64_t x_rows,
+                          int Bx, int By, int D, const float* omega, int ratio, void* y,
+                          int y_dtype, int64_t y_bstride, uint8_t* y_scales,
+                          int64_t ys_bstride);
 
 int hcsa_compress_kv(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
                      const float* omega, int ratio, void* y, int y_dtype, int64_t y_bstride,
                      uint8_t* y_scales, int64_t ys_bstride, hcsa_stream stream) {
-  const int rc = check_compress(x, x_dtype, x_bstride, B, T, D, omega, ratio, y, y_dtype,
+  const int rc = check_compress(x, x_dtype, x_bstride, T, T, B, B, D, omega, ratio, y, y_dtype,
                                 y_bstride, y_scales, ys_bstride);
   if (rc) return rc;
   if (T / ratio == 0) return ok();
@@ -122,27 +130,40 @@ int hcsa_compress_kv_batched(const hcsa_pool_job* jobs, int n_jobs, int B,
   if (n_jobs > 0 && !jobs) return fail(HCSA_EINVAL, "jobs must be non-null");
   int rc = check_pages(pages, {});
   if (rc) return rc;
+  const bool paged = is_paged(pages);
+  const int64_t ring = raw_ring(pages);
   for (int i = 0; i < n_jobs; ++i) {
     const hcsa_pool_job& q = jobs[i];
-    // paged: the strides are unused (checked as for one sequence)
-    rc = check_compress(q.x, q.x_dtype, q.x_bstride, pages ? 1 : B, q.T, q.D, q.omega, q.ratio,
+    // strides of page pools are unused; a ring's sequences are x_bstride apart and hold
+    // `ring` rows each
+    rc = check_compress(q.x, q.x_dtype, q.x_bstride, q.T, ring ? ring : q.T,
+                        ring || !paged ? B : 1, paged ? 1 : B, q.D, q.omega, q.ratio,
                         q.y, q.y_dtype, q.y_bstride, q.y_scales, q.ys_bstride);
-    if (!rc && pages) {
+    if (!rc && (paged || ring)) {
       rc = check_pages(pages, {q.ratio});
+      if (!rc && (q.ratio > 128 || 128 % q.ratio != 0))
+        rc = fail(HCSA_EINVAL, "ratio must divide 128");
       if (!rc && (q.pos0 < 0 || q.pos0 % q.ratio != 0))
         rc = fail(HCSA_EINVAL, "pos0 must be a non-negative multiple of ratio");
+      if (!rc && ring && q.T > ring)
+        rc = fail(HCSA_EINVAL, "T (%d) exceeds the raw-token ring (%lld rows)", q.T,
+                  static_cast<long long>(ring));
     }
     if (rc) return fail(rc, "job %d: %s", i, g_err.c_str());
   }
   return hip_status(hcsa::launch_compress_batched(jobs, n_jobs, B, page_table(pages),
-                                                  page_stride(pages),
+                                                  page_stride(pages), ring,
                                                   static_cast<hipStream_t>(stream)),
                     "hcsa_compress_kv_batched");
 }
 
-static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
-                          const float* omega, int ratio, void* y, int y_dtype,
-                          int64_t y_bstride, uint8_t* y_scales, int64_t ys_bstride) {
+// x holds x_rows rows per sequence (x_bstride apart, checked when Bx > 1); y's sequences
+// are y_bstride apart (checked when By > 1).
+static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int T, int64_t x_rows,
+                          int Bx, int By, int D, const float* omega, int ratio, void* y,
+                          int y_dtype, int64_t y_bstride, uint8_t* y_scales,
+                          int64_t ys_bstride) {
+  const int B = Bx > By ? Bx : By;
   if (x_dtype != HCSA_F32 && x_dtype != HCSA_BF16)
     return fail(HCSA_EDTYPE, "x_dtype must be F32 or BF16");
   if (y_dtype != HCSA_F32 && y_dtype != HCSA_BF16 && y_dtype != HCSA_MXFP4)
@@ -155,8 +176,8 @@ static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int B, 
   if (!x || !y || !omega) return fail(HCSA_EINVAL, "x, omega and y must be non-null");
   if (y_dtype == HCSA_MXFP4 && !y_scales) return fail(HCSA_EINVAL, "MXFP4 output needs y_scales");
   const int n_out = T / ratio;
-  if (B > 1) {
-    if (x_bstride < static_cast<int64_t>(T) * D) return fail(HCSA_EINVAL, "x_bstride < T*D");
+  if (Bx > 1 && x_bstride < x_rows * D) return fail(HCSA_EINVAL, "x_bstride < rows*D");
+  if (By > 1) {
     const int64_t yrow = y_dtype == HCSA_MXFP4 ? D / 2 : D;
     if (y_bstride < static_cast<int64_t>(n_out) * yrow) return fail(HCSA_EINVAL, "y_bstride too small");
     if (y_dtype == HCSA_MXFP4 && ys_bstride < static_cast<int64_t>(n_out) * (D / 32))
@@ -282,7 +303,7 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
   rc = check_pages(pages, {ratio});
   if (rc) return rc;
   rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
-                        B, Nq, H_I, d_I, N, pages != nullptr);
+                        B, Nq, H_I, d_I, N, is_paged(pages));
   if (rc) return rc;
   if (!scores) return fail(HCSA_EINVAL, "scores must be non-null");
   if (!aligned16(scores)) return fail(HCSA_EALIGN, "scores must be 16-byte aligned");
@@ -307,7 +328,7 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   rc = check_pages(pages, {ratio});
   if (rc) return rc;
   rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
-                        B, Nq, H_I, d_I, N, pages != nullptr);
+                        B, Nq, H_I, d_I, N, is_paged(pages));
   if (rc) return rc;
   if (!topk_idx) return fail(HCSA_EINVAL, "topk_idx must be non-null");
   if (!aligned16(topk_idx) || (scores_out && !aligned16(scores_out)))
@@ -351,8 +372,10 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
   if (rc) return rc;
   rc = check_pages(pages, {ratio});
   if (rc) return rc;
-  if (pages && raw_pos0 != 0) return fail(HCSA_EINVAL, "paged raw tokens need raw_pos0 == 0");
-  const bool paged = pages != nullptr;
+  const bool paged = is_paged(pages);
+  const int64_t ring = raw_ring(pages);
+  if ((paged || ring) && raw_pos0 != 0)
+    return fail(HCSA_EINVAL, "paged or ring raw tokens need raw_pos0 == 0");
   if (k < 0 || k > 4096) return fail(HCSA_EINVAL, "k must be in [0, 4096]");
   if (n_win < 0 || n_win > 4096) return fail(HCSA_EINVAL, "n_win must be in [0, 4096]");
   if (k > 0) {
@@ -367,12 +390,17 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
     if (!aligned16(k_raw) || !aligned16(v_raw)) return fail(HCSA_EALIGN, "k_raw and v_raw alignment");
     if ((raw_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "raw_bstride alignment");
     if (T_raw < 1) return fail(HCSA_EINVAL, "T_raw must be >= 1");
-    if (!paged && B > 1 && raw_bstride < T_raw * d) return fail(HCSA_EINVAL, "raw_bstride < T_raw*d");
-    // (with per-sequence positions, which sit in device memory, or paged raw tokens, the
-    // caller guarantees it)
+    if (ring && T_raw != ring) return fail(HCSA_EINVAL, "a raw-token ring needs T_raw == raw_ring");
+    // a chunk's windows span n_win + Nq - 1 positions, all of which the ring must hold
+    if (ring && n_win + static_cast<int64_t>(Nq) - 1 > ring)
+      return fail(HCSA_EINVAL, "n_win + Nq - 1 exceeds the raw-token ring");
+    if ((ring || !paged) && B > 1 && raw_bstride < T_raw * d)
+      return fail(HCSA_EINVAL, "raw_bstride < T_raw*d");
+    // (with per-sequence positions, which sit in device memory, paged raw tokens or a
+    // ring, the caller guarantees it)
     const int64_t first = pos0 - n_win + 1 > 0 ? pos0 - n_win + 1 : 0;
     const int64_t last = pos0 + Nq - 1;
-    if (!seq_pos && !paged && (first < raw_pos0 || last >= raw_pos0 + T_raw))
+    if (!seq_pos && !paged && !ring && (first < raw_pos0 || last >= raw_pos0 + T_raw))
       return fail(HCSA_EINVAL, "window positions [%lld, %lld] not inside the raw rows [%lld, %lld)",
                   static_cast<long long>(first), static_cast<long long>(last),
                   static_cast<long long>(raw_pos0), static_cast<long long>(raw_pos0 + T_raw));
@@ -385,7 +413,7 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
   a.q = q; a.kc = kc; a.vc = vc; a.c_bstride = c_bstride; a.N = N > 0 ? N : 0; a.ratio = ratio;
   a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
   a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0; a.seq_pos = seq_pos;
-  a.block_table = page_table(pages); a.table_stride = page_stride(pages);
+  a.block_table = page_table(pages); a.table_stride = page_stride(pages); a.raw_ring = ring;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
   a.out = out; a.lse = lse;
   return hip_status(hcsa::launch_attention(true, a, plan, workspace, static_cast<hipStream_t>(stream)),
@@ -415,7 +443,8 @@ int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h
     if (!kh || !vh) return fail(HCSA_EINVAL, "kh and vh must be non-null");
     if (!aligned16(kh) || !aligned16(vh)) return fail(HCSA_EALIGN, "kh and vh must be 16-byte aligned");
     if ((h_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "h_bstride alignment");
-    if (!pages && B > 1 && h_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "h_bstride < N*d");
+    if (!is_paged(pages) && B > 1 && h_bstride < static_cast<int64_t>(N) * d)
+      return fail(HCSA_EINVAL, "h_bstride < N*d");
   }
   const hcsa::AttnPlan plan = hcsa::plan_attention(false, kv_dtype, B, Nq, H, d, N);
   rc = check_ws(workspace, ws_bytes, plan.total_bytes);

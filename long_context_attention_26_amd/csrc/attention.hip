@@ -53,6 +53,7 @@ struct AttnDev {
   const int64_t* seq_pos;   // [B] or null
   PageMap pm;               // paged caches (table null: contiguous)
   int c_log2;               // log2 of the compressed cache's rows per page
+  int64_t raw_ring;         // 0, or raw tokens in a ring of raw_ring (a power of two) rows
   int Nq, H, d;
   float scale;
   int chunk, splits, rows;
@@ -110,7 +111,10 @@ __device__ __forceinline__ const TE* key_row(const AttnDev& A, int b, int code, 
     return base + b * A.c_bstride + static_cast<int64_t>(code) * A.d;
   }
   const TE* base = static_cast<const TE*>(value ? A.v_raw : A.k_raw);
-  // raw rows: one per token, 128 per page, at position raw_pos0 + row
+  // raw rows: one per token at position raw_pos0 + row; in a ring, position t sits in row
+  // t mod raw_ring; paged, 128 per page
+  if (A.raw_ring)
+    return base + b * A.raw_bstride + ((-code - 2) & (A.raw_ring - 1)) * A.d;
   if (A.pm.table) return base + row_off<true>(A.pm, 0, b, A.raw_pos0 + (-code - 2), 7, A.d);
   return base + b * A.raw_bstride + static_cast<int64_t>(-code - 2) * A.d;
 }
@@ -775,6 +779,7 @@ hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, v
   A.seq_pos = a.seq_pos;
   A.pm.table = a.block_table;
   A.pm.stride = a.table_stride;
+  A.raw_ring = a.raw_ring;
   A.c_log2 = 0;
   for (int per = kPageTokens / a.ratio; per > 1; per >>= 1) ++A.c_log2;
   A.Nq = a.Nq;

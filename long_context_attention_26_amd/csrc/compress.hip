@@ -99,6 +99,17 @@ __device__ __forceinline__ void paged_rows(const PageMap& pm, int b, int64_t pos
   yrow = row_off<true>(pm, 0, b, pos0 / r + j, __builtin_ctz(kPageTokens / r), 1);
 }
 
+// Element offset of entry j's first source token: a ring of `ring` rows per sequence
+// (position t in row t mod ring; r divides 128 and the ring is a power of two >= 128, so an
+// entry's r rows never wrap), a page pool (xrow from paged_rows), or rows from the job's
+// first token.
+template <bool PAGED>
+__device__ __forceinline__ int64_t src_off(int64_t ring, int64_t x_bs, int D, int b,
+                                           int64_t pos0, int r, int64_t j, int64_t xrow) {
+  if (ring) return b * x_bs + ((pos0 + j * r) & (ring - 1)) * D;
+  return PAGED ? xrow * D : b * x_bs + j * r * D;
+}
+
 // One block of the pooling: this thread's 8 channels of entry `j` (block-local row `local`).
 template <bool IN_BF16, int OUT, bool PAGED = false>
 __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_bs, int D,
@@ -106,7 +117,7 @@ __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_
                                           int64_t y_bs, uint8_t* __restrict__ ys, int64_t ys_bs,
                                           int n_out, int64_t jblock, int b,
                                           const PageMap& pm = PageMap{nullptr, 0},
-                                          int64_t pos0 = 0) {
+                                          int64_t pos0 = 0, int64_t ring = 0) {
   const int tpr = D >> 3;                       // threads per output row
   const int rows_per_block = blockDim.x / tpr;
   const int local = threadIdx.x / tpr;
@@ -118,7 +129,7 @@ __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_
   int64_t xrow = 0, yrow = 0;
   if constexpr (PAGED) paged_rows(pm, b, pos0, r, j, xrow, yrow);
   const char* src = static_cast<const char*>(x) +
-                    ((PAGED ? xrow * D : b * x_bs + j * r * D) + c8 * 8) * ES;
+                    (src_off<PAGED>(ring, x_bs, D, b, pos0, r, j, xrow) + c8 * 8) * ES;
   const int64_t row_bytes = static_cast<int64_t>(D) * ES;
 
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -150,7 +161,7 @@ __device__ __forceinline__ void pool_rows_wide(const void* __restrict__ x, int64
                                                int64_t y_bs, uint8_t* __restrict__ ys,
                                                int64_t ys_bs, int64_t j, int b, float* s_part,
                                                const PageMap& pm = PageMap{nullptr, 0},
-                                               int64_t pos0 = 0) {
+                                               int64_t pos0 = 0, int64_t ring = 0) {
   const int tpr = D >> 3;
   const int G = blockDim.x / tpr;
   const int g = threadIdx.x / tpr;
@@ -161,7 +172,7 @@ __device__ __forceinline__ void pool_rows_wide(const void* __restrict__ x, int64
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (g < G) {
     const char* src = static_cast<const char*>(x) +
-                      ((PAGED ? xrow * D : b * x_bs + j * r * D) + c8 * 8) * ES;
+                      (src_off<PAGED>(ring, x_bs, D, b, pos0, r, j, xrow) + c8 * 8) * ES;
     const int64_t row_bytes = static_cast<int64_t>(D) * ES;
 #pragma unroll 8
     for (int i = g; i < r; i += G) {
@@ -223,19 +234,21 @@ struct PoolJobs {
   int first_block[HCSA_MAX_POOL_JOBS + 1];
   int n;
   PageMap pm;        // paged caches (table null: contiguous)
+  int64_t ring;      // 0, or raw tokens (every job's x) in a ring of this many rows
 };
 
 template <bool IN_BF16, int OUT, bool PAGED>
 __device__ __forceinline__ void pool_job_blocks(const hcsa_pool_job& q, const PageMap& pm,
-                                                const float* alpha, int64_t jb, int n_out,
-                                                float* s_part) {
+                                                int64_t ring, const float* alpha, int64_t jb,
+                                                int n_out, float* s_part) {
   if (q.ratio >= kWideRatio)
     pool_rows_wide<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y,
                                         q.y_bstride, q.y_scales, q.ys_bstride, jb, blockIdx.y,
-                                        s_part, pm, q.pos0);
+                                        s_part, pm, q.pos0, ring);
   else
     pool_rows<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride,
-                                   q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y, pm, q.pos0);
+                                   q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y, pm, q.pos0,
+                                   ring);
 }
 
 template <bool PAGED>
@@ -250,21 +263,23 @@ __global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
   const int n_out = q.T / q.ratio;
   const bool ib = q.x_dtype == 1;
   const PageMap& pm = J.pm;
-  if (ib && q.y_dtype == 1) pool_job_blocks<true, OUT_BF16, PAGED>(q, pm, alpha, jb, n_out, s_part);
-  else if (ib && q.y_dtype == 2) pool_job_blocks<true, OUT_MXFP4, PAGED>(q, pm, alpha, jb, n_out, s_part);
-  else if (ib) pool_job_blocks<true, OUT_F32, PAGED>(q, pm, alpha, jb, n_out, s_part);
-  else if (q.y_dtype == 1) pool_job_blocks<false, OUT_BF16, PAGED>(q, pm, alpha, jb, n_out, s_part);
-  else if (q.y_dtype == 2) pool_job_blocks<false, OUT_MXFP4, PAGED>(q, pm, alpha, jb, n_out, s_part);
-  else pool_job_blocks<false, OUT_F32, PAGED>(q, pm, alpha, jb, n_out, s_part);
+  const int64_t rg = J.ring;
+  if (ib && q.y_dtype == 1) pool_job_blocks<true, OUT_BF16, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
+  else if (ib && q.y_dtype == 2) pool_job_blocks<true, OUT_MXFP4, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
+  else if (ib) pool_job_blocks<true, OUT_F32, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
+  else if (q.y_dtype == 1) pool_job_blocks<false, OUT_BF16, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
+  else if (q.y_dtype == 2) pool_job_blocks<false, OUT_MXFP4, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
+  else pool_job_blocks<false, OUT_F32, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
 }
 
 hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B,
                                    const int32_t* block_table, int64_t table_stride,
-                                   hipStream_t s) {
+                                   int64_t raw_ring, hipStream_t s) {
   PoolJobs J{};
   J.n = 0;
   J.pm.table = block_table;
   J.pm.stride = table_stride;
+  J.ring = raw_ring;
   int blocks = 0;
   for (int i = 0; i < n; ++i) {
     const int n_out = jobs[i].T / jobs[i].ratio;

@@ -15,7 +15,7 @@ hipError_t launch_compress(const void* x, int x_dtype, int64_t x_bstride, int B,
                            int64_t y_bstride, uint8_t* ys, int64_t ys_bstride,
                            hipStream_t s);
 hipError_t launch_compress_batched(const struct hcsa_pool_job* jobs, int n, int B,
-                                   const int32_t* block_table, int64_t table_stride,
+                                   const int32_t* block_table, int64_t table_stride, int64_t raw_ring,
                                    hipStream_t s);
 hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int D,
                                  uint8_t* packed, uint8_t* scales, hipStream_t s);
@@ -61,6 +61,7 @@ struct AttnArgs {
   const int64_t* seq_pos;  // [B] or null: query i of sequence b at seq_pos[b] + i
   const int32_t* block_table;   // paged caches [B][table_stride], or null (contiguous)
   int64_t table_stride;
+  int64_t raw_ring;        // 0, or raw tokens in a ring of raw_ring rows (position t at t & (raw_ring-1))
   int kv_dtype, B, Nq, H, d;
   float scale;
   float* out;

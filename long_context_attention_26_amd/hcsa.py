@@ -54,17 +54,21 @@ class PoolJob(ctypes.Structure):
 
 class Pages(ctypes.Structure):
     """Mirror of struct hcsa_pages."""
-    _fields_ = [("block_table", _p), ("table_stride", _i64)]
+    _fields_ = [("block_table", _p), ("table_stride", _i64), ("raw_ring", _i64)]
 
 
-def _pages(table):
-    """hcsa_pages for a block table (int32 [B, max_blocks] device tensor), or None."""
-    if table is None:
+def _pages(table, raw_ring=0):
+    """hcsa_pages for a block table (int32 [B, max_blocks] device tensor) and/or a raw-token
+    ring of raw_ring rows, or None for contiguous caches."""
+    if table is None and not raw_ring:
         return None
-    if table.dtype != torch.int32 or table.dim() != 2 or table.stride(1) != 1:
+    if table is not None and (table.dtype != torch.int32 or table.dim() != 2
+                              or table.stride(1) != 1):
         raise ValueError("the block table must be an int32 [B, max_blocks] tensor with unit "
                          "column stride")
-    return ctypes.byref(Pages(table.data_ptr(), table.stride(0)))
+    if table is None:
+        return ctypes.byref(Pages(None, 0, raw_ring))
+    return ctypes.byref(Pages(table.data_ptr(), table.stride(0), raw_ring))
 
 
 for _name, (_res, _args) in _SIGS.items():
@@ -161,12 +165,13 @@ def pool_job(x, omega, ratio, y, y_scales=None, T=None, pos0=0):
                    y.stride(0), _ptr(y_scales), ysb, pos0)
 
 
-def compress_kv_batched(jobs, B, stream=None, block_table=None):
+def compress_kv_batched(jobs, B, stream=None, block_table=None, raw_ring=0):
     """Run up to MAX_POOL_JOBS pooling jobs (from pool_job) of one batch in one launch;
-    block_table (int32 [B, max_blocks]) selects the paged form."""
+    block_table (int32 [B, max_blocks]) selects paged caches, raw_ring > 0 raw tokens (the
+    jobs' x) in a ring of that many rows per sequence."""
     arr = (PoolJob * max(1, len(jobs)))(*jobs)
-    _check(lib.hcsa_compress_kv_batched(ctypes.cast(arr, _p), len(jobs), B, _pages(block_table),
-                                        _stream(stream)))
+    _check(lib.hcsa_compress_kv_batched(ctypes.cast(arr, _p), len(jobs), B,
+                                        _pages(block_table, raw_ring), _stream(stream)))
 
 
 def mxfp4_quantize(x, packed, scales, stream=None):
@@ -242,8 +247,10 @@ def csa_attn_workspace_size(B, Nq, H, d, k, n_win):
 
 
 def csa_sparse_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio, pos0, scale,
-                    out, lse, workspace=None, stream=None, seq_pos=None, block_table=None):
-    """q [B, Nq, H, d]; kc, vc [B, >=N, d]; topk_idx [B, Nq, k]; k_raw, v_raw [B, T_raw, d]."""
+                    out, lse, workspace=None, stream=None, seq_pos=None, block_table=None,
+                    raw_ring=0):
+    """q [B, Nq, H, d]; kc, vc [B, >=N, d]; topk_idx [B, Nq, k]; k_raw, v_raw [B, T_raw, d]
+    (with raw_ring > 0: rings [B, raw_ring, d], position t in row t % raw_ring)."""
     B, Nq, H, d = q.shape
     k = topk_idx.shape[-1]
     if workspace is None:
@@ -251,7 +258,7 @@ def csa_sparse_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio
     _check(lib.hcsa_csa_sparse_attn(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N,
                                     _ptr(topk_idx), k, _ptr(k_raw), _ptr(v_raw),
                                     k_raw.stride(0), k_raw.shape[1], raw_pos0, n_win, ratio,
-                                    pos0, _pos_ptr(seq_pos, B), _pages(block_table),
+                                    pos0, _pos_ptr(seq_pos, B), _pages(block_table, raw_ring),
                                     dtype_code(q), B, Nq, H, d, scale, _ptr(out),
                                     _ptr(lse), _ptr(workspace), workspace.numel(),
                                     _stream(stream)))

@@ -124,6 +124,38 @@ def test_attention_validation(H):
                                  16, 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
 
 
+def test_raw_ring_validation(H):
+    """Raw tokens in a ring: a power of two >= 128 rows; CSA attention needs T_raw equal to
+    it, raw_pos0 0 and every chunk window inside it; pooling jobs need T within it."""
+    L = H.lib
+    ring = lambda r, table=None, stride=0: ctypes.byref(H.Pages(table, stride, r))
+    ws = L.hcsa_csa_sparse_attn_workspace_size(2, 1, 16, 128, 64, 128)
+
+    def csa(pages, T_raw=256, raw_pos0=0, n_win=128, Nq=1, raw_bstride=256 * 128, B=2):
+        return L.hcsa_csa_sparse_attn(FAKE, FAKE, FAKE, 1024 * 128, 1024, FAKE, 64, FAKE, FAKE,
+                                      raw_bstride, T_raw, raw_pos0, n_win, 4, 4095, None, pages,
+                                      H.BF16, B, Nq, 16, 128, 0.1, FAKE, FAKE, FAKE, ws, None)
+    assert csa(ring(100)) == H.EINVAL                    # not a power of two
+    assert csa(ring(64)) == H.EINVAL                     # below 128 rows
+    assert csa(ring(256), T_raw=512) == H.EINVAL         # T_raw must be the ring size
+    assert csa(ring(256), raw_pos0=7) == H.EINVAL
+    assert csa(ring(128), T_raw=128, n_win=128, Nq=2, raw_bstride=128 * 128) == H.EINVAL
+    assert csa(ring(256), raw_bstride=100 * 128) == H.EINVAL   # sequences overlap
+
+    def job(T, ratio=4, x_bstride=256 * 64, pos0=0):
+        return H.PoolJob(FAKE, H.BF16, x_bstride, T, 64, FAKE, ratio, FAKE, H.BF16, 1 << 20,
+                         None, 0, pos0)
+
+    def pool(j, pages, B=2):
+        arr = (H.PoolJob * 1)(j)
+        return L.hcsa_compress_kv_batched(ctypes.cast(arr, ctypes.c_void_p), 1, B, pages, None)
+    assert pool(job(300), ring(256)) == H.EINVAL                 # more tokens than the ring
+    assert pool(job(12, ratio=3), ring(256)) == H.EINVAL         # ratio must divide 128
+    assert pool(job(8, pos0=6), ring(256)) == H.EINVAL           # pos0 not on an entry
+    assert pool(job(8, x_bstride=100 * 64), ring(256)) == H.EINVAL   # ring rows overlap
+    assert b"x_bstride" in L.hcsa_last_error()
+
+
 def test_workspace_sizes_are_monotone(H):
     L = H.lib
     a = L.hcsa_topk_workspace_size(H.F32, 1, 1, 1000, 10)
