@@ -38,6 +38,11 @@ readings taken here (each is marked READING in the function that uses it):
   R7  MXFP4 (OCP Microscaling v1.0, e2m1 elements, e8m0 scale per 32 elements): scale
       exponent floor(log2(amax)) - 2, element = round-to-nearest-even of v / 2^e onto the
       e2m1 grid, saturating at +-6; amax = 0 gives exponent -127 and zero elements.
+  R8  training (the sparse attention is trained from the 64K stage of the length
+      curriculum [LH 八.2]): the gradients are those of the forward functions above, the
+      exact derivative of softmax attention and of the pooled sum; the selection (top-k)
+      is held fixed (not differentiated) and a rounding to the storage type passes the
+      gradient unchanged.
 """
 
 import math
@@ -302,3 +307,79 @@ def softmax_weights(q, keys, scale):
 def log2_floor(x):
     """floor(log2 x) for x > 0, exactly."""
     return math.frexp(x)[1] - 1
+
+
+# --------------------------------------------------------------------------- backward (READING R8)
+
+def attend_backward(q, keys, values, scale, dout, dlse=None):
+    """Gradients of attend(q, keys, values, scale) for the loss sum(dout * o) +
+    sum(dlse * lse): returns (dq [H, d], dkeys [L, d], dvalues [L, d]).  With the
+    probabilities P = softmax(scale q k^T) of each head: dvalues = P^T dout,
+    dS = P (dout v^T - rowsum(dout * o) + dlse), dq = scale dS keys, dkeys = scale dS^T q.
+    An empty key list gives dq = 0."""
+    q = np.asarray(q, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    H, d = q.shape
+    if keys.shape[0] == 0:
+        return np.zeros((H, d)), np.zeros((0, d)), np.zeros((0, d))
+    P = softmax_weights(q, keys, scale)                  # [H, L]
+    o = P @ values                                       # [H, d]
+    dP = dout @ values.T                                 # [H, L]
+    rowterm = (dout * o).sum(axis=1, keepdims=True)      # [H, 1]
+    if dlse is not None:
+        rowterm = rowterm - np.asarray(dlse, dtype=np.float64)[:, None]
+    dS = P * (dP - rowterm)
+    return scale * dS @ keys, scale * dS.T @ q, P.T @ dout
+
+
+def csa_attention_backward(q, Kc, Vc, idx, K_raw, V_raw, raw_pos0, p, n_win, scale, dout,
+                           dlse=None, ratio=CSA_RATIO):
+    """Gradients of csa_attention for one query token (READINGS R4, R6, R8): dq [H, d], and
+    the contributions to the compressed entries dKc, dVc (shape of Kc) and to the raw rows
+    dK_raw, dV_raw (shape of K_raw), each key's gradient added to the row it came from."""
+    n_vis = visible_entries(p, Kc.shape[0], ratio)
+    keys, vals = csa_keys(Kc, Vc, idx, K_raw, V_raw, raw_pos0, p, n_win, n_vis)
+    dq, dk, dv = attend_backward(q, keys, vals, scale, dout, dlse)
+    sel = [int(j) for j in idx if 0 <= j < n_vis]
+    win = window_positions(p, n_win) - raw_pos0
+    dKc = np.zeros(np.shape(Kc))
+    dVc = np.zeros(np.shape(Vc))
+    dKr = np.zeros(np.shape(K_raw))
+    dVr = np.zeros(np.shape(V_raw))
+    ns = len(sel)
+    np.add.at(dKc, sel, dk[:ns])
+    np.add.at(dVc, sel, dv[:ns])
+    np.add.at(dKr, win, dk[ns:])
+    np.add.at(dVr, win, dv[ns:])
+    return dq, dKc, dVc, dKr, dVr
+
+
+def hca_attention_backward(q, Kh, Vh, p, scale, dout, dlse=None, ratio=HCA_RATIO):
+    """Gradients of hca_attention for one query token (READINGS R5, R6, R8): dq, dKh, dVh
+    (the entries past the visible count get zero)."""
+    n = visible_entries(p, Kh.shape[0], ratio)
+    dq, dk, dv = attend_backward(q, Kh[:n], Vh[:n], scale, dout, dlse)
+    dKh = np.zeros(np.shape(Kh))
+    dVh = np.zeros(np.shape(Vh))
+    dKh[:n] = dk
+    dVh[:n] = dv
+    return dq, dKh, dVh
+
+
+def compress_backward(x, omega, ratio, dy):
+    """Gradients of sum(dy * compress(x, omega, ratio)) (READINGS R1, R8): dx [T, D] (token
+    j*ratio + i gets alpha_i dy[j]; the unpooled tail gets zero) and domega [ratio]
+    (domega_k = alpha_k (g_k - sum_i alpha_i g_i) with g_i = sum_j dy[j] . x[j*ratio + i],
+    the softmax's derivative)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    alpha = pool_weights(omega)
+    n = x.shape[0] // ratio
+    dx = np.zeros_like(x)
+    dx[: n * ratio] = (alpha[None, :, None] * dy[:n, None, :]).reshape(n * ratio, x.shape[1])
+    blocks = x[: n * ratio].reshape(n, ratio, x.shape[1])
+    g = np.einsum("jid,jd->i", blocks, dy[:n])
+    domega = alpha * (g - (alpha * g).sum())
+    return dx, domega

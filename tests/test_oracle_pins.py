@@ -364,3 +364,115 @@ def test_decode_query_composition_shapes():
                        cfg.topk, cfg.n_win, cfg.scale, "f32")
     assert r["idx"].shape == (16,) and (np.diff(r["idx"]) > 0).all()
     assert r["csa"][0].shape == (1, 64) and r["hca"][0].shape == (1, 64)
+
+
+# --------------------------------------------------------------------------- backward pins
+# The gradients are pinned to central finite differences of the forward functions (which
+# the pins above tie to the pages and to closed forms), so a wrong sign, a dropped term or
+# a transposed product in the backward fails here.
+
+def _fd_grad(f, x, h=1e-6):
+    """Central finite-difference gradient of the scalar f at x (every element)."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp, xm = x.copy(), x.copy()
+        xp[i] += h
+        xm[i] -= h
+        g[i] = (f(xp) - f(xm)) / (2 * h)
+    return g
+
+
+def _close(a, b, tol=1e-6):
+    assert np.allclose(a, b, rtol=tol, atol=tol), np.abs(a - b).max()
+
+
+def test_attend_backward_matches_finite_differences():
+    r = np.random.default_rng(41)
+    H, L, d, scale = 3, 6, 5, 0.37
+    q, k, v = r.standard_normal((H, d)), r.standard_normal((L, d)), r.standard_normal((L, d))
+    do, dl = r.standard_normal((H, d)), r.standard_normal(H)
+
+    def loss(q_, k_, v_):
+        o, lse = O.attend(q_, k_, v_, scale)
+        return (do * o).sum() + (dl * lse).sum()
+    dq, dk, dv = O.attend_backward(q, k, v, scale, do, dl)
+    _close(dq, _fd_grad(lambda x: loss(x, k, v), q))
+    _close(dk, _fd_grad(lambda x: loss(q, x, v), k))
+    _close(dv, _fd_grad(lambda x: loss(q, k, x), v))
+    # without dlse the lse term drops out
+    dq0, _, _ = O.attend_backward(q, k, v, scale, do)
+    _close(dq0, _fd_grad(lambda x: (do * O.attend(x, k, v, scale)[0]).sum(), q))
+
+
+def test_attend_backward_closed_forms():
+    r = np.random.default_rng(42)
+    H, L, d, scale = 4, 7, 6, 0.5
+    q, k, v = r.standard_normal((H, d)), r.standard_normal((L, d)), r.standard_normal((L, d))
+    do, dl = r.standard_normal((H, d)), r.standard_normal(H)
+    # the value gradients sum to the summed output gradient (each head's weights sum to one)
+    _, _, dv = O.attend_backward(q, k, v, scale, do, dl)
+    _close(dv.sum(axis=0), do.sum(axis=0), 1e-12)
+    # identical keys: uniform weights, and only the lse term moves q: dq_h = scale dlse_h k
+    kk = np.repeat(k[:1], L, axis=0)
+    dq, dk, _ = O.attend_backward(q, kk, v, scale, do, dl)
+    _close(dq, scale * dl[:, None] * kk[0][None, :], 1e-12)
+    # one key: the output is v whatever q is, so dq = scale dlse k and dv = sum_h dout_h
+    dq1, dk1, dv1 = O.attend_backward(q, k[:1], v[:1], scale, do, dl)
+    _close(dq1, scale * dl[:, None] * k[0][None, :], 1e-12)
+    _close(dv1[0], do.sum(axis=0), 1e-12)
+    _close(dk1[0], scale * (dl[:, None] * q).sum(axis=0), 1e-12)
+
+
+def test_csa_backward_matches_finite_differences():
+    r = np.random.default_rng(43)
+    H, d, N, scale, w = 2, 4, 6, 0.4, 3
+    p, raw_pos0 = 13, 9                      # window positions 11..13 -> raw rows 2..4
+    Kc, Vc = r.standard_normal((N, d)), r.standard_normal((N, d))
+    Kr, Vr = r.standard_normal((6, d)), r.standard_normal((6, d))
+    q, do, dl = r.standard_normal((H, d)), r.standard_normal((H, d)), r.standard_normal(H)
+    idx = np.array([0, 2, 3, -1, 5])         # 5 is past n_c(13) = 3: skipped, like the padding
+
+    def loss(q_, Kc_, Vc_, Kr_, Vr_):
+        o, lse = O.csa_attention(q_, Kc_, Vc_, idx, Kr_, Vr_, raw_pos0, p, w, scale, 4)
+        return (do * o).sum() + (dl * lse).sum()
+    dq, dKc, dVc, dKr, dVr = O.csa_attention_backward(q, Kc, Vc, idx, Kr, Vr, raw_pos0, p, w,
+                                                      scale, do, dl, 4)
+    _close(dq, _fd_grad(lambda x: loss(x, Kc, Vc, Kr, Vr), q))
+    _close(dKc, _fd_grad(lambda x: loss(q, x, Vc, Kr, Vr), Kc))
+    _close(dVc, _fd_grad(lambda x: loss(q, Kc, x, Kr, Vr), Vc))
+    _close(dKr, _fd_grad(lambda x: loss(q, Kc, Vc, x, Vr), Kr))
+    _close(dVr, _fd_grad(lambda x: loss(q, Kc, Vc, Kr, x), Vr))
+    assert not dKc[1].any() and not dKc[4:].any() and not dKr[[0, 1, 5]].any()
+
+
+def test_hca_backward_matches_finite_differences():
+    r = np.random.default_rng(44)
+    H, d, N, scale = 3, 4, 5, 0.3
+    Kh, Vh = r.standard_normal((N, d)), r.standard_normal((N, d))
+    q, do, dl = r.standard_normal((H, d)), r.standard_normal((H, d)), r.standard_normal(H)
+    p = 3 * 128 + 5                          # three entries visible
+
+    def loss(q_, K_, V_):
+        o, lse = O.hca_attention(q_, K_, V_, p, scale, 128)
+        return (do * o).sum() + (dl * lse).sum()
+    dq, dK, dV = O.hca_attention_backward(q, Kh, Vh, p, scale, do, dl, 128)
+    _close(dq, _fd_grad(lambda x: loss(x, Kh, Vh), q))
+    _close(dK, _fd_grad(lambda x: loss(q, x, Vh), Kh))
+    _close(dV, _fd_grad(lambda x: loss(q, Kh, x), Vh))
+    assert not dK[3:].any()
+
+
+def test_compress_backward_matches_finite_differences():
+    r = np.random.default_rng(45)
+    T, D, ratio = 11, 3, 4                   # two entries and a tail of 3 tokens
+    x, om = r.standard_normal((T, D)), r.standard_normal(ratio)
+    dy = r.standard_normal((T // ratio, D))
+    loss = lambda x_, om_: (dy * O.compress(x_, om_, ratio)).sum()
+    dx, dom = O.compress_backward(x, om, ratio, dy)
+    _close(dx, _fd_grad(lambda v: loss(v, om), x))
+    _close(dom, _fd_grad(lambda v: loss(x, v), om))
+    assert not dx[8:].any()
+    # the weights sum to one, so shifting every logit changes nothing
+    assert abs(dom.sum()) < 1e-12
