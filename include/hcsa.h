@@ -275,6 +275,57 @@ int hcsa_hca_dense_attn(const void *q, const void *kh, const void *vh, int64_t h
                         float scale, float *out, float *lse, void *workspace, size_t ws_bytes,
                         hcsa_stream stream);
 
+/*
+ * Backward (training) [Lighthouse section 八 item 2: the sparse attention is trained from
+ * the 64K stage of the length curriculum; item 3 for the attention itself].  Gradients of
+ * the loss sum(dout * out) + sum(dlse * lse) of the forward call with the same arguments;
+ * the top-k selection is held fixed, a rounding to the cache type passes gradients
+ * unchanged.  Caches are contiguous (no pages, no raw-token ring).
+ *
+ * out, lse   the forward's outputs [B][Nq][H][d], [B][Nq][H] (F32).
+ * dout       [B][Nq][H][d] F32; dlse [B][Nq][H] F32 or NULL (no gradient on lse).
+ * dq         [B][Nq][H][d] F32, written.
+ * CSA: dkc, dvc [B][N][d] F32 (dc_bstride elements), the selected entries' gradients, and
+ *      dk_raw, dv_raw [B][T_raw][d] F32 (draw_bstride), the window rows' gradients, are
+ *      accumulated (+=): they may be shared with other calls, and start from the caller's
+ *      values (zero them first for a fresh gradient).
+ * HCA: dkh, dvh [B][N][d] F32 (dh_bstride), accumulated.
+ * The accumulations use floating-point atomics: their order, and the last bits of the
+ * accumulated gradients, can differ between runs; dq is deterministic.
+ * Limits: the forward's, and H <= 64/c with c = 1, 2, 4 for d <= 64, 128, 256 (H counted
+ * rounded up to 4, 16, 32 or 64).  No workspace.
+ */
+int hcsa_csa_sparse_attn_bwd(const void *q, const void *kc, const void *vc, int64_t c_bstride,
+                             int N, const int32_t *topk_idx, int k, const void *k_raw,
+                             const void *v_raw, int64_t raw_bstride, int64_t T_raw,
+                             int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
+                             const int64_t *seq_pos, int kv_dtype, int B, int Nq, int H, int d,
+                             float scale, const float *out, const float *lse,
+                             const float *dout, const float *dlse, float *dq, float *dkc,
+                             float *dvc, int64_t dc_bstride, float *dk_raw, float *dv_raw,
+                             int64_t draw_bstride, hcsa_stream stream);
+int hcsa_hca_dense_attn_bwd(const void *q, const void *kh, const void *vh, int64_t h_bstride,
+                            int N, int ratio, int64_t pos0, const int64_t *seq_pos,
+                            int kv_dtype, int B, int Nq, int H, int d, float scale,
+                            const float *out, const float *lse, const float *dout,
+                            const float *dlse, float *dq, float *dkh, float *dvh,
+                            int64_t dh_bstride, hcsa_stream stream);
+
+/*
+ * Backward of hcsa_compress_kv (same x, omega, ratio, B, T, D) [Lighthouse section 八 items 2
+ * and 3]: given dy [B][T/ratio][D] F32 (dy_bstride elements), accumulates dx [B][T][D] F32
+ * (dx_bstride; token j*ratio + i gets alpha_i dy_j, the unpooled tail nothing) and, when
+ * domega is not NULL, domega [ratio] F32 (the softmax's derivative: alpha_k (g_k -
+ * sum_i alpha_i g_i) with g_i = sum over sequences and entries of dy_j . x_{j*ratio+i}).
+ * The sums run in a fixed order (deterministic).  workspace: at least
+ * hcsa_compress_kv_bwd_workspace_size(B, T, ratio) bytes, 256-byte aligned.
+ */
+size_t hcsa_compress_kv_bwd_workspace_size(int B, int T, int ratio);
+int hcsa_compress_kv_bwd(const void *x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                         const float *omega, int ratio, const float *dy, int64_t dy_bstride,
+                         float *dx, int64_t dx_bstride, float *domega, void *workspace,
+                         size_t ws_bytes, hcsa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhcsa.so")
-SOURCES = ["compress.hip", "indexer.hip", "topk.hip", "attention.hip", "abi.cpp"]
+SOURCES = ["compress.hip", "indexer.hip", "topk.hip", "attention.hip", "backward.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
          "-Wno-unused-function",

@@ -251,11 +251,10 @@ int hcsa_topk(const void* scores, int score_dtype, int64_t row_stride, int B, in
                     "hcsa_topk");
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score_dtype) {
   if (B < 1 || Nq < 1 || N < 1 || k < 1) return 0;
-  const size_t scores = align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
+  const size_t scores = hcsa::align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
   return scores + hcsa::plan_topk(score_dtype, B * Nq, N, k).total_bytes;
 }
 
@@ -333,7 +332,7 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   if (!topk_idx) return fail(HCSA_EINVAL, "topk_idx must be non-null");
   if (!aligned16(topk_idx) || (scores_out && !aligned16(scores_out)))
     return fail(HCSA_EALIGN, "topk_idx and scores_out must be 16-byte aligned");
-  const size_t sbytes = align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
+  const size_t sbytes = hcsa::align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
   const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
   rc = check_ws(workspace, ws_bytes, sbytes + plan.total_bytes);
   if (rc) return rc;
@@ -359,13 +358,13 @@ size_t hcsa_csa_sparse_attn_workspace_size(int B, int Nq, int H, int d, int k, i
   return a > b ? a : b;
 }
 
-int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t c_bstride,
-                         int N, const int32_t* topk_idx, int k, const void* k_raw,
-                         const void* v_raw, int64_t raw_bstride, int64_t T_raw,
-                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
-                         const int64_t* seq_pos, const hcsa_pages* pages, int kv_dtype, int B,
-                         int Nq, int H, int d, float scale, float* out, float* lse,
-                         void* workspace, size_t ws_bytes, hcsa_stream stream) {
+// Arguments of CSA attention (forward and backward), checked on the host.
+static int check_csa(const void* q, const void* kc, const void* vc, int64_t c_bstride, int N,
+                     const int32_t* topk_idx, int k, const void* k_raw, const void* v_raw,
+                     int64_t raw_bstride, int64_t T_raw, int64_t raw_pos0, int n_win,
+                     int ratio, int64_t pos0, const int64_t* seq_pos, const hcsa_pages* pages,
+                     int kv_dtype, int B, int Nq, int H, int d, float scale, const float* out,
+                     const float* lse) {
   int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
@@ -405,6 +404,23 @@ int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t 
                   static_cast<long long>(first), static_cast<long long>(last),
                   static_cast<long long>(raw_pos0), static_cast<long long>(raw_pos0 + T_raw));
   }
+  return HCSA_OK;
+}
+
+int hcsa_csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t c_bstride,
+                         int N, const int32_t* topk_idx, int k, const void* k_raw,
+                         const void* v_raw, int64_t raw_bstride, int64_t T_raw,
+                         int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
+                         const int64_t* seq_pos, const hcsa_pages* pages, int kv_dtype, int B,
+                         int Nq, int H, int d, float scale, float* out, float* lse,
+                         void* workspace, size_t ws_bytes, hcsa_stream stream) {
+  int rc = check_csa(q, kc, vc, c_bstride, N, topk_idx, k, k_raw, v_raw, raw_bstride, T_raw,
+                     raw_pos0, n_win, ratio, pos0, seq_pos, pages, kv_dtype, B, Nq, H, d, scale,
+                     out, lse);
+  if (rc) return rc;
+  const bool paged = is_paged(pages);
+  const int64_t ring = raw_ring(pages);
+  (void)paged;
   const hcsa::AttnPlan plan =
       hcsa::plan_attention(true, kv_dtype, B, Nq, H, d, attn_max_len_csa(k, n_win));
   rc = check_ws(workspace, ws_bytes, plan.total_bytes);
@@ -458,6 +474,114 @@ int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h
   a.out = out; a.lse = lse;
   return hip_status(hcsa::launch_attention(false, a, plan, workspace, static_cast<hipStream_t>(stream)),
                     "hcsa_hca_dense_attn");
+}
+
+// ------------------------------------------------------------------ backward (training)
+
+static int check_bwd_grads(const float* dout, const float* dq, int B, int Nq, int H, int d) {
+  if (!dout || !dq) return fail(HCSA_EINVAL, "dout and dq must be non-null");
+  if (!aligned16(dout) || !aligned16(dq)) return fail(HCSA_EALIGN, "dout and dq must be 16-byte aligned");
+  if (!hcsa::attn_bwd_shape_supported(H, d))
+    return fail(HCSA_EINVAL, "backward needs H <= 64/c with c = 1, 2, 4 for d <= 64, 128, 256 "
+                "(H rounded up to 4, 16, 32 or 64)");
+  (void)B; (void)Nq;
+  return HCSA_OK;
+}
+
+int hcsa_csa_sparse_attn_bwd(const void* q, const void* kc, const void* vc, int64_t c_bstride,
+                             int N, const int32_t* topk_idx, int k, const void* k_raw,
+                             const void* v_raw, int64_t raw_bstride, int64_t T_raw,
+                             int64_t raw_pos0, int n_win, int ratio, int64_t pos0,
+                             const int64_t* seq_pos, int kv_dtype, int B, int Nq, int H, int d,
+                             float scale, const float* out, const float* lse,
+                             const float* dout, const float* dlse, float* dq, float* dkc,
+                             float* dvc, int64_t dc_bstride, float* dk_raw, float* dv_raw,
+                             int64_t draw_bstride, hcsa_stream stream) {
+  int rc = check_csa(q, kc, vc, c_bstride, N, topk_idx, k, k_raw, v_raw, raw_bstride, T_raw,
+                     raw_pos0, n_win, ratio, pos0, seq_pos, nullptr, kv_dtype, B, Nq, H, d,
+                     scale, out, lse);
+  if (rc) return rc;
+  rc = check_bwd_grads(dout, dq, B, Nq, H, d);
+  if (rc) return rc;
+  if (k > 0) {
+    if (!dkc || !dvc) return fail(HCSA_EINVAL, "dkc and dvc must be non-null when k > 0");
+    if (B > 1 && dc_bstride < static_cast<int64_t>(N) * d) return fail(HCSA_EINVAL, "dc_bstride < N*d");
+  }
+  if (n_win > 0) {
+    if (!dk_raw || !dv_raw) return fail(HCSA_EINVAL, "dk_raw and dv_raw must be non-null when n_win > 0");
+    if (B > 1 && draw_bstride < T_raw * d) return fail(HCSA_EINVAL, "draw_bstride < T_raw*d");
+  }
+  hcsa::AttnArgs a{};
+  a.q = q; a.kc = kc; a.vc = vc; a.c_bstride = c_bstride; a.N = N > 0 ? N : 0; a.ratio = ratio;
+  a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
+  a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0; a.seq_pos = seq_pos;
+  a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
+  hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkc, dvc, dc_bstride, dk_raw, dv_raw, draw_bstride};
+  return hip_status(hcsa::launch_attention_bwd(true, a, g, static_cast<hipStream_t>(stream)),
+                    "hcsa_csa_sparse_attn_bwd");
+}
+
+int hcsa_hca_dense_attn_bwd(const void* q, const void* kh, const void* vh, int64_t h_bstride,
+                            int N, int ratio, int64_t pos0, const int64_t* seq_pos,
+                            int kv_dtype, int B, int Nq, int H, int d, float scale,
+                            const float* out, const float* lse, const float* dout,
+                            const float* dlse, float* dq, float* dkh, float* dvh,
+                            int64_t dh_bstride, hcsa_stream stream) {
+  int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
+  if (rc) return rc;
+  rc = check_seq_pos(seq_pos);
+  if (rc) return rc;
+  rc = check_bwd_grads(dout, dq, B, Nq, H, d);
+  if (rc) return rc;
+  if (N < 0) return fail(HCSA_EINVAL, "N must be >= 0");
+  if (N > 0) {
+    if (!kh || !vh || !dkh || !dvh) return fail(HCSA_EINVAL, "kh, vh, dkh and dvh must be non-null");
+    if (!aligned16(kh) || !aligned16(vh)) return fail(HCSA_EALIGN, "kh and vh must be 16-byte aligned");
+    if ((h_bstride * elem_size(kv_dtype)) % 16 != 0) return fail(HCSA_EALIGN, "h_bstride alignment");
+    if (B > 1 && (h_bstride < static_cast<int64_t>(N) * d || dh_bstride < static_cast<int64_t>(N) * d))
+      return fail(HCSA_EINVAL, "h_bstride and dh_bstride must be >= N*d");
+  }
+  hcsa::AttnArgs a{};
+  a.q = q; a.kc = kh; a.vc = vh; a.c_bstride = h_bstride; a.N = N; a.ratio = ratio;
+  a.pos0 = pos0; a.seq_pos = seq_pos;
+  a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
+  hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkh, dvh, dh_bstride, nullptr, nullptr, 0};
+  return hip_status(hcsa::launch_attention_bwd(false, a, g, static_cast<hipStream_t>(stream)),
+                    "hcsa_hca_dense_attn_bwd");
+}
+
+size_t hcsa_compress_kv_bwd_workspace_size(int B, int T, int ratio) {
+  if (B < 1 || T < 0 || ratio < 1) return 0;
+  return hcsa::compress_bwd_workspace_bytes(B, T, ratio);
+}
+
+int hcsa_compress_kv_bwd(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
+                         const float* omega, int ratio, const float* dy, int64_t dy_bstride,
+                         float* dx, int64_t dx_bstride, float* domega, void* workspace,
+                         size_t ws_bytes, hcsa_stream stream) {
+  if (x_dtype != HCSA_F32 && x_dtype != HCSA_BF16)
+    return fail(HCSA_EDTYPE, "x_dtype must be F32 or BF16");
+  if (B < 1 || B > 65535) return fail(HCSA_EINVAL, "B must be in [1, 65535]");
+  if (T < 0) return fail(HCSA_EINVAL, "T must be >= 0");
+  if (D < 8 || D > 2048 || D % 8 != 0) return fail(HCSA_EINVAL, "D must be a multiple of 8 in [8, 2048]");
+  if (ratio < 1 || ratio > 1024) return fail(HCSA_EINVAL, "ratio must be in [1, 1024]");
+  if (!x || !omega || !dy || !dx) return fail(HCSA_EINVAL, "x, omega, dy and dx must be non-null");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx))
+    return fail(HCSA_EALIGN, "x, dy and dx must be 16-byte aligned");
+  if ((x_bstride * elem_size(x_dtype)) % 16 != 0 || (dy_bstride * 4) % 16 != 0 ||
+      (dx_bstride * 4) % 16 != 0)
+    return fail(HCSA_EALIGN, "x_bstride, dy_bstride and dx_bstride must keep 16-byte alignment");
+  const int n_out = T / ratio;
+  if (B > 1 && (x_bstride < static_cast<int64_t>(T) * D || dx_bstride < static_cast<int64_t>(T) * D ||
+                dy_bstride < static_cast<int64_t>(n_out) * D))
+    return fail(HCSA_EINVAL, "x_bstride, dx_bstride (>= T*D) or dy_bstride (>= (T/ratio)*D) too small");
+  const int rc = check_ws(workspace, ws_bytes, hcsa::compress_bwd_workspace_bytes(B, T, ratio));
+  if (rc) return rc;
+  if (n_out == 0) return ok();
+  return hip_status(hcsa::launch_compress_bwd(x, x_dtype, x_bstride, B, T, D, omega, ratio, dy,
+                                              dy_bstride, dx, dx_bstride, domega, workspace,
+                                              static_cast<hipStream_t>(stream)),
+                    "hcsa_compress_kv_bwd");
 }
 
 }  // extern "C"

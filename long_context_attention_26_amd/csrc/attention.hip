@@ -28,6 +28,7 @@
 //   attn_generic_kernel  any head count / head dim, fp32 or bf16, plain VALU (small and
 //                        fp32 shapes).
 //   lse_merge_kernel     o = sum_s e^{lse_s - L} o_s, L = log sum_s e^{lse_s}.
+#include "attn_keys.h"
 #include "common.h"
 #include "internal.h"
 
@@ -37,97 +38,12 @@ namespace hcsa {
 
 namespace {
 
-struct AttnDev {
-  const void* q;
-  const void* kc;
-  const void* vc;
-  int64_t c_bstride;
-  int N, ratio;
-  const int32_t* idx;
-  int k;
-  const void* k_raw;
-  const void* v_raw;
-  int64_t raw_bstride, T_raw, raw_pos0;
-  int n_win;
-  int64_t pos0;
-  const int64_t* seq_pos;   // [B] or null
-  PageMap pm;               // paged caches (table null: contiguous)
-  int c_log2;               // log2 of the compressed cache's rows per page
-  int64_t raw_ring;         // 0, or raw tokens in a ring of raw_ring (a power of two) rows
-  int Nq, H, d;
-  float scale;
-  int chunk, splits, rows;
-  float* out;      // final [rows][H][d] (splits == 1) or partial [splits][rows][H][d]
-  float* lse;      // final [rows][H] or partial [splits][rows][H]
-};
-
-// Key-list geometry of one query row.
-struct RowKeys {
-  int b;
-  int nv;          // visible compressed entries
-  int L;           // key list length
-  int64_t wstart;  // first window position (CSA)
-};
-
-template <bool CSA>
-__device__ __forceinline__ RowKeys row_keys(const AttnDev& A, int row) {
-  RowKeys r;
-  r.b = row / A.Nq;
-  const int64_t p = query_pos(A.seq_pos, A.pos0, r.b, row % A.Nq);
-  const int64_t v = (p + 1) / A.ratio;
-  r.nv = static_cast<int>(v < A.N ? v : A.N);
-  if constexpr (CSA) {
-    r.wstart = p - A.n_win + 1 > 0 ? p - A.n_win + 1 : 0;
-    const int winlen = A.n_win > 0 ? static_cast<int>(p - r.wstart + 1) : 0;
-    r.L = A.k + winlen;
-  } else {
-    r.wstart = 0;
-    r.L = r.nv;
-  }
-  return r;
-}
-
-// Source of key-list position `pos`: >= 0 compressed row, -1 none, <= -2 raw row -(code+2).
-template <bool CSA>
-__device__ __forceinline__ int key_code(const AttnDev& A, const RowKeys& r, int row, int pos) {
-  if (pos >= r.L) return -1;
-  if constexpr (CSA) {
-    if (pos < A.k) {
-      const int e = A.idx[static_cast<int64_t>(row) * A.k + pos];
-      return (e >= 0 && e < r.nv) ? e : -1;
-    }
-    const int64_t t = r.wstart + (pos - A.k) - A.raw_pos0;
-    return -static_cast<int>(t) - 2;
-  } else {
-    return pos;
-  }
-}
-
-template <typename TE>
-__device__ __forceinline__ const TE* key_row(const AttnDev& A, int b, int code, bool value) {
-  if (code >= 0) {
-    const TE* base = static_cast<const TE*>(value ? A.vc : A.kc);
-    if (A.pm.table) return base + row_off<true>(A.pm, 0, b, code, A.c_log2, A.d);
-    return base + b * A.c_bstride + static_cast<int64_t>(code) * A.d;
-  }
-  const TE* base = static_cast<const TE*>(value ? A.v_raw : A.k_raw);
-  // raw rows: one per token at position raw_pos0 + row; in a ring, position t sits in row
-  // t mod raw_ring; paged, 128 per page
-  if (A.raw_ring)
-    return base + b * A.raw_bstride + ((-code - 2) & (A.raw_ring - 1)) * A.d;
-  if (A.pm.table) return base + row_off<true>(A.pm, 0, b, A.raw_pos0 + (-code - 2), 7, A.d);
-  return base + b * A.raw_bstride + static_cast<int64_t>(-code - 2) * A.d;
-}
+using namespace attn;
 
 // ------------------------------------------------------------------ generic VALU path
 
 constexpr int kGenChunk = 64;
 
-template <bool BF16>
-__device__ __forceinline__ float ld(const void* p, int64_t i) {
-  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  else return static_cast<const float*>(p)[i];
-}
 
 // grid: (splits, rows); block 256; dynamic LDS: H*d + H*kGenChunk floats + kGenChunk ints.
 template <bool CSA, bool BF16>
@@ -716,7 +632,6 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
 
 }  // namespace
 
-static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len) {
   AttnPlan p{};
@@ -760,32 +675,7 @@ AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int
 
 hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
                             hipStream_t s) {
-  AttnDev A;
-  A.q = a.q;
-  A.kc = a.kc;
-  A.vc = a.vc;
-  A.c_bstride = a.c_bstride;
-  A.N = a.N;
-  A.ratio = a.ratio;
-  A.idx = a.idx;
-  A.k = a.k;
-  A.k_raw = a.k_raw;
-  A.v_raw = a.v_raw;
-  A.raw_bstride = a.raw_bstride;
-  A.T_raw = a.T_raw;
-  A.raw_pos0 = a.raw_pos0;
-  A.n_win = a.n_win;
-  A.pos0 = a.pos0;
-  A.seq_pos = a.seq_pos;
-  A.pm.table = a.block_table;
-  A.pm.stride = a.table_stride;
-  A.raw_ring = a.raw_ring;
-  A.c_log2 = 0;
-  for (int per = kPageTokens / a.ratio; per > 1; per >>= 1) ++A.c_log2;
-  A.Nq = a.Nq;
-  A.H = a.H;
-  A.d = a.d;
-  A.scale = a.scale;
+  AttnDev A = make_attn_dev(a);
   A.chunk = plan.chunk;
   A.splits = plan.splits;
   A.rows = plan.rows;

@@ -102,6 +102,50 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
+// Eight consecutive values (F32, or BF16 widened) from a 16-byte aligned address.
+template <bool IN_BF16>
+__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+  if constexpr (IN_BF16) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[2 * c] = bf16_lo(w[c]);
+      v[2 * c + 1] = bf16_hi(w[c]);
+    }
+  } else {
+    f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+    f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = a[c];
+      v[4 + c] = b[c];
+    }
+  }
+}
+
+// Softmax of the pooling logits into LDS (weight 1 when omega is null and r == 1).
+__device__ __forceinline__ void pool_weights(const float* __restrict__ omega, int r,
+                                             float* alpha) {
+  if (threadIdx.x < kWave) {
+    if (omega == nullptr) {
+      if (threadIdx.x == 0) alpha[0] = 1.0f;
+    } else {
+      float m = -INFINITY;
+      for (int i = threadIdx.x; i < r; i += kWave) m = fmaxf(m, omega[i]);
+      m = wave_max(m);
+      float s = 0.0f;
+      for (int i = threadIdx.x; i < r; i += kWave) {
+        const float e = expf(omega[i] - m);
+        alpha[i] = e;
+        s += e;
+      }
+      s = wave_sum(s);
+      for (int i = threadIdx.x; i < r; i += kWave) alpha[i] = alpha[i] / s;
+    }
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ unsigned lane_id() { return __lane_id(); }
 
 // Number of set bits of a 64-bit wave ballot below this lane.

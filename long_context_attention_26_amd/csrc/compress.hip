@@ -16,26 +16,6 @@ namespace hcsa {
 
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_MXFP4 = 2 };
 
-template <bool IN_BF16>
-__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
-  if constexpr (IN_BF16) {
-    u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v[2 * c] = bf16_lo(w[c]);
-      v[2 * c + 1] = bf16_hi(w[c]);
-    }
-  } else {
-    f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-    f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v[c] = a[c];
-      v[4 + c] = b[c];
-    }
-  }
-}
-
 // Writes 8 values of one row: F32, BF16, or MXFP4 (4 code bytes; the lane holding the
 // first 8 channels of each 32-channel block also writes the block's scale byte).
 template <int OUT>
@@ -67,28 +47,6 @@ __device__ __forceinline__ void store8(const float (&acc)[8], void* y, int64_t y
   }
 }
 
-// Softmax of the pooling logits into LDS (weight 1 when omega is null and r == 1).
-__device__ __forceinline__ void pool_weights(const float* __restrict__ omega, int r,
-                                             float* alpha) {
-  if (threadIdx.x < kWave) {
-    if (omega == nullptr) {
-      if (threadIdx.x == 0) alpha[0] = 1.0f;
-    } else {
-      float m = -INFINITY;
-      for (int i = threadIdx.x; i < r; i += kWave) m = fmaxf(m, omega[i]);
-      m = wave_max(m);
-      float s = 0.0f;
-      for (int i = threadIdx.x; i < r; i += kWave) {
-        const float e = expf(omega[i] - m);
-        alpha[i] = e;
-        s += e;
-      }
-      s = wave_sum(s);
-      for (int i = threadIdx.x; i < r; i += kWave) alpha[i] = alpha[i] / s;
-    }
-  }
-  __syncthreads();
-}
 
 // Source row (in D-element rows) of entry j's first token and the entry's output row, for
 // paged tensors: the entry's r tokens lie in one 128-token page (r divides 128 and the

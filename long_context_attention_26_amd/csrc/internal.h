@@ -9,6 +9,9 @@
 
 namespace hcsa {
 
+// Byte counts rounded up to the 256-byte alignment of workspace parts.
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 // ---- compress.hip
 hipError_t launch_compress(const void* x, int x_dtype, int64_t x_bstride, int B, int T, int D,
                            const float* omega, int ratio, void* y, int y_dtype,
@@ -72,6 +75,31 @@ struct AttnPlan {
   bool mfma, tiled, hca_decode;
   size_t part_bytes, total_bytes;
 };
+// Backward of the attention: the forward's arguments (a) plus these.
+struct AttnBwdArgs {
+  const float* out;     // forward output [rows][H][d]
+  const float* lse;     // forward log-sum-exp [rows][H]
+  const float* dout;    // [rows][H][d]
+  const float* dlse;    // [rows][H] or null
+  float* dq;            // [rows][H][d], written
+  float* dkc;           // [B][N][d] F32, accumulated (HCA: the entries)
+  float* dvc;
+  int64_t dc_bstride;
+  float* dkr;           // [B][T_raw][d] F32, accumulated (CSA window rows)
+  float* dvr;
+  int64_t dr_bstride;
+};
+// register tiling of the backward kernel: heads rounded up to 4, 16, 32 or 64 and channels
+// per lane (d / 64 rounded up to 1, 2 or 4); supported when heads * channels <= 64
+inline int bwd_heads(int H) { return H <= 4 ? 4 : H <= 16 ? 16 : H <= 32 ? 32 : H <= 64 ? 64 : 0; }
+inline int bwd_cpl(int d) { return d <= 64 ? 1 : d <= 128 ? 2 : d <= 256 ? 4 : 0; }
+bool attn_bwd_shape_supported(int H, int d);
+hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& g, hipStream_t s);
+size_t compress_bwd_workspace_bytes(int B, int T, int ratio);
+hipError_t launch_compress_bwd(const void* x, int x_dtype, int64_t x_bstride, int B, int T,
+                               int D, const float* omega, int ratio, const float* dy,
+                               int64_t dy_bstride, float* dx, int64_t dx_bstride,
+                               float* domega, void* ws, hipStream_t s);
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len);
 hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
                             hipStream_t s);

@@ -799,7 +799,6 @@ __global__ __launch_bounds__(kResThreads) void seg_resolve_kernel(TopkDev P, Seg
 
 }  // namespace
 
-static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 TopkPlan plan_topk(int score_dtype, int rows, int N, int k) {
   TopkPlan p{};

@@ -29,6 +29,14 @@ _SIGS = {
     "hcsa_mxfp4_quantize": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
     "hcsa_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_topk": (_i, [_p, _i, _i64, _i, _i, _i, _i, _i64, _p, _i, _p, _p, _sz, _p]),
+    "hcsa_csa_sparse_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64,
+                                      _i, _i, _i64, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p,
+                                      _p, _p, _p, _p, _i64, _p, _p, _i64, _p]),
+    "hcsa_hca_dense_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _p, _i, _i, _i, _i, _i,
+                                     _f, _p, _p, _p, _p, _p, _p, _p, _i64, _p]),
+    "hcsa_compress_kv_bwd_workspace_size": (_sz, [_i, _i, _i]),
+    "hcsa_compress_kv_bwd": (_i, [_p, _i, _i64, _i, _i, _i, _p, _i, _p, _i64, _p, _i64, _p, _p,
+                                  _sz, _p]),
     "hcsa_csa_index_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_csa_index_topk": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
                                  _i64, _p, _p, _i, _i, _p, _p, _p, _sz, _p]),
@@ -280,3 +288,48 @@ def hca_dense_attn(q, kh, vh, N, ratio, pos0, scale, out, lse, workspace=None, s
                                    Nq, H, d, scale, _ptr(out), _ptr(lse),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
+
+
+# ------------------------------------------------------------------ backward (training)
+
+def csa_sparse_attn_bwd(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio, pos0,
+                        scale, out, lse, dout, dq, dkc, dvc, dk_raw, dv_raw, dlse=None,
+                        stream=None, seq_pos=None):
+    """Backward of csa_sparse_attn: writes dq [B, Nq, H, d] f32; adds into dkc, dvc
+    [B, >=N, d] f32 and dk_raw, dv_raw [B, T_raw, d] f32."""
+    B, Nq, H, d = q.shape
+    k = topk_idx.shape[-1]
+    _check(lib.hcsa_csa_sparse_attn_bwd(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N,
+                                        _ptr(topk_idx), k, _ptr(k_raw), _ptr(v_raw),
+                                        k_raw.stride(0), k_raw.shape[1], raw_pos0, n_win, ratio,
+                                        pos0, _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d,
+                                        scale, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse),
+                                        _ptr(dq), _ptr(dkc), _ptr(dvc), dkc.stride(0),
+                                        _ptr(dk_raw), _ptr(dv_raw), dk_raw.stride(0),
+                                        _stream(stream)))
+    return dq
+
+
+def hca_dense_attn_bwd(q, kh, vh, N, ratio, pos0, scale, out, lse, dout, dq, dkh, dvh,
+                       dlse=None, stream=None, seq_pos=None):
+    """Backward of hca_dense_attn: writes dq; adds into dkh, dvh [B, >=N, d] f32."""
+    B, Nq, H, d = q.shape
+    _check(lib.hcsa_hca_dense_attn_bwd(_ptr(q), _ptr(kh), _ptr(vh), kh.stride(0), N, ratio, pos0,
+                                       _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d, scale,
+                                       _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq),
+                                       _ptr(dkh), _ptr(dvh), dkh.stride(0), _stream(stream)))
+    return dq
+
+
+def compress_kv_bwd(x, omega, ratio, dy, dx, domega=None, workspace=None, stream=None):
+    """Backward of compress_kv over x [B, T, D] (F32/BF16): adds into dx [B, T, D] f32 and,
+    if given, domega [ratio] f32, from dy [B, T/ratio, D] f32."""
+    B, T, D = x.shape
+    if workspace is None:
+        workspace = alloc_workspace(lib.hcsa_compress_kv_bwd_workspace_size(B, T, ratio),
+                                    x.device)
+    _check(lib.hcsa_compress_kv_bwd(_ptr(x), dtype_code(x), x.stride(0), B, T, D, _ptr(omega),
+                                    ratio, _ptr(dy), dy.stride(0), _ptr(dx), dx.stride(0),
+                                    _ptr(domega), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
+    return dx, domega
