@@ -168,6 +168,133 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
+def train_backward(args):
+    """--train: the attention part of one training step at the 64K stage of the length
+    curriculum (one sequence of 65 536 tokens, every token a query; CSA top-1024 + window
+    128, HCA, 16 heads x 128, bf16).  The selection (indexer + top-k over all 65 536 rows)
+    and the forward run untimed first; the timed step is the backward: zeroing the
+    gradient buffers, CSA attention backward, HCA attention backward and the pooling
+    backward of the four pooled K/V streams into the raw-token gradients and the pooling
+    logits.  The forward (CSA + HCA) is timed beside it for the ratio.  Prints one JSON
+    line."""
+    import torch
+    import workloads as W
+    from long_context_attention_26_amd import hcsa
+
+    T, Hh, d, H_I, d_I, k, w = 65536, 16, 128, 4, 64, 1024, 128
+    cfg = W.Config(0, "train b1 ctx65536 bf16 H16 d128 topk1024", B=1, T=T, Nq=T, pos0=0,
+                   H=Hh, d=d, H_I=H_I, d_I=d_I, topk=k, n_win=w, kv="bf16", idx="bf16",
+                   score="bf16")
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    K, V, I = (x.to(dev).unsqueeze(0) for x in W.raw_sequence(cfg, 0))
+    om = W.pool_logits(cfg, dev)
+    q, qi, wi = (x.to(dev) for x in W.queries(cfg))
+    Nc, Nh = T // 4, T // 128
+    Kc, Vc, Ic = (torch.empty(1, Nc, D, dtype=bf, device=dev) for D in (d, d, d_I))
+    Kh, Vh = (torch.empty(1, Nh, d, dtype=bf, device=dev) for _ in range(2))
+    hcsa.compress_kv_batched([hcsa.pool_job(K, om["csa_k"], 4, Kc), hcsa.pool_job(V, om["csa_v"], 4, Vc),
+                              hcsa.pool_job(I, om["idx_k"], 4, Ic), hcsa.pool_job(K, om["hca_k"], 128, Kh),
+                              hcsa.pool_job(V, om["hca_v"], 128, Vh)], 1)
+    # a call takes at most 65 535 query rows: the sequence's tokens go in two halves
+    HALF = T // 2
+    halves = [(h0, slice(h0, h0 + HALF)) for h0 in (0, HALF)]
+    idx = torch.empty(1, T, k, dtype=torch.int32, device=dev)
+    for h0, sl in halves:
+        hcsa.csa_index_topk(qi[:, sl], wi[:, sl], Ic, Nc, 4, h0, k, hcsa.BF16, idx[:, sl])
+    scale = cfg.scale
+    oc, oh = (torch.empty(1, T, Hh, d, device=dev) for _ in range(2))
+    lc, lh = (torch.empty(1, T, Hh, device=dev) for _ in range(2))
+    ws_c = hcsa.alloc_workspace(hcsa.csa_attn_workspace_size(1, HALF, Hh, d, k, w), dev)
+    ws_h = hcsa.alloc_workspace(hcsa.hca_attn_workspace_size(1, HALF, Hh, d, Nh), dev)
+
+    def forward():
+        for h0, sl in halves:
+            hcsa.csa_sparse_attn(q[:, sl], Kc, Vc, Nc, idx[:, sl], K, V, 0, w, 4, h0, scale,
+                                 oc[:, sl], lc[:, sl], workspace=ws_c)
+            hcsa.hca_dense_attn(q[:, sl], Kh, Vh, Nh, 128, h0, scale, oh[:, sl], lh[:, sl],
+                                workspace=ws_h)
+
+    forward()
+    g = torch.Generator(device=dev).manual_seed(7)
+    doc = torch.randn(1, T, Hh, d, device=dev, generator=g)
+    doh = torch.randn(1, T, Hh, d, device=dev, generator=g)
+    dqc, dqh = torch.empty_like(doc), torch.empty_like(doh)
+    grads = {n: torch.zeros(1, r_, d, device=dev) for n, r_ in
+             (("Kc", Nc), ("Vc", Nc), ("Kh", Nh), ("Vh", Nh), ("K", T), ("V", T))}
+    dom = {n: torch.zeros(r_, device=dev) for n, r_ in
+           (("csa_k", 4), ("csa_v", 4), ("hca_k", 128), ("hca_v", 128))}
+    ws_p = hcsa.alloc_workspace(hcsa.lib.hcsa_compress_kv_bwd_workspace_size(1, T, 128), dev)
+
+    stages = ["zero", "csa_bwd", "hca_bwd", "pool_bwd"]
+
+    def backward(ev=None):
+        mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        mark(0)
+        for t in grads.values():
+            t.zero_()
+        for t in dom.values():
+            t.zero_()
+        mark(1)
+        for h0, sl in halves:
+            hcsa.csa_sparse_attn_bwd(q[:, sl], Kc, Vc, Nc, idx[:, sl], K, V, 0, w, 4, h0, scale,
+                                     oc[:, sl], lc[:, sl], doc[:, sl], dqc[:, sl], grads["Kc"],
+                                     grads["Vc"], grads["K"], grads["V"])
+        mark(2)
+        for h0, sl in halves:
+            hcsa.hca_dense_attn_bwd(q[:, sl], Kh, Vh, Nh, 128, h0, scale, oh[:, sl], lh[:, sl],
+                                    doh[:, sl], dqh[:, sl], grads["Kh"], grads["Vh"])
+        mark(3)
+        for x, n, r_, gy, gx in ((K, "csa_k", 4, "Kc", "K"), (V, "csa_v", 4, "Vc", "V"),
+                                 (K, "hca_k", 128, "Kh", "K"), (V, "hca_v", 128, "Vh", "V")):
+            hcsa.compress_kv_bwd(x, om[n], r_, grads[gy], grads[gx], dom[n], workspace=ws_p)
+        mark(4)
+
+    for _ in range(args.warmup):
+        backward()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        backward(e)
+        evs.append(e)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / args.steps
+    br = {s_: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / len(evs) for j, s_ in enumerate(stages)}
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        forward()
+    f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
+
+    # (query, key) pairs of the CSA backward: selected entries plus window of every token
+    pairs = sum(min(k, (p + 1) // 4) + min(w, p + 1) for p in range(T))
+    flops = pairs * 5 * 2 * Hh * d          # q.k, dout.v, dk, dv, dq: H*d multiply-adds each
+    achieved = flops / (br["csa_bwd"] * 1e-3) / 1e12   # bf16 products on the matrix cores
+    out = {
+        "metric": "training attention backward tokens/s (CSA + HCA + pooling, 64K stage)",
+        "value": round(T / el, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(el * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and output gradients)",
+        "config": {"workload": cfg.workload, "context": T, "queries": T, "heads": Hh,
+                   "head_dim": d, "topk": k, "n_win": w},
+        "breakdown_ms": {k_: round(v, 3) for k_, v in br.items()},
+        "forward_ms": round(fwd_ms, 3),
+        "roofline": {"kernel": "attn_bwd_mfma_kernel (CSA, 2 launches)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_step": flops,
+                     "note": "limited by the fp32 atomic adds of dk/dv (256 per query-key pair)"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,7 +311,15 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 2 GiB device-to-device copy 3 times (the known-size "
                          "kernel that scales the HBM byte counters)")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training backward (CSA + HCA attention and pooling) at "
+                         "one 65 536-token sequence instead of the decode step")
     args = ap.parse_args()
+    if args.train:
+        if args.gpus != 1:
+            sys.exit("bench.py: this build runs on one GPU only")
+        train_backward(args)
+        return
     if args.copy_calibration:
         copy_calibration()
         return

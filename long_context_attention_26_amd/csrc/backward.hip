@@ -12,8 +12,8 @@
 // attn_bwd_kernel takes one query token per block; its 4 waves split the key list.  Lanes
 // own channels (c = lane + 64 t), so a key's K and V rows are read, and its dk/dv rows
 // added, as whole coalesced rows.  The 2H dot products of a key (q_h.k and dout_h.v) are
-// summed over the 64 lanes in one batched butterfly: every exchange step halves the
-// values a lane keeps, so 2H values cost about 2H shuffles instead of 12 H.
+// summed over the 64 lanes together: two half-swapping lane permutes leave each 16-lane group
+// a quarter of the values, summed over 4 lanes, and DPP row rotations finish the sums.
 //
 // Pooling: y_j = sum_i alpha_i x_{jr+i} with alpha = softmax(omega) gives
 //   dx_{jr+i} += alpha_i dy_j,   domega_k += alpha_k (g_k - sum_i alpha_i g_i),
@@ -48,29 +48,32 @@ struct AttnBwdDev {
   int64_t dr_bstride;
 };
 
-// Sums each of the N values v[0..N) over the 64 lanes of the wave.  Each step pairs value i
-// with value i + n/2: the lane with the step's lane bit set keeps the upper one, its partner
-// the lower one, and each adds what the other sends.  With N <= 64 the lane ends holding
-// value j = lane >> (6 - log2 N) in v[0]; with N = 128, values 2 lane and 2 lane + 1 in
-// v[0], v[1].
+// Sums each of the N values v[0..N) over the 64 lanes of the wave with no lane-dependent
+// selection: v_permlane32_swap exchanges lanes 32..63 of one register with lanes 0..31 of
+// another, so adding the two results sums value i over lanes l, l^32 in the lower half-wave
+// and value i + N/2 in the upper one; v_permlane16_swap does the same for 16-lane rows; the
+// rest is summed within each 16-lane row by DPP rotations of 8, 4, 2 and 1.  Afterwards
+// lane group g = lane / 16 holds the full sums of values g*N/4 .. g*N/4 + N/4 - 1 in u.
 template <int N>
-__device__ __forceinline__ void wave_reduce_scatter(float (&v)[N], int lane) {
-  constexpr int R = N >= 64 ? 6 : (N >= 32 ? 5 : (N >= 16 ? 4 : (N >= 8 ? 3 : (N >= 4 ? 2 : 1))));
+__device__ __forceinline__ void wave_sum_quarters(const float (&v)[N], float (&u)[N / 4]) {
+  float w[N / 2];
 #pragma unroll
-  for (int st = 0; st < R; ++st) {
-    const int delta = 32 >> st;
-    const bool up = (lane & delta) != 0;
-    const int half = (N >> (st + 1));
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float keep = up ? v[i + half] : v[i];
-      const float send = up ? v[i] : v[i + half];
-      v[i] = keep + __shfl_xor(send, delta, kWave);
-    }
+  for (int i = 0; i < N / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[i + N / 2]), false, false);
+    w[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  if constexpr (N <= 64) {
 #pragma unroll
-    for (int delta = 32 >> R; delta >= 1; delta >>= 1) v[0] += __shfl_xor(v[0], delta, kWave);
+  for (int i = 0; i < N / 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[i]),
+                                                    __float_as_uint(w[i + N / 4]), false, false);
+    float x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    // DPP row_ror:8, 4, 2, 1 (controls 0x128, 0x124, 0x122, 0x121)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+    u[i] = x;
   }
 }
 
@@ -82,17 +85,17 @@ __device__ __forceinline__ float bcast(float v, int src_lane) {
 template <bool CSA, bool BF16, int HH, int CPL>
 __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdDev G) {
   constexpr int NV = 2 * HH;                     // q.k and dout.v per head
-  constexpr int R = NV >= 64 ? 6 : (NV >= 32 ? 5 : (NV >= 16 ? 4 : 3));
+  constexpr int HQ = HH / 4;                     // heads per 16-lane group after the sums
   __shared__ float s_dq[4096];
+  __shared__ float s_dt[HH];
   const AttnDev& A = G.A;
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = A.H, d = A.d;
   const RowKeys r = row_keys<CSA>(A, row);
 
-  // this lane's channels of q, dout and o for every head; per-head D_h = dout_h . o_h
+  // this lane's channels of q and dout for every head; D_h = dout_h . o_h per head
   float qv[HH][CPL], dov[HH][CPL], dqv[HH][CPL];
-  float dterm[HH];
   const int64_t hb = static_cast<int64_t>(row) * H * d;
 #pragma unroll
   for (int h = 0; h < HH; ++h) {
@@ -106,17 +109,19 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdDev G) {
       dqv[h][t] = 0.0f;
       if (ok) part = fmaf(dov[h][t], G.out[hb + h * d + c], part);
     }
-    dterm[h] = wave_sum(part);
+    part = wave_sum(part);
+    if (threadIdx.x == 0) s_dt[h] = part;
   }
-  // the head whose (q.k, dout.v) pair this lane holds after the reduction, and its terms
-  const int my_h = NV <= 64 ? (lane >> (7 - R)) : lane;
-  float my_lse = -INFINITY, my_dt = 0.0f;
+  __syncthreads();
+  // the heads whose sums this lane's group holds: g*HQ + m
+  const int g = lane >> 4;
+  float my_lse[HQ], my_dt[HQ];
 #pragma unroll
-  for (int h = 0; h < HH; ++h) {
-    if (h == my_h && h < H) {
-      my_lse = G.lse[static_cast<int64_t>(row) * H + h];
-      my_dt = dterm[h] - (G.dlse ? G.dlse[static_cast<int64_t>(row) * H + h] : 0.0f);
-    }
+  for (int m = 0; m < HQ; ++m) {
+    const int h = g * HQ + m;
+    const int64_t li = static_cast<int64_t>(row) * H + h;
+    my_lse[m] = h < H ? G.lse[li] : -INFINITY;
+    my_dt[m] = h < H ? s_dt[h] - (G.dlse ? G.dlse[li] : 0.0f) : 0.0f;
   }
 
   for (int pos = wave; pos < r.L; pos += 4) {
@@ -135,38 +140,32 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdDev G) {
     float v[NV];
 #pragma unroll
     for (int h = 0; h < HH; ++h) {
-      float s = 0.0f, dp = 0.0f;
+      float sk = 0.0f, dp = 0.0f;
 #pragma unroll
       for (int t = 0; t < CPL; ++t) {
-        s = fmaf(qv[h][t], kv[t], s);
+        sk = fmaf(qv[h][t], kv[t], sk);
         dp = fmaf(dov[h][t], vv[t], dp);
       }
-      v[2 * h] = s;
+      v[2 * h] = sk;
       v[2 * h + 1] = dp;
     }
-    wave_reduce_scatter<NV>(v, lane);
-    float s_my, dp_my;
-    if constexpr (NV <= 64) {
-      // lanes of value 2h hold q.k, lanes of value 2h + 1 dout.v: swap to have both
-      const float other = __shfl_xor(v[0], 1 << (6 - R), kWave);
-      const bool odd = ((lane >> (6 - R)) & 1) != 0;
-      s_my = odd ? other : v[0];
-      dp_my = odd ? v[0] : other;
-    } else {
-      s_my = v[0];
-      dp_my = v[1];
+    float u[NV / 4];
+    wave_sum_quarters<NV>(v, u);
+    float p[HQ], ds[HQ];
+#pragma unroll
+    for (int m = 0; m < HQ; ++m) {
+      p[m] = my_lse[m] == -INFINITY ? 0.0f : __expf(A.scale * u[2 * m] - my_lse[m]);
+      ds[m] = p[m] * (u[2 * m + 1] - my_dt[m]);
     }
-    const float p = my_lse == -INFINITY ? 0.0f : __expf(A.scale * s_my - my_lse);
-    const float ds = p * (dp_my - my_dt);
-    // every head's P and dS, broadcast from the lane that holds it
+    // every head's P and dS, read from the first lane of the group that holds it
     float dk[CPL], dv[CPL];
 #pragma unroll
     for (int t = 0; t < CPL; ++t) dk[t] = dv[t] = 0.0f;
 #pragma unroll
     for (int h = 0; h < HH; ++h) {
       if (h >= H) break;
-      const int src = NV <= 64 ? (h << (7 - R)) : h;
-      const float ph = bcast(p, src), dsh = bcast(ds, src);
+      const float ph = bcast(p[h % HQ], 16 * (h / HQ));
+      const float dsh = bcast(ds[h % HQ], 16 * (h / HQ));
 #pragma unroll
       for (int t = 0; t < CPL; ++t) {
         dk[t] = fmaf(dsh, qv[h][t], dk[t]);
@@ -214,6 +213,221 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdDev G) {
   for (int i = threadIdx.x; i < H * d; i += 256) G.dq[hb + i] = A.scale * s_dq[i];
 }
 
+
+// ------------------------------------------------------------------ matrix-core path (bf16, 16 x 128)
+
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma32(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const u32x2& a, const u32x2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Backward of one query token's 16 heads over its key list, 32 keys per wave step, on the
+// matrix cores (bf16 operands, fp32 accumulation).  Lane (col = lane % 16, g = lane / 16).
+// The logits and dout.v products are formed twice, as S^T = K Q^T (lane = head col, keys
+// 4g + i of each 16-key tile) and as S = Q K^T (lane = key col, heads 4g + i), so that every
+// later product finds its operand in the accumulator layout it already has:
+//   dQ^T += K^T dS^T  (16x16x32, the forward's V^T P^T form with K slices for V),
+//   dK    = dS^T Q,  dV = P^T dout  (16x16x16 over the 16 heads, one per 16-channel tile),
+// and the dK / dV tiles go to memory with atomics, 4 rows x 16 channels per instruction.
+template <bool CSA>
+__global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
+  __shared__ float s_dq[4][16][129];
+  __shared__ float s_lse2[16];
+  __shared__ float s_dt[16];
+  constexpr float kLog2e = 1.4426950408889634f;
+  const AttnDev& A = G.A;
+  const int row = blockIdx.x;
+  const RowKeys r = row_keys<CSA>(A, row);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, g = lane >> 4;
+  const int64_t hb = static_cast<int64_t>(row) * 2048;
+  const uint16_t* q16 = static_cast<const uint16_t*>(A.q) + hb;
+  const float* dout = G.dout + hb;
+
+  // per-head terms: D_h = dout_h . o_h - dlse_h, and lse_h in base 2 (16 threads per head)
+  {
+    const int h = threadIdx.x >> 4, c0 = (threadIdx.x & 15) * 8;
+    float part = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part = fmaf(dout[h * 128 + c0 + e], G.out[hb + h * 128 + c0 + e], part);
+    part += __shfl_xor(part, 8, kWave);
+    part += __shfl_xor(part, 4, kWave);
+    part += __shfl_xor(part, 2, kWave);
+    part += __shfl_xor(part, 1, kWave);
+    if ((threadIdx.x & 15) == 0) {
+      const int64_t li = static_cast<int64_t>(row) * 16 + h;
+      s_dt[h] = part - (G.dlse ? G.dlse[li] : 0.0f);
+      s_lse2[h] = G.lse[li] * kLog2e;
+    }
+  }
+  __syncthreads();
+
+  // q and dout (rounded to bf16) as operands: rows of head col at channels 32s + 8g (16x16x32)
+  // and heads 4g..4g+3 at channel 16c + col (16x16x16 B operand)
+  u32x4 qB[4], doB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qB[s] = *reinterpret_cast<const u32x4*>(q16 + col * 128 + 32 * s + 8 * g);
+    const float* dr = dout + col * 128 + 32 * s + 8 * g;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) doB[s][m] = pack_bf16x2(dr[2 * m], dr[2 * m + 1]);
+  }
+  u32x2 qT[8], doT[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int h0 = 4 * g + 2 * m, ch = 16 * c + col;
+      qT[c][m] = static_cast<uint32_t>(q16[h0 * 128 + ch]) |
+                 (static_cast<uint32_t>(q16[(h0 + 1) * 128 + ch]) << 16);
+      doT[c][m] = pack_bf16x2(dout[h0 * 128 + ch], dout[(h0 + 1) * 128 + ch]);
+    }
+  }
+  const float lse2_col = s_lse2[col], dt_col = s_dt[col];
+  float lse2_g[4], dt_g[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lse2_g[i] = s_lse2[4 * g + i];
+    dt_g[i] = s_dt[4 * g + i];
+  }
+  const float sl2 = A.scale * kLog2e;
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0, 0, 0, 0};
+
+  for (int base = wave * 32; base < r.L; base += 128) {
+    // key codes: operand rows base + 16t + col, and keys base + 16(j/4) + 4g + j%4
+    int ca[2], cs[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int pos = base + 16 * t + col;
+      ca[t] = pos < r.L ? key_code<CSA>(A, r, row, pos) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int pos = base + 16 * (j >> 2) + 4 * g + (j & 3);
+      cs[j] = pos < r.L ? key_code<CSA>(A, r, row, pos) : -1;
+    }
+    u32x4 ka[2][4], va[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (ca[t] != -1) {
+        const uint16_t* kr = key_row<uint16_t>(A, r.b, ca[t], false);
+        const uint16_t* vr = key_row<uint16_t>(A, r.b, ca[t], true);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          ka[t][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g);
+          va[t][s] = *reinterpret_cast<const u32x4*>(vr + 32 * s + 8 * g);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[t][s] = va[t][s] = u32x4{0, 0, 0, 0};
+      }
+    }
+    u32x4 ks[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ks[j] = cs[j] != -1 ? *reinterpret_cast<const u32x4*>(key_row<uint16_t>(A, r.b, cs[j], false) + 8 * col)
+                          : u32x4{0, 0, 0, 0};
+
+    // ---- lane = head: S^T and dP^T, dS^T for keys 16(j/4) + 4g + j%4
+    f32x4 st[2], dpt[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = dpt[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        st[t] = mma32(ka[t][s], qB[s], st[t]);
+        dpt[t] = mma32(va[t][s], doB[s], dpt[t]);
+      }
+    }
+    float dsT[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = cs[j] != -1 ? exp2f(st[j >> 2][j & 3] * sl2 - lse2_col) : 0.0f;
+      dsT[j] = pj * (dpt[j >> 2][j & 3] - dt_col);
+    }
+    u32x4 dsB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dsB[m] = pack_bf16x2(dsT[2 * m], dsT[2 * m + 1]);
+    // dQ^T tiles: channel 8 col + ct of the K slices, as the forward's V^T
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const uint32_t sel = (ct & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 kA;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        kA[m] = __builtin_amdgcn_perm(ks[2 * m + 1][ct >> 1], ks[2 * m][ct >> 1], sel);
+      acc[ct] = mma32(kA, dsB, acc[ct]);
+    }
+
+    // ---- lane = key: S and dP of key base + 16t + col for heads 4g + i; dK, dV tiles
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 sk = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sk = mma32(qB[s], ka[t][s], sk);
+        dp = mma32(doB[s], va[t][s], dp);
+      }
+      float pk[4], dsk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pk[i] = ca[t] != -1 ? exp2f(sk[i] * sl2 - lse2_g[i]) : 0.0f;
+        dsk[i] = pk[i] * (dp[i] - dt_g[i]);
+      }
+      const u32x2 pA = {pack_bf16x2(pk[0], pk[1]), pack_bf16x2(pk[2], pk[3])};
+      const u32x2 dsA = {pack_bf16x2(dsk[0], dsk[1]), pack_bf16x2(dsk[2], dsk[3])};
+      float* dkr[4];
+      float* dvr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int code = cs[4 * t + i];
+        dkr[i] = dvr[i] = nullptr;
+        if (code >= 0) {
+          const int64_t o = r.b * G.dc_bstride + static_cast<int64_t>(code) * 128;
+          dkr[i] = G.dkc + o;
+          dvr[i] = G.dvc + o;
+        } else if (code != -1) {
+          const int64_t o = r.b * G.dr_bstride + static_cast<int64_t>(-code - 2) * 128;
+          dkr[i] = G.dkr + o;
+          dvr[i] = G.dvr + o;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 dkt = mma16(dsA, qT[c], f32x4{0, 0, 0, 0});
+        const f32x4 dvt = mma16(pA, doT[c], f32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (dkr[i]) {
+            unsafeAtomicAdd(dkr[i] + 16 * c + col, A.scale * dkt[i]);
+            unsafeAtomicAdd(dvr[i] + 16 * c + col, dvt[i]);
+          }
+        }
+      }
+    }
+  }
+
+  // dQ: lane holds dQ^T[channel 32g + 8i + t][head col] = acc[t][i]; the 4 waves add up
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s_dq[wave][col][32 * g + 8 * i + t] = acc[t][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 2048; e += 256) {
+    const int h = e >> 7, c = e & 127;
+    G.dq[hb + e] = A.scale * (((s_dq[0][h][c] + s_dq[1][h][c]) + s_dq[2][h][c]) + s_dq[3][h][c]);
+  }
+}
 
 // ------------------------------------------------------------------ pooling backward
 
@@ -348,6 +562,11 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
   if (rows == 0) return hipSuccess;
   const int hh = bwd_heads(a.H), cpl = bwd_cpl(a.d);
   const bool bf = a.kv_dtype == 1;
+  if (bf && a.H == 16 && a.d == 128) {          // the matrix-core path
+    if (csa) attn_bwd_mfma_kernel<true><<<rows, 256, 0, s>>>(G);
+    else attn_bwd_mfma_kernel<false><<<rows, 256, 0, s>>>(G);
+    return hipGetLastError();
+  }
   if (csa) return bf ? launch_bwd_typed<true, true>(G, rows, hh, cpl, s)
                      : launch_bwd_typed<true, false>(G, rows, hh, cpl, s);
   return bf ? launch_bwd_typed<false, true>(G, rows, hh, cpl, s)

@@ -2,7 +2,8 @@
 pooling against the oracle's (which the CPU pins tie to finite differences of the forward).
 The backward takes the forward's output and log-sum-exp; the stage tests hand it the oracle's
 own (rounded to fp32), so only the backward's arithmetic is measured: fp32 sums of exact
-bf16/fp32 inputs, checked to 2e-5 of each gradient's largest magnitude.  One case chains the
+bf16/fp32 inputs, checked to 2e-5 of each gradient's largest magnitude (1e-2 on the
+matrix-core path, whose products take bf16 operands).  One case chains the
 GPU forward into the GPU backward, as a training step does."""
 import math
 
@@ -34,13 +35,21 @@ def _tdt(dt):
     return torch.float32 if dt == "f32" else torch.bfloat16
 
 
+def _tol(dt, Hh, d):
+    """bf16 with 16 heads x 128 runs on the matrix cores, whose products take dS, P and
+    dout rounded to bf16 (2^-9 relative each); every other shape sums in fp32."""
+    return 1e-2 if (dt == "bf16" and Hh == 16 and d == 128) else 2e-5
+
+
 CSA_CASES = [
     dict(dt="f32", H=1, d=64, N=1024, k=64, n_win=128, Nq=1, B=1, pos0=4095, dlse=False),
     # chunked rows: windows of neighbouring queries overlap, selections repeat entries
     dict(dt="bf16", H=16, d=128, N=800, k=256, n_win=128, Nq=8, B=2, pos0=3190, dlse=True),
     # k above the visible count (padding), window clipped at position 0
     dict(dt="bf16", H=4, d=64, N=40, k=64, n_win=128, Nq=3, B=1, pos0=60, dlse=True),
-    # head / channel tilings: 32 x 128, 8 x 256, 64 x 64, 5 heads (rounded up to 16)
+    # fp32 16 x 128 (plain-ALU path); head / channel tilings: 32 x 128, 8 x 256, 64 x 64,
+    # 5 heads (rounded up to 16)
+    dict(dt="f32", H=16, d=128, N=500, k=200, n_win=128, Nq=4, B=2, pos0=1900, dlse=True),
     dict(dt="f32", H=32, d=128, N=300, k=100, n_win=64, Nq=2, B=1, pos0=1300, dlse=True),
     dict(dt="bf16", H=8, d=256, N=200, k=50, n_win=32, Nq=2, B=2, pos0=900, dlse=False),
     dict(dt="f32", H=64, d=64, N=100, k=30, n_win=16, Nq=1, B=1, pos0=420, dlse=True),
@@ -104,7 +113,7 @@ def test_csa_backward(H, gpu, case):
                           dev(dout, torch.float32, gpu), dq, dKc, dVc, dKr, dVr,
                           dlse=None if dlse is None else dev(dlse, torch.float32, gpu))
     torch.cuda.synchronize()
-    tol = 2e-5
+    tol = _tol(dt, Hh, d)
     _rel_close(f64(dq), dq_ref, tol, "dq")
     _rel_close(f64(dKc) - base[0], dKc_ref, tol, "dKc")
     _rel_close(f64(dVc) - base[1], dVc_ref, tol, "dVc")
@@ -152,9 +161,10 @@ def test_hca_backward(H, gpu, case):
                          dev(l_ref, torch.float32, gpu), dev(dout, torch.float32, gpu), dq, dK,
                          dV, dlse=None if dlse is None else dev(dlse, torch.float32, gpu))
     torch.cuda.synchronize()
-    _rel_close(f64(dq), dq_ref, 2e-5, "dq")
-    _rel_close(f64(dK), dK_ref, 2e-5, "dKh")
-    _rel_close(f64(dV), dV_ref, 2e-5, "dVh")
+    tol = _tol(dt, Hh, d)
+    _rel_close(f64(dq), dq_ref, tol, "dq")
+    _rel_close(f64(dK), dK_ref, tol, "dKh")
+    _rel_close(f64(dV), dV_ref, tol, "dVh")
 
 
 @pytest.mark.parametrize("ratio,T,D,B,io", [(4, 1003, 64, 2, "bf16"), (128, 1000, 128, 1, "f32"),
