@@ -38,7 +38,8 @@ readings taken here (each is marked READING in the function that uses it):
   R7  MXFP4 (OCP Microscaling v1.0, e2m1 elements, e8m0 scale per 32 elements): scale
       exponent floor(log2(amax)) - 2, element = round-to-nearest-even of v / 2^e onto the
       e2m1 grid, saturating at +-6; amax = 0 gives exponent -127 and zero elements.
-  R8  training (the sparse attention is trained from the 64K stage of the length
+  (R8-R10 -- heads and scale, positions, layer order -- concern the callers, not this module.)
+  R11 training (the sparse attention is trained from the 64K stage of the length
       curriculum [LH 八.2]): the gradients are those of the forward functions above, the
       exact derivative of softmax attention and of the pooled sum; the selection (top-k)
       is held fixed (not differentiated) and a rounding to the storage type passes the
@@ -309,7 +310,7 @@ def log2_floor(x):
     return math.frexp(x)[1] - 1
 
 
-# --------------------------------------------------------------------------- backward (READING R8)
+# --------------------------------------------------------------------------- backward (READING R11)
 
 def attend_backward(q, keys, values, scale, dout, dlse=None):
     """Gradients of attend(q, keys, values, scale) for the loss sum(dout * o) +
@@ -336,7 +337,7 @@ def attend_backward(q, keys, values, scale, dout, dlse=None):
 
 def csa_attention_backward(q, Kc, Vc, idx, K_raw, V_raw, raw_pos0, p, n_win, scale, dout,
                            dlse=None, ratio=CSA_RATIO):
-    """Gradients of csa_attention for one query token (READINGS R4, R6, R8): dq [H, d], and
+    """Gradients of csa_attention for one query token (READINGS R4, R6, R11): dq [H, d], and
     the contributions to the compressed entries dKc, dVc (shape of Kc) and to the raw rows
     dK_raw, dV_raw (shape of K_raw), each key's gradient added to the row it came from."""
     n_vis = visible_entries(p, Kc.shape[0], ratio)
@@ -357,7 +358,7 @@ def csa_attention_backward(q, Kc, Vc, idx, K_raw, V_raw, raw_pos0, p, n_win, sca
 
 
 def hca_attention_backward(q, Kh, Vh, p, scale, dout, dlse=None, ratio=HCA_RATIO):
-    """Gradients of hca_attention for one query token (READINGS R5, R6, R8): dq, dKh, dVh
+    """Gradients of hca_attention for one query token (READINGS R5, R6, R11): dq, dKh, dVh
     (the entries past the visible count get zero)."""
     n = visible_entries(p, Kh.shape[0], ratio)
     dq, dk, dv = attend_backward(q, Kh[:n], Vh[:n], scale, dout, dlse)
@@ -369,7 +370,7 @@ def hca_attention_backward(q, Kh, Vh, p, scale, dout, dlse=None, ratio=HCA_RATIO
 
 
 def compress_backward(x, omega, ratio, dy):
-    """Gradients of sum(dy * compress(x, omega, ratio)) (READINGS R1, R8): dx [T, D] (token
+    """Gradients of sum(dy * compress(x, omega, ratio)) (READINGS R1, R11): dx [T, D] (token
     j*ratio + i gets alpha_i dy[j]; the unpooled tail gets zero) and domega [ratio]
     (domega_k = alpha_k (g_k - sum_i alpha_i g_i) with g_i = sum_j dy[j] . x[j*ratio + i],
     the softmax's derivative)."""
