@@ -276,6 +276,26 @@ int hcsa_hca_dense_attn(const void *q, const void *kh, const void *vh, int64_t h
                         hcsa_stream stream);
 
 /*
+ * CSA sparse attention and HCA dense attention of the same query tokens in one call
+ * [Lighthouse section 八 item 3: CSA and HCA layers over the same tokens]: the arguments of
+ * hcsa_csa_sparse_attn (kc ... ratio, out_c, lse_c) and of hcsa_hca_dense_attn (kh, vh,
+ * h_bstride, N_h, ratio_h, out_h, lse_h), sharing q, positions, pages, dtype, shapes and
+ * scale; same results as the two calls.  For one-token decode in bf16 with 16 heads x 128,
+ * both attentions run as one launch (their blocks side by side) and their split merges as
+ * one more; other shapes run the two calls' kernels in turn.
+ * workspace: at least hcsa_csa_hca_attn_workspace_size(B, Nq, H, d, k, n_win, N_h) bytes.
+ */
+size_t hcsa_csa_hca_attn_workspace_size(int B, int Nq, int H, int d, int k, int n_win, int N_h);
+int hcsa_csa_hca_attn(const void *q, const void *kc, const void *vc, int64_t c_bstride, int N,
+                      const int32_t *topk_idx, int k, const void *k_raw, const void *v_raw,
+                      int64_t raw_bstride, int64_t T_raw, int64_t raw_pos0, int n_win,
+                      int ratio, const void *kh, const void *vh, int64_t h_bstride, int N_h,
+                      int ratio_h, int64_t pos0, const int64_t *seq_pos,
+                      const hcsa_pages *pages, int kv_dtype, int B, int Nq, int H, int d,
+                      float scale, float *out_c, float *lse_c, float *out_h, float *lse_h,
+                      void *workspace, size_t ws_bytes, hcsa_stream stream);
+
+/*
  * Backward (training) [Lighthouse section 八 item 2: the sparse attention is trained from
  * the 64K stage of the length curriculum; item 3 for the attention itself].  Gradients of
  * the loss sum(dout * out) + sum(dlse * lse) of the forward call with the same arguments;

@@ -443,11 +443,11 @@ size_t hcsa_hca_dense_attn_workspace_size(int B, int Nq, int H, int d, int N) {
   return a > b ? a : b;
 }
 
-int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h_bstride,
-                        int N, int ratio, int64_t pos0, const int64_t* seq_pos,
-                        const hcsa_pages* pages, int kv_dtype, int B, int Nq, int H, int d,
-                        float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
-                        hcsa_stream stream) {
+// Arguments of HCA attention, checked on the host.
+static int check_hca(const void* q, const void* kh, const void* vh, int64_t h_bstride, int N,
+                     int ratio, int64_t pos0, const int64_t* seq_pos, const hcsa_pages* pages,
+                     int kv_dtype, int B, int Nq, int H, int d, float scale, const float* out,
+                     const float* lse) {
   int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
@@ -462,6 +462,17 @@ int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h
     if (!is_paged(pages) && B > 1 && h_bstride < static_cast<int64_t>(N) * d)
       return fail(HCSA_EINVAL, "h_bstride < N*d");
   }
+  return HCSA_OK;
+}
+
+int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h_bstride,
+                        int N, int ratio, int64_t pos0, const int64_t* seq_pos,
+                        const hcsa_pages* pages, int kv_dtype, int B, int Nq, int H, int d,
+                        float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                        hcsa_stream stream) {
+  int rc = check_hca(q, kh, vh, h_bstride, N, ratio, pos0, seq_pos, pages, kv_dtype, B, Nq, H,
+                     d, scale, out, lse);
+  if (rc) return rc;
   const hcsa::AttnPlan plan = hcsa::plan_attention(false, kv_dtype, B, Nq, H, d, N);
   rc = check_ws(workspace, ws_bytes, plan.total_bytes);
   if (rc) return rc;
@@ -474,6 +485,53 @@ int hcsa_hca_dense_attn(const void* q, const void* kh, const void* vh, int64_t h
   a.out = out; a.lse = lse;
   return hip_status(hcsa::launch_attention(false, a, plan, workspace, static_cast<hipStream_t>(stream)),
                     "hcsa_hca_dense_attn");
+}
+
+// ------------------------------------------------------------------ CSA + HCA in one call
+
+size_t hcsa_csa_hca_attn_workspace_size(int B, int Nq, int H, int d, int k, int n_win, int N_h) {
+  const size_t c = hcsa_csa_sparse_attn_workspace_size(B, Nq, H, d, k, n_win);
+  const size_t h = hcsa_hca_dense_attn_workspace_size(B, Nq, H, d, N_h);
+  if ((B >= 1 && Nq >= 1 && H >= 1 && d >= 1) == false) return 0;
+  return hcsa::align256(c) + h;
+}
+
+int hcsa_csa_hca_attn(const void* q, const void* kc, const void* vc, int64_t c_bstride, int N,
+                      const int32_t* topk_idx, int k, const void* k_raw, const void* v_raw,
+                      int64_t raw_bstride, int64_t T_raw, int64_t raw_pos0, int n_win,
+                      int ratio, const void* kh, const void* vh, int64_t h_bstride, int N_h,
+                      int ratio_h, int64_t pos0, const int64_t* seq_pos,
+                      const hcsa_pages* pages, int kv_dtype, int B, int Nq, int H, int d,
+                      float scale, float* out_c, float* lse_c, float* out_h, float* lse_h,
+                      void* workspace, size_t ws_bytes, hcsa_stream stream) {
+  int rc = check_csa(q, kc, vc, c_bstride, N, topk_idx, k, k_raw, v_raw, raw_bstride, T_raw,
+                     raw_pos0, n_win, ratio, pos0, seq_pos, pages, kv_dtype, B, Nq, H, d, scale,
+                     out_c, lse_c);
+  if (rc) return rc;
+  rc = check_hca(q, kh, vh, h_bstride, N_h, ratio_h, pos0, seq_pos, pages, kv_dtype, B, Nq, H,
+                 d, scale, out_h, lse_h);
+  if (rc) return rc;
+  const hcsa::AttnPlan pc =
+      hcsa::plan_attention(true, kv_dtype, B, Nq, H, d, attn_max_len_csa(k, n_win));
+  const hcsa::AttnPlan ph = hcsa::plan_attention(false, kv_dtype, B, Nq, H, d, N_h);
+  rc = check_ws(workspace, ws_bytes, hcsa::align256(pc.total_bytes) + ph.total_bytes);
+  if (rc) return rc;
+  hcsa::AttnArgs c{};
+  c.q = q; c.kc = kc; c.vc = vc; c.c_bstride = c_bstride; c.N = N > 0 ? N : 0; c.ratio = ratio;
+  c.idx = topk_idx; c.k = k; c.k_raw = k_raw; c.v_raw = v_raw; c.raw_bstride = raw_bstride;
+  c.T_raw = T_raw; c.raw_pos0 = raw_pos0; c.n_win = n_win; c.pos0 = pos0; c.seq_pos = seq_pos;
+  c.block_table = page_table(pages); c.table_stride = page_stride(pages);
+  c.raw_ring = raw_ring(pages);
+  c.kv_dtype = kv_dtype; c.B = B; c.Nq = Nq; c.H = H; c.d = d; c.scale = scale;
+  c.out = out_c; c.lse = lse_c;
+  hcsa::AttnArgs h{};
+  h.q = q; h.kc = kh; h.vc = vh; h.c_bstride = h_bstride; h.N = N_h; h.ratio = ratio_h;
+  h.pos0 = pos0; h.seq_pos = seq_pos;
+  h.block_table = page_table(pages); h.table_stride = page_stride(pages);
+  h.kv_dtype = kv_dtype; h.B = B; h.Nq = Nq; h.H = H; h.d = d; h.scale = scale;
+  h.out = out_h; h.lse = lse_h;
+  return hip_status(hcsa::launch_csa_hca(c, pc, h, ph, workspace, static_cast<hipStream_t>(stream)),
+                    "hcsa_csa_hca_attn");
 }
 
 // ------------------------------------------------------------------ backward (training)

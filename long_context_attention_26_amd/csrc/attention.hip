@@ -220,15 +220,11 @@ __device__ __forceinline__ void combine_waves(const AttnDev& A, const f32x4 (&ac
   }
 }
 
-// grid: (splits, rows); block 256 (4 waves).
+// One (split, row) block of the MFMA attention; LDS passed in by the kernel.
 template <bool CSA>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
-  __shared__ int s_code[kMfmaMaxChunk];
-  __shared__ float s_o[4][16][129];
-  __shared__ float s_ml[4][2][16];
-
-  const int row = blockIdx.y;
-  const int split = blockIdx.x;
+__device__ __forceinline__ void attn_mfma_block(const AttnDev& A, int split, int row,
+                                                int* s_code, float (*s_o)[16][129],
+                                                float (*s_ml)[2][16]) {
   const RowKeys r = row_keys<CSA>(A, row);
   const int k0 = split * A.chunk;
   const int cnt = max(0, min(A.chunk, r.L - k0));
@@ -290,17 +286,23 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
   combine_waves(A, acc, m_run, l_run, s_o, s_ml, split, row);
 }
 
+// grid: (splits, rows); block 256 (4 waves).
+template <bool CSA>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
+  __shared__ int s_code[kMfmaMaxChunk];
+  __shared__ float s_o[4][16][129];
+  __shared__ float s_ml[4][2][16];
+  attn_mfma_block<CSA>(A, blockIdx.x, blockIdx.y, s_code, s_o, s_ml);
+}
+
 // ------------------------------------------------------------------ HCA, one token per sequence
 
 // Decode HCA: the visible entries 0..nv-1 are contiguous, so no key list is built; each of
 // a block's 4 waves streams its own contiguous run of the block's chunk, 32 entries a step,
 // the next step's K and V rows loaded while the current step is computed.
-// grid: (splits, rows); block 256.
 template <bool PAGED>
-__global__ __launch_bounds__(256, 2) void hca_decode_kernel(AttnDev A) {
-  __shared__ float s_o[4][16][129];
-  __shared__ float s_ml[4][2][16];
-  const int row = blockIdx.y, split = blockIdx.x;
+__device__ __forceinline__ void hca_decode_block(const AttnDev& A, int split, int row,
+                                                 float (*s_o)[16][129], float (*s_ml)[2][16]) {
   const RowKeys r = row_keys<false>(A, row);       // r.L = visible entries
   const int k0 = split * A.chunk;
   const int cnt = max(0, min(A.chunk, r.L - k0));
@@ -355,6 +357,28 @@ __global__ __launch_bounds__(256, 2) void hca_decode_kernel(AttnDev A) {
     attend_step(kaB, vvB, okB, qB, acc, m_run, l_run, sl2);
   }
   combine_waves(A, acc, m_run, l_run, s_o, s_ml, split, row);
+}
+
+// grid: (splits, rows); block 256.
+template <bool PAGED>
+__global__ __launch_bounds__(256, 2) void hca_decode_kernel(AttnDev A) {
+  __shared__ float s_o[4][16][129];
+  __shared__ float s_ml[4][2][16];
+  hca_decode_block<PAGED>(A, blockIdx.x, blockIdx.y, s_o, s_ml);
+}
+
+// CSA and HCA attention of the same decode tokens in one launch: blocks 0 .. nH-1 are the
+// HCA (split, row) blocks (the long streaming ones, started first), the rest the CSA blocks,
+// so the CSA gathers run beside the HCA stream instead of after it.  grid: nH + nC; block 256.
+template <bool PAGED>
+__global__ __launch_bounds__(256, 2) void csa_hca_decode_kernel(AttnDev C, AttnDev Hd) {
+  __shared__ int s_code[kMfmaMaxChunk];
+  __shared__ float s_o[4][16][129];
+  __shared__ float s_ml[4][2][16];
+  const int nH = Hd.splits * Hd.rows;
+  const int b = blockIdx.x;
+  if (b < nH) hca_decode_block<PAGED>(Hd, b % Hd.splits, b / Hd.splits, s_o, s_ml);
+  else attn_mfma_block<true>(C, (b - nH) % C.splits, (b - nH) / C.splits, s_code, s_o, s_ml);
 }
 
 // ------------------------------------------------------------------ HCA, many query tokens
@@ -544,14 +568,11 @@ constexpr int kMergeRegSplits = 16;
 // issues all of its loads -- the splits' log-sum-exps and its channel's partial outputs --
 // before using any, so the merge costs one memory latency; beyond that the split weights
 // are formed once in LDS and each thread sums its channel over the splits.
-__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ part_o,
-                                                        const float* __restrict__ part_l,
-                                                        int splits, int rows, int H, int d,
-                                                        float* __restrict__ out,
-                                                        float* __restrict__ lse) {
-  __shared__ float s_w[1024];
-  __shared__ float s_red[2];
-  const int h = blockIdx.x, row = blockIdx.y;
+__device__ __forceinline__ void lse_merge_row(const float* __restrict__ part_o,
+                                              const float* __restrict__ part_l, int splits,
+                                              int rows, int H, int d, float* __restrict__ out,
+                                              float* __restrict__ lse, int h, int row,
+                                              float* s_w, float* s_red) {
   const int64_t lstride = static_cast<int64_t>(rows) * H;
   const int64_t ostride = static_cast<int64_t>(rows) * H * d;
   const float* pl = part_l + static_cast<int64_t>(row) * H + h;
@@ -630,6 +651,35 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   }
 }
 
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_l,
+                                                        int splits, int rows, int H, int d,
+                                                        float* __restrict__ out,
+                                                        float* __restrict__ lse) {
+  __shared__ float s_w[1024];
+  __shared__ float s_red[2];
+  lse_merge_row(part_o, part_l, splits, rows, H, d, out, lse, blockIdx.x, blockIdx.y, s_w, s_red);
+}
+
+// The merges of two attention calls in one launch: rows 0 .. a.rows-1 of grid.y merge the
+// first call's splits, the rest the second's.  grid: (H, rows_a + rows_b); block d threads.
+struct MergeJob {
+  const float* part_o;
+  const float* part_l;
+  int splits, rows;
+  float* out;
+  float* lse;
+};
+__global__ __launch_bounds__(256) void lse_merge2_kernel(MergeJob a, MergeJob b, int H, int d) {
+  __shared__ float s_w[1024];
+  __shared__ float s_red[2];
+  const int y = blockIdx.y;
+  const MergeJob& m = y < a.rows ? a : b;
+  const int row = y < a.rows ? y : y - a.rows;
+  lse_merge_row(m.part_o, m.part_l, m.splits, m.rows, H, d, m.out, m.lse, blockIdx.x, row,
+                s_w, s_red);
+}
+
 }  // namespace
 
 
@@ -673,25 +723,30 @@ AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int
   return p;
 }
 
-hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
-                            hipStream_t s) {
+// Kernel arguments of one attention call: with splits, the partials go to the workspace
+// (outputs [splits][rows][H][d], then log-sum-exps [splits][rows][H]).
+static AttnDev attn_dev_for(const AttnArgs& a, const AttnPlan& plan, void* ws) {
   AttnDev A = make_attn_dev(a);
   A.chunk = plan.chunk;
   A.splits = plan.splits;
   A.rows = plan.rows;
-  float* part_o = nullptr;
-  float* part_l = nullptr;
   if (plan.splits > 1) {
-    part_o = static_cast<float*>(ws);
-    part_l = reinterpret_cast<float*>(
+    A.out = static_cast<float*>(ws);
+    A.lse = reinterpret_cast<float*>(
         static_cast<char*>(ws) +
         align256(static_cast<size_t>(plan.splits) * plan.rows * a.H * a.d * 4));
-    A.out = part_o;
-    A.lse = part_l;
   } else {
     A.out = a.out;
     A.lse = a.lse;
   }
+  return A;
+}
+
+hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
+                            hipStream_t s) {
+  AttnDev A = attn_dev_for(a, plan, ws);
+  float* part_o = plan.splits > 1 ? A.out : nullptr;
+  float* part_l = plan.splits > 1 ? A.lse : nullptr;
   if (plan.tiled) {
     hca_tiled_kernel<<<dim3((a.Nq + kTokTile - 1) / kTokTile, a.B), 512, 0, s>>>(A);
     return hipGetLastError();
@@ -716,6 +771,40 @@ hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, v
   if (e != hipSuccess || plan.splits == 1) return e;
   lse_merge_kernel<<<dim3(a.H, plan.rows), a.d, 0, s>>>(part_o, part_l, plan.splits,
                                                           plan.rows, a.H, a.d, a.out, a.lse);
+  return hipGetLastError();
+}
+
+bool csa_hca_fused(const AttnPlan& pc, const AttnPlan& ph) {
+  return pc.mfma && !pc.tiled && ph.hca_decode;
+}
+
+hipError_t launch_csa_hca(const AttnArgs& c, const AttnPlan& pc, const AttnArgs& h,
+                          const AttnPlan& ph, void* ws, hipStream_t s) {
+  void* ws_h = static_cast<char*>(ws) + align256(pc.total_bytes);
+  if (!csa_hca_fused(pc, ph)) {
+    hipError_t e = launch_attention(true, c, pc, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_attention(false, h, ph, ws_h, s);
+  }
+  const AttnDev C = attn_dev_for(c, pc, ws);
+  const AttnDev Hd = attn_dev_for(h, ph, ws_h);
+  const int blocks = pc.splits * pc.rows + ph.splits * ph.rows;
+  if (blocks > 0) {
+    if (h.block_table) csa_hca_decode_kernel<true><<<blocks, 256, 0, s>>>(C, Hd);
+    else csa_hca_decode_kernel<false><<<blocks, 256, 0, s>>>(C, Hd);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const MergeJob mc{C.out, C.lse, pc.splits, pc.rows, c.out, c.lse};
+  const MergeJob mh{Hd.out, Hd.lse, ph.splits, ph.rows, h.out, h.lse};
+  if (pc.splits > 1 && ph.splits > 1)
+    lse_merge2_kernel<<<dim3(c.H, pc.rows + ph.rows), c.d, 0, s>>>(mc, mh, c.H, c.d);
+  else if (pc.splits > 1)
+    lse_merge_kernel<<<dim3(c.H, pc.rows), c.d, 0, s>>>(C.out, C.lse, pc.splits, pc.rows, c.H,
+                                                          c.d, c.out, c.lse);
+  else if (ph.splits > 1)
+    lse_merge_kernel<<<dim3(h.H, ph.rows), h.d, 0, s>>>(Hd.out, Hd.lse, ph.splits, ph.rows,
+                                                          h.H, h.d, h.out, h.lse);
   return hipGetLastError();
 }
 

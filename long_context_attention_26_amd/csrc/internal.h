@@ -103,5 +103,11 @@ hipError_t launch_compress_bwd(const void* x, int x_dtype, int64_t x_bstride, in
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len);
 hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
                             hipStream_t s);
+// CSA and HCA attention of the same query tokens: one launch for both (plus one merge) on
+// the decode fast path, else the two calls in turn; workspace = align256(pc.total_bytes) +
+// ph.total_bytes.
+bool csa_hca_fused(const AttnPlan& pc, const AttnPlan& ph);
+hipError_t launch_csa_hca(const AttnArgs& c, const AttnPlan& pc, const AttnArgs& h,
+                          const AttnPlan& ph, void* ws, hipStream_t s);
 
 }  // namespace hcsa

@@ -29,6 +29,10 @@ _SIGS = {
     "hcsa_mxfp4_quantize": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
     "hcsa_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_topk": (_i, [_p, _i, _i64, _i, _i, _i, _i, _i64, _p, _i, _p, _p, _sz, _p]),
+    "hcsa_csa_hca_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "hcsa_csa_hca_attn": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64, _i, _i,
+                               _p, _p, _i64, _i, _i, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _p,
+                               _p, _p, _p, _p, _sz, _p]),
     "hcsa_csa_sparse_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64,
                                       _i, _i, _i64, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p,
                                       _p, _p, _p, _p, _i64, _p, _p, _i64, _p]),
@@ -271,6 +275,30 @@ def csa_sparse_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio
                                     _ptr(lse), _ptr(workspace), workspace.numel(),
                                     _stream(stream)))
     return out, lse
+
+
+def csa_hca_attn_workspace_size(B, Nq, H, d, k, n_win, N_h):
+    return lib.hcsa_csa_hca_attn_workspace_size(B, Nq, H, d, k, n_win, N_h)
+
+
+def csa_hca_attn(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio, kh, vh, N_h,
+                 ratio_h, pos0, scale, out_c, lse_c, out_h, lse_h, workspace=None, stream=None,
+                 seq_pos=None, block_table=None, raw_ring=0):
+    """csa_sparse_attn and hca_dense_attn of the same query tokens in one call (one launch
+    on the decode fast path)."""
+    B, Nq, H, d = q.shape
+    k = topk_idx.shape[-1]
+    if workspace is None:
+        workspace = alloc_workspace(csa_hca_attn_workspace_size(B, Nq, H, d, k, n_win, N_h),
+                                    q.device)
+    _check(lib.hcsa_csa_hca_attn(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N, _ptr(topk_idx), k,
+                                 _ptr(k_raw), _ptr(v_raw), k_raw.stride(0), k_raw.shape[1],
+                                 raw_pos0, n_win, ratio, _ptr(kh), _ptr(vh), kh.stride(0), N_h,
+                                 ratio_h, pos0, _pos_ptr(seq_pos, B),
+                                 _pages(block_table, raw_ring), dtype_code(q), B, Nq, H, d,
+                                 scale, _ptr(out_c), _ptr(lse_c), _ptr(out_h), _ptr(lse_h),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out_c, lse_c), (out_h, lse_h)
 
 
 def hca_attn_workspace_size(B, Nq, H, d, N):

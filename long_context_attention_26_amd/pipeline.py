@@ -91,9 +91,8 @@ class DecodeStep:
                                   dtype=torch.bfloat16 if score_dtype == "bf16" else torch.float32)
         self.ws_topk = hcsa.alloc_workspace(
             hcsa.topk_workspace_size(self.score_code, B, Nq, st.Nc, topk), dev)
-        self.ws_csa = hcsa.alloc_workspace(
-            hcsa.csa_attn_workspace_size(B, Nq, H, d, topk, n_win), dev)
-        self.ws_hca = hcsa.alloc_workspace(hcsa.hca_attn_workspace_size(B, Nq, H, d, st.Nh), dev)
+        self.ws_attn = hcsa.alloc_workspace(
+            hcsa.csa_hca_attn_workspace_size(B, Nq, H, d, topk, n_win, st.Nh), dev)
 
     def run_pool(self, pos0, stream=None):
         """Pool the blocks completed by the query tokens."""
@@ -105,20 +104,25 @@ class DecodeStep:
         hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, self.scores,
                               k_scales=st.Ics, stream=stream, mx_fp8=self.mx_fp8)
 
+    def _attend(self, q, pos0, stream):
+        """CSA sparse attention and HCA dense attention of the query tokens (one call)."""
+        st = self.st
+        hcsa.csa_hca_attn(q, st.Kc, st.Vc, st.Nc, self.idx, st.K_raw, st.V_raw, 0, self.n_win,
+                          R_CSA, st.Kh, st.Vh, st.Nh, R_HCA, pos0, self.scale, self.out_csa,
+                          self.lse_csa, self.out_hca, self.lse_hca, workspace=self.ws_attn,
+                          stream=stream)
+
     def run_select_attend(self, q, pos0, stream=None):
         st = self.st
         hcsa.topk(self.scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
                   workspace=self.ws_topk, stream=stream)
-        hcsa.csa_sparse_attn(q, st.Kc, st.Vc, st.Nc, self.idx, st.K_raw, st.V_raw, 0, self.n_win,
-                             R_CSA, pos0, self.scale, self.out_csa, self.lse_csa,
-                             workspace=self.ws_csa, stream=stream)
-        hcsa.hca_dense_attn(q, st.Kh, st.Vh, st.Nh, R_HCA, pos0, self.scale, self.out_hca,
-                            self.lse_hca, workspace=self.ws_hca, stream=stream)
+        self._attend(q, pos0, stream)
 
     def run(self, q, q_idx, w_idx, pos0, append=True, scores_out=None, stream=None,
             marks=None):
         """Full hot path for the query tokens at pos0..pos0+Nq-1: pool the blocks those
-        tokens complete (append), indexer scores, top-k, CSA sparse attention, HCA attention.
+        tokens complete (append), indexer scores, top-k, CSA sparse attention and HCA
+        attention (one call).
         `marks`, if given, is called with a stage name before each stage and with "end"
         after the last (used to record timing events on the stream)."""
         st = self.st
@@ -133,12 +137,7 @@ class DecodeStep:
         mark("topk")
         hcsa.topk(scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
                   workspace=self.ws_topk, stream=stream)
-        mark("csa_attn")
-        hcsa.csa_sparse_attn(q, st.Kc, st.Vc, st.Nc, self.idx, st.K_raw, st.V_raw, 0, self.n_win,
-                             R_CSA, pos0, self.scale, self.out_csa, self.lse_csa,
-                             workspace=self.ws_csa, stream=stream)
-        mark("hca_attn")
-        hcsa.hca_dense_attn(q, st.Kh, st.Vh, st.Nh, R_HCA, pos0, self.scale, self.out_hca,
-                            self.lse_hca, workspace=self.ws_hca, stream=stream)
+        mark("attention")
+        self._attend(q, pos0, stream)
         mark("end")
         return self.idx, (self.out_csa, self.lse_csa), (self.out_hca, self.lse_hca)

@@ -1,0 +1,103 @@
+"""CSA + HCA attention in one call: the same outputs as the two separate calls, bit for bit
+(on the decode fast path both run as one launch with one merge; other shapes run the
+separate kernels in turn).  The separate calls are checked against the oracle elsewhere;
+one row per case is also checked against the oracle here."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import assert_attention_close, f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H(gpu):
+    from long_context_attention_26_amd import hcsa
+    return hcsa
+
+
+CASES = [
+    dict(name="decode-b4", B=4, Nq=1, pos=[80000] * 4, dt="bf16", Hh=16, d=128, k=1024, paged=False),
+    dict(name="decode-b1-1M", B=1, Nq=1, pos=[1048575], dt="bf16", Hh=16, d=128, k=1024, paged=False),
+    dict(name="decode-ragged-paged", B=3, Nq=1, pos=[30000, 7777, 100], dt="bf16", Hh=16, d=128,
+         k=512, paged=True),
+    dict(name="decode-ring", B=2, Nq=1, pos=[20000, 12345], dt="bf16", Hh=16, d=128, k=256,
+         paged=False, ring=256),
+    dict(name="prefill-fallback", B=1, Nq=32, pos=[5000], dt="bf16", Hh=16, d=128, k=300,
+         paged=False),
+    dict(name="fp32-fallback", B=2, Nq=1, pos=[4095, 3000], dt="f32", Hh=1, d=64, k=64,
+         paged=False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_fused_equals_separate(H, gpu, case):
+    print(f"fused attn {case['name']}", flush=True)
+    B, Nq, Hh, d, k, pos = case["B"], case["Nq"], case["Hh"], case["d"], case["k"], case["pos"]
+    w, scale = 128, 1 / math.sqrt(case["d"])
+    tdt = torch.float32 if case["dt"] == "f32" else torch.bfloat16
+    top = max(pos) + Nq
+    Nc, Nh = top // 4 + 8, top // 128 + 1
+    ring = case.get("ring", 0)
+    g = torch.Generator().manual_seed(21)
+    q = torch.randn(B, Nq, Hh, d, generator=g).to(tdt).to(gpu)
+    Kc, Vc = (torch.randn(B, Nc, d, generator=g).to(tdt).to(gpu) for _ in range(2))
+    Kh, Vh = (torch.randn(B, Nh, d, generator=g).to(tdt).to(gpu) for _ in range(2))
+    T_raw = ring if ring else top
+    Kr, Vr = (torch.randn(B, T_raw, d, generator=g).to(tdt).to(gpu) for _ in range(2))
+    seq_pos = torch.tensor(pos, dtype=torch.int64, device=gpu)
+    idx = torch.full((B, Nq, k), -1, dtype=torch.int32)
+    for b in range(B):
+        for i in range(Nq):
+            nv = O.visible_entries(pos[b] + i, Nc, 4)
+            sel = torch.randperm(max(nv, 1), generator=g)[: min(k, nv)].sort().values
+            idx[b, i, : sel.numel()] = sel.to(torch.int32) if nv else idx[b, i, :0]
+    idx = idx.to(gpu)
+    table = None
+    if case["paged"]:
+        # every tensor through one block table: a random page per 128-token block
+        nblk = -(-top // 128)
+        P = B * nblk + 2
+        table = torch.randperm(P, generator=g)[: B * nblk].to(torch.int32).view(B, nblk).to(gpu)
+
+        def pool(x, per):
+            pool_ = torch.zeros((P, per, d), dtype=tdt, device=gpu)
+            full = torch.zeros((B, nblk * per, d), dtype=tdt, device=gpu)
+            full[:, : x.shape[1]] = x[:, : nblk * per]
+            pool_[table.reshape(-1).long()] = full.reshape(B * nblk, per, d)
+            return pool_
+        Kc_, Vc_, Kh_, Vh_, Kr_, Vr_ = pool(Kc, 32), pool(Vc, 32), pool(Kh, 1), pool(Vh, 1), \
+            pool(Kr, 128), pool(Vr, 128)
+    else:
+        Kc_, Vc_, Kh_, Vh_, Kr_, Vr_ = Kc, Vc, Kh, Vh, Kr, Vr
+
+    def nan(*s):
+        return torch.full(s, float("nan"), device=gpu)
+
+    oc, lc, oh, lh = nan(B, Nq, Hh, d), nan(B, Nq, Hh), nan(B, Nq, Hh, d), nan(B, Nq, Hh)
+    H.csa_hca_attn(q, Kc_, Vc_, Nc, idx, Kr_, Vr_, 0, w, 4, Kh_, Vh_, Nh, 128, 0, scale, oc, lc,
+                   oh, lh, seq_pos=seq_pos, block_table=table, raw_ring=ring)
+    oc2, lc2, oh2, lh2 = nan(B, Nq, Hh, d), nan(B, Nq, Hh), nan(B, Nq, Hh, d), nan(B, Nq, Hh)
+    H.csa_sparse_attn(q, Kc_, Vc_, Nc, idx, Kr_, Vr_, 0, w, 4, 0, scale, oc2, lc2,
+                      seq_pos=seq_pos, block_table=table, raw_ring=ring)
+    H.hca_dense_attn(q, Kh_, Vh_, Nh, 128, 0, scale, oh2, lh2, seq_pos=seq_pos,
+                     block_table=table)
+    torch.cuda.synchronize()
+    for name, a, b in (("csa out", oc, oc2), ("csa lse", lc, lc2), ("hca out", oh, oh2),
+                       ("hca lse", lh, lh2)):
+        assert torch.equal(a, b), f"{case['name']}: {name} differs from the separate call"
+
+    # the last query of sequence 0 against the oracle
+    b, i = 0, Nq - 1
+    p = pos[b] + i
+    lo = max(0, p - w - 2)
+    rows = torch.arange(lo, p + 1, device=gpu) % ring if ring else torch.arange(lo, p + 1, device=gpu)
+    ro, rl = O.csa_attention(f64(q[b, i]), f64(Kc[b]), f64(Vc[b]), idx[b, i].cpu().numpy().astype(np.int64),
+                             f64(Kr[b, rows]), f64(Vr[b, rows]), lo, p, w, scale, 4)
+    assert_attention_close(f64(oc[b, i]), f64(lc[b, i]), ro, rl, case["dt"] == "f32", "fused csa")
+    ro, rl = O.hca_attention(f64(q[b, i]), f64(Kh[b]), f64(Vh[b]), p, scale, 128)
+    assert_attention_close(f64(oh[b, i]), f64(lh[b, i]), ro, rl, case["dt"] == "f32", "fused hca")
