@@ -351,11 +351,14 @@ def main():
             stp.mx_fp8 = True
     torch.cuda.synchronize()
 
-    # Each copy's step is captured as one HIP graph (one launch per step), and once more as
-    # three graphs (pooling + selector clear | indexer scores | top-k + CSA + HCA attention).
-    # Every SAMPLE-th timed step runs the three-graph form with timing events between the
-    # graphs on the launch stream: they give the per-stage split and the indexer kernel's
-    # duration for the roofline; the other steps are single launches.
+    # Each copy's step is captured as one HIP graph, and once more as three graphs (pooling +
+    # selector clear | indexer scores | top-k + CSA + HCA attention).  Every SAMPLE-th timed
+    # step runs the three-graph form with timing events between the graphs on the launch
+    # stream: they give the per-stage split and the indexer kernel's duration for the
+    # roofline.  The SAMPLE - 1 steps between two sampled ones replay one graph that chains
+    # them (each on its own cache copy, every kernel of every step executed), as a model's
+    # per-token graph chains its layers: the host's graph-launch latency, several
+    # microseconds per launch, then falls on one step in SAMPLE instead of every step.
     SAMPLE = 8
     stages = ["pool", "index_scores", "select_attend"]
     full, split = [], []
@@ -383,6 +386,19 @@ def main():
             g_rest.capture_end()
         full.append(g_all)
         split.append((g_pool, g_idx, g_rest))
+    torch.cuda.synchronize()
+    chain = []                                  # chain[c]: SAMPLE - 1 steps from copy c on
+    for c in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap_stream):
+            g.capture_begin()
+            for j in range(SAMPLE - 1):
+                stp = steps[(c + j) % R]
+                stp.run_pool(cfg.pos0)
+                stp.run_index_scores(qi, wi, cfg.pos0)
+                stp.run_select_attend(q, cfg.pos0)
+            g.capture_end()
+        chain.append(g)
     torch.cuda.synchronize()
 
     ev = []
@@ -413,8 +429,14 @@ def main():
         one_step(i, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(i, True)
+    i = 0
+    while i < args.steps:
+        if i % SAMPLE == 1 and i + SAMPLE - 1 <= args.steps:
+            chain[i % R].replay()                # steps i .. i + SAMPLE - 2
+            i += SAMPLE - 1
+        else:
+            one_step(i, True)
+            i += 1
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el / args.steps * 1e3
@@ -468,7 +490,8 @@ def main():
         "step_tflops": round(sum(flops.values()) / (el / args.steps) / 1e12, 2),
         "breakdown_us": {k: round(v, 2) for k, v in br.items()},
         "breakdown_note": f"sampled every {SAMPLE}th step ({len(ev)} samples): pooling graph | "
-                          "indexer launch | selection + attention graph",
+                          "indexer launch | selection + attention graph; the steps between "
+                          f"samples replay one graph of {SAMPLE - 1} chained steps",
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
