@@ -1,6 +1,6 @@
 """CSA + HCA attention in one call: the same outputs as the two separate calls, bit for bit
-(on the decode fast path both run as one launch with one merge; other shapes run the
-separate kernels in turn).  The separate calls are checked against the oracle elsewhere;
+(on the decode fast path both run as one launch with one merge launch; other shapes run
+the separate kernels in turn).  The separate calls are checked against the oracle elsewhere;
 one row per case is also checked against the oracle here."""
 import math
 
@@ -78,9 +78,18 @@ def test_fused_equals_separate(H, gpu, case):
     def nan(*s):
         return torch.full(s, float("nan"), device=gpu)
 
-    oc, lc, oh, lh = nan(B, Nq, Hh, d), nan(B, Nq, Hh), nan(B, Nq, Hh, d), nan(B, Nq, Hh)
-    H.csa_hca_attn(q, Kc_, Vc_, Nc, idx, Kr_, Vr_, 0, w, 4, Kh_, Vh_, Nh, 128, 0, scale, oc, lc,
-                   oh, lh, seq_pos=seq_pos, block_table=table, raw_ring=ring)
+    # twice on one workspace: the second call must not depend on what the first left there
+    ws = H.alloc_workspace(H.csa_hca_attn_workspace_size(B, Nq, Hh, d, k, w, Nh), gpu)
+    runs = []
+    for _ in range(2):
+        oc, lc, oh, lh = nan(B, Nq, Hh, d), nan(B, Nq, Hh), nan(B, Nq, Hh, d), nan(B, Nq, Hh)
+        H.csa_hca_attn(q, Kc_, Vc_, Nc, idx, Kr_, Vr_, 0, w, 4, Kh_, Vh_, Nh, 128, 0, scale, oc,
+                       lc, oh, lh, workspace=ws, seq_pos=seq_pos, block_table=table,
+                       raw_ring=ring)
+        runs.append((oc, lc, oh, lh))
+    torch.cuda.synchronize()
+    for a, b in zip(*runs):
+        assert torch.equal(a, b), "second call on the same workspace differs"
     oc2, lc2, oh2, lh2 = nan(B, Nq, Hh, d), nan(B, Nq, Hh), nan(B, Nq, Hh, d), nan(B, Nq, Hh)
     H.csa_sparse_attn(q, Kc_, Vc_, Nc, idx, Kr_, Vr_, 0, w, 4, 0, scale, oc2, lc2,
                       seq_pos=seq_pos, block_table=table, raw_ring=ring)
