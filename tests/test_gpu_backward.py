@@ -249,3 +249,61 @@ def test_training_step_chain(H, gpu):
                dKh=dKh[0], dVh=dVh[0])
     for n_, t in got.items():
         _rel_close(f64(t), ref[n_], 2e-2, n_)
+
+
+@pytest.mark.parametrize("dt,Hh,d", [("bf16", 16, 128), ("f32", 4, 64)])
+def test_backward_ragged_positions(H, gpu, dt, Hh, d):
+    """Per-sequence positions (seq_pos): each sequence's gradients against the oracle at its
+    own position, CSA and HCA."""
+    print(f"bwd ragged {dt} H{Hh} d{d}", flush=True)
+    pos = [5000, 777, 2999]
+    B, Nq, k, w = len(pos), 2, 128, 64
+    scale = 1 / math.sqrt(d)
+    top = max(pos) + Nq
+    N, Nh = top // 4 + 2, top // 128 + 1
+    q = O.round_to(rng.standard_normal((B, Nq, Hh, d)), dt)
+    Kc, Vc = (O.round_to(rng.standard_normal((B, N, d)), dt) for _ in range(2))
+    Kh, Vh = (O.round_to(rng.standard_normal((B, Nh, d)), dt) for _ in range(2))
+    Kr, Vr = (O.round_to(rng.standard_normal((B, top, d)), dt) for _ in range(2))
+    idx = np.stack([np.stack([O.select_topk(rng.standard_normal(N),
+                                            O.visible_entries(pos[b] + i, N, 4), k)
+                              for i in range(Nq)]) for b in range(B)])
+    dout = O.round_fp32(rng.standard_normal((B, Nq, Hh, d)))
+    dlse = O.round_fp32(rng.standard_normal((B, Nq, Hh)))
+    oc, lc, oh, lh = (np.zeros(s) for s in ((B, Nq, Hh, d), (B, Nq, Hh), (B, Nq, Hh, d), (B, Nq, Hh)))
+    ref = {n: np.zeros(s) for n, s in (("dqc", (B, Nq, Hh, d)), ("dKc", (B, N, d)), ("dVc", (B, N, d)),
+                                      ("dKr", (B, top, d)), ("dVr", (B, top, d)),
+                                      ("dqh", (B, Nq, Hh, d)), ("dKh", (B, Nh, d)), ("dVh", (B, Nh, d)))}
+    for b in range(B):
+        for i in range(Nq):
+            p = pos[b] + i
+            oc[b, i], lc[b, i] = O.csa_attention(q[b, i], Kc[b], Vc[b], idx[b, i], Kr[b], Vr[b],
+                                                 0, p, w, scale, 4)
+            oh[b, i], lh[b, i] = O.hca_attention(q[b, i], Kh[b], Vh[b], p, scale, 128)
+            g = O.csa_attention_backward(q[b, i], Kc[b], Vc[b], idx[b, i], Kr[b], Vr[b], 0, p, w,
+                                         scale, dout[b, i], dlse[b, i], 4)
+            ref["dqc"][b, i] = g[0]
+            for n_, x in zip(("dKc", "dVc", "dKr", "dVr"), g[1:]):
+                ref[n_][b] += x
+            g = O.hca_attention_backward(q[b, i], Kh[b], Vh[b], p, scale, dout[b, i],
+                                         dlse[b, i], 128)
+            ref["dqh"][b, i] = g[0]
+            ref["dKh"][b] += g[1]
+            ref["dVh"][b] += g[2]
+    tdt = _tdt(dt)
+    f32 = lambda x: dev(O.round_fp32(x), torch.float32, gpu)
+    sp = torch.tensor(pos, dtype=torch.int64, device=gpu)
+    qt = dev(q, tdt, gpu)
+    got = {n_: torch.zeros(v.shape, device=gpu) for n_, v in ref.items()}
+    H.csa_sparse_attn_bwd(qt, dev(Kc, tdt, gpu), dev(Vc, tdt, gpu), N,
+                          torch.from_numpy(idx.astype(np.int32)).to(gpu), dev(Kr, tdt, gpu),
+                          dev(Vr, tdt, gpu), 0, w, 4, 0, scale, f32(oc), f32(lc), f32(dout),
+                          got["dqc"], got["dKc"], got["dVc"], got["dKr"], got["dVr"],
+                          dlse=f32(dlse), seq_pos=sp)
+    H.hca_dense_attn_bwd(qt, dev(Kh, tdt, gpu), dev(Vh, tdt, gpu), Nh, 128, 0, scale, f32(oh),
+                         dev(lh, torch.float32, gpu), f32(dout), got["dqh"], got["dKh"],
+                         got["dVh"], dlse=f32(dlse), seq_pos=sp)
+    torch.cuda.synchronize()
+    tol = _tol(dt, Hh, d)
+    for n_, t in got.items():
+        _rel_close(f64(t), ref[n_], tol, f"ragged {n_}")
