@@ -225,6 +225,8 @@ def train_backward(args):
     dom = {n: torch.zeros(r_, device=dev) for n, r_ in
            (("csa_k", 4), ("csa_v", 4), ("hca_k", 128), ("hca_v", 128))}
     ws_p = hcsa.alloc_workspace(hcsa.lib.hcsa_compress_kv_bwd_workspace_size(1, T, 128), dev)
+    ws_hb = hcsa.alloc_workspace(
+        hcsa.lib.hcsa_hca_dense_attn_bwd_workspace_size(1, HALF, Hh, d, hcsa.BF16), dev)
 
     stages = ["zero", "csa_bwd", "hca_bwd", "pool_bwd"]
 
@@ -243,7 +245,8 @@ def train_backward(args):
         mark(2)
         for h0, sl in halves:
             hcsa.hca_dense_attn_bwd(q[:, sl], Kh, Vh, Nh, 128, h0, scale, oh[:, sl], lh[:, sl],
-                                    doh[:, sl], dqh[:, sl], grads["Kh"], grads["Vh"])
+                                    doh[:, sl], dqh[:, sl], grads["Kh"], grads["Vh"],
+                                    workspace=ws_hb)
         mark(3)
         for x, n, r_, gy, gx in ((K, "csa_k", 4, "Kc", "K"), (V, "csa_v", 4, "Vc", "V"),
                                  (K, "hca_k", 128, "Kh", "K"), (V, "hca_v", 128, "Vh", "V")):

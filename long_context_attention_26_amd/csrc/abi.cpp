@@ -574,9 +574,17 @@ int hcsa_csa_sparse_attn_bwd(const void* q, const void* kc, const void* vc, int6
   a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
   a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
-  hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkc, dvc, dc_bstride, dk_raw, dv_raw, draw_bstride};
+  hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkc, dvc, dc_bstride, dk_raw, dv_raw,
+                      draw_bstride, nullptr};
   return hip_status(hcsa::launch_attention_bwd(true, a, g, static_cast<hipStream_t>(stream)),
                     "hcsa_csa_sparse_attn_bwd");
+}
+
+size_t hcsa_hca_dense_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype) {
+  if (B < 1 || Nq < 1 || H < 1 || d < 1) return 0;
+  hcsa::AttnArgs a{};
+  a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.kv_dtype = kv_dtype;
+  return hcsa::hca_bwd_workspace_bytes(a);
 }
 
 int hcsa_hca_dense_attn_bwd(const void* q, const void* kh, const void* vh, int64_t h_bstride,
@@ -584,7 +592,8 @@ int hcsa_hca_dense_attn_bwd(const void* q, const void* kh, const void* vh, int64
                             int kv_dtype, int B, int Nq, int H, int d, float scale,
                             const float* out, const float* lse, const float* dout,
                             const float* dlse, float* dq, float* dkh, float* dvh,
-                            int64_t dh_bstride, hcsa_stream stream) {
+                            int64_t dh_bstride, void* workspace, size_t ws_bytes,
+                            hcsa_stream stream) {
   int rc = check_attn_common(q, kv_dtype, B, Nq, H, d, scale, out, lse, ratio, pos0);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
@@ -603,7 +612,10 @@ int hcsa_hca_dense_attn_bwd(const void* q, const void* kh, const void* vh, int64
   a.q = q; a.kc = kh; a.vc = vh; a.c_bstride = h_bstride; a.N = N; a.ratio = ratio;
   a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
-  hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkh, dvh, dh_bstride, nullptr, nullptr, 0};
+  rc = check_ws(workspace, ws_bytes, hcsa::hca_bwd_workspace_bytes(a));
+  if (rc) return rc;
+  hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkh, dvh, dh_bstride, nullptr, nullptr, 0,
+                      workspace};
   return hip_status(hcsa::launch_attention_bwd(false, a, g, static_cast<hipStream_t>(stream)),
                     "hcsa_hca_dense_attn_bwd");
 }

@@ -46,6 +46,7 @@ struct AttnBwdDev {
   float* dkr;            // raw-row gradients [B][T_raw][d] (dr_bstride)
   float* dvr;
   int64_t dr_bstride;
+  float* dt_out;         // [rows][16] or null: dout.o - dlse per head, for the key-major pass
 };
 
 // Sums each of the N values v[0..N) over the 64 lanes of the wave with no lane-dependent
@@ -236,7 +237,9 @@ __device__ __forceinline__ f32x4 mma16(const u32x2& a, const u32x2& b, f32x4 c) 
 //   dQ^T += K^T dS^T  (16x16x32, the forward's V^T P^T form with K slices for V),
 //   dK    = dS^T Q,  dV = P^T dout  (16x16x16 over the 16 heads, one per 16-channel tile),
 // and the dK / dV tiles go to memory with atomics, 4 rows x 16 channels per instruction.
-template <bool CSA>
+// With DKV false only dq is formed (the key-major kernel below takes dK and dV), and the
+// per-head terms dout.o - dlse are stored for it.
+template <bool CSA, bool DKV>
 __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
   __shared__ float s_dq[4][16][129];
   __shared__ float s_lse2[16];
@@ -265,6 +268,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
       const int64_t li = static_cast<int64_t>(row) * 16 + h;
       s_dt[h] = part - (G.dlse ? G.dlse[li] : 0.0f);
       s_lse2[h] = G.lse[li] * kLog2e;
+      if (!DKV) G.dt_out[li] = s_dt[h];
     }
   }
   __syncthreads();
@@ -372,6 +376,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
     // ---- lane = key: S and dP of key base + 16t + col for heads 4g + i; dK, dV tiles
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      if constexpr (!DKV) break;
       f32x4 sk = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -426,6 +431,140 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
   for (int e = threadIdx.x; e < 2048; e += 256) {
     const int h = e >> 7, c = e & 127;
     G.dq[hb + e] = A.scale * (((s_dq[0][h][c] + s_dq[1][h][c]) + s_dq[2][h][c]) + s_dq[3][h][c]);
+  }
+}
+
+// Key-major dK / dV of HCA attention (bf16, 16 heads x 128), the entries being shared by
+// every later query token: a block owns 16 entries for a chunk of 128 query tokens; each
+// wave takes two tokens (32 query rows) per step.  S = Q K^T and dP = dout V^T run with
+// lane = entry (16x16x32, K as the B operand), so P and dS are already the B operand of
+//   dK^T += Q^T dS,  dV^T += dout^T P   (16x16x32 over the step's 32 rows; Q^T and dout^T
+// built from 16-byte row slices by byte permutes, as the forward builds V^T),
+// accumulated over the chunk in registers, summed over the 4 waves in LDS and added to
+// memory once per element.  dout.o - dlse per (token, head) comes from the dq pass.
+constexpr int kDkvEntries = 16;
+constexpr int kDkvTokens = 128;
+
+// grid: (ceil(N / 16), ceil(Nq / 128), B); block 256.
+__global__ __launch_bounds__(256) void hca_bwd_dkv_kernel(AttnBwdDev G) {
+  __shared__ float s_acc[2][kDkvEntries][129];
+  constexpr float kLog2e = 1.4426950408889634f;
+  const AttnDev& A = G.A;
+  const int e0 = blockIdx.x * kDkvEntries, t0 = blockIdx.y * kDkvTokens, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, g = lane >> 4;
+  // the chunk's last token must see the tile's first entry, else nothing to do
+  const int64_t plast = query_pos(A.seq_pos, A.pos0, b, min(t0 + kDkvTokens, A.Nq) - 1);
+  if (static_cast<int64_t>(e0 + 1) * A.ratio > plast + 1) return;      // block-uniform
+
+  const int e = e0 + col;
+  const bool e_ok = e < A.N;
+  u32x4 ka[4], va[4];                 // B operand: K[e][32s + 8g ..], V likewise
+  {
+    const uint16_t* kr = static_cast<const uint16_t*>(A.kc) + b * A.c_bstride + static_cast<int64_t>(e) * 128;
+    const uint16_t* vr = static_cast<const uint16_t*>(A.vc) + b * A.c_bstride + static_cast<int64_t>(e) * 128;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      ka[s] = e_ok ? *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
+      va[s] = e_ok ? *reinterpret_cast<const u32x4*>(vr + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x4 accK[8], accV[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) accK[t] = accV[t] = f32x4{0, 0, 0, 0};
+  const float sl2 = A.scale * kLog2e;
+  const uint16_t* q16 = static_cast<const uint16_t*>(A.q);
+
+  for (int it = 0; it < kDkvTokens / 8; ++it) {
+    const int ta = t0 + 2 * wave + 8 * it;          // tokens ta (rows 0..15), ta + 1 (16..31)
+    float pv[2][4], dsv[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = ta + tt;
+      const bool t_ok = tok < A.Nq;
+      const int64_t row = static_cast<int64_t>(b) * A.Nq + (t_ok ? tok : 0);
+      const int64_t p = query_pos(A.seq_pos, A.pos0, b, t_ok ? tok : 0);
+      const bool vis = t_ok && e_ok && static_cast<int64_t>(e + 1) * A.ratio <= p + 1;
+      // A operands: q and dout rows of head col at channels 32s + 8g
+      u32x4 qa[4], da[4];
+      const uint16_t* qrow = q16 + (row * 16 + col) * 128;
+      const float* drow = G.dout + (row * 16 + col) * 128;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        qa[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+        const float* d8 = drow + 32 * s + 8 * g;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) da[s][m] = pack_bf16x2(d8[2 * m], d8[2 * m + 1]);
+      }
+      f32x4 sv = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sv = mma32(qa[s], ka[s], sv);               // S[head 4g + i][entry col]
+        dp = mma32(da[s], va[s], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t li = row * 16 + 4 * g + i;
+        const float pe = vis ? exp2f(sv[i] * sl2 - G.lse[li] * kLog2e) : 0.0f;
+        pv[tt][i] = pe;
+        dsv[tt][i] = pe * (dp[i] - G.dt_out[li]);
+      }
+    }
+    // B operands: rows k = 8g + j <-> (token ta + j / 4, head 4g + j % 4)
+    const u32x4 pB = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                      pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
+    const u32x4 dsB = {pack_bf16x2(dsv[0][0], dsv[0][1]), pack_bf16x2(dsv[0][2], dsv[0][3]),
+                       pack_bf16x2(dsv[1][0], dsv[1][1]), pack_bf16x2(dsv[1][2], dsv[1][3])};
+    // row slices (channels 8col .. 8col + 7) of the same 8 rows, q and dout
+    u32x4 qs[8], ds8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = ta + (j >> 2);
+      const int64_t row = static_cast<int64_t>(b) * A.Nq + (tok < A.Nq ? tok : 0);
+      const int64_t hrow = row * 16 + 4 * g + (j & 3);
+      qs[j] = *reinterpret_cast<const u32x4*>(q16 + hrow * 128 + 8 * col);
+      const float* d8 = G.dout + hrow * 128 + 8 * col;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ds8[j][m] = pack_bf16x2(d8[2 * m], d8[2 * m + 1]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const uint32_t sel = (ct & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 qA, dA;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        qA[m] = __builtin_amdgcn_perm(qs[2 * m + 1][ct >> 1], qs[2 * m][ct >> 1], sel);
+        dA[m] = __builtin_amdgcn_perm(ds8[2 * m + 1][ct >> 1], ds8[2 * m][ct >> 1], sel);
+      }
+      accK[ct] = mma32(qA, dsB, accK[ct]);          // dK^T[channel 32g + 8i + ct][entry col]
+      accV[ct] = mma32(dA, pB, accV[ct]);
+    }
+  }
+  // the 4 waves' tiles summed in wave order, then one atomic add per element
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int c = 32 * g + 8 * i + t;
+          if (w == 0) {
+            s_acc[0][col][c] = accK[t][i];
+            s_acc[1][col][c] = accV[t][i];
+          } else {
+            s_acc[0][col][c] += accK[t][i];
+            s_acc[1][col][c] += accV[t][i];
+          }
+        }
+    }
+    __syncthreads();
+  }
+  for (int x = threadIdx.x; x < 2 * kDkvEntries * 128; x += 256) {
+    const int m = x >> 11, r = (x >> 7) & 15, c = x & 127;
+    if (e0 + r < A.N) {
+      float* dst = (m ? G.dvc : G.dkc) + b * G.dc_bstride + static_cast<int64_t>(e0 + r) * 128 + c;
+      unsafeAtomicAdd(dst, m ? s_acc[1][r][c] : A.scale * s_acc[0][r][c]);
+    }
   }
 }
 
@@ -537,6 +676,14 @@ hipError_t launch_bwd_typed(const AttnBwdDev& G, int rows, int hh, int cpl, hipS
 
 }  // namespace
 
+bool hca_bwd_key_major(const AttnArgs& a) {
+  return a.kv_dtype == 1 && a.H == 16 && a.d == 128 && a.Nq >= 16;
+}
+
+size_t hca_bwd_workspace_bytes(const AttnArgs& a) {
+  return hca_bwd_key_major(a) ? align256(static_cast<size_t>(a.B) * a.Nq * 16 * 4) : 0;
+}
+
 bool attn_bwd_shape_supported(int H, int d) {
   const int hh = bwd_heads(H), cpl = bwd_cpl(d);
   return hh > 0 && cpl > 0 && hh * cpl <= 64;
@@ -558,13 +705,27 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
   G.dkr = g.dkr;
   G.dvr = g.dvr;
   G.dr_bstride = g.dr_bstride;
+  G.dt_out = nullptr;
   const int rows = a.B * a.Nq;
   if (rows == 0) return hipSuccess;
   const int hh = bwd_heads(a.H), cpl = bwd_cpl(a.d);
   const bool bf = a.kv_dtype == 1;
   if (bf && a.H == 16 && a.d == 128) {          // the matrix-core path
-    if (csa) attn_bwd_mfma_kernel<true><<<rows, 256, 0, s>>>(G);
-    else attn_bwd_mfma_kernel<false><<<rows, 256, 0, s>>>(G);
+    if (csa) {
+      attn_bwd_mfma_kernel<true, true><<<rows, 256, 0, s>>>(G);
+    } else if (hca_bwd_key_major(a) && g.ws) {
+      // many query tokens share the entries: dq query-major, dK / dV key-major
+      G.dt_out = static_cast<float*>(g.ws);
+      attn_bwd_mfma_kernel<false, false><<<rows, 256, 0, s>>>(G);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (a.N > 0) {
+        dim3 grid((a.N + kDkvEntries - 1) / kDkvEntries, (a.Nq + kDkvTokens - 1) / kDkvTokens, a.B);
+        hca_bwd_dkv_kernel<<<grid, 256, 0, s>>>(G);
+      }
+    } else {
+      attn_bwd_mfma_kernel<false, true><<<rows, 256, 0, s>>>(G);
+    }
     return hipGetLastError();
   }
   if (csa) return bf ? launch_bwd_typed<true, true>(G, rows, hh, cpl, s)

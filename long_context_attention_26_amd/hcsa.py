@@ -36,8 +36,9 @@ _SIGS = {
     "hcsa_csa_sparse_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64,
                                       _i, _i, _i64, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p,
                                       _p, _p, _p, _p, _i64, _p, _p, _i64, _p]),
+    "hcsa_hca_dense_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_hca_dense_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _p, _i, _i, _i, _i, _i,
-                                     _f, _p, _p, _p, _p, _p, _p, _p, _i64, _p]),
+                                     _f, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _sz, _p]),
     "hcsa_compress_kv_bwd_workspace_size": (_sz, [_i, _i, _i]),
     "hcsa_compress_kv_bwd": (_i, [_p, _i, _i64, _i, _i, _i, _p, _i, _p, _i64, _p, _i64, _p, _p,
                                   _sz, _p]),
@@ -339,13 +340,18 @@ def csa_sparse_attn_bwd(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, r
 
 
 def hca_dense_attn_bwd(q, kh, vh, N, ratio, pos0, scale, out, lse, dout, dq, dkh, dvh,
-                       dlse=None, stream=None, seq_pos=None):
+                       dlse=None, workspace=None, stream=None, seq_pos=None):
     """Backward of hca_dense_attn: writes dq; adds into dkh, dvh [B, >=N, d] f32."""
     B, Nq, H, d = q.shape
+    nbytes = lib.hcsa_hca_dense_attn_bwd_workspace_size(B, Nq, H, d, dtype_code(q))
+    if workspace is None and nbytes:
+        workspace = alloc_workspace(nbytes, q.device)
     _check(lib.hcsa_hca_dense_attn_bwd(_ptr(q), _ptr(kh), _ptr(vh), kh.stride(0), N, ratio, pos0,
                                        _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d, scale,
                                        _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq),
-                                       _ptr(dkh), _ptr(dvh), dkh.stride(0), _stream(stream)))
+                                       _ptr(dkh), _ptr(dvh), dkh.stride(0), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel(),
+                                       _stream(stream)))
     return dq
 
 

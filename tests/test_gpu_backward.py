@@ -128,6 +128,10 @@ HCA_CASES = [
     dict(dt="bf16", H=16, d=128, N=300, Nq=16, B=2, pos0=128 * 280, dlse=True),   # causal rows
     dict(dt="bf16", H=16, d=128, N=8, Nq=2, B=1, pos0=100, dlse=False),            # nothing visible
     dict(dt="bf16", H=8, d=64, N=50, Nq=3, B=2, pos0=6399, dlse=False),
+    # many query tokens (key-major entry gradients): three 128-token chunks, the last ragged,
+    # 45 entries (a partial 16-entry tile), and a tile no token of the chunk sees
+    dict(dt="bf16", H=16, d=128, N=45, Nq=300, B=2, pos0=128 * 40 - 150, dlse=True),
+    dict(dt="bf16", H=16, d=128, N=45, Nq=300, B=1, pos0=128 * 20, dlse=False),
 ]
 
 
