@@ -227,6 +227,8 @@ def train_backward(args):
     ws_p = hcsa.alloc_workspace(hcsa.lib.hcsa_compress_kv_bwd_workspace_size(1, T, 128), dev)
     ws_hb = hcsa.alloc_workspace(
         hcsa.lib.hcsa_hca_dense_attn_bwd_workspace_size(1, HALF, Hh, d, hcsa.BF16), dev)
+    ws_cb = hcsa.alloc_workspace(
+        hcsa.lib.hcsa_csa_sparse_attn_bwd_workspace_size(1, HALF, Hh, d, hcsa.BF16), dev)
 
     stages = ["zero", "csa_bwd", "hca_bwd", "pool_bwd"]
 
@@ -241,7 +243,7 @@ def train_backward(args):
         for h0, sl in halves:
             hcsa.csa_sparse_attn_bwd(q[:, sl], Kc, Vc, Nc, idx[:, sl], K, V, 0, w, 4, h0, scale,
                                      oc[:, sl], lc[:, sl], doc[:, sl], dqc[:, sl], grads["Kc"],
-                                     grads["Vc"], grads["K"], grads["V"])
+                                     grads["Vc"], grads["K"], grads["V"], workspace=ws_cb)
         mark(2)
         for h0, sl in halves:
             hcsa.hca_dense_attn_bwd(q[:, sl], Kh, Vh, Nh, 128, h0, scale, oh[:, sl], lh[:, sl],

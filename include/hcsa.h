@@ -313,11 +313,13 @@ int hcsa_csa_hca_attn(const void *q, const void *kc, const void *vc, int64_t c_b
  * The accumulations use floating-point atomics: their order, and the last bits of the
  * accumulated gradients, can differ between runs; dq is deterministic.
  * Limits: the forward's, and H <= 64/c with c = 1, 2, 4 for d <= 64, 128, 256 (H counted
- * rounded up to 4, 16, 32 or 64).  The CSA call takes no workspace; the HCA call takes
- * hcsa_hca_dense_attn_bwd_workspace_size(...) bytes (256-byte aligned; zero bytes, and a
- * NULL workspace, except for bf16 16 x 128 with 16 or more query tokens, where the entry
- * gradients are formed key-major, one block per 16 entries and 128 tokens).
+ * rounded up to 4, 16, 32 or 64).  Workspace: hcsa_csa_sparse_attn_bwd_workspace_size or
+ * hcsa_hca_dense_attn_bwd_workspace_size bytes, 256-byte aligned (zero bytes, and NULL
+ * allowed, except for bf16 16 x 128 with 16 or more query tokens, where the keys shared by
+ * consecutive tokens -- HCA entries, CSA window rows -- get their gradients key-major, one
+ * block per 16 keys and 128 tokens; with a NULL workspace they stay query-major).
  */
+size_t hcsa_csa_sparse_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype);
 int hcsa_csa_sparse_attn_bwd(const void *q, const void *kc, const void *vc, int64_t c_bstride,
                              int N, const int32_t *topk_idx, int k, const void *k_raw,
                              const void *v_raw, int64_t raw_bstride, int64_t T_raw,
@@ -326,7 +328,8 @@ int hcsa_csa_sparse_attn_bwd(const void *q, const void *kc, const void *vc, int6
                              float scale, const float *out, const float *lse,
                              const float *dout, const float *dlse, float *dq, float *dkc,
                              float *dvc, int64_t dc_bstride, float *dk_raw, float *dv_raw,
-                             int64_t draw_bstride, hcsa_stream stream);
+                             int64_t draw_bstride, void *workspace, size_t ws_bytes,
+                             hcsa_stream stream);
 size_t hcsa_hca_dense_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype);
 int hcsa_hca_dense_attn_bwd(const void *q, const void *kh, const void *vh, int64_t h_bstride,
                             int N, int ratio, int64_t pos0, const int64_t *seq_pos,

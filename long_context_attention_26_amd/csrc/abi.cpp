@@ -546,6 +546,13 @@ static int check_bwd_grads(const float* dout, const float* dq, int B, int Nq, in
   return HCSA_OK;
 }
 
+size_t hcsa_csa_sparse_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype) {
+  if (B < 1 || Nq < 1 || H < 1 || d < 1) return 0;
+  hcsa::AttnArgs a{};
+  a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.kv_dtype = kv_dtype;
+  return hcsa::bwd_workspace_bytes(a);
+}
+
 int hcsa_csa_sparse_attn_bwd(const void* q, const void* kc, const void* vc, int64_t c_bstride,
                              int N, const int32_t* topk_idx, int k, const void* k_raw,
                              const void* v_raw, int64_t raw_bstride, int64_t T_raw,
@@ -554,7 +561,8 @@ int hcsa_csa_sparse_attn_bwd(const void* q, const void* kc, const void* vc, int6
                              float scale, const float* out, const float* lse,
                              const float* dout, const float* dlse, float* dq, float* dkc,
                              float* dvc, int64_t dc_bstride, float* dk_raw, float* dv_raw,
-                             int64_t draw_bstride, hcsa_stream stream) {
+                             int64_t draw_bstride, void* workspace, size_t ws_bytes,
+                             hcsa_stream stream) {
   int rc = check_csa(q, kc, vc, c_bstride, N, topk_idx, k, k_raw, v_raw, raw_bstride, T_raw,
                      raw_pos0, n_win, ratio, pos0, seq_pos, nullptr, kv_dtype, B, Nq, H, d,
                      scale, out, lse);
@@ -574,8 +582,10 @@ int hcsa_csa_sparse_attn_bwd(const void* q, const void* kc, const void* vc, int6
   a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
   a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
+  rc = check_ws(workspace, ws_bytes, hcsa::bwd_workspace_bytes(a));
+  if (rc) return rc;
   hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkc, dvc, dc_bstride, dk_raw, dv_raw,
-                      draw_bstride, nullptr};
+                      draw_bstride, workspace};
   return hip_status(hcsa::launch_attention_bwd(true, a, g, static_cast<hipStream_t>(stream)),
                     "hcsa_csa_sparse_attn_bwd");
 }
@@ -584,7 +594,7 @@ size_t hcsa_hca_dense_attn_bwd_workspace_size(int B, int Nq, int H, int d, int k
   if (B < 1 || Nq < 1 || H < 1 || d < 1) return 0;
   hcsa::AttnArgs a{};
   a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.kv_dtype = kv_dtype;
-  return hcsa::hca_bwd_workspace_bytes(a);
+  return hcsa::bwd_workspace_bytes(a);
 }
 
 int hcsa_hca_dense_attn_bwd(const void* q, const void* kh, const void* vh, int64_t h_bstride,
@@ -612,7 +622,7 @@ int hcsa_hca_dense_attn_bwd(const void* q, const void* kh, const void* vh, int64
   a.q = q; a.kc = kh; a.vc = vh; a.c_bstride = h_bstride; a.N = N; a.ratio = ratio;
   a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
-  rc = check_ws(workspace, ws_bytes, hcsa::hca_bwd_workspace_bytes(a));
+  rc = check_ws(workspace, ws_bytes, hcsa::bwd_workspace_bytes(a));
   if (rc) return rc;
   hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkh, dvh, dh_bstride, nullptr, nullptr, 0,
                       workspace};

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
       const int64_t li = static_cast<int64_t>(row) * 16 + h;
       s_dt[h] = part - (G.dlse ? G.dlse[li] : 0.0f);
       s_lse2[h] = G.lse[li] * kLog2e;
-      if (!DKV) G.dt_out[li] = s_dt[h];
+      if (G.dt_out) G.dt_out[li] = s_dt[h];
     }
   }
   __syncthreads();
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
           const int64_t o = r.b * G.dc_bstride + static_cast<int64_t>(code) * 128;
           dkr[i] = G.dkc + o;
           dvr[i] = G.dvc + o;
-        } else if (code != -1) {
+        } else if (code != -1 && G.dkr) {           // window rows (unless taken key-major)
           const int64_t o = r.b * G.dr_bstride + static_cast<int64_t>(-code - 2) * 128;
           dkr[i] = G.dkr + o;
           dvr[i] = G.dvr + o;
@@ -434,35 +434,52 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
   }
 }
 
-// Key-major dK / dV of HCA attention (bf16, 16 heads x 128), the entries being shared by
-// every later query token: a block owns 16 entries for a chunk of 128 query tokens; each
-// wave takes two tokens (32 query rows) per step.  S = Q K^T and dP = dout V^T run with
-// lane = entry (16x16x32, K as the B operand), so P and dS are already the B operand of
+// Key-major dK / dV for keys shared by many query tokens (bf16, 16 heads x 128): the HCA
+// entries (every later token sees them) and the CSA window rows (the next n_win tokens see
+// each).  A block owns 16 keys for a chunk of 128 query tokens; each wave takes two tokens
+// (32 query rows) per step.  S = Q K^T and dP = dout V^T run with lane = key (16x16x32, K as
+// the B operand), so P and dS are already the B operand of
 //   dK^T += Q^T dS,  dV^T += dout^T P   (16x16x32 over the step's 32 rows; Q^T and dout^T
 // built from 16-byte row slices by byte permutes, as the forward builds V^T),
 // accumulated over the chunk in registers, summed over the 4 waves in LDS and added to
 // memory once per element.  dout.o - dlse per (token, head) comes from the dq pass.
+// HCA: grid (ceil(N / 16), chunks, B), keys e0 = 16 * blockIdx.x.  Window: grid
+// (ceil((128 + n_win - 1) / 16), chunks, B), the tiles covering the band of raw rows that the
+// chunk's windows reach, from its first query's window start on.
 constexpr int kDkvEntries = 16;
 constexpr int kDkvTokens = 128;
 
-// grid: (ceil(N / 16), ceil(Nq / 128), B); block 256.
-__global__ __launch_bounds__(256) void hca_bwd_dkv_kernel(AttnBwdDev G) {
+// block 256.
+template <bool WIN>
+__global__ __launch_bounds__(256) void key_bwd_kernel(AttnBwdDev G) {
   __shared__ float s_acc[2][kDkvEntries][129];
   constexpr float kLog2e = 1.4426950408889634f;
   const AttnDev& A = G.A;
-  const int e0 = blockIdx.x * kDkvEntries, t0 = blockIdx.y * kDkvTokens, b = blockIdx.z;
+  const int t0 = blockIdx.y * kDkvTokens, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, g = lane >> 4;
-  // the chunk's last token must see the tile's first entry, else nothing to do
+  const int64_t pfirst = query_pos(A.seq_pos, A.pos0, b, t0);
   const int64_t plast = query_pos(A.seq_pos, A.pos0, b, min(t0 + kDkvTokens, A.Nq) - 1);
-  if (static_cast<int64_t>(e0 + 1) * A.ratio > plast + 1) return;      // block-uniform
+  int64_t e0;                         // first key of the tile: entry, or raw row
+  if constexpr (WIN) {
+    e0 = pfirst - A.n_win + 1 - A.raw_pos0 + static_cast<int64_t>(blockIdx.x) * kDkvEntries;
+    // rows of the tile inside the raw rows and reached by some window of the chunk
+    if (e0 + kDkvEntries <= 0 || e0 >= A.T_raw || A.raw_pos0 + e0 > plast) return;
+  } else {
+    e0 = static_cast<int64_t>(blockIdx.x) * kDkvEntries;
+    // the chunk's last token must see the tile's first entry, else nothing to do
+    if ((e0 + 1) * A.ratio > plast + 1) return;                          // block-uniform
+  }
 
-  const int e = e0 + col;
-  const bool e_ok = e < A.N;
+  const int64_t e = e0 + col;
+  const bool e_ok = WIN ? (e >= 0 && e < A.T_raw) : (e < A.N);
+  const int64_t kpos = A.raw_pos0 + e;      // window: the key's position
   u32x4 ka[4], va[4];                 // B operand: K[e][32s + 8g ..], V likewise
   {
-    const uint16_t* kr = static_cast<const uint16_t*>(A.kc) + b * A.c_bstride + static_cast<int64_t>(e) * 128;
-    const uint16_t* vr = static_cast<const uint16_t*>(A.vc) + b * A.c_bstride + static_cast<int64_t>(e) * 128;
+    const uint16_t* kr = WIN ? static_cast<const uint16_t*>(A.k_raw) + b * A.raw_bstride + e * 128
+                             : static_cast<const uint16_t*>(A.kc) + b * A.c_bstride + e * 128;
+    const uint16_t* vr = WIN ? static_cast<const uint16_t*>(A.v_raw) + b * A.raw_bstride + e * 128
+                             : static_cast<const uint16_t*>(A.vc) + b * A.c_bstride + e * 128;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       ka[s] = e_ok ? *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
@@ -484,7 +501,8 @@ __global__ __launch_bounds__(256) void hca_bwd_dkv_kernel(AttnBwdDev G) {
       const bool t_ok = tok < A.Nq;
       const int64_t row = static_cast<int64_t>(b) * A.Nq + (t_ok ? tok : 0);
       const int64_t p = query_pos(A.seq_pos, A.pos0, b, t_ok ? tok : 0);
-      const bool vis = t_ok && e_ok && static_cast<int64_t>(e + 1) * A.ratio <= p + 1;
+      const bool vis = t_ok && e_ok &&
+                       (WIN ? (kpos <= p && kpos > p - A.n_win) : (e + 1) * A.ratio <= p + 1);
       // A operands: q and dout rows of head col at channels 32s + 8g
       u32x4 qa[4], da[4];
       const uint16_t* qrow = q16 + (row * 16 + col) * 128;
@@ -561,8 +579,10 @@ __global__ __launch_bounds__(256) void hca_bwd_dkv_kernel(AttnBwdDev G) {
   }
   for (int x = threadIdx.x; x < 2 * kDkvEntries * 128; x += 256) {
     const int m = x >> 11, r = (x >> 7) & 15, c = x & 127;
-    if (e0 + r < A.N) {
-      float* dst = (m ? G.dvc : G.dkc) + b * G.dc_bstride + static_cast<int64_t>(e0 + r) * 128 + c;
+    const int64_t er = e0 + r;
+    if (WIN ? (er >= 0 && er < A.T_raw) : (er < A.N)) {
+      float* dst = WIN ? (m ? G.dvr : G.dkr) + b * G.dr_bstride + er * 128 + c
+                       : (m ? G.dvc : G.dkc) + b * G.dc_bstride + er * 128 + c;
       unsafeAtomicAdd(dst, m ? s_acc[1][r][c] : A.scale * s_acc[0][r][c]);
     }
   }
@@ -676,12 +696,12 @@ hipError_t launch_bwd_typed(const AttnBwdDev& G, int rows, int hh, int cpl, hipS
 
 }  // namespace
 
-bool hca_bwd_key_major(const AttnArgs& a) {
+bool bwd_key_major(const AttnArgs& a) {
   return a.kv_dtype == 1 && a.H == 16 && a.d == 128 && a.Nq >= 16;
 }
 
-size_t hca_bwd_workspace_bytes(const AttnArgs& a) {
-  return hca_bwd_key_major(a) ? align256(static_cast<size_t>(a.B) * a.Nq * 16 * 4) : 0;
+size_t bwd_workspace_bytes(const AttnArgs& a) {
+  return bwd_key_major(a) ? align256(static_cast<size_t>(a.B) * a.Nq * 16 * 4) : 0;
 }
 
 bool attn_bwd_shape_supported(int H, int d) {
@@ -711,17 +731,28 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
   const int hh = bwd_heads(a.H), cpl = bwd_cpl(a.d);
   const bool bf = a.kv_dtype == 1;
   if (bf && a.H == 16 && a.d == 128) {          // the matrix-core path
-    if (csa) {
+    const int chunks = (a.Nq + kDkvTokens - 1) / kDkvTokens;
+    if (csa && bwd_key_major(a) && g.ws && a.n_win > 0) {
+      // the window rows, shared by consecutive query tokens, key-major; the rest per query
+      G.dt_out = static_cast<float*>(g.ws);
+      AttnBwdDev Gq = G;
+      Gq.dkr = Gq.dvr = nullptr;
+      attn_bwd_mfma_kernel<true, true><<<rows, 256, 0, s>>>(Gq);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      dim3 grid((kDkvTokens + a.n_win - 1 + kDkvEntries - 1) / kDkvEntries, chunks, a.B);
+      key_bwd_kernel<true><<<grid, 256, 0, s>>>(G);
+    } else if (csa) {
       attn_bwd_mfma_kernel<true, true><<<rows, 256, 0, s>>>(G);
-    } else if (hca_bwd_key_major(a) && g.ws) {
+    } else if (bwd_key_major(a) && g.ws) {
       // many query tokens share the entries: dq query-major, dK / dV key-major
       G.dt_out = static_cast<float*>(g.ws);
       attn_bwd_mfma_kernel<false, false><<<rows, 256, 0, s>>>(G);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (a.N > 0) {
-        dim3 grid((a.N + kDkvEntries - 1) / kDkvEntries, (a.Nq + kDkvTokens - 1) / kDkvTokens, a.B);
-        hca_bwd_dkv_kernel<<<grid, 256, 0, s>>>(G);
+        dim3 grid((a.N + kDkvEntries - 1) / kDkvEntries, chunks, a.B);
+        key_bwd_kernel<false><<<grid, 256, 0, s>>>(G);
       }
     } else {
       attn_bwd_mfma_kernel<false, true><<<rows, 256, 0, s>>>(G);

@@ -88,12 +88,13 @@ struct AttnBwdArgs {
   float* dkr;           // [B][T_raw][d] F32, accumulated (CSA window rows)
   float* dvr;
   int64_t dr_bstride;
-  void* ws;             // HCA: hca_bwd_workspace_bytes(a) bytes (or null)
+  void* ws;             // bwd_workspace_bytes(a) bytes (or null)
 };
-// HCA backward with many query tokens (bf16 16 x 128) runs dq query-major and dK / dV
-// key-major; the per-(token, head) terms pass through the workspace.
-bool hca_bwd_key_major(const AttnArgs& a);
-size_t hca_bwd_workspace_bytes(const AttnArgs& a);
+// Backward with many query tokens (bf16 16 x 128): the keys shared by consecutive tokens
+// (HCA entries, CSA window rows) get their gradients key-major; the per-(token, head) terms
+// of the query-major pass reach that kernel through the workspace.
+bool bwd_key_major(const AttnArgs& a);
+size_t bwd_workspace_bytes(const AttnArgs& a);
 // register tiling of the backward kernel: heads rounded up to 4, 16, 32 or 64 and channels
 // per lane (d / 64 rounded up to 1, 2 or 4); supported when heads * channels <= 64
 inline int bwd_heads(int H) { return H <= 4 ? 4 : H <= 16 ? 16 : H <= 32 ? 32 : H <= 64 ? 64 : 0; }

@@ -33,9 +33,10 @@ _SIGS = {
     "hcsa_csa_hca_attn": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64, _i, _i,
                                _p, _p, _i64, _i, _i, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _p,
                                _p, _p, _p, _p, _sz, _p]),
+    "hcsa_csa_sparse_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_csa_sparse_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64,
                                       _i, _i, _i64, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p,
-                                      _p, _p, _p, _p, _i64, _p, _p, _i64, _p]),
+                                      _p, _p, _p, _p, _i64, _p, _p, _i64, _p, _sz, _p]),
     "hcsa_hca_dense_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_hca_dense_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _p, _i, _i, _i, _i, _i,
                                      _f, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _sz, _p]),
@@ -323,11 +324,14 @@ def hca_dense_attn(q, kh, vh, N, ratio, pos0, scale, out, lse, workspace=None, s
 
 def csa_sparse_attn_bwd(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio, pos0,
                         scale, out, lse, dout, dq, dkc, dvc, dk_raw, dv_raw, dlse=None,
-                        stream=None, seq_pos=None):
+                        workspace=None, stream=None, seq_pos=None):
     """Backward of csa_sparse_attn: writes dq [B, Nq, H, d] f32; adds into dkc, dvc
     [B, >=N, d] f32 and dk_raw, dv_raw [B, T_raw, d] f32."""
     B, Nq, H, d = q.shape
     k = topk_idx.shape[-1]
+    nbytes = lib.hcsa_csa_sparse_attn_bwd_workspace_size(B, Nq, H, d, dtype_code(q))
+    if workspace is None and nbytes:
+        workspace = alloc_workspace(nbytes, q.device)
     _check(lib.hcsa_csa_sparse_attn_bwd(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N,
                                         _ptr(topk_idx), k, _ptr(k_raw), _ptr(v_raw),
                                         k_raw.stride(0), k_raw.shape[1], raw_pos0, n_win, ratio,
@@ -335,6 +339,8 @@ def csa_sparse_attn_bwd(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, r
                                         scale, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse),
                                         _ptr(dq), _ptr(dkc), _ptr(dvc), dkc.stride(0),
                                         _ptr(dk_raw), _ptr(dv_raw), dk_raw.stride(0),
+                                        _ptr(workspace),
+                                        0 if workspace is None else workspace.numel(),
                                         _stream(stream)))
     return dq
 

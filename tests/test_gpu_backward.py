@@ -56,6 +56,10 @@ CSA_CASES = [
     dict(dt="bf16", H=5, d=96, N=150, k=40, n_win=20, Nq=2, B=1, pos0=640, dlse=True),
     # nothing to attend
     dict(dt="f32", H=2, d=32, N=100, k=0, n_win=0, Nq=1, B=1, pos0=399, dlse=True),
+    # many query tokens (window rows key-major): raw rows starting past position 0, and
+    # windows clipped at position 0 with padded selections
+    dict(dt="bf16", H=16, d=128, N=900, k=128, n_win=128, Nq=300, B=2, pos0=3300, dlse=True),
+    dict(dt="bf16", H=16, d=128, N=80, k=64, n_win=64, Nq=200, B=1, pos0=20, dlse=False),
 ]
 
 
