@@ -17,11 +17,11 @@
 // the row is >= L while at least k keys are (checked).
 //  - Many short rows (prefill: >= 64 rows of <= 128K keys): one block per row streams the
 //    row once (topk_rows_kernel), sampling the first chunks it loads.
-//  - Otherwise (decode: a few long rows): seg_floor_kernel (a block per row: 4096 keys from
-//    evenly spaced 16-byte chunks, the floor, the row's segment counters zeroed),
-//    seg_extract_kernel (a block per 8192-key segment: the segment's keys >= L into its
-//    candidate list, in index order) and seg_resolve_kernel (a block per row: T among the
-//    concatenated lists and the ordered output).
+//  - Otherwise (decode: a few long rows): seg_extract_kernel (a block per 8192-key segment:
+//    the row's floor from 4096 keys at evenly spaced 16-byte chunks, the same in every
+//    block of the row, then the segment's keys >= L into its candidate list, in index
+//    order) and seg_resolve_kernel (a block per row: T among the concatenated lists by
+//    8-bit LDS histogram passes, and the ordered output).
 // When the candidates overflow their lists or fall short of k (massive ties, a skewed row,
 // an unlucky sample), T is found bit by bit over the whole row and the output is written by
 // an ordered ballot compaction.  Every step is integer-only, so results do not depend on
@@ -292,12 +292,17 @@ __device__ void select_exact_row(const RowView<KB>& V, int k, int32_t* out,
 
 // Exact selection among candidates (all >= L) held by NT threads in order: thread t holds
 // the candidates [t*per, t*per + cnt_t) of the list (keys ck, indices cj, cnt_t <= PER).
-// The bits of T above the highest one in which some candidate differs from L are shared
-// by every candidate and by T, so the bit-by-bit search starts below them.
+// The bits of T above the highest one in which some candidate differs from L (bit nb - 1)
+// are shared by every candidate and by T; the bits below are found 8 at a time from bit
+// nb - 1 down, each pass an LDS histogram of the digit over the candidates that match T so
+// far (two passes for BF16 keys, at most four for F32).  Digits taken from the top of the
+// differing bits spread the candidates over the bins; digits aligned to bytes would pile
+// them into the few bins of their common exponent, and LDS atomics on one address
+// serialise.
 template <int KB, int NT, int PER>
 __device__ void select_candidates(const uint32_t (&ck)[PER], const int32_t (&cj)[PER], int cnt,
-                                  uint32_t L, int k, int32_t* out, int (*s_cnt)[NT / 64],
-                                  int* s_gt, int* s_eq, int* s_hb) {
+                                  uint32_t L, int k, int32_t* out, int* s_gt, int* s_eq,
+                                  int* s_hb, int (*s_hist)[256], int* s_sel) {
   constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t below = (1ull << lane) - 1;
@@ -312,18 +317,34 @@ __device__ void select_candidates(const uint32_t (&ck)[PER], const int32_t (&cj)
     }
   }
   if (lane == 0) s_hb[w] = hb;
+  for (int i = threadIdx.x; i < 512; i += NT) s_hist[i >> 8][i & 255] = 0;
   __syncthreads();
   int nb = 0;
 #pragma unroll
   for (int u = 0; u < W; ++u) nb = s_hb[u] > nb ? s_hb[u] : nb;
+  const int D = (nb + 7) / 8;
   uint32_t T = nb >= 32 ? 0u : (L >> nb) << nb;
+  int rem = k;                                   // rank of T among the candidates still open
 #pragma unroll 1
-  for (int b = nb - 1; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    int n = 0;
+  for (int p = 0; p < D; ++p) {
+    const int top = nb - 8 * p;                  // this pass: bits [sh, top)
+    const int sh = top > 8 ? top - 8 : 0;
+    const uint32_t dmask = (1u << (top - sh)) - 1u;
+    int* hist = s_hist[p & 1];
+    const uint32_t hi = top >= 32 ? 0u : T >> top;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) n += u < cnt && ck[u] >= cand;
-    if (block_total_bits<W, 5>(n, s_cnt, b & 1) >= k) T = cand;
+    for (int u = 0; u < PER; ++u)
+      if (u < cnt && (top >= 32 || (ck[u] >> top) == hi))
+        atomicAdd(&hist[(ck[u] >> sh) & dmask], 1);
+    if (p >= 1)                                  // the previous pass's bins, read already
+      for (int i = threadIdx.x; i < 256; i += NT) s_hist[(p + 1) & 1][i] = 0;
+    __syncthreads();
+    if (w == 0) hist_pick(hist, rem, s_sel);
+    __syncthreads();
+    // every thread reads s_sel before it reaches the next pass's first barrier, and the
+    // next pick comes after that barrier
+    T |= static_cast<uint32_t>(s_sel[0]) << sh;
+    rem -= s_sel[1];
   }
   int gt = 0, eq = 0;
 #pragma unroll
@@ -518,20 +539,23 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
   int nb = 0;
 #pragma unroll
   for (int u = 0; u < kRowsWaves; ++u) nb = s_hb[u] > nb ? s_hb[u] : nb;
-  // T = the k-th largest candidate, 8 bits a pass below the bits every candidate shares
-  // with L: an LDS histogram of the pass's digit over the candidates that match T so far
+  // T = the k-th largest candidate, 8 bits a pass from the highest bit in which the
+  // candidates differ from L: an LDS histogram of the pass's digit over the candidates that
+  // match T so far (digits from the top of the differing bits spread over the bins)
   const int D = (nb + 7) / 8;
-  uint32_t T = 8 * D >= 32 ? 0u : (L >> (8 * D)) << (8 * D);
+  uint32_t T = nb >= 32 ? 0u : (L >> nb) << nb;
   int rem = P.k;                                 // rank of T among the candidates still open
 #pragma unroll 1
   for (int p = 0; p < D; ++p) {
-    const int sh = 8 * (D - 1 - p);
+    const int top = nb - 8 * p;                  // this pass: bits [sh, top)
+    const int sh = top > 8 ? top - 8 : 0;
+    const uint32_t dmask = (1u << (top - sh)) - 1u;
     int* hist = s_hist[p & 1];
-    const uint32_t hi = sh + 8 >= 32 ? 0u : T >> (sh + 8);
+    const uint32_t hi = top >= 32 ? 0u : T >> top;
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
       const bool in = 64 * u + lane < wslot;
-      if (in && (sh + 8 >= 32 || (ck[u] >> (sh + 8)) == hi)) atomicAdd(&hist[(ck[u] >> sh) & 255u], 1);
+      if (in && (top >= 32 || (ck[u] >> top) == hi)) atomicAdd(&hist[(ck[u] >> sh) & dmask], 1);
     }
     if (p >= 1) s_hist[(p + 1) & 1][threadIdx.x & 255] = 0;   // the previous pass's bins
     __syncthreads();
@@ -590,7 +614,6 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
 constexpr int kSegKeys = 8192;            // keys per segment (one extract block)
 constexpr int kSegCap = 1024;             // candidate list per segment
 constexpr int kSegThreads = 256;
-constexpr int kFloorThreads = 256;
 constexpr int kFloorSamples = 4096;       // 16 per thread
 constexpr int kResThreads = 512;
 constexpr int kResPer = 16;               // candidates per resolve thread at most
@@ -604,73 +627,90 @@ struct SegWs {
   int nseg;
 };
 
-// grid: rows; block 256.  The floor of each row from 4096 sampled keys, and the row's
-// segment counters zeroed.
-template <int KB>
-__global__ __launch_bounds__(kFloorThreads) void seg_floor_kernel(TopkDev P, SegWs S, int vec) {
-  constexpr int W = kFloorThreads / 64;
-  __shared__ int s_rdx[2][W][3];
-  const int row = blockIdx.x;
-  const RowView<KB> V(P, row, vec);
+// The row's candidate floor from 4096 keys in 32 runs of 16 consecutive 16-byte chunks (two
+// cache lines) at evenly spaced positions; every block of the row samples the same keys
+// and so finds the same floor.  Called by all NT threads.
+// Only the candidate count depends on the floor (too few or too many candidates send the
+// row to the exact path), so it is an estimate of the 16-bit prefix of the m-th largest
+// sample, m about twice the rank at which the k-th largest key is expected:
+//  - shallow ranks (the decode case): each thread keeps the largest of its samples, and the
+//    m-th largest of these group maxima stands in for the m-th largest sample (it is at or
+//    below it, so it admits slightly more candidates); one ballot per tested threshold;
+//  - deeper ranks: the m-th largest sample itself, every sample counted per threshold.
+// Each wave finds the ceil(m/W)-th largest of its own values by radix 4 from the top
+// (ballot counts, no barriers); the floor is the smallest of the W results, at or below
+// the block's m-th largest.
+template <int KB, int NT>
+__device__ uint32_t row_floor(const RowView<KB>& V, int k, uint32_t* s_min) {
+  constexpr int W = NT / 64;
   const int nv = V.nv;
-  for (int s = threadIdx.x; s < S.nseg; s += kFloorThreads)
-    S.cnt[static_cast<int64_t>(row) * S.nseg + s] = 0u;
-  if (P.k >= nv || nv <= kSegCap) {              // every visible key is a candidate
-    if (threadIdx.x == 0) S.floor[row] = 0u;
-    return;
-  }
+  if (nv <= kSegCap) return 0u;                  // every visible key is a candidate
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // samples: whole 16-byte chunks at evenly spaced chunk positions, 4096 keys in two loads
-  // per thread (chunks hold 8 BF16 or 4 F32 keys)
   using V_t = RowView<KB>;
   constexpr int EPC = V_t::EPC;
-  constexpr int NPOS = kFloorSamples / EPC;      // sampled chunks
-  constexpr int LPT = NPOS / kFloorThreads;      // per thread
+  constexpr int NPOS = kFloorSamples / EPC;      // sampled 16-byte chunks (8 BF16 / 4 F32 keys)
+  constexpr int LPT = NPOS / NT;                 // per thread
   constexpr int PT = LPT * EPC;
-  const int nch = V.nchunks();                   // positions repeat when nch < NPOS
+  constexpr int RUN = 16, NRUN = NPOS / RUN;     // runs of consecutive chunks
+  const int nch = V.nchunks();                   // runs overlap when nch < NPOS
+  // a missing key (past the visible count, last chunk only) reads as 0 and never counts:
+  // every tested threshold is >= 1
   uint32_t top[PT];
 #pragma unroll
   for (int u = 0; u < LPT; ++u) {
-    const int c = static_cast<int>(static_cast<int64_t>(threadIdx.x + u * kFloorThreads) * nch / NPOS);
+    const int i = threadIdx.x + u * NT, run = i / RUN;
+    const int r0 = static_cast<int>(static_cast<int64_t>(run) * nch / NRUN);
+    const int c = min(r0 + i % RUN, nch - 1);
     const u32x4 x = V.load_raw(c);
-    const int r = nv - c * EPC;                  // visible keys of the chunk (last chunk: fewer)
+    const int r = nv - c * EPC;                  // visible keys of the chunk
 #pragma unroll
     for (int e = 0; e < EPC; ++e)
       top[u * EPC + e] = e < r ? V_t::to_key(V_t::raw_of(x, e)) >> (KB - 16) : 0u;
   }
-  // all but at most one sampled chunk are full; a missing key reads as 0 and never counts
-  // (every tested threshold is >= 1).  Each wave selects the ceil(m/W)-th largest of its
-  // own 1024 samples (radix 4 from the top, ballot counts, no barriers) and the floor is the
-  // smallest of the W results: at least m samples are >= it, so it is at or below the
-  // block's m-th largest sample.  Only the candidate count depends on the floor.
   const int m = min(kFloorSamples - EPC,
-                    static_cast<int>((2LL * P.k * kFloorSamples + nv - 1) / nv) + 8);
+                    static_cast<int>((2LL * k * kFloorSamples + nv - 1) / nv) + 8);
   const int mw = (m + W - 1) / W;
   uint32_t pre = 0;
+  if (mw <= 16) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) mx = max(mx, top[u]);
 #pragma unroll 1
-  for (int sh = 14; sh >= 0; sh -= 2) {
-    int cnt[3];
+    for (int sh = 14; sh >= 0; sh -= 2) {
+      int cnt[3];
 #pragma unroll
-    for (int d = 1; d <= 3; ++d) {
-      const uint32_t th = pre | (static_cast<uint32_t>(d) << sh);
-      int n = 0;
-#pragma unroll
-      for (int u = 0; u < PT; ++u) n += top[u] >= th;
-      cnt[d - 1] = wave_sum_bits<5>(n);
+      for (int d = 1; d <= 3; ++d)
+        cnt[d - 1] = __popcll(__ballot(mx >= (pre | (static_cast<uint32_t>(d) << sh))));
+      const uint32_t d = cnt[2] >= mw ? 3u : cnt[1] >= mw ? 2u : cnt[0] >= mw ? 1u : 0u;
+      pre |= d << sh;
     }
-    const uint32_t d = cnt[2] >= mw ? 3u : cnt[1] >= mw ? 2u : cnt[0] >= mw ? 1u : 0u;
-    pre |= d << sh;
+  } else {
+#pragma unroll 1
+    for (int sh = 14; sh >= 0; sh -= 2) {
+      int cnt[3];
+#pragma unroll
+      for (int d = 1; d <= 3; ++d) {
+        const uint32_t th = pre | (static_cast<uint32_t>(d) << sh);
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < PT; ++u) n += top[u] >= th;
+        cnt[d - 1] = wave_sum_bits<5>(n);
+      }
+      const uint32_t d = cnt[2] >= mw ? 3u : cnt[1] >= mw ? 2u : cnt[0] >= mw ? 1u : 0u;
+      pre |= d << sh;
+    }
   }
-  if (lane == 0) s_rdx[0][w][0] = static_cast<int>(pre);
+  if (lane == 0) s_min[w] = pre;
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < W; ++u) pre = min(pre, static_cast<uint32_t>(s_rdx[0][u][0]));
-  if (threadIdx.x == 0) S.floor[row] = pre << (KB - 16);
+  for (int u = 0; u < W; ++u) pre = min(pre, s_min[u]);
+  return pre << (KB - 16);
 }
 
-// grid: (nseg, rows); block 256.  Wave w owns 1/4 of the segment's chunks, lane l chunks
-// 64u + l of it (4 chunks for BF16 keys, 8 for F32); the keys >= floor go to the segment's
-// list in index order.
+// grid: (nseg, rows); block 256.  The row's floor (block 0 of the row stores it), then the
+// segment: wave w owns 1/4 of its chunks, lane l chunks 64u + l of it (4 chunks for BF16
+// keys, 8 for F32); the keys >= floor go to the segment's list in index order, and the
+// segment's count (which may exceed the list) to the counters.
 template <int KB>
 __global__ __launch_bounds__(kSegThreads) void seg_extract_kernel(TopkDev P, SegWs S, int vec) {
   using V_t = RowView<KB>;
@@ -679,12 +719,12 @@ __global__ __launch_bounds__(kSegThreads) void seg_extract_kernel(TopkDev P, Seg
   constexpr int CPW = kSegKeys / EPC / W;        // chunks per wave
   constexpr int CPL = CPW / 64;                  // chunks per lane
   __shared__ int s_w[W];
+  __shared__ uint32_t s_min[W];
   const int row = blockIdx.y, seg = blockIdx.x;
   const V_t V(P, row, vec);
   if (P.k >= V.nv || seg * kSegKeys >= V.nv) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t below = (1ull << lane) - 1;
-  const uint32_t L = S.floor[row];
   const int nch = V.nchunks();
   const int ch0 = seg * (kSegKeys / EPC) + w * CPW + lane;
   u32x4 x[CPL];
@@ -693,6 +733,8 @@ __global__ __launch_bounds__(kSegThreads) void seg_extract_kernel(TopkDev P, Seg
     const int ch = ch0 + 64 * u;
     x[u] = ch < nch ? V.load_raw(ch) : u32x4{0u, 0u, 0u, 0u};
   }
+  const uint32_t L = row_floor<KB, kSegThreads>(V, P.k, s_min);
+  if (seg == 0 && threadIdx.x == 0) S.floor[row] = L;
   uint32_t msk[CPL];
   int c = 0;
 #pragma unroll
@@ -738,6 +780,8 @@ __global__ __launch_bounds__(kResThreads) void seg_resolve_kernel(TopkDev P, Seg
   __shared__ int s_pre[kResMaxSeg + 1];
   __shared__ int s_cnt[2][W];
   __shared__ int s_gt[W], s_eq[W], s_hb[W];
+  __shared__ int s_hist[2][256];
+  __shared__ int s_sel[4];
   __shared__ int s_over;
   const int row = blockIdx.x;
   const RowView<KB> V(P, row, vec);
@@ -749,18 +793,28 @@ __global__ __launch_bounds__(kResThreads) void seg_resolve_kernel(TopkDev P, Seg
   }
   const int nseg = (nv + kSegKeys - 1) / kSegKeys;   // segments holding visible keys
   const uint32_t* cnt = S.cnt + static_cast<int64_t>(row) * S.nseg;
-  for (int s = threadIdx.x; s < nseg; s += kResThreads) s_pre[s + 1] = static_cast<int>(cnt[s]);
-  __syncthreads();
-  if (threadIdx.x == 0) {                        // prefix of the segment counts
-    int acc = 0, over = 0;
-    s_pre[0] = 0;
-    for (int s = 1; s <= nseg; ++s) {
-      const int c = s_pre[s];
-      acc += c < kSegCap ? c : kSegCap;
+  if (threadIdx.x < 64) {                        // prefix of the listed counts, 64 at a time
+    const int lane = threadIdx.x;
+    int carry = 0;
+    bool over = false;
+    for (int base = 0; base < nseg; base += 64) {
+      const int sg = base + lane;
+      const int c = sg < nseg ? static_cast<int>(cnt[sg]) : 0;
       over |= c > kSegCap;
-      s_pre[s] = acc;
+      int inc = c < kSegCap ? c : kSegCap;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += y;
+      }
+      if (sg < nseg) s_pre[sg + 1] = carry + inc;
+      carry += __shfl(inc, 63, kWave);
     }
-    s_over = over;
+    const bool any_over = __ballot(over) != 0;
+    if (lane == 0) {
+      s_pre[0] = 0;
+      s_over = any_over;
+    }
   }
   __syncthreads();
   const int C = s_pre[nseg];
@@ -793,8 +847,8 @@ __global__ __launch_bounds__(kResThreads) void seg_resolve_kernel(TopkDev P, Seg
       cj[u] = static_cast<int32_t>(v & 0xffffffffu);
     }
   }
-  select_candidates<KB, kResThreads, kResPer>(ck, cj, my, S.floor[row], P.k, out, s_cnt, s_gt,
-                                              s_eq, s_hb);
+  select_candidates<KB, kResThreads, kResPer>(ck, cj, my, S.floor[row], P.k, out, s_gt, s_eq,
+                                              s_hb, s_hist, s_sel);
 }
 
 }  // namespace
@@ -849,11 +903,9 @@ hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype
   S.nseg = plan.nseg;
   const dim3 grid(plan.nseg, plan.rows);
   if (plan.key_bits == 16) {
-    seg_floor_kernel<16><<<plan.rows, kFloorThreads, 0, s>>>(P, S, vec);
     seg_extract_kernel<16><<<grid, kSegThreads, 0, s>>>(P, S, vec);
     seg_resolve_kernel<16><<<plan.rows, kResThreads, 0, s>>>(P, S, vec);
   } else {
-    seg_floor_kernel<32><<<plan.rows, kFloorThreads, 0, s>>>(P, S, vec);
     seg_extract_kernel<32><<<grid, kSegThreads, 0, s>>>(P, S, vec);
     seg_resolve_kernel<32><<<plan.rows, kResThreads, 0, s>>>(P, S, vec);
   }
