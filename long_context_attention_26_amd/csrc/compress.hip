@@ -68,36 +68,72 @@ __device__ __forceinline__ int64_t src_off(int64_t ring, int64_t x_bs, int D, in
   return PAGED ? xrow * D : b * x_bs + j * r * D;
 }
 
+// 8 channels of one input row as loaded (BF16: one 16-byte word, F32: two), so that a row's
+// load can be issued before its pooling weight is known.
+template <bool IN_BF16>
+struct Row8 {
+  u32x4 w[IN_BF16 ? 1 : 2];
+  __device__ __forceinline__ void load(const char* p) {
+    w[0] = *reinterpret_cast<const u32x4*>(p);
+    if constexpr (!IN_BF16) w[1] = *reinterpret_cast<const u32x4*>(p + 16);
+  }
+  __device__ __forceinline__ void fma_into(float a, float (&acc)[8]) const {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (IN_BF16) {
+        acc[2 * c] = fmaf(a, bf16_lo(w[0][c]), acc[2 * c]);
+        acc[2 * c + 1] = fmaf(a, bf16_hi(w[0][c]), acc[2 * c + 1]);
+      } else {
+        acc[c] = fmaf(a, __uint_as_float(w[0][c]), acc[c]);
+        acc[4 + c] = fmaf(a, __uint_as_float(w[1][c]), acc[4 + c]);
+      }
+    }
+  }
+};
+
 // One block of the pooling: this thread's 8 channels of entry `j` (block-local row `local`).
+// The first rows are loaded before the weights softmax(omega) are formed in `alpha` (a
+// block-wide step), so the two memory latencies overlap; every thread of the block calls.
 template <bool IN_BF16, int OUT, bool PAGED = false>
 __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_bs, int D,
-                                          const float* alpha, int r, void* __restrict__ y,
-                                          int64_t y_bs, uint8_t* __restrict__ ys, int64_t ys_bs,
-                                          int n_out, int64_t jblock, int b,
+                                          const float* __restrict__ omega, float* alpha, int r,
+                                          void* __restrict__ y, int64_t y_bs,
+                                          uint8_t* __restrict__ ys, int64_t ys_bs, int n_out,
+                                          int64_t jblock, int b,
                                           const PageMap& pm = PageMap{nullptr, 0},
                                           int64_t pos0 = 0, int64_t ring = 0) {
+  constexpr int PF = 4;                         // rows loaded ahead of the weights
   const int tpr = D >> 3;                       // threads per output row
   const int rows_per_block = blockDim.x / tpr;
   const int local = threadIdx.x / tpr;
   const int c8 = threadIdx.x - local * tpr;
-  if (local >= rows_per_block) return;
   const int64_t j = jblock * rows_per_block + local;
-  if (j >= n_out) return;
+  const bool active = local < rows_per_block && j < n_out;
   constexpr int ES = IN_BF16 ? 2 : 4;
-  int64_t xrow = 0, yrow = 0;
-  if constexpr (PAGED) paged_rows(pm, b, pos0, r, j, xrow, yrow);
-  const char* src = static_cast<const char*>(x) +
-                    (src_off<PAGED>(ring, x_bs, D, b, pos0, r, j, xrow) + c8 * 8) * ES;
   const int64_t row_bytes = static_cast<int64_t>(D) * ES;
+  int64_t xrow = 0, yrow = 0;
+  const char* src = nullptr;
+  Row8<IN_BF16> pre[PF];
+  if (active) {
+    if constexpr (PAGED) paged_rows(pm, b, pos0, r, j, xrow, yrow);
+    src = static_cast<const char*>(x) +
+          (src_off<PAGED>(ring, x_bs, D, b, pos0, r, j, xrow) + c8 * 8) * ES;
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (u < r) pre[u].load(src + u * row_bytes);
+  }
+  pool_weights(omega, r, alpha);
+  if (!active) return;
 
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int i = 0; i < r; ++i) {
-    float v[8];
-    load8<IN_BF16>(src + i * row_bytes, v);
-    const float a = alpha[i];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = fmaf(a, v[c], acc[c]);
+  for (int u = 0; u < PF; ++u)
+    if (u < r) pre[u].fma_into(alpha[u], acc);
+#pragma unroll 4
+  for (int i = PF; i < r; ++i) {
+    Row8<IN_BF16> v;
+    v.load(src + i * row_bytes);
+    v.fma_into(alpha[i], acc);
   }
 
   if constexpr (OUT == OUT_MXFP4) {
@@ -110,35 +146,46 @@ __device__ __forceinline__ void pool_rows(const void* __restrict__ x, int64_t x_
 
 // Long blocks (ratio >= kWideRatio): one block per output entry.  Thread (g, c8) sums
 // rows g, g + G, g + 2G, ... of its 8 channels (G = 256 / (D/8) row groups), so all of a
-// thread's loads are independent; the G partial sums are added in group order in LDS.
+// thread's loads are independent (the first PF of them issued before the weights are
+// formed); the G partial sums are added in group order in LDS.
 constexpr int kWideRatio = 32;
 
 template <bool IN_BF16, int OUT, bool PAGED = false>
 __device__ __forceinline__ void pool_rows_wide(const void* __restrict__ x, int64_t x_bs, int D,
-                                               const float* alpha, int r, void* __restrict__ y,
-                                               int64_t y_bs, uint8_t* __restrict__ ys,
-                                               int64_t ys_bs, int64_t j, int b, float* s_part,
+                                               const float* __restrict__ omega, float* alpha,
+                                               int r, void* __restrict__ y, int64_t y_bs,
+                                               uint8_t* __restrict__ ys, int64_t ys_bs,
+                                               int64_t j, int b, float* s_part,
                                                const PageMap& pm = PageMap{nullptr, 0},
                                                int64_t pos0 = 0, int64_t ring = 0) {
+  constexpr int PF = 8;
   const int tpr = D >> 3;
   const int G = blockDim.x / tpr;
   const int g = threadIdx.x / tpr;
   const int c8 = threadIdx.x - g * tpr;
   constexpr int ES = IN_BF16 ? 2 : 4;
+  const int64_t row_bytes = static_cast<int64_t>(D) * ES;
   int64_t xrow = 0, yrow = 0;
   if constexpr (PAGED) paged_rows(pm, b, pos0, r, j, xrow, yrow);
+  const char* src = static_cast<const char*>(x) +
+                    (src_off<PAGED>(ring, x_bs, D, b, pos0, r, j, xrow) + c8 * 8) * ES;
+  Row8<IN_BF16> pre[PF];
+  if (g < G) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (g + u * G < r) pre[u].load(src + (g + u * G) * row_bytes);
+  }
+  pool_weights(omega, r, alpha);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (g < G) {
-    const char* src = static_cast<const char*>(x) +
-                      (src_off<PAGED>(ring, x_bs, D, b, pos0, r, j, xrow) + c8 * 8) * ES;
-    const int64_t row_bytes = static_cast<int64_t>(D) * ES;
-#pragma unroll 8
-    for (int i = g; i < r; i += G) {
-      float v[8];
-      load8<IN_BF16>(src + i * row_bytes, v);
-      const float a = alpha[i];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = fmaf(a, v[c], acc[c]);
+    for (int u = 0; u < PF; ++u)
+      if (g + u * G < r) pre[u].fma_into(alpha[g + u * G], acc);
+#pragma unroll 8
+    for (int i = g + PF * G; i < r; i += G) {
+      Row8<IN_BF16> v;
+      v.load(src + i * row_bytes);
+      v.fma_into(alpha[i], acc);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) s_part[g * D + c8 * 8 + c] = acc[c];
@@ -176,13 +223,12 @@ __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ 
                                                        int n_out) {
   __shared__ float alpha[1024];
   __shared__ float s_part[2048];
-  pool_weights(omega, r, alpha);
   if (r >= kWideRatio)
-    pool_rows_wide<IN_BF16, OUT>(x, x_bs, D, alpha, r, y, y_bs, ys, ys_bs, blockIdx.x,
+    pool_rows_wide<IN_BF16, OUT>(x, x_bs, D, omega, alpha, r, y, y_bs, ys, ys_bs, blockIdx.x,
                                  blockIdx.y, s_part);
   else
-    pool_rows<IN_BF16, OUT>(x, x_bs, D, alpha, r, y, y_bs, ys, ys_bs, n_out, blockIdx.x,
-                            blockIdx.y);
+    pool_rows<IN_BF16, OUT>(x, x_bs, D, omega, alpha, r, y, y_bs, ys, ys_bs, n_out,
+                            blockIdx.x, blockIdx.y);
 }
 
 // Several pooling jobs in one launch (the blocks completed by a decode token in every
@@ -197,16 +243,16 @@ struct PoolJobs {
 
 template <bool IN_BF16, int OUT, bool PAGED>
 __device__ __forceinline__ void pool_job_blocks(const hcsa_pool_job& q, const PageMap& pm,
-                                                int64_t ring, const float* alpha, int64_t jb,
+                                                int64_t ring, float* alpha, int64_t jb,
                                                 int n_out, float* s_part) {
   if (q.ratio >= kWideRatio)
-    pool_rows_wide<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y,
+    pool_rows_wide<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, q.omega, alpha, q.ratio, q.y,
                                         q.y_bstride, q.y_scales, q.ys_bstride, jb, blockIdx.y,
                                         s_part, pm, q.pos0, ring);
   else
-    pool_rows<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, alpha, q.ratio, q.y, q.y_bstride,
-                                   q.y_scales, q.ys_bstride, n_out, jb, blockIdx.y, pm, q.pos0,
-                                   ring);
+    pool_rows<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, q.omega, alpha, q.ratio, q.y,
+                                   q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb,
+                                   blockIdx.y, pm, q.pos0, ring);
 }
 
 template <bool PAGED>
@@ -216,7 +262,6 @@ __global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
   int t = 0;
   while (t + 1 < J.n && static_cast<int>(blockIdx.x) >= J.first_block[t + 1]) ++t;
   const hcsa_pool_job& q = J.job[t];
-  pool_weights(q.omega, q.ratio, alpha);
   const int64_t jb = blockIdx.x - J.first_block[t];
   const int n_out = q.T / q.ratio;
   const bool ib = q.x_dtype == 1;
