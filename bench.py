@@ -93,8 +93,7 @@ def measured_traffic(cfg, mx_fp8=False):
         rec = json.load(f)
     src = open(os.path.join(ROOT, "long_context_attention_26_amd", "csrc", "indexer.hip")).read()
     try:
-        a = src.index("template <int HI, bool QBF16, bool SBF16, bool PAGED, bool F8>\n"
-                      "__global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel")
+        a = src.index("constexpr int kMxMaxUnits = 16 * 4;")
         b = src.index("template <int HI, bool QBF16, bool F8>\nhipError_t launch_mx_mfma_hi(")
     except ValueError:
         return None
@@ -356,8 +355,8 @@ def main():
             stp.mx_fp8 = True
     torch.cuda.synchronize()
 
-    # Each copy's step is captured as one HIP graph, and once more as three graphs (pooling +
-    # selector clear | indexer scores | top-k + CSA + HCA attention).  Every SAMPLE-th timed
+    # Each copy's step is captured as one HIP graph, and once more as three graphs (pooling |
+    # indexer + top-k | CSA + HCA attention).  Every SAMPLE-th timed
     # step runs the three-graph form with timing events between the graphs on the launch
     # stream: they give the per-stage split and the indexer kernel's duration for the
     # roofline.  The SAMPLE - 1 steps between two sampled ones replay one graph that chains
@@ -365,7 +364,7 @@ def main():
     # per-token graph chains its layers: the host's graph-launch latency, several
     # microseconds per launch, then falls on one step in SAMPLE instead of every step.
     SAMPLE = 8
-    stages = ["pool", "index_scores", "select_attend"]
+    stages = ["pool", "index_topk", "attend"]
     full, split = [], []
     cap_stream = torch.cuda.Stream()
     for stp in steps:
@@ -377,17 +376,17 @@ def main():
         with torch.cuda.stream(cap_stream):
             g_all.capture_begin()
             stp.run_pool(cfg.pos0)
-            stp.run_index_scores(qi, wi, cfg.pos0)
-            stp.run_select_attend(q, cfg.pos0)
+            stp.run_index_topk(qi, wi, cfg.pos0)
+            stp.run_attend(q, cfg.pos0)
             g_all.capture_end()
             g_pool.capture_begin()
             stp.run_pool(cfg.pos0)
             g_pool.capture_end()
             g_idx.capture_begin()
-            stp.run_index_scores(qi, wi, cfg.pos0)
+            stp.run_index_topk(qi, wi, cfg.pos0)
             g_idx.capture_end()
             g_rest.capture_begin()
-            stp.run_select_attend(q, cfg.pos0)
+            stp.run_attend(q, cfg.pos0)
             g_rest.capture_end()
         full.append(g_all)
         split.append((g_pool, g_idx, g_rest))
@@ -400,8 +399,8 @@ def main():
             for j in range(SAMPLE - 1):
                 stp = steps[(c + j) % R]
                 stp.run_pool(cfg.pos0)
-                stp.run_index_scores(qi, wi, cfg.pos0)
-                stp.run_select_attend(q, cfg.pos0)
+                stp.run_index_topk(qi, wi, cfg.pos0)
+                stp.run_attend(q, cfg.pos0)
             g.capture_end()
         chain.append(g)
     torch.cuda.synchronize()
@@ -412,8 +411,9 @@ def main():
 
     def one_step(i, timed):
         if timed and i % SAMPLE == 0:
-            # sampled step: pooling graph, the indexer launched directly with dispatch-recorded
-            # events (its own execution time), then the selection + attention graph
+            # sampled step: pooling graph, the indexer + top-k call launched directly (its key
+            # scan kernel records dispatch-level events: its own execution time), then the
+            # attention graph
             g = split[i % R]
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -421,7 +421,7 @@ def main():
             g[0].replay()
             e[1].record()
             hcsa.time_next_indexer(k0, k1)
-            steps[i % R].run_index_scores(qi, wi, cfg.pos0)
+            steps[i % R].run_index_topk(qi, wi, cfg.pos0)
             e[2].record()
             g[2].replay()
             e[3].record()
@@ -455,7 +455,10 @@ def main():
     if cfg.Nq == 1:
         # decode: the indexer streams every compressed key once per query
         achieved = index_scan_bytes(cfg) / (idx_us * 1e-6) / 1e9
-        roof = {"kernel": "index_scores (lightning-indexer key scan)", "bound": "hbm",
+        kname = ("index_scores_mx_mfma_kernel (MXFP4 key scan writing candidate lists; no "
+                 "score array)" if cfg.idx == "mxfp4" else
+                 "index_scores_kernel (key scan writing the score array)")
+        roof = {"kernel": kname, "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg, args.mx_fp8),
                 "bytes_per_launch": index_scan_bytes(cfg)}
@@ -495,7 +498,7 @@ def main():
         "step_tflops": round(sum(flops.values()) / (el / args.steps) / 1e12, 2),
         "breakdown_us": {k: round(v, 2) for k, v in br.items()},
         "breakdown_note": f"sampled every {SAMPLE}th step ({len(ev)} samples): pooling graph | "
-                          "indexer launch | selection + attention graph; the steps between "
+                          "indexer + top-k launches | attention graph; the steps between "
                           f"samples replay one graph of {SAMPLE - 1} chained steps",
         "roofline": roof,
     }

@@ -252,10 +252,23 @@ int hcsa_topk(const void* scores, int score_dtype, int64_t row_stride, int B, in
 }
 
 
+// Few long rows of bf16 scores over MXFP4 keys, with no score copy requested: the fused
+// selection (no score array).
+static bool index_topk_fused(int k_dtype, int score_dtype, int B, int Nq, int N, int k,
+                             const void* scores_out) {
+  return scores_out == nullptr && (k_dtype == HCSA_MXFP4 || k_dtype == HCSA_MXFP4_FP8) &&
+         !hcsa::plan_topk(score_dtype, B * Nq, N, k).rows_path &&
+         hcsa::mx_topk_fused_ok(B * Nq, N, score_dtype);
+}
+
 size_t hcsa_csa_index_topk_workspace_size(int B, int Nq, int N, int k, int score_dtype) {
   if (B < 1 || Nq < 1 || N < 1 || k < 1) return 0;
   const size_t scores = hcsa::align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
-  return scores + hcsa::plan_topk(score_dtype, B * Nq, N, k).total_bytes;
+  const size_t two_pass = scores + hcsa::plan_topk(score_dtype, B * Nq, N, k).total_bytes;
+  // the key dtype is not an argument: cover the fused selection of MXFP4 keys too
+  const size_t fused = index_topk_fused(HCSA_MXFP4, score_dtype, B, Nq, N, k, nullptr)
+                           ? hcsa::mx_topk_workspace_bytes(B * Nq, N) : 0;
+  return two_pass > fused ? two_pass : fused;
 }
 
 static int check_index_args(const void* q_idx, int q_dtype, const float* w_idx,
@@ -332,11 +345,21 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   if (!topk_idx) return fail(HCSA_EINVAL, "topk_idx must be non-null");
   if (!aligned16(topk_idx) || (scores_out && !aligned16(scores_out)))
     return fail(HCSA_EALIGN, "topk_idx and scores_out must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (index_topk_fused(k_dtype, score_dtype, B, Nq, N, k, scores_out)) {
+    rc = check_ws(workspace, ws_bytes, hcsa::mx_topk_workspace_bytes(B * Nq, N));
+    if (rc) return rc;
+    return hip_status(hcsa::launch_mxfp4_index_topk(
+                          q_idx, q_dtype, w_idx, static_cast<const uint8_t*>(k_idx), k_bstride,
+                          k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos,
+                          page_table(pages), page_stride(pages), k, topk_idx,
+                          k_dtype == HCSA_MXFP4_FP8, workspace, s),
+                      "hcsa_csa_index_topk (fused)");
+  }
   const size_t sbytes = hcsa::align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
   const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
   rc = check_ws(workspace, ws_bytes, sbytes + plan.total_bytes);
   if (rc) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   void* scores = scores_out ? scores_out : workspace;
   void* tws = static_cast<char*>(workspace) + sbytes;
   hipError_t e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,

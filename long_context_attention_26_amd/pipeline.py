@@ -91,6 +91,8 @@ class DecodeStep:
                                   dtype=torch.bfloat16 if score_dtype == "bf16" else torch.float32)
         self.ws_topk = hcsa.alloc_workspace(
             hcsa.topk_workspace_size(self.score_code, B, Nq, st.Nc, topk), dev)
+        self.ws_itopk = hcsa.alloc_workspace(
+            hcsa.index_topk_workspace_size(B, Nq, st.Nc, topk, self.score_code), dev)
         self.ws_attn = hcsa.alloc_workspace(
             hcsa.csa_hca_attn_workspace_size(B, Nq, H, d, topk, n_win, st.Nh), dev)
 
@@ -118,11 +120,24 @@ class DecodeStep:
                   workspace=self.ws_topk, stream=stream)
         self._attend(q, pos0, stream)
 
+    def run_index_topk(self, q_idx, w_idx, pos0, stream=None):
+        """Indexer scores and top-k in one call with no score copy: for MXFP4 keys at
+        decode the scores are never stored (floor, candidate scan, resolve)."""
+        st = self.st
+        hcsa.csa_index_topk(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, self.topk,
+                            self.score_code, self.idx, k_scales=st.Ics,
+                            workspace=self.ws_itopk, stream=stream, mx_fp8=self.mx_fp8)
+
+    def run_attend(self, q, pos0, stream=None):
+        self._attend(q, pos0, stream)
+
     def run(self, q, q_idx, w_idx, pos0, append=True, scores_out=None, stream=None,
             marks=None):
         """Full hot path for the query tokens at pos0..pos0+Nq-1: pool the blocks those
-        tokens complete (append), indexer scores, top-k, CSA sparse attention and HCA
-        attention (one call).
+        tokens complete (append), indexer scores and top-k, CSA sparse attention and HCA
+        attention (one call).  With scores_out the scores are written there and selected
+        by a second call; without, one indexer + top-k call (which, for MXFP4 keys at
+        decode, never stores them).
         `marks`, if given, is called with a stage name before each stage and with "end"
         after the last (used to record timing events on the stream)."""
         st = self.st
@@ -130,13 +145,14 @@ class DecodeStep:
         mark("compress")
         if append:
             st.compress_range(pos0, pos0 + self.Nq, stream=stream)
-        scores = self.scores if scores_out is None else scores_out
-        mark("index_scores")
-        hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, scores,
-                              k_scales=st.Ics, stream=stream, mx_fp8=self.mx_fp8)
-        mark("topk")
-        hcsa.topk(scores, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
-                  workspace=self.ws_topk, stream=stream)
+        mark("index_topk")
+        if scores_out is None:
+            self.run_index_topk(q_idx, w_idx, pos0, stream=stream)
+        else:
+            hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, scores_out,
+                                  k_scales=st.Ics, stream=stream, mx_fp8=self.mx_fp8)
+            hcsa.topk(scores_out, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,
+                      workspace=self.ws_topk, stream=stream)
         mark("attention")
         self._attend(q, pos0, stream)
         mark("end")

@@ -1,0 +1,130 @@
+"""Indexer + top-k of MXFP4 keys without the score array (hcsa_csa_index_topk with no
+score copy, few long rows, bf16 scores): a floor per row from scored samples, per-chunk
+candidate lists from the scan, the exact threshold among the candidates, and a rescan of
+rows whose lists hold too few or too many candidates.  The selection must equal that of
+the two-call path (scores, then hcsa_topk on them) bit for bit, and the oracle's selection
+on those scores; the two-call path is checked against the oracle's scores elsewhere."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H(gpu):
+    from long_context_attention_26_amd import hcsa
+    return hcsa
+
+
+def _nv(p, N):
+    return min(N, (p + 1) // 4)
+
+
+CASES = [
+    # every row on the list path
+    dict(name="b4-262144-k1024", B=4, Nq=1, N=262144, pos=[4 * 262144 - 1] * 4, k=1024, H_I=4,
+         d_I=64),
+    # ragged positions, f32 queries, 8 heads x 128 channels
+    dict(name="ragged-f32q", B=3, Nq=1, N=300000, pos=[4 * 300000 - 1, 4 * 123457 + 2, 4 * 70001],
+         k=512, H_I=8, d_I=128, qdt="f32"),
+    # rows of <= 4096 visible keys (every key a candidate) and a row seeing fewer than k
+    dict(name="short-rows", B=3, Nq=1, N=6000, pos=[4 * 6000 - 1, 4 * 3000 - 1, 4 * 200 - 1],
+         k=256, H_I=1, d_I=32),
+    # every score 0: the floor admits every key, the row is rescanned; ties to the lowest index
+    dict(name="all-ties-rescan", B=2, Nq=1, N=40000, pos=[4 * 40000 - 1, 4 * 39000 - 1], k=700,
+         H_I=4, d_I=64, w_zero=True),
+    # k near the visible count: almost every key is a candidate
+    dict(name="dense-k4096", B=1, Nq=1, N=4300, pos=[4 * 4300 - 1], k=4096, H_I=4, d_I=64),
+    # large keys planted at exactly the floor's sample positions (32 runs of 128 keys at
+    # r * (nv - 128) // 31): the floor lands above the k-th largest key, the list holds
+    # fewer than k candidates and the row is rescanned
+    dict(name="sampled-runs-rescan", B=1, Nq=1, N=262144, pos=[4 * 262144 - 1], k=1024, H_I=4,
+         d_I=64, boost_samples=True),
+    # paged keys on FP8 operands
+    dict(name="paged-fp8", B=2, Nq=1, N=70000, pos=[4 * 70000 - 1, 4 * 51234 + 1], k=1024, H_I=4,
+         d_I=64, paged=True, fp8=True),
+    # several query tokens per sequence (few rows), 16 heads
+    dict(name="nq8-h16", B=1, Nq=8, N=100000, pos=[4 * 99990], k=1024, H_I=16, d_I=64),
+    # large scales on one stretch: the top keys crowd a few chunks
+    dict(name="skewed", B=2, Nq=1, N=200000, pos=[4 * 200000 - 1] * 2, k=1024, H_I=4, d_I=64,
+         skew=(50000, 58000)),
+]
+
+
+def _page_pool(x, table, per, gpu):
+    """x [B, n, ...] into a pool of pages of `per` rows at the table's page numbers."""
+    B, nblk = table.shape
+    P = int(table.max().item()) + 3
+    pool = torch.zeros((P, per) + tuple(x.shape[2:]), dtype=x.dtype, device=gpu)
+    full = torch.zeros((B, nblk * per) + tuple(x.shape[2:]), dtype=x.dtype, device=gpu)
+    n = min(x.shape[1], nblk * per)
+    full[:, :n] = x[:, :n]
+    pool[table.reshape(-1).long()] = full.reshape((B * nblk, per) + tuple(x.shape[2:]))
+    return pool
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_fused_index_topk_equals_two_calls(H, gpu, case):
+    print(f"fused index-topk {case['name']}", flush=True)
+    B, Nq, N, k, H_I, d_I = case["B"], case["Nq"], case["N"], case["k"], case["H_I"], case["d_I"]
+    g = torch.Generator().manual_seed(77)
+    Nt = N + 3
+    codes = torch.randint(0, 256, (B, Nt, d_I // 2), generator=g, dtype=torch.uint8)
+    scales = torch.randint(120, 128, (B, Nt, d_I // 32), generator=g, dtype=torch.uint8)
+    if "skew" in case:
+        lo, hi = case["skew"]
+        scales[:, lo:hi] = 131
+    if case.get("boost_samples"):
+        for b in range(B):
+            nv = _nv(case["pos"][b], N)
+            for run in range(32):
+                r0 = run * (nv - 128) // 31
+                scales[b, r0:r0 + 128] = 134
+    qdt = torch.float32 if case.get("qdt") == "f32" else torch.bfloat16
+    q = torch.randn(B, Nq, H_I, d_I, generator=g).to(qdt).to(gpu)
+    w = (torch.randn(B, Nq, H_I, generator=g).abs() / math.sqrt(H_I)).to(gpu)
+    if case.get("w_zero"):
+        w.zero_()
+    seq_pos = torch.tensor(case["pos"], dtype=torch.int64, device=gpu)
+    codes, scales = codes.to(gpu), scales.to(gpu)
+    table = None
+    kc, ks = codes, scales
+    if case.get("paged"):
+        nblk = -(-Nt // 32)
+        perm = torch.randperm(B * nblk + 5, generator=g)[: B * nblk].to(torch.int32)
+        table = perm.view(B, nblk).to(gpu)
+        kc, ks = _page_pool(codes, table, 32, gpu), _page_pool(scales, table, 32, gpu)
+    fp8 = case.get("fp8", False)
+
+    idx = torch.full((B, Nq, k), -7, dtype=torch.int32, device=gpu)
+    H.csa_index_topk(q, w, kc, N, 4, 0, k, H.BF16, idx, k_scales=ks, seq_pos=seq_pos,
+                     block_table=table, mx_fp8=fp8)
+    # a second call on a fresh workspace holding junk: nothing carries over
+    ws = H.alloc_workspace(H.index_topk_workspace_size(B, Nq, N, k, H.BF16), gpu)
+    ws.fill_(0x5A)
+    idx_b = torch.full_like(idx, -7)
+    H.csa_index_topk(q, w, kc, N, 4, 0, k, H.BF16, idx_b, k_scales=ks, seq_pos=seq_pos,
+                     block_table=table, mx_fp8=fp8, workspace=ws)
+    # two calls: scores, then the selector on them
+    scores = torch.zeros(B * Nq, N, dtype=torch.bfloat16, device=gpu)
+    H.csa_index_scores(q, w, kc, N, 4, 0, scores, k_scales=ks, seq_pos=seq_pos,
+                       block_table=table, mx_fp8=fp8)
+    idx2 = torch.full_like(idx, -7)
+    H.topk(scores, B, Nq, N, 4, 0, k, idx2.view(B * Nq, k), seq_pos=seq_pos)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_b), "fused selection depends on the workspace's contents"
+    got, want = idx.view(B * Nq, k).cpu().numpy(), idx2.view(B * Nq, k).cpu().numpy()
+    for r in range(B * Nq):
+        assert np.array_equal(got[r], want[r]), (case["name"], r)
+    # the oracle's selection on the GPU's scores, for a few rows
+    sc = f64(scores)
+    for r in sorted({0, B * Nq - 1}):
+        b, i = divmod(r, Nq)
+        nv = _nv(case["pos"][b] + i, N)
+        assert np.array_equal(got[r], O.select_topk(sc[r], nv, k)), (case["name"], r)
