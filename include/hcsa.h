@@ -211,6 +211,14 @@ int hcsa_topk(const void *scores, int score_dtype, int64_t row_stride, int B, in
  * Scores s_j = sum_g w_g max(0, q_g . k_j) for the visible j (see hcsa_topk), rounded to
  * score_dtype, then top-k as in hcsa_topk.
  * scores_out  optional [B*Nq][N] score_dtype copy of the scores (NULL to skip).
+ * Without a copy, MXFP4 keys, BF16 scores and a few long rows (the decode case: fewer than
+ * 64 rows, or rows of more than 131072 entries), the scores are never stored: a floor per
+ * row is set from 4096 scored samples, the key scan keeps the keys scoring at or above it
+ * in per-chunk candidate lists, and the exact threshold is found among them; a row whose
+ * lists hold fewer than k or too many candidates is rescanned into the workspace and
+ * selected over all its scores.  The selection is the same as with a copy.
+ * workspace   hcsa_csa_index_topk_workspace_size(B, Nq, N, k, score_dtype) bytes (covers
+ *             every key dtype), 256-byte aligned; its contents need not be initialized.
  * Limits: H_I in {1, 2, 4, 8, 16}; d_I in {32, 64, 128} (F32 keys: {32, 64});
  *         q dtype F32 with F32 keys, BF16 with BF16 keys, F32 or BF16 with MXFP4 keys.
  */
