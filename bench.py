@@ -355,7 +355,7 @@ def main():
             stp.mx_fp8 = True
     torch.cuda.synchronize()
 
-    # Each copy's step is captured as one HIP graph, and once more as three graphs (pooling |
+    # Each copy's step is captured as one HIP graph, and once more as two graphs (pooling +
     # indexer + top-k | CSA + HCA attention).  Every SAMPLE-th timed
     # step runs the three-graph form with timing events between the graphs on the launch
     # stream: they give the per-stage split and the indexer kernel's duration for the
@@ -364,7 +364,7 @@ def main():
     # per-token graph chains its layers: the host's graph-launch latency, several
     # microseconds per launch, then falls on one step in SAMPLE instead of every step.
     SAMPLE = 8
-    stages = ["pool", "index_topk", "attend"]
+    stages = ["pool_index_topk", "attend"]
     full, split = [], []
     cap_stream = torch.cuda.Stream()
     for stp in steps:
@@ -372,24 +372,20 @@ def main():
             stp.run(q, qi, wi, cfg.pos0)
         torch.cuda.synchronize()
         g_all = torch.cuda.CUDAGraph()
-        g_pool, g_idx, g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        g_idx, g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.stream(cap_stream):
             g_all.capture_begin()
-            stp.run_pool(cfg.pos0)
-            stp.run_index_topk(qi, wi, cfg.pos0)
+            stp.run_pool_index_topk(qi, wi, cfg.pos0)
             stp.run_attend(q, cfg.pos0)
             g_all.capture_end()
-            g_pool.capture_begin()
-            stp.run_pool(cfg.pos0)
-            g_pool.capture_end()
             g_idx.capture_begin()
-            stp.run_index_topk(qi, wi, cfg.pos0)
+            stp.run_pool_index_topk(qi, wi, cfg.pos0)
             g_idx.capture_end()
             g_rest.capture_begin()
             stp.run_attend(q, cfg.pos0)
             g_rest.capture_end()
         full.append(g_all)
-        split.append((g_pool, g_idx, g_rest))
+        split.append((g_idx, g_rest))
     torch.cuda.synchronize()
     chain = []                                  # chain[c]: SAMPLE - 1 steps from copy c on
     for c in range(R):
@@ -398,8 +394,7 @@ def main():
             g.capture_begin()
             for j in range(SAMPLE - 1):
                 stp = steps[(c + j) % R]
-                stp.run_pool(cfg.pos0)
-                stp.run_index_topk(qi, wi, cfg.pos0)
+                stp.run_pool_index_topk(qi, wi, cfg.pos0)
                 stp.run_attend(q, cfg.pos0)
             g.capture_end()
         chain.append(g)
@@ -411,20 +406,18 @@ def main():
 
     def one_step(i, timed):
         if timed and i % SAMPLE == 0:
-            # sampled step: pooling graph, the indexer + top-k call launched directly (its key
-            # scan kernel records dispatch-level events: its own execution time), then the
+            # sampled step: the pooling + indexer + top-k call launched directly (its key scan
+            # kernel records dispatch-level events: its own execution time), then the
             # attention graph
             g = split[i % R]
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e[0].record()
-            g[0].replay()
-            e[1].record()
             hcsa.time_next_indexer(k0, k1)
-            steps[i % R].run_index_topk(qi, wi, cfg.pos0)
+            steps[i % R].run_pool_index_topk(qi, wi, cfg.pos0)
+            e[1].record()
+            g[1].replay()
             e[2].record()
-            g[2].replay()
-            e[3].record()
             ev.append(e)
             kev.append((k0, k1))
         else:
@@ -497,7 +490,7 @@ def main():
         "step_bytes": total_bytes,
         "step_tflops": round(sum(flops.values()) / (el / args.steps) / 1e12, 2),
         "breakdown_us": {k: round(v, 2) for k, v in br.items()},
-        "breakdown_note": f"sampled every {SAMPLE}th step ({len(ev)} samples): pooling graph | "
+        "breakdown_note": f"sampled every {SAMPLE}th step ({len(ev)} samples): pooling + "
                           "indexer + top-k launches | attention graph; the steps between "
                           f"samples replay one graph of {SAMPLE - 1} chained steps",
         "roofline": roof,

@@ -231,6 +231,24 @@ int hcsa_csa_index_topk(const void *q_idx, int q_dtype, const float *w_idx, cons
                         size_t ws_bytes, hcsa_stream stream);
 
 /*
+ * Pooling on append + indexer + top-k: hcsa_compress_kv_batched(jobs, n_jobs, B, pages)
+ * then hcsa_csa_index_topk(...) with the same arguments, as one call with the same results
+ * [Lighthouse section 八 items 3 and 7: the tokens of a step complete the blocks the step's
+ * indexer then scans].  Every job and argument is validated before anything is launched.
+ * When the selection runs without a score array (see hcsa_csa_index_topk), the pooling
+ * blocks share the launch of the per-row floors, whose samples then read only the entries
+ * completed before each sequence's first query token: the jobs must not rewrite those.
+ * workspace as for hcsa_csa_index_topk.
+ */
+int hcsa_csa_pool_index_topk(const hcsa_pool_job *jobs, int n_jobs, const void *q_idx,
+                             int q_dtype, const float *w_idx, const void *k_idx, int k_dtype,
+                             int64_t k_bstride, const uint8_t *k_scales, int64_t ks_bstride,
+                             int B, int Nq, int H_I, int d_I, int N, int ratio, int64_t pos0,
+                             const int64_t *seq_pos, const hcsa_pages *pages, int k,
+                             int score_dtype, int32_t *topk_idx, void *scores_out,
+                             void *workspace, size_t ws_bytes, hcsa_stream stream);
+
+/*
  * Lightning-indexer scores only (the first half of hcsa_csa_index_topk; same arguments
  * and limits): scores [B*Nq][N] in score_dtype, entries at or past the visible count of a
  * row are left untouched.  No workspace.

@@ -123,8 +123,8 @@ int hcsa_compress_kv(const void* x, int x_dtype, int64_t x_bstride, int B, int T
                     "hcsa_compress_kv");
 }
 
-int hcsa_compress_kv_batched(const hcsa_pool_job* jobs, int n_jobs, int B,
-                             const hcsa_pages* pages, hcsa_stream stream) {
+static int check_pool_jobs(const hcsa_pool_job* jobs, int n_jobs, int B,
+                           const hcsa_pages* pages) {
   if (n_jobs < 0 || n_jobs > HCSA_MAX_POOL_JOBS)
     return fail(HCSA_EINVAL, "n_jobs must be in [0, %d]", HCSA_MAX_POOL_JOBS);
   if (n_jobs > 0 && !jobs) return fail(HCSA_EINVAL, "jobs must be non-null");
@@ -151,6 +151,14 @@ int hcsa_compress_kv_batched(const hcsa_pool_job* jobs, int n_jobs, int B,
     }
     if (rc) return fail(rc, "job %d: %s", i, g_err.c_str());
   }
+  return HCSA_OK;
+}
+
+int hcsa_compress_kv_batched(const hcsa_pool_job* jobs, int n_jobs, int B,
+                             const hcsa_pages* pages, hcsa_stream stream) {
+  const int rc = check_pool_jobs(jobs, n_jobs, B, pages);
+  if (rc) return rc;
+  const int64_t ring = raw_ring(pages);
   return hip_status(hcsa::launch_compress_batched(jobs, n_jobs, B, page_table(pages),
                                                   page_stride(pages), ring,
                                                   static_cast<hipStream_t>(stream)),
@@ -327,12 +335,15 @@ int hcsa_csa_index_scores(const void* q_idx, int q_dtype, const float* w_idx,
                     "hcsa_csa_index_scores");
 }
 
-int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, const void* k_idx,
-                        int k_dtype, int64_t k_bstride, const uint8_t* k_scales,
-                        int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
-                        int64_t pos0, const int64_t* seq_pos, const hcsa_pages* pages, int k,
-                        int score_dtype, int32_t* topk_idx, void* scores_out, void* workspace,
-                        size_t ws_bytes, hcsa_stream stream) {
+// Indexer + top-k, after the pooling jobs (validated) when given: in the fused selection
+// the pooling runs in the floors' launch, otherwise in its own launch first.
+static int index_topk_impl(const void* q_idx, int q_dtype, const float* w_idx, const void* k_idx,
+                           int k_dtype, int64_t k_bstride, const uint8_t* k_scales,
+                           int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
+                           int64_t pos0, const int64_t* seq_pos, const hcsa_pages* pages, int k,
+                           int score_dtype, int32_t* topk_idx, void* scores_out, void* workspace,
+                           size_t ws_bytes, hcsa_stream stream, const hcsa_pool_job* jobs,
+                           int n_jobs) {
   int rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
   if (rc) return rc;
   rc = check_seq_pos(seq_pos);
@@ -346,29 +357,61 @@ int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, cons
   if (!aligned16(topk_idx) || (scores_out && !aligned16(scores_out)))
     return fail(HCSA_EALIGN, "topk_idx and scores_out must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (index_topk_fused(k_dtype, score_dtype, B, Nq, N, k, scores_out)) {
-    rc = check_ws(workspace, ws_bytes, hcsa::mx_topk_workspace_bytes(B * Nq, N));
-    if (rc) return rc;
+  const bool fused = index_topk_fused(k_dtype, score_dtype, B, Nq, N, k, scores_out);
+  const size_t sbytes = hcsa::align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
+  const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
+  rc = check_ws(workspace, ws_bytes,
+                fused ? hcsa::mx_topk_workspace_bytes(B * Nq, N) : sbytes + plan.total_bytes);
+  if (rc) return rc;
+  if (fused)
     return hip_status(hcsa::launch_mxfp4_index_topk(
                           q_idx, q_dtype, w_idx, static_cast<const uint8_t*>(k_idx), k_bstride,
                           k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos,
                           page_table(pages), page_stride(pages), k, topk_idx,
-                          k_dtype == HCSA_MXFP4_FP8, workspace, s),
+                          k_dtype == HCSA_MXFP4_FP8, workspace, s, jobs, n_jobs,
+                          raw_ring(pages)),
                       "hcsa_csa_index_topk (fused)");
+  hipError_t e = hipSuccess;
+  if (jobs && n_jobs > 0) {
+    e = hcsa::launch_compress_batched(jobs, n_jobs, B, page_table(pages), page_stride(pages),
+                                      raw_ring(pages), s);
+    if (e != hipSuccess) return hip_status(e, "hcsa_csa_pool_index_topk (pooling)");
   }
-  const size_t sbytes = hcsa::align256(static_cast<size_t>(B) * Nq * N * (score_dtype == HCSA_BF16 ? 2 : 4));
-  const hcsa::TopkPlan plan = hcsa::plan_topk(score_dtype, B * Nq, N, k);
-  rc = check_ws(workspace, ws_bytes, sbytes + plan.total_bytes);
-  if (rc) return rc;
   void* scores = scores_out ? scores_out : workspace;
   void* tws = static_cast<char*>(workspace) + sbytes;
-  hipError_t e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride,
-                                           k_scales, ks_bstride, B, Nq, H_I, d_I, N, ratio,
-                                           pos0, seq_pos, page_table(pages), page_stride(pages),
-                                           score_dtype, scores, s);
+  e = hcsa::launch_index_scores(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales,
+                                ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos,
+                                page_table(pages), page_stride(pages), score_dtype, scores, s);
   if (e != hipSuccess) return hip_status(e, "hcsa_csa_index_topk (scores)");
   e = hcsa::launch_topk(plan, scores, score_dtype, N, Nq, ratio, pos0, seq_pos, topk_idx, tws, s);
   return hip_status(e, "hcsa_csa_index_topk (select)");
+}
+
+int hcsa_csa_index_topk(const void* q_idx, int q_dtype, const float* w_idx, const void* k_idx,
+                        int k_dtype, int64_t k_bstride, const uint8_t* k_scales,
+                        int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N, int ratio,
+                        int64_t pos0, const int64_t* seq_pos, const hcsa_pages* pages, int k,
+                        int score_dtype, int32_t* topk_idx, void* scores_out, void* workspace,
+                        size_t ws_bytes, hcsa_stream stream) {
+  return index_topk_impl(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales,
+                         ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos, pages, k,
+                         score_dtype, topk_idx, scores_out, workspace, ws_bytes, stream,
+                         nullptr, 0);
+}
+
+int hcsa_csa_pool_index_topk(const hcsa_pool_job* jobs, int n_jobs, const void* q_idx,
+                             int q_dtype, const float* w_idx, const void* k_idx, int k_dtype,
+                             int64_t k_bstride, const uint8_t* k_scales, int64_t ks_bstride,
+                             int B, int Nq, int H_I, int d_I, int N, int ratio, int64_t pos0,
+                             const int64_t* seq_pos, const hcsa_pages* pages, int k,
+                             int score_dtype, int32_t* topk_idx, void* scores_out,
+                             void* workspace, size_t ws_bytes, hcsa_stream stream) {
+  const int rc = check_pool_jobs(jobs, n_jobs, B, pages);
+  if (rc) return rc;
+  return index_topk_impl(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales,
+                         ks_bstride, B, Nq, H_I, d_I, N, ratio, pos0, seq_pos, pages, k,
+                         score_dtype, topk_idx, scores_out, workspace, ws_bytes, stream, jobs,
+                         n_jobs);
 }
 
 static int attn_max_len_csa(int k, int n_win) { return k + n_win; }

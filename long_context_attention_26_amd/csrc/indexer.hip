@@ -15,6 +15,7 @@
 
 #include "internal.h"
 #include "select_dev.h"
+#include "pool_dev.h"
 
 namespace hcsa {
 
@@ -714,8 +715,13 @@ constexpr int kMxMaxChunks = 4096;
 // wave its own ceil(m/W)-th, and take the smallest of the W.  Rows of at most 4096 visible
 // keys take every key (floor 0).  All sample loads are issued before the query is
 // quantized.
+//
+// prior_only: sample only the entries completed before the sequence's first query token
+// (those a pooling launch of the same tokens does not write), for the fused pooling launch.
+// One 512-thread block; called by every thread.
 template <int HI, int KS, bool QBF16, bool PAGED, bool F8>
-__global__ __launch_bounds__(kMxFloorThreads) void mx_floor_kernel(IdxMxDev A, int k) {
+__device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row,
+                                               bool prior_only) {
   constexpr int W = kMxFloorThreads / 64;
   constexpr int PT = kMxSamples / kMxFloorThreads;      // samples per thread
   __shared__ uint32_t s_qa[kMxMaxUnits][4];
@@ -723,12 +729,16 @@ __global__ __launch_bounds__(kMxFloorThreads) void mx_floor_kernel(IdxMxDev A, i
   __shared__ uint16_t s_samp[kMxSamples];
   __shared__ uint32_t s_gmax[kMxFloorThreads];
   __shared__ uint32_t s_min[W];
-  const int row = blockIdx.x;
   const int b = row / A.Nq;
   const int64_t p = query_pos(A.seq_pos, A.pos0, b, row % A.Nq);
   const int64_t nv64 = (p + 1) / A.ratio;
   const int nv = static_cast<int>(nv64 < A.N ? nv64 : A.N);
-  if (k >= nv || nv <= kMxSamples) {
+  int ns = nv;                                         // entries the samples may read
+  if (prior_only) {
+    const int64_t e0 = query_pos(A.seq_pos, A.pos0, b, 0) / A.ratio;
+    ns = static_cast<int>(e0 < nv ? e0 : nv);
+  }
+  if (k >= nv || ns <= kMxSamples) {
     if (threadIdx.x == 0) A.floor[row] = 0u;
     return;
   }
@@ -744,7 +754,7 @@ __global__ __launch_bounds__(kMxFloorThreads) void mx_floor_kernel(IdxMxDev A, i
 #pragma unroll
   for (int u = 0; u < NG; ++u) {
     const int run = wave * RPW + u / GPR;
-    const int r0 = static_cast<int>(static_cast<int64_t>(run) * (nv - kMxRunKeys) /
+    const int r0 = static_cast<int>(static_cast<int64_t>(run) * (ns - kMxRunKeys) /
                                     (kMxFloorRuns - 1));
     mx_load<KS, PAGED, F8>(A, kbase, sbase, b, r0 + (u % GPR) * 32 + col, true, kraw[u], ksc[u]);
   }
@@ -813,6 +823,26 @@ __global__ __launch_bounds__(kMxFloorThreads) void mx_floor_kernel(IdxMxDev A, i
 #pragma unroll
   for (int u = 0; u < W; ++u) pre = min(pre, s_min[u]);
   if (threadIdx.x == 0) A.floor[row] = pre;
+}
+
+// grid: rows; block 512.
+template <int HI, int KS, bool QBF16, bool PAGED, bool F8>
+__global__ __launch_bounds__(kMxFloorThreads) void mx_floor_kernel(IdxMxDev A, int k) {
+  mx_floor_block<HI, KS, QBF16, PAGED, F8>(A, k, blockIdx.x, false);
+}
+
+// The floors and the pooling of the same tokens in one launch: blocks x < Nq of grid row y
+// set the floor of query row y*Nq + x (sampling only entries completed before the call),
+// the rest run the pooling jobs (sequence y).  grid: (Nq + pooling blocks, B); block 512.
+template <int HI, int KS, bool QBF16, bool PAGED, bool F8>
+__global__ __launch_bounds__(kMxFloorThreads) void mx_pool_floor_kernel(PoolJobs J, IdxMxDev A,
+                                                                        int k) {
+  __shared__ float alpha[1024];
+  __shared__ float s_part[kMxFloorThreads * 8];
+  if (static_cast<int>(blockIdx.x) < A.Nq)
+    mx_floor_block<HI, KS, QBF16, PAGED, F8>(A, k, blockIdx.y * A.Nq + blockIdx.x, true);
+  else
+    pool_jobs_block<PAGED>(J, blockIdx.x - A.Nq, alpha, s_part);
 }
 
 // The exact threshold among the row's C candidates (the concatenated chunk lists, prefix
@@ -953,9 +983,15 @@ hipError_t launch_mx_mfma_hi(const IdxMxDev& A, int rows, int score_dtype, hipSt
   return launch_mx_mfma_ks<HI, 1, QBF16, F8>(A, rows, score_dtype, s);
 }
 
+// pool: null, or the pooling jobs to run in the floors' launch (pool_blocks of 512 threads)
 template <int HI, int KS, bool QBF16, bool F8, bool PAGED>
-hipError_t launch_mx_topk_ks(const IdxMxDev& A, int rows, int k, int32_t* idx, hipStream_t s) {
-  mx_floor_kernel<HI, KS, QBF16, PAGED, F8><<<rows, kMxFloorThreads, 0, s>>>(A, k);
+hipError_t launch_mx_topk_ks(const IdxMxDev& A, int rows, int k, int32_t* idx,
+                             const PoolJobs* pool, int pool_blocks_n, int B, hipStream_t s) {
+  if (pool && pool_blocks_n > 0)
+    mx_pool_floor_kernel<HI, KS, QBF16, PAGED, F8>
+        <<<dim3(A.Nq + pool_blocks_n, B), kMxFloorThreads, 0, s>>>(*pool, A, k);
+  else
+    mx_floor_kernel<HI, KS, QBF16, PAGED, F8><<<rows, kMxFloorThreads, 0, s>>>(A, k);
   launch_timed(index_scores_mx_mfma_kernel<HI, KS, QBF16, true, PAGED, F8, true>,
                dim3(A.nchunks, rows), dim3(256), s, A);
   mx_list_resolve_kernel<HI, KS, QBF16, PAGED, F8><<<rows, kMxResThreads, 0, s>>>(A, k, idx);
@@ -963,9 +999,11 @@ hipError_t launch_mx_topk_ks(const IdxMxDev& A, int rows, int k, int32_t* idx, h
 }
 
 template <int HI, bool QBF16, bool F8, bool PAGED>
-hipError_t launch_mx_topk_hi(const IdxMxDev& A, int rows, int k, int32_t* idx, hipStream_t s) {
-  if (A.d_I > 64 || F8) return launch_mx_topk_ks<HI, 2, QBF16, F8, PAGED>(A, rows, k, idx, s);
-  return launch_mx_topk_ks<HI, 1, QBF16, F8, PAGED>(A, rows, k, idx, s);
+hipError_t launch_mx_topk_hi(const IdxMxDev& A, int rows, int k, int32_t* idx,
+                             const PoolJobs* pool, int pool_blocks_n, int B, hipStream_t s) {
+  if (A.d_I > 64 || F8)
+    return launch_mx_topk_ks<HI, 2, QBF16, F8, PAGED>(A, rows, k, idx, pool, pool_blocks_n, B, s);
+  return launch_mx_topk_ks<HI, 1, QBF16, F8, PAGED>(A, rows, k, idx, pool, pool_blocks_n, B, s);
 }
 
 template <bool QBF16, bool F8>
@@ -982,13 +1020,13 @@ hipError_t launch_mx_mfma(const IdxMxDev& A, int rows, int H_I, int score_dtype,
 
 template <bool QBF16, bool F8, bool PAGED>
 hipError_t launch_mx_topk(const IdxMxDev& A, int rows, int H_I, int k, int32_t* idx,
-                          hipStream_t s) {
+                          const PoolJobs* pool, int pb, int B, hipStream_t s) {
   switch (H_I) {
-    case 1: return launch_mx_topk_hi<1, QBF16, F8, PAGED>(A, rows, k, idx, s);
-    case 2: return launch_mx_topk_hi<2, QBF16, F8, PAGED>(A, rows, k, idx, s);
-    case 4: return launch_mx_topk_hi<4, QBF16, F8, PAGED>(A, rows, k, idx, s);
-    case 8: return launch_mx_topk_hi<8, QBF16, F8, PAGED>(A, rows, k, idx, s);
-    case 16: return launch_mx_topk_hi<16, QBF16, F8, PAGED>(A, rows, k, idx, s);
+    case 1: return launch_mx_topk_hi<1, QBF16, F8, PAGED>(A, rows, k, idx, pool, pb, B, s);
+    case 2: return launch_mx_topk_hi<2, QBF16, F8, PAGED>(A, rows, k, idx, pool, pb, B, s);
+    case 4: return launch_mx_topk_hi<4, QBF16, F8, PAGED>(A, rows, k, idx, pool, pb, B, s);
+    case 8: return launch_mx_topk_hi<8, QBF16, F8, PAGED>(A, rows, k, idx, pool, pb, B, s);
+    case 16: return launch_mx_topk_hi<16, QBF16, F8, PAGED>(A, rows, k, idx, pool, pb, B, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1067,7 +1105,9 @@ hipError_t launch_mxfp4_index_topk(const void* q, int q_dtype, const float* w,
                                    int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                    int ratio, int64_t pos0, const int64_t* seq_pos,
                                    const int32_t* block_table, int64_t table_stride, int k,
-                                   int32_t* idx, bool fp8, void* ws, hipStream_t s) {
+                                   int32_t* idx, bool fp8, void* ws, hipStream_t s,
+                                   const hcsa_pool_job* pool_jobs, int n_pool_jobs,
+                                   int64_t raw_ring) {
   const int rows = B * Nq;
   const MxTopkLayout l = mx_topk_layout(rows, N);
   char* base = static_cast<char*>(ws);
@@ -1076,17 +1116,23 @@ hipError_t launch_mxfp4_index_topk(const void* q, int q_dtype, const float* w,
   A.floor = reinterpret_cast<uint32_t*>(base);
   A.counts = reinterpret_cast<uint32_t*>(base + l.counts_off);
   A.lists = reinterpret_cast<uint32_t*>(base + l.lists_off);
+  PoolJobs J;
+  int pb = 0;
+  if (pool_jobs)
+    pb = pool_jobs_fill(pool_jobs, n_pool_jobs, block_table, table_stride, raw_ring,
+                        kMxFloorThreads, J);
+  const PoolJobs* pj = pool_jobs ? &J : nullptr;
   const bool paged = block_table != nullptr, qb = q_dtype == 1;
   if (fp8) {
-    if (qb) return paged ? launch_mx_topk<true, true, true>(A, rows, H_I, k, idx, s)
-                         : launch_mx_topk<true, true, false>(A, rows, H_I, k, idx, s);
-    return paged ? launch_mx_topk<false, true, true>(A, rows, H_I, k, idx, s)
-                 : launch_mx_topk<false, true, false>(A, rows, H_I, k, idx, s);
+    if (qb) return paged ? launch_mx_topk<true, true, true>(A, rows, H_I, k, idx, pj, pb, B, s)
+                         : launch_mx_topk<true, true, false>(A, rows, H_I, k, idx, pj, pb, B, s);
+    return paged ? launch_mx_topk<false, true, true>(A, rows, H_I, k, idx, pj, pb, B, s)
+                 : launch_mx_topk<false, true, false>(A, rows, H_I, k, idx, pj, pb, B, s);
   }
-  if (qb) return paged ? launch_mx_topk<true, false, true>(A, rows, H_I, k, idx, s)
-                       : launch_mx_topk<true, false, false>(A, rows, H_I, k, idx, s);
-  return paged ? launch_mx_topk<false, false, true>(A, rows, H_I, k, idx, s)
-               : launch_mx_topk<false, false, false>(A, rows, H_I, k, idx, s);
+  if (qb) return paged ? launch_mx_topk<true, false, true>(A, rows, H_I, k, idx, pj, pb, B, s)
+                       : launch_mx_topk<true, false, false>(A, rows, H_I, k, idx, pj, pb, B, s);
+  return paged ? launch_mx_topk<false, false, true>(A, rows, H_I, k, idx, pj, pb, B, s)
+               : launch_mx_topk<false, false, false>(A, rows, H_I, k, idx, pj, pb, B, s);
 }
 
 

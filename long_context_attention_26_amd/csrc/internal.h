@@ -48,7 +48,9 @@ void time_next_indexer(hipEvent_t start, hipEvent_t stop);
 // Indexer + top-k of MXFP4 keys without the score array (few long rows, bf16 scores): a
 // floor per row from scored samples, the scan's per-chunk candidate lists, the exact
 // threshold among them (rows with too few or too many candidates rescanned and selected
-// over the whole row).  Same result as launch_index_scores + launch_topk.
+// over the whole row).  Same result as launch_index_scores + launch_topk.  With pooling
+// jobs (validated, the blocks completed by the query tokens), the pooling runs in the
+// floors' launch and the floors sample only entries completed before the query tokens.
 bool mx_topk_fused_ok(int rows, int N, int score_dtype);
 size_t mx_topk_workspace_bytes(int rows, int N);
 hipError_t launch_mxfp4_index_topk(const void* q, int q_dtype, const float* w,
@@ -56,7 +58,9 @@ hipError_t launch_mxfp4_index_topk(const void* q, int q_dtype, const float* w,
                                    int64_t ks_bstride, int B, int Nq, int H_I, int d_I, int N,
                                    int ratio, int64_t pos0, const int64_t* seq_pos,
                                    const int32_t* block_table, int64_t table_stride, int k,
-                                   int32_t* idx, bool fp8, void* ws, hipStream_t s);
+                                   int32_t* idx, bool fp8, void* ws, hipStream_t s,
+                                   const struct hcsa_pool_job* pool_jobs = nullptr,
+                                   int n_pool_jobs = 0, int64_t raw_ring = 0);
 
 // ---- attention.hip
 struct AttnArgs {

@@ -46,6 +46,9 @@ _SIGS = {
     "hcsa_csa_index_topk_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "hcsa_csa_index_topk": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
                                  _i64, _p, _p, _i, _i, _p, _p, _p, _sz, _p]),
+    "hcsa_csa_pool_index_topk": (_i, [_p, _i, _p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i,
+                                      _i, _i, _i, _i, _i64, _p, _p, _i, _i, _p, _p, _p, _sz,
+                                      _p]),
     "hcsa_csa_index_scores": (_i, [_p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i, _i, _i, _i,
                                    _i64, _p, _p, _i, _p, _p]),
     "hcsa_csa_sparse_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -237,6 +240,30 @@ def csa_index_topk(q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx
                                    _pages(block_table), k, score_dtype, _ptr(topk_idx),
                                    _ptr(scores_out), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
+    return topk_idx
+
+
+def csa_pool_index_topk(jobs, q_idx, w_idx, k_idx, N, ratio, pos0, k, score_dtype, topk_idx,
+                        k_scales=None, scores_out=None, workspace=None, stream=None,
+                        seq_pos=None, block_table=None, raw_ring=0, mx_fp8=False):
+    """compress_kv_batched(jobs, ...) then csa_index_topk(...) as one call (the pooling runs
+    in the launch of the selection's per-row floors when the scores are not stored)."""
+    B, Nq, H_I, d_I = q_idx.shape
+    if k_idx.dtype == torch.uint8:
+        k_dt, ksb = (MXFP4_FP8 if mx_fp8 else MXFP4), k_scales.stride(0)
+    else:
+        k_dt, ksb = dtype_code(k_idx), 0
+    if workspace is None:
+        workspace = alloc_workspace(index_topk_workspace_size(B, Nq, N, k, score_dtype),
+                                    q_idx.device)
+    arr = (PoolJob * max(1, len(jobs)))(*jobs)
+    _check(lib.hcsa_csa_pool_index_topk(ctypes.cast(arr, _p), len(jobs), _ptr(q_idx),
+                                        dtype_code(q_idx), _ptr(w_idx), _ptr(k_idx), k_dt,
+                                        k_idx.stride(0), _ptr(k_scales), ksb, B, Nq, H_I, d_I,
+                                        N, ratio, pos0, _pos_ptr(seq_pos, B),
+                                        _pages(block_table, raw_ring), k, score_dtype,
+                                        _ptr(topk_idx), _ptr(scores_out), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
     return topk_idx
 
 

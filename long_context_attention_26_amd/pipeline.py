@@ -54,6 +54,12 @@ class HybridAttentionState:
     def compress_range(self, t0, t1, stream=None):
         """Pool the CSA and HCA blocks whose last token lies in [t0, t1), all streams in
         one launch; each block is written at its own entry index."""
+        jobs = self.pool_jobs(t0, t1)
+        if jobs:
+            hcsa.compress_kv_batched(jobs, self.B, stream=stream)
+
+    def pool_jobs(self, t0, t1):
+        """The pooling jobs of the CSA and HCA blocks whose last token lies in [t0, t1)."""
         jobs = []
         for ratio, pairs in ((R_CSA, ((self.K_raw, "csa_k", self.Kc), (self.V_raw, "csa_v", self.Vc),
                                       (self.I_raw, "idx_k", self.Ic))),
@@ -67,8 +73,7 @@ class HybridAttentionState:
                 ys = self.Ics[:, j0:j1] if (y is self.Ic and self.Ics is not None) else None
                 jobs.append(hcsa.pool_job(x[:, j0 * ratio: j1 * ratio], self.omegas[name], ratio,
                                           y[:, j0:j1], ys))
-        if jobs:
-            hcsa.compress_kv_batched(jobs, self.B, stream=stream)
+        return jobs
 
 
 class DecodeStep:
@@ -128,6 +133,15 @@ class DecodeStep:
                             self.score_code, self.idx, k_scales=st.Ics,
                             workspace=self.ws_itopk, stream=stream, mx_fp8=self.mx_fp8)
 
+    def run_pool_index_topk(self, q_idx, w_idx, pos0, stream=None):
+        """Pooling of the blocks the query tokens complete, then indexer + top-k, as one
+        call (for MXFP4 keys at decode the pooling shares the selection floors' launch)."""
+        st = self.st
+        hcsa.csa_pool_index_topk(st.pool_jobs(pos0, pos0 + self.Nq), q_idx, w_idx, st.Ic,
+                                 st.Nc, R_CSA, pos0, self.topk, self.score_code, self.idx,
+                                 k_scales=st.Ics, workspace=self.ws_itopk, stream=stream,
+                                 mx_fp8=self.mx_fp8)
+
     def run_attend(self, q, pos0, stream=None):
         self._attend(q, pos0, stream)
 
@@ -142,13 +156,14 @@ class DecodeStep:
         after the last (used to record timing events on the stream)."""
         st = self.st
         mark = marks or (lambda name: None)
-        mark("compress")
-        if append:
-            st.compress_range(pos0, pos0 + self.Nq, stream=stream)
-        mark("index_topk")
-        if scores_out is None:
+        mark("pool_index_topk")
+        if scores_out is None and append:
+            self.run_pool_index_topk(q_idx, w_idx, pos0, stream=stream)
+        elif scores_out is None:
             self.run_index_topk(q_idx, w_idx, pos0, stream=stream)
         else:
+            if append:
+                st.compress_range(pos0, pos0 + self.Nq, stream=stream)
             hcsa.csa_index_scores(q_idx, w_idx, st.Ic, st.Nc, R_CSA, pos0, scores_out,
                                   k_scales=st.Ics, stream=stream, mx_fp8=self.mx_fp8)
             hcsa.topk(scores_out, st.B, self.Nq, st.Nc, R_CSA, pos0, self.topk, self.idx,

@@ -128,3 +128,97 @@ def test_fused_index_topk_equals_two_calls(H, gpu, case):
         b, i = divmod(r, Nq)
         nv = _nv(case["pos"][b] + i, N)
         assert np.array_equal(got[r], O.select_topk(sc[r], nv, k)), (case["name"], r)
+
+
+POOL_CASES = [
+    # the query token completes a 4-token and a 128-token block
+    dict(name="decode-b4", B=4, Nq=1, P=128 * 2188 - 1, k=1024, paged=False, fp8=False),
+    dict(name="decode-paged-fp8", B=2, Nq=1, P=128 * 1563 - 1, k=512, paged=True, fp8=True),
+    dict(name="nq4", B=2, Nq=4, P=4 * 40000 - 2, k=700, paged=False, fp8=False),
+    dict(name="bf16-keys", B=2, Nq=1, P=4 * 30000 - 1, k=512, paged=False, fp8=False,
+         bf16_keys=True),
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=[c["name"] for c in POOL_CASES])
+def test_pool_index_topk_equals_separate_calls(H, gpu, case):
+    """Pooling + indexer + top-k in one call against the pooling call then the indexer +
+    top-k call: the same pooled caches and the same selection, bit for bit.  The jobs pool
+    the blocks the query tokens complete (indexer keys, a 4-token K stream and a 128-token
+    K stream); with MXFP4 keys the pooling shares the launch of the selection floors."""
+    print(f"pool + index-topk {case['name']}", flush=True)
+    B, Nq, P, k = case["B"], case["Nq"], case["P"], case["k"]
+    d_I, H_I, D = 64, 4, 128
+    T = P + Nq                                    # raw tokens up to the last query
+    N = T // 4 + 4
+    g = torch.Generator().manual_seed(5)
+    Ir = torch.randn(B, T, d_I, generator=g).to(torch.bfloat16).to(gpu)
+    Kr = torch.randn(B, T, D, generator=g).to(torch.bfloat16).to(gpu)
+    om4 = (torch.randn(4, generator=g) / 2).to(gpu)
+    om128 = (torch.randn(128, generator=g) / 11).to(gpu)
+    q = torch.randn(B, Nq, H_I, d_I, generator=g).to(torch.bfloat16).to(gpu)
+    w = (torch.randn(B, Nq, H_I, generator=g).abs() / 2).to(gpu)
+    mx = not case.get("bf16_keys")
+
+    def fresh():
+        c = {}
+        if mx:
+            c["Ic"] = torch.zeros(B, N, d_I // 2, dtype=torch.uint8, device=gpu)
+            c["Ics"] = torch.zeros(B, N, d_I // 32, dtype=torch.uint8, device=gpu)
+        else:
+            c["Ic"], c["Ics"] = torch.zeros(B, N, d_I, dtype=torch.bfloat16, device=gpu), None
+        c["Kc"] = torch.zeros(B, N, D, dtype=torch.bfloat16, device=gpu)
+        c["Kh"] = torch.zeros(B, N // 32 + 1, D, dtype=torch.bfloat16, device=gpu)
+        # entries completed before the first query token
+        H.compress_kv_batched([H.pool_job(Ir[:, :P], om4, 4, c["Ic"], c["Ics"]),
+                               H.pool_job(Kr[:, :P], om4, 4, c["Kc"]),
+                               H.pool_job(Kr[:, :P], om128, 128, c["Kh"])], B)
+        return c
+
+    def jobs(c):
+        out = []
+        for ratio, x, om, y, ys in ((4, Ir, om4, c["Ic"], c["Ics"]), (4, Kr, om4, c["Kc"], None),
+                                    (128, Kr, om128, c["Kh"], None)):
+            j0, j1 = -(-(P + 1) // ratio) - 1, (P + Nq) // ratio
+            if j1 > j0:
+                out.append(H.pool_job(x[:, j0 * ratio: j1 * ratio], om, ratio, y[:, j0:j1],
+                                      None if ys is None else ys[:, j0:j1]))
+        return out
+
+    table = None
+    ca, cb = fresh(), fresh()
+    if case["paged"]:
+        nblk = -(-T // 128)
+        perm = torch.randperm(B * nblk + 3, generator=g)[: B * nblk].to(torch.int32)
+        table = perm.view(B, nblk).to(gpu)
+
+        def paged(c):
+            r = {"Ic": _page_pool(c["Ic"], table, 32, gpu), "Ics": _page_pool(c["Ics"], table, 32, gpu),
+                 "Kc": _page_pool(c["Kc"], table, 32, gpu), "Kh": _page_pool(c["Kh"], table, 1, gpu)}
+            return r
+        ca, cb = paged(ca), paged(cb)
+        Irp, Krp = _page_pool(Ir, table, 128, gpu), _page_pool(Kr, table, 128, gpu)
+
+        def jobs(c):                                         # noqa: F811 (paged form)
+            out = []
+            for ratio, x, om, y, ys in ((4, Irp, om4, c["Ic"], c["Ics"]), (4, Krp, om4, c["Kc"], None),
+                                        (128, Krp, om128, c["Kh"], None)):
+                j0, j1 = -(-(P + 1) // ratio) - 1, (P + Nq) // ratio
+                if j1 > j0:
+                    out.append(H.pool_job(x, om, ratio, y, ys, T=(j1 - j0) * ratio,
+                                          pos0=j0 * ratio))
+            return out
+    fp8 = case["fp8"]
+    idx_a = torch.full((B, Nq, k), -7, dtype=torch.int32, device=gpu)
+    idx_b = torch.full_like(idx_a, -7)
+    H.compress_kv_batched(jobs(ca), B, block_table=table)
+    H.csa_index_topk(q, w, ca["Ic"], N, 4, P, k, H.BF16, idx_a, k_scales=ca["Ics"],
+                     block_table=table, mx_fp8=fp8)
+    H.csa_pool_index_topk(jobs(cb), q, w, cb["Ic"], N, 4, P, k, H.BF16, idx_b,
+                          k_scales=cb["Ics"], block_table=table, mx_fp8=fp8)
+    torch.cuda.synchronize()
+    for name in ca:
+        if ca[name] is not None:
+            assert torch.equal(ca[name], cb[name]), f"{case['name']}: pooled {name} differs"
+    assert torch.equal(idx_a, idx_b), f"{case['name']}: selection differs"
+    assert (idx_a[:, :, 0] >= 0).all()
