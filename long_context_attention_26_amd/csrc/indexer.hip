@@ -907,6 +907,41 @@ __global__ __launch_bounds__(kMxResThreads) void mx_list_resolve_kernel(IdxMxDev
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = (nv + A.chunk - 1) / A.chunk;        // chunks holding visible keys
   const uint32_t* cnt = A.counts + static_cast<int64_t>(row) * A.nchunks;
+  // Direct form (few chunks): tpc threads per chunk, thread (c, sub) loads the slice
+  // [16 sub, 16 sub + 16) of chunk c's list together with the count, without waiting for
+  // a prefix; thread order is index order.  Taken when every chunk's count fits its
+  // threads' slices and the row holds at least k candidates, else the prefix form below.
+  int pw = 1;
+  while (pw < nch) pw <<= 1;
+  const int tpc = pw <= kMxResThreads ? kMxResThreads / pw : 0;
+  if (tpc > 0 && tpc * 16 <= A.chunk) {
+    const int c = threadIdx.x / tpc, sub = threadIdx.x % tpc;
+    int cc = 0;
+    u32x4 e[4] = {};
+    if (c < nch) {
+      cc = static_cast<int>(cnt[c]);
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          A.lists + (static_cast<int64_t>(row) * A.nchunks + c) * A.chunk + 16 * sub);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) e[v] = src[v];
+    }
+    const int my = min(max(cc - 16 * sub, 0), 16);
+    const int over = __syncthreads_or(cc > tpc * 16);
+    const int C = sel::block_total_bits<W, 5>(my, s_cnt, 0);
+    if (!over && C >= k) {
+      uint32_t ck[16];
+      int32_t cj[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t v = e[u >> 2][u & 3];
+        ck[u] = u < my ? v >> 16 : 0u;
+        cj[u] = u < my ? c * A.chunk + static_cast<int>(v & 0xffffu) : 0;
+      }
+      sel::select_candidates<16, kMxResThreads, 16>(ck, cj, my, A.floor[row], k, out, s_gt,
+                                                    s_eq, s_hb, s_hist, s_sel);
+      return;
+    }
+  }
   if (threadIdx.x < 64) {                              // prefix of the counts, 64 at a time
     int carry = 0;
     for (int base = 0; base < nch; base += 64) {
