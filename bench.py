@@ -94,7 +94,7 @@ def measured_traffic(cfg, mx_fp8=False):
     src = open(os.path.join(ROOT, "long_context_attention_26_amd", "csrc", "indexer.hip")).read()
     try:
         a = src.index("constexpr int kMxMaxUnits = 16 * 4;")
-        b = src.index("template <int HI, bool QBF16, bool F8>\nhipError_t launch_mx_mfma_hi(")
+        b = src.index("// ---------------------------------------------------------------- fused decode selection")
     except ValueError:
         return None
     if hashlib.sha256(src[a:b].encode()).hexdigest() != rec.get("kernel_text_sha256"):
