@@ -137,6 +137,8 @@ POOL_CASES = [
     dict(name="nq4", B=2, Nq=4, P=4 * 40000 - 2, k=700, paged=False, fp8=False),
     dict(name="bf16-keys", B=2, Nq=1, P=4 * 30000 - 1, k=512, paged=False, fp8=False,
          bf16_keys=True),
+    # raw tokens in a ring of 256 rows per sequence (the state cache)
+    dict(name="ring", B=3, Nq=1, P=128 * 700 - 1, k=1024, paged=False, fp8=False, ring=256),
 ]
 
 
@@ -208,14 +210,34 @@ def test_pool_index_topk_equals_separate_calls(H, gpu, case):
                     out.append(H.pool_job(x, om, ratio, y, ys, T=(j1 - j0) * ratio,
                                           pos0=j0 * ratio))
             return out
+    ring = case.get("ring", 0)
+    if ring:
+        # the last `ring` raw tokens of each sequence, position t in row t mod ring
+        rows = torch.arange(T - ring, T, device=gpu)
+        Ir_ring = torch.zeros(B, ring, d_I, dtype=torch.bfloat16, device=gpu)
+        Kr_ring = torch.zeros(B, ring, D, dtype=torch.bfloat16, device=gpu)
+        Ir_ring[:, rows % ring] = Ir[:, rows]
+        Kr_ring[:, rows % ring] = Kr[:, rows]
+
+        def jobs(c):                                         # noqa: F811 (ring form)
+            out = []
+            for ratio, x, om, y, ys in ((4, Ir_ring, om4, c["Ic"], c["Ics"]),
+                                        (4, Kr_ring, om4, c["Kc"], None),
+                                        (128, Kr_ring, om128, c["Kh"], None)):
+                j0, j1 = -(-(P + 1) // ratio) - 1, (P + Nq) // ratio
+                if j1 > j0:
+                    out.append(H.pool_job(x, om, ratio, y[:, j0:j1],
+                                          None if ys is None else ys[:, j0:j1],
+                                          T=(j1 - j0) * ratio, pos0=j0 * ratio))
+            return out
     fp8 = case["fp8"]
     idx_a = torch.full((B, Nq, k), -7, dtype=torch.int32, device=gpu)
     idx_b = torch.full_like(idx_a, -7)
-    H.compress_kv_batched(jobs(ca), B, block_table=table)
+    H.compress_kv_batched(jobs(ca), B, block_table=table, raw_ring=ring)
     H.csa_index_topk(q, w, ca["Ic"], N, 4, P, k, H.BF16, idx_a, k_scales=ca["Ics"],
                      block_table=table, mx_fp8=fp8)
     H.csa_pool_index_topk(jobs(cb), q, w, cb["Ic"], N, 4, P, k, H.BF16, idx_b,
-                          k_scales=cb["Ics"], block_table=table, mx_fp8=fp8)
+                          k_scales=cb["Ics"], block_table=table, raw_ring=ring, mx_fp8=fp8)
     torch.cuda.synchronize()
     for name in ca:
         if ca[name] is not None:
