@@ -321,7 +321,7 @@ def main():
     args = ap.parse_args()
     if args.train:
         if args.gpus != 1:
-            sys.exit("bench.py: this build runs on one GPU only")
+            sys.exit("bench.py: the benchmark runs on one GPU only (--gpus 1)")
         train_backward(args)
         return
     if args.copy_calibration:
@@ -330,9 +330,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); multi-GPU sharding is described in the design notes "
-              "but not implemented.", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); how the path would shard over several GPUs is "
+              "described, not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
