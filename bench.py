@@ -355,15 +355,15 @@ def main():
             stp.mx_fp8 = True
     torch.cuda.synchronize()
 
-    # Each copy's step is captured as one HIP graph, and once more as two graphs (pooling +
-    # indexer + top-k | CSA + HCA attention).  Every SAMPLE-th timed
-    # step runs the three-graph form with timing events between the graphs on the launch
-    # stream: they give the per-stage split and the indexer kernel's duration for the
-    # roofline.  The SAMPLE - 1 steps between two sampled ones replay one graph that chains
+    # Each copy's step is captured as one HIP graph, and its attention once more as a graph of
+    # its own.  Every SAMPLE-th timed step runs the pooling + indexer + top-k call directly
+    # (its key scan records dispatch-level events) and then the attention graph, with timing
+    # events between them on the launch stream: they give the per-stage split and the key
+    # scan's duration for the roofline.  The SAMPLE - 1 steps between two sampled ones replay one graph that chains
     # them (each on its own cache copy, every kernel of every step executed), as a model's
     # per-token graph chains its layers: the host's graph-launch latency, several
     # microseconds per launch, then falls on one step in SAMPLE instead of every step.
-    SAMPLE = 8
+    SAMPLE = 16
     stages = ["pool_index_topk", "attend"]
     full, split = [], []
     cap_stream = torch.cuda.Stream()
