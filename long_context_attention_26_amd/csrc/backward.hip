@@ -47,6 +47,7 @@ struct AttnBwdDev {
   float* dvr;
   int64_t dr_bstride;
   float* dt_out;         // [rows][16] or null: dout.o - dlse per head, for the key-major pass
+  const uint16_t* dout16;  // [rows][16][128] bf16 copy of dout for the key-major pass, or null
 };
 
 // Sums each of the N values v[0..N) over the 64 lanes of the wave with no lane-dependent
@@ -442,7 +443,8 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
 //   dK^T += Q^T dS,  dV^T += dout^T P   (16x16x32 over the step's 32 rows; Q^T and dout^T
 // built from 16-byte row slices by byte permutes, as the forward builds V^T),
 // accumulated over the chunk in registers, summed over the 4 waves in LDS and added to
-// memory once per element.  dout.o - dlse per (token, head) comes from the dq pass.
+// memory once per element.  dout.o - dlse per (token, head) comes from the dq pass, dout as
+// a bf16 copy (the MFMA operand precision) made once before this pass.
 // HCA: grid (ceil(N / 16), chunks, B), keys e0 = 16 * blockIdx.x.  Window: grid
 // (ceil((128 + n_win - 1) / 16), chunks, B), the tiles covering the band of raw rows that the
 // chunk's windows reach, from its first query's window start on.
@@ -506,13 +508,11 @@ __global__ __launch_bounds__(256) void key_bwd_kernel(AttnBwdDev G) {
       // A operands: q and dout rows of head col at channels 32s + 8g
       u32x4 qa[4], da[4];
       const uint16_t* qrow = q16 + (row * 16 + col) * 128;
-      const float* drow = G.dout + (row * 16 + col) * 128;
+      const uint16_t* drow = G.dout16 + (row * 16 + col) * 128;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         qa[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
-        const float* d8 = drow + 32 * s + 8 * g;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) da[s][m] = pack_bf16x2(d8[2 * m], d8[2 * m + 1]);
+        da[s] = *reinterpret_cast<const u32x4*>(drow + 32 * s + 8 * g);
       }
       f32x4 sv = f32x4{0, 0, 0, 0}, dp = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -541,9 +541,7 @@ __global__ __launch_bounds__(256) void key_bwd_kernel(AttnBwdDev G) {
       const int64_t row = static_cast<int64_t>(b) * A.Nq + (tok < A.Nq ? tok : 0);
       const int64_t hrow = row * 16 + 4 * g + (j & 3);
       qs[j] = *reinterpret_cast<const u32x4*>(q16 + hrow * 128 + 8 * col);
-      const float* d8 = G.dout + hrow * 128 + 8 * col;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) ds8[j][m] = pack_bf16x2(d8[2 * m], d8[2 * m + 1]);
+      ds8[j] = *reinterpret_cast<const u32x4*>(G.dout16 + hrow * 128 + 8 * col);
     }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
@@ -585,6 +583,17 @@ __global__ __launch_bounds__(256) void key_bwd_kernel(AttnBwdDev G) {
                        : (m ? G.dvc : G.dkc) + b * G.dc_bstride + er * 128 + c;
       unsafeAtomicAdd(dst, m ? s_acc[1][r][c] : A.scale * s_acc[0][r][c]);
     }
+  }
+}
+
+// bf16 copy (round to nearest even) of n8 groups of 8 floats; grid-stride, block 256.
+__global__ __launch_bounds__(256) void bf16_copy_kernel(const float* __restrict__ x,
+                                                        uint16_t* __restrict__ y, int64_t n8) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n8; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(x)[2 * i];
+    const f32x4 b = reinterpret_cast<const f32x4*>(x)[2 * i + 1];
+    reinterpret_cast<u32x4*>(y)[i] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                            pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
   }
 }
 
@@ -700,8 +709,15 @@ bool bwd_key_major(const AttnArgs& a) {
   return a.kv_dtype == 1 && a.H == 16 && a.d == 128 && a.Nq >= 16;
 }
 
+// key-major pass: dout.o - dlse [rows][16] f32, then dout as bf16 [rows][16][128]
+static size_t bwd_dt_bytes(const AttnArgs& a) {
+  return align256(static_cast<size_t>(a.B) * a.Nq * 16 * 4);
+}
+
 size_t bwd_workspace_bytes(const AttnArgs& a) {
-  return bwd_key_major(a) ? align256(static_cast<size_t>(a.B) * a.Nq * 16 * 4) : 0;
+  return bwd_key_major(a)
+             ? bwd_dt_bytes(a) + align256(static_cast<size_t>(a.B) * a.Nq * 16 * 128 * 2)
+             : 0;
 }
 
 bool attn_bwd_shape_supported(int H, int d) {
@@ -726,7 +742,17 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
   G.dvr = g.dvr;
   G.dr_bstride = g.dr_bstride;
   G.dt_out = nullptr;
+  G.dout16 = nullptr;
   const int rows = a.B * a.Nq;
+  // the key-major pass's inputs in the workspace: dt_out, and dout converted to bf16 once
+  auto key_major_inputs = [&]() {
+    G.dt_out = static_cast<float*>(g.ws);
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(static_cast<char*>(g.ws) + bwd_dt_bytes(a));
+    G.dout16 = d16;
+    const int64_t n8 = static_cast<int64_t>(rows) * 16 * 128 / 8;
+    const int blocks = static_cast<int>(std::min<int64_t>((n8 + 255) / 256, 4096));
+    bf16_copy_kernel<<<blocks, 256, 0, s>>>(g.dout, d16, n8);
+  };
   if (rows == 0) return hipSuccess;
   const int hh = bwd_heads(a.H), cpl = bwd_cpl(a.d);
   const bool bf = a.kv_dtype == 1;
@@ -734,7 +760,7 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
     const int chunks = (a.Nq + kDkvTokens - 1) / kDkvTokens;
     if (csa && bwd_key_major(a) && g.ws && a.n_win > 0) {
       // the window rows, shared by consecutive query tokens, key-major; the rest per query
-      G.dt_out = static_cast<float*>(g.ws);
+      key_major_inputs();
       AttnBwdDev Gq = G;
       Gq.dkr = Gq.dvr = nullptr;
       attn_bwd_mfma_kernel<true, true><<<rows, 256, 0, s>>>(Gq);
@@ -746,7 +772,7 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
       attn_bwd_mfma_kernel<true, true><<<rows, 256, 0, s>>>(G);
     } else if (bwd_key_major(a) && g.ws) {
       // many query tokens share the entries: dq query-major, dK / dV key-major
-      G.dt_out = static_cast<float*>(g.ws);
+      key_major_inputs();
       attn_bwd_mfma_kernel<false, false><<<rows, 256, 0, s>>>(G);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
