@@ -648,7 +648,8 @@ int hcsa_csa_sparse_attn_bwd(const void* q, const void* kc, const void* vc, int6
   a.idx = topk_idx; a.k = k; a.k_raw = k_raw; a.v_raw = v_raw; a.raw_bstride = raw_bstride;
   a.T_raw = T_raw; a.raw_pos0 = raw_pos0; a.n_win = n_win; a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
-  rc = check_ws(workspace, ws_bytes, hcsa::bwd_workspace_bytes(a));
+  // a null workspace is allowed: the shared keys then get their gradients query-major
+  rc = workspace ? check_ws(workspace, ws_bytes, hcsa::bwd_workspace_bytes(a)) : HCSA_OK;
   if (rc) return rc;
   hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkc, dvc, dc_bstride, dk_raw, dv_raw,
                       draw_bstride, workspace};
@@ -688,7 +689,8 @@ int hcsa_hca_dense_attn_bwd(const void* q, const void* kh, const void* vh, int64
   a.q = q; a.kc = kh; a.vc = vh; a.c_bstride = h_bstride; a.N = N; a.ratio = ratio;
   a.pos0 = pos0; a.seq_pos = seq_pos;
   a.kv_dtype = kv_dtype; a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.scale = scale;
-  rc = check_ws(workspace, ws_bytes, hcsa::bwd_workspace_bytes(a));
+  // a null workspace is allowed: the shared keys then get their gradients query-major
+  rc = workspace ? check_ws(workspace, ws_bytes, hcsa::bwd_workspace_bytes(a)) : HCSA_OK;
   if (rc) return rc;
   hcsa::AttnBwdArgs g{out, lse, dout, dlse, dq, dkh, dvh, dh_bstride, nullptr, nullptr, 0,
                       workspace};

@@ -351,13 +351,16 @@ def hca_dense_attn(q, kh, vh, N, ratio, pos0, scale, out, lse, workspace=None, s
 
 def csa_sparse_attn_bwd(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, ratio, pos0,
                         scale, out, lse, dout, dq, dkc, dvc, dk_raw, dv_raw, dlse=None,
-                        workspace=None, stream=None, seq_pos=None):
+                        workspace=None, stream=None, seq_pos=None,
+                        key_major=True):
     """Backward of csa_sparse_attn: writes dq [B, Nq, H, d] f32; adds into dkc, dvc
-    [B, >=N, d] f32 and dk_raw, dv_raw [B, T_raw, d] f32."""
+    [B, >=N, d] f32 and dk_raw, dv_raw [B, T_raw, d] f32.
+    key_major=False (with no workspace given) passes a null workspace: keys shared by
+    consecutive tokens then get their gradients query-major, with atomics."""
     B, Nq, H, d = q.shape
     k = topk_idx.shape[-1]
     nbytes = lib.hcsa_csa_sparse_attn_bwd_workspace_size(B, Nq, H, d, dtype_code(q))
-    if workspace is None and nbytes:
+    if workspace is None and nbytes and key_major:
         workspace = alloc_workspace(nbytes, q.device)
     _check(lib.hcsa_csa_sparse_attn_bwd(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N,
                                         _ptr(topk_idx), k, _ptr(k_raw), _ptr(v_raw),
@@ -373,11 +376,14 @@ def csa_sparse_attn_bwd(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, r
 
 
 def hca_dense_attn_bwd(q, kh, vh, N, ratio, pos0, scale, out, lse, dout, dq, dkh, dvh,
-                       dlse=None, workspace=None, stream=None, seq_pos=None):
-    """Backward of hca_dense_attn: writes dq; adds into dkh, dvh [B, >=N, d] f32."""
+                       dlse=None, workspace=None, stream=None, seq_pos=None,
+                       key_major=True):
+    """Backward of hca_dense_attn: writes dq; adds into dkh, dvh [B, >=N, d] f32.
+    key_major=False (with no workspace given) passes a null workspace: keys shared by
+    consecutive tokens then get their gradients query-major, with atomics."""
     B, Nq, H, d = q.shape
     nbytes = lib.hcsa_hca_dense_attn_bwd_workspace_size(B, Nq, H, d, dtype_code(q))
-    if workspace is None and nbytes:
+    if workspace is None and nbytes and key_major:
         workspace = alloc_workspace(nbytes, q.device)
     _check(lib.hcsa_hca_dense_attn_bwd(_ptr(q), _ptr(kh), _ptr(vh), kh.stride(0), N, ratio, pos0,
                                        _pos_ptr(seq_pos, B), dtype_code(q), B, Nq, H, d, scale,

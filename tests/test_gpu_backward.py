@@ -60,11 +60,14 @@ CSA_CASES = [
     # windows clipped at position 0 with padded selections
     dict(dt="bf16", H=16, d=128, N=900, k=128, n_win=128, Nq=300, B=2, pos0=3300, dlse=True),
     dict(dt="bf16", H=16, d=128, N=80, k=64, n_win=64, Nq=200, B=1, pos0=20, dlse=False),
+    # the same rows with a null workspace: the window rows' gradients stay query-major
+    dict(dt="bf16", H=16, d=128, N=900, k=128, n_win=128, Nq=300, B=2, pos0=3300, dlse=True,
+         nows=True),
 ]
 
 
 @pytest.mark.parametrize("case", CSA_CASES, ids=lambda c: f"{c['dt']}-H{c['H']}-d{c['d']}-"
-                         f"k{c['k']}-Nq{c['Nq']}")
+                         f"k{c['k']}-Nq{c['Nq']}" + ("-nows" if c.get("nows") else ""))
 def test_csa_backward(H, gpu, case):
     print(f"csa bwd {case}", flush=True)
     B, Nq, Hh, d, N, k, w = case["B"], case["Nq"], case["H"], case["d"], case["N"], case["k"], case["n_win"]
@@ -115,7 +118,8 @@ def test_csa_backward(H, gpu, case):
                           torch.from_numpy(idx.astype(np.int32)).to(gpu), dev(Kr, tdt, gpu),
                           dev(Vr, tdt, gpu), raw_pos0, w, ratio, pos0, scale, out_t, lse_t,
                           dev(dout, torch.float32, gpu), dq, dKc, dVc, dKr, dVr,
-                          dlse=None if dlse is None else dev(dlse, torch.float32, gpu))
+                          dlse=None if dlse is None else dev(dlse, torch.float32, gpu),
+                          key_major=not case.get("nows", False))
     torch.cuda.synchronize()
     tol = _tol(dt, Hh, d)
     _rel_close(f64(dq), dq_ref, tol, "dq")
@@ -136,10 +140,13 @@ HCA_CASES = [
     # 45 entries (a partial 16-entry tile), and a tile no token of the chunk sees
     dict(dt="bf16", H=16, d=128, N=45, Nq=300, B=2, pos0=128 * 40 - 150, dlse=True),
     dict(dt="bf16", H=16, d=128, N=45, Nq=300, B=1, pos0=128 * 20, dlse=False),
+    # a null workspace: the entries' gradients stay query-major
+    dict(dt="bf16", H=16, d=128, N=45, Nq=300, B=2, pos0=128 * 40 - 150, dlse=True, nows=True),
 ]
 
 
-@pytest.mark.parametrize("case", HCA_CASES, ids=lambda c: f"{c['dt']}-H{c['H']}-N{c['N']}-Nq{c['Nq']}")
+@pytest.mark.parametrize("case", HCA_CASES, ids=lambda c: f"{c['dt']}-H{c['H']}-N{c['N']}-Nq{c['Nq']}"
+                         + ("-nows" if c.get("nows") else ""))
 def test_hca_backward(H, gpu, case):
     print(f"hca bwd {case}", flush=True)
     B, Nq, Hh, d, N, pos0, dt = case["B"], case["Nq"], case["H"], case["d"], case["N"], case["pos0"], case["dt"]
@@ -167,7 +174,8 @@ def test_hca_backward(H, gpu, case):
     H.hca_dense_attn_bwd(dev(q, tdt, gpu), dev(Kh, tdt, gpu), dev(Vh, tdt, gpu), N, 128, pos0,
                          scale, dev(O.round_fp32(o_ref), torch.float32, gpu),
                          dev(l_ref, torch.float32, gpu), dev(dout, torch.float32, gpu), dq, dK,
-                         dV, dlse=None if dlse is None else dev(dlse, torch.float32, gpu))
+                         dV, dlse=None if dlse is None else dev(dlse, torch.float32, gpu),
+                         key_major=not case.get("nows", False))
     torch.cuda.synchronize()
     tol = _tol(dt, Hh, d)
     _rel_close(f64(dq), dq_ref, tol, "dq")
