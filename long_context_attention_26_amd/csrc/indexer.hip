@@ -793,7 +793,7 @@ __device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row
           int n = 0;
 #pragma unroll
           for (int e = 0; e < MPL; ++e) n += v[e] >= th;
-          cnt[d - 1] = sel::wave_sum_bits<4>(n);
+          cnt[d - 1] = sel::wave_sum_bits<sel::bits_for(MPL)>(n);
         }
         const uint32_t d = cnt[2] >= m ? 3u : cnt[1] >= m ? 2u : cnt[0] >= m ? 1u : 0u;
         pre |= d << sh;
@@ -813,7 +813,7 @@ __device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row
       int n = 0;
 #pragma unroll
       for (int e = 0; e < PT; ++e) n += top[e] >= th;
-      cnt[d - 1] = sel::wave_sum_bits<4>(n);
+      cnt[d - 1] = sel::wave_sum_bits<sel::bits_for(PT)>(n);
     }
     const uint32_t d = cnt[2] >= mw ? 3u : cnt[1] >= mw ? 2u : cnt[0] >= mw ? 1u : 0u;
     pre |= d << sh;
@@ -927,7 +927,7 @@ __global__ __launch_bounds__(kMxResThreads) void mx_list_resolve_kernel(IdxMxDev
     }
     const int my = min(max(cc - 16 * sub, 0), 16);
     const int over = __syncthreads_or(cc > tpc * 16);
-    const int C = sel::block_total_bits<W, 5>(my, s_cnt, 0);
+    const int C = sel::block_total_bits<W, sel::bits_for(16)>(my, s_cnt, 0);
     if (!over && C >= k) {
       uint32_t ck[16];
       int32_t cj[16];

@@ -16,6 +16,18 @@ namespace sel {
 
 // ---------------------------------------------------------------- wave / block counting
 
+// Bits that hold every value in [0, max_value]: the BITS argument of the ballot counts
+// below for per-thread values bounded by max_value (a value needing more bits is counted
+// wrongly, so callers derive BITS from their bound with this).
+constexpr int bits_for(int max_value) {
+  int b = 0;
+  while (b < 31 && (1 << b) <= max_value) ++b;
+  return b;
+}
+static_assert(bits_for(0) == 0 && bits_for(1) == 1 && bits_for(16) == 5 && bits_for(31) == 5 &&
+                  bits_for(32) == 6,
+              "bits_for");
+
 // Wave sum of a small non-negative int (< 2^BITS) from the ballots of its bits: scalar
 // popcounts, no cross-lane data movement (a lane shuffle goes through the LDS crossbar).
 template <int BITS>
@@ -231,19 +243,20 @@ __device__ void select_exact_row(const RowView<KB>& V, int k, int32_t* out,
   }
   const int need = k - gt_all;                   // 1 <= need <= keys equal to T
   slot += min(need, eq_rank);
+  constexpr int CB = bits_for(EPC);              // a chunk's keys above / equal to T
   for (int base = cw0; base < cw1; base += 64) {
     const int ch = base + lane;
     uint32_t gtm = 0, eqm = 0;
     if (ch < cw1) gt_eq(ch, gtm, eqm);
     int eq_tot;
-    int r = eq_rank + wave_prefix_bits<4>(__popc(eqm), below, eq_tot);
+    int r = eq_rank + wave_prefix_bits<CB>(__popc(eqm), below, eq_tot);
     uint32_t sel = gtm;
     for (uint32_t m = eqm; m; m &= m - 1) {      // ties in index order while some are needed
       if (r < need) sel |= m & (~m + 1);
       ++r;
     }
     int tot;
-    int o = slot + wave_prefix_bits<4>(__popc(sel), below, tot);
+    int o = slot + wave_prefix_bits<CB>(__popc(sel), below, tot);
     while (sel) {
       if (o < k) out[o] = ch * EPC + __ffs(sel) - 1;
       ++o;
@@ -316,9 +329,11 @@ __device__ void select_candidates(const uint32_t (&ck)[PER], const int32_t (&cj)
     gt += u < cnt && ck[u] > T;
     eq += u < cnt && ck[u] == T;
   }
+  // a thread holds up to PER candidates, so its counts need bits_for(PER) bits (6 for 32)
+  constexpr int CB = bits_for(PER);
   int gt_w, eq_w;
-  const int gt_pre = wave_prefix_bits<5>(gt, below, gt_w);
-  const int eq_pre = wave_prefix_bits<5>(eq, below, eq_w);
+  const int gt_pre = wave_prefix_bits<CB>(gt, below, gt_w);
+  const int eq_pre = wave_prefix_bits<CB>(eq, below, eq_w);
   if (lane == 0) {
     s_gt[w] = gt_w;
     s_eq[w] = eq_w;

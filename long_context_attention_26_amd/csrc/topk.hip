@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
       st[u] = sv ? V_t::to_key(V_t::raw_of(cur[u], 0)) >> (KB - 16) : 0u;
       nmine += sv;
     }
-    const int ns = block_total_bits<kRowsWaves, 3>(nmine, s_cnt, 0);   // also orders the zeroing
+    const int ns = block_total_bits<kRowsWaves, bits_for(4)>(nmine, s_cnt, 0);   // also orders the zeroing
     const int m = max(1, min(ns, static_cast<int>((2LL * P.k * ns + nv - 1) / nv) + 16));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
       const int ch = base + 64 * u + lane;
       uint32_t msk = ch < cw1 ? V.ge_mask(cur[u], ch * EPC, L) : 0u;
       int tot;
-      int o = wslot + wave_prefix_bits<4>(__popc(msk), below, tot);
+      int o = wslot + wave_prefix_bits<bits_for(EPC)>(__popc(msk), below, tot);
       while (msk) {
         const int e = __ffs(msk) - 1;
         msk &= msk - 1;
@@ -256,8 +256,8 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
     gt += in && ck[u] > T;
     eq += in && ck[u] == T;
   }
-  gt = wave_sum_bits<4>(gt);
-  eq = wave_sum_bits<4>(eq);
+  gt = wave_sum_bits<bits_for(STEPS)>(gt);
+  eq = wave_sum_bits<bits_for(STEPS)>(eq);
   if (lane == 0) {
     s_gt[w] = gt;
     s_eq[w] = eq;
@@ -376,7 +376,7 @@ __device__ uint32_t row_floor(const RowView<KB>& V, int k, uint32_t* s_min) {
         int n = 0;
 #pragma unroll
         for (int u = 0; u < PT; ++u) n += top[u] >= th;
-        cnt[d - 1] = wave_sum_bits<5>(n);
+        cnt[d - 1] = wave_sum_bits<bits_for(PT)>(n);
       }
       const uint32_t d = cnt[2] >= mw ? 3u : cnt[1] >= mw ? 2u : cnt[0] >= mw ? 1u : 0u;
       pre |= d << sh;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_extract_kernel(TopkDev P, Seg
     msk[u] = ch < nch ? V.ge_mask(x[u], ch * EPC, L) : 0u;
     c += __popc(msk[u]);
   }
-  c = wave_sum_bits<6>(c);
+  c = wave_sum_bits<bits_for(CPL * EPC)>(c);
   if (lane == 0) s_w[w] = c;
   __syncthreads();
   int slot = 0, total = 0;
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_extract_kernel(TopkDev P, Seg
   for (int u = 0; u < CPL; ++u) {
     const int ch = ch0 + 64 * u;
     int tot;
-    int o = slot + wave_prefix_bits<4>(__popc(msk[u]), below, tot);
+    int o = slot + wave_prefix_bits<bits_for(EPC)>(__popc(msk[u]), below, tot);
     uint32_t m = msk[u];
     while (m) {
       const int e = __ffs(m) - 1;

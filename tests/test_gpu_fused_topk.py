@@ -54,6 +54,16 @@ CASES = [
     # large scales on one stretch: the top keys crowd a few chunks
     dict(name="skewed", B=2, Nq=1, N=200000, pos=[4 * 200000 - 1] * 2, k=1024, H_I=4, d_I=64,
          skew=(50000, 58000)),
+    # every score 0 and 15 873 .. 16 384 candidates: the resolve's prefix form puts 32 tied
+    # candidates on a thread (its counts need 6 bits); expected 0 .. k-1
+    dict(name="all-ties-16000", B=1, Nq=1, N=16000, pos=[4 * 16000 - 1], k=1024, H_I=4,
+         d_I=64, w_zero=True, expect_first_k=True),
+    dict(name="all-ties-16384", B=1, Nq=1, N=16384, pos=[4 * 16384 - 1], k=1024, H_I=4,
+         d_I=64, w_zero=True, expect_first_k=True),
+    # zero keys (score 0) except a run of 32 keys scoring above 0 that one resolve thread
+    # holds whole: 32 candidates above the threshold on one thread
+    dict(name="planted-run-16000", B=1, Nq=1, N=16000, pos=[4 * 16000 - 1], k=1024, H_I=4,
+         d_I=64, zero_codes=True, plant=(3200, 3232)),
 ]
 
 
@@ -86,8 +96,17 @@ def test_fused_index_topk_equals_two_calls(H, gpu, case):
             for run in range(32):
                 r0 = run * (nv - 128) // 31
                 scales[b, r0:r0 + 128] = 134
+    if case.get("zero_codes"):
+        codes.zero_()
+    if "plant" in case:                 # positive e2m1 codes (magnitudes 1..7 in both nibbles)
+        lo, hi = case["plant"]
+        mag = torch.randint(1, 8, (B, hi - lo, d_I // 2, 2), generator=g, dtype=torch.uint8)
+        codes[:, lo:hi] = mag[..., 0] | (mag[..., 1] << 4)
     qdt = torch.float32 if case.get("qdt") == "f32" else torch.bfloat16
-    q = torch.randn(B, Nq, H_I, d_I, generator=g).to(qdt).to(gpu)
+    q = torch.randn(B, Nq, H_I, d_I, generator=g)
+    if "plant" in case:                 # positive queries: the planted keys score above 0
+        q = q.abs() + 0.25
+    q = q.to(qdt).to(gpu)
     w = (torch.randn(B, Nq, H_I, generator=g).abs() / math.sqrt(H_I)).to(gpu)
     if case.get("w_zero"):
         w.zero_()
@@ -122,6 +141,12 @@ def test_fused_index_topk_equals_two_calls(H, gpu, case):
     got, want = idx.view(B * Nq, k).cpu().numpy(), idx2.view(B * Nq, k).cpu().numpy()
     for r in range(B * Nq):
         assert np.array_equal(got[r], want[r]), (case["name"], r)
+    if case.get("expect_first_k"):
+        assert np.array_equal(got[0], np.arange(k)), case["name"]
+    if "plant" in case:
+        lo, hi = case["plant"]
+        want_p = np.sort(np.concatenate([np.arange(k - (hi - lo)), np.arange(lo, hi)]))
+        assert np.array_equal(got[0], want_p), case["name"]
     # the oracle's selection on the GPU's scores, for a few rows
     sc = f64(scores)
     for r in sorted({0, B * Nq - 1}):

@@ -366,6 +366,99 @@ def test_decode_query_composition_shapes():
     assert r["csa"][0].shape == (1, 64) and r["hca"][0].shape == (1, 64)
 
 
+def _sdpa(q, K, V, scale):
+    """torch's scaled-dot-product attention (float64, CPU) of every head of q [H, d] over
+    K, V [L, d], and the log-sum-exp of the scaled logits (torch.logsumexp)."""
+    qt, Kt, Vt = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)) for a in (q, K, V))
+    o = torch.nn.functional.scaled_dot_product_attention(qt[None], Kt[None], Vt[None],
+                                                         scale=scale)[0]
+    lse = torch.logsumexp(scale * (qt @ Kt.T), dim=1)
+    return o.numpy(), lse.numpy()
+
+
+def _brute_scores(qi, wi, Ic, n, dtype):
+    """Indexer scores by Python loops: sum_g w_g max(0, sum_e q[g, e] k[j, e]), rounded to
+    fp32 by numpy's cast, then to bf16 by torch's cast when asked; -0 read as +0."""
+    out = []
+    for j in range(n):
+        s = 0.0
+        for g in range(qi.shape[0]):
+            dot = 0.0
+            for e in range(qi.shape[1]):
+                dot += float(qi[g, e]) * float(Ic[j, e])
+            s += float(wi[g]) * max(0.0, dot)
+        out.append(s)
+    x = np.array(out, dtype=np.float64).astype(np.float32)
+    if dtype == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    return x.astype(np.float64) + 0.0
+
+
+def _brute_topk(scores, k):
+    """k largest by sorted() on (-score, index), ascending, padded with -1."""
+    order = sorted(range(len(scores)), key=lambda j: (-scores[j], j))[:k]
+    return sorted(order) + [-1] * (k - min(k, len(scores)))
+
+
+def _composition_case(seed, Nc=64, Nh=3, T=260, d=16, H=3, H_I=2, d_I=8):
+    """Independent random arrays for every input of decode_query (distinct per stream, so a
+    swapped or misrouted operand changes the result)."""
+    g = np.random.default_rng(seed)
+    r = lambda *s: g.standard_normal(s)
+    return dict(q=r(H, d), qi=r(H_I, d_I), wi=np.abs(r(H_I)), Kc=r(Nc, d), Vc=r(Nc, d),
+                Ic=r(Nc, d_I), K=r(T, d), V=r(T, d), Kh=r(Nh, d), Vh=r(Nh, d))
+
+
+@pytest.mark.parametrize("score_dtype", ["f32", "bf16"])
+def test_decode_query_all_selected_no_window_is_sdpa(score_dtype):
+    """Every visible entry selected (k >= n_c), no window: the CSA result is plain softmax
+    attention over the visible compressed entries, the HCA result over the visible HCA
+    entries (n_h = floor((p+1)/128): 2 of the 3 rows at p = 259), both by torch SDPA."""
+    c = _composition_case(1)
+    p, scale = 259, 0.37
+    n_c, n_h = min(64, (p + 1) // 4), min(3, (p + 1) // 128)
+    r = O.decode_query(c["q"], c["qi"], c["wi"], c["Kc"], c["Vc"], c["Ic"], c["K"], c["V"], 0,
+                       c["Kh"], c["Vh"], p, 100, 0, scale, score_dtype)
+    o, lse = _sdpa(c["q"], c["Kc"][:n_c], c["Vc"][:n_c], scale)
+    assert np.allclose(r["csa"][0], o, atol=1e-12) and np.allclose(r["csa"][1], lse, atol=1e-12)
+    o, lse = _sdpa(c["q"], c["Kh"][:n_h], c["Vh"][:n_h], scale)
+    assert np.allclose(r["hca"][0], o, atol=1e-12) and np.allclose(r["hca"][1], lse, atol=1e-12)
+    assert list(r["idx"]) == list(range(n_c)) + [-1] * (100 - n_c)
+
+
+@pytest.mark.parametrize("score_dtype,raw_pos0", [("f32", 0), ("bf16", 0), ("f32", 37)])
+def test_decode_query_selection_and_window_against_brute_force(score_dtype, raw_pos0):
+    """k < n_c and a window: scores equal the Python-loop scores, idx the sorted() selection
+    on them, and the CSA result SDPA over [selected entries] ++ [raw tokens p-w+1 .. p]
+    (raw rows held from raw_pos0 on); the HCA result is unaffected by k and the window."""
+    c = _composition_case(2)
+    p, scale, k, w = 259, 0.29, 10, 16
+    n_c, n_h = min(64, (p + 1) // 4), min(3, (p + 1) // 128)
+    K, V = c["K"][raw_pos0:], c["V"][raw_pos0:]
+    r = O.decode_query(c["q"], c["qi"], c["wi"], c["Kc"], c["Vc"], c["Ic"], K, V, raw_pos0,
+                       c["Kh"], c["Vh"], p, k, w, scale, score_dtype)
+    sc = _brute_scores(c["qi"], c["wi"], c["Ic"], n_c, score_dtype)
+    assert np.array_equal(r["scores"], sc)
+    sel = _brute_topk(list(sc), k)
+    assert list(r["idx"]) == sel
+    win = list(range(p - w + 1, p + 1))
+    keys = np.concatenate([c["Kc"][sel], c["K"][win]])
+    vals = np.concatenate([c["Vc"][sel], c["V"][win]])
+    o, lse = _sdpa(c["q"], keys, vals, scale)
+    assert np.allclose(r["csa"][0], o, atol=1e-12) and np.allclose(r["csa"][1], lse, atol=1e-12)
+    o, lse = _sdpa(c["q"], c["Kh"][:n_h], c["Vh"][:n_h], scale)
+    assert np.allclose(r["hca"][0], o, atol=1e-12) and np.allclose(r["hca"][1], lse, atol=1e-12)
+
+
+def test_decode_query_ties_select_lowest_indices():
+    """All-zero indexer weights: every score is +0 and the selection is entries 0..k-1."""
+    c = _composition_case(3)
+    r = O.decode_query(c["q"], c["qi"], 0.0 * c["wi"], c["Kc"], c["Vc"], c["Ic"], c["K"], c["V"],
+                       0, c["Kh"], c["Vh"], 259, 7, 4, 0.5, "bf16")
+    assert list(r["idx"]) == list(range(7)) and (r["scores"] == 0).all()
+    assert not np.signbit(r["scores"]).any()
+
+
 # --------------------------------------------------------------------------- backward pins
 # The gradients are pinned to central finite differences of the forward functions (which
 # the pins above tie to the pages and to closed forms), so a wrong sign, a dropped term or
