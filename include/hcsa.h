@@ -122,6 +122,18 @@ const char *hcsa_last_error(void);
 int hcsa_time_next_indexer(void *start_event, void *stop_event);
 
 /*
+ * Split count of the attention calls made later on this thread, for tuning and for checking
+ * that results do not depend on it: 0 (the default) lets each call choose; n in [1, 1024]
+ * asks the split-K kernels (bf16, 16 heads x 128; the query-by-query decode forms of
+ * hcsa_csa_sparse_attn, hcsa_hca_dense_attn and hcsa_csa_hca_attn) for n splits of each
+ * query's key list, as far as their 4096-key blocks allow; other forms are unaffected.
+ * The workspace sizes reported afterwards follow the same choice.  The split results are
+ * combined exactly (log-sum-exp merge), so outputs agree across split counts up to the
+ * rounding of fp32 sums [Lighthouse section 八 item 3: one softmax over the key list].
+ */
+int hcsa_set_attn_splits(int splits);
+
+/*
  * Block pooling (CSA m = 4, HCA m' = 128, indexer keys m = 4)
  * [Lighthouse section 八 item 3; tulong.co 技术架构创新 item 1].
  *

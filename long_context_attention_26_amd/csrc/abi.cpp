@@ -103,6 +103,12 @@ int hcsa_time_next_indexer(void* start_event, void* stop_event) {
   return ok();
 }
 
+int hcsa_set_attn_splits(int splits) {
+  if (splits < 0 || splits > 1024) return fail(HCSA_EINVAL, "splits must be in [0, 1024]");
+  hcsa::set_attn_splits(splits);
+  return ok();
+}
+
 const char* hcsa_last_error(void) { return g_err.c_str(); }
 
 static int check_compress(const void* x, int x_dtype, int64_t x_bstride, int T, int64_t x_rows,

@@ -683,6 +683,10 @@ __global__ __launch_bounds__(256) void lse_merge2_kernel(MergeJob a, MergeJob b,
 }  // namespace
 
 
+// Split count asked for by hcsa_set_attn_splits (0: the plan's own choice), this thread.
+static thread_local int t_attn_splits = 0;
+void set_attn_splits(int splits) { t_attn_splits = splits; }
+
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len) {
   AttnPlan p{};
   p.rows = B * Nq;
@@ -712,6 +716,11 @@ AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int
     p.chunk = static_cast<int>(c);
   } else {
     p.chunk = kGenChunk;
+  }
+  if (t_attn_splits > 0 && p.mfma) {
+    // the split kernels take any key range per block up to their LDS key list
+    const int L = std::max(max_len, 1);
+    p.chunk = std::min((L + t_attn_splits - 1) / t_attn_splits, kMfmaMaxChunk);
   }
   p.splits = std::max(1, (max_len + p.chunk - 1) / p.chunk);
   if (p.splits > 1) {

@@ -24,6 +24,7 @@ _SIGS = {
     "hcsa_version": (_i, []),
     "hcsa_last_error": (ctypes.c_char_p, []),
     "hcsa_time_next_indexer": (_i, [_p, _p]),
+    "hcsa_set_attn_splits": (_i, [_i]),
     "hcsa_compress_kv": (_i, [_p, _i, _i64, _i, _i, _i, _p, _i, _p, _i, _i64, _p, _i64, _p]),
     "hcsa_compress_kv_batched": (_i, [_p, _i, _i, _p, _p]),
     "hcsa_mxfp4_quantize": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
@@ -141,6 +142,11 @@ def time_next_indexer(start_event, stop_event):
         if e.cuda_event == 0:
             e.record()          # creates the underlying event
     _check(lib.hcsa_time_next_indexer(start_event.cuda_event, stop_event.cuda_event))
+
+
+def set_attn_splits(splits):
+    """Split count of this thread's later attention calls (0: each call chooses)."""
+    _check(lib.hcsa_set_attn_splits(int(splits)))
 
 
 def alloc_workspace(nbytes, device):

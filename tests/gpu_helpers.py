@@ -54,9 +54,10 @@ def assert_attention_close(out, lse, ref_o, ref_l, fp32, what):
     assert (le <= 1e-3).all(), f"{what}: lse error {le.max()}"
 
 
-def topk_set_ok(gpu_idx, ref_idx, ref_scores, k, what, rel=1e-5):
+def topk_set_ok(gpu_idx, ref_idx, ref_scores, k, what, rel=1e-5, tol_abs=None):
     """End-to-end index check when scores differ by rounding: the two selections may
-    differ only among entries whose exact scores lie within `rel` of the k-th score."""
+    differ only among entries whose exact scores lie within `rel` of the k-th score (or,
+    with tol_abs, an array of per-entry absolute tolerances, within tol_abs[j] of it)."""
     g = set(int(j) for j in gpu_idx if j >= 0)
     r = set(int(j) for j in ref_idx if j >= 0)
     assert list(gpu_idx) == sorted(gpu_idx[gpu_idx >= 0]) + [-1] * int((gpu_idx < 0).sum()), \
@@ -66,6 +67,7 @@ def topk_set_ok(gpu_idx, ref_idx, ref_scores, k, what, rel=1e-5):
         return 0
     kth = np.sort(ref_scores)[::-1][min(k, len(ref_scores)) - 1]
     for j in g ^ r:
-        assert abs(ref_scores[j] - kth) <= rel * max(abs(kth), 1e-30) + 1e-30, \
+        tol = rel * max(abs(kth), 1e-30) + 1e-30 if tol_abs is None else tol_abs[j]
+        assert abs(ref_scores[j] - kth) <= tol, \
             f"{what}: entry {j} differs away from the threshold ({ref_scores[j]} vs {kth})"
     return len(g ^ r) // 2

@@ -484,17 +484,74 @@ def test_hca_dense_attention(H, gpu, case):
     assert_attention_close(go, gl, ro, rl, dt == "f32", f"hca {case}")
 
 
-def test_attention_deterministic_and_split_invariant(H, gpu):
-    B, Nq, Hh, d, N = 1, 1, 16, 128, 8192
-    q, Kh, Vh, _, _ = _attn_inputs(B, Nq, Hh, d, N, 1, "bf16")
-    args = [dev(q, torch.bfloat16, gpu), dev(Kh, torch.bfloat16, gpu), dev(Vh, torch.bfloat16, gpu)]
-    res = []
-    for _ in range(2):
-        out = torch.empty(B, Nq, Hh, d, device=gpu)
-        lse = torch.empty(B, Nq, Hh, device=gpu)
-        H.hca_dense_attn(*args, N, 128, 128 * N - 1, 1 / math.sqrt(d), out, lse)
-        res.append((out.cpu(), lse.cpu()))
-    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+@pytest.mark.parametrize("kind", ["csa", "hca", "csa+hca"])
+def test_attention_deterministic_and_split_invariant(H, gpu, kind):
+    """Split counts 1, 2, 7 and 64 of each query's key list (hcsa_set_attn_splits; 64
+    takes the merge's LDS-weight form, 7 and 2 its register form, 1 no merge): every count
+    agrees with the others and with the oracle, and repeating a call gives the same bits."""
+    print(f"split invariance {kind}", flush=True)
+    B, Nq, Hh, d, N, Nh, k, w, ratio = 2, 1, 16, 128, 3000, 90, 1024, 128, 4
+    pos0 = 128 * Nh - 1
+    scale = 1 / math.sqrt(d)
+    q, Kc, Vc, Kr, Vr = _attn_inputs(B, Nq, Hh, d, N, pos0 + 1, "bf16")
+    _, Kh, Vh, _, _ = _attn_inputs(B, Nq, Hh, d, Nh, 1, "bf16")
+    idx = np.stack([O.select_topk(rng.standard_normal(N), O.visible_entries(pos0, N, ratio), k)
+                    for _ in range(B)])[:, None, :]
+    t = lambda a: dev(a, torch.bfloat16, gpu)
+    args_c = dict(q=t(q), kc=t(Kc), vc=t(Vc), idx=torch.from_numpy(idx.astype(np.int32)).to(gpu),
+                  kr=t(Kr), vr=t(Vr))
+    kh, vh = t(Kh), t(Vh)
+    ref = {}
+    for b in range(B):
+        ref[("c", b)] = O.csa_attention(q[b, 0], Kc[b], Vc[b], idx[b, 0], Kr[b], Vr[b], 0, pos0,
+                                        w, scale, ratio)
+        ref[("h", b)] = O.hca_attention(q[b, 0], Kh[b], Vh[b], pos0, scale, 128)
+
+    def run(splits):
+        H.set_attn_splits(splits)
+        try:
+            oc, lc = torch.empty(B, Nq, Hh, d, device=gpu), torch.empty(B, Nq, Hh, device=gpu)
+            oh, lh = torch.empty_like(oc), torch.empty_like(lc)
+            if kind == "csa":
+                H.csa_sparse_attn(args_c["q"], args_c["kc"], args_c["vc"], N, args_c["idx"],
+                                  args_c["kr"], args_c["vr"], 0, w, ratio, pos0, scale, oc, lc)
+            elif kind == "hca":
+                H.hca_dense_attn(args_c["q"], kh, vh, Nh, 128, pos0, scale, oh, lh)
+            else:
+                H.csa_hca_attn(args_c["q"], args_c["kc"], args_c["vc"], N, args_c["idx"],
+                               args_c["kr"], args_c["vr"], 0, w, ratio, kh, vh, Nh, 128, pos0,
+                               scale, oc, lc, oh, lh)
+            _sync()
+        finally:
+            H.set_attn_splits(0)
+        return [x.cpu() for x in (oc, lc, oh, lh)]
+
+    results = {}
+    for splits in (1, 2, 7, 64):
+        a, b2 = run(splits), run(splits)
+        for x, y in zip(a, b2):
+            assert torch.equal(x, y), f"{kind}: splits {splits} not deterministic"
+        results[splits] = a
+        for b in range(B):
+            if kind != "hca":
+                assert_attention_close(f64(a[0][b]), f64(a[1][b]), ref[("c", b)][0][None],
+                                       ref[("c", b)][1][None], False, f"csa splits {splits}")
+            if kind != "csa":
+                assert_attention_close(f64(a[2][b]), f64(a[3][b]), ref[("h", b)][0][None],
+                                       ref[("h", b)][1][None], False, f"hca splits {splits}")
+    # the split counts differ only in the order of fp32 sums: well inside the bf16 bound
+    base = results[1]
+    for splits in (2, 7, 64):
+        for which, (x, y) in enumerate(zip(base, results[splits])):
+            if (kind == "csa" and which >= 2) or (kind == "hca" and which < 2):
+                continue
+            xf, yf = x.double(), y.double()
+            fin = torch.isfinite(xf)
+            assert torch.equal(fin, torch.isfinite(yf))
+            assert (xf[fin] - yf[fin]).abs().max().item() <= 1e-5 * max(1.0, xf[fin].abs().max().item()), \
+                f"{kind}: splits 1 vs {splits}, output {which}"
+    with pytest.raises(H.HcsaError):
+        H.set_attn_splits(-1)
 
 
 def test_compress_batched_equals_single_calls(H, gpu):

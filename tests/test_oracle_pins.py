@@ -366,7 +366,7 @@ def test_decode_query_composition_shapes():
     assert r["csa"][0].shape == (1, 64) and r["hca"][0].shape == (1, 64)
 
 
-def _sdpa(q, K, V, scale):
+def _sdpa_lse(q, K, V, scale):
     """torch's scaled-dot-product attention (float64, CPU) of every head of q [H, d] over
     K, V [L, d], and the log-sum-exp of the scaled logits (torch.logsumexp)."""
     qt, Kt, Vt = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)) for a in (q, K, V))
@@ -376,7 +376,7 @@ def _sdpa(q, K, V, scale):
     return o.numpy(), lse.numpy()
 
 
-def _brute_scores(qi, wi, Ic, n, dtype):
+def _loop_scores(qi, wi, Ic, n, dtype):
     """Indexer scores by Python loops: sum_g w_g max(0, sum_e q[g, e] k[j, e]), rounded to
     fp32 by numpy's cast, then to bf16 by torch's cast when asked; -0 read as +0."""
     out = []
@@ -394,7 +394,7 @@ def _brute_scores(qi, wi, Ic, n, dtype):
     return x.astype(np.float64) + 0.0
 
 
-def _brute_topk(scores, k):
+def _sorted_topk(scores, k):
     """k largest by sorted() on (-score, index), ascending, padded with -1."""
     order = sorted(range(len(scores)), key=lambda j: (-scores[j], j))[:k]
     return sorted(order) + [-1] * (k - min(k, len(scores)))
@@ -410,7 +410,7 @@ def _composition_case(seed, Nc=64, Nh=3, T=260, d=16, H=3, H_I=2, d_I=8):
 
 
 @pytest.mark.parametrize("score_dtype", ["f32", "bf16"])
-def test_decode_query_all_selected_no_window_is_sdpa(score_dtype):
+def test_decode_query_all_selected_no_window_is_sdpa_lse(score_dtype):
     """Every visible entry selected (k >= n_c), no window: the CSA result is plain softmax
     attention over the visible compressed entries, the HCA result over the visible HCA
     entries (n_h = floor((p+1)/128): 2 of the 3 rows at p = 259), both by torch SDPA."""
@@ -419,9 +419,9 @@ def test_decode_query_all_selected_no_window_is_sdpa(score_dtype):
     n_c, n_h = min(64, (p + 1) // 4), min(3, (p + 1) // 128)
     r = O.decode_query(c["q"], c["qi"], c["wi"], c["Kc"], c["Vc"], c["Ic"], c["K"], c["V"], 0,
                        c["Kh"], c["Vh"], p, 100, 0, scale, score_dtype)
-    o, lse = _sdpa(c["q"], c["Kc"][:n_c], c["Vc"][:n_c], scale)
+    o, lse = _sdpa_lse(c["q"], c["Kc"][:n_c], c["Vc"][:n_c], scale)
     assert np.allclose(r["csa"][0], o, atol=1e-12) and np.allclose(r["csa"][1], lse, atol=1e-12)
-    o, lse = _sdpa(c["q"], c["Kh"][:n_h], c["Vh"][:n_h], scale)
+    o, lse = _sdpa_lse(c["q"], c["Kh"][:n_h], c["Vh"][:n_h], scale)
     assert np.allclose(r["hca"][0], o, atol=1e-12) and np.allclose(r["hca"][1], lse, atol=1e-12)
     assert list(r["idx"]) == list(range(n_c)) + [-1] * (100 - n_c)
 
@@ -437,16 +437,16 @@ def test_decode_query_selection_and_window_against_brute_force(score_dtype, raw_
     K, V = c["K"][raw_pos0:], c["V"][raw_pos0:]
     r = O.decode_query(c["q"], c["qi"], c["wi"], c["Kc"], c["Vc"], c["Ic"], K, V, raw_pos0,
                        c["Kh"], c["Vh"], p, k, w, scale, score_dtype)
-    sc = _brute_scores(c["qi"], c["wi"], c["Ic"], n_c, score_dtype)
+    sc = _loop_scores(c["qi"], c["wi"], c["Ic"], n_c, score_dtype)
     assert np.array_equal(r["scores"], sc)
-    sel = _brute_topk(list(sc), k)
+    sel = _sorted_topk(list(sc), k)
     assert list(r["idx"]) == sel
     win = list(range(p - w + 1, p + 1))
     keys = np.concatenate([c["Kc"][sel], c["K"][win]])
     vals = np.concatenate([c["Vc"][sel], c["V"][win]])
-    o, lse = _sdpa(c["q"], keys, vals, scale)
+    o, lse = _sdpa_lse(c["q"], keys, vals, scale)
     assert np.allclose(r["csa"][0], o, atol=1e-12) and np.allclose(r["csa"][1], lse, atol=1e-12)
-    o, lse = _sdpa(c["q"], c["Kh"][:n_h], c["Vh"][:n_h], scale)
+    o, lse = _sdpa_lse(c["q"], c["Kh"][:n_h], c["Vh"][:n_h], scale)
     assert np.allclose(r["hca"][0], o, atol=1e-12) and np.allclose(r["hca"][1], lse, atol=1e-12)
 
 
