@@ -102,13 +102,34 @@ def measured_traffic(cfg, mx_fp8=False):
     return int(round(rec["traffic_bytes"]))
 
 
-def cpu_baseline(cfg, st, om, q, qi, wi, seconds):
+def _host_cpus():
+    """CPUs this process may run on, and the host's CPU model name."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(cfg, st, om, q, qi, wi, seconds, gpu_idx=None):
     """The CPU oracle on sequence 0: its own pooled caches are built untimed from the raw
     tokens, then whole decode queries (pooling of the completed blocks, indexer, top-k,
-    CSA and HCA attention) are timed until `seconds` of work."""
+    CSA and HCA attention) are timed until `seconds` of work, with the BLAS thread pool as
+    configured and then with one thread.  With the GPU's selection of sequence 0 it also
+    reports the recall of that selection against the exact fp32 top-k of the unquantized
+    (bf16-stored) indexer queries and keys."""
     import numpy as np
     import oracle as O
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     f = lambda t: t.float().cpu().double().numpy()
     K, V, I = f(st.K_raw[0]), f(st.V_raw[0]), f(st.I_raw[0])
@@ -120,8 +141,8 @@ def cpu_baseline(cfg, st, om, q, qi, wi, seconds):
     Vc = O.round_to(O.compress(V[: p + 1], omd["csa_v"], 4), cfg.kv)
     Kh = O.round_to(O.compress(K[: p + 1], omd["hca_k"], 128), cfg.kv)
     Vh = O.round_to(O.compress(V[: p + 1], omd["hca_v"], 128), cfg.kv)
-    Ic = O.compress(I[: p + 1], omd["idx_k"], 4)
-    Ic = O.mxfp4_roundtrip(O.round_fp32(Ic)) if cfg.idx == "mxfp4" else O.round_to(Ic, cfg.idx)
+    Ic_exact = O.compress(I[: p + 1], omd["idx_k"], 4)
+    Ic = O.mxfp4_roundtrip(Ic_exact) if cfg.idx == "mxfp4" else O.round_to(Ic_exact, cfg.idx)
     qv, qiv, wiv = f(q[0, 0]), f(qi[0, 0]), f(wi[0, 0])
 
     def query():
@@ -130,7 +151,7 @@ def cpu_baseline(cfg, st, om, q, qi, wi, seconds):
         ic = O.compress(I[p - 3: p + 1], omd["idx_k"], 4)
         qq = qiv
         if cfg.idx == "mxfp4":
-            Ic[-1] = O.mxfp4_roundtrip(O.round_fp32(ic))[0]
+            Ic[-1] = O.mxfp4_roundtrip(ic)[0]
             qq = O.mxfp4_roundtrip(qiv)
         else:
             Ic[-1] = O.round_to(ic, cfg.idx)[0]
@@ -139,18 +160,68 @@ def cpu_baseline(cfg, st, om, q, qi, wi, seconds):
         return O.decode_query(qv, qq, wiv, Kc, Vc, Ic, K, V, 0, Kh, Vh, p, cfg.topk, cfg.n_win,
                               cfg.scale, cfg.score)
 
-    query()  # warm-up
-    n, t0 = 0, time.perf_counter()
-    while True:
-        query()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    def rate(secs):
+        query()  # warm-up
+        n, t0 = 0, time.perf_counter()
+        while True:
+            query()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= secs:
+                return n / el, n, el
+
+    value, n, el = rate(seconds)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": n / el, "unit": "decode queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode queries of sequence 0 (p={p}, full context) through the "
-                      f"float64 numpy oracle, {el:.1f} s; caches pooled untimed"}
+    with threadpool_limits(limits=1):
+        one, n1, el1 = rate(seconds / 2)
+    host, model = _host_cpus()
+    out = {"value": value, "unit": "decode queries/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} decode queries of sequence 0 (p={p}, full context) through the "
+                     f"float64 numpy oracle, {el:.1f} s ({threads} BLAS threads); caches "
+                     f"pooled untimed",
+           "single_core_value": one, "single_core_sample": f"{n1} queries, {el1:.1f} s",
+           "host_cpus": host, "cpu_model": model}
+    if gpu_idx is not None:
+        nv = O.visible_entries(p, Kc.shape[0], 4)
+        ref = O.select_topk(O.index_scores(O.round_bf16(qiv), wiv, O.round_bf16(Ic_exact), nv,
+                                           "f32"), nv, cfg.topk)
+        g = set(int(j) for j in gpu_idx if j >= 0)
+        r = set(int(j) for j in ref if j >= 0)
+        out["recall"] = {"value": len(g & r) / max(1, len(r)), "sequence": 0,
+                         "reference": "exact fp32 top-k of the bf16-stored indexer query and "
+                                      "keys (no MXFP4 rounding)",
+                         "context": "the pages quote 99.7 % on real model data"}
+    return out
+
+
+def selector_ratio(cfg, stp, q_idx, w_idx, dev, reps=20):
+    """Top-k selector on the same indexer scores stored as fp32 and as bf16 (the pages'
+    FP32 -> BF16 index-score change for the selector): the selector call's average time
+    for each and their ratio."""
+    import torch
+    from long_context_attention_26_amd import hcsa
+    st = stp.st
+    rows, N = cfg.B * cfg.Nq, st.Nc
+    res = {}
+    for name, code, dt in (("fp32", hcsa.F32, torch.float32), ("bf16", hcsa.BF16, torch.bfloat16)):
+        sc = torch.empty(rows, N, dtype=dt, device=dev)
+        hcsa.csa_index_scores(q_idx, w_idx, st.Ic, N, 4, cfg.pos0, sc, k_scales=st.Ics)
+        idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
+        ws = hcsa.alloc_workspace(hcsa.topk_workspace_size(code, cfg.B, cfg.Nq, N, cfg.topk), dev)
+        for _ in range(3):
+            hcsa.topk(sc, cfg.B, cfg.Nq, N, 4, cfg.pos0, cfg.topk, idx, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            hcsa.topk(sc, cfg.B, cfg.Nq, N, 4, cfg.pos0, cfg.topk, idx, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        del sc
+    res["speedup_bf16_over_fp32"] = round(res["fp32_us"] / res["bf16_us"], 3)
+    res["note"] = (f"{rows} row(s) of {N} scores, k {cfg.topk}; back-to-back calls (scores "
+                   "partly cache-resident); context: the pages quote 2x")
+    return res
 
 
 def copy_calibration():
@@ -355,37 +426,28 @@ def main():
             stp.mx_fp8 = True
     torch.cuda.synchronize()
 
-    # Each copy's step is captured as one HIP graph, and its attention once more as a graph of
-    # its own.  Every SAMPLE-th timed step runs the pooling + indexer + top-k call directly
-    # (its key scan records dispatch-level events) and then the attention graph, with timing
-    # events between them on the launch stream: they give the per-stage split and the key
-    # scan's duration for the roofline.  The SAMPLE - 1 steps between two sampled ones replay one graph that chains
-    # them (each on its own cache copy, every kernel of every step executed), as a model's
-    # per-token graph chains its layers: the host's graph-launch latency, several
-    # microseconds per launch, then falls on one step in SAMPLE instead of every step.
+    # Each copy's step (one decode-step call) is captured as one HIP graph.  Every SAMPLE-th
+    # timed step runs the call directly, its key scan recording dispatch-level events (the
+    # kernel's own duration, for the roofline), with events around the whole call.  The
+    # SAMPLE - 1 steps between two sampled ones replay one graph that chains them (each on
+    # its own cache copy, every kernel of every step executed), as a model's per-token graph
+    # chains its layers: the host's graph-launch latency, several microseconds per launch,
+    # then falls on one step in SAMPLE instead of every step.  Timed step i runs on copy
+    # (warmup + i) mod R, so the first timed step does not read the copy the last warm-up
+    # step has just streamed (part of it would still sit in the Infinity Cache).
     SAMPLE = 16
-    stages = ["pool_index_topk", "attend"]
-    full, split = [], []
+    full = []
     cap_stream = torch.cuda.Stream()
     for stp in steps:
         for _ in range(2):                      # run once eagerly before capture
-            stp.run(q, qi, wi, cfg.pos0)
+            stp.run_step(q, qi, wi, cfg.pos0)
         torch.cuda.synchronize()
         g_all = torch.cuda.CUDAGraph()
-        g_idx, g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.stream(cap_stream):
             g_all.capture_begin()
-            stp.run_pool_index_topk(qi, wi, cfg.pos0)
-            stp.run_attend(q, cfg.pos0)
+            stp.run_step(q, qi, wi, cfg.pos0)
             g_all.capture_end()
-            g_idx.capture_begin()
-            stp.run_pool_index_topk(qi, wi, cfg.pos0)
-            g_idx.capture_end()
-            g_rest.capture_begin()
-            stp.run_attend(q, cfg.pos0)
-            g_rest.capture_end()
         full.append(g_all)
-        split.append((g_idx, g_rest))
     torch.cuda.synchronize()
     chain = []                                  # chain[c]: SAMPLE - 1 steps from copy c on
     for c in range(R):
@@ -393,57 +455,49 @@ def main():
         with torch.cuda.stream(cap_stream):
             g.capture_begin()
             for j in range(SAMPLE - 1):
-                stp = steps[(c + j) % R]
-                stp.run_pool_index_topk(qi, wi, cfg.pos0)
-                stp.run_attend(q, cfg.pos0)
+                steps[(c + j) % R].run_step(q, qi, wi, cfg.pos0)
             g.capture_end()
         chain.append(g)
     torch.cuda.synchronize()
 
-    ev = []
+    ev, kev = [], []
+    base = args.warmup
 
-    kev = []
-
-    def one_step(i, timed):
-        if timed and i % SAMPLE == 0:
-            # sampled step: the pooling + indexer + top-k call launched directly (its key scan
-            # kernel records dispatch-level events: its own execution time), then the
-            # attention graph
-            g = split[i % R]
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    def one_step(c, sampled):
+        if sampled:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e[0].record()
             hcsa.time_next_indexer(k0, k1)
-            steps[i % R].run_pool_index_topk(qi, wi, cfg.pos0)
+            steps[c].run_step(q, qi, wi, cfg.pos0)
             e[1].record()
-            g[1].replay()
-            e[2].record()
             ev.append(e)
             kev.append((k0, k1))
         else:
-            full[i % R].replay()
+            full[c].replay()
 
     for i in range(args.warmup):
-        one_step(i, False)
+        one_step(i % R, False)
     torch.cuda.synchronize()
+    assert args.steps == 0 or (base % R) != ((args.warmup - 1) % R) or R == 1
     t0 = time.perf_counter()
     i = 0
     while i < args.steps:
         if i % SAMPLE == 1 and i + SAMPLE - 1 <= args.steps:
-            chain[i % R].replay()                # steps i .. i + SAMPLE - 2
+            chain[(base + i) % R].replay()       # steps i .. i + SAMPLE - 2
             i += SAMPLE - 1
         else:
-            one_step(i, True)
+            one_step((base + i) % R, i % SAMPLE == 0)
             i += 1
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el / args.steps * 1e3
     qps = cfg.B * cfg.Nq / (el / args.steps)
 
-    # per-stage durations from the events recorded on the launch stream
-    br = {s: sum(e[j].elapsed_time(e[j + 1]) for e in ev) * 1e3 / len(ev)
-          for j, s in enumerate(stages)}
+    # durations from the events recorded on the launch stream
     idx_us = sum(a.elapsed_time(b) for a, b in kev) * 1e3 / len(kev)
+    br = {"step_call": sum(e[0].elapsed_time(e[1]) for e in ev) * 1e3 / len(ev),
+          "key_scan": idx_us}
     flops = step_flops(cfg)
     if cfg.Nq == 1:
         # decode: the indexer streams every compressed key once per query
@@ -490,13 +544,17 @@ def main():
         "step_bytes": total_bytes,
         "step_tflops": round(sum(flops.values()) / (el / args.steps) / 1e12, 2),
         "breakdown_us": {k: round(v, 2) for k, v in br.items()},
-        "breakdown_note": f"sampled every {SAMPLE}th step ({len(ev)} samples): pooling + "
-                          "indexer + top-k launches | attention graph; the steps between "
-                          f"samples replay one graph of {SAMPLE - 1} chained steps",
+        "breakdown_note": f"sampled every {SAMPLE}th step ({len(ev)} samples): the decode-step "
+                          "call launched directly (host launch included) and its key scan "
+                          "kernel alone; the steps between samples replay one graph of "
+                          f"{SAMPLE - 1} chained steps",
         "roofline": roof,
     }
+    if cfg.Nq == 1 and cfg.score == "bf16":
+        out["selector_fp32_vs_bf16"] = selector_ratio(cfg, steps[0], qi, wi, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, st, om, q, qi, wi, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, st, om, q, qi, wi, args.cpu_seconds,
+                                           gpu_idx=step0.idx[0, 0].cpu().numpy())
     print(json.dumps(out), flush=True)
 
 

@@ -334,6 +334,40 @@ int hcsa_csa_hca_attn(const void *q, const void *kc, const void *vc, int64_t c_b
                       void *workspace, size_t ws_bytes, hcsa_stream stream);
 
 /*
+ * One decode step of a CSA layer and an HCA layer [Lighthouse section 八 items 3 and 7: the
+ * tokens of a step complete the blocks its indexer scans; CSA and HCA layers over the same
+ * tokens]: hcsa_csa_pool_index_topk(jobs, ..., scores_out = NULL) followed by
+ * hcsa_csa_hca_attn(...) with the same arguments, as one call with the same results bit for
+ * bit.  The indexer shares N and ratio with CSA (one indexer key per CSA entry).
+ *
+ * For one query token per sequence with MXFP4 keys (fp4 operands), bf16 queries and scores,
+ * the selection without a score array, bf16 16 x 128 attention and contiguous caches, the
+ * step runs in four launches: the per-row selection floors and the pooling beside the first
+ * HCA splits (entries completed before the step); the key scan; per-row resolves beside the
+ * remaining HCA splits and the CSA splits, which wait for their row's selection; the split
+ * merge.  Other shapes run the two calls' kernels in turn.
+ *
+ * workspace: hcsa_decode_step_workspace_size(B, Nq, N, k, score_dtype, H, d, n_win, N_h)
+ * bytes, 256-byte aligned; its contents need not be initialized.  Its first 32-bit word
+ * counts the back launch's waits for a selection that timed out (about a second each; zero
+ * unless the device misbehaves; outputs of a step with a nonzero count are undefined); it
+ * is reset by every call.
+ */
+size_t hcsa_decode_step_workspace_size(int B, int Nq, int N, int k, int score_dtype, int H,
+                                       int d, int n_win, int N_h);
+int hcsa_decode_step(const hcsa_pool_job *jobs, int n_jobs, const void *q_idx, int q_dtype,
+                     const float *w_idx, const void *k_idx, int k_dtype, int64_t k_bstride,
+                     const uint8_t *k_scales, int64_t ks_bstride, int H_I, int d_I,
+                     int score_dtype, int32_t *topk_idx, const void *q, const void *kc,
+                     const void *vc, int64_t c_bstride, int N, int k, const void *k_raw,
+                     const void *v_raw, int64_t raw_bstride, int64_t T_raw, int64_t raw_pos0,
+                     int n_win, int ratio, const void *kh, const void *vh, int64_t h_bstride,
+                     int N_h, int ratio_h, int64_t pos0, const int64_t *seq_pos,
+                     const hcsa_pages *pages, int kv_dtype, int B, int Nq, int H, int d,
+                     float scale, float *out_c, float *lse_c, float *out_h, float *lse_h,
+                     void *workspace, size_t ws_bytes, hcsa_stream stream);
+
+/*
  * Backward (training) [Lighthouse section 八 item 2: the sparse attention is trained from
  * the 64K stage of the length curriculum; item 3 for the attention itself].  Gradients of
  * the loss sum(dout * out) + sum(dlse * lse) of the forward call with the same arguments;

@@ -2,6 +2,7 @@
 // caller's stream.  No call allocates device memory or synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
@@ -604,6 +605,99 @@ int hcsa_csa_hca_attn(const void* q, const void* kc, const void* vc, int64_t c_b
   h.out = out_h; h.lse = lse_h;
   return hip_status(hcsa::launch_csa_hca(c, pc, h, ph, workspace, static_cast<hipStream_t>(stream)),
                     "hcsa_csa_hca_attn");
+}
+
+// ------------------------------------------------------------------ one decode step
+
+size_t hcsa_decode_step_workspace_size(int B, int Nq, int N, int k, int score_dtype, int H,
+                                       int d, int n_win, int N_h) {
+  if (B < 1 || Nq < 1 || N < 1 || k < 1 || H < 1 || d < 1) return 0;
+  // attention partials: those of the two calls, or of the four-launch form's finer HCA
+  // splits, whichever is larger
+  const size_t pc = hcsa::align256(hcsa_csa_sparse_attn_workspace_size(B, Nq, H, d, k, n_win));
+  const size_t attn = std::max(hcsa_csa_hca_attn_workspace_size(B, Nq, H, d, k, n_win, N_h),
+                               pc + hcsa::plan_step_hca(B, Nq, H, d, N_h).total_bytes);
+  return hcsa::decode_step_sync_bytes(B * Nq) +
+         hcsa::align256(hcsa_csa_index_topk_workspace_size(B, Nq, N, k, score_dtype)) + attn;
+}
+
+int hcsa_decode_step(const hcsa_pool_job* jobs, int n_jobs, const void* q_idx, int q_dtype,
+                     const float* w_idx, const void* k_idx, int k_dtype, int64_t k_bstride,
+                     const uint8_t* k_scales, int64_t ks_bstride, int H_I, int d_I,
+                     int score_dtype, int32_t* topk_idx, const void* q, const void* kc,
+                     const void* vc, int64_t c_bstride, int N, int k, const void* k_raw,
+                     const void* v_raw, int64_t raw_bstride, int64_t T_raw, int64_t raw_pos0,
+                     int n_win, int ratio, const void* kh, const void* vh, int64_t h_bstride,
+                     int N_h, int ratio_h, int64_t pos0, const int64_t* seq_pos,
+                     const hcsa_pages* pages, int kv_dtype, int B, int Nq, int H, int d,
+                     float scale, float* out_c, float* lse_c, float* out_h, float* lse_h,
+                     void* workspace, size_t ws_bytes, hcsa_stream stream) {
+  int rc = n_jobs > 0 ? check_pool_jobs(jobs, n_jobs, B, pages) : HCSA_OK;
+  if (rc) return rc;
+  rc = check_topk_args(score_dtype, B, Nq, N, ratio, pos0, k);
+  if (rc) return rc;
+  rc = check_seq_pos(seq_pos);
+  if (rc) return rc;
+  rc = check_pages(pages, {ratio});
+  if (rc) return rc;
+  rc = check_index_args(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
+                        B, Nq, H_I, d_I, N, is_paged(pages));
+  if (rc) return rc;
+  if (!topk_idx) return fail(HCSA_EINVAL, "topk_idx must be non-null");
+  if (!aligned16(topk_idx)) return fail(HCSA_EALIGN, "topk_idx must be 16-byte aligned");
+  rc = check_csa(q, kc, vc, c_bstride, N, topk_idx, k, k_raw, v_raw, raw_bstride, T_raw,
+                 raw_pos0, n_win, ratio, pos0, seq_pos, pages, kv_dtype, B, Nq, H, d, scale,
+                 out_c, lse_c);
+  if (rc) return rc;
+  rc = check_hca(q, kh, vh, h_bstride, N_h, ratio_h, pos0, seq_pos, pages, kv_dtype, B, Nq, H,
+                 d, scale, out_h, lse_h);
+  if (rc) return rc;
+  const size_t sync = hcsa::decode_step_sync_bytes(B * Nq);
+  const size_t mx_bytes = hcsa::align256(hcsa_csa_index_topk_workspace_size(B, Nq, N, k, score_dtype));
+  const hcsa::AttnPlan pc =
+      hcsa::plan_attention(true, kv_dtype, B, Nq, H, d, attn_max_len_csa(k, n_win));
+  const hcsa::AttnPlan ph = hcsa::plan_attention(false, kv_dtype, B, Nq, H, d, N_h);
+  const hcsa::AttnPlan ph_step = hcsa::plan_step_hca(B, Nq, H, d, N_h);
+  const size_t attn_bytes = hcsa::align256(pc.total_bytes) +
+                            std::max(ph.total_bytes, ph_step.total_bytes);
+  rc = check_ws(workspace, ws_bytes, sync + mx_bytes + attn_bytes);
+  if (rc) return rc;
+  hcsa::DecodeStepArgs a{};
+  a.jobs = jobs; a.n_jobs = n_jobs; a.q_idx = q_idx; a.q_dtype = q_dtype; a.w_idx = w_idx;
+  a.k_idx = static_cast<const uint8_t*>(k_idx); a.k_dtype = k_dtype; a.k_bstride = k_bstride;
+  a.k_scales = k_scales; a.ks_bstride = ks_bstride; a.H_I = H_I; a.d_I = d_I; a.N = N;
+  a.score_dtype = score_dtype; a.idx = topk_idx; a.block_table = page_table(pages);
+  a.raw_ring = raw_ring(pages); a.seq_pos = seq_pos; a.B = B; a.Nq = Nq;
+  hcsa::AttnArgs& c = a.c;
+  c.q = q; c.kc = kc; c.vc = vc; c.c_bstride = c_bstride; c.N = N; c.ratio = ratio;
+  c.idx = topk_idx; c.k = k; c.k_raw = k_raw; c.v_raw = v_raw; c.raw_bstride = raw_bstride;
+  c.T_raw = T_raw; c.raw_pos0 = raw_pos0; c.n_win = n_win; c.pos0 = pos0; c.seq_pos = seq_pos;
+  c.block_table = page_table(pages); c.table_stride = page_stride(pages);
+  c.raw_ring = raw_ring(pages);
+  c.kv_dtype = kv_dtype; c.B = B; c.Nq = Nq; c.H = H; c.d = d; c.scale = scale;
+  c.out = out_c; c.lse = lse_c;
+  hcsa::AttnArgs& h = a.h;
+  h.q = q; h.kc = kh; h.vc = vh; h.c_bstride = h_bstride; h.N = N_h; h.ratio = ratio_h;
+  h.pos0 = pos0; h.seq_pos = seq_pos;
+  h.block_table = page_table(pages); h.table_stride = page_stride(pages);
+  h.kv_dtype = kv_dtype; h.B = B; h.Nq = Nq; h.H = H; h.d = d; h.scale = scale;
+  h.out = out_h; h.lse = lse_h;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = index_topk_fused(k_dtype, score_dtype, B, Nq, N, k, nullptr);
+  if (hcsa::decode_step_fast(a, pc, ph, fused))
+    return hip_status(hcsa::launch_decode_step(a, pc, ph_step, workspace, sync, sync + mx_bytes,
+                                               s),
+                      "hcsa_decode_step");
+  // other shapes: the two calls in turn, on the same parts of the workspace
+  hipError_t e0 = hcsa::launch_decode_step_reset(workspace, B * Nq, s);
+  if (e0 != hipSuccess) return hip_status(e0, "hcsa_decode_step");
+  rc = index_topk_impl(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
+                       B, Nq, H_I, d_I, N, ratio, pos0, seq_pos, pages, k, score_dtype,
+                       topk_idx, nullptr, static_cast<char*>(workspace) + sync, mx_bytes,
+                       stream, n_jobs > 0 ? jobs : nullptr, n_jobs);
+  if (rc) return rc;
+  return hip_status(hcsa::launch_csa_hca(c, pc, h, ph, static_cast<char*>(workspace) + sync + mx_bytes, s),
+                    "hcsa_decode_step (attention)");
 }
 
 // ------------------------------------------------------------------ backward (training)

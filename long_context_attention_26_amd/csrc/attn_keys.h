@@ -62,12 +62,17 @@ __device__ __forceinline__ RowKeys row_keys(const AttnDev& A, int row) {
 }
 
 // Source of key-list position `pos`: >= 0 compressed row, -1 none, <= -2 raw row -(code+2).
-template <bool CSA>
+// COH: the selection is read with agent-coherent loads (written by another block of the same
+// launch).
+template <bool CSA, bool COH = false>
 __device__ __forceinline__ int key_code(const AttnDev& A, const RowKeys& r, int row, int pos) {
   if (pos >= r.L) return -1;
   if constexpr (CSA) {
     if (pos < A.k) {
-      const int e = A.idx[static_cast<int64_t>(row) * A.k + pos];
+      const int32_t* ip = A.idx + static_cast<int64_t>(row) * A.k + pos;
+      const int e = COH ? __hip_atomic_load(const_cast<int32_t*>(ip), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : *ip;
       return (e >= 0 && e < r.nv) ? e : -1;
     }
     const int64_t t = r.wstart + (pos - A.k) - A.raw_pos0;
@@ -127,6 +132,25 @@ inline AttnDev make_attn_dev(const AttnArgs& a) {
   A.H = a.H;
   A.d = a.d;
   A.scale = a.scale;
+  return A;
+}
+
+// Kernel arguments of one attention call: with splits, the partials go to the workspace
+// (outputs [splits][rows][H][d], then log-sum-exps [splits][rows][H]).
+inline AttnDev attn_dev_for(const AttnArgs& a, const AttnPlan& plan, void* ws) {
+  AttnDev A = make_attn_dev(a);
+  A.chunk = plan.chunk;
+  A.splits = plan.splits;
+  A.rows = plan.rows;
+  if (plan.splits > 1) {
+    A.out = static_cast<float*>(ws);
+    A.lse = reinterpret_cast<float*>(
+        static_cast<char*>(ws) +
+        align256(static_cast<size_t>(plan.splits) * plan.rows * a.H * a.d * 4));
+  } else {
+    A.out = a.out;
+    A.lse = a.lse;
+  }
   return A;
 }
 

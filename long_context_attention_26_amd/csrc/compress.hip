@@ -36,7 +36,7 @@ template <bool PAGED>
 __global__ __launch_bounds__(256) void compress_batched_kernel(PoolJobs J) {
   __shared__ float alpha[1024];
   __shared__ float s_part[2048];
-  pool_jobs_block<PAGED>(J, blockIdx.x, alpha, s_part);
+  pool_jobs_block<PAGED>(J, blockIdx.x, alpha, s_part, blockIdx.y);
 }
 
 hipError_t launch_compress_batched(const hcsa_pool_job* jobs, int n, int B,

@@ -134,4 +134,38 @@ bool csa_hca_fused(const AttnPlan& pc, const AttnPlan& ph);
 hipError_t launch_csa_hca(const AttnArgs& c, const AttnPlan& pc, const AttnArgs& h,
                           const AttnPlan& ph, void* ws, hipStream_t s);
 
+// ---- decode.hip
+// One decode step (pooling of the completed blocks, MXFP4 indexer + top-k without a score
+// array, CSA and HCA attention) in four launches with the same results as
+// hcsa_csa_pool_index_topk followed by hcsa_csa_hca_attn.
+struct DecodeStepArgs {
+  const struct hcsa_pool_job* jobs;
+  int n_jobs;
+  const void* q_idx;
+  int q_dtype;
+  const float* w_idx;
+  const uint8_t* k_idx;
+  int k_dtype;
+  int64_t k_bstride;
+  const uint8_t* k_scales;
+  int64_t ks_bstride;
+  int H_I, d_I, N, score_dtype;
+  int32_t* idx;                 // [B*Nq][k] selection
+  const int32_t* block_table;
+  int64_t raw_ring;
+  const int64_t* seq_pos;
+  AttnArgs c, h;                // CSA (k, N, ratio, window) and HCA attention
+  int B, Nq;
+};
+// the four-launch form applies (else the two calls run in turn)
+bool decode_step_fast(const DecodeStepArgs& a, const AttnPlan& pc, const AttnPlan& ph,
+                      bool fused_selection);
+size_t decode_step_sync_bytes(int rows);
+AttnPlan plan_step_hca(int B, int Nq, int H, int d, int N_h);   // HCA splits of the four launches
+hipError_t launch_decode_step_reset(void* ws, int rows, hipStream_t s);
+// workspace: [sync words: decode_step_sync_bytes][selection state at mx_off][attention
+// partials at attn_off: CSA, then HCA at align256(pc.total_bytes)]
+hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const AttnPlan& ph,
+                              void* ws, size_t mx_off, size_t attn_off, hipStream_t s);
+
 }  // namespace hcsa

@@ -225,22 +225,22 @@ struct PoolJobs {
 template <bool IN_BF16, int OUT, bool PAGED>
 __device__ __forceinline__ void pool_job_blocks(const hcsa_pool_job& q, const PageMap& pm,
                                                 int64_t ring, float* alpha, int64_t jb,
-                                                int n_out, float* s_part) {
+                                                int n_out, float* s_part, int b) {
   if (q.ratio >= kWideRatio)
     pool_rows_wide<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, q.omega, alpha, q.ratio, q.y,
-                                        q.y_bstride, q.y_scales, q.ys_bstride, jb, blockIdx.y,
+                                        q.y_bstride, q.y_scales, q.ys_bstride, jb, b,
                                         s_part, pm, q.pos0, ring);
   else
     pool_rows<IN_BF16, OUT, PAGED>(q.x, q.x_bstride, q.D, q.omega, alpha, q.ratio, q.y,
                                    q.y_bstride, q.y_scales, q.ys_bstride, n_out, jb,
-                                   blockIdx.y, pm, q.pos0, ring);
+                                   b, pm, q.pos0, ring);
 }
 
-// Block bx of a batched pooling launch (grid.y = sequence): finds its job and runs it.
+// Block bx of sequence b of a batched pooling launch: finds its job and runs it.
 // alpha: LDS for 1024 weights; s_part: LDS for blockDim.x * 8 floats.
 template <bool PAGED>
 __device__ __forceinline__ void pool_jobs_block(const PoolJobs& J, int bx, float* alpha,
-                                                float* s_part) {
+                                                float* s_part, int b) {
   int t = 0;
   while (t + 1 < J.n && bx >= J.first_block[t + 1]) ++t;
   const hcsa_pool_job& q = J.job[t];
@@ -249,12 +249,12 @@ __device__ __forceinline__ void pool_jobs_block(const PoolJobs& J, int bx, float
   const bool ib = q.x_dtype == 1;
   const PageMap& pm = J.pm;
   const int64_t rg = J.ring;
-  if (ib && q.y_dtype == 1) pool_job_blocks<true, OUT_BF16, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
-  else if (ib && q.y_dtype == 2) pool_job_blocks<true, OUT_MXFP4, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
-  else if (ib) pool_job_blocks<true, OUT_F32, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
-  else if (q.y_dtype == 1) pool_job_blocks<false, OUT_BF16, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
-  else if (q.y_dtype == 2) pool_job_blocks<false, OUT_MXFP4, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
-  else pool_job_blocks<false, OUT_F32, PAGED>(q, pm, rg, alpha, jb, n_out, s_part);
+  if (ib && q.y_dtype == 1) pool_job_blocks<true, OUT_BF16, PAGED>(q, pm, rg, alpha, jb, n_out, s_part, b);
+  else if (ib && q.y_dtype == 2) pool_job_blocks<true, OUT_MXFP4, PAGED>(q, pm, rg, alpha, jb, n_out, s_part, b);
+  else if (ib) pool_job_blocks<true, OUT_F32, PAGED>(q, pm, rg, alpha, jb, n_out, s_part, b);
+  else if (q.y_dtype == 1) pool_job_blocks<false, OUT_BF16, PAGED>(q, pm, rg, alpha, jb, n_out, s_part, b);
+  else if (q.y_dtype == 2) pool_job_blocks<false, OUT_MXFP4, PAGED>(q, pm, rg, alpha, jb, n_out, s_part, b);
+  else pool_job_blocks<false, OUT_F32, PAGED>(q, pm, rg, alpha, jb, n_out, s_part, b);
 }
 
 // The jobs of a batched pooling call with their block ranges for blocks of `threads`;

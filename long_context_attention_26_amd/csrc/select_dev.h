@@ -144,9 +144,20 @@ struct RowView {
   }
 };
 
+// A selected index written to the output: COH stores are agent-coherent (relaxed atomic
+// stores), for outputs that other blocks of the same launch read.
+template <bool COH>
+__device__ __forceinline__ void put_idx(int32_t* p, int32_t v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // Rows that see at most k entries take all of them.
+template <bool COH = false>
 __device__ __forceinline__ void take_all(int nv, int k, int32_t* out, int nthreads) {
-  for (int j = threadIdx.x; j < k; j += nthreads) out[j] = j < nv ? j : -1;
+  for (int j = threadIdx.x; j < k; j += nthreads) put_idx<COH>(out + j, j < nv ? j : -1);
 }
 
 // One wave: the bin b (of 256) holding the m-th largest of the values counted in hist, and
@@ -195,7 +206,7 @@ __device__ __forceinline__ void hist_pick(const int* hist, int m, int* out) {
 // the visible count are masked), then every key above T and the first need = k - #(> T)
 // keys equal to T, written in index order: wave w owns a contiguous run of chunks, so the
 // order is (wave, step, lane, element) and ballots give each lane's output slots.
-template <int KB, int NT>
+template <int KB, int NT, bool COH = false>
 __device__ void select_exact_row(const RowView<KB>& V, int k, int32_t* out,
                                  int (*s_cnt)[NT / 64], int* s_gt, int* s_eq) {
   constexpr int W = NT / 64, EPC = RowView<KB>::EPC;
@@ -258,7 +269,7 @@ __device__ void select_exact_row(const RowView<KB>& V, int k, int32_t* out,
     int tot;
     int o = slot + wave_prefix_bits<CB>(__popc(sel), below, tot);
     while (sel) {
-      if (o < k) out[o] = ch * EPC + __ffs(sel) - 1;
+      if (o < k) put_idx<COH>(out + o, ch * EPC + __ffs(sel) - 1);
       ++o;
       sel &= sel - 1;
     }
@@ -276,7 +287,7 @@ __device__ void select_exact_row(const RowView<KB>& V, int k, int32_t* out,
 // differing bits spread the candidates over the bins; digits aligned to bytes would pile
 // them into the few bins of their common exponent, and LDS atomics on one address
 // serialise.
-template <int KB, int NT, int PER>
+template <int KB, int NT, int PER, bool COH = false>
 __device__ void select_candidates(const uint32_t (&ck)[PER], const int32_t (&cj)[PER], int cnt,
                                   uint32_t L, int k, int32_t* out, int* s_gt, int* s_eq,
                                   int* s_hb, int (*s_hist)[256], int* s_sel) {
@@ -354,7 +365,7 @@ __device__ void select_candidates(const uint32_t (&ck)[PER], const int32_t (&cj)
       const bool sel = ck[u] > T || (ck[u] == T && eq_rank < need);
       eq_rank += ck[u] == T;
       if (sel) {
-        if (o < k) out[o] = cj[u];
+        if (o < k) put_idx<COH>(out + o, cj[u]);
         ++o;
       }
     }

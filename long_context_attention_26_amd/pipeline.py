@@ -100,6 +100,9 @@ class DecodeStep:
             hcsa.index_topk_workspace_size(B, Nq, st.Nc, topk, self.score_code), dev)
         self.ws_attn = hcsa.alloc_workspace(
             hcsa.csa_hca_attn_workspace_size(B, Nq, H, d, topk, n_win, st.Nh), dev)
+        self.ws_step = hcsa.alloc_workspace(
+            hcsa.decode_step_workspace_size(B, Nq, st.Nc, topk, self.score_code, H, d, n_win,
+                                            st.Nh), dev)
 
     def run_pool(self, pos0, stream=None):
         """Pool the blocks completed by the query tokens."""
@@ -142,20 +145,36 @@ class DecodeStep:
                                  k_scales=st.Ics, workspace=self.ws_itopk, stream=stream,
                                  mx_fp8=self.mx_fp8)
 
+    def run_step(self, q, q_idx, w_idx, pos0, stream=None):
+        """The whole step (pooling of the completed blocks, indexer + top-k, CSA and HCA
+        attention) as one call: for MXFP4 keys at one-token decode, four launches that run
+        the HCA stream beside the floors and the resolves."""
+        st = self.st
+        hcsa.decode_step(st.pool_jobs(pos0, pos0 + self.Nq), q_idx, w_idx, st.Ic,
+                         self.score_code, self.idx, q, st.Kc, st.Vc, st.Nc, self.topk,
+                         st.K_raw, st.V_raw, 0, self.n_win, R_CSA, st.Kh, st.Vh, st.Nh, R_HCA,
+                         pos0, self.scale, self.out_csa, self.lse_csa, self.out_hca,
+                         self.lse_hca, k_scales=st.Ics, workspace=self.ws_step, stream=stream,
+                         mx_fp8=self.mx_fp8)
+        return self.idx, (self.out_csa, self.lse_csa), (self.out_hca, self.lse_hca)
+
     def run_attend(self, q, pos0, stream=None):
         self._attend(q, pos0, stream)
 
     def run(self, q, q_idx, w_idx, pos0, append=True, scores_out=None, stream=None,
-            marks=None):
+            marks=None, two_calls=False):
         """Full hot path for the query tokens at pos0..pos0+Nq-1: pool the blocks those
         tokens complete (append), indexer scores and top-k, CSA sparse attention and HCA
-        attention (one call).  With scores_out the scores are written there and selected
-        by a second call; without, one indexer + top-k call (which, for MXFP4 keys at
-        decode, never stores them).
+        attention.  By default (append, no score copy) one decode-step call; two_calls runs
+        it as the pooling + indexer + top-k call and the attention call (same results).
+        With scores_out the scores are written there and selected by a second call;
+        without, the indexer + top-k never stores them for MXFP4 keys at decode.
         `marks`, if given, is called with a stage name before each stage and with "end"
         after the last (used to record timing events on the stream)."""
         st = self.st
         mark = marks or (lambda name: None)
+        if scores_out is None and append and not two_calls and marks is None:
+            return self.run_step(q, q_idx, w_idx, pos0, stream=stream)
         mark("pool_index_topk")
         if scores_out is None and append:
             self.run_pool_index_topk(q_idx, w_idx, pos0, stream=stream)

@@ -71,3 +71,14 @@ def topk_set_ok(gpu_idx, ref_idx, ref_scores, k, what, rel=1e-5, tol_abs=None):
         assert abs(ref_scores[j] - kth) <= tol, \
             f"{what}: entry {j} differs away from the threshold ({ref_scores[j]} vs {kth})"
     return len(g ^ r) // 2
+
+
+def pv_rounding_bound(q, K, V, scale):
+    """Bound on the difference between two split plans of the same bf16 16 x 128 attention:
+    the P.V product takes the probabilities as bf16, each split rounding them relative to
+    its own running maximum (relative error <= 2^-9 per term on each side), so
+    |do| <= 2^-8 sum_j p_j |v_j| / sum_j p_j (+ fp32 slack).  q [H, d], K, V [L, d] (float64)."""
+    if K.shape[0] == 0:
+        return np.full(q.shape, 1e-6)
+    w = O.softmax_weights(q, K, scale)
+    return 2.0 ** -8 * (w @ np.abs(V)) + 1e-6

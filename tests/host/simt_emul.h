@@ -73,6 +73,12 @@ inline int __shfl_xor(int v, int mask, int width = 64) {
 }
 inline void __syncthreads() { emu::g_block->block_bar->arrive_and_wait(); }
 inline int atomicAdd(int* p, int v) { return std::atomic_ref<int>(*p).fetch_add(v); }
+#define __HIP_MEMORY_SCOPE_AGENT 3
+template <typename T>
+inline void __hip_atomic_store(T* p, T v, int order, int scope) {
+  (void)scope;
+  __atomic_store_n(p, v, order);
+}
 inline int __popcll(uint64_t m) { return __builtin_popcountll(m); }
 inline int __popc(uint32_t m) { return __builtin_popcount(m); }
 inline int __ffs(uint32_t m) { return __builtin_ffs(static_cast<int>(m)); }
