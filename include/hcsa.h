@@ -337,21 +337,21 @@ int hcsa_csa_hca_attn(const void *q, const void *kc, const void *vc, int64_t c_b
  * One decode step of a CSA layer and an HCA layer [Lighthouse section 八 items 3 and 7: the
  * tokens of a step complete the blocks its indexer scans; CSA and HCA layers over the same
  * tokens]: hcsa_csa_pool_index_topk(jobs, ..., scores_out = NULL) followed by
- * hcsa_csa_hca_attn(...) with the same arguments, as one call with the same results bit for
- * bit.  The indexer shares N and ratio with CSA (one indexer key per CSA entry).
+ * hcsa_csa_hca_attn(...) with the same arguments, as one call.  The indexer shares N and
+ * ratio with CSA (one indexer key per CSA entry).
  *
  * For one query token per sequence with MXFP4 keys (fp4 operands), bf16 queries and scores,
- * the selection without a score array, bf16 16 x 128 attention and contiguous caches, the
- * step runs in four launches: the per-row selection floors and the pooling beside the first
- * HCA splits (entries completed before the step); the key scan; per-row resolves beside the
- * remaining HCA splits and the CSA splits, which wait for their row's selection; the split
- * merge.  Other shapes run the two calls' kernels in turn.
+ * the selection without a score array, bf16 16 x 128 attention, contiguous caches and
+ * k + n_win <= 4096, the step runs in four launches: the per-row selection floors beside the
+ * pooling; the key scan; one block per row resolving its top-k and then attending over it
+ * and its window (CSA), beside the HCA splits on the other compute units; the HCA split
+ * merge.  The pooled caches and the selection equal those of the two calls bit for bit; the
+ * attention outputs are split differently and agree with theirs up to the rounding of the
+ * split sums (the softmax probabilities enter P.V as bf16, rounded relative to each split's
+ * running maximum).  Other shapes run the two calls' kernels in turn, with their results.
  *
  * workspace: hcsa_decode_step_workspace_size(B, Nq, N, k, score_dtype, H, d, n_win, N_h)
- * bytes, 256-byte aligned; its contents need not be initialized.  Its first 32-bit word
- * counts the back launch's waits for a selection that timed out (about a second each; zero
- * unless the device misbehaves; outputs of a step with a nonzero count are undefined); it
- * is reset by every call.
+ * bytes, 256-byte aligned; its contents need not be initialized.
  */
 size_t hcsa_decode_step_workspace_size(int B, int Nq, int N, int k, int score_dtype, int H,
                                        int d, int n_win, int N_h);

@@ -612,13 +612,13 @@ int hcsa_csa_hca_attn(const void* q, const void* kc, const void* vc, int64_t c_b
 size_t hcsa_decode_step_workspace_size(int B, int Nq, int N, int k, int score_dtype, int H,
                                        int d, int n_win, int N_h) {
   if (B < 1 || Nq < 1 || N < 1 || k < 1 || H < 1 || d < 1) return 0;
-  // attention partials: those of the two calls, or of the four-launch form's finer HCA
-  // splits, whichever is larger
-  const size_t pc = hcsa::align256(hcsa_csa_sparse_attn_workspace_size(B, Nq, H, d, k, n_win));
-  const size_t attn = std::max(hcsa_csa_hca_attn_workspace_size(B, Nq, H, d, k, n_win, N_h),
-                               pc + hcsa::plan_step_hca(B, Nq, H, d, N_h).total_bytes);
-  return hcsa::decode_step_sync_bytes(B * Nq) +
-         hcsa::align256(hcsa_csa_index_topk_workspace_size(B, Nq, N, k, score_dtype)) + attn;
+  // attention partials: those of the two calls, or of the four-launch form's splits,
+  // whichever is larger
+  const size_t two = hcsa_csa_hca_attn_workspace_size(B, Nq, H, d, k, n_win, N_h);
+  const size_t four = hcsa::align256(hcsa::plan_step_csa(B, Nq, H, d, k, n_win).total_bytes) +
+                      hcsa::plan_step_hca(B, Nq, H, d, N_h).total_bytes;
+  return hcsa::align256(hcsa_csa_index_topk_workspace_size(B, Nq, N, k, score_dtype)) +
+         hcsa::decode_step_sync_bytes(B * Nq) + std::max(two, four);
 }
 
 int hcsa_decode_step(const hcsa_pool_job* jobs, int n_jobs, const void* q_idx, int q_dtype,
@@ -652,15 +652,17 @@ int hcsa_decode_step(const hcsa_pool_job* jobs, int n_jobs, const void* q_idx, i
   rc = check_hca(q, kh, vh, h_bstride, N_h, ratio_h, pos0, seq_pos, pages, kv_dtype, B, Nq, H,
                  d, scale, out_h, lse_h);
   if (rc) return rc;
-  const size_t sync = hcsa::decode_step_sync_bytes(B * Nq);
   const size_t mx_bytes = hcsa::align256(hcsa_csa_index_topk_workspace_size(B, Nq, N, k, score_dtype));
   const hcsa::AttnPlan pc =
       hcsa::plan_attention(true, kv_dtype, B, Nq, H, d, attn_max_len_csa(k, n_win));
   const hcsa::AttnPlan ph = hcsa::plan_attention(false, kv_dtype, B, Nq, H, d, N_h);
+  const hcsa::AttnPlan pc_step = hcsa::plan_step_csa(B, Nq, H, d, k, n_win);
   const hcsa::AttnPlan ph_step = hcsa::plan_step_hca(B, Nq, H, d, N_h);
-  const size_t attn_bytes = hcsa::align256(pc.total_bytes) +
-                            std::max(ph.total_bytes, ph_step.total_bytes);
-  rc = check_ws(workspace, ws_bytes, sync + mx_bytes + attn_bytes);
+  const size_t attn_bytes =
+      std::max(hcsa::align256(pc.total_bytes) + ph.total_bytes,
+               hcsa::align256(pc_step.total_bytes) + ph_step.total_bytes);
+  const size_t sync_bytes = hcsa::decode_step_sync_bytes(B * Nq);
+  rc = check_ws(workspace, ws_bytes, mx_bytes + sync_bytes + attn_bytes);
   if (rc) return rc;
   hcsa::DecodeStepArgs a{};
   a.jobs = jobs; a.n_jobs = n_jobs; a.q_idx = q_idx; a.q_dtype = q_dtype; a.w_idx = w_idx;
@@ -685,18 +687,18 @@ int hcsa_decode_step(const hcsa_pool_job* jobs, int n_jobs, const void* q_idx, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fused = index_topk_fused(k_dtype, score_dtype, B, Nq, N, k, nullptr);
   if (hcsa::decode_step_fast(a, pc, ph, fused))
-    return hip_status(hcsa::launch_decode_step(a, pc, ph_step, workspace, sync, sync + mx_bytes,
-                                               s),
+    return hip_status(hcsa::launch_decode_step(a, pc_step, ph_step, workspace, mx_bytes,
+                                               mx_bytes + sync_bytes, s),
                       "hcsa_decode_step");
   // other shapes: the two calls in turn, on the same parts of the workspace
-  hipError_t e0 = hcsa::launch_decode_step_reset(workspace, B * Nq, s);
-  if (e0 != hipSuccess) return hip_status(e0, "hcsa_decode_step");
   rc = index_topk_impl(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
                        B, Nq, H_I, d_I, N, ratio, pos0, seq_pos, pages, k, score_dtype,
-                       topk_idx, nullptr, static_cast<char*>(workspace) + sync, mx_bytes,
-                       stream, n_jobs > 0 ? jobs : nullptr, n_jobs);
+                       topk_idx, nullptr, workspace, mx_bytes, stream,
+                       n_jobs > 0 ? jobs : nullptr, n_jobs);
   if (rc) return rc;
-  return hip_status(hcsa::launch_csa_hca(c, pc, h, ph, static_cast<char*>(workspace) + sync + mx_bytes, s),
+  return hip_status(hcsa::launch_csa_hca(c, pc, h, ph,
+                                         static_cast<char*>(workspace) + mx_bytes + sync_bytes,
+                                         s),
                     "hcsa_decode_step (attention)");
 }
 

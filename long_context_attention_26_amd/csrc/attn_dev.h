@@ -75,11 +75,12 @@ __device__ __forceinline__ void attend_step(const u32x4 (&ka)[2][4], const u32x4
   }
 }
 
-// The 4 waves' partial results of one (split, row) block merged in LDS and written as the
+// The W waves' partial results of one (split, row) unit merged in LDS and written as the
 // split's normalized output and log-sum-exp (or the final ones with a single split).
 //
-// tid: the thread's index in its 256-thread unit (a block may hold two units, each with its
-// own LDS; both reach the same barriers).
+// tid: the thread's index in its 64*W-thread unit (a block may hold two 4-wave units, each
+// with its own LDS; both reach the same barriers).
+template <int W = 4>
 __device__ __forceinline__ void combine_waves(const AttnDev& A, const f32x4 (&acc)[8],
                                               float m_run, float l_run, float (*s_o)[16][129],
                                               float (*s_ml)[2][16], int split, int row,
@@ -103,15 +104,15 @@ __device__ __forceinline__ void combine_waves(const AttnDev& A, const f32x4 (&ac
 
   float* o = A.out + (static_cast<int64_t>(split) * A.rows + row) * 2048;
   float* ls = A.lse + static_cast<int64_t>(split) * A.rows * 16 + static_cast<int64_t>(row) * 16;
-  for (int t = tid; t < 2048; t += 256) {
+  for (int t = tid; t < 2048; t += 64 * W) {
     const int h = t >> 7, c = t & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_ml[w][0][h]);
     float num = 0.0f, den = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float mw = s_ml[w][0][h];
         if (mw != -INFINITY) {
           const float f = exp2f(mw - M);
@@ -191,6 +192,81 @@ __device__ __forceinline__ void attn_mfma_block(const AttnDev& A, int split, int
   }
 
   combine_waves(A, acc, m_run, l_run, s_o, s_ml, split, row, tid);
+}
+
+// CSA attention of one query row by an 8-wave (512-thread) block over ranges of its key
+// list, accumulated into one online softmax (acc, m_run, l_run held by the caller): wave w
+// takes steps of 32 positions at p0 + w*32, p0 + w*32 + 256, ..., with the next step's K rows
+// and V slices in flight while the current step is computed.  A range holds at most
+// kMfmaMaxChunk positions.  COH: the selection is read with agent-coherent loads (written
+// by another block of the same launch).  The step math is that of the split kernels; only
+// the partition of the key list differs.
+template <bool COH>
+__device__ __forceinline__ void csa_range8(const AttnDev& A, const RowKeys& r, int row, int p0,
+                                           int p1, int* s_code, const u32x4 (&qB)[4],
+                                           f32x4 (&acc)[8], float& m_run, float& l_run,
+                                           float sl2) {
+  const int cnt = max(0, min(p1 - p0, kMfmaMaxChunk));
+  __syncthreads();                                 // s_code free again
+  for (int i = threadIdx.x; i < cnt; i += 512) s_code[i] = key_code<true, COH>(A, r, row, p0 + i);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, g = lane >> 4;
+  // K rows of keys base + 16t + col; V slices (channels 8col..) of keys base + 16*(j/4) +
+  // 4g + j%4 (the layouts of attend_step)
+  auto load = [&](int base, u32x4 (&ka)[2][4], u32x4 (&vv)[8], bool (&ok)[8]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int pos = base + 16 * t + col;
+      const int c = pos < cnt ? s_code[pos] : -1;
+      if (c != -1) {
+        const uint16_t* kr = key_row<uint16_t>(A, r.b, c, false);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[t][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[t][s] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int pos = base + 16 * (j >> 2) + 4 * g + (j & 3);
+      const int c = pos < cnt ? s_code[pos] : -1;
+      ok[j] = c != -1;
+      vv[j] = ok[j] ? *reinterpret_cast<const u32x4*>(key_row<uint16_t>(A, r.b, c, true) + 8 * col)
+                    : u32x4{0, 0, 0, 0};
+    }
+  };
+  u32x4 kaA[2][4], vvA[8], kaB[2][4], vvB[8];
+  bool okA[8], okB[8];
+  const int w0 = wave * 32;
+  if (w0 < cnt) load(w0, kaA, vvA, okA);
+  for (int base = w0; base < cnt; base += 512) {
+    if (base + 256 < cnt) load(base + 256, kaB, vvB, okB);
+    attend_step(kaA, vvA, okA, qB, acc, m_run, l_run, sl2);
+    if (base + 256 >= cnt) break;
+    if (base + 512 < cnt) load(base + 512, kaA, vvA, okA);
+    attend_step(kaB, vvB, okB, qB, acc, m_run, l_run, sl2);
+  }
+}
+
+// The query operand and empty accumulators of an 8-wave CSA row unit.
+struct Row8State {
+  u32x4 qB[4];                                     // B of S^T: Q[head col][32s + 8g .. +8]
+  f32x4 acc[8];
+  float m_run, l_run, sl2;
+};
+
+__device__ __forceinline__ void row8_init(const AttnDev& A, int row, Row8State& st) {
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  const uint16_t* qrow = static_cast<const uint16_t*>(A.q) + (static_cast<int64_t>(row) * 16 + col) * 128;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) st.qB[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.acc[t] = f32x4{0, 0, 0, 0};
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
+  st.sl2 = A.scale * 1.4426950408889634f;          // logits in base 2
 }
 
 // Decode HCA: the visible entries 0..nv-1 are contiguous, so no key list is built; each of

@@ -160,12 +160,13 @@ struct DecodeStepArgs {
 // the four-launch form applies (else the two calls run in turn)
 bool decode_step_fast(const DecodeStepArgs& a, const AttnPlan& pc, const AttnPlan& ph,
                       bool fused_selection);
+// attention splits of the four-launch form
+AttnPlan plan_step_csa(int B, int Nq, int H, int d, int k, int n_win);
+AttnPlan plan_step_hca(int B, int Nq, int H, int d, int N_h);
+// workspace: [selection state (mx_topk_layout)][sync words at sync_off][attention partials
+// at attn_off: CSA, then HCA at align256(pc.total_bytes)]
 size_t decode_step_sync_bytes(int rows);
-AttnPlan plan_step_hca(int B, int Nq, int H, int d, int N_h);   // HCA splits of the four launches
-hipError_t launch_decode_step_reset(void* ws, int rows, hipStream_t s);
-// workspace: [sync words: decode_step_sync_bytes][selection state at mx_off][attention
-// partials at attn_off: CSA, then HCA at align256(pc.total_bytes)]
 hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const AttnPlan& ph,
-                              void* ws, size_t mx_off, size_t attn_off, hipStream_t s);
+                              void* ws, size_t sync_off, size_t attn_off, hipStream_t s);
 
 }  // namespace hcsa
