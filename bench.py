@@ -91,13 +91,9 @@ def measured_traffic(cfg, mx_fp8=False):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = open(os.path.join(ROOT, "long_context_attention_26_amd", "csrc", "indexer.hip")).read()
-    try:
-        a = src.index("constexpr int kMxMaxUnits = 16 * 4;")
-        b = src.index("// ---------------------------------------------------------------- fused decode selection")
-    except ValueError:
-        return None
-    if hashlib.sha256(src[a:b].encode()).hexdigest() != rec.get("kernel_text_sha256"):
+    csrc = os.path.join(ROOT, "long_context_attention_26_amd", "csrc")
+    src = "".join(open(os.path.join(csrc, f)).read() for f in ("mx_dev.h", "mx_scan.h"))
+    if hashlib.sha256(src.encode()).hexdigest() != rec.get("kernel_text_sha256"):
         return None
     return int(round(rec["traffic_bytes"]))
 

@@ -18,9 +18,7 @@ namespace hcsa {
 
 namespace {
 
-// KS: 64-channel MFMA steps the kernels hold registers for (d_I <= 64: one).  The FP8
-// form keeps two: built with one, its scores differed from the FP4 form's (measured; the
-// cause was not found), with two they are identical, as the tests require.
+// KS: 64-channel MFMA steps the kernels hold registers for (d_I <= 64: one).
 template <int HI, int KS, bool QBF16, bool F8>
 hipError_t launch_mx_mfma_ks(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
@@ -36,7 +34,7 @@ hipError_t launch_mx_mfma_ks(const IdxMxDev& A, int rows, int score_dtype, hipSt
 
 template <int HI, bool QBF16, bool F8>
 hipError_t launch_mx_mfma_hi(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
-  if (A.d_I > 64 || F8) return launch_mx_mfma_ks<HI, 2, QBF16, F8>(A, rows, score_dtype, s);
+  if (A.d_I > 64) return launch_mx_mfma_ks<HI, 2, QBF16, F8>(A, rows, score_dtype, s);
   return launch_mx_mfma_ks<HI, 1, QBF16, F8>(A, rows, score_dtype, s);
 }
 

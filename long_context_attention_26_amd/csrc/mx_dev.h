@@ -210,6 +210,14 @@ __device__ __forceinline__ void mx_load(const IdxMxDev& A, const uint8_t* kbase,
 
 // Score of the key whose codes this lane's column holds (valid in lane half 0, and in both
 // halves for H_I > 4): sum over heads of w_g * relu(q_g . k) from one or two MFMAs.
+//
+// The MFMA reads the operand registers of all 64 lanes whatever the EXEC mask, so every lane
+// must assemble its operands before it.  With the score used only in half 0 (callers store it
+// under `half == 0`), the compiler sank the FP8 form's e2m1-to-e4m3 widening and the MFMA
+// into that store's branch, where half 1 never wrote its widened operand and the MFMA read
+// stale registers (measured: wrong and run-dependent scores at H_I 1 and 4).  An empty
+// volatile asm that takes the lane's sum in every lane keeps the MFMA, and so its operands,
+// where the whole wave runs it; it emits no instruction and holds one register.
 template <int HI, int KS, bool F8>
 __device__ __forceinline__ float mx_score(const MxQuery<HI, KS>& Q, const u32x4 (&kraw)[KS],
                                           const int (&ksc)[KS], int ksteps) {
@@ -247,6 +255,7 @@ __device__ __forceinline__ float mx_score(const MxQuery<HI, KS>& Q, const u32x4 
     const int g = 8 * (r >> 2) + 4 * half + (r & 3);
     if (g < HI) part = fmaf(Q.w[g], relu(d[r]), part);
   }
+  asm volatile("" : "+v"(part));
   if constexpr (HI > 4) part += __shfl_xor(part, 32, kWave);
   return part + 0.0f;
 }
