@@ -368,6 +368,33 @@ int hcsa_decode_step(const hcsa_pool_job *jobs, int n_jobs, const void *q_idx, i
                      void *workspace, size_t ws_bytes, hcsa_stream stream);
 
 /*
+ * hcsa_decode_step without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The step's workspace is a scratch array of HCSA_DECODE_STEP_SCRATCH_BYTES in
+ * the library's own device memory: one copy on each GPU the call runs on, reserved when the
+ * library's code is loaded there and held until the process ends.  Nothing is allocated by
+ * the call.  Arguments, results and errors are those of hcsa_decode_step; a step whose
+ * hcsa_decode_step_workspace_size exceeds the scratch (a batch of 32 sequences at
+ * 1 048 576 tokens needs about 85 MiB) is rejected with HCSA_EWORKSPACE before any launch.
+ * All calls on one GPU share its scratch: calls that overlap on one GPU (other streams,
+ * other host threads) race and give wrong results; serialize them.  The scratch needs no
+ * clearing between calls (the step initializes what it reads).
+ */
+#define HCSA_DECODE_STEP_SCRATCH_BYTES ((size_t)128 << 20)
+int hcsa_decode_step_noalloc(const hcsa_pool_job *jobs, int n_jobs, const void *q_idx,
+                             int q_dtype, const float *w_idx, const void *k_idx, int k_dtype,
+                             int64_t k_bstride, const uint8_t *k_scales, int64_t ks_bstride,
+                             int H_I, int d_I, int score_dtype, int32_t *topk_idx,
+                             const void *q, const void *kc, const void *vc, int64_t c_bstride,
+                             int N, int k, const void *k_raw, const void *v_raw,
+                             int64_t raw_bstride, int64_t T_raw, int64_t raw_pos0, int n_win,
+                             int ratio, const void *kh, const void *vh, int64_t h_bstride,
+                             int N_h, int ratio_h, int64_t pos0, const int64_t *seq_pos,
+                             const hcsa_pages *pages, int kv_dtype, int B, int Nq, int H,
+                             int d, float scale, float *out_c, float *lse_c, float *out_h,
+                             float *lse_h, hcsa_stream stream);
+
+/*
  * Backward (training) [Lighthouse section 八 item 2: the sparse attention is trained from
  * the 64K stage of the length curriculum; item 3 for the attention itself].  Gradients of
  * the loss sum(dout * out) + sum(dlse * lse) of the forward call with the same arguments;

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhcsa.so")
 SOURCES = ["compress.hip", "indexer.hip", "indexer_mx.hip", "indexer_mx_topk.hip", "topk.hip",
-           "attention.hip", "backward.hip", "decode.hip", "abi.cpp"]
+           "attention.hip", "backward.hip", "decode.hip", "noalloc.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
          "-Wno-unused-function",

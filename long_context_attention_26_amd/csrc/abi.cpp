@@ -93,6 +93,20 @@ int64_t raw_ring(const hcsa_pages* pages) { return pages ? pages->raw_ring : 0; 
 
 }  // namespace
 
+namespace hcsa {
+
+int abi_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+}  // namespace hcsa
+
 extern "C" {
 
 int hcsa_version(void) { return 100; }

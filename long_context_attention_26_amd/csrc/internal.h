@@ -125,6 +125,8 @@ hipError_t launch_compress_bwd(const void* x, int x_dtype, int64_t x_bstride, in
                                float* domega, void* ws, hipStream_t s);
 AttnPlan plan_attention(bool csa, int kv_dtype, int B, int Nq, int H, int d, int max_len);
 void set_attn_splits(int splits);   // 0: automatic (this thread's later plans)
+// Sets the calling thread's error message (hcsa_last_error) and returns `code`.
+int abi_fail(int code, const char* fmt, ...);
 hipError_t launch_attention(bool csa, const AttnArgs& a, const AttnPlan& plan, void* ws,
                             hipStream_t s);
 // CSA and HCA attention of the same query tokens: one launch for both (plus one merge) on

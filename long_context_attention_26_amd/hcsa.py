@@ -62,10 +62,15 @@ _SIGS = {
                               _p, _p, _p, _i64, _i, _i, _p, _p, _i64, _i64, _i64, _i, _i,
                               _p, _p, _i64, _i, _i, _i64, _p, _p, _i, _i, _i, _i, _i, _f,
                               _p, _p, _p, _p, _p, _sz, _p]),
+    "hcsa_decode_step_noalloc": (_i, [_p, _i, _p, _i, _p, _p, _i, _i64, _p, _i64, _i, _i, _i,
+                                      _p, _p, _p, _p, _i64, _i, _i, _p, _p, _i64, _i64, _i64,
+                                      _i, _i, _p, _p, _i64, _i, _i, _i64, _p, _p, _i, _i, _i,
+                                      _i, _i, _f, _p, _p, _p, _p, _p]),
     "hcsa_hca_dense_attn": (_i, [_p, _p, _p, _i64, _i, _i, _i64, _p, _p, _i, _i, _i, _i, _i,
                                  _f, _p, _p, _p, _sz, _p]),
 }
 MAX_POOL_JOBS = 8
+DECODE_STEP_SCRATCH_BYTES = 128 << 20    # HCSA_DECODE_STEP_SCRATCH_BYTES
 
 
 class PoolJob(ctypes.Structure):
@@ -282,6 +287,29 @@ def decode_step_workspace_size(B, Nq, N, k, score_dtype, H, d, n_win, N_h):
     return lib.hcsa_decode_step_workspace_size(B, Nq, N, k, score_dtype, H, d, n_win, N_h)
 
 
+def _decode_step_args(jobs, q_idx, w_idx, k_idx, score_dtype, topk_idx, q, kc, vc, N, k,
+                      k_raw, v_raw, raw_pos0, n_win, ratio, kh, vh, N_h, ratio_h, pos0, scale,
+                      out_c, lse_c, out_h, lse_h, k_scales, seq_pos, block_table, raw_ring,
+                      mx_fp8):
+    """The step's arguments up to lse_h, as the C calls take them (the first is the pool-job
+    array, which must stay referenced until the call returns)."""
+    B, Nq, H_I, d_I = q_idx.shape
+    _, _, H, d = q.shape
+    if k_idx.dtype == torch.uint8:
+        k_dt, ksb = (MXFP4_FP8 if mx_fp8 else MXFP4), k_scales.stride(0)
+    else:
+        k_dt, ksb = dtype_code(k_idx), 0
+    arr = (PoolJob * max(1, len(jobs)))(*jobs)
+    return (arr, len(jobs), _ptr(q_idx), dtype_code(q_idx), _ptr(w_idx),
+            _ptr(k_idx), k_dt, k_idx.stride(0), _ptr(k_scales), ksb, H_I, d_I, score_dtype,
+            _ptr(topk_idx), _ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N, k, _ptr(k_raw),
+            _ptr(v_raw), k_raw.stride(0) if k_raw is not None else 0,
+            k_raw.shape[1] if k_raw is not None else 0, raw_pos0, n_win, ratio, _ptr(kh),
+            _ptr(vh), kh.stride(0), N_h, ratio_h, pos0, _pos_ptr(seq_pos, B),
+            _pages(block_table, raw_ring), dtype_code(q), B, Nq, H, d, scale, _ptr(out_c),
+            _ptr(lse_c), _ptr(out_h), _ptr(lse_h))
+
+
 def decode_step(jobs, q_idx, w_idx, k_idx, score_dtype, topk_idx, q, kc, vc, N, k, k_raw,
                 v_raw, raw_pos0, n_win, ratio, kh, vh, N_h, ratio_h, pos0, scale, out_c,
                 lse_c, out_h, lse_h, k_scales=None, workspace=None, stream=None,
@@ -289,25 +317,32 @@ def decode_step(jobs, q_idx, w_idx, k_idx, score_dtype, topk_idx, q, kc, vc, N, 
     """One decode step: csa_pool_index_topk(jobs, ...) then csa_hca_attn(...) as one call
     (same results).  q_idx [B, Nq, H_I, d_I]; q [B, Nq, H, d]; the indexer shares N and
     ratio with CSA."""
-    B, Nq, H_I, d_I = q_idx.shape
-    _, _, H, d = q.shape
-    if k_idx.dtype == torch.uint8:
-        k_dt, ksb = (MXFP4_FP8 if mx_fp8 else MXFP4), k_scales.stride(0)
-    else:
-        k_dt, ksb = dtype_code(k_idx), 0
+    B, Nq = q_idx.shape[:2]
+    H, d = q.shape[2:]
     if workspace is None:
         workspace = alloc_workspace(decode_step_workspace_size(B, Nq, N, k, score_dtype, H, d,
                                                                n_win, N_h), q.device)
-    arr = (PoolJob * max(1, len(jobs)))(*jobs)
-    _check(lib.hcsa_decode_step(
-        ctypes.cast(arr, _p), len(jobs), _ptr(q_idx), dtype_code(q_idx), _ptr(w_idx),
-        _ptr(k_idx), k_dt, k_idx.stride(0), _ptr(k_scales), ksb, H_I, d_I, score_dtype,
-        _ptr(topk_idx), _ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N, k, _ptr(k_raw),
-        _ptr(v_raw), k_raw.stride(0) if k_raw is not None else 0,
-        k_raw.shape[1] if k_raw is not None else 0, raw_pos0, n_win, ratio, _ptr(kh), _ptr(vh),
-        kh.stride(0), N_h, ratio_h, pos0, _pos_ptr(seq_pos, B), _pages(block_table, raw_ring),
-        dtype_code(q), B, Nq, H, d, scale, _ptr(out_c), _ptr(lse_c), _ptr(out_h), _ptr(lse_h),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+    args = _decode_step_args(jobs, q_idx, w_idx, k_idx, score_dtype, topk_idx, q, kc, vc, N,
+                             k, k_raw, v_raw, raw_pos0, n_win, ratio, kh, vh, N_h, ratio_h,
+                             pos0, scale, out_c, lse_c, out_h, lse_h, k_scales, seq_pos,
+                             block_table, raw_ring, mx_fp8)
+    _check(lib.hcsa_decode_step(ctypes.cast(args[0], _p), *args[1:], _ptr(workspace),
+                                workspace.numel(), _stream(stream)))
+    return topk_idx
+
+
+def decode_step_noalloc(jobs, q_idx, w_idx, k_idx, score_dtype, topk_idx, q, kc, vc, N, k,
+                        k_raw, v_raw, raw_pos0, n_win, ratio, kh, vh, N_h, ratio_h, pos0,
+                        scale, out_c, lse_c, out_h, lse_h, k_scales=None, stream=None,
+                        seq_pos=None, block_table=None, raw_ring=0, mx_fp8=False):
+    """decode_step with the library's fixed per-GPU scratch as its workspace: nothing is
+    allocated (steps needing up to DECODE_STEP_SCRATCH_BYTES of workspace; calls that
+    overlap on one GPU race)."""
+    args = _decode_step_args(jobs, q_idx, w_idx, k_idx, score_dtype, topk_idx, q, kc, vc, N,
+                             k, k_raw, v_raw, raw_pos0, n_win, ratio, kh, vh, N_h, ratio_h,
+                             pos0, scale, out_c, lse_c, out_h, lse_h, k_scales, seq_pos,
+                             block_table, raw_ring, mx_fp8)
+    _check(lib.hcsa_decode_step_noalloc(ctypes.cast(args[0], _p), *args[1:], _stream(stream)))
     return topk_idx
 
 

@@ -145,17 +145,21 @@ class DecodeStep:
                                  k_scales=st.Ics, workspace=self.ws_itopk, stream=stream,
                                  mx_fp8=self.mx_fp8)
 
-    def run_step(self, q, q_idx, w_idx, pos0, stream=None):
+    def run_step(self, q, q_idx, w_idx, pos0, stream=None, noalloc=False):
         """The whole step (pooling of the completed blocks, indexer + top-k, CSA and HCA
         attention) as one call: for MXFP4 keys at one-token decode, four launches that run
-        the HCA stream beside the floors and the resolves."""
+        the HCA stream beside the floors and the resolves.  noalloc: the call that takes the
+        library's fixed scratch instead of this step's workspace."""
         st = self.st
-        hcsa.decode_step(st.pool_jobs(pos0, pos0 + self.Nq), q_idx, w_idx, st.Ic,
-                         self.score_code, self.idx, q, st.Kc, st.Vc, st.Nc, self.topk,
-                         st.K_raw, st.V_raw, 0, self.n_win, R_CSA, st.Kh, st.Vh, st.Nh, R_HCA,
-                         pos0, self.scale, self.out_csa, self.lse_csa, self.out_hca,
-                         self.lse_hca, k_scales=st.Ics, workspace=self.ws_step, stream=stream,
-                         mx_fp8=self.mx_fp8)
+        args = (st.pool_jobs(pos0, pos0 + self.Nq), q_idx, w_idx, st.Ic, self.score_code,
+                self.idx, q, st.Kc, st.Vc, st.Nc, self.topk, st.K_raw, st.V_raw, 0, self.n_win,
+                R_CSA, st.Kh, st.Vh, st.Nh, R_HCA, pos0, self.scale, self.out_csa,
+                self.lse_csa, self.out_hca, self.lse_hca)
+        if noalloc:
+            hcsa.decode_step_noalloc(*args, k_scales=st.Ics, stream=stream, mx_fp8=self.mx_fp8)
+        else:
+            hcsa.decode_step(*args, k_scales=st.Ics, workspace=self.ws_step, stream=stream,
+                             mx_fp8=self.mx_fp8)
         return self.idx, (self.out_csa, self.lse_csa), (self.out_hca, self.lse_hca)
 
     def run_attend(self, q, pos0, stream=None):
