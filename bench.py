@@ -140,19 +140,21 @@ def cpu_baseline(cfg, st, om, q, qi, wi, seconds, gpu_idx=None):
     Ic_exact = O.compress(I[: p + 1], omd["idx_k"], 4)
     Ic = O.mxfp4_roundtrip(Ic_exact) if cfg.idx == "mxfp4" else O.round_to(Ic_exact, cfg.idx)
     qv, qiv, wiv = f(q[0, 0]), f(qi[0, 0]), f(wi[0, 0])
+    c0 = 4 * (Kc.shape[0] - 1)                 # tokens of the last completed entries
+    h0 = 128 * (Kh.shape[0] - 1)
 
     def query():
-        Kc[-1] = O.round_to(O.compress(K[p - 3: p + 1], omd["csa_k"], 4), cfg.kv)[0]
-        Vc[-1] = O.round_to(O.compress(V[p - 3: p + 1], omd["csa_v"], 4), cfg.kv)[0]
-        ic = O.compress(I[p - 3: p + 1], omd["idx_k"], 4)
+        Kc[-1] = O.round_to(O.compress(K[c0: c0 + 4], omd["csa_k"], 4), cfg.kv)[0]
+        Vc[-1] = O.round_to(O.compress(V[c0: c0 + 4], omd["csa_v"], 4), cfg.kv)[0]
+        ic = O.compress(I[c0: c0 + 4], omd["idx_k"], 4)
         qq = qiv
         if cfg.idx == "mxfp4":
             Ic[-1] = O.mxfp4_roundtrip(ic)[0]
             qq = O.mxfp4_roundtrip(qiv)
         else:
             Ic[-1] = O.round_to(ic, cfg.idx)[0]
-        Kh[-1] = O.round_to(O.compress(K[p - 127: p + 1], omd["hca_k"], 128), cfg.kv)[0]
-        Vh[-1] = O.round_to(O.compress(V[p - 127: p + 1], omd["hca_v"], 128), cfg.kv)[0]
+        Kh[-1] = O.round_to(O.compress(K[h0: h0 + 128], omd["hca_k"], 128), cfg.kv)[0]
+        Vh[-1] = O.round_to(O.compress(V[h0: h0 + 128], omd["hca_v"], 128), cfg.kv)[0]
         return O.decode_query(qv, qq, wiv, Kc, Vc, Ic, K, V, 0, Kh, Vh, p, cfg.topk, cfg.n_win,
                               cfg.scale, cfg.score)
 
@@ -171,8 +173,10 @@ def cpu_baseline(cfg, st, om, q, qi, wi, seconds, gpu_idx=None):
     with threadpool_limits(limits=1):
         one, n1, el1 = rate(seconds / 2)
     host, model = _host_cpus()
-    out = {"value": value, "unit": "decode queries/s", "cores": threads, "kind": "oracle",
-           "sample": f"{n} decode queries of sequence 0 (p={p}, full context) through the "
+    what = "decode queries" if cfg.Nq == 1 else "prefill query tokens (the chunk's first)"
+    unit = "decode queries/s" if cfg.Nq == 1 else "prefill query tokens/s"
+    out = {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": f"{n} {what} of sequence 0 (p={p}, full context) through the "
                      f"float64 numpy oracle, {el:.1f} s ({threads} BLAS threads); caches "
                      f"pooled untimed",
            "single_core_value": one, "single_core_sample": f"{n1} queries, {el1:.1f} s",

@@ -18,7 +18,9 @@ namespace hcsa {
 
 namespace {
 
-// KS: 64-channel MFMA steps the kernels hold registers for (d_I <= 64: one).
+// KS: 64-channel MFMA steps the kernels hold registers for (d_I <= 64: one).  The FP8 form
+// holds two: at 108 registers (4 waves per SIMD) its candidate scan took 71-74 us at batch 32
+// x 1M tokens, against 80-81 us with one (72 registers, 7 waves), on the same box.
 template <int HI, int KS, bool QBF16, bool F8>
 hipError_t launch_mx_mfma_ks(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
   const int nchunks = (A.N + A.chunk - 1) / A.chunk;
@@ -34,7 +36,7 @@ hipError_t launch_mx_mfma_ks(const IdxMxDev& A, int rows, int score_dtype, hipSt
 
 template <int HI, bool QBF16, bool F8>
 hipError_t launch_mx_mfma_hi(const IdxMxDev& A, int rows, int score_dtype, hipStream_t s) {
-  if (A.d_I > 64) return launch_mx_mfma_ks<HI, 2, QBF16, F8>(A, rows, score_dtype, s);
+  if (A.d_I > 64 || F8) return launch_mx_mfma_ks<HI, 2, QBF16, F8>(A, rows, score_dtype, s);
   return launch_mx_mfma_ks<HI, 1, QBF16, F8>(A, rows, score_dtype, s);
 }
 

@@ -63,7 +63,7 @@ hipError_t launch_mx_topk_ks(const IdxMxDev& A, int rows, int k, int32_t* idx,
 template <int HI, bool QBF16, bool F8, bool PAGED>
 hipError_t launch_mx_topk_hi(const IdxMxDev& A, int rows, int k, int32_t* idx,
                              const PoolJobs* pool, int pool_blocks_n, int B, hipStream_t s) {
-  if (A.d_I > 64)
+  if (A.d_I > 64 || F8)   // FP8: two register steps (see launch_mx_mfma_hi)
     return launch_mx_topk_ks<HI, 2, QBF16, F8, PAGED>(A, rows, k, idx, pool, pool_blocks_n, B, s);
   return launch_mx_topk_ks<HI, 1, QBF16, F8, PAGED>(A, rows, k, idx, pool, pool_blocks_n, B, s);
 }
