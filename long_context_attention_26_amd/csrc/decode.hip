@@ -11,8 +11,9 @@
 // splits differ from hcsa_csa_hca_attn's, so its outputs agree up to the rounding of the
 // split sums.
 //
-//  1. front: the per-row selection floors (one 512-thread block per row, sampling only
-//     entries completed before the step) and the pooling of the blocks the step completes.
+//  1. front: the per-row selection floors (kMxFloorParts 512-thread blocks per row, each
+//     scoring a quarter of the samples, taken only from entries completed before the step)
+//     and the pooling of the blocks the step completes.
 //  2. the MXFP4 key scan writing per-chunk candidate lists (the indexer's own launch).
 //  3. back: one block per row resolves the row's top-k among its candidates and then runs
 //     the row's CSA attention over it and the window with all 8 waves (the row's final
@@ -46,18 +47,19 @@ struct StepDev {
   uint32_t* hca_next;  // next HCA unit of the back launch (zeroed by the front launch)
 };
 
-// grid: rows + B * pool_blocks; block 512.
+// grid: rows * kMxFloorParts + B * pool_blocks; block 512.
 template <int HI, int KS>
 __global__ __launch_bounds__(kStepThreads) void step_front_kernel(StepDev S) {
   __shared__ float alpha[1024];
   __shared__ float s_part[kStepThreads * 8];
   const int bx = blockIdx.x;
   if (bx == 0 && threadIdx.x == 0) *S.hca_next = 0u;   // the back launch's unit counter
-  if (bx < S.rows) {
-    mx_floor_block<HI, KS, true, false, false>(S.X, S.k, bx, true);
+  if (bx < S.rows * kMxFloorParts) {
+    mx_floor_block<HI, KS, true, false, false>(S.X, S.k, bx / kMxFloorParts,
+                                               bx % kMxFloorParts, true);
     return;
   }
-  const int b2 = bx - S.rows;
+  const int b2 = bx - S.rows * kMxFloorParts;
   pool_jobs_block<false>(S.J, b2 % S.pool_blocks, alpha, s_part, b2 / S.pool_blocks);
 }
 
@@ -139,8 +141,8 @@ static int device_cus() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cached[dev] == 0) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
+    const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n < 1) n = 256;
     cached[dev] = n;
   }
   return cached[dev];
@@ -213,7 +215,7 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const
                                : 0;
   S.hca_units = rows * ph.splits;
   S.hca_next = reinterpret_cast<uint32_t*>(base + sync_off);
-  const int front = rows + a.B * S.pool_blocks;
+  const int front = rows * kMxFloorParts + a.B * S.pool_blocks;
   const int back = rows + std::min(step_hca_workers(rows), (S.hca_units + 1) / 2);
   hipError_t e = hipErrorInvalidValue;
   const bool ks2 = a.d_I > 64;
@@ -232,5 +234,6 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const
   if (gy > 0) step_merge_kernel<<<dim3(a.c.H, gy), a.c.d, 0, s>>>(mc, mh, a.c.H, a.c.d);
   return hipGetLastError();
 }
+
 
 }  // namespace hcsa

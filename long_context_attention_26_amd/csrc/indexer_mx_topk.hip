@@ -18,24 +18,29 @@ namespace hcsa {
 
 namespace {
 
-// grid: rows; block 512.
+// grid: rows * kMxFloorParts (the parts of a row adjacent); block 512.
 template <int HI, int KS, bool QBF16, bool PAGED, bool F8>
 __global__ __launch_bounds__(kMxFloorThreads) void mx_floor_kernel(IdxMxDev A, int k) {
-  mx_floor_block<HI, KS, QBF16, PAGED, F8>(A, k, blockIdx.x, false);
+  mx_floor_block<HI, KS, QBF16, PAGED, F8>(A, k, blockIdx.x / kMxFloorParts,
+                                           blockIdx.x % kMxFloorParts, false);
 }
 
-// The floors and the pooling of the same tokens in one launch: blocks x < Nq of grid row y
-// set the floor of query row y*Nq + x (sampling only entries completed before the call),
-// the rest run the pooling jobs (sequence y).  grid: (Nq + pooling blocks, B); block 512.
+// The floors and the pooling of the same tokens in one launch: blocks x < Nq * parts of
+// grid row y set part x % parts of the floor of query row y*Nq + x / parts (sampling only
+// entries completed before the call), the rest run the pooling jobs (sequence y).
+// grid: (Nq * parts + pooling blocks, B); block 512.
 template <int HI, int KS, bool QBF16, bool PAGED, bool F8>
 __global__ __launch_bounds__(kMxFloorThreads) void mx_pool_floor_kernel(PoolJobs J, IdxMxDev A,
                                                                         int k) {
   __shared__ float alpha[1024];
   __shared__ float s_part[kMxFloorThreads * 8];
-  if (static_cast<int>(blockIdx.x) < A.Nq)
-    mx_floor_block<HI, KS, QBF16, PAGED, F8>(A, k, blockIdx.y * A.Nq + blockIdx.x, true);
+  const int nf = A.Nq * kMxFloorParts;
+  if (static_cast<int>(blockIdx.x) < nf)
+    mx_floor_block<HI, KS, QBF16, PAGED, F8>(A, k,
+                                             blockIdx.y * A.Nq + blockIdx.x / kMxFloorParts,
+                                             blockIdx.x % kMxFloorParts, true);
   else
-    pool_jobs_block<PAGED>(J, blockIdx.x - A.Nq, alpha, s_part, blockIdx.y);
+    pool_jobs_block<PAGED>(J, blockIdx.x - nf, alpha, s_part, blockIdx.y);
 }
 
 // grid: rows; block 512.
@@ -51,9 +56,10 @@ hipError_t launch_mx_topk_ks(const IdxMxDev& A, int rows, int k, int32_t* idx,
                              const PoolJobs* pool, int pool_blocks_n, int B, hipStream_t s) {
   if (pool && pool_blocks_n > 0)
     mx_pool_floor_kernel<HI, KS, QBF16, PAGED, F8>
-        <<<dim3(A.Nq + pool_blocks_n, B), kMxFloorThreads, 0, s>>>(*pool, A, k);
+        <<<dim3(A.Nq * kMxFloorParts + pool_blocks_n, B), kMxFloorThreads, 0, s>>>(*pool, A, k);
   else
-    mx_floor_kernel<HI, KS, QBF16, PAGED, F8><<<rows, kMxFloorThreads, 0, s>>>(A, k);
+    mx_floor_kernel<HI, KS, QBF16, PAGED, F8>
+        <<<rows * kMxFloorParts, kMxFloorThreads, 0, s>>>(A, k);
   launch_timed(index_scores_mx_mfma_kernel<HI, KS, QBF16, true, PAGED, F8, true>,
                dim3(A.nchunks, rows), dim3(256), s, A);
   mx_list_resolve_kernel<HI, KS, QBF16, PAGED, F8><<<rows, kMxResThreads, 0, s>>>(A, k, idx);

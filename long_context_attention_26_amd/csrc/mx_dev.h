@@ -48,7 +48,7 @@ struct IdxMxDev {
   void* scores;        // scores [rows][N]; the fused selection's rescan rows
   int chunk;
   // fused selection (candidate lists instead of scores)
-  uint32_t* floor;     // [rows] 16-bit key floor of each row
+  uint32_t* floor;     // [rows][kMxFloorParts] 16-bit key floors (the row's: their minimum)
   uint32_t* lists;     // [rows][nchunks][chunk] (key << 16 | index in the chunk)
   uint32_t* counts;    // [rows][nchunks]
   int nchunks;
@@ -273,32 +273,40 @@ constexpr int kMxFloorThreads = 512;
 constexpr int kMxFloorRuns = 32;          // sampled runs of consecutive keys
 constexpr int kMxRunKeys = 128;
 constexpr int kMxSamples = kMxFloorRuns * kMxRunKeys;
+constexpr int kMxFloorParts = 4;          // blocks per row, each scoring a share of the runs
+constexpr int kMxPartSamples = kMxSamples / kMxFloorParts;
 constexpr int kMxResThreads = 512;
 constexpr int kMxResPer = 32;
 constexpr int kMxResMax = kMxResThreads * kMxResPer;
 constexpr int kMxMaxChunks = 4096;
 
-// grid: rows; block 512.  Scores 32 runs of 128 consecutive visible keys at evenly spaced
-// positions and sets the row's floor: the 16-bit key of about the m-th largest sample, m
-// about twice the rank at which the k-th largest key is expected (only the candidate count
-// depends on it).  For shallow ranks it is the m-th largest of the 512 per-thread maxima
-// (8 consecutive samples each), which is at or below the m-th largest sample, found exactly
-// by one wave (radix 4 from the top, ballot counts); deeper ranks count every sample, each
-// wave its own ceil(m/W)-th, and take the smallest of the W.  Rows of at most 4096 visible
-// keys take every key (floor 0).  All sample loads are issued before the query is
-// quantized.
+// One of a row's kMxFloorParts floor blocks (block 512).  The row's samples are 32 runs of
+// 128 consecutive visible keys at evenly spaced positions; part p scores runs 8p .. 8p+7
+// and stores the 16-bit key of about its m_p-th largest sample, m_p = ceil(m / parts) and m
+// about twice the rank at which the k-th largest key is expected among the 4096 samples.
+// The row's floor is the second smallest of the parts' values (mx_row_floor).  Only the
+// candidate count depends on the floor (a row left with fewer than k candidates is
+// rescanned).  Rank statistics of 4 parts of 1024 samples at k = 1024 of 262 144 keys put
+// the floor at rank 2 747 on average (p99 4 093) against 2 557 (p99 3 595) for the m-th
+// largest of all 4096 samples, and below rank k in none of 200 000 rows; the smallest part
+// value would admit 3 421 on average (p99 5 385).  Within a part: for shallow ranks the
+// m_p-th largest of the 512 per-thread maxima, found exactly by one wave (radix 4 from the
+// top, ballot counts); deeper ranks count every sample, each wave its own ceil(m_p/W)-th,
+// and take the smallest of the W.
+// Rows of at most 4096 visible keys take every key (floor 0).  All sample loads are issued
+// before the query is quantized.
 //
 // prior_only: sample only the entries completed before the sequence's first query token
 // (those a pooling launch of the same tokens does not write), for the fused pooling launch.
-// One 512-thread block; called by every thread.
+// Called by every thread of the block.
 template <int HI, int KS, bool QBF16, bool PAGED, bool F8>
-__device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row,
+__device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row, int part,
                                                bool prior_only) {
   constexpr int W = kMxFloorThreads / 64;
-  constexpr int PT = kMxSamples / kMxFloorThreads;      // samples per thread
+  constexpr int PT = kMxPartSamples / kMxFloorThreads;  // samples per thread
   __shared__ uint32_t s_qa[kMxMaxUnits][4];
   __shared__ int s_qs[kMxMaxUnits];
-  __shared__ uint16_t s_samp[kMxSamples];
+  __shared__ uint16_t s_samp[kMxPartSamples];
   __shared__ uint32_t s_gmax[kMxFloorThreads];
   __shared__ uint32_t s_min[W];
   const int b = row / A.Nq;
@@ -310,8 +318,9 @@ __device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row
     const int64_t e0 = query_pos(A.seq_pos, A.pos0, b, 0) / A.ratio;
     ns = static_cast<int>(e0 < nv ? e0 : nv);
   }
+  uint32_t* floor_out = A.floor + row * kMxFloorParts + part;
   if (k >= nv || ns <= kMxSamples) {
-    if (threadIdx.x == 0) A.floor[row] = 0u;
+    if (threadIdx.x == 0) *floor_out = 0u;
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -319,13 +328,16 @@ __device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row
   const int ksteps = A.d_I > 64 ? A.d_I / 64 : 1;
   const uint8_t* kbase = PAGED ? A.k : A.k + b * A.k_bstride;
   const uint8_t* sbase = PAGED ? A.ks : A.ks + b * A.ks_bstride;
-  // wave w scores runs RPW*w .. RPW*w + RPW-1: NG groups of 32 keys, all loads in flight
-  constexpr int RPW = kMxFloorRuns / W, GPR = kMxRunKeys / 32, NG = RPW * GPR;
+  // wave w scores the part's runs RPW*w .. RPW*w + RPW-1: NG groups of 32 keys, all loads
+  // in flight
+  constexpr int RPP = kMxFloorRuns / kMxFloorParts;    // runs per part
+  constexpr int RPW = RPP / W, GPR = kMxRunKeys / 32, NG = RPW * GPR;
+  static_assert(RPW >= 1 && RPW * W == RPP, "whole runs per wave");
   u32x4 kraw[NG][KS];
   int ksc[NG][KS];
 #pragma unroll
   for (int u = 0; u < NG; ++u) {
-    const int run = wave * RPW + u / GPR;
+    const int run = part * RPP + wave * RPW + u / GPR;
     const int r0 = static_cast<int>(static_cast<int64_t>(run) * (ns - kMxRunKeys) /
                                     (kMxFloorRuns - 1));
     mx_load<KS, PAGED, F8>(A, kbase, sbase, b, r0 + (u % GPR) * 32 + col, true, kraw[u], ksc[u]);
@@ -333,17 +345,18 @@ __device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row
   const MxQuery<HI, KS> Q = mx_query<HI, KS, QBF16, F8>(A, row, s_qa, s_qs);
 #pragma unroll
   for (int u = 0; u < NG; ++u) {
-    const int run = wave * RPW + u / GPR;
+    const int lrun = wave * RPW + u / GPR;             // run within the part
     const float s = mx_score<HI, KS, F8>(Q, kraw[u], ksc[u], ksteps);
     if (half == 0)
-      s_samp[run * kMxRunKeys + (u % GPR) * 32 + col] =
+      s_samp[lrun * kMxRunKeys + (u % GPR) * 32 + col] =
           static_cast<uint16_t>(bf16_key(f32_to_bf16_bits(s)));
   }
   __syncthreads();
   uint32_t top[PT];
 #pragma unroll
   for (int e = 0; e < PT; ++e) top[e] = s_samp[threadIdx.x * PT + e];
-  const int m = min(kMxSamples - 8, static_cast<int>((2LL * k * kMxSamples + nv - 1) / nv) + 8);
+  const int m_all = min(kMxSamples - 8, static_cast<int>((2LL * k * kMxSamples + nv - 1) / nv) + 8);
+  const int m = (m_all + kMxFloorParts - 1) / kMxFloorParts;
   if (m <= 64) {
     uint32_t mx = 0;
 #pragma unroll
@@ -370,7 +383,7 @@ __device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row
         const uint32_t d = cnt[2] >= m ? 3u : cnt[1] >= m ? 2u : cnt[0] >= m ? 1u : 0u;
         pre |= d << sh;
       }
-      if (lane == 0) A.floor[row] = pre;
+      if (lane == 0) *floor_out = pre;
     }
     return;
   }
@@ -394,7 +407,16 @@ __device__ __forceinline__ void mx_floor_block(const IdxMxDev& A, int k, int row
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < W; ++u) pre = min(pre, s_min[u]);
-  if (threadIdx.x == 0) A.floor[row] = pre;
+  if (threadIdx.x == 0) *floor_out = pre;
+}
+
+// The row's floor: the second smallest of its parts' values.
+__device__ __forceinline__ uint32_t mx_row_floor(const IdxMxDev& A, int row) {
+  static_assert(kMxFloorParts == 4, "one 16-byte load");
+  const u32x4 f = *reinterpret_cast<const u32x4*>(A.floor + row * kMxFloorParts);
+  const uint32_t lo01 = min(f[0], f[1]), hi01 = max(f[0], f[1]);
+  const uint32_t lo23 = min(f[2], f[3]), hi23 = max(f[2], f[3]);
+  return min(max(lo01, lo23), min(hi01, hi23));
 }
 
 // The exact threshold among the row's C candidates (the concatenated chunk lists, prefix
@@ -429,8 +451,8 @@ __device__ __forceinline__ void mx_resolve_lists(const IdxMxDev& A, int row, int
       cj[u] = c * A.chunk + static_cast<int>(v & 0xffffu);
     }
   }
-  sel::select_candidates<16, kMxResThreads, PER, COH>(ck, cj, my, A.floor[row], k, out, s_gt, s_eq,
-                                                 s_hb, s_hist, s_sel);
+  sel::select_candidates<16, kMxResThreads, PER, COH>(ck, cj, my, mx_row_floor(A, row), k, out,
+                                                      s_gt, s_eq, s_hb, s_hist, s_sel);
 }
 
 // The selection of one row by a 512-thread block: the row's candidates are the
@@ -489,8 +511,8 @@ __device__ __forceinline__ void mx_resolve_row(const IdxMxDev& A, int k, int32_t
         ck[u] = u < my ? v >> 16 : 0u;
         cj[u] = u < my ? c * A.chunk + static_cast<int>(v & 0xffffu) : 0;
       }
-      sel::select_candidates<16, kMxResThreads, 16, COH>(ck, cj, my, A.floor[row], k, out, s_gt,
-                                                    s_eq, s_hb, s_hist, s_sel);
+      sel::select_candidates<16, kMxResThreads, 16, COH>(ck, cj, my, mx_row_floor(A, row), k,
+                                                         out, s_gt, s_eq, s_hb, s_hist, s_sel);
       return;
     }
   }
@@ -584,7 +606,7 @@ inline MxTopkLayout mx_topk_layout(int rows, int N) {
   const int chunk = std::min(index_chunk(rows, N), 2048);
   const int64_t nchunks = (N + chunk - 1) / chunk;
   MxTopkLayout l;
-  l.counts_off = align256(static_cast<size_t>(rows) * 4);
+  l.counts_off = align256(static_cast<size_t>(rows) * kMxFloorParts * 4);   // floors first
   l.lists_off = l.counts_off + align256(static_cast<size_t>(rows) * nchunks * 4);
   l.scores_off = l.lists_off + align256(static_cast<size_t>(rows) * nchunks * chunk * 4);
   l.total = l.scores_off + align256(static_cast<size_t>(rows) * N * 2);

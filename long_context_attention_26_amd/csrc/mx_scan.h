@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void index_scores_mx_mfma_kernel(IdxMxDev A) {
   __shared__ int s_cnt[CAND ? 64 : 1], s_off[CAND ? 64 : 1];
   uint32_t L = 0;
   if constexpr (CAND) {
-    L = A.floor[row];
+    L = mx_row_floor(A, row);
     if (threadIdx.x < 64) s_cnt[threadIdx.x] = 0;   // ordered by the barrier in mx_query
   }
   const MxQuery<HI, KS> Q = mx_query<HI, KS, QBF16, F8>(A, row, s_qa, s_qs);
