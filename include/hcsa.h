@@ -343,9 +343,9 @@ int hcsa_csa_hca_attn(const void *q, const void *kc, const void *vc, int64_t c_b
  * For one query token per sequence with MXFP4 keys (fp4 operands), bf16 queries and scores,
  * the selection without a score array, bf16 16 x 128 attention, contiguous caches and
  * k + n_win <= 4096, the step runs in four launches: the per-row selection floors beside the
- * pooling; the key scan; one block per row resolving its top-k and then attending over it
- * and its window (CSA), beside the HCA splits on the other compute units; the HCA split
- * merge.  The pooled caches and the selection equal those of the two calls bit for bit; the
+ * pooling; the key scan; two blocks per row each resolving the row's top-k and then
+ * attending over half of its CSA key list, beside the HCA splits on the other compute
+ * units; the merge of the CSA and HCA splits.  The pooled caches and the selection equal those of the two calls bit for bit; the
  * attention outputs are split differently and agree with theirs up to the rounding of the
  * split sums (the softmax probabilities enter P.V as bf16, rounded relative to each split's
  * running maximum).  Other shapes run the two calls' kernels in turn, with their results.

@@ -15,11 +15,12 @@
 //     scoring a quarter of the samples, taken only from entries completed before the step)
 //     and the pooling of the blocks the step completes.
 //  2. the MXFP4 key scan writing per-chunk candidate lists (the indexer's own launch).
-//  3. back: one block per row resolves the row's top-k among its candidates and then runs
-//     the row's CSA attention over it and the window with all 8 waves (the row's final
-//     output), so the selection never crosses blocks; the HCA splits run as 4-wave units,
-//     two per block, on the other CUs, taken from a counter until none is left.
-//  4. the log-sum-exp merge of the HCA splits.
+//  3. back: kRowParts blocks per row each resolve the row's top-k among its candidates (the
+//     same deterministic selection, so it never crosses blocks) and then run the CSA
+//     attention over their split of the row's key list (selected entries and window) with
+//     all 8 waves; the HCA splits run as 4-wave units, two per block, on the other CUs,
+//     taken from a counter until none is left.
+//  4. the log-sum-exp merge of the CSA and the HCA splits.
 #include "attn_dev.h"
 #include "internal.h"
 #include "mx_dev.h"
@@ -35,6 +36,7 @@ namespace {
 using namespace attn;
 
 constexpr int kStepThreads = 512;        // two 256-thread attention units per block
+constexpr int kRowParts = 2;             // blocks per query row in the back launch
 
 struct StepDev {
   IdxMxDev X;          // indexer: floors, candidate lists, rescan rows
@@ -63,11 +65,11 @@ __global__ __launch_bounds__(kStepThreads) void step_front_kernel(StepDev S) {
   pool_jobs_block<false>(S.J, b2 % S.pool_blocks, alpha, s_part, b2 / S.pool_blocks);
 }
 
-// grid: rows + HCA workers; block 512.  Blocks below rows: the row's resolve, then its CSA
-// attention over the whole key list by all 8 waves (the row's final output; the selection
-// never leaves the block); the rest take pairs of HCA units (one per 4-wave half) from a
-// counter until none is left.  Which block computes a unit does not change its result, so
-// the outputs do not depend on the order the units are taken in.
+// grid: rows * kRowParts + HCA workers; block 512.  Blocks below rows * kRowParts: the
+// row's resolve, then the CSA attention over split `part` of its key list by all 8 waves;
+// the rest take pairs of HCA units (one per 4-wave half) from a counter until none is
+// left.  Which block computes a unit does not change its result, so the outputs do not
+// depend on the order the units are taken in.
 template <int HI, int KS>
 __global__ __launch_bounds__(kStepThreads) void step_back_kernel(StepDev S) {
   __shared__ int s_code[kMfmaMaxChunk];
@@ -75,14 +77,18 @@ __global__ __launch_bounds__(kStepThreads) void step_back_kernel(StepDev S) {
   __shared__ float s_ml[8][2][16];
   __shared__ int s_next;
   const int bx = blockIdx.x;
-  if (bx < S.rows) {
-    mx_resolve_row<HI, KS, true, false, false, false>(S.X, S.k, S.idx, bx);
-    const RowKeys r = row_keys<true>(S.C, bx);
+  if (bx < S.rows * kRowParts) {
+    // every part of a row runs the row's (deterministic) resolve, so each holds the same
+    // selection without waiting for another block, then attends over its split of the list
+    const int row = bx / kRowParts, part = bx % kRowParts;
+    mx_resolve_row<HI, KS, true, false, false, false>(S.X, S.k, S.idx, row);
+    const RowKeys r = row_keys<true>(S.C, row);
     Row8State st;
-    row8_init(S.C, bx, st);
+    row8_init(S.C, row, st);
     // (csa_range8 begins with a barrier: the selection is then visible to the block)
-    csa_range8<false>(S.C, r, bx, 0, r.L, s_code, st.qB, st.acc, st.m_run, st.l_run, st.sl2);
-    combine_waves<8>(S.C, st.acc, st.m_run, st.l_run, s_o, s_ml, 0, bx, threadIdx.x);
+    const int p0 = part * S.C.chunk, p1 = min(r.L, p0 + S.C.chunk);
+    csa_range8<false>(S.C, r, row, p0, p1, s_code, st.qB, st.acc, st.m_run, st.l_run, st.sl2);
+    combine_waves<8>(S.C, st.acc, st.m_run, st.l_run, s_o, s_ml, part, row, threadIdx.x);
     return;
   }
   const int half = threadIdx.x >> 8, tid = threadIdx.x & 255;
@@ -155,13 +161,15 @@ static int device_cus() {
 // rounding of the split sums.
 AttnPlan plan_step_csa(int B, int Nq, int H, int d, int k, int n_win) {
   AttnPlan p = plan_attention(true, HCSA_BF16, B, Nq, H, d, k + n_win);
-  p.chunk = std::max(k + n_win, 1);
-  p.splits = 1;
-  p.part_bytes = p.total_bytes = 0;
+  // one split per block of the row
+  p.chunk = std::max((k + n_win + kRowParts - 1) / kRowParts, 1);
+  p.splits = kRowParts;
+  p.part_bytes = p.total_bytes = align256(static_cast<size_t>(kRowParts) * p.rows * H * d * 4) +
+                                 align256(static_cast<size_t>(kRowParts) * p.rows * H * 4);
   return p;
 }
 
-static int step_hca_workers(int rows) { return std::max(1, device_cus() - rows); }
+static int step_hca_workers(int rows) { return std::max(1, device_cus() - kRowParts * rows); }
 
 AttnPlan plan_step_hca(int B, int Nq, int H, int d, int N_h) {
   AttnPlan p = plan_attention(false, HCSA_BF16, B, Nq, H, d, N_h);
@@ -216,7 +224,7 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const
   S.hca_units = rows * ph.splits;
   S.hca_next = reinterpret_cast<uint32_t*>(base + sync_off);
   const int front = rows * kMxFloorParts + a.B * S.pool_blocks;
-  const int back = rows + std::min(step_hca_workers(rows), (S.hca_units + 1) / 2);
+  const int back = kRowParts * rows + std::min(step_hca_workers(rows), (S.hca_units + 1) / 2);
   hipError_t e = hipErrorInvalidValue;
   const bool ks2 = a.d_I > 64;
 #define HCSA_STEP(HI_)                                                              \

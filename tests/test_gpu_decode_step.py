@@ -1,5 +1,5 @@
 """One decode step as one call (hcsa_decode_step: floors and pooling in one launch; the key
-scan; per-row resolve + CSA blocks beside the HCA splits in one launch; the HCA merge) against
+scan; per-row resolve + CSA blocks beside the HCA splits in one launch; the split merge) against
 the same step as two calls (hcsa_csa_pool_index_topk, then hcsa_csa_hca_attn): pooled caches
 and selection equal bit for bit; both attentions, split differently in the four-launch
 form, within the bound that their bf16 probabilities allow between two split plans.  Both
