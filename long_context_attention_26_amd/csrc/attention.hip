@@ -166,6 +166,15 @@ constexpr int kHKeys = 64;                // entries per tile (two MFMA tiles)
 constexpr int kKPitch = 128 + 8;          // K tile row pitch (elements): no bank conflicts
 constexpr int kVPitch = kHKeys + 8;       // V^T tile row pitch (elements)
 
+// Entry e of V^T row (channel) ch sits at e ^ vt_swizzle(ch) within the row.  The XOR moves
+// whole 8-entry groups, so the P.V reads (two aligned runs of four entries) stay contiguous;
+// it spreads the transposing writes, whose 16 channel groups would otherwise all fall on
+// one bank (8 x 36 dwords is a multiple of the bank count), over all banks, and keeps the
+// reads free of conflicts, with 32 banks of 4 bytes and with 64.
+__device__ __forceinline__ int vt_swizzle(int ch) {
+  return 8 * (((ch >> 3) & 1) ^ ((ch >> 4) & 7));
+}
+
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16a;
 
 __device__ __forceinline__ f32x16a mfma32x32x16(const u32x4& a, const u32x4& b, f32x16a c) {
@@ -223,6 +232,7 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
                        : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  const int e_st = (2 * lkey) ^ vt_swizzle(8 * lpart);   // the same for all 8 channels
   auto stash = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -231,8 +241,8 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
     for (int c = 0; c < 4; ++c) {                 // channel 8*lpart + 2c (+1): entries 2*lkey, +1
       const uint32_t lo = (vf[0][c] & 0xffffu) | (vf[1][c] << 16);
       const uint32_t hi = (vf[0][c] >> 16) | (vf[1][c] & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * lpart + 2 * c) * kVPitch + 2 * lkey]) = lo;
-      *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * lpart + 2 * c + 1) * kVPitch + 2 * lkey]) = hi;
+      *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * lpart + 2 * c) * kVPitch + e_st]) = lo;
+      *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * lpart + 2 * c + 1) * kVPitch + e_st]) = hi;
     }
   };
 
@@ -297,11 +307,13 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
       // O^T tiles: A = V^T rows (channel 32ct + col), entries 32h + 16s + 4hh + 0..3 and +8
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
+        const int ch = 32 * ct + col, sw = vt_swizzle(ch);
+        const uint16_t* vrow = &s_vt[buf][ch * kVPitch];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const uint16_t* vr = &s_vt[buf][(32 * ct + col) * kVPitch + 32 * h2 + 16 * s + 4 * hh];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+          const int e = 32 * h2 + 16 * s + 4 * hh;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (e ^ sw));
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + ((e + 8) ^ sw));
           acc[ct] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[s], acc[ct]);
         }
       }
