@@ -298,7 +298,8 @@ def train_backward(args):
     ws_hb = hcsa.alloc_workspace(
         hcsa.lib.hcsa_hca_dense_attn_bwd_workspace_size(1, HALF, Hh, d, hcsa.BF16), dev)
     ws_cb = hcsa.alloc_workspace(
-        hcsa.lib.hcsa_csa_sparse_attn_bwd_workspace_size(1, HALF, Hh, d, hcsa.BF16), dev)
+        hcsa.lib.hcsa_csa_sparse_attn_bwd_workspace_size(1, HALF, Hh, d, hcsa.BF16, Nc, k),
+        dev)
 
     stages = ["zero", "csa_bwd", "hca_bwd", "pool_bwd"]
 

@@ -412,13 +412,19 @@ int hcsa_decode_step_noalloc(const hcsa_pool_job *jobs, int n_jobs, const void *
  * The accumulations use floating-point atomics: their order, and the last bits of the
  * accumulated gradients, can differ between runs; dq is deterministic.
  * Limits: the forward's, and H <= 64/c with c = 1, 2, 4 for d <= 64, 128, 256 (H counted
- * rounded up to 4, 16, 32 or 64).  Workspace: hcsa_csa_sparse_attn_bwd_workspace_size or
- * hcsa_hca_dense_attn_bwd_workspace_size bytes, 256-byte aligned (zero bytes, and NULL
- * allowed, except for bf16 16 x 128 with 16 or more query tokens, where the keys shared by
- * consecutive tokens -- HCA entries, CSA window rows -- get their gradients key-major, one
- * block per 16 keys and 128 tokens; with a NULL workspace they stay query-major).
+ * rounded up to 4, 16, 32 or 64).  Workspace: hcsa_csa_sparse_attn_bwd_workspace_size
+ * (the call's B, Nq, H, d, kv_dtype, N and k) or hcsa_hca_dense_attn_bwd_workspace_size
+ * bytes, 256-byte aligned (zero bytes, and NULL allowed, except for bf16 16 x 128 with 16
+ * or more query tokens, where the keys shared by consecutive tokens -- HCA entries, CSA
+ * window rows -- get their gradients key-major, one block per 16 keys and 128 tokens, and
+ * the CSA selected entries key-major by tiles of 128 entries: each row's selections are
+ * sorted by tile, the pairs' probabilities and dS are kept in the workspace (64 bytes per
+ * selected pair: about B * Nq * k * 64 bytes in all), and each tile's gradients are summed
+ * over 4096 tokens before they are added; with a NULL workspace all of them stay
+ * query-major).
  */
-size_t hcsa_csa_sparse_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype);
+size_t hcsa_csa_sparse_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype,
+                                               int N, int k);
 int hcsa_csa_sparse_attn_bwd(const void *q, const void *kc, const void *vc, int64_t c_bstride,
                              int N, const int32_t *topk_idx, int k, const void *k_raw,
                              const void *v_raw, int64_t raw_bstride, int64_t T_raw,

@@ -728,10 +728,12 @@ static int check_bwd_grads(const float* dout, const float* dq, int B, int Nq, in
   return HCSA_OK;
 }
 
-size_t hcsa_csa_sparse_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype) {
+size_t hcsa_csa_sparse_attn_bwd_workspace_size(int B, int Nq, int H, int d, int kv_dtype, int N,
+                                                int k) {
   if (B < 1 || Nq < 1 || H < 1 || d < 1) return 0;
   hcsa::AttnArgs a{};
   a.B = B; a.Nq = Nq; a.H = H; a.d = d; a.kv_dtype = kv_dtype;
+  a.N = N > 0 ? N : 0; a.k = k > 0 ? k : 0;
   return hcsa::bwd_workspace_bytes(a);
 }
 

@@ -48,6 +48,14 @@ struct AttnBwdDev {
   int64_t dr_bstride;
   float* dt_out;         // [rows][16] or null: dout.o - dlse per head, for the key-major pass
   const uint16_t* dout16;  // [rows][16][128] bf16 copy of dout for the key-major pass, or null
+  // CSA selected entries key-major (else null): the dq pass stores each valid (row, position)
+  // pair's P and dS per head, bf16, at rec[row][slot[row][position]] (16 words: P pairs of
+  // heads 2m, 2m + 1 in words m, dS pairs in words 8 + m)
+  const uint16_t* slot;  // [rows][k]
+  uint32_t* rec;         // [rows][k][16]
+  // with the records: rows listing an entry twice (dup[row] = 1) are left out of the dq
+  // pass and taken whole by the query-major kernel with dK / dV (which skips the others)
+  const uint8_t* dup;    // [rows] or null
 };
 
 // Sums each of the N values v[0..N) over the 64 lanes of the wave with no lane-dependent
@@ -248,6 +256,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
   constexpr float kLog2e = 1.4426950408889634f;
   const AttnDev& A = G.A;
   const int row = blockIdx.x;
+  if (G.dup && (G.dup[row] != 0) != DKV) return;   // block-uniform
   const RowKeys r = row_keys<CSA>(A, row);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, g = lane >> 4;
@@ -359,6 +368,19 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
     for (int j = 0; j < 8; ++j) {
       const float pj = cs[j] != -1 ? exp2f(st[j >> 2][j & 3] * sl2 - lse2_col) : 0.0f;
       dsT[j] = pj * (dpt[j >> 2][j & 3] - dt_col);
+      if (CSA && !DKV && G.rec) {
+        // the selected entry's record: even lanes store P of heads col, col + 1, odd lanes
+        // dS of heads col - 1, col (the partner lane holds the same key)
+        const float mine = (col & 1) ? dsT[j] : pj;
+        const float other = __shfl_xor((col & 1) ? pj : dsT[j], 1, kWave);
+        if (cs[j] >= 0) {
+          const int pos = base + 16 * (j >> 2) + 4 * g + (j & 3);
+          const int64_t rb = static_cast<int64_t>(row) * A.k;
+          uint32_t* rp = G.rec + (rb + G.slot[rb + pos]) * 16;
+          if (col & 1) rp[8 + (col >> 1)] = pack_bf16x2(other, mine);
+          else rp[col >> 1] = pack_bf16x2(mine, other);
+        }
+      }
     }
     u32x4 dsB;
 #pragma unroll
@@ -597,6 +619,289 @@ __global__ __launch_bounds__(256) void bf16_copy_kernel(const float* __restrict_
   }
 }
 
+// ------------------------------------------------------------------ CSA selected entries, key-major
+//
+// A query token's selected entries differ from its neighbours', so no block of consecutive
+// tokens shares them; the pairs are instead grouped by entry.  The entries are cut into
+// tiles of kSelE; each row's valid selections are bucket-sorted by tile (sel_sort_kernel),
+// the dq pass stores every pair's P and dS (bf16) in the row's sorted order, and
+// sel_bwd_kernel takes one tile for a chunk of query tokens.  For a batch of tokens it
+// scatters their pairs' P and dS into a dense [token][entry] table in LDS (zero where a
+// token did not select the entry), and then per token
+//   dK[tile entries] += dS^T Q,   dV[tile entries] += P^T dout
+// run as 32x32x8 products over the 16 heads with the tile's entries as rows, summed in
+// registers over the whole chunk: no atomics until one add per element per block at the
+// end, where the query-major pass needs one per element per pair.  A row that lists an
+// entry twice is left to the query-major kernel (its pairs are not sorted), which keeps
+// each listed position its own key.
+constexpr int kSelE = 128;              // entries per tile
+constexpr int kSelTokens = 4096;        // query tokens per block
+constexpr int kSelBatch = 8;            // tokens staged at once
+constexpr int kSelThreads = 64 * kSelBatch;
+constexpr int kSelMaxN = 262144;        // entries a row's sort can mark in an LDS bitmap
+
+struct SelDev {
+  const uint32_t* qT;    // [rows][128][16] bf16: q, channel-major (heads adjacent)
+  const uint32_t* doT;   // [rows][128][16] bf16: dout rounded, channel-major
+  uint16_t* slot;        // [rows][k] sorted position of a valid (row, position) pair
+  uint8_t* el;           // [rows][k] entry within the tile of each sorted pair
+  uint16_t* off;         // [tiles + 1][rows] first sorted position of each tile's pairs
+  uint8_t* dup;          // [rows] 1: the row lists an entry twice (query-major instead)
+  const uint32_t* rec;   // [rows][k][16] the dq pass's P / dS records, sorted order
+  int tiles, rows;
+};
+
+// grid: rows; block 256.  A pair (row, position p) is valid when its entry e lies in the
+// row's visible entries [0, nv); it goes to tile e / kSelE.  off[t][row] is the row's
+// exclusive count of pairs in tiles before t (off[tiles][row]: all valid pairs); within a
+// tile the order is that of the LDS counter (not deterministic).  A row with a repeated
+// valid entry gets no pairs (all offsets 0) and dup[row] = 1.
+__global__ __launch_bounds__(256) void sel_sort_kernel(AttnBwdDev G, SelDev S) {
+  __shared__ uint32_t s_bits[kSelMaxN / 32];
+  __shared__ uint32_t s_cnt[kSelMaxN / kSelE + 1];
+  __shared__ uint32_t s_part[256];
+  __shared__ int s_dup;
+  const AttnDev& A = G.A;
+  const int row = blockIdx.x;
+  const RowKeys r = row_keys<true>(A, row);
+  const int64_t rb = static_cast<int64_t>(row) * A.k;
+  const int32_t* ip = A.idx + rb;
+  const int nt = S.tiles;
+  for (int t = threadIdx.x; t <= nt; t += 256) s_cnt[t] = 0;
+  for (int w = threadIdx.x; w < (r.nv + 31) / 32; w += 256) s_bits[w] = 0;
+  if (threadIdx.x == 0) s_dup = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < A.k; p += 256) {
+    const int e = ip[p];
+    if (e >= 0 && e < r.nv) {
+      const uint32_t bit = 1u << (e & 31);
+      if (atomicOr(&s_bits[e >> 5], bit) & bit) s_dup = 1;
+      atomicAdd(&s_cnt[e / kSelE], 1u);
+    }
+  }
+  __syncthreads();
+  if (s_dup) {                                   // block-uniform
+    for (int t = threadIdx.x; t <= nt; t += 256) S.off[static_cast<int64_t>(t) * S.rows + row] = 0;
+    if (threadIdx.x == 0) S.dup[row] = 1;
+    return;
+  }
+  // exclusive scan of s_cnt[0..nt]: thread u takes the segment [u seg, (u + 1) seg)
+  const int seg = (nt + 1 + 255) / 256;
+  const int s0 = threadIdx.x * seg;
+  uint32_t sum = 0;
+  for (int i = 0; i < seg; ++i)
+    if (s0 + i <= nt) sum += s_cnt[s0 + i];
+  s_part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {       // inclusive scan of the 256 segment sums
+    const uint32_t v = threadIdx.x >= d ? s_part[threadIdx.x - d] : 0u;
+    __syncthreads();
+    s_part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  uint32_t run = s_part[threadIdx.x] - sum;
+  for (int i = 0; i < seg; ++i) {
+    if (s0 + i <= nt) {
+      const uint32_t c = s_cnt[s0 + i];
+      s_cnt[s0 + i] = run;
+      S.off[static_cast<int64_t>(s0 + i) * S.rows + row] = static_cast<uint16_t>(run);
+      run += c;
+    }
+  }
+  if (threadIdx.x == 0) S.dup[row] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < A.k; p += 256) {
+    const int e = ip[p];
+    if (e >= 0 && e < r.nv) {
+      const int t = e / kSelE;
+      const uint32_t sl = atomicAdd(&s_cnt[t], 1u);
+      S.slot[rb + p] = static_cast<uint16_t>(sl);
+      S.el[rb + sl] = static_cast<uint8_t>(e - t * kSelE);
+    }
+  }
+}
+
+// grid: rows; block 256.  q [row][16][128] bf16 and dout [row][16][128] f32 to channel-major
+// bf16 copies [row][128][16] (dout rounded to nearest even, the products' operand precision).
+__global__ __launch_bounds__(256) void sel_transpose_kernel(const uint16_t* __restrict__ q,
+                                                            const float* __restrict__ dout,
+                                                            uint32_t* __restrict__ qT,
+                                                            uint32_t* __restrict__ doT) {
+  __shared__ uint16_t s_q[16][130];
+  __shared__ uint16_t s_d[16][130];
+  const int64_t row = blockIdx.x;
+  for (int x = threadIdx.x; x < 2048; x += 256) {
+    const int h = x >> 7, c = x & 127;
+    s_q[h][c] = q[row * 2048 + x];
+    s_d[h][c] = static_cast<uint16_t>(f32_to_bf16_bits(dout[row * 2048 + x]));
+  }
+  __syncthreads();
+  // thread u: channel u / 2, heads 8 (u % 2) .. + 7 -> four words of each copy
+  const int c = threadIdx.x >> 1, h0 = 8 * (threadIdx.x & 1);
+  u32x4 wq, wd;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    wq[m] = static_cast<uint32_t>(s_q[h0 + 2 * m][c]) | (static_cast<uint32_t>(s_q[h0 + 2 * m + 1][c]) << 16);
+    wd[m] = static_cast<uint32_t>(s_d[h0 + 2 * m][c]) | (static_cast<uint32_t>(s_d[h0 + 2 * m + 1][c]) << 16);
+  }
+  reinterpret_cast<u32x4*>(qT + row * 1024)[threadIdx.x] = wq;
+  reinterpret_cast<u32x4*>(doT + row * 1024)[threadIdx.x] = wd;
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mma32x8(const u32x2& a, const u32x2& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                  __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// grid: (tiles, ceil(Nq / kSelTokens), B); block kSelThreads (8 waves).  Wave w forms dK
+// (w < 4) or dV (w >= 4) of channels 32 (w % 4) .. + 31 for all kSelE entries of the tile:
+// four 32-entry row blocks, each a 32x32 accumulator (lane l: column l % 32, rows
+// 8 (r / 4) + 4 (l / 32) + r % 4 of register r).  A operand: the staged dS or P of entries
+// 32m + l % 32, heads 8s + 4 (l / 32) .. + 3; B operand: q or dout of the same heads at
+// channel 32 (w % 4) + l % 32, from the channel-major copies.
+// Table rows hold a record's eight 8-byte slots (P heads 4j .. 4j + 3 in slot j, dS in
+// slot 4 + j) in the permuted order of sel_slot.
+// Staging: wave u stages token u of a batch, lane l its pairs l / 4 + 16 n (16-byte quarter
+// l % 4).  The table is double-buffered: the next batch's records and B operands are read
+// into registers while the current batch's products run, one barrier per batch.
+constexpr int kSelRegPairs = 4;          // pairs per staging thread held in registers
+
+// Word offset of 8-byte slot s of table row e: the slots are XOR-permuted by (e / 4) % 8,
+// so that the 32 rows one operand read takes (32m .. 32m + 31, one slot each) fall in 32
+// different bank pairs (a row is 16 words: unpermuted, rows 4 apart share banks).
+__device__ __forceinline__ int sel_slot(int e, int s) { return 2 * (s ^ ((e >> 2) & 7)); }
+
+struct SelStage {
+  u32x4 v[kSelRegPairs];
+  int e[kSelRegPairs];
+};
+
+__global__ __launch_bounds__(kSelThreads) void sel_bwd_kernel(AttnBwdDev G, SelDev S) {
+  __shared__ uint32_t s_A[2][kSelBatch][kSelE][16];  // P pairs (words 0..7), dS (8..15)
+  __shared__ uint16_t s_lo[kSelTokens + kSelBatch], s_hi[kSelTokens + kSelBatch];
+  const AttnDev& A = G.A;
+  const int tile = blockIdx.x, b = blockIdx.z;
+  const int t0 = blockIdx.y * kSelTokens, t1 = min(t0 + kSelTokens, A.Nq);
+  // the chunk's last token must see the tile's first entry, else nothing to do
+  const int64_t plast = query_pos(A.seq_pos, A.pos0, b, t1 - 1);
+  if (static_cast<int64_t>(tile * kSelE + 1) * A.ratio > plast + 1) return;   // block-uniform
+  const int64_t row0 = static_cast<int64_t>(b) * A.Nq + t0;
+  const int nb = (t1 - t0 + kSelBatch - 1) / kSelBatch;
+  for (int x = threadIdx.x; x < nb * kSelBatch; x += kSelThreads) {
+    const bool in = t0 + x < t1;
+    s_lo[x] = in ? S.off[static_cast<int64_t>(tile) * S.rows + row0 + x] : 0;
+    s_hi[x] = in ? S.off[static_cast<int64_t>(tile + 1) * S.rows + row0 + x] : 0;
+  }
+  for (int x = threadIdx.x; x < 2 * kSelBatch * kSelE * 16 / 4; x += kSelThreads)
+    reinterpret_cast<u32x4*>(&s_A[0][0][0][0])[x] = u32x4{0u, 0u, 0u, 0u};
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lc = lane & 31, kg = lane >> 5;
+  const bool isV = wave >= 4;
+  const int ch = 32 * (wave & 3) + lc;
+  const uint32_t* bsrc = (isV ? S.doT : S.qT) + ch * 8 + 2 * kg;
+  const int as = (isV ? 0 : 4) + kg;               // A operand slot of heads 4kg .. (+2 per step)
+  const int q4 = lane >> 2, qr = lane & 3;
+  f32x16 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
+  __syncthreads();
+
+  // reads of batch i's staging (this thread's pairs of token `wave`) and B operands
+  auto fetch = [&](int i, SelStage& st, u32x2 (&bop)[kSelBatch][2]) {
+    const int x = i * kSelBatch + wave;
+    const int lo = s_lo[x], hi = s_hi[x];
+    const int64_t rb = (row0 + x) * A.k;
+#pragma unroll
+    for (int n = 0; n < kSelRegPairs; ++n) {
+      const int j = lo + q4 + 16 * n;
+      st.e[n] = -1;
+      if (j < hi) {
+        st.e[n] = S.el[rb + j];
+        st.v[n] = reinterpret_cast<const u32x4*>(S.rec + (rb + j) * 16)[qr];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const int t = t0 + i * kSelBatch + u < t1 ? i * kSelBatch + u : 0;
+      const uint32_t* p = bsrc + (row0 + t) * 1024;
+      bop[u][0] = *reinterpret_cast<const u32x2*>(p);
+      bop[u][1] = *reinterpret_cast<const u32x2*>(p + 4);
+    }
+  };
+  // write (or, with clear, zero) batch i's staged pairs in buffer i & 1: quarter qr of a
+  // record is its 8-byte slots 2qr and 2qr + 1
+  auto put = [&](uint32_t (*tab)[16], int e, const u32x4& v) {
+    *reinterpret_cast<u32x2*>(&tab[e][sel_slot(e, 2 * qr)]) = u32x2{v[0], v[1]};
+    *reinterpret_cast<u32x2*>(&tab[e][sel_slot(e, 2 * qr + 1)]) = u32x2{v[2], v[3]};
+  };
+  auto stage = [&](int i, const SelStage& st, bool clear) {
+    const int x = i * kSelBatch + wave;
+    const int lo = s_lo[x], hi = s_hi[x];
+    uint32_t(*tab)[16] = s_A[i & 1][wave];
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int n = 0; n < kSelRegPairs; ++n)
+      if (st.e[n] >= 0) put(tab, st.e[n], clear ? z : st.v[n]);
+    // pairs beyond the registers' (a row holding most of the tile), read in place
+    const int64_t rb = (row0 + x) * A.k;
+    for (int j = lo + q4 + 16 * kSelRegPairs; j < hi; j += 16) {
+      const int e = S.el[rb + j];
+      put(tab, e, clear ? z : reinterpret_cast<const u32x4*>(S.rec + (rb + j) * 16)[qr]);
+    }
+  };
+
+  SelStage cur, nxt;
+  u32x2 bcur[kSelBatch][2], bnxt[kSelBatch][2];
+  fetch(0, cur, bcur);
+  // the first batch's reads complete here: the loop then carries no read in flight into
+  // its products, whose operands would otherwise wait on the prefetch (the counter of
+  // vector reads is in order)
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int i = 0; i < nb; ++i) {
+    stage(i, cur, false);
+    if (i + 1 < nb) fetch(i + 1, nxt, bnxt);
+    __syncthreads();              // batch i staged; batch i - 1's buffer cleared
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const int x = i * kSelBatch + u;
+      if (s_hi[x] == s_lo[x]) continue;           // block-uniform: no pair in the tile
+      u32x2 a[4][2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = 32 * m + lc;
+        const uint32_t* ar = s_A[i & 1][u][r];
+        a[m][0] = *reinterpret_cast<const u32x2*>(ar + sel_slot(r, as));
+        a[m][1] = *reinterpret_cast<const u32x2*>(ar + sel_slot(r, as + 2));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = mma32x8(a[m][h], bcur[u][h], acc[m]);
+    }
+    __syncthreads();              // every wave done with batch i's buffer
+    stage(i, cur, true);
+    cur = nxt;
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      bcur[u][0] = bnxt[u][0];
+      bcur[u][1] = bnxt[u][1];
+    }
+  }
+  float* dst = (isV ? G.dvc : G.dkc) + b * G.dc_bstride + ch;
+  const float f = isV ? 1.0f : A.scale;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t er = static_cast<int64_t>(tile) * kSelE + 32 * m + 8 * (r >> 2) + 4 * kg + (r & 3);
+      if (er < A.N && acc[m][r] != 0.0f) unsafeAtomicAdd(dst + er * 128, f * acc[m][r]);
+    }
+}
+
 // ------------------------------------------------------------------ pooling backward
 
 // grid: (ceil(n_out * r / rows_per_block), B); block 256.  Thread (local row, c8) handles 8
@@ -709,16 +1014,42 @@ bool bwd_key_major(const AttnArgs& a) {
   return a.kv_dtype == 1 && a.H == 16 && a.d == 128 && a.Nq >= 16;
 }
 
-// key-major pass: dout.o - dlse [rows][16] f32, then dout as bf16 [rows][16][128]
-static size_t bwd_dt_bytes(const AttnArgs& a) {
-  return align256(static_cast<size_t>(a.B) * a.Nq * 16 * 4);
+// CSA selected entries key-major: needs the sort's offsets to fit 16 bits and its entry
+// bitmap to fit LDS
+static int sel_tiles(int N) { return (N + kSelE - 1) / kSelE; }
+static bool bwd_sel_key_major(const AttnArgs& a) {
+  return bwd_key_major(a) && a.k > 0 && a.k <= 65535 && a.N > 0 && a.N <= kSelMaxN;
 }
 
-size_t bwd_workspace_bytes(const AttnArgs& a) {
-  return bwd_key_major(a)
-             ? bwd_dt_bytes(a) + align256(static_cast<size_t>(a.B) * a.Nq * 16 * 128 * 2)
-             : 0;
+// Workspace of the key-major passes: dout.o - dlse [rows][16] f32, dout as bf16
+// [rows][16][128]; for the CSA selected entries also the channel-major q and dout copies,
+// the records [rows][k][16] words, the sorted slots [rows][k] u16, the tile entries
+// [rows][k] u8 and the tile offsets [tiles + 1][rows] u16.
+struct BwdWs {
+  size_t dt, d16, qT, doT, rec, slot, el, off, dup, total;
+};
+static BwdWs bwd_ws_layout(const AttnArgs& a) {
+  BwdWs w{};
+  if (!bwd_key_major(a)) return w;
+  const size_t rows = static_cast<size_t>(a.B) * a.Nq;
+  size_t o = 0;
+  w.dt = o;  o += align256(rows * 16 * 4);
+  w.d16 = o; o += align256(rows * 2048 * 2);
+  if (bwd_sel_key_major(a)) {
+    const size_t k = static_cast<size_t>(a.k);
+    w.qT = o;   o += align256(rows * 2048 * 2);
+    w.doT = o;  o += align256(rows * 2048 * 2);
+    w.rec = o;  o += align256(rows * k * 64);
+    w.slot = o; o += align256(rows * k * 2);
+    w.el = o;   o += align256(rows * k);
+    w.off = o;  o += align256((static_cast<size_t>(sel_tiles(a.N)) + 1) * rows * 2);
+    w.dup = o;  o += align256(rows);
+  }
+  w.total = o;
+  return w;
 }
+
+size_t bwd_workspace_bytes(const AttnArgs& a) { return bwd_ws_layout(a).total; }
 
 bool attn_bwd_shape_supported(int H, int d) {
   const int hh = bwd_heads(H), cpl = bwd_cpl(d);
@@ -744,10 +1075,15 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
   G.dt_out = nullptr;
   G.dout16 = nullptr;
   const int rows = a.B * a.Nq;
+  G.slot = nullptr;
+  G.rec = nullptr;
+  G.dup = nullptr;
+  const BwdWs wl = bwd_ws_layout(a);
+  char* wsb = static_cast<char*>(g.ws);
   // the key-major pass's inputs in the workspace: dt_out, and dout converted to bf16 once
   auto key_major_inputs = [&]() {
-    G.dt_out = static_cast<float*>(g.ws);
-    uint16_t* d16 = reinterpret_cast<uint16_t*>(static_cast<char*>(g.ws) + bwd_dt_bytes(a));
+    G.dt_out = reinterpret_cast<float*>(wsb + wl.dt);
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(wsb + wl.d16);
     G.dout16 = d16;
     const int64_t n8 = static_cast<int64_t>(rows) * 16 * 128 / 8;
     const int blocks = static_cast<int>(std::min<int64_t>((n8 + 255) / 256, 4096));
@@ -758,7 +1094,41 @@ hipError_t launch_attention_bwd(bool csa, const AttnArgs& a, const AttnBwdArgs& 
   const bool bf = a.kv_dtype == 1;
   if (bf && a.H == 16 && a.d == 128) {          // the matrix-core path
     const int chunks = (a.Nq + kDkvTokens - 1) / kDkvTokens;
-    if (csa && bwd_key_major(a) && g.ws && a.n_win > 0) {
+    if (csa && g.ws && bwd_sel_key_major(a)) {
+      // selected entries key-major by tile (sort, dq pass storing the pairs' P and dS,
+      // tile pass), window rows key-major by token chunk
+      key_major_inputs();
+      SelDev S{};
+      S.qT = reinterpret_cast<const uint32_t*>(wsb + wl.qT);
+      S.doT = reinterpret_cast<const uint32_t*>(wsb + wl.doT);
+      S.slot = reinterpret_cast<uint16_t*>(wsb + wl.slot);
+      S.el = reinterpret_cast<uint8_t*>(wsb + wl.el);
+      S.off = reinterpret_cast<uint16_t*>(wsb + wl.off);
+      S.rec = reinterpret_cast<const uint32_t*>(wsb + wl.rec);
+      S.dup = reinterpret_cast<uint8_t*>(wsb + wl.dup);
+      S.tiles = sel_tiles(a.N);
+      S.rows = rows;
+      sel_sort_kernel<<<rows, 256, 0, s>>>(G, S);
+      sel_transpose_kernel<<<rows, 256, 0, s>>>(static_cast<const uint16_t*>(a.q), g.dout,
+                                                const_cast<uint32_t*>(S.qT),
+                                                const_cast<uint32_t*>(S.doT));
+      AttnBwdDev Gq = G;
+      Gq.slot = S.slot;
+      Gq.rec = reinterpret_cast<uint32_t*>(wsb + wl.rec);
+      Gq.dup = S.dup;
+      attn_bwd_mfma_kernel<true, false><<<rows, 256, 0, s>>>(Gq);
+      // rows that list an entry twice: dq and the selected entries' dK / dV query-major
+      Gq.dkr = Gq.dvr = nullptr;
+      attn_bwd_mfma_kernel<true, true><<<rows, 256, 0, s>>>(Gq);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      dim3 sgrid(S.tiles, (a.Nq + kSelTokens - 1) / kSelTokens, a.B);
+      sel_bwd_kernel<<<sgrid, kSelThreads, 0, s>>>(G, S);
+      e = hipGetLastError();
+      if (e != hipSuccess || a.n_win == 0) return e;
+      dim3 grid((kDkvTokens + a.n_win - 1 + kDkvEntries - 1) / kDkvEntries, chunks, a.B);
+      key_bwd_kernel<true><<<grid, 256, 0, s>>>(G);
+    } else if (csa && bwd_key_major(a) && g.ws && a.n_win > 0) {
       // the window rows, shared by consecutive query tokens, key-major; the rest per query
       key_major_inputs();
       AttnBwdDev Gq = G;

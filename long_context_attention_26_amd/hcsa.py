@@ -34,7 +34,7 @@ _SIGS = {
     "hcsa_csa_hca_attn": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64, _i, _i,
                                _p, _p, _i64, _i, _i, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _p,
                                _p, _p, _p, _p, _sz, _p]),
-    "hcsa_csa_sparse_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "hcsa_csa_sparse_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "hcsa_csa_sparse_attn_bwd": (_i, [_p, _p, _p, _i64, _i, _p, _i, _p, _p, _i64, _i64, _i64,
                                       _i, _i, _i64, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p,
                                       _p, _p, _p, _p, _i64, _p, _p, _i64, _p, _sz, _p]),
@@ -438,7 +438,7 @@ def csa_sparse_attn_bwd(q, kc, vc, N, topk_idx, k_raw, v_raw, raw_pos0, n_win, r
     consecutive tokens then get their gradients query-major, with atomics."""
     B, Nq, H, d = q.shape
     k = topk_idx.shape[-1]
-    nbytes = lib.hcsa_csa_sparse_attn_bwd_workspace_size(B, Nq, H, d, dtype_code(q))
+    nbytes = lib.hcsa_csa_sparse_attn_bwd_workspace_size(B, Nq, H, d, dtype_code(q), N, k)
     if workspace is None and nbytes and key_major:
         workspace = alloc_workspace(nbytes, q.device)
     _check(lib.hcsa_csa_sparse_attn_bwd(_ptr(q), _ptr(kc), _ptr(vc), kc.stride(0), N,

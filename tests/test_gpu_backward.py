@@ -63,6 +63,13 @@ CSA_CASES = [
     # the same rows with a null workspace: the window rows' gradients stay query-major
     dict(dt="bf16", H=16, d=128, N=900, k=128, n_win=128, Nq=300, B=2, pos0=3300, dlse=True,
          nows=True),
+    # selected entries key-major by 128-entry tile: two 4096-token chunks (the second
+    # ragged), ten tiles, the last partial
+    dict(dt="bf16", H=16, d=128, N=1200, k=32, n_win=16, Nq=4200, B=1, pos0=500, dlse=True),
+    # selections with repeated entries, padding and invisible entries anywhere in the list
+    # (each listed position is its own key), no window
+    dict(dt="bf16", H=16, d=128, N=300, k=96, n_win=0, Nq=40, B=2, pos0=1000, dlse=True,
+         dup=True),
 ]
 
 
@@ -82,7 +89,9 @@ def test_csa_backward(H, gpu, case):
     for b in range(B):
         for i in range(Nq):
             nv = O.visible_entries(pos0 + i, N, ratio)
-            if k:
+            if k and case.get("dup"):
+                idx[b, i] = rng.integers(-3, nv + 5, size=k)
+            elif k:
                 idx[b, i] = O.select_topk(rng.standard_normal(N), nv, k)
     dout = O.round_fp32(rng.standard_normal((B, Nq, Hh, d)))
     dlse = O.round_fp32(rng.standard_normal((B, Nq, Hh))) if case["dlse"] else None
@@ -267,13 +276,14 @@ def test_training_step_chain(H, gpu):
         _rel_close(f64(t), ref[n_], 2e-2, n_)
 
 
-@pytest.mark.parametrize("dt,Hh,d", [("bf16", 16, 128), ("f32", 4, 64)])
-def test_backward_ragged_positions(H, gpu, dt, Hh, d):
+@pytest.mark.parametrize("dt,Hh,d,Nq", [("bf16", 16, 128, 2), ("f32", 4, 64, 2),
+                                         ("bf16", 16, 128, 24)])
+def test_backward_ragged_positions(H, gpu, dt, Hh, d, Nq):
     """Per-sequence positions (seq_pos): each sequence's gradients against the oracle at its
-    own position, CSA and HCA."""
-    print(f"bwd ragged {dt} H{Hh} d{d}", flush=True)
+    own position, CSA and HCA (24 tokens: the key-major passes)."""
+    print(f"bwd ragged {dt} H{Hh} d{d} Nq{Nq}", flush=True)
     pos = [5000, 777, 2999]
-    B, Nq, k, w = len(pos), 2, 128, 64
+    B, k, w = len(pos), 128, 64
     scale = 1 / math.sqrt(d)
     top = max(pos) + Nq
     N, Nh = top // 4 + 2, top // 128 + 1
