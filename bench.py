@@ -362,11 +362,15 @@ def train_backward(args):
                    "head_dim": d, "topk": k, "n_win": w},
         "breakdown_ms": {k_: round(v, 3) for k_, v in br.items()},
         "forward_ms": round(fwd_ms, 3),
-        "roofline": {"kernel": "attn_bwd_mfma_kernel (CSA, 2 launches)", "bound": "mfma",
+        "roofline": {"kernel": "CSA attention backward (sort, dq pass, key-major selected "
+                               "entries and window rows; 2 calls)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "flops_per_step": flops,
-                     "note": "limited by the fp32 atomic adds of dk/dv (256 per query-key pair)"},
+                     "note": "algorithmic flops over the csa_bwd stage time; the dq pass "
+                             "gathers key rows query-major, the selected entries' dK/dV run as "
+                             "dense products over 128-entry tiles (about 8 % of whose "
+                             "(token, entry) cells are selected)"},
     }
     print(json.dumps(out), flush=True)
 

@@ -750,17 +750,18 @@ __global__ __launch_bounds__(256) void sel_transpose_kernel(const uint16_t* __re
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ f32x16 mma32x8(const u32x2& a, const u32x2& b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                  __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mma32x16(const u32x4& a, const u32x4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 // grid: (tiles, ceil(Nq / kSelTokens), B); block kSelThreads (8 waves).  Wave w forms dK
 // (w < 4) or dV (w >= 4) of channels 32 (w % 4) .. + 31 for all kSelE entries of the tile:
 // four 32-entry row blocks, each a 32x32 accumulator (lane l: column l % 32, rows
-// 8 (r / 4) + 4 (l / 32) + r % 4 of register r).  A operand: the staged dS or P of entries
-// 32m + l % 32, heads 8s + 4 (l / 32) .. + 3; B operand: q or dout of the same heads at
-// channel 32 (w % 4) + l % 32, from the channel-major copies.
+// 8 (r / 4) + 4 (l / 32) + r % 4 of register r), one 32x32x16 product per block and token
+// over its 16 heads.  A operand: the staged dS or P of entries 32m + l % 32, heads
+// 8 (l / 32) .. + 7; B operand: q or dout of the same heads at channel 32 (w % 4) + l % 32,
+// from the channel-major copies.
 // Table rows hold a record's eight 8-byte slots (P heads 4j .. 4j + 3 in slot j, dS in
 // slot 4 + j) in the permuted order of sel_slot.
 // Staging: wave u stages token u of a batch, lane l its pairs l / 4 + 16 n (16-byte quarter
@@ -800,8 +801,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_bwd_kernel(AttnBwdDev G, SelD
   const int lc = lane & 31, kg = lane >> 5;
   const bool isV = wave >= 4;
   const int ch = 32 * (wave & 3) + lc;
-  const uint32_t* bsrc = (isV ? S.doT : S.qT) + ch * 8 + 2 * kg;
-  const int as = (isV ? 0 : 4) + kg;               // A operand slot of heads 4kg .. (+2 per step)
+  const uint32_t* bsrc = (isV ? S.doT : S.qT) + ch * 8 + 4 * kg;
+  const int as = (isV ? 0 : 4) + 2 * kg;           // A operand slots of heads 8kg .. 8kg + 7
   const int q4 = lane >> 2, qr = lane & 3;
   f32x16 acc[4];
 #pragma unroll
@@ -811,7 +812,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_bwd_kernel(AttnBwdDev G, SelD
   __syncthreads();
 
   // reads of batch i's staging (this thread's pairs of token `wave`) and B operands
-  auto fetch = [&](int i, SelStage& st, u32x2 (&bop)[kSelBatch][2]) {
+  auto fetch = [&](int i, SelStage& st, u32x4 (&bop)[kSelBatch]) {
     const int x = i * kSelBatch + wave;
     const int lo = s_lo[x], hi = s_hi[x];
     const int64_t rb = (row0 + x) * A.k;
@@ -827,9 +828,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_bwd_kernel(AttnBwdDev G, SelD
 #pragma unroll
     for (int u = 0; u < kSelBatch; ++u) {
       const int t = t0 + i * kSelBatch + u < t1 ? i * kSelBatch + u : 0;
-      const uint32_t* p = bsrc + (row0 + t) * 1024;
-      bop[u][0] = *reinterpret_cast<const u32x2*>(p);
-      bop[u][1] = *reinterpret_cast<const u32x2*>(p + 4);
+      bop[u] = *reinterpret_cast<const u32x4*>(bsrc + (row0 + t) * 1024);
     }
   };
   // write (or, with clear, zero) batch i's staged pairs in buffer i & 1: quarter qr of a
@@ -855,7 +854,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_bwd_kernel(AttnBwdDev G, SelD
   };
 
   SelStage cur, nxt;
-  u32x2 bcur[kSelBatch][2], bnxt[kSelBatch][2];
+  u32x4 bcur[kSelBatch], bnxt[kSelBatch];
   fetch(0, cur, bcur);
   // the first batch's reads complete here: the loop then carries no read in flight into
   // its products, whose operands would otherwise wait on the prefetch (the counter of
@@ -869,27 +868,23 @@ __global__ __launch_bounds__(kSelThreads) void sel_bwd_kernel(AttnBwdDev G, SelD
     for (int u = 0; u < kSelBatch; ++u) {
       const int x = i * kSelBatch + u;
       if (s_hi[x] == s_lo[x]) continue;           // block-uniform: no pair in the tile
-      u32x2 a[4][2];
+      u32x4 a[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int r = 32 * m + lc;
         const uint32_t* ar = s_A[i & 1][u][r];
-        a[m][0] = *reinterpret_cast<const u32x2*>(ar + sel_slot(r, as));
-        a[m][1] = *reinterpret_cast<const u32x2*>(ar + sel_slot(r, as + 2));
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(ar + sel_slot(r, as));
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(ar + sel_slot(r, as + 1));
+        a[m] = u32x4{a0[0], a0[1], a1[0], a1[1]};
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m] = mma32x8(a[m][h], bcur[u][h], acc[m]);
+      for (int m = 0; m < 4; ++m) acc[m] = mma32x16(a[m], bcur[u], acc[m]);
     }
     __syncthreads();              // every wave done with batch i's buffer
     stage(i, cur, true);
     cur = nxt;
 #pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) {
-      bcur[u][0] = bnxt[u][0];
-      bcur[u][1] = bnxt[u][1];
-    }
+    for (int u = 0; u < kSelBatch; ++u) bcur[u] = bnxt[u];
   }
   float* dst = (isV ? G.dvc : G.dkc) + b * G.dc_bstride + ch;
   const float f = isV ? 1.0f : A.scale;
