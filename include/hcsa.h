@@ -341,10 +341,11 @@ int hcsa_csa_hca_attn(const void *q, const void *kc, const void *vc, int64_t c_b
  * ratio with CSA (one indexer key per CSA entry).
  *
  * For one query token per sequence with MXFP4 keys (fp4 operands), bf16 queries and scores,
- * the selection without a score array, bf16 16 x 128 attention, contiguous caches and
- * k + n_win <= 4096, the step runs in four launches: the per-row selection floors beside the
- * pooling; the key scan; two blocks per row each resolving the row's top-k and then
- * attending over half of its CSA key list, beside the HCA splits on the other compute
+ * the selection without a score array, bf16 16 x 128 attention and k + n_win <= 4096 (caches
+ * contiguous or paged, raw tokens in rows or a ring, one position for all sequences or
+ * per-sequence positions), the step runs in four launches: the per-row selection floors
+ * beside the pooling; the key scan; two blocks per row each resolving the row's top-k and
+ * then attending over half of its CSA key list, beside the HCA splits on the other compute
  * units; the merge of the CSA and HCA splits.  The pooled caches and the selection equal those of the two calls bit for bit; the
  * attention outputs are split differently and agree with theirs up to the rounding of the
  * split sums (the softmax probabilities enter P.V as bf16, rounded relative to each split's

@@ -9,7 +9,8 @@
 // indexer's QK path, BF16 index scores).  The pooled caches and the selection are those of
 // hcsa_csa_pool_index_topk bit for bit (the same device code runs here); the attention
 // splits differ from hcsa_csa_hca_attn's, so its outputs agree up to the rounding of the
-// split sums.
+// split sums.  Paged caches, the raw-token ring and per-sequence positions take the same
+// launches (the paged kernels are instantiated separately).
 //
 //  1. front: the per-row selection floors (kMxFloorParts 512-thread blocks per row, each
 //     scoring a quarter of the samples, taken only from entries completed before the step)
@@ -49,20 +50,21 @@ struct StepDev {
   uint32_t* hca_next;  // next HCA unit of the back launch (zeroed by the front launch)
 };
 
-// grid: rows * kMxFloorParts + B * pool_blocks; block 512.
-template <int HI, int KS>
+// grid: rows * kMxFloorParts + B * pool_blocks; block 512.  PAGED: caches in 128-token
+// pages through the block table.
+template <int HI, int KS, bool PAGED>
 __global__ __launch_bounds__(kStepThreads) void step_front_kernel(StepDev S) {
   __shared__ float alpha[1024];
   __shared__ float s_part[kStepThreads * 8];
   const int bx = blockIdx.x;
   if (bx == 0 && threadIdx.x == 0) *S.hca_next = 0u;   // the back launch's unit counter
   if (bx < S.rows * kMxFloorParts) {
-    mx_floor_block<HI, KS, true, false, false>(S.X, S.k, bx / kMxFloorParts,
+    mx_floor_block<HI, KS, true, PAGED, false>(S.X, S.k, bx / kMxFloorParts,
                                                bx % kMxFloorParts, true);
     return;
   }
   const int b2 = bx - S.rows * kMxFloorParts;
-  pool_jobs_block<false>(S.J, b2 % S.pool_blocks, alpha, s_part, b2 / S.pool_blocks);
+  pool_jobs_block<PAGED>(S.J, b2 % S.pool_blocks, alpha, s_part, b2 / S.pool_blocks);
 }
 
 // grid: rows * kRowParts + HCA workers; block 512.  Blocks below rows * kRowParts: the
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(kStepThreads) void step_front_kernel(StepDev S) {
 // the rest take pairs of HCA units (one per 4-wave half) from a counter until none is
 // left.  Which block computes a unit does not change its result, so the outputs do not
 // depend on the order the units are taken in.
-template <int HI, int KS>
+template <int HI, int KS, bool PAGED>
 __global__ __launch_bounds__(kStepThreads) void step_back_kernel(StepDev S) {
   __shared__ int s_code[kMfmaMaxChunk];
   __shared__ float s_o[8][16][129];
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kStepThreads) void step_back_kernel(StepDev S) {
     // every part of a row runs the row's (deterministic) resolve, so each holds the same
     // selection without waiting for another block, then attends over its split of the list
     const int row = bx / kRowParts, part = bx % kRowParts;
-    mx_resolve_row<HI, KS, true, false, false, false>(S.X, S.k, S.idx, row);
+    mx_resolve_row<HI, KS, true, PAGED, false, false>(S.X, S.k, S.idx, row);
     const RowKeys r = row_keys<true>(S.C, row);
     Row8State st;
     row8_init(S.C, row, st);
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kStepThreads) void step_back_kernel(StepDev S) {
     if (u0 >= S.hca_units) break;                // block-uniform
     const int u = u0 + half;
     if (u < S.hca_units)
-      hca_decode_block<false>(S.Hd, u % S.Hd.splits, u / S.Hd.splits, s_o + 4 * half,
+      hca_decode_block<PAGED>(S.Hd, u % S.Hd.splits, u / S.Hd.splits, s_o + 4 * half,
                               s_ml + 4 * half, tid);
     else
       __syncthreads();                           // the unit's one barrier
@@ -126,15 +128,15 @@ __global__ __launch_bounds__(256) void step_merge_kernel(StepMerge c, StepMerge 
                 s_w, s_red);
 }
 
-template <int HI, int KS>
+template <int HI, int KS, bool PAGED>
 hipError_t launch_step_hi(const StepDev& S, int front_blocks, int back_blocks, int H_I,
                           hipStream_t s) {
-  step_front_kernel<HI, KS><<<front_blocks, kStepThreads, 0, s>>>(S);
+  step_front_kernel<HI, KS, PAGED><<<front_blocks, kStepThreads, 0, s>>>(S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_mx_candidate_scan(S.X, S.rows, H_I, s);
+  e = launch_mx_candidate_scan(S.X, S.rows, H_I, PAGED, s);
   if (e != hipSuccess) return e;
-  step_back_kernel<HI, KS><<<back_blocks, kStepThreads, 0, s>>>(S);
+  step_back_kernel<HI, KS, PAGED><<<back_blocks, kStepThreads, 0, s>>>(S);
   return hipGetLastError();
 }
 
@@ -191,8 +193,7 @@ bool decode_step_fast(const DecodeStepArgs& a, const AttnPlan& pc, const AttnPla
                       bool fused_selection) {
   const bool hi_ok = a.H_I == 1 || a.H_I == 2 || a.H_I == 4 || a.H_I == 8 || a.H_I == 16;
   return fused_selection && a.Nq == 1 && a.k_dtype == HCSA_MXFP4 && a.q_dtype == HCSA_BF16 &&
-         a.score_dtype == HCSA_BF16 && a.block_table == nullptr && a.raw_ring == 0 &&
-         a.seq_pos == nullptr && hi_ok && csa_hca_fused(pc, ph) &&
+         a.score_dtype == HCSA_BF16 && hi_ok && csa_hca_fused(pc, ph) &&
          a.c.k + a.c.n_win <= kMfmaMaxChunk;
 }
 
@@ -206,8 +207,8 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const
   const MxTopkLayout l = mx_topk_layout(rows, a.N);
   char* mx = base;
   S.X = make_mx_dev(a.q_idx, a.w_idx, a.k_idx, a.k_bstride, a.k_scales, a.ks_bstride, a.B,
-                    a.Nq, a.d_I, a.N, a.c.ratio, a.c.pos0, nullptr, nullptr, 0,
-                    mx + l.scores_off);
+                    a.Nq, a.d_I, a.N, a.c.ratio, a.c.pos0, a.seq_pos, a.block_table,
+                    a.c.table_stride, mx + l.scores_off);
   S.X.floor = reinterpret_cast<uint32_t*>(mx);
   S.X.counts = reinterpret_cast<uint32_t*>(mx + l.counts_off);
   S.X.lists = reinterpret_cast<uint32_t*>(mx + l.lists_off);
@@ -219,18 +220,24 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const
   S.rows = rows;
   S.k = a.c.k;
   S.idx = a.idx;
-  S.pool_blocks = a.n_jobs > 0 ? pool_jobs_fill(a.jobs, a.n_jobs, nullptr, 0, 0, kStepThreads, S.J)
+  S.pool_blocks = a.n_jobs > 0 ? pool_jobs_fill(a.jobs, a.n_jobs, a.block_table,
+                                                a.c.table_stride, a.raw_ring, kStepThreads, S.J)
                                : 0;
   S.hca_units = rows * ph.splits;
   S.hca_next = reinterpret_cast<uint32_t*>(base + sync_off);
   const int front = rows * kMxFloorParts + a.B * S.pool_blocks;
   const int back = kRowParts * rows + std::min(step_hca_workers(rows), (S.hca_units + 1) / 2);
   hipError_t e = hipErrorInvalidValue;
-  const bool ks2 = a.d_I > 64;
+  const bool ks2 = a.d_I > 64, paged = a.block_table != nullptr;
 #define HCSA_STEP(HI_)                                                              \
-  if (a.H_I == HI_)                                                                 \
-    e = ks2 ? launch_step_hi<HI_, 2>(S, front, back, a.H_I, s)                       \
-            : launch_step_hi<HI_, 1>(S, front, back, a.H_I, s);
+  if (a.H_I == HI_) {                                                               \
+    if (paged)                                                                      \
+      e = ks2 ? launch_step_hi<HI_, 2, true>(S, front, back, a.H_I, s)               \
+              : launch_step_hi<HI_, 1, true>(S, front, back, a.H_I, s);              \
+    else                                                                            \
+      e = ks2 ? launch_step_hi<HI_, 2, false>(S, front, back, a.H_I, s)              \
+              : launch_step_hi<HI_, 1, false>(S, front, back, a.H_I, s);             \
+  }
   HCSA_STEP(1) HCSA_STEP(2) HCSA_STEP(4) HCSA_STEP(8) HCSA_STEP(16)
 #undef HCSA_STEP
   if (e != hipSuccess) return e;

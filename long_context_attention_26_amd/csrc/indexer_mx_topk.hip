@@ -89,20 +89,26 @@ hipError_t launch_mx_topk(const IdxMxDev& A, int rows, int H_I, int k, int32_t* 
 
 }  // namespace
 
-hipError_t launch_mx_candidate_scan(const IdxMxDev& A, int rows, int H_I, hipStream_t s) {
+hipError_t launch_mx_candidate_scan(const IdxMxDev& A, int rows, int H_I, bool paged,
+                                     hipStream_t s) {
   const dim3 grid(A.nchunks, rows);
+#define HCSA_SCAN_KS(HI_, KS_, P_)                                                           \
+  launch_timed(index_scores_mx_mfma_kernel<HI_, KS_, true, true, P_, false, true>, grid,    \
+               dim3(256), s, A)
 #define HCSA_SCAN(HI_)                                                                        \
   if (H_I == HI_) {                                                                           \
-    if (A.d_I > 64)                                                                           \
-      launch_timed(index_scores_mx_mfma_kernel<HI_, 2, true, true, false, false, true>, grid, \
-                   dim3(256), s, A);                                                          \
-    else                                                                                      \
-      launch_timed(index_scores_mx_mfma_kernel<HI_, 1, true, true, false, false, true>, grid, \
-                   dim3(256), s, A);                                                          \
+    if (A.d_I > 64) {                                                                         \
+      if (paged) HCSA_SCAN_KS(HI_, 2, true);                                                  \
+      else HCSA_SCAN_KS(HI_, 2, false);                                                       \
+    } else {                                                                                  \
+      if (paged) HCSA_SCAN_KS(HI_, 1, true);                                                  \
+      else HCSA_SCAN_KS(HI_, 1, false);                                                       \
+    }                                                                                         \
     return hipGetLastError();                                                                 \
   }
   HCSA_SCAN(1) HCSA_SCAN(2) HCSA_SCAN(4) HCSA_SCAN(8) HCSA_SCAN(16)
 #undef HCSA_SCAN
+#undef HCSA_SCAN_KS
   return hipErrorInvalidValue;
 }
 

@@ -613,9 +613,10 @@ inline MxTopkLayout mx_topk_layout(int rows, int N) {
   return l;
 }
 
-// The candidate scan of the fused selection (bf16 queries, contiguous MXFP4 keys on fp4
-// operands): per-chunk lists of the keys scoring at or above each row's floor.
-hipError_t launch_mx_candidate_scan(const IdxMxDev& A, int rows, int H_I, hipStream_t s);
+// The candidate scan of the fused selection (bf16 queries, MXFP4 keys on fp4 operands,
+// contiguous or paged): per-chunk lists of the keys scoring at or above each row's floor.
+hipError_t launch_mx_candidate_scan(const IdxMxDev& A, int rows, int H_I, bool paged,
+                                     hipStream_t s);
 
 // Scores of MXFP4 keys (fp4 operands, or widened to e4m3 with fp8) into scores [rows][N].
 hipError_t launch_mxfp4_index_scores(const void* q, int q_dtype, const float* w,

@@ -158,7 +158,9 @@ __device__ __forceinline__ void pool_rows_wide(const void* __restrict__ x, int64
                                                int64_t pos0 = 0, int64_t ring = 0) {
   constexpr int PF = 8;
   const int tpr = D >> 3;
-  const int G = blockDim.x / tpr;
+  // the groups of a 256-thread block whatever the launch's block size: the partial sums,
+  // and so the entry's bits, are the same in every launch that pools it
+  const int G = min(static_cast<int>(blockDim.x), 256) / tpr;
   const int g = threadIdx.x / tpr;
   const int c8 = threadIdx.x - g * tpr;
   constexpr int ES = IN_BF16 ? 2 : 4;
