@@ -122,18 +122,28 @@ struct RowView {
   // bit e set when element e of a chunk (first index j0) is a visible key >= L.  For a
   // floor above +0 the keys >= L are exactly the non-negative raw values in
   // [raw(L), largest positive pattern], an unsigned range test on the raw bits.
+  // bf16, both halves of a word at once: with H = 0x8000 in each half, (w | H) - raw(L)
+  // per half cannot borrow across halves and keeps H exactly when the half's low 15 bits
+  // are >= raw(L); and-ing with ~w keeps it only for non-negative raw values.  A byte
+  // permute gathers the eight flags and a multiply packs them into the mask (about 16
+  // instructions a chunk instead of 40).
   __device__ uint32_t ge_mask(const u32x4& x, int j0, uint32_t L) const {
     uint32_t m = 0;
     if (L > kSign) {
       const uint32_t lo_raw = L - kSign, span = kSign - 1 - lo_raw;
+      if constexpr (KB == 16) {
+        const uint32_t H = 0x80008000u, LL = lo_raw * 0x10001u;
+        uint32_t cb[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if constexpr (KB == 16) {
-          m |= static_cast<uint32_t>((x[c] & 0xffffu) - lo_raw <= span) << (2 * c);
-          m |= static_cast<uint32_t>((x[c] >> 16) - lo_raw <= span) << (2 * c + 1);
-        } else {
-          m |= static_cast<uint32_t>(x[c] - lo_raw <= span) << c;
-        }
+        for (int c = 0; c < 4; ++c) cb[c] = ((x[c] | H) - LL) & ~x[c] & H;
+        // high bytes of the halves, keys 0..3 and 4..7: flags at bits 7, 15, 23, 31
+        const uint32_t a = (__builtin_amdgcn_perm(cb[1], cb[0], 0x07050301u) >> 7) & 0x01010101u;
+        const uint32_t b = (__builtin_amdgcn_perm(cb[3], cb[2], 0x07050301u) >> 7) & 0x01010101u;
+        // one bit per byte -> four adjacent bits (bits 21..24 of the product)
+        m = ((a * 0x204081u) >> 21 & 0xfu) | ((b * 0x204081u) >> 17 & 0xf0u);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m |= static_cast<uint32_t>(x[c] - lo_raw <= span) << c;
       }
     } else {
 #pragma unroll
