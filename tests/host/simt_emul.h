@@ -79,6 +79,25 @@ inline void __hip_atomic_store(T* p, T v, int order, int scope) {
   (void)scope;
   __atomic_store_n(p, v, order);
 }
+// v_perm_b32: byte i of the result is chosen by byte i of sel from the eight bytes of
+// (hi:lo), lo's bytes 0..3 first; selector 12 gives 0x00, 13 and above 0xff, and 8..11
+// replicate the sign bit of bytes 1, 3, 5, 7 (the ISA manual's table).
+inline uint32_t __builtin_amdgcn_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  const uint64_t v = (static_cast<uint64_t>(hi) << 32) | lo;
+  uint32_t r = 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t s = (sel >> (8 * i)) & 0xffu;
+    uint32_t b;
+    if (s < 8)
+      b = static_cast<uint32_t>(v >> (8 * s)) & 0xffu;
+    else if (s < 12)
+      b = (v >> (16 * (s - 8) + 15)) & 1u ? 0xffu : 0u;
+    else
+      b = s == 12 ? 0u : 0xffu;
+    r |= b << (8 * i);
+  }
+  return r;
+}
 inline int __popcll(uint64_t m) { return __builtin_popcountll(m); }
 inline int __popc(uint32_t m) { return __builtin_popcount(m); }
 inline int __ffs(uint32_t m) { return __builtin_ffs(static_cast<int>(m)); }

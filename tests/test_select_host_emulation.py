@@ -83,3 +83,15 @@ def test_select_candidates_host_emulation(emul, name, per, C, k, kind):
         keys = L + rng.integers(0, 700, size=C)
     got = run(emul, per, keys, idx, k, L)
     assert got == brute(keys, idx, k)
+
+
+def test_bf16_ge_mask_word_parallel_host_emulation(emul):
+    """The selector's test of two bf16 keys per 32-bit word against a floor (subtracting the
+    floor's raw bits from both halves at once, a byte permute gathering the flags) equals
+    the key-by-key comparison on 400 000 random chunks, including +-0, the extremes, keys
+    one step either side of the floor and every tail length."""
+    r = subprocess.run([emul, "gemask"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    bad, runs = (int(x) for x in r.stdout.split())
+    assert runs == 400000
+    assert bad == 0
