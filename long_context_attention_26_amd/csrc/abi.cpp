@@ -704,6 +704,10 @@ int hcsa_decode_step(const hcsa_pool_job* jobs, int n_jobs, const void* q_idx, i
     return hip_status(hcsa::launch_decode_step(a, pc_step, ph_step, workspace, mx_bytes,
                                                mx_bytes + sync_bytes, s),
                       "hcsa_decode_step");
+  if (!fused && hcsa::decode_step_scores_ok(a, pc, ph))
+    return hip_status(hcsa::launch_decode_step_scores(a, pc_step, ph_step, workspace,
+                                                      mx_bytes, mx_bytes + sync_bytes, s),
+                      "hcsa_decode_step");
   // other shapes: the two calls in turn, on the same parts of the workspace
   rc = index_topk_impl(q_idx, q_dtype, w_idx, k_idx, k_dtype, k_bstride, k_scales, ks_bstride,
                        B, Nq, H_I, d_I, N, ratio, pos0, seq_pos, pages, k, score_dtype,

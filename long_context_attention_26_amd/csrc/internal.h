@@ -34,6 +34,17 @@ bool topk_plan_ok(const TopkPlan& plan);        // the row length is within the 
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
                        int64_t row_stride, int Nq, int ratio, int64_t pos0,
                        const int64_t* seq_pos, int32_t* idx, void* ws, hipStream_t s);
+// The segment path's device view and workspace of a plan (the decode step runs the extract
+// launch itself and the per-row resolve inside its own launch), and the extract launch.
+namespace segsel {
+struct TopkDev;
+struct SegWs;
+}
+void seg_select_view(const TopkPlan& plan, const void* scores, int64_t row_stride, int Nq,
+                     int ratio, int64_t pos0, const int64_t* seq_pos, int32_t* idx, void* ws,
+                     segsel::TopkDev* P, segsel::SegWs* S, int* vec);
+hipError_t launch_seg_extract(const segsel::TopkDev& P, const segsel::SegWs& S, int vec,
+                              int key_bits, int rows, hipStream_t s);
 
 // ---- indexer.hip
 hipError_t launch_index_scores(const void* q, int q_dtype, const float* w, const void* kx,
@@ -170,5 +181,12 @@ AttnPlan plan_step_hca(int B, int Nq, int H, int d, int N_h);
 size_t decode_step_sync_bytes(int rows);
 hipError_t launch_decode_step(const DecodeStepArgs& a, const AttnPlan& pc, const AttnPlan& ph,
                               void* ws, size_t sync_off, size_t attn_off, hipStream_t s);
+// bf16 or fp32 indexer keys at decode (few long rows): the score-array form (pooling, key
+// scan writing scores, segment extract, resolve + CSA beside the HCA splits, merge); its
+// selection state is laid out as the selector's own call lays it out, at the workspace start
+bool decode_step_scores_ok(const DecodeStepArgs& a, const AttnPlan& pc, const AttnPlan& ph);
+hipError_t launch_decode_step_scores(const DecodeStepArgs& a, const AttnPlan& pc,
+                                     const AttnPlan& ph, void* ws, size_t sync_off,
+                                     size_t attn_off, hipStream_t s);
 
 }  // namespace hcsa

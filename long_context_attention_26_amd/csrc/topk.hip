@@ -29,6 +29,7 @@
 #include "common.h"
 #include "internal.h"
 #include "select_dev.h"
+#include "seg_dev.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -39,30 +40,7 @@ namespace {
 
 using namespace sel;
 
-struct TopkDev {
-  const void* scores;
-  int64_t row_stride;   // elements
-  int Nq, N, ratio, k;
-  int64_t pos0;
-  const int64_t* seq_pos;   // [B] or null
-  int32_t* idx;         // [rows][k]
-};
-
-__device__ __forceinline__ int visible(const TopkDev& P, int row) {
-  const int64_t p = query_pos(P.seq_pos, P.pos0, row / P.Nq, row % P.Nq);
-  const int64_t v = (p + 1) / P.ratio;
-  return static_cast<int>(v < P.N ? v : P.N);
-}
-
-// A row of scores of a call as a RowView.
-template <int KB>
-__device__ __forceinline__ RowView<KB> row_view(const TopkDev& P, int row, int vec) {
-  using KT = typename RowView<KB>::KT;
-  const char* p = static_cast<const char*>(P.scores) +
-                  static_cast<int64_t>(row) * P.row_stride * sizeof(KT);
-  const int nv = visible(P, row);
-  return RowView<KB>(p, nv, vec ? P.N / RowView<KB>::EPC : 0);
-}
+using namespace segsel;
 
 // ---------------------------------------------------------------- many rows: one block per row
 
@@ -293,21 +271,6 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
 
 // ---------------------------------------------------------------- few long rows: segments
 
-constexpr int kSegKeys = 8192;            // keys per segment (one extract block)
-constexpr int kSegCap = 1024;             // candidate list per segment
-constexpr int kSegThreads = 256;
-constexpr int kFloorSamples = 4096;       // 16 per thread
-constexpr int kResThreads = 512;
-constexpr int kResPer = 16;               // candidates per resolve thread at most
-constexpr int kResMax = kResThreads * kResPer;
-constexpr int kResMaxSeg = 4096;          // segments per row (rows of up to 32M keys)
-
-struct SegWs {
-  uint32_t* floor;    // [rows]
-  uint32_t* cnt;      // [rows][nseg]   keys >= floor per segment (may exceed the cap)
-  uint64_t* cand;     // [rows][nseg][kSegCap]   key << 32 | index
-  int nseg;
-};
 
 // The row's candidate floor from 4096 keys in 32 runs of 16 consecutive 16-byte chunks (two
 // cache lines) at evenly spaced positions; every block of the row samples the same keys
@@ -403,6 +366,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_extract_kernel(TopkDev P, Seg
   __shared__ int s_w[W];
   __shared__ uint32_t s_min[W];
   const int row = blockIdx.y, seg = blockIdx.x;
+  if (S.clear != nullptr && row == 0 && seg == 0 && threadIdx.x == 0) *S.clear = 0u;
   const V_t V = row_view<KB>(P, row, vec);
   if (P.k >= V.nv || seg * kSegKeys >= V.nv) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -454,8 +418,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_extract_kernel(TopkDev P, Seg
   if (threadIdx.x == 0) S.cnt[static_cast<int64_t>(row) * S.nseg + seg] = static_cast<uint32_t>(total);
 }
 
-// grid: rows; block 512.  The segment lists concatenated in segment order are the row's
-// candidates in index order; thread t takes a contiguous run of them.
+// grid: rows; block 512.
 template <int KB>
 __global__ __launch_bounds__(kResThreads) void seg_resolve_kernel(TopkDev P, SegWs S, int vec) {
   constexpr int W = kResThreads / 64;
@@ -465,72 +428,8 @@ __global__ __launch_bounds__(kResThreads) void seg_resolve_kernel(TopkDev P, Seg
   __shared__ int s_hist[2][256];
   __shared__ int s_sel[4];
   __shared__ int s_over;
-  const int row = blockIdx.x;
-  const RowView<KB> V = row_view<KB>(P, row, vec);
-  const int nv = V.nv;
-  int32_t* out = P.idx + static_cast<int64_t>(row) * P.k;
-  if (P.k >= nv) {
-    take_all(nv, P.k, out, kResThreads);
-    return;
-  }
-  const int nseg = (nv + kSegKeys - 1) / kSegKeys;   // segments holding visible keys
-  const uint32_t* cnt = S.cnt + static_cast<int64_t>(row) * S.nseg;
-  if (threadIdx.x < 64) {                        // prefix of the listed counts, 64 at a time
-    const int lane = threadIdx.x;
-    int carry = 0;
-    bool over = false;
-    for (int base = 0; base < nseg; base += 64) {
-      const int sg = base + lane;
-      const int c = sg < nseg ? static_cast<int>(cnt[sg]) : 0;
-      over |= c > kSegCap;
-      int inc = c < kSegCap ? c : kSegCap;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(inc, d, kWave);
-        if (lane >= d) inc += y;
-      }
-      if (sg < nseg) s_pre[sg + 1] = carry + inc;
-      carry += __shfl(inc, 63, kWave);
-    }
-    const bool any_over = __ballot(over) != 0;
-    if (lane == 0) {
-      s_pre[0] = 0;
-      s_over = any_over;
-    }
-  }
-  __syncthreads();
-  const int C = s_pre[nseg];
-  if (s_over || C < P.k || C > kResMax) {
-    select_exact_row<KB, kResThreads>(V, P.k, out, s_cnt, s_gt, s_eq);
-    return;
-  }
-  const int per = (C + kResThreads - 1) / kResThreads;
-  const int g0 = min(C, static_cast<int>(threadIdx.x) * per);
-  const int my = min(per, C - g0);
-  // segment of the first candidate: the last s with s_pre[s] <= g0
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_pre[mid] <= g0) lo = mid;
-    else hi = mid - 1;
-  }
-  int seg = lo;
-  uint32_t ck[kResPer];
-  int32_t cj[kResPer];
-#pragma unroll
-  for (int u = 0; u < kResPer; ++u) {
-    ck[u] = 0u;
-    cj[u] = 0;
-    if (u < my) {
-      const int g = g0 + u;
-      while (g >= s_pre[seg + 1]) ++seg;
-      const uint64_t v = S.cand[(static_cast<int64_t>(row) * S.nseg + seg) * kSegCap + (g - s_pre[seg])];
-      ck[u] = static_cast<uint32_t>(v >> 32);
-      cj[u] = static_cast<int32_t>(v & 0xffffffffu);
-    }
-  }
-  select_candidates<KB, kResThreads, kResPer>(ck, cj, my, S.floor[row], P.k, out, s_gt, s_eq,
-                                              s_hb, s_hist, s_sel);
+  seg_resolve_row<KB>(P, S, vec, blockIdx.x, s_pre, s_cnt, s_gt, s_eq, s_hb, s_hist, s_sel,
+                      &s_over);
 }
 
 }  // namespace
@@ -557,40 +456,55 @@ TopkPlan plan_topk(int score_dtype, int rows, int N, int k) {
 
 bool topk_plan_ok(const TopkPlan& plan) { return plan.rows_path || plan.nseg <= kResMaxSeg; }
 
+void seg_select_view(const TopkPlan& plan, const void* scores, int64_t row_stride, int Nq,
+                     int ratio, int64_t pos0, const int64_t* seq_pos, int32_t* idx, void* ws,
+                     segsel::TopkDev* P, segsel::SegWs* S, int* vec) {
+  *P = segsel::TopkDev{};
+  P->scores = scores;
+  P->row_stride = row_stride;
+  P->Nq = Nq;
+  P->N = plan.N;
+  P->ratio = ratio;
+  P->k = plan.k;
+  P->pos0 = pos0;
+  P->seq_pos = seq_pos;
+  P->idx = idx;
+  const int esz = plan.key_bits / 8;
+  *vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride * esz) % 16 == 0;
+  *S = segsel::SegWs{};
+  if (!plan.rows_path) {
+    S->floor = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + plan.floor_off);
+    S->cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + plan.cnt_off);
+    S->cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + plan.cand_off);
+    S->nseg = plan.nseg;
+  }
+}
+
+hipError_t launch_seg_extract(const segsel::TopkDev& P, const segsel::SegWs& S, int vec,
+                              int key_bits, int rows, hipStream_t s) {
+  const dim3 grid(S.nseg, rows);
+  if (key_bits == 16) seg_extract_kernel<16><<<grid, kSegThreads, 0, s>>>(P, S, vec);
+  else seg_extract_kernel<32><<<grid, kSegThreads, 0, s>>>(P, S, vec);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkPlan& plan, const void* scores, int score_dtype,
                        int64_t row_stride, int Nq, int ratio, int64_t pos0,
                        const int64_t* seq_pos, int32_t* idx, void* ws, hipStream_t s) {
   (void)score_dtype;
-  TopkDev P{};
-  P.scores = scores;
-  P.row_stride = row_stride;
-  P.Nq = Nq;
-  P.N = plan.N;
-  P.ratio = ratio;
-  P.k = plan.k;
-  P.pos0 = pos0;
-  P.seq_pos = seq_pos;
-  P.idx = idx;
-  const int esz = plan.key_bits / 8;
-  const int vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride * esz) % 16 == 0;
+  TopkDev P;
+  SegWs S;
+  int vec = 0;
+  seg_select_view(plan, scores, row_stride, Nq, ratio, pos0, seq_pos, idx, ws, &P, &S, &vec);
   if (plan.rows_path) {
     if (plan.key_bits == 16) topk_rows_kernel<16><<<plan.rows, kRowsThreads, 0, s>>>(P, vec);
     else topk_rows_kernel<32><<<plan.rows, kRowsThreads, 0, s>>>(P, vec);
     return hipGetLastError();
   }
-  SegWs S;
-  S.floor = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + plan.floor_off);
-  S.cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + plan.cnt_off);
-  S.cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + plan.cand_off);
-  S.nseg = plan.nseg;
-  const dim3 grid(plan.nseg, plan.rows);
-  if (plan.key_bits == 16) {
-    seg_extract_kernel<16><<<grid, kSegThreads, 0, s>>>(P, S, vec);
-    seg_resolve_kernel<16><<<plan.rows, kResThreads, 0, s>>>(P, S, vec);
-  } else {
-    seg_extract_kernel<32><<<grid, kSegThreads, 0, s>>>(P, S, vec);
-    seg_resolve_kernel<32><<<plan.rows, kResThreads, 0, s>>>(P, S, vec);
-  }
+  const hipError_t e = launch_seg_extract(P, S, vec, plan.key_bits, plan.rows, s);
+  if (e != hipSuccess) return e;
+  if (plan.key_bits == 16) seg_resolve_kernel<16><<<plan.rows, kResThreads, 0, s>>>(P, S, vec);
+  else seg_resolve_kernel<32><<<plan.rows, kResThreads, 0, s>>>(P, S, vec);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 """One decode step as one call (hcsa_decode_step: floors and pooling in one launch; the key
-scan; per-row resolve + CSA blocks beside the HCA splits in one launch; the split merge) against
+scan; per-row resolve + CSA blocks beside the HCA splits in one launch; the split merge; with
+bf16 indexer keys the scan writes scores and a segment extract launch lists the candidates) against
 the same step as two calls (hcsa_csa_pool_index_topk, then hcsa_csa_hca_attn): pooled caches
 and selection equal bit for bit; both attentions, split differently in the four-launch
 form, within the bound that their bf16 probabilities allow between two split plans.  Both
@@ -24,8 +25,13 @@ CASES = [
     # few and many HCA units per sequence
     dict(name="w5-b2-64k", cid=5, B=2, T=65536),
     dict(name="w5-b300-short", cid=5, B=300, T=128 * 40),
-    # other shapes take the two calls in turn inside the same call
+    # bf16 indexer keys: the score-array form (scan writing scores, segment extract, resolve +
+    # CSA beside the HCA splits, merge)
     dict(name="cfg2-bf16-keys", cid=2, B=2, T=32768),
+    dict(name="cfg2-full", cid=2, B=None, T=None),
+    dict(name="cfg3-full", cid=3, B=None, T=None),
+    dict(name="cfg2-b5-ragged-tail", cid=2, B=5, T=128 * 333),
+    # other shapes take the two calls in turn inside the same call
     dict(name="cfg1-fp32", cid=1, B=None, T=None),
 ]
 

@@ -27,6 +27,11 @@ CASES = [
     dict(name="ragged", paged=False, ring=False, pos=[128 * 150 + 127, 9000, 15001]),
     # both
     dict(name="paged-ragged", paged=True, ring=False, pos=[128 * 159 + 5, 4097, 12345]),
+    # bf16 indexer keys (the score-array form of the step)
+    dict(name="bf16-keys-paged-ring-pool", paged=True, ring=True, pos=[128 * 150 + 127] * 3,
+         keys="bf16"),
+    dict(name="bf16-keys-paged-ragged", paged=True, ring=False, pos=[128 * 159 + 5, 4097, 12345],
+         keys="bf16"),
 ]
 
 
@@ -66,14 +71,17 @@ def test_decode_step_layouts(H, gpu, case):
     ragged = len(set(pos)) > 1
 
     # reference caches: every block pooled from the contiguous raw tokens
+    mx = case.get("keys", "mxfp4") == "mxfp4"
     ref = dict(Kc=torch.empty(B, N, d, dtype=bf, device=gpu),
                Vc=torch.empty(B, N, d, dtype=bf, device=gpu),
-               Ic=torch.empty(B, N, d_I // 2, dtype=torch.uint8, device=gpu),
-               Ics=torch.empty(B, N, d_I // 32, dtype=torch.uint8, device=gpu),
+               Ic=(torch.empty(B, N, d_I // 2, dtype=torch.uint8, device=gpu) if mx
+                   else torch.empty(B, N, d_I, dtype=bf, device=gpu)),
                Kh=torch.empty(B, N_h, d, dtype=bf, device=gpu),
                Vh=torch.empty(B, N_h, d, dtype=bf, device=gpu))
+    if mx:
+        ref["Ics"] = torch.empty(B, N, d_I // 32, dtype=torch.uint8, device=gpu)
     H.compress_kv_batched([H.pool_job(K, om["ck"], 4, ref["Kc"]), H.pool_job(V, om["cv"], 4, ref["Vc"]),
-                           H.pool_job(I, om["ik"], 4, ref["Ic"], ref["Ics"]),
+                           H.pool_job(I, om["ik"], 4, ref["Ic"], ref.get("Ics")),
                            H.pool_job(K, om["hk"], 128, ref["Kh"]),
                            H.pool_job(V, om["hv"], 128, ref["Vh"])], B)
 
@@ -118,7 +126,7 @@ def test_decode_step_layouts(H, gpu, case):
                               ("Kh", raw_k, "hk", 128), ("Vh", raw_v, "hv", 128)):
             j = p // r
             ys = None
-            if name == "Ic":
+            if name == "Ic" and mx:
                 ys = c["Ics"] if case["paged"] else c["Ics"][:, j:j + 1]
             y = c[name] if case["paged"] else c[name][:, j:j + 1]
             out.append(H.pool_job(x, om[o], r, y, ys, T=r, pos0=j * r))
@@ -142,13 +150,13 @@ def test_decode_step_layouts(H, gpu, case):
     o1 = outs()
     H.decode_step(jobs(c1), qi, wi, c1["Ic"], H.BF16, idx1, q, c1["Kc"], c1["Vc"], N, k, raw_k,
                   raw_v, 0, w, 4, c1["Kh"], c1["Vh"], N_h, 128, pos0, scale, *o1,
-                  k_scales=c1["Ics"], seq_pos=sp, block_table=table, raw_ring=ring)
+                  k_scales=c1.get("Ics"), seq_pos=sp, block_table=table, raw_ring=ring)
     # ---- the same step as two calls
     c2 = layout(start)
     idx2 = torch.full((B, 1, k), -9, dtype=torch.int32, device=gpu)
     o2 = outs()
     H.csa_pool_index_topk(jobs(c2), qi, wi, c2["Ic"], N, 4, pos0, k, H.BF16, idx2,
-                          k_scales=c2["Ics"], seq_pos=sp, block_table=table, raw_ring=ring)
+                          k_scales=c2.get("Ics"), seq_pos=sp, block_table=table, raw_ring=ring)
     H.csa_hca_attn(q, c2["Kc"], c2["Vc"], N, idx2, raw_k, raw_v, 0, w, 4, c2["Kh"], c2["Vh"], N_h,
                    128, pos0, scale, *o2, seq_pos=sp, block_table=table, raw_ring=ring)
     torch.cuda.synchronize()
