@@ -41,14 +41,14 @@ __device__ __forceinline__ RowView<KB> row_view(const TopkDev& P, int row, int v
   const int nv = visible(P, row);
   return RowView<KB>(p, nv, vec ? P.N / RowView<KB>::EPC : 0);
 }
-constexpr int kSegKeys = 8192;            // keys per segment (one extract block)
-constexpr int kSegCap = 1024;             // candidate list per segment
+constexpr int kSegKeys = 2048;            // keys per segment (one extract block)
+constexpr int kSegCap = 512;              // candidate list per segment
 constexpr int kSegThreads = 256;
 constexpr int kFloorSamples = 4096;       // 16 per thread
 constexpr int kResThreads = 512;
 constexpr int kResPer = 16;               // candidates per resolve thread at most
 constexpr int kResMax = kResThreads * kResPer;
-constexpr int kResMaxSeg = 4096;          // segments per row (rows of up to 32M keys)
+constexpr int kResMaxSeg = 16384;         // segments per row (rows of up to 32M keys)
 
 struct SegWs {
   uint32_t* floor;    // [rows]

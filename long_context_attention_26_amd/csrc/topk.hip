@@ -17,7 +17,7 @@
 // the row is >= L while at least k keys are (checked).
 //  - Many short rows (prefill: >= 64 rows of <= 128K keys): one block per row streams the
 //    row once (topk_rows_kernel), sampling the first chunks it loads.
-//  - Otherwise (decode: a few long rows): seg_extract_kernel (a block per 8192-key segment:
+//  - Otherwise (decode: a few long rows): seg_extract_kernel (a block per 2048-key segment:
 //    the row's floor from 4096 keys at evenly spaced 16-byte chunks, the same in every
 //    block of the row, then the segment's keys >= L into its candidate list, in index
 //    order) and seg_resolve_kernel (a block per row: T among the concatenated lists by
