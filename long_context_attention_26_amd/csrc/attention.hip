@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnDev A) {
 
 // grid: (splits, rows); block 256 (4 waves).
 template <bool CSA>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnDev A) {
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnDev A) {
   __shared__ int s_code[kMfmaMaxChunk];
   __shared__ float s_o[4][16][129];
   __shared__ float s_ml[4][2][16];

@@ -159,9 +159,9 @@ __device__ __forceinline__ void attn_mfma_block(const AttnDev& A, int split, int
   float l_run = 0.0f;
   const float sl2 = A.scale * 1.4426950408889634f;  // logits in base 2
 
-  for (int base = wave * 32; base < cnt; base += 128) {
-    // ---- K rows for the A operand: keys base + col and base + 16 + col
-    u32x4 ka[2][4];
+  // K rows for the A operand (keys base + col and base + 16 + col) and V slices (keys
+  // base + 4g + j for j < 4 and base + 16 + 4g + (j - 4), channels 8col..8col+7)
+  auto load = [&](int base, u32x4 (&ka)[2][4], u32x4 (&vv)[8], bool (&ok)[8]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int pos = base + 16 * t + col;
@@ -175,20 +175,27 @@ __device__ __forceinline__ void attn_mfma_block(const AttnDev& A, int split, int
         for (int s = 0; s < 4; ++s) ka[t][s] = u32x4{0, 0, 0, 0};
       }
     }
-    // ---- V slices: keys base + 4g + j (j<4) and base + 16 + 4g + (j-4), channels 8col..8col+7
-    u32x4 vv[8];
-    bool ok[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int pos = base + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
       const int c = pos < cnt ? s_code[pos] : -1;
       ok[j] = c != -1;
-      if (ok[j])
-        vv[j] = *reinterpret_cast<const u32x4*>(key_row<uint16_t>(A, r.b, c, true) + 8 * col);
-      else
-        vv[j] = u32x4{0, 0, 0, 0};
+      vv[j] = ok[j] ? *reinterpret_cast<const u32x4*>(key_row<uint16_t>(A, r.b, c, true) + 8 * col)
+                    : u32x4{0, 0, 0, 0};
     }
-    attend_step(ka, vv, ok, qB, acc, m_run, l_run, sl2);
+  };
+  // wave w takes the 32-key steps at w*32, w*32 + 128, ...; the next step's rows load while
+  // the current one is computed (the same steps in the same order as one at a time)
+  u32x4 kaA[2][4], vvA[8], kaB[2][4], vvB[8];
+  bool okA[8], okB[8];
+  const int w0 = wave * 32;
+  if (w0 < cnt) load(w0, kaA, vvA, okA);
+  for (int base = w0; base < cnt; base += 256) {
+    if (base + 128 < cnt) load(base + 128, kaB, vvB, okB);
+    attend_step(kaA, vvA, okA, qB, acc, m_run, l_run, sl2);
+    if (base + 128 >= cnt) break;
+    if (base + 256 < cnt) load(base + 256, kaA, vvA, okA);
+    attend_step(kaB, vvB, okB, qB, acc, m_run, l_run, sl2);
   }
 
   combine_waves(A, acc, m_run, l_run, s_o, s_ml, split, row, tid);
