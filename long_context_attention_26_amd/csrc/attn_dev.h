@@ -22,6 +22,11 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f3
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 2^x on the transcendental unit.  The library's exp2f only adds a rescaling for results
+// below the smallest normal float (x < -126); a softmax weight that small changes no sum,
+// and 2^-inf is still 0.
+__device__ __forceinline__ float exp2_unit(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // One 32-key step of the MFMA attention (16 heads, d = 128), for lane (head col, k-group g):
 // S^T tiles t = 0, 1 from the K rows ka[t] (keys 16t + col of the step), online softmax of
 // the logits of keys 16*(j/4) + 4g + j%4 (valid where ok[j]), O^T += V^T P^T with the V rows
@@ -48,13 +53,13 @@ __device__ __forceinline__ void attend_step(const u32x4 (&ka)[2][4], const u32x4
   mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
   const float m_new = fmaxf(m_run, mt);
   if (m_new == -INFINITY) return;        // nothing visible yet for this head
-  const float alpha = exp2f(m_run - m_new);
+  const float alpha = exp2_unit(m_run - m_new);
   m_run = m_new;
   float pj[8];
   float psum = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    pj[j] = exp2f(lg[j] - m_new);
+    pj[j] = exp2_unit(lg[j] - m_new);
     psum += pj[j];
   }
   l_run = l_run * alpha + psum;
@@ -326,14 +331,33 @@ __device__ __forceinline__ void hca_decode_block(const AttnDev& A, int split, in
                     : u32x4{0, 0, 0, 0};
     }
   };
+  // a step wholly inside the run (the wave-uniform common case) loads without per-entry
+  // checks; only the run's last step may be partial
+  auto load_step = [&](int base, u32x4 (&ka)[2][4], u32x4 (&vv)[8], bool (&ok)[8]) {
+    if (base + 32 > w1) {
+      load(base, ka, vv, ok);
+      return;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t o = erow(base + 16 * t + col);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[t][s] = *reinterpret_cast<const u32x4*>(kb + o + 32 * s + 8 * g);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ok[j] = true;
+      vv[j] = *reinterpret_cast<const u32x4*>(vb + erow(base + 16 * (j >> 2) + 4 * g + (j & 3)) + 8 * col);
+    }
+  };
   u32x4 kaA[2][4], vvA[8], kaB[2][4], vvB[8];
   bool okA[8], okB[8];
-  if (w0 < w1) load(w0, kaA, vvA, okA);
+  if (w0 < w1) load_step(w0, kaA, vvA, okA);
   for (int base = w0; base < w1; base += 64) {
-    if (base + 32 < w1) load(base + 32, kaB, vvB, okB);
+    if (base + 32 < w1) load_step(base + 32, kaB, vvB, okB);
     attend_step(kaA, vvA, okA, qB, acc, m_run, l_run, sl2);
     if (base + 32 >= w1) break;
-    if (base + 64 < w1) load(base + 64, kaA, vvA, okA);
+    if (base + 64 < w1) load_step(base + 64, kaA, vvA, okA);
     attend_step(kaB, vvB, okB, qB, acc, m_run, l_run, sl2);
   }
   combine_waves(A, acc, m_run, l_run, s_o, s_ml, split, row, tid);
