@@ -200,6 +200,7 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
   };
   const int nv = tok_ok ? visible(tok) : 0;
   const int nv_max = visible(min(t0 + kTokTile, A.Nq) - 1);   // tokens ascend
+  const int nv_min = visible(t0);                 // every token of the block sees these
   const int ntiles = (nv_max + kHKeys - 1) / kHKeys;
   const int64_t row = static_cast<int64_t>(b) * A.Nq + tok;
 
@@ -274,18 +275,28 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
     }
     const int kb = tile * kHKeys;
     float mx = -INFINITY;
+    if (kb + kHKeys <= nv_min) {                  // block-uniform: no entry of the tile masked
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int e = kb + 32 * h2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        st[h2][r] = e < nv ? st[h2][r] * sl2 : -INFINITY;
-        mx = fmaxf(mx, st[h2][r]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          st[h2][r] *= sl2;
+          mx = fmaxf(mx, st[h2][r]);
+        }
+    } else {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = kb + 32 * h2 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          st[h2][r] = e < nv ? st[h2][r] * sl2 : -INFINITY;
+          mx = fmaxf(mx, st[h2][r]);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float m_new = fmaxf(m_run, mx);
     if (__ballot(m_new > m_run)) {                // some row's maximum moved: rescale
-      const float alpha = m_new > m_run ? exp2f(m_run - m_new) : 1.0f;   // exp2(-inf) = 0
+      const float alpha = m_new > m_run ? exp2_unit(m_run - m_new) : 1.0f;   // exp2(-inf) = 0
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[ct] *= alpha;
       l_run *= alpha;
@@ -299,8 +310,8 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float p0 = exp2f(st[h2][8 * s + 2 * m] - mref);
-          const float p1 = exp2f(st[h2][8 * s + 2 * m + 1] - mref);
+          const float p0 = exp2_unit(st[h2][8 * s + 2 * m] - mref);
+          const float p1 = exp2_unit(st[h2][8 * s + 2 * m + 1] - mref);
           l_run += p0 + p1;
           pb[s][m] = pack_bf16x2(p0, p1);
         }
