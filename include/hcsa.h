@@ -26,7 +26,8 @@
  *     iff (j+1)*r <= p+1.  Query i of sequence b sits at position pos0 + i, or at
  *     seq_pos[b] + i when the call is given seq_pos (ragged batches: each sequence at its
  *     own length).
- *   - one KV head shared by all query heads (MQA); logits are scale * q.k.
+ *   - one KV head shared by all query heads (MQA); logits are scale * q.k, with scale
+ *     positive and finite (the attention calls reject other values with HCSA_EINVAL).
  *   - MXFP4: OCP MX e2m1 elements with one e8m0 scale per 32 elements, scale exponent
  *     floor(log2 amax) - 2 (clamped to [-127, 127]; amax = 0 gives -127), elements
  *     rounded to nearest-even on the e2m1 grid and saturated at +-6.  Two elements per

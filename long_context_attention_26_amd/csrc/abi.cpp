@@ -1,5 +1,6 @@
 // C ABI of libhcsa: argument validation on the host, then asynchronous launches on the
 // caller's stream.  No call allocates device memory or synchronizes.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -60,7 +61,8 @@ int check_attn_common(const void* q, int kv_dtype, int B, int Nq, int H, int d, 
   if (H < 1 || H > 64) return fail(HCSA_EINVAL, "H must be in [1, 64]");
   if (d < 8 || d > 256 || d % 8 != 0) return fail(HCSA_EINVAL, "d must be a multiple of 8 in [8, 256]");
   if (H * d > 4096) return fail(HCSA_EINVAL, "H*d must be <= 4096");
-  if (!(scale == scale)) return fail(HCSA_EINVAL, "scale is NaN");
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(HCSA_EINVAL, "scale must be positive and finite");
   if (ratio < 1) return fail(HCSA_EINVAL, "ratio must be >= 1");
   if (pos0 < 0) return fail(HCSA_EINVAL, "pos0 must be >= 0");
   if (!q || !out || !lse) return fail(HCSA_EINVAL, "q, out and lse must be non-null");

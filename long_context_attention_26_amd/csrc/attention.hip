@@ -275,25 +275,24 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
     }
     const int kb = tile * kHKeys;
     float mx = -INFINITY;
+    // the logits stay unscaled (scale > 0 keeps their order); the scale enters the
+    // exponent's fma below
     if (kb + kHKeys <= nv_min) {                  // block-uniform: no entry of the tile masked
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          st[h2][r] *= sl2;
-          mx = fmaxf(mx, st[h2][r]);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[h2][r]);
     } else {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int e = kb + 32 * h2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          st[h2][r] = e < nv ? st[h2][r] * sl2 : -INFINITY;
+          st[h2][r] = e < nv ? st[h2][r] : -INFINITY;
           mx = fmaxf(mx, st[h2][r]);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
     const float m_new = fmaxf(m_run, mx);
     if (__ballot(m_new > m_run)) {                // some row's maximum moved: rescale
       const float alpha = m_new > m_run ? exp2_unit(m_run - m_new) : 1.0f;   // exp2(-inf) = 0
@@ -302,7 +301,7 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
       l_run *= alpha;
       m_run = m_new;
     }
-    const float mref = m_run == -INFINITY ? 0.0f : m_run;
+    const float mneg = m_run == -INFINITY ? 0.0f : -m_run;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       u32x4 pb[2];
@@ -310,8 +309,8 @@ __global__ __launch_bounds__(512) void hca_tiled_kernel(AttnDev A) {
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float p0 = exp2_unit(st[h2][8 * s + 2 * m] - mref);
-          const float p1 = exp2_unit(st[h2][8 * s + 2 * m + 1] - mref);
+          const float p0 = exp2_unit(fmaf(st[h2][8 * s + 2 * m], sl2, mneg));
+          const float p1 = exp2_unit(fmaf(st[h2][8 * s + 2 * m + 1], sl2, mneg));
           l_run += p0 + p1;
           pb[s][m] = pack_bf16x2(p0, p1);
         }

@@ -115,6 +115,11 @@ def test_attention_validation(H):
                                  16, 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EALIGN
     assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 0, 4095, None, None, H.BF16, 1, 1,
                                  16, 128, 0.1, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
+    # the logit scale must be positive and finite
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 128, 4095, None, None, H.BF16, 1, 1,
+                                     16, 128, bad, FAKE, FAKE, FAKE, hws, None) == H.EINVAL
+        assert b"scale" in L.hcsa_last_error()
     # paged caches: the ratio must divide the 128-token page, the table be 4-byte aligned
     pg = ctypes.byref(H.Pages(FAKE, 64))
     assert L.hcsa_hca_dense_attn(FAKE, FAKE, FAKE, 0, 32, 96, 4095, None, pg, H.BF16, 1, 1,
