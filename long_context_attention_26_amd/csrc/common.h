@@ -29,8 +29,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return b >> 16;
 }
 
+// Two values to bf16 (lo in the low half) by the conversion instruction: round to nearest
+// even, the same bits as f32_to_bf16_bits for every non-NaN value (a NaN stays a NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
 }
 
 // ---------------------------------------------------------------- order-preserving keys
