@@ -82,8 +82,12 @@ __device__ __forceinline__ int64_t query_pos(const int64_t* seq_pos, int64_t pos
   return (seq_pos ? seq_pos[b] : pos0) + i;
 }
 
+// max(x, 0) for every finite x in one median-of-three instruction (with +inf as the third
+// operand the compiler turns the median into a maximum that first canonicalizes x: two
+// instructions).  A sum of weighted ReLUs starting from +0 never ends at -0 whichever zero
+// this gives for -0.
 __device__ __forceinline__ float relu(float x) {
-  return __builtin_amdgcn_fmed3f(x, 0.0f, __builtin_inff());
+  return __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e+38f);
 }
 
 // ---------------------------------------------------------------- wave reductions
