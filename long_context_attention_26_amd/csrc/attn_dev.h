@@ -141,13 +141,39 @@ __device__ __forceinline__ void attn_mfma_block(const AttnDev& A, int split, int
   const RowKeys r = row_keys<CSA>(A, row);
   const int k0 = split * A.chunk;
   const int cnt = max(0, min(A.chunk, r.L - k0));
-  for (int i = tid; i < cnt; i += 256) s_code[i] = key_code<CSA, COH>(A, r, row, k0 + i);
+  // Contiguous caches (raw rows contiguous or in a ring) whose element offsets within a
+  // sequence fit in 31 bits: the list holds each key's element offset instead of its code
+  // (>= 0: compressed row, < 0: -1 - offset of a raw row, kNoKey: none), so a load is one
+  // add to the sequence's base.  Paged caches keep the codes.
+  constexpr int kNoKey = INT32_MIN;
+  const int64_t raw_rows = A.raw_ring ? A.raw_ring : A.T_raw;
+  const bool flat = A.pm.table == nullptr && static_cast<int64_t>(A.N) * A.d < (int64_t{1} << 31) &&
+                    raw_rows * A.d < (int64_t{1} << 31);          // block-uniform
+  for (int i = tid; i < cnt; i += 256) {
+    const int c = key_code<CSA, COH>(A, r, row, k0 + i);
+    int v = c;
+    if (flat) {
+      if (c == -1) {
+        v = kNoKey;
+      } else if (c >= 0) {
+        v = c * A.d;
+      } else {
+        const int64_t t = -static_cast<int64_t>(c) - 2;
+        v = -1 - static_cast<int>((A.raw_ring ? (t & (A.raw_ring - 1)) : t) * A.d);
+      }
+    }
+    s_code[i] = v;
+  }
   __syncthreads();
 
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int col = lane & 15;   // head owned by this lane
   const int g = lane >> 4;     // k-group
+  const uint16_t* kc_b = static_cast<const uint16_t*>(A.kc) + r.b * A.c_bstride;
+  const uint16_t* vc_b = static_cast<const uint16_t*>(A.vc) + r.b * A.c_bstride;
+  const uint16_t* kr_b = static_cast<const uint16_t*>(A.k_raw) + r.b * A.raw_bstride;
+  const uint16_t* vr_b = static_cast<const uint16_t*>(A.v_raw) + r.b * A.raw_bstride;
 
   // B operand of S^T = K Q^T: Q[head col][32s + 8g .. +8] for s = 0..3.
   u32x4 qB[4];
@@ -167,6 +193,30 @@ __device__ __forceinline__ void attn_mfma_block(const AttnDev& A, int split, int
   // K rows for the A operand (keys base + col and base + 16 + col) and V slices (keys
   // base + 4g + j for j < 4 and base + 16 + 4g + (j - 4), channels 8col..8col+7)
   auto load = [&](int base, u32x4 (&ka)[2][4], u32x4 (&vv)[8], bool (&ok)[8]) {
+    if (flat) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int pos = base + 16 * t + col;
+        const int v = pos < cnt ? s_code[pos] : kNoKey;
+        if (v != kNoKey) {
+          const uint16_t* kr = v >= 0 ? kc_b + v : kr_b + (-1 - v);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) ka[t][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) ka[t][s] = u32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int pos = base + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+        const int v = pos < cnt ? s_code[pos] : kNoKey;
+        ok[j] = v != kNoKey;
+        vv[j] = ok[j] ? *reinterpret_cast<const u32x4*>((v >= 0 ? vc_b + v : vr_b + (-1 - v)) + 8 * col)
+                      : u32x4{0, 0, 0, 0};
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int pos = base + 16 * t + col;

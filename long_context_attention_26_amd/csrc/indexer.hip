@@ -228,6 +228,18 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
   constexpr int PPT = (CHUNKS + NT - 1) / NT;     // key-tile pieces per thread
   u32x4 pf[PPT];
   auto fetch = [&](int j0) {
+    if (!A.pm.table && j0 + kGemmTile <= A.N) {
+      // contiguous keys, the whole tile in the row: one run of kGemmTile * DI elements,
+      // piece c at element 8c
+      const uint16_t* tile = kpool + static_cast<int64_t>(b) * A.k_bstride +
+                             static_cast<int64_t>(j0) * DI;
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int c = threadIdx.x + u * NT;
+        pf[u] = c < CHUNKS ? *reinterpret_cast<const u32x4*>(tile + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int c = threadIdx.x + u * NT;
