@@ -128,6 +128,12 @@ struct RowView {
   // permute gathers the eight flags and a multiply packs them into the mask (about 16
   // instructions a chunk instead of 40).
   __device__ uint32_t ge_mask(const u32x4& x, int j0, uint32_t L) const {
+    const uint32_t m = ge_bits(x, L);
+    const int r = nv - j0;
+    return r >= EPC ? m : m & ((1u << r) - 1u);
+  }
+  // the same for a chunk whose keys are all visible
+  __device__ uint32_t ge_bits(const u32x4& x, uint32_t L) const {
     uint32_t m = 0;
     if (L > kSign) {
       const uint32_t lo_raw = L - kSign, span = kSign - 1 - lo_raw;
@@ -149,8 +155,7 @@ struct RowView {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) m |= static_cast<uint32_t>(to_key(raw_of(x, e)) >= L) << e;
     }
-    const int r = nv - j0;
-    return r >= EPC ? m : m & ((1u << r) - 1u);
+    return m;
   }
 };
 

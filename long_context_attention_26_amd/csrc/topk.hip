@@ -48,7 +48,9 @@ using namespace segsel;
 // so one block's loads overlap the others' arithmetic.  Wave w owns a contiguous run of
 // chunks and walks it 64 chunks at a time (index order = wave, step, lane, element); the
 // floor comes from the first key of each lane's first four chunks (up to 2048 samples,
-// loaded anyway), and the stream appends every key >= L to the wave's LDS list.
+// loaded anyway), and the stream appends the index of every key >= L to the wave's LDS
+// list (the threshold search re-reads those keys from the row, which the block has just
+// streamed).
 constexpr int kRowsThreads = 512;
 constexpr int kRowsWaves = kRowsThreads / 64;
 constexpr int kRowsMaxKeys = 131072;
@@ -64,8 +66,7 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
   using V_t = RowView<KB>;
   constexpr int EPC = V_t::EPC;
   constexpr int STEPS = kRowsWaveCap / 64;       // list entries per lane at most
-  __shared__ uint32_t s_ck[kRowsWaves][kRowsWaveCap];
-  __shared__ int32_t s_cj[kRowsWaves][kRowsWaveCap];
+  __shared__ int32_t s_cj[kRowsWaves][kRowsWaveCap];   // candidate indices (keys re-read)
   __shared__ int s_cnt[2][kRowsWaves];
   __shared__ int s_wave[kRowsWaves], s_gt[kRowsWaves], s_eq[kRowsWaves], s_hb[kRowsWaves];
   __shared__ int s_hist[2][256];
@@ -127,31 +128,39 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
   }
 
   // ---- 2. stream the wave's chunks 256 at a time (the next 256 loading meanwhile),
-  // appending keys >= L to the wave's list
+  // appending the indices of keys >= L to the wave's list.  Steps whose chunks are all
+  // whole and visible (every step but a row's last, as a rule) load and test them without
+  // per-chunk checks.
+  const int whole = min(min(V.nfull, nv / EPC), cw1);   // chunks below: whole, visible
   int wslot = 0;
   for (int base = cw0; base < cw1; base += 256) {
     u32x4 nxt[4];
     const bool more = base + 256 < cw1;          // wave-uniform
     if (more) {
+      if (base + 512 <= whole) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int ch = base + 256 + 64 * u + lane;
-        nxt[u] = ch < cw1 ? V.load_raw(ch) : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < 4; ++u)
+          nxt[u] = *reinterpret_cast<const u32x4*>(
+              V.rowp + static_cast<int64_t>(base + 256 + 64 * u + lane) * EPC);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int ch = base + 256 + 64 * u + lane;
+          nxt[u] = ch < cw1 ? V.load_raw(ch) : u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
+    const bool full = base + 256 <= whole;       // wave-uniform
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int ch = base + 64 * u + lane;
-      uint32_t msk = ch < cw1 ? V.ge_mask(cur[u], ch * EPC, L) : 0u;
+      uint32_t msk = full ? V.ge_bits(cur[u], L) : ch < cw1 ? V.ge_mask(cur[u], ch * EPC, L) : 0u;
       int tot;
       int o = wslot + wave_prefix_bits<bits_for(EPC)>(__popc(msk), below, tot);
       while (msk) {
         const int e = __ffs(msk) - 1;
         msk &= msk - 1;
-        if (o < kRowsWaveCap) {
-          s_ck[w][o] = V_t::to_key(V_t::raw_of(cur[u], e));
-          s_cj[w][o] = ch * EPC + e;
-        }
+        if (o < kRowsWaveCap) s_cj[w][o] = ch * EPC + e;
         ++o;
       }
       wslot += tot;
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(TopkDev P, int 
 #pragma unroll
   for (int u = 0; u < STEPS; ++u) {
     const bool in = 64 * u + lane < wslot;
-    ck[u] = in ? s_ck[w][64 * u + lane] : 0u;
+    ck[u] = in ? V.key(s_cj[w][64 * u + lane]) : 0u;   // the row's own key, re-read
     dor |= in ? (ck[u] ^ L) : 0u;
   }
   int hb = 0;
