@@ -22,11 +22,6 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f3
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 2^x on the transcendental unit.  The library's exp2f only adds a rescaling for results
-// below the smallest normal float (x < -126); a softmax weight that small changes no sum,
-// and 2^-inf is still 0.
-__device__ __forceinline__ float exp2_unit(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // One 32-key step of the MFMA attention (16 heads, d = 128), for lane (head col, k-group g):
 // S^T tiles t = 0, 1 from the K rows ka[t] (keys 16t + col of the step), online softmax of
 // the logits of keys 16*(j/4) + 4g + j%4 (valid where ok[j]), O^T += V^T P^T with the V rows

@@ -35,6 +35,11 @@ struct AttnDev {
   float* lse;      // final [rows][H] or partial [splits][rows][H]
 };
 
+// 2^x on the transcendental unit.  The library's exp2f only adds a rescaling for results
+// below the smallest normal float (x < -126); a softmax weight that small changes no sum,
+// and 2^-inf is still 0.
+__device__ __forceinline__ float exp2_unit(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Key-list geometry of one query row.
 struct RowKeys {
   int b;

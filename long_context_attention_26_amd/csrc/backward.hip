@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
     float dsT[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pj = cs[j] != -1 ? exp2f(st[j >> 2][j & 3] * sl2 - lse2_col) : 0.0f;
+      const float pj = cs[j] != -1 ? exp2_unit(st[j >> 2][j & 3] * sl2 - lse2_col) : 0.0f;
       dsT[j] = pj * (dpt[j >> 2][j & 3] - dt_col);
       if (CSA && !DKV && G.rec) {
         // the selected entry's record: even lanes store P of heads col, col + 1, odd lanes
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mfma_kernel(AttnBwdDev G) {
       float pk[4], dsk[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pk[i] = ca[t] != -1 ? exp2f(sk[i] * sl2 - lse2_g[i]) : 0.0f;
+        pk[i] = ca[t] != -1 ? exp2_unit(sk[i] * sl2 - lse2_g[i]) : 0.0f;
         dsk[i] = pk[i] * (dp[i] - dt_g[i]);
       }
       const u32x2 pA = {pack_bf16x2(pk[0], pk[1]), pack_bf16x2(pk[2], pk[3])};
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void key_bwd_kernel(AttnBwdDev G) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t li = row * 16 + 4 * g + i;
-        const float pe = vis ? exp2f(sv[i] * sl2 - G.lse[li] * kLog2e) : 0.0f;
+        const float pe = vis ? exp2_unit(sv[i] * sl2 - G.lse[li] * kLog2e) : 0.0f;
         pv[tt][i] = pe;
         dsv[tt][i] = pe * (dp[i] - G.dt_out[li]);
       }
