@@ -4,7 +4,7 @@
 //
 // The indexer keeps the top-k compressed entries of each query (Lighthouse, "deep deepseek
 // v4 release", section 八 item 3); ties go to the lowest index and the output is ascending
-// (the reading taken where the pages are silent).  A segment extract block per 8192 keys
+// (the reading taken where the pages are silent).  A segment extract block per 2048 keys
 // lists the keys at or above the row's sampled floor; the resolve takes the row's exact
 // top-k among the concatenated lists, or falls back to the exact whole-row selection when
 // a list overflowed or fewer than k keys were listed.
@@ -79,9 +79,24 @@ __device__ void seg_resolve_row(const TopkDev& P, const SegWs& S, int vec, int r
     const int lane = threadIdx.x;
     int carry = 0;
     bool over = false;
+    // the first four rounds' counts are loaded together (one memory latency for rows of up
+    // to 256 segments), later rounds' as they come
+    int pre4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sg = 64 * q + lane;
+      pre4[q] = sg < nseg ? static_cast<int>(cnt[sg]) : 0;
+    }
     for (int base = 0; base < nseg; base += 64) {
       const int sg = base + lane;
-      const int c = sg < nseg ? static_cast<int>(cnt[sg]) : 0;
+      int c = 0;
+      if (base < 256) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (base == 64 * q) c = pre4[q];
+      } else {
+        c = sg < nseg ? static_cast<int>(cnt[sg]) : 0;
+      }
       over |= c > kSegCap;
       int inc = c < kSegCap ? c : kSegCap;
 #pragma unroll
