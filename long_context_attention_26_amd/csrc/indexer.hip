@@ -152,9 +152,11 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IdxDev A) {
 // accumulator sets, so one sub-tile's epilogue overlaps the next one's MFMAs.  Output lane
 // layout: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 of the tile and key l%32,
 // so the H_I <= 4 heads of a query token sit in consecutive registers of one lane and the
-// ReLU / weight / head-sum epilogue is lane-local.  A wave stages a sub-tile's scores in LDS
-// as [token][32 keys] and writes each token's 32 scores with 16-byte stores; sub-tiles that
-// straddle the causal edge of the block's tokens are written score by score, masked.
+// ReLU / weight / head-sum epilogue is lane-local.  A wave stages its tokens' scores in LDS
+// and writes them with 16-byte stores: a whole 128-key tile per token (one 256-byte run at
+// bf16) when every token of the block sees the tile and the staging fits in 4 KB per wave,
+// else each 32-key sub-tile; sub-tiles that straddle the causal edge of the block's tokens are
+// written score by score, masked.  The kernel is held to four waves per SIMD.
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16g;
 
 // fp32 -> bf16 bits, round to nearest even (the gfx950 conversion instruction): a pair
@@ -172,7 +174,7 @@ constexpr int kGemmKeys = 32;           // keys per MFMA tile
 constexpr int kGemmTile = 128;          // keys per LDS tile (four MFMA tiles)
 
 template <int HI, bool SBF16, int KSTEPS, int NT>
-__global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
+__global__ __launch_bounds__(NT, 4) void index_scores_gemm_kernel(IdxDev A) {
   constexpr int DI = KSTEPS * 16;                 // channels
   constexpr int STRIDE = DI + 8;                  // LDS row pitch (elements): no bank conflicts
   constexpr int CHUNKS = kGemmTile * DI / 8;      // 16-byte pieces of one key tile
@@ -180,7 +182,11 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
   constexpr int TOK = 32 / HI;                    // query tokens of a wave
   constexpr int ES = SBF16 ? 2 : 4;               // score bytes
   __shared__ __align__(16) uint16_t s_k[2][kGemmTile * STRIDE];
-  __shared__ __align__(16) uint32_t s_o[NT / 64][TOK * kGemmKeys * ES / 4];   // per wave
+  // a whole tile's scores of the wave's tokens are staged when they fit in 4 KB per wave,
+  // so each token's 128 scores leave as one contiguous run
+  constexpr bool STAGE = TOK * kGemmTile * ES <= 4096;
+  constexpr int SO = (STAGE ? kGemmTile : kGemmKeys) * TOK * ES / 4;
+  __shared__ __align__(16) uint32_t s_o[NT / 64][SO];   // per wave
   // 16-byte score stores need 16-byte aligned rows
   const bool vec_out = (A.N * ES) % 16 == 0 && reinterpret_cast<uintptr_t>(A.scores) % 16 == 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
   };
   // scores sum_g w_g max(d_g, 0) of the sub-tile starting at key js (a +0-started chain
   // never ends at -0)
-  auto emit = [&](const f32x16g& d, int js) {
+  auto emit = [&](const f32x16g& d, int js, bool stage, int u) {
     const int j = js + col;
     float sc[QPL];
 #pragma unroll
@@ -282,6 +288,23 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
 #pragma unroll
       for (int g = 0; g < HI; ++g) v = fmaf(w[t][g], relu(d[t * HI + g]), v);
       sc[t] = v;
+    }
+    if (STAGE && stage) {
+      // into the wave's staging rows (one per token, kGemmTile scores), sub-tile u
+#pragma unroll
+      for (int t = 0; t < QPL; t += 2) {
+        if constexpr (SBF16) {
+          uint16_t* o16 = reinterpret_cast<uint16_t*>(&s_o[wave][0]);
+          const uint32_t pk = bf16_pair(sc[t], sc[t + 1]);
+          o16[qloc[t] * kGemmTile + u * kGemmKeys + col] = static_cast<uint16_t>(pk & 0xffffu);
+          o16[qloc[t + 1] * kGemmTile + u * kGemmKeys + col] = static_cast<uint16_t>(pk >> 16);
+        } else {
+          float* o32 = reinterpret_cast<float*>(&s_o[wave][0]);
+          o32[qloc[t] * kGemmTile + u * kGemmKeys + col] = sc[t];
+          o32[qloc[t + 1] * kGemmTile + u * kGemmKeys + col] = sc[t + 1];
+        }
+      }
+      return;
     }
     if (vec_out && js + kGemmKeys <= nv_lo) {
       // every token of the block sees the whole sub-tile
@@ -326,6 +349,24 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
     }
   };
 
+  // a staged tile's scores: token ql's kGemmTile scores from key j0 as 16-byte pieces
+  auto store_tile = [&](int j0) {
+    constexpr int EPP = 16 / ES;                 // scores per 16-byte piece
+    constexpr int PPQ = kGemmTile / EPP;         // pieces per token
+    constexpr int NPIECE = TOK * PPQ;
+#pragma unroll
+    for (int p0 = 0; p0 < NPIECE; p0 += 64) {
+      const int p = p0 + lane;
+      if (NPIECE % 64 == 0 || p < NPIECE) {
+        const int ql = p / PPQ, kp = p % PPQ;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const char*>(&s_o[wave][0]) + (ql * kGemmTile + kp * EPP) * ES);
+        *reinterpret_cast<u32x4*>(static_cast<char*>(A.scores) +
+                                  ((tok0 + ql) * A.N + j0 + kp * EPP) * ES) = v;
+      }
+    }
+  };
+
   fetch(kstart);
   stash(0);
   __syncthreads();
@@ -334,15 +375,18 @@ __global__ __launch_bounds__(NT) void index_scores_gemm_kernel(IdxDev A) {
     const bool more = j0 + kGemmTile < kstop;
     if (more) fetch(j0 + kGemmTile);              // in flight during this tile
     const int nsub = min(kGemmTile, kstop - j0 + kGemmKeys - 1) / kGemmKeys;   // block-uniform
+    // every token of the block sees the whole tile: stage it and store whole runs
+    const bool stage = STAGE && vec_out && j0 + kGemmTile <= nv_lo;   // block-uniform
     f32x16g da, db;
     mma(da, buf, 0);
 #pragma unroll
     for (int u = 0; u < kGemmTile / kGemmKeys; u += 2) {
       if (u + 1 < nsub) mma(db, buf, u + 1);
-      if (u < nsub) emit(da, j0 + u * kGemmKeys);
+      if (u < nsub) emit(da, j0 + u * kGemmKeys, stage, u);
       if (u + 2 < nsub) mma(da, buf, u + 2);
-      if (u + 1 < nsub) emit(db, j0 + (u + 1) * kGemmKeys);
+      if (u + 1 < nsub) emit(db, j0 + (u + 1) * kGemmKeys, stage, u + 1);
     }
+    if (stage) store_tile(j0);
     if (more) stash(buf ^ 1);
     __syncthreads();
     buf ^= 1;
