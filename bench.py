@@ -326,10 +326,14 @@ def train_backward(args):
             hcsa.compress_kv_bwd(x, om[n], r_, grads[gy], grads[gx], dom[n], workspace=ws_p)
         mark(4)
 
+    nvtx = torch.cuda.nvtx                       # roctx ranges (rocprofv3 --marker-trace)
+    nvtx.range_push("backward warmup")
     for _ in range(args.warmup):
         backward()
     torch.cuda.synchronize()
+    nvtx.range_pop()
     evs = []
+    nvtx.range_push("backward timed steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -337,6 +341,7 @@ def train_backward(args):
         evs.append(e)
     torch.cuda.synchronize()
     el = (time.perf_counter() - t0) / args.steps
+    nvtx.range_pop()
     br = {s_: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / len(evs) for j, s_ in enumerate(stages)}
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     f0.record()
@@ -481,10 +486,14 @@ def main():
         else:
             full[c].replay()
 
+    nvtx = torch.cuda.nvtx                       # roctx ranges (rocprofv3 --marker-trace)
+    nvtx.range_push("decode warmup")
     for i in range(args.warmup):
         one_step(i % R, False)
     torch.cuda.synchronize()
+    nvtx.range_pop()
     assert args.steps == 0 or (base % R) != ((args.warmup - 1) % R) or R == 1
+    nvtx.range_push("decode timed steps")
     t0 = time.perf_counter()
     i = 0
     while i < args.steps:
@@ -496,6 +505,7 @@ def main():
             i += 1
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    nvtx.range_pop()
     ms = el / args.steps * 1e3
     qps = cfg.B * cfg.Nq / (el / args.steps)
 
